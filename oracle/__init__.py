@@ -1,0 +1,39 @@
+"""CPU oracle for the Multi-Latent Attention (MLA) forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or run
+anything in this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+library (no kernels, headers, tables or helpers); the only module both sides use
+is ``mla_inputs``, which draws the seeded inputs and holds none of the method's
+arithmetic.
+
+Everything is float64 NumPy (``mla.py``) or pure-Python scalar loops
+(``brute.py``), written from the pages' statement of the layer:
+
+* "CSDN walkthrough of HF DeepseekV3Attention" (``__init__`` and ``forward``
+  listing): projections, latent RMSNorm, split, RoPE on the 64-wide slice with a
+  single shared key head, concatenation, YaRN softmax-scale correction.
+* "kimi_vl.py - KimiVL (DeepSeek-V3 architecture) attention adapter", sections
+  "Q projection and KV compression" and "concatenating the final Q and K".
+* "MiniMind: attention forward pass", section 3 (RMSNorm in fp32, rotate_half
+  RoPE), section 5 (scaled dot product, causal mask, fp32 softmax), section 7
+  (merge heads, output projection).
+* "Megatron-LM MLA guide", sections on projection dimensions, YaRN parameters,
+  softmax scale, THD packing and the inference section (latent cache and weight
+  absorption).
+* "Kimi-K3 atlas: Gated MLA" (mla-init, mla-forward, rmsnorm excerpts): the
+  unrotated shared key part and the full-rank output gate.
+
+Parity status of each function is listed in its docstring ("pinned by ...").
+Two readings are not pinned by anything on the pages, because the pages cite the
+YaRN paper without printing its formulas: the constant of the YaRN attention
+factor (``yarn_get_mscale``) and the ramp of the YaRN frequency blend
+(``rope_inv_freq`` for kind "yarn").  Their structural properties are pinned
+(identity at factor 1, wavelength limits); the constants are "parity unpinned".
+"""
+from .mla import (  # noqa: F401
+    rms_norm, yarn_get_mscale, softmax_scale, rope_inv_freq, rope_cos_sin,
+    rotate_half, apply_rope, causal_varlen_attention, mla_prefill, mla_prefill_rows,
+    kv_latent, gather_paged, decode_naive, decode_absorbed, prefill_latent_absorbed,
+    row_rel_error,
+)

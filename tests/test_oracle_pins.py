@@ -1,0 +1,329 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these compares the oracle with itself: each test checks a closed form,
+an invariant, a special case that reduces to a library routine, a second
+formulation written independently, or the scalar brute force.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import mla_inputs as mi
+from oracle import brute
+from oracle import mla as om
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "page_dims.json")
+
+
+def tiny_shape(**kw):
+    base = dict(name="tiny", dtype="f32", hidden=8, num_heads=2, q_lora_rank=6, kv_lora_rank=4,
+                qk_nope_dim=4, qk_rope_dim=4, v_head_dim=3, rope=mi.RopeSpec(kind="plain", theta=10000.0),
+                num_docs=1, total_tokens=5, seed=11)
+    base.update(kw)
+    return mi.MLAShape(**base)
+
+
+# ----------------------------------------------------------------------------- RMSNorm
+def test_rmsnorm_constant_vector_closed_form():
+    for a in (-3.0, -1e-4, 0.5, 7.0):
+        x = np.full((1, 16), a)
+        y = om.rms_norm(x, np.ones(16), 1e-6)
+        want = a / math.sqrt(a * a + 1e-6)
+        assert np.allclose(y, want, rtol=0, atol=1e-15)
+
+
+def test_rmsnorm_mean_square_identity_and_gain():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((7, 33)) * 0.01
+    eps = 1e-4
+    y = om.rms_norm(x, np.ones(33), eps)
+    ms = np.mean(x * x, -1)
+    assert np.allclose(np.mean(y * y, -1), ms / (ms + eps), rtol=1e-13)
+    g = rng.standard_normal(33)
+    assert np.allclose(om.rms_norm(x, g, eps), y * g, rtol=1e-14)
+
+
+# ----------------------------------------------------------------------------- RoPE
+def _plain(theta=10000.0):
+    return mi.RopeSpec(kind="plain", theta=theta)
+
+
+def test_rope_position_zero_is_identity():
+    x = np.random.default_rng(1).standard_normal((3, 64))
+    c, s = om.rope_cos_sin([0, 0, 0], 64, _plain())
+    assert np.array_equal(om.apply_rope(x, c, s), x)
+
+
+def test_rope_basis_vector_closed_form():
+    d, p = 16, 5
+    c, s = om.rope_cos_sin([p], d, _plain())
+    for i in range(d // 2):
+        th = 10000.0 ** (-2 * i / d)
+        e = np.zeros((1, d)); e[0, i] = 1.0
+        y = om.apply_rope(e, c, s)[0]
+        want = np.zeros(d); want[i] = math.cos(p * th); want[i + d // 2] = math.sin(p * th)
+        assert np.allclose(y, want, atol=1e-15)
+        e2 = np.zeros((1, d)); e2[0, i + d // 2] = 1.0
+        y2 = om.apply_rope(e2, c, s)[0]
+        want2 = np.zeros(d); want2[i] = -math.sin(p * th); want2[i + d // 2] = math.cos(p * th)
+        assert np.allclose(y2, want2, atol=1e-15)
+
+
+@pytest.mark.parametrize("rope", [_plain(), mi.YARN_V3])
+def test_rope_norm_preserving_and_relative(rope):
+    rng = np.random.default_rng(2)
+    q, k = rng.standard_normal((2, 64))
+    for m, n, dlt in [(0, 3, 11), (100, 7, 500), (4000, 4095, 1)]:
+        cm, sm = om.rope_cos_sin([m, n, m + dlt, n + dlt], 64, rope)
+        rq = om.apply_rope(q[None], cm[0:1], sm[0:1])[0]
+        rk = om.apply_rope(k[None], cm[1:2], sm[1:2])[0]
+        rq2 = om.apply_rope(q[None], cm[2:3], sm[2:3])[0]
+        rk2 = om.apply_rope(k[None], cm[3:4], sm[3:4])[0]
+        assert abs(np.linalg.norm(rq) - np.linalg.norm(q)) < 1e-12
+        assert abs(rq @ rk - rq2 @ rk2) < 1e-9
+
+
+# ----------------------------------------------------------------------------- YaRN
+def test_yarn_factor_one_is_plain_rope():
+    y = mi.RopeSpec(kind="yarn", theta=10000.0, factor=1.0, original_max_pos=4096, mscale=1.0, mscale_all_dim=1.0)
+    assert np.allclose(om.rope_inv_freq(64, y), om.rope_inv_freq(64, _plain()), rtol=2e-16, atol=0)
+    assert om.yarn_get_mscale(1.0, 1.0) == 1.0
+    assert om.yarn_get_mscale(0.5, 3.0) == 1.0
+    assert om.yarn_get_mscale(40.0, 0.0) == 1.0
+
+
+def test_yarn_wavelength_limits():
+    """High-frequency pairs (wavelength < L/beta_fast) keep their frequency;
+    low-frequency pairs (wavelength > L/beta_slow) are divided by s exactly;
+    the ratio in between is monotone."""
+    y = mi.YARN_V3
+    plain = om.rope_inv_freq(64, _plain())
+    yarn = om.rope_inv_freq(64, y)
+    wl = 2 * math.pi / plain
+    L = y.original_max_pos
+    fast = wl < L / y.beta_fast
+    slow = wl > L / y.beta_slow
+    assert fast.sum() >= 8 and slow.sum() >= 8
+    assert np.array_equal(yarn[fast], plain[fast])
+    assert np.allclose(yarn[slow], plain[slow] / y.factor, rtol=1e-15)
+    ratio = yarn / plain
+    assert np.all(np.diff(ratio) <= 1e-15) and ratio.min() >= 1 / y.factor - 1e-15
+
+
+def test_softmax_scale_readings():
+    ws = mi.WORKLOADS
+    assert om.softmax_scale(ws["tiny_fp32_t64"]) == 48 ** -0.5
+    assert om.softmax_scale(ws["megatron_2x2048"]) == 192 ** -0.5
+    assert om.softmax_scale(ws["kimi_gated_varlen_8192"]) == 192 ** -0.5
+    # mscale_all_dim = 0 leaves the plain scale (page 2: only applied when set)
+    s0 = mi.WORKLOADS["dsv3_prefill_4096"].replace(rope=mi.YARN_V3.__class__(**{**mi.YARN_V3.__dict__, "mscale_all_dim": 0.0}))
+    assert om.softmax_scale(s0) == 192 ** -0.5
+    v3 = om.softmax_scale(ws["dsv3_prefill_4096"])
+    assert v3 > 192 ** -0.5
+
+
+# ----------------------------------------------------------------------------- attention
+def _rand_qkv(n, h, dqk, dv, seed=3):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((n, h, dqk)), rng.standard_normal((n, h, dqk)), rng.standard_normal((n, h, dv))
+
+
+def test_attention_single_token_returns_own_value():
+    q, k, v = _rand_qkv(4, 3, 6, 5)
+    out = om.causal_varlen_attention(q, k, v, 0.3, [0, 1, 2, 3, 4])
+    assert np.array_equal(out, v)
+
+
+def test_attention_zero_query_is_prefix_mean():
+    q, k, v = _rand_qkv(9, 2, 6, 5)
+    q[:] = 0
+    out = om.causal_varlen_attention(q, k, v, 0.7, [0, 9])
+    want = np.cumsum(v, 0) / np.arange(1, 10)[:, None, None]
+    assert np.allclose(out, want, rtol=1e-13)
+
+
+def test_attention_dominant_score_selects_value():
+    q, k, v = _rand_qkv(6, 1, 4, 3)
+    k[:] = 0
+    k[2, 0, 0] = 1.0
+    q[:, 0, 0] = 1e4
+    out = om.causal_varlen_attention(q, k, v, 1.0, [0, 6])
+    assert np.allclose(out[2:], np.broadcast_to(v[2], (4, 1, 3)), atol=1e-12)
+
+
+def test_attention_causality_bit_exact_and_varlen_split():
+    q, k, v = _rand_qkv(12, 2, 6, 4)
+    cu = [0, 5, 12]
+    base = om.causal_varlen_attention(q, k, v, 0.4, cu)
+    q2, k2, v2 = q.copy(), k.copy(), v.copy()
+    q2[8:] += 1.0; k2[8:] -= 2.0; v2[8:] *= 3.0
+    pert = om.causal_varlen_attention(q2, k2, v2, 0.4, cu)
+    assert np.array_equal(base[:8], pert[:8])
+    a = om.causal_varlen_attention(q[:5], k[:5], v[:5], 0.4, [0, 5])
+    b = om.causal_varlen_attention(q[5:], k[5:], v[5:], 0.4, [0, 7])
+    assert np.array_equal(np.concatenate([a, b]), base)
+    # evaluating selected rows only gives the same rows as the full evaluation
+    rows = om.causal_varlen_attention(q, k, v, 0.4, cu, rows=[3, 11])
+    assert np.allclose(rows, base[[3, 11]], rtol=1e-13)
+
+
+def test_attention_matches_torch_sdpa_float64():
+    q, k, v = _rand_qkv(17, 3, 12, 7)
+    out = om.causal_varlen_attention(q, k, v, 12 ** -0.5, [0, 17])
+    tq, tk, tv = (torch.from_numpy(a).permute(1, 0, 2).contiguous() for a in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True).permute(1, 0, 2).numpy()
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------- layer vs brute force
+@pytest.mark.parametrize("kw", [
+    dict(),
+    dict(q_lora_rank=0, num_heads=1, total_tokens=6),
+    dict(rope=mi.RopeSpec(kind="none"), output_gate=True),
+])
+def test_prefill_matches_scalar_brute_force(kw):
+    sh = tiny_shape(**kw)
+    lens = [2, 1, 4] if sh.total_tokens != 6 else [6]
+    case = mi.make_prefill_case(sh, doc_lengths=lens)
+    ref = om.mla_prefill(sh, case.w, case.x, case.cu_seqlens)["out"]
+    bf = np.array(brute.prefill(sh, case.w, case.x, case.cu_seqlens))
+    assert np.allclose(ref, bf, rtol=1e-12, atol=1e-14)
+
+
+def test_tiny_fp32_workload_rows_match_brute_force():
+    sh = mi.WORKLOADS["tiny_fp32_t64"]
+    case = mi.make_prefill_case(sh, doc_lengths=[12])      # first 12 tokens of the workload draws
+    ref = om.mla_prefill(sh, case.w, case.x, case.cu_seqlens)["out"]
+    bf = np.array(brute.prefill(sh, case.w, case.x, case.cu_seqlens))
+    assert np.allclose(ref, bf, rtol=1e-11, atol=1e-13)
+
+
+def test_prefill_rows_equals_full():
+    sh = tiny_shape(total_tokens=10, rope=mi.YARN_V3.__class__(**{**mi.YARN_V3.__dict__, "original_max_pos": 8}))
+    case = mi.make_prefill_case(sh, doc_lengths=[3, 7])
+    full = om.mla_prefill(sh, case.w, case.x, case.cu_seqlens)
+    rows = [0, 2, 3, 9]
+    part = om.mla_prefill_rows(sh, case.w, case.x, case.cu_seqlens, rows)
+    assert np.allclose(part["out"], full["out"][rows], rtol=1e-13)
+
+
+# ----------------------------------------------------------------------------- MLA identities
+def _absorbed_equals_naive(sh, lens):
+    case = mi.make_prefill_case(sh, doc_lengths=lens)
+    res = om.mla_prefill(sh, case.w, case.x, case.cu_seqlens)
+    A_lat = om.prefill_latent_absorbed(sh, case.w["w_kv_b"], res["q"], res["latent"], case.cu_seqlens)
+    A = res["attn"].reshape(A_lat.shape)
+    if sh.output_gate:
+        return
+    assert np.allclose(A_lat, A, rtol=1e-11, atol=1e-13)
+
+
+def test_mla_latent_form_equals_decompressed_mha():
+    _absorbed_equals_naive(tiny_shape(total_tokens=9), [4, 5])
+    sh = mi.WORKLOADS["megatron_2x2048"].replace(hidden=64, num_heads=2)
+    _absorbed_equals_naive(sh, [5, 11])
+
+
+def test_decode_absorbed_equals_naive_and_paged_equals_dense():
+    sh = mi.WORKLOADS["dsv3_decode_64"].replace(num_heads=4)
+    dc = mi.make_decode_case(sh, batch=3, len_lo=5, len_hi=150, block_size=16)
+    a = om.decode_absorbed(sh, dc.w_kv_b, dc.q_nope, dc.q_pe, dc.cache, dc.block_table, dc.seq_lens, 16)
+    n = om.decode_naive(sh, dc.w_kv_b, dc.q_nope, dc.q_pe, dc.cache, dc.block_table, dc.seq_lens, 16)
+    assert np.all(np.isfinite(a)) and np.allclose(a, n, rtol=1e-10, atol=1e-12)
+    # paged gather equals the rows stored densely in table order
+    b = 1
+    L = int(dc.seq_lens[b])
+    dense = np.concatenate([dc.cache[blk] for blk in dc.block_table[b] if blk >= 0], 0)[:L]
+    assert np.array_equal(om.gather_paged(dc.cache, dc.block_table, b, L, 16), dense)
+
+
+def test_prefill_last_row_equals_decode_over_written_latents():
+    """Row t of a prefill over one document equals decode of the query at t over
+    the latent cache that prefill wrote for tokens 0..t (ties the prefill
+    latent row to the decode path)."""
+    sh = mi.WORKLOADS["megatron_2x2048"].replace(hidden=32, num_heads=2)
+    T = 7
+    case = mi.make_prefill_case(sh, doc_lengths=[T])
+    res = om.mla_prefill(sh, case.w, case.x, case.cu_seqlens)
+    bs = 4
+    nblk = (T + bs - 1) // bs
+    cache = np.full((nblk + 1, bs, res["latent"].shape[1]), np.nan)
+    table = np.array([[2, 0]], dtype=np.int32)
+    for j in range(T):
+        cache[table[0, j // bs], j % bs] = res["latent"][j]
+    q = res["q"][T - 1][None]
+    out = om.decode_absorbed(sh, case.w["w_kv_b"], q[..., :128], q[..., 128:], cache, table, [T], bs)
+    assert np.allclose(out[0], res["attn"][T - 1].reshape(2, 128), rtol=1e-11, atol=1e-13)
+
+
+def test_gate_and_nope_variant_single_token_returns_own_value():
+    """A one-token document: out = W_o (v * sigmoid(g)) for the gated NoPE layer."""
+    sh = tiny_shape(rope=mi.RopeSpec(kind="none"), output_gate=True, total_tokens=3)
+    case = mi.make_prefill_case(sh, doc_lengths=[1, 1, 1])
+    res = om.mla_prefill(sh, case.w, case.x, case.cu_seqlens)
+    v = res["kv"][..., sh.qk_nope_dim:].reshape(3, -1)
+    g = case.x.astype(np.float64) @ case.w["w_g"].astype(np.float64).T
+    want = (v / (1 + np.exp(-g))) @ case.w["w_o"].astype(np.float64).T
+    assert np.allclose(res["out"], want, rtol=1e-12)
+
+
+# ----------------------------------------------------------------------------- page-printed dims
+def test_page_dimension_relations():
+    g = json.load(open(GOLD))
+    d = g["megatron_config_class_defaults"]
+    # cache row width per token = kv_lora_rank + qk_pos_emb_head_dim
+    sh = mi.WORKLOADS["dsv3_prefill_4096"]
+    assert sh.kv_lora_rank + sh.qk_rope_dim == d["kv_lora_rank"] + d["qk_pos_emb_head_dim"] == 576
+    assert d["qk_head_dim"] + d["qk_pos_emb_head_dim"] == 192
+    k3 = g["kimi_k3_text_config"]
+    kimi = mi.WORKLOADS["kimi_gated_varlen_8192"]
+    for a, b in [("hidden_size", "hidden"), ("num_attention_heads", "num_heads"), ("q_lora_rank", "q_lora_rank"),
+                 ("qk_nope_head_dim", "qk_nope_dim"), ("qk_rope_head_dim", "qk_rope_dim"), ("v_head_dim", "v_head_dim")]:
+        assert k3[a] == getattr(kimi, b)
+    assert kimi.rope.kind == "none" and k3["mla_use_nope"]
+    y = g["megatron_yarn_defaults"]
+    assert (mi.YARN_V3.theta, mi.YARN_V3.factor, mi.YARN_V3.original_max_pos, mi.YARN_V3.beta_fast,
+            mi.YARN_V3.beta_slow, mi.YARN_V3.mscale) == (y["rotary_base"], y["rotary_scaling_factor"],
+                                                           y["original_max_position_embeddings"], y["beta_fast"],
+                                                           y["beta_slow"], y["mscale"])
+
+
+def test_megatron_unit_test_config_shapes_and_identity():
+    """The unit-test configuration printed on the Megatron page, with YaRN at
+    its defaults and original_max_position_embeddings = 32: the intermediate
+    widths follow the page's projection table and the latent form of the
+    attention equals the decompressed form."""
+    g = json.load(open(GOLD))
+    c = g["megatron_unit_test_config"]
+    y = g["megatron_yarn_defaults"]
+    rope = mi.RopeSpec(kind="yarn", theta=y["rotary_base"], factor=y["rotary_scaling_factor"],
+                       original_max_pos=c["original_max_position_embeddings"], beta_fast=y["beta_fast"],
+                       beta_slow=y["beta_slow"], mscale=y["mscale"], mscale_all_dim=y["mscale_all_dim"])
+    sh = mi.MLAShape(name="megatron_test", dtype="f32", hidden=c["hidden_size"], num_heads=c["num_attention_heads"],
+                     q_lora_rank=c["q_lora_rank"], kv_lora_rank=c["kv_lora_rank"], qk_nope_dim=c["qk_head_dim"],
+                     qk_rope_dim=c["qk_pos_emb_head_dim"], v_head_dim=c["v_head_dim"], rope=rope, seed=7)
+    case = mi.make_prefill_case(sh, doc_lengths=[6, 3])
+    res = om.mla_prefill(sh, case.w, case.x, case.cu_seqlens)
+    H = c["num_attention_heads"]
+    assert res["q"].reshape(9, -1).shape[1] == H * (c["qk_head_dim"] + c["qk_pos_emb_head_dim"])
+    assert res["latent"].shape[1] == c["kv_lora_rank"] + c["qk_pos_emb_head_dim"]
+    assert res["kv"].reshape(9, -1).shape[1] == H * (c["qk_head_dim"] + c["v_head_dim"])
+    assert res["attn"].shape[1] == c["v_head_dim"] * H and res["out"].shape[1] == c["hidden_size"]
+    A_lat = om.prefill_latent_absorbed(sh, case.w["w_kv_b"], res["q"], res["latent"], case.cu_seqlens)
+    assert np.allclose(A_lat.reshape(9, -1), res["attn"], rtol=1e-11, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------- planted mistakes
+def test_planted_mistakes_are_caught(monkeypatch):
+    """A wrong sign in rotate_half, or a transposed kv_b split, must break the
+    brute-force or identity pins (checks that the pins have teeth)."""
+    sh = tiny_shape()
+    case = mi.make_prefill_case(sh, doc_lengths=[5])
+    bf = np.array(brute.prefill(sh, case.w, case.x, case.cu_seqlens))
+    monkeypatch.setattr(om, "rotate_half", lambda x: np.concatenate([x[..., x.shape[-1] // 2:], -x[..., :x.shape[-1] // 2]], -1))
+    bad = om.mla_prefill(sh, case.w, case.x, case.cu_seqlens)["out"]
+    assert not np.allclose(bad, bf, rtol=1e-6)
