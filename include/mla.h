@@ -1,0 +1,247 @@
+/*
+ * libmla — Multi-Latent Attention (MLA) forward pass for AMD Instinct MI355X
+ * (gfx950 / CDNA4).  C ABI: plain pointers and sizes only.
+ *
+ * The layer (as stated by "CSDN walkthrough of HF DeepseekV3Attention",
+ * __init__/forward, and "kimi_vl.py - KimiVL attention adapter", sections
+ * "Q projection and KV compression" and "concatenating the final Q and K"):
+ *
+ *   q        = q_lora_rank ? W_qb * RMSNorm_q(W_qa x) : W_q x     [N, H, d_nope + d_rope]
+ *   [c|k_pe] = W_kva x                                            [N, r_kv + d_rope]
+ *   c_n      = RMSNorm_kv(c)
+ *   kv       = W_kvb c_n                                          [N, H, d_nope + d_v]
+ *   q_pe, k_pe rotated by RoPE (plain or YaRN) at each token's position, k_pe
+ *   being ONE head shared by all H heads; not rotated for MLA_ROPE_NONE (the
+ *   unrotated shared part of "Kimi-K3 atlas: Gated MLA")
+ *   A_h      = softmax(scale * [q_nope|q_pe]_h [k_nope_h|k_pe]^T + causal) v_h
+ *   A        = A * sigmoid(W_g x)          (output_gate, "Kimi-K3 atlas" mla-init)
+ *   out      = W_o A                                              [N, hidden]
+ *
+ * Conventions for every call
+ *   - Ownership: the caller owns every buffer.  The library allocates no device
+ *     or host memory, keeps no device state between calls and never
+ *     synchronises: device work is enqueued on `stream` (a hipStream_t; NULL is
+ *     the default stream) and runs asynchronously.
+ *   - Errors: all argument checks run on the host before anything is enqueued,
+ *     so a call enqueues all of its work or none of it.  A failed check returns
+ *     a status other than MLA_OK; mla_last_error() returns a message for the
+ *     last failure on the calling thread.  A failed kernel launch returns
+ *     MLA_ERR_HIP (work enqueued before it in the same call may have run).
+ *   - Layout: row-major, token-major ("THD": packed tokens, no padding).
+ *     Linear weights use the nn.Linear layout [out_features, in_features] and
+ *     compute y = x W^T ("MiniMind: attention forward pass" section 2).  Device
+ *     pointers must be 16-byte aligned and row strides multiples of 8 elements
+ *     (MLA_ERR_MISALIGNED otherwise).
+ *   - Dtypes: cfg.dtype MLA_BF16 (bf16 storage, fp32 accumulation and fp32
+ *     softmax/norm arithmetic) or MLA_F32 (fp32 everywhere).  Norm gains use the
+ *     weight dtype; RoPE tables are fp32; index arrays are int32.
+ *   - Shapes supported by the bf16 kernels: d_nope = 128, d_rope = 64,
+ *     d_v = 128, r_kv = 512 (the DeepSeek-V3 / Kimi head shape); other shapes
+ *     return MLA_ERR_UNSUPPORTED for bf16.  The fp32 kernels take any
+ *     d_nope, d_v <= 256, even d_rope <= 128 and r_kv <= 1024.
+ */
+#ifndef LIBMLA_MLA_H
+#define LIBMLA_MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+
+typedef enum mla_status {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1,   /* null pointer, bad dimension, inconsistent sizes      */
+  MLA_ERR_UNSUPPORTED = 2,   /* valid MLA configuration with no compiled kernel       */
+  MLA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than the *_workspace_size */
+  MLA_ERR_MISALIGNED = 4,    /* pointer not 16-byte aligned / stride not a multiple of 8 */
+  MLA_ERR_HIP = 5            /* a HIP launch or copy failed                            */
+} mla_status;
+
+typedef enum mla_dtype { MLA_BF16 = 0, MLA_F32 = 1 } mla_dtype;
+
+/* RoPE variant ("Megatron-LM MLA guide", normalization and position-encoding
+ * parameters: rope or yarn; "Kimi-K3 atlas": no rotary embedding). */
+typedef enum mla_rope_kind { MLA_ROPE_NONE = 0, MLA_ROPE_PLAIN = 1, MLA_ROPE_YARN = 2 } mla_rope_kind;
+
+/* Layer configuration.  Every field is explicit; nothing is defaulted.
+ * Dimension names follow "CSDN walkthrough of HF DeepseekV3Attention" (__init__):
+ * q_head_dim = qk_nope_dim + qk_rope_dim. */
+typedef struct mla_config {
+  int32_t hidden;            /* model width                                           */
+  int32_t num_heads;         /* H                                                     */
+  int32_t q_lora_rank;       /* r_q; 0 => direct q projection (no query latent)       */
+  int32_t kv_lora_rank;      /* r_kv                                                  */
+  int32_t qk_nope_dim;       /* d_nope                                                */
+  int32_t qk_rope_dim;       /* d_rope (even)                                         */
+  int32_t v_head_dim;        /* d_v (may differ from d_nope + d_rope; never padded)   */
+  int32_t dtype;             /* mla_dtype                                             */
+  int32_t rope_kind;         /* mla_rope_kind                                         */
+  int32_t yarn_original_max_pos; /* YaRN original_max_position_embeddings              */
+  int32_t output_gate;       /* 1 => out = W_o (A * sigmoid(W_g x))                    */
+  float norm_eps;            /* RMSNorm epsilon (inside the mean)                     */
+  float softmax_scale;       /* > 0: used as is; <= 0: derived (mla_softmax_scale)     */
+  double rope_theta;         /* rotary base                                           */
+  double yarn_factor;        /* YaRN scale s                                          */
+  double yarn_beta_fast;
+  double yarn_beta_slow;
+  double yarn_mscale;
+  double yarn_mscale_all_dim;
+} mla_config;
+
+/* Device pointers to the layer weights, nn.Linear layout, dtype = cfg.dtype. */
+typedef struct mla_weights {
+  const void* w_q_a;       /* [r_q, hidden]            (q_lora_rank > 0, else NULL)   */
+  const void* q_a_gamma;   /* [r_q]                    (q_lora_rank > 0, else NULL)   */
+  const void* w_q_b;       /* [H*(d_nope+d_rope), r_q] (q_lora_rank > 0, else NULL)   */
+  const void* w_q;         /* [H*(d_nope+d_rope), hidden] (q_lora_rank == 0, else NULL) */
+  const void* w_kv_a;      /* [r_kv + d_rope, hidden]                                 */
+  const void* kv_a_gamma;  /* [r_kv]                                                  */
+  const void* w_kv_b;      /* [H*(d_nope+d_v), r_kv]; rows of head h: [k_nope | v]    */
+  const void* w_o;         /* [hidden, H*d_v]                                         */
+  const void* w_g;         /* [H*d_v, hidden] (output_gate, else NULL)                */
+} mla_weights;
+
+/* ---------------------------------------------------------------- host-only */
+
+/* ABI version of the loaded library (MLA_ABI_VERSION). */
+int32_t mla_abi_version(void);
+
+/* Checks a configuration (dims positive, rope dim even, YaRN parameters
+ * sensible).  Host-only, no device work. */
+mla_status mla_validate_config(const mla_config* cfg);
+
+/* Softmax scale: (d_nope + d_rope)^-0.5, times mscale^2 for YaRN with a
+ * non-zero mscale_all_dim, where mscale = 0.1 * mscale_all_dim * ln(s) + 1 for
+ * s > 1 ("CSDN walkthrough of HF DeepseekV3Attention", __init__, citing the
+ * YaRN paper's equations 21-22; "Megatron-LM MLA guide", softmax_scale =
+ * mscale * mscale / sqrt(q_head_dim)).  Returns cfg->softmax_scale when it is
+ * positive.  Host-only.  Returns 0 for an invalid configuration. */
+float mla_softmax_scale(const mla_config* cfg);
+
+/* RoPE table, host-only: cos_out/sin_out are caller-owned HOST arrays of
+ * max_pos * (d_rope/2) floats, row p = position p, column i = frequency i.
+ * Angles are p * theta_i evaluated in double and rounded once to float.
+ * Plain: theta_i = base^(-2i/d_rope).  YaRN ("Megatron-LM MLA guide",
+ * rotary_base, scaling factor, original_max_position_embeddings, beta_fast,
+ * beta_slow, mscale, mscale_all_dim): pairs turning more than beta_fast times
+ * over the original context keep theta_i, pairs turning fewer than beta_slow
+ * times use theta_i / s, linear ramp in the pair index between them; amplitude
+ * mscale(s, mscale) / mscale(s, mscale_all_dim).  Upload the arrays to device
+ * memory for the device calls.  MLA_ERR_INVALID_ARG for rope_kind NONE. */
+mla_status mla_rope_table(const mla_config* cfg, int32_t max_pos, float* cos_out, float* sin_out);
+
+/* Workspace (device bytes) needed by mla_prefill_fwd for num_tokens packed
+ * tokens in num_seqs documents. */
+size_t mla_prefill_workspace_size(const mla_config* cfg, int32_t num_tokens, int32_t num_seqs);
+
+/* Workspace (device bytes) needed by mla_decode_absorbed_fwd; seq_lens_host
+ * is a HOST array of batch lengths. */
+size_t mla_decode_workspace_size(const mla_config* cfg, const int32_t* seq_lens_host, int32_t batch);
+
+const char* mla_status_string(mla_status s);
+/* Message for the last failed call on this thread ("" if none). */
+const char* mla_last_error(void);
+
+/* -------------------------------------------------------------- device calls */
+
+/* Fused latent RMSNorm + RoPE (+ optional paged scatter) over token rows.
+ * Follows the latent path of "CSDN walkthrough of HF DeepseekV3Attention"
+ * (kv_a_layernorm on the compressed part, RoPE on the single k_pe head) and the
+ * fused rope-for-kv of "Megatron-LM MLA guide"; the same call applies RoPE in
+ * place to the H rope slices of q (rope_slices = H).
+ *   src  [n_rows, src_row_stride] (dtype), row r read from src + r*stride.
+ *   For each row, columns [0, row_width) are written to the destination row:
+ *     c <  norm_dim              : gamma[c] * x[c] / sqrt(mean(x[0:norm_dim]^2) + eps)
+ *     c in a rope slice          : rotate_half RoPE at positions[r] ("MiniMind"
+ *                                  section 3); slice s covers [rope_offset +
+ *                                  s*rope_slice_stride, + d_rope)
+ *     otherwise                  : copied.
+ *   norm_dim = 0 disables the norm; rope_slices = 0 (or rope_kind NONE)
+ *   disables RoPE.  rope_cos/rope_sin: DEVICE tables from mla_rope_table with
+ *   rope_table_len rows; positions: DEVICE [n_rows] (may be NULL without RoPE);
+ *   a position outside [0, rope_table_len) writes NaN into that row's slices.
+ *   Destination: slot_mapping NULL -> dst + r*dst_row_stride; else DEVICE
+ *   slot_mapping[r] gives the destination row (a paged-cache slot); rows with a
+ *   slot < 0 or >= num_slots are skipped.  src == dst (in place) is allowed
+ *   without a slot mapping. */
+mla_status mla_latent_norm_rope(const mla_config* cfg,
+                                const void* src, int64_t src_row_stride, int32_t n_rows,
+                                int32_t row_width, int32_t norm_dim, const void* gamma,
+                                int32_t rope_offset, int32_t rope_slices, int32_t rope_slice_stride,
+                                const float* rope_cos, const float* rope_sin, int32_t rope_table_len,
+                                const int32_t* positions,
+                                void* dst, int64_t dst_row_stride,
+                                const int32_t* slot_mapping, int64_t num_slots,
+                                void* stream);
+
+/* Linear layer y = x W^T (the nn.Linear projections of the layer).
+ *   x [m, k] with row stride ldx, w [n, k] (row stride k), y [m, n] with row
+ *   stride ldy; all DEVICE, dtype = cfg.dtype.  fp32 accumulation. */
+mla_status mla_linear(const mla_config* cfg, const void* x, int64_t ldx, const void* w,
+                      void* y, int64_t ldy, int32_t m, int32_t n, int32_t k, void* stream);
+
+/* Causal varlen attention core of the layer (MLA step "A" above) on
+ * already-projected tensors, all DEVICE, dtype = cfg.dtype:
+ *   q      [N, H, d_nope + d_rope]  per head [q_nope | q_pe] (q_pe rotated)
+ *   kv     [N, H, d_nope + d_v]     per head [k_nope | v]
+ *   latent [N, latent_stride] whose columns [r_kv, r_kv + d_rope) hold the
+ *          shared k_pe (rotated), broadcast to every head
+ *   cu_seqlens_dev / cu_seqlens_host: [num_seqs + 1] offsets (DEVICE / HOST,
+ *          same values), documents attend only within themselves, causally
+ *          ("Megatron-LM MLA guide", THD packing)
+ *   attn   [N, H, d_v] output.  d_v != d_nope + d_rope is handled natively (no
+ *          padding of v, unlike the FlashAttention adapters on the pages). */
+mla_status mla_attention_prefill(const mla_config* cfg, const void* q, const void* kv,
+                                 const void* latent, int64_t latent_stride,
+                                 const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                                 int32_t num_seqs, void* attn,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* The full MLA prefill layer on packed documents.
+ *   x [N, hidden] DEVICE; N = cu_seqlens_host[num_seqs].
+ *   positions_dev: DEVICE [N] RoPE positions, or NULL for 0..len-1 within each
+ *     document.
+ *   rope_cos/rope_sin: DEVICE tables (mla_rope_table) with rope_table_len rows,
+ *     NULL for rope_kind NONE.
+ *   out [N, hidden] DEVICE (the attention output before any residual).
+ *   latent_out: NULL, or DEVICE [N, r_kv + d_rope] receiving [c_n | k_pe'] per
+ *     token, the latent-cache row ("Megatron-LM MLA guide", inference section).
+ *   workspace: DEVICE, >= mla_prefill_workspace_size(cfg, N, num_seqs). */
+mla_status mla_prefill_fwd(const mla_config* cfg, const mla_weights* w, const void* x,
+                           const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                           int32_t num_seqs, const int32_t* positions_dev,
+                           const float* rope_cos, const float* rope_sin, int32_t rope_table_len,
+                           void* out, void* latent_out,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Weight-absorbed MLA decode over a paged latent cache ("Megatron-LM MLA
+ * guide", inference section: kv up-projection split per head into up_k and
+ * up_v; up_k folded into the no-position query, attention over the cached
+ * latents, up_v restoring d_v), bf16 only.
+ *   w_kv_b   [H*(d_nope+d_v), r_kv]  rows of head h = [W_UK (d_nope rows) | W_UV (d_v rows)]
+ *   q_nope   [B, H, d_nope], q_pe [B, H, d_rope] (already rotated)
+ *   kv_cache [num_blocks, block_size, r_kv + d_rope]: per token [c_n | k_pe']
+ *   block_table [B, max_blocks]: block ids; token j of sequence b lives in slot
+ *            block_table[b, j / block_size] * block_size + j % block_size
+ *   seq_lens_dev / seq_lens_host: [B] keys to attend, INCLUDING the current
+ *            token (already written to the cache by the caller)
+ *   out      [B, H, d_v]: attention output before the output projection.
+ *   A block id outside [0, num_blocks) makes that sequence's output NaN; cache
+ *   slots past seq_lens are never read.  block_size must be a multiple of 16.
+ *   workspace: DEVICE, >= mla_decode_workspace_size(cfg, seq_lens_host, B). */
+mla_status mla_decode_absorbed_fwd(const mla_config* cfg, const void* w_kv_b,
+                                   const void* q_nope, const void* q_pe,
+                                   const void* kv_cache, int32_t num_blocks, int32_t block_size,
+                                   const int32_t* block_table, int32_t max_blocks,
+                                   const int32_t* seq_lens_dev, const int32_t* seq_lens_host,
+                                   int32_t batch, void* out,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIBMLA_MLA_H */

@@ -1,0 +1,501 @@
+// libmla C ABI: argument checks, workspace carving, the RoPE / YaRN table
+// builder, and the launch sequences of the prefill layer and the absorbed
+// decode.  Host code; every device step runs in the kernels of this library.
+#include "mla_internal.hpp"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+#include <algorithm>
+
+using namespace mla;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mla_status fail(mla_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+mla_status ok() {
+  g_last_error.clear();
+  return MLA_OK;
+}
+
+mla_status hip_fail(hipError_t e, const char* what) {
+  return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_size(const mla_config* c) { return c->dtype == MLA_BF16 ? 2 : 4; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+mla_status check_config(const mla_config* c) {
+  if (!c) return fail(MLA_ERR_INVALID_ARG, "config is NULL");
+  if (c->hidden <= 0 || c->num_heads <= 0 || c->kv_lora_rank <= 0 || c->qk_nope_dim <= 0 ||
+      c->v_head_dim <= 0 || c->qk_rope_dim < 0 || c->q_lora_rank < 0)
+    return fail(MLA_ERR_INVALID_ARG, "dimensions must be positive (q_lora_rank, qk_rope_dim may be 0)");
+  if (c->qk_rope_dim % 2) return fail(MLA_ERR_INVALID_ARG, "qk_rope_dim must be even");
+  if (c->dtype != MLA_BF16 && c->dtype != MLA_F32) return fail(MLA_ERR_INVALID_ARG, "unknown dtype %d", c->dtype);
+  if (c->rope_kind < MLA_ROPE_NONE || c->rope_kind > MLA_ROPE_YARN)
+    return fail(MLA_ERR_INVALID_ARG, "unknown rope_kind %d", c->rope_kind);
+  if (c->rope_kind != MLA_ROPE_NONE) {
+    if (c->qk_rope_dim <= 0) return fail(MLA_ERR_INVALID_ARG, "rope needs qk_rope_dim > 0");
+    if (!(c->rope_theta > 0.0)) return fail(MLA_ERR_INVALID_ARG, "rope_theta must be > 0");
+  }
+  if (c->rope_kind == MLA_ROPE_YARN) {
+    if (!(c->yarn_factor > 0.0) || c->yarn_original_max_pos <= 0 || !(c->yarn_beta_fast > 0.0) ||
+        !(c->yarn_beta_slow > 0.0) || !(c->yarn_beta_fast >= c->yarn_beta_slow))
+      return fail(MLA_ERR_INVALID_ARG, "YaRN needs factor > 0, original_max_pos > 0, beta_fast >= beta_slow > 0");
+  }
+  if (!(c->norm_eps >= 0.f) || !std::isfinite(c->norm_eps)) return fail(MLA_ERR_INVALID_ARG, "norm_eps must be finite and >= 0");
+  if (!std::isfinite(c->softmax_scale)) return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite");
+  if (c->output_gate != 0 && c->output_gate != 1) return fail(MLA_ERR_INVALID_ARG, "output_gate must be 0 or 1");
+  return MLA_OK;
+}
+
+// Shapes the compiled kernels cover.
+mla_status check_supported(const mla_config* c) {
+  if (c->dtype == MLA_BF16) {
+    if (c->qk_nope_dim != 128 || c->qk_rope_dim != 64 || c->v_head_dim != 128 || c->kv_lora_rank != 512)
+      return fail(MLA_ERR_UNSUPPORTED, "bf16 kernels need d_nope=128, d_rope=64, d_v=128, r_kv=512");
+    if (c->hidden % 8 || c->q_lora_rank % 8)
+      return fail(MLA_ERR_UNSUPPORTED, "bf16 kernels need hidden and q_lora_rank multiples of 8");
+  } else {
+    if (c->qk_nope_dim + c->qk_rope_dim > 512 || c->v_head_dim > 256 || c->qk_rope_dim > 128 || c->kv_lora_rank > 1024)
+      return fail(MLA_ERR_UNSUPPORTED, "fp32 kernels need d_nope+d_rope <= 512, d_v <= 256, d_rope <= 128, r_kv <= 1024");
+  }
+  return MLA_OK;
+}
+
+double yarn_mscale(double s, double m) { return s <= 1.0 ? 1.0 : 0.1 * m * std::log(s) + 1.0; }
+
+double derived_scale(const mla_config* c) {
+  double s = std::pow((double)(c->qk_nope_dim + c->qk_rope_dim), -0.5);
+  if (c->rope_kind == MLA_ROPE_YARN && c->yarn_mscale_all_dim != 0.0) {
+    const double m = yarn_mscale(c->yarn_factor, c->yarn_mscale_all_dim);
+    s = s * m * m;
+  }
+  return s;
+}
+
+float scale_of(const mla_config* c) { return c->softmax_scale > 0.f ? c->softmax_scale : (float)derived_scale(c); }
+
+// Rotation frequency of each pair; YaRN blends theta_i and theta_i / s over the
+// pair index between the pairs that turn beta_fast and beta_slow times over the
+// original context.
+std::vector<double> rope_frequencies(const mla_config* c) {
+  const int d = c->qk_rope_dim, half = d / 2;
+  std::vector<double> f(half);
+  for (int i = 0; i < half; ++i) f[i] = std::pow(c->rope_theta, -2.0 * (double)i / (double)d);
+  if (c->rope_kind != MLA_ROPE_YARN) return f;
+  const double L = (double)c->yarn_original_max_pos, base = c->rope_theta, s = c->yarn_factor;
+  auto turns_to_index = [&](double turns) {
+    return (double)d * std::log(L / (turns * 2.0 * M_PI)) / (2.0 * std::log(base));
+  };
+  double lo = std::max(std::floor(turns_to_index(c->yarn_beta_fast)), 0.0);
+  double hi = std::min(std::ceil(turns_to_index(c->yarn_beta_slow)), (double)(d - 1));
+  if (lo == hi) hi += 0.001;
+  for (int i = 0; i < half; ++i) {
+    double r = ((double)i - lo) / (hi - lo);
+    r = std::min(std::max(r, 0.0), 1.0);
+    f[i] = f[i] * (1.0 - r) + (f[i] / s) * r;
+  }
+  return f;
+}
+
+// ---------------------------------------------------------------- prefill workspace
+struct PrefillWs {
+  size_t pos, q_lat, q, ckv, latent, kv, attn, total;
+};
+
+PrefillWs prefill_layout(const mla_config* c, int64_t n) {
+  const size_t es = elem_size(c);
+  const int64_t H = c->num_heads, dqk = c->qk_nope_dim + c->qk_rope_dim;
+  const int64_t lw = c->kv_lora_rank + c->qk_rope_dim;
+  PrefillWs w;
+  size_t off = 0;
+  w.pos = off; off += align256(n * 4);
+  w.q_lat = off; off += align256(n * c->q_lora_rank * es);
+  w.q = off; off += align256(n * H * dqk * es);
+  w.ckv = off; off += align256(n * lw * es);
+  w.latent = off; off += align256(n * lw * es);
+  w.kv = off; off += align256(n * H * (c->qk_nope_dim + c->v_head_dim) * es);
+  w.attn = off; off += align256(n * H * c->v_head_dim * es);
+  w.total = off;
+  return w;
+}
+
+mla_status check_cu(const int32_t* cu_host, int num_seqs, int* n_out) {
+  if (!cu_host) return fail(MLA_ERR_INVALID_ARG, "cu_seqlens_host is NULL");
+  if (num_seqs <= 0) return fail(MLA_ERR_INVALID_ARG, "num_seqs must be > 0");
+  if (cu_host[0] != 0) return fail(MLA_ERR_INVALID_ARG, "cu_seqlens[0] must be 0");
+  for (int i = 0; i < num_seqs; ++i)
+    if (cu_host[i + 1] < cu_host[i]) return fail(MLA_ERR_INVALID_ARG, "cu_seqlens must be non-decreasing");
+  if (num_seqs >= 65536) return fail(MLA_ERR_UNSUPPORTED, "at most 65535 documents per call");
+  for (int i = 0; i < num_seqs; ++i)
+    if (cu_host[i + 1] - cu_host[i] >= 65536 * 128) return fail(MLA_ERR_UNSUPPORTED, "documents are limited to 8388607 tokens");
+  *n_out = cu_host[num_seqs];
+  return MLA_OK;
+}
+
+// ---------------------------------------------------------------- decode plan
+constexpr int kDecodeTargetGroups = 256;   // one wave of workgroups on 256 CUs
+
+struct DecodePlan {
+  int chunk, max_chunks;
+  size_t qt, olat, part_o, part_ml, total;
+};
+
+DecodePlan decode_plan(const mla_config* c, const int32_t* lens, int batch, int64_t key_cap) {
+  DecodePlan p{};
+  int64_t total = 0, maxl = 1;
+  for (int b = 0; b < batch; ++b) {
+    const int64_t L = std::min<int64_t>(std::max(lens[b], 0), key_cap);
+    total += L;
+    maxl = std::max(maxl, L);
+  }
+  int chunk = 32 * (int)std::max<int64_t>(1, (total + 32LL * kDecodeTargetGroups - 1) / (32LL * kDecodeTargetGroups));
+  for (;;) {
+    int64_t groups = 0;
+    for (int b = 0; b < batch; ++b) {
+      const int64_t L = std::min<int64_t>(std::max(lens[b], 0), key_cap);
+      groups += (L + chunk - 1) / chunk;
+    }
+    if (groups <= kDecodeTargetGroups || chunk >= maxl) break;
+    chunk += 32;
+  }
+  p.chunk = chunk;
+  p.max_chunks = (int)((maxl + chunk - 1) / chunk);
+  const int64_t H = c->num_heads, R = c->kv_lora_rank;
+  size_t off = 0;
+  p.qt = off; off += align256((size_t)batch * H * R * 2);
+  p.olat = off; off += align256((size_t)batch * H * R * 2);
+  p.part_o = off; off += align256((size_t)batch * p.max_chunks * H * R * 4);
+  p.part_ml = off; off += align256((size_t)batch * p.max_chunks * H * 2 * 4);
+  p.total = off;
+  return p;
+}
+
+}  // namespace
+
+// ============================================================================ C ABI
+extern "C" {
+
+int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+const char* mla_status_string(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE";
+    case MLA_ERR_MISALIGNED: return "MLA_ERR_MISALIGNED";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+  }
+  return "MLA_ERR_UNKNOWN";
+}
+
+const char* mla_last_error(void) { return g_last_error.c_str(); }
+
+mla_status mla_validate_config(const mla_config* cfg) {
+  const mla_status s = check_config(cfg);
+  return s == MLA_OK ? ok() : s;
+}
+
+float mla_softmax_scale(const mla_config* cfg) {
+  if (check_config(cfg) != MLA_OK) return 0.f;
+  return scale_of(cfg);
+}
+
+mla_status mla_rope_table(const mla_config* cfg, int32_t max_pos, float* cos_out, float* sin_out) {
+  mla_status s = check_config(cfg);
+  if (s != MLA_OK) return s;
+  if (cfg->rope_kind == MLA_ROPE_NONE) return fail(MLA_ERR_INVALID_ARG, "rope_kind NONE has no table");
+  if (max_pos <= 0 || !cos_out || !sin_out) return fail(MLA_ERR_INVALID_ARG, "max_pos > 0 and host outputs required");
+  const std::vector<double> f = rope_frequencies(cfg);
+  double amp = 1.0;
+  if (cfg->rope_kind == MLA_ROPE_YARN)
+    amp = yarn_mscale(cfg->yarn_factor, cfg->yarn_mscale) / yarn_mscale(cfg->yarn_factor, cfg->yarn_mscale_all_dim);
+  const int half = cfg->qk_rope_dim / 2;
+  for (int64_t p = 0; p < max_pos; ++p)
+    for (int i = 0; i < half; ++i) {
+      const double ang = (double)p * f[i];
+      cos_out[p * half + i] = (float)(std::cos(ang) * amp);
+      sin_out[p * half + i] = (float)(std::sin(ang) * amp);
+    }
+  return ok();
+}
+
+size_t mla_prefill_workspace_size(const mla_config* cfg, int32_t num_tokens, int32_t num_seqs) {
+  (void)num_seqs;
+  if (check_config(cfg) != MLA_OK || num_tokens < 0) return 0;
+  return prefill_layout(cfg, num_tokens).total;
+}
+
+size_t mla_decode_workspace_size(const mla_config* cfg, const int32_t* seq_lens_host, int32_t batch) {
+  if (check_config(cfg) != MLA_OK || !seq_lens_host || batch <= 0) return 0;
+  return decode_plan(cfg, seq_lens_host, batch, INT32_MAX).total;
+}
+
+mla_status mla_latent_norm_rope(const mla_config* cfg, const void* src, int64_t src_row_stride, int32_t n_rows,
+                                int32_t row_width, int32_t norm_dim, const void* gamma, int32_t rope_offset,
+                                int32_t rope_slices, int32_t rope_slice_stride, const float* rope_cos,
+                                const float* rope_sin, int32_t rope_table_len, const int32_t* positions, void* dst,
+                                int64_t dst_row_stride, const int32_t* slot_mapping, int64_t num_slots,
+                                void* stream) {
+  mla_status s = check_config(cfg);
+  if (s != MLA_OK) return s;
+  if (n_rows < 0 || row_width < 0) return fail(MLA_ERR_INVALID_ARG, "n_rows and row_width must be >= 0");
+  if (n_rows == 0) return ok();
+  if (!src || !dst) return fail(MLA_ERR_INVALID_ARG, "src and dst are required");
+  if (src_row_stride < row_width || (!slot_mapping && dst_row_stride < row_width) || dst_row_stride < row_width)
+    return fail(MLA_ERR_INVALID_ARG, "row strides must be >= row_width");
+  if (norm_dim < 0 || norm_dim > row_width) return fail(MLA_ERR_INVALID_ARG, "norm_dim must be in [0, row_width]");
+  if (norm_dim > 0 && !gamma) return fail(MLA_ERR_INVALID_ARG, "gamma is required when norm_dim > 0");
+  const bool rope = rope_slices > 0 && cfg->rope_kind != MLA_ROPE_NONE;
+  if (rope_slices < 0) return fail(MLA_ERR_INVALID_ARG, "rope_slices must be >= 0");
+  if (rope) {
+    const int d = cfg->qk_rope_dim;
+    if (!rope_cos || !rope_sin || !positions || rope_table_len <= 0)
+      return fail(MLA_ERR_INVALID_ARG, "RoPE needs device cos/sin tables, their length and positions");
+    if (rope_offset < norm_dim) return fail(MLA_ERR_INVALID_ARG, "rope slices must not overlap the normalised columns");
+    if (rope_slices > 1 && rope_slice_stride < d) return fail(MLA_ERR_INVALID_ARG, "rope_slice_stride must be >= d_rope");
+    const int64_t last = (int64_t)rope_offset + (int64_t)(rope_slices - 1) * std::max(rope_slice_stride, d) + d;
+    if (last > row_width) return fail(MLA_ERR_INVALID_ARG, "rope slices exceed row_width");
+  }
+  if (slot_mapping && num_slots <= 0) return fail(MLA_ERR_INVALID_ARG, "num_slots must be > 0 with a slot mapping");
+  if (slot_mapping && src == dst) return fail(MLA_ERR_INVALID_ARG, "in-place update cannot use a slot mapping");
+  NormRopeArgs a{};
+  a.src = src; a.src_stride = src_row_stride; a.n_rows = n_rows; a.row_width = row_width;
+  a.norm_dim = norm_dim; a.gamma = gamma; a.eps = cfg->norm_eps;
+  a.rope_offset = rope_offset; a.rope_slices = rope ? rope_slices : 0;
+  a.rope_stride = std::max(rope_slice_stride, cfg->qk_rope_dim); a.rope_dim = cfg->qk_rope_dim;
+  a.cos_t = rope_cos; a.sin_t = rope_sin; a.table_len = rope_table_len; a.positions = positions;
+  a.dst = dst; a.dst_stride = dst_row_stride; a.slots = slot_mapping; a.num_slots = num_slots;
+  const hipError_t e = launch_norm_rope(a, cfg->dtype == MLA_BF16, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "latent_norm_rope launch");
+  return ok();
+}
+
+static mla_status linear_impl(const mla_config* cfg, const void* x, int64_t ldx, const void* w, void* y, int64_t ldy,
+                              int m, int n, int k, const void* gate_src, int64_t ldg, hipStream_t st) {
+  GemmArgs g{};
+  g.a = x; g.lda = ldx; g.b = w; g.ldb = k; g.c = y; g.ldc = ldy;
+  g.gate_src = gate_src; g.ldg = ldg; g.m = m; g.n = n; g.k = k; g.batch = 1;
+  g.b_kn = false; g.epilogue = gate_src ? EPI_GATE : EPI_STORE;
+  const hipError_t e = cfg->dtype == MLA_BF16 ? launch_gemm_bf16(g, st) : launch_gemm_f32(g, st);
+  if (e != hipSuccess) return hip_fail(e, "linear launch");
+  return MLA_OK;
+}
+
+mla_status mla_linear(const mla_config* cfg, const void* x, int64_t ldx, const void* w, void* y, int64_t ldy,
+                      int32_t m, int32_t n, int32_t k, void* stream) {
+  mla_status s = check_config(cfg);
+  if (s != MLA_OK) return s;
+  if (m < 0 || n <= 0 || k <= 0) return fail(MLA_ERR_INVALID_ARG, "linear needs m >= 0, n > 0, k > 0");
+  if (m == 0) return ok();
+  if (!x || !w || !y) return fail(MLA_ERR_INVALID_ARG, "x, w and y are required");
+  if (ldx < k || ldy < n) return fail(MLA_ERR_INVALID_ARG, "ldx >= k and ldy >= n required");
+  if (cfg->dtype == MLA_BF16) {
+    if (!aligned16(x) || !aligned16(w) || !aligned16(y) || ldx % 8 || ldy % 8 || k % 8 || n % 8)
+      return fail(MLA_ERR_MISALIGNED, "bf16 linear needs 16-byte aligned pointers and k, n, ldx, ldy multiples of 8");
+  }
+  s = linear_impl(cfg, x, ldx, w, y, ldy, m, n, k, nullptr, 0, (hipStream_t)stream);
+  return s == MLA_OK ? ok() : s;
+}
+
+static mla_status attention_impl(const mla_config* cfg, const void* q, const void* kv, const void* latent,
+                                 int64_t latent_stride, const int32_t* cu_dev, const int32_t* cu_host, int num_seqs,
+                                 int n, void* attn, hipStream_t st) {
+  FlashArgs f{};
+  f.q = q; f.kv = kv; f.latent = latent; f.latent_stride = latent_stride; f.cu_dev = cu_dev; f.out = attn;
+  f.n_tokens = n; f.heads = cfg->num_heads; f.nope = cfg->qk_nope_dim; f.rope = cfg->qk_rope_dim;
+  f.dv = cfg->v_head_dim; f.kv_lora = cfg->kv_lora_rank; f.scale = scale_of(cfg); f.num_seqs = num_seqs;
+  const hipError_t e = cfg->dtype == MLA_BF16 ? launch_flash_bf16(f, cu_host, num_seqs, st) : launch_flash_f32(f, st);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return MLA_OK;
+}
+
+mla_status mla_attention_prefill(const mla_config* cfg, const void* q, const void* kv, const void* latent,
+                                 int64_t latent_stride, const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                                 int32_t num_seqs, void* attn, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace; (void)workspace_bytes;
+  mla_status s = check_config(cfg);
+  if (s != MLA_OK) return s;
+  if ((s = check_supported(cfg)) != MLA_OK) return s;
+  int n = 0;
+  if ((s = check_cu(cu_seqlens_host, num_seqs, &n)) != MLA_OK) return s;
+  if (n == 0) return ok();
+  if (!q || !kv || !latent || !cu_seqlens_dev || !attn) return fail(MLA_ERR_INVALID_ARG, "q, kv, latent, cu_seqlens_dev and attn are required");
+  if (latent_stride < cfg->kv_lora_rank + cfg->qk_rope_dim) return fail(MLA_ERR_INVALID_ARG, "latent_stride too small");
+  if (cfg->dtype == MLA_BF16 && (!aligned16(q) || !aligned16(kv) || !aligned16(latent) || !aligned16(attn) || latent_stride % 8))
+    return fail(MLA_ERR_MISALIGNED, "bf16 attention needs 16-byte aligned tensors and latent_stride % 8 == 0");
+  s = attention_impl(cfg, q, kv, latent, latent_stride, cu_seqlens_dev, cu_seqlens_host, num_seqs, n, attn, (hipStream_t)stream);
+  return s == MLA_OK ? ok() : s;
+}
+
+mla_status mla_prefill_fwd(const mla_config* cfg, const mla_weights* w, const void* x, const int32_t* cu_seqlens_dev,
+                           const int32_t* cu_seqlens_host, int32_t num_seqs, const int32_t* positions_dev,
+                           const float* rope_cos, const float* rope_sin, int32_t rope_table_len, void* out,
+                           void* latent_out, void* workspace, size_t workspace_bytes, void* stream) {
+  mla_status s = check_config(cfg);
+  if (s != MLA_OK) return s;
+  if ((s = check_supported(cfg)) != MLA_OK) return s;
+  if (!w) return fail(MLA_ERR_INVALID_ARG, "weights are NULL");
+  int n = 0;
+  if ((s = check_cu(cu_seqlens_host, num_seqs, &n)) != MLA_OK) return s;
+  if (n == 0) return ok();
+  if (!x || !out || !cu_seqlens_dev) return fail(MLA_ERR_INVALID_ARG, "x, out and cu_seqlens_dev are required");
+  if (cfg->q_lora_rank > 0 && (!w->w_q_a || !w->q_a_gamma || !w->w_q_b))
+    return fail(MLA_ERR_INVALID_ARG, "q_lora_rank > 0 needs w_q_a, q_a_gamma, w_q_b");
+  if (cfg->q_lora_rank == 0 && !w->w_q) return fail(MLA_ERR_INVALID_ARG, "q_lora_rank == 0 needs w_q");
+  if (!w->w_kv_a || !w->kv_a_gamma || !w->w_kv_b || !w->w_o) return fail(MLA_ERR_INVALID_ARG, "w_kv_a, kv_a_gamma, w_kv_b, w_o are required");
+  if (cfg->output_gate && !w->w_g) return fail(MLA_ERR_INVALID_ARG, "output_gate needs w_g");
+  const bool rope = cfg->rope_kind != MLA_ROPE_NONE;
+  if (rope && (!rope_cos || !rope_sin || rope_table_len <= 0))
+    return fail(MLA_ERR_INVALID_ARG, "RoPE needs device cos/sin tables and their length");
+  const PrefillWs L = prefill_layout(cfg, n);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, workspace_bytes);
+  if (cfg->dtype == MLA_BF16) {
+    const void* ptrs[] = {x, out, w->w_kv_a, w->kv_a_gamma, w->w_kv_b, w->w_o, workspace};
+    for (const void* p : ptrs)
+      if (!aligned16(p)) return fail(MLA_ERR_MISALIGNED, "bf16 prefill needs 16-byte aligned tensors");
+    if ((latent_out && !aligned16(latent_out)) || (w->w_q && !aligned16(w->w_q)) || (w->w_q_a && !aligned16(w->w_q_a)) ||
+        (w->w_q_b && !aligned16(w->w_q_b)) || (w->w_g && !aligned16(w->w_g)))
+      return fail(MLA_ERR_MISALIGNED, "bf16 prefill needs 16-byte aligned tensors");
+  }
+  const hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const size_t es = elem_size(cfg);
+  (void)es;
+  const int H = cfg->num_heads, hid = cfg->hidden, rq = cfg->q_lora_rank, rkv = cfg->kv_lora_rank;
+  const int dn = cfg->qk_nope_dim, dr = cfg->qk_rope_dim, dv = cfg->v_head_dim, dqk = dn + dr, lw = rkv + dr;
+  int32_t* pos = (int32_t*)(ws + L.pos);
+  void* q_lat = ws + L.q_lat;
+  void* q = ws + L.q;
+  void* ckv = ws + L.ckv;
+  void* lat = latent_out ? latent_out : (void*)(ws + L.latent);
+  void* kv = ws + L.kv;
+  void* attn = ws + L.attn;
+  hipError_t e;
+
+  // positions (0..len-1 per document) unless the caller gives them
+  const int32_t* positions = positions_dev;
+  if (rope && !positions) {
+    if ((e = launch_positions(cu_seqlens_dev, num_seqs, n, pos, st)) != hipSuccess) return hip_fail(e, "positions");
+    positions = pos;
+  }
+  // query path
+  if (rq > 0) {
+    if ((s = linear_impl(cfg, x, hid, w->w_q_a, q_lat, rq, n, rq, hid, nullptr, 0, st)) != MLA_OK) return s;
+    NormRopeArgs a{};
+    a.src = q_lat; a.src_stride = rq; a.n_rows = n; a.row_width = rq; a.norm_dim = rq; a.gamma = w->q_a_gamma;
+    a.eps = cfg->norm_eps; a.rope_stride = 1; a.dst = q_lat; a.dst_stride = rq;
+    if ((e = launch_norm_rope(a, cfg->dtype == MLA_BF16, st)) != hipSuccess) return hip_fail(e, "q latent norm");
+    if ((s = linear_impl(cfg, q_lat, rq, w->w_q_b, q, (int64_t)H * dqk, n, H * dqk, rq, nullptr, 0, st)) != MLA_OK) return s;
+  } else {
+    if ((s = linear_impl(cfg, x, hid, w->w_q, q, (int64_t)H * dqk, n, H * dqk, hid, nullptr, 0, st)) != MLA_OK) return s;
+  }
+  if (rope) {   // RoPE on the H rope slices of q, in place
+    NormRopeArgs a{};
+    a.src = q; a.src_stride = (int64_t)H * dqk; a.n_rows = n; a.row_width = H * dqk; a.norm_dim = 0;
+    a.rope_offset = dn; a.rope_slices = H; a.rope_stride = dqk; a.rope_dim = dr;
+    a.cos_t = rope_cos; a.sin_t = rope_sin; a.table_len = rope_table_len; a.positions = positions;
+    a.dst = q; a.dst_stride = (int64_t)H * dqk;
+    if ((e = launch_norm_rope(a, cfg->dtype == MLA_BF16, st)) != hipSuccess) return hip_fail(e, "q rope");
+  }
+  // joint latent: down-projection, latent norm + k_pe RoPE -> [c_n | k_pe']
+  if ((s = linear_impl(cfg, x, hid, w->w_kv_a, ckv, lw, n, lw, hid, nullptr, 0, st)) != MLA_OK) return s;
+  {
+    NormRopeArgs a{};
+    a.src = ckv; a.src_stride = lw; a.n_rows = n; a.row_width = lw; a.norm_dim = rkv; a.gamma = w->kv_a_gamma;
+    a.eps = cfg->norm_eps; a.rope_offset = rkv; a.rope_slices = rope ? 1 : 0; a.rope_stride = dr; a.rope_dim = dr;
+    a.cos_t = rope_cos; a.sin_t = rope_sin; a.table_len = rope_table_len; a.positions = positions;
+    a.dst = lat; a.dst_stride = lw;
+    if ((e = launch_norm_rope(a, cfg->dtype == MLA_BF16, st)) != hipSuccess) return hip_fail(e, "kv latent norm rope");
+  }
+  // per-head keys/values from the normalised latent
+  if ((s = linear_impl(cfg, lat, lw, w->w_kv_b, kv, (int64_t)H * (dn + dv), n, H * (dn + dv), rkv, nullptr, 0, st)) != MLA_OK) return s;
+  // attention
+  if ((s = attention_impl(cfg, q, kv, lat, lw, cu_seqlens_dev, cu_seqlens_host, num_seqs, n, attn, st)) != MLA_OK) return s;
+  // optional gate, output projection
+  if (cfg->output_gate) {
+    if ((s = linear_impl(cfg, x, hid, w->w_g, attn, (int64_t)H * dv, n, H * dv, hid, attn, (int64_t)H * dv, st)) != MLA_OK) return s;
+  }
+  if ((s = linear_impl(cfg, attn, (int64_t)H * dv, w->w_o, out, hid, n, hid, H * dv, nullptr, 0, st)) != MLA_OK) return s;
+  return ok();
+}
+
+mla_status mla_decode_absorbed_fwd(const mla_config* cfg, const void* w_kv_b, const void* q_nope, const void* q_pe,
+                                   const void* kv_cache, int32_t num_blocks, int32_t block_size,
+                                   const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens_dev,
+                                   const int32_t* seq_lens_host, int32_t batch, void* out, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  mla_status s = check_config(cfg);
+  if (s != MLA_OK) return s;
+  if (cfg->dtype != MLA_BF16) return fail(MLA_ERR_UNSUPPORTED, "absorbed decode is compiled for bf16 only");
+  if ((s = check_supported(cfg)) != MLA_OK) return s;
+  const int H = cfg->num_heads;
+  if (H != 32 && H != 64 && H != 96 && H != 128) return fail(MLA_ERR_UNSUPPORTED, "decode supports 32, 64, 96 or 128 heads");
+  if (batch <= 0) return fail(MLA_ERR_INVALID_ARG, "batch must be > 0");
+  if (!w_kv_b || !q_nope || !q_pe || !kv_cache || !block_table || !seq_lens_dev || !seq_lens_host || !out)
+    return fail(MLA_ERR_INVALID_ARG, "all tensors are required");
+  if (num_blocks <= 0 || max_blocks <= 0) return fail(MLA_ERR_INVALID_ARG, "num_blocks and max_blocks must be > 0");
+  if (block_size <= 0 || block_size % 16) return fail(MLA_ERR_INVALID_ARG, "block_size must be a positive multiple of 16");
+  for (int b = 0; b < batch; ++b)
+    if (seq_lens_host[b] <= 0 || (int64_t)seq_lens_host[b] > (int64_t)max_blocks * block_size)
+      return fail(MLA_ERR_INVALID_ARG, "seq_lens[%d] = %d outside [1, max_blocks * block_size]", b, seq_lens_host[b]);
+  const void* ptrs[] = {w_kv_b, q_nope, q_pe, kv_cache, out, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(MLA_ERR_MISALIGNED, "decode needs 16-byte aligned tensors");
+  const DecodePlan P = decode_plan(cfg, seq_lens_host, batch, (int64_t)max_blocks * block_size);
+  if (!workspace || workspace_bytes < P.total)
+    return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", P.total, workspace_bytes);
+  const hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int dn = cfg->qk_nope_dim, dv = cfg->v_head_dim, R = cfg->kv_lora_rank;
+  bf16* qt = (bf16*)(ws + P.qt);
+  bf16* olat = (bf16*)(ws + P.olat);
+  hipError_t e;
+  // absorb W_UK into the query: qt[b, h, :] = q_nope[b, h, :] . W_kv_b[h*(dn+dv) + 0:dn, :]
+  {
+    GemmArgs g{};
+    g.a = q_nope; g.lda = (int64_t)H * dn; g.a_bstride = dn;
+    g.b = w_kv_b; g.ldb = R; g.b_bstride = (int64_t)(dn + dv) * R; g.b_kn = true;
+    g.c = qt; g.ldc = (int64_t)H * R; g.c_bstride = R;
+    g.m = batch; g.n = R; g.k = dn; g.batch = H; g.epilogue = EPI_STORE;
+    if ((e = launch_gemm_bf16(g, st)) != hipSuccess) return hip_fail(e, "absorb q");
+  }
+  DecodeArgs d{};
+  d.qt = qt; d.q_pe = (const bf16*)q_pe; d.cache = (const bf16*)kv_cache; d.block_table = block_table;
+  d.max_blocks = max_blocks; d.num_blocks = num_blocks; d.block_size = block_size; d.seq_lens = seq_lens_dev;
+  d.part_o = (float*)(ws + P.part_o); d.part_ml = (float*)(ws + P.part_ml); d.o_lat = olat;
+  d.batch = batch; d.heads = H; d.chunk = P.chunk; d.max_chunks = P.max_chunks; d.scale = scale_of(cfg);
+  if ((e = launch_decode_split(d, st)) != hipSuccess) return hip_fail(e, "decode split");
+  if ((e = launch_decode_combine(d, st)) != hipSuccess) return hip_fail(e, "decode combine");
+  // un-absorb W_UV: out[b, h, :] = W_kv_b[h*(dn+dv) + dn : +dv, :] . o_lat[b, h, :]
+  {
+    GemmArgs g{};
+    g.a = olat; g.lda = (int64_t)H * R; g.a_bstride = R;
+    g.b = (const bf16*)w_kv_b + (int64_t)dn * R; g.ldb = R; g.b_bstride = (int64_t)(dn + dv) * R; g.b_kn = false;
+    g.c = out; g.ldc = (int64_t)H * dv; g.c_bstride = dv;
+    g.m = batch; g.n = dv; g.k = R; g.batch = H; g.epilogue = EPI_STORE;
+    if ((e = launch_gemm_bf16(g, st)) != hipSuccess) return hip_fail(e, "un-absorb");
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,230 @@
+// Projection GEMMs of the MLA layer: y = x W^T (nn.Linear layout), and the
+// batched per-head products of the absorbed decode.
+//
+// bf16 kernel: 128x128 output tile per 256-thread workgroup, K step 64, fp32
+// accumulation on v_mfma_f32_32x32x16_bf16.  Operand tiles are staged through
+// LDS with double buffering; global->register prefetch of tile k+1 overlaps
+// the MFMAs of tile k.  Each wave owns a 64x64 quadrant (2x2 MFMA tiles).
+//
+// The MFMA "A" operand is taken from the weight tile and the "B" operand from
+// the activation tile, so each lane ends up holding 4 consecutive output
+// columns of one row and stores them with one 8-byte write.
+#include "mla_internal.hpp"
+
+namespace mla {
+namespace {
+
+constexpr int BM = 128, BN = 128, BK = 64, NT = 256;
+
+// K-contiguous tile [rows][64]: 8 chunks of 16 B per row, chunk c of row r is
+// stored at chunk c ^ (r & 7) so that 8 consecutive rows read at the same
+// logical chunk hit 8 different 16 B bank groups.
+__device__ __forceinline__ int kmaj(int r, int c) { return r * BK + ((c ^ (r & 7)) << 3); }
+// N-contiguous tile [64 k][128 n] for the transposed (NN) operand: 16 chunks per
+// row, chunk c of row k stored at c ^ ((k & 3) << 1).  A transpose read touches
+// 4 consecutive k rows x 32 B; the swizzle spreads them over 128 B.
+__device__ __forceinline__ int nmaj(int k, int n) { return k * BN + ((((n >> 3) ^ ((k & 3) << 1))) << 3) + (n & 7); }
+
+__device__ __forceinline__ bf16x8 zero8() { return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0)); }
+
+__device__ __forceinline__ int2 tile_coords(int pid, int num_m, int num_n) {
+  // Spread consecutive tiles of one band across the workgroups that share an
+  // XCD (workgroup ids are dealt to the 8 XCDs round-robin), then walk bands of
+  // 8 m-tiles so that a band's activation rows and weight columns stay in L2.
+  const int total = num_m * num_n;
+  if ((total & 7) == 0) pid = (pid & 7) * (total >> 3) + (pid >> 3);
+  const int group = 8 * num_n;
+  const int first_m = (pid / group) * 8;
+  const int gsize = min(num_m - first_m, 8);
+  const int in_group = pid % group;
+  return make_int2(first_m + in_group % gsize, in_group / gsize);
+}
+
+template <bool B_KN, int EPI>
+__global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) bf16 sA[2][BM * BK];
+  __shared__ __attribute__((aligned(16))) bf16 sB[2][BN * BK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int num_m = (g.m + BM - 1) / BM, num_n = (g.n + BN - 1) / BN;
+  const int2 tc = tile_coords(blockIdx.x, num_m, num_n);
+  const int m0 = tc.x * BM, n0 = tc.y * BN;
+  const bf16* A = (const bf16*)g.a + (int64_t)blockIdx.z * g.a_bstride;
+  const bf16* B = (const bf16*)g.b + (int64_t)blockIdx.z * g.b_bstride;
+  bf16* C = (bf16*)g.c + (int64_t)blockIdx.z * g.c_bstride;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nk = (g.k + BK - 1) / BK;
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  bf16x8 ra[4], rb[4];
+  auto gload = [&](int kt) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int id = tid + i * NT;
+      const int r = id >> 3, c = id & 7;
+      const int gm = m0 + r, gk = k0 + c * 8;
+      ra[i] = (gm < g.m && gk < g.k) ? *(const bf16x8*)(A + (int64_t)gm * g.lda + gk) : zero8();
+      if (!B_KN) {
+        const int gn = n0 + r;
+        rb[i] = (gn < g.n && gk < g.k) ? *(const bf16x8*)(B + (int64_t)gn * g.ldb + gk) : zero8();
+      } else {
+        const int rk = id >> 4, cn = id & 15;
+        const int gk2 = k0 + rk, gn = n0 + cn * 8;
+        rb[i] = (gk2 < g.k && gn < g.n) ? *(const bf16x8*)(B + (int64_t)gk2 * g.ldb + gn) : zero8();
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int id = tid + i * NT;
+      const int r = id >> 3, c = id & 7;
+      *(bf16x8*)&sA[buf][kmaj(r, c)] = ra[i];
+      if (!B_KN) {
+        *(bf16x8*)&sB[buf][kmaj(r, c)] = rb[i];
+      } else {
+        const int rk = id >> 4, cn = id & 15;
+        *(bf16x8*)&sB[buf][nmaj(rk, cn * 8)] = rb[i];
+      }
+    }
+  };
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8 xa[2], wb[2];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        const int r = wm * 64 + mi * 32 + (lane & 31);
+        xa[mi] = *(const bf16x8*)&sA[buf][kmaj(r, ks * 2 + (lane >> 5))];
+      }
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        const int rn = wn * 64 + ni * 32;
+        if (!B_KN) {
+          wb[ni] = *(const bf16x8*)&sB[buf][kmaj(rn + (lane & 31), ks * 2 + (lane >> 5))];
+        } else {
+          const int L = lane & 15, grp = lane >> 4;
+          const int nb = rn + (grp & 1) * 16 + 4 * (L & 3);
+          const int kr = ks * 16 + (grp >> 1) * 8 + (L >> 2);
+          const bf16x4 lo = lds_read_tr(&sB[buf][nmaj(kr, nb)]);
+          const bf16x4 hi = lds_read_tr(&sB[buf][nmaj(kr + 4, nb)]);
+          wb[ni] = cat8(lo, hi);
+        }
+      }
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) acc[ni][mi] = mfma32(wb[ni], xa[mi], acc[ni][mi]);
+    }
+  };
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+    compute(buf);
+    if (kt + 1 < nk) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds row m = col index of the MFMA output, 4 runs of 4
+  // consecutive n.
+  const bf16* G = (const bf16*)g.gate_src + (EPI == EPI_GATE ? (int64_t)blockIdx.z * g.c_bstride : 0);
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+      const int m = m0 + wm * 64 + mi * 32 + (lane & 31);
+      if (m >= g.m) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * 64 + ni * 32 + q * 8 + (lane >> 5) * 4;
+        if (n >= g.n) continue;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[ni][mi][q * 4 + e];
+        if (EPI == EPI_GATE) {
+          const bf16x4 gs = *(const bf16x4*)(G + (int64_t)m * g.ldg + n);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (float)gs[e] * (1.f / (1.f + __expf(-v[e])));
+        }
+        bf16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (bf16)v[e];
+        *(bf16x4*)(C + (int64_t)m * g.ldc + n) = o;
+      }
+    }
+}
+
+// fp32 kernel for the fp32 dtype: 16x16 outputs per 256-thread block, K tiles of
+// 16 through LDS, one output per thread.
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
+  __shared__ float sa[16][17], sb[16][17];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int m = blockIdx.y * 16 + ty, n = blockIdx.x * 16 + tx;
+  const float* A = (const float*)g.a + (int64_t)blockIdx.z * g.a_bstride;
+  const float* B = (const float*)g.b + (int64_t)blockIdx.z * g.b_bstride;
+  float* C = (float*)g.c + (int64_t)blockIdx.z * g.c_bstride;
+  float acc = 0.f;
+  for (int k0 = 0; k0 < g.k; k0 += 16) {
+    const int am = blockIdx.y * 16 + ty, ak = k0 + tx;
+    sa[ty][tx] = (am < g.m && ak < g.k) ? A[(int64_t)am * g.lda + ak] : 0.f;
+    const int bn = blockIdx.x * 16 + ty, bk = k0 + tx;   // sb[n][k]
+    if (!g.b_kn)
+      sb[ty][tx] = (bn < g.n && bk < g.k) ? B[(int64_t)bn * g.ldb + bk] : 0.f;
+    else {
+      const int kk = k0 + ty, nn = blockIdx.x * 16 + tx;    // B[k][n] -> sb[n][k]
+      sb[tx][ty] = (kk < g.k && nn < g.n) ? B[(int64_t)kk * g.ldb + nn] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) acc = fmaf(sa[ty][kk], sb[tx][kk], acc);
+    __syncthreads();
+  }
+  if (m < g.m && n < g.n) {
+    if (EPI == EPI_GATE) {
+      const float* G = (const float*)g.gate_src + (int64_t)blockIdx.z * g.c_bstride;
+      acc = G[(int64_t)m * g.ldg + n] * (1.f / (1.f + expf(-acc)));
+    }
+    C[(int64_t)m * g.ldc + n] = acc;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
+  if (g.m <= 0 || g.n <= 0 || g.batch <= 0) return hipSuccess;
+  const int num_m = (g.m + BM - 1) / BM, num_n = (g.n + BN - 1) / BN;
+  dim3 grid(num_m * num_n, 1, g.batch);
+  if (g.b_kn) {
+    if (g.epilogue == EPI_GATE) return hipErrorInvalidValue;
+    gemm_bf16_kernel<true, EPI_STORE><<<grid, NT, 0, s>>>(g);
+  } else if (g.epilogue == EPI_GATE) {
+    gemm_bf16_kernel<false, EPI_GATE><<<grid, NT, 0, s>>>(g);
+  } else {
+    gemm_bf16_kernel<false, EPI_STORE><<<grid, NT, 0, s>>>(g);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_f32(const GemmArgs& g, hipStream_t s) {
+  if (g.m <= 0 || g.n <= 0 || g.batch <= 0) return hipSuccess;
+  dim3 grid((g.n + 15) / 16, (g.m + 15) / 16, g.batch);
+  if (g.epilogue == EPI_GATE)
+    gemm_f32_kernel<EPI_GATE><<<grid, 256, 0, s>>>(g);
+  else
+    gemm_f32_kernel<EPI_STORE><<<grid, 256, 0, s>>>(g);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,127 @@
+// Internal declarations shared by the libmla HIP sources (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "mla.h"
+
+namespace mla {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+#define MLA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------- device helpers
+__device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
+__device__ __forceinline__ float to_f32(float v) { return v; }
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// MFMA wrappers (lane layouts checked on gfx950):
+//  16x16x32: A lane l -> row l%16, k (l/16)*8+[0,8); B lane l -> col l%16, same k;
+//            C lane l -> col l%16, rows (l/16)*4+[0,4).
+//  32x32x16: A lane l -> row l%32, k (l/32)*8+[0,8); B lane l -> col l%32, same k;
+//            C lane l -> col l%32, rows (i/4)*8 + (l/32)*4 + i%4, i in [0,16).
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane
+// L supplies the address of 4 consecutive 16-bit elements ("row" L); the result
+// of lane i is element i%4 of rows i/4, i/4+4, i/4+8, i/4+12.
+// Used so that lane i of a group receives X[k0 + j][n0 + i], j = 0..3, from a
+// row-major X[k][n] tile: lane L then addresses &X[k0 + L/4][n0 + 4*(L%4)].
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+// Asynchronous global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4).
+// The destination of lane l is lds_base + 16 * l; lds_base must be uniform
+// across the wave.  Completion is awaited with vm_wait_all() before a barrier.
+__device__ __forceinline__ void lds_dma16(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (MLA_LDS void*)(lds_base), 16, 0, 0);
+}
+__device__ __forceinline__ void vm_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// ---------------------------------------------------------------- launchers
+struct GemmArgs {
+  const void* a; int64_t lda; int64_t a_bstride;   // A [m, k]
+  const void* b; int64_t ldb; int64_t b_bstride;   // B [n, k] (NT) or [k, n] (NN)
+  void* c; int64_t ldc; int64_t c_bstride;         // C [m, n]
+  const void* gate_src; int64_t ldg;               // epilogue "gate": c = gate_src * sigmoid(acc)
+  int m, n, k, batch;
+  bool b_kn;                                       // true: B stored [k, n] (NN)
+  int epilogue;                                    // 0 store, 1 gate
+};
+enum { EPI_STORE = 0, EPI_GATE = 1 };
+
+hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s);
+hipError_t launch_gemm_f32(const GemmArgs& g, hipStream_t s);
+
+struct NormRopeArgs {
+  const void* src; int64_t src_stride; int n_rows; int row_width;
+  int norm_dim; const void* gamma; float eps;
+  int rope_offset; int rope_slices; int rope_stride; int rope_dim;
+  const float* cos_t; const float* sin_t; int table_len; const int32_t* positions;
+  void* dst; int64_t dst_stride; const int32_t* slots; int64_t num_slots;
+};
+hipError_t launch_norm_rope(const NormRopeArgs& a, bool bf16_io, hipStream_t s);
+
+hipError_t launch_positions(const int32_t* cu_dev, int num_seqs, int n_tokens, int32_t* pos, hipStream_t s);
+
+struct FlashArgs {
+  const void* q; const void* kv; const void* latent; int64_t latent_stride;
+  const int32_t* cu_dev; void* out;
+  int n_tokens; int heads; int nope; int rope; int dv; int kv_lora;
+  float scale; int num_seqs;
+};
+// bf16 MFMA kernel (nope 128, rope 64, dv 128).  The tile plan is built from the
+// host offsets inside.
+hipError_t launch_flash_bf16(const FlashArgs& a, const int32_t* cu_host, int num_seqs, hipStream_t s);
+hipError_t launch_flash_f32(const FlashArgs& a, hipStream_t s);
+
+struct DecodeArgs {
+  const bf16* qt;         // [B, H, 512] absorbed query
+  const bf16* q_pe;       // [B, H, 64]
+  const bf16* cache;      // [num_blocks, block_size, 576]
+  const int32_t* block_table; int max_blocks; int num_blocks; int block_size;
+  const int32_t* seq_lens;
+  float* part_o;          // [B, max_chunks, H, 512]
+  float* part_ml;         // [B, max_chunks, H, 2]
+  bf16* o_lat;            // [B, H, 512]
+  int batch; int heads; int chunk; int max_chunks;
+  float scale;
+};
+hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t s);
+
+}  // namespace mla

@@ -1,0 +1,147 @@
+"""Host-side tests of the C ABI (no GPU needed): the library loads and exports
+every function declared in include/mla.h, argument checks reject bad input
+before any device work, and the host-only helpers (softmax scale, RoPE / YaRN
+table) agree with the oracle."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import mla_inputs as mi
+from oracle import mla as om
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+mla = pytest.importorskip("latent_attention_forward_amd")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mla.LIB_PATH):
+        pytest.skip("libmla.so not built")
+    return mla.load_library()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported(lib):
+    names = header_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(mla.exported_symbols())
+    assert lib.mla_abi_version() == 1
+
+
+def test_config_validation(lib):
+    ok = mla.make_config(mi.WORKLOADS["dsv3_prefill_4096"])
+    assert lib.mla_validate_config(ctypes.byref(ok)) == mla.MLA_OK
+    bad = [
+        dict(qk_rope_dim=63), dict(num_heads=0), dict(dtype=7), dict(rope_kind=9),
+        dict(yarn_beta_fast=0.5), dict(rope_theta=0.0), dict(output_gate=3), dict(kv_lora_rank=-1),
+    ]
+    for kw in bad:
+        c = mla.make_config(mi.WORKLOADS["dsv3_prefill_4096"], **kw)
+        assert lib.mla_validate_config(ctypes.byref(c)) == mla.MLA_ERR_INVALID_ARG, kw
+        assert lib.mla_last_error().decode()
+    assert lib.mla_validate_config(None) == mla.MLA_ERR_INVALID_ARG
+
+
+def test_softmax_scale_matches_oracle(lib):
+    for name in ("tiny_fp32_t64", "megatron_2x2048", "dsv3_prefill_4096", "kimi_gated_varlen_8192"):
+        sh = mi.WORKLOADS[name]
+        got = mla.softmax_scale(mla.make_config(sh))
+        assert got == np.float32(om.softmax_scale(sh)), name
+    c = mla.make_config(mi.WORKLOADS["megatron_2x2048"], softmax_scale=0.5)
+    assert mla.softmax_scale(c) == 0.5
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32_t64", "megatron_2x2048", "dsv3_prefill_4096"])
+def test_rope_table_equals_oracle_rounded(lib, name):
+    sh = mi.WORKLOADS[name]
+    cfg = mla.make_config(sh)
+    P = 4096
+    cos, sin = mla.rope_table_host(cfg, P)
+    oc, os_ = om.rope_cos_sin(np.arange(P), sh.qk_rope_dim, sh.rope)
+    assert np.array_equal(cos, oc.astype(np.float32))
+    assert np.array_equal(sin, os_.astype(np.float32))
+
+
+def test_rope_table_rejects_nope(lib):
+    cfg = mla.make_config(mi.WORKLOADS["kimi_gated_varlen_8192"])
+    buf = np.empty(64, np.float32)
+    assert lib.mla_rope_table(ctypes.byref(cfg), 2, buf.ctypes.data, buf.ctypes.data) == mla.MLA_ERR_INVALID_ARG
+
+
+def test_workspace_sizes(lib):
+    cfg = mla.make_config(mi.WORKLOADS["dsv3_prefill_4096"])
+    s1 = mla.prefill_workspace_size(cfg, 4096, 1)
+    H = 128
+    need = 4096 * (1536 + H * 192 + 576 * 2 + H * 256 + H * 128) * 2
+    assert s1 >= need and s1 < need + 16 * 4096
+    assert mla.prefill_workspace_size(cfg, 8192, 1) > s1
+    d = mla.decode_workspace_size(mla.make_config(mi.WORKLOADS["dsv3_decode_64"]), [1024] * 64)
+    assert d >= 2 * 64 * 128 * 512 * 2
+
+
+def test_device_calls_reject_bad_arguments_before_launch(lib):
+    """Every check below fails on the host; no HIP call is made."""
+    sh = mi.WORKLOADS["dsv3_prefill_4096"]
+    cfg = mla.make_config(sh)
+    w = mla.MlaWeights()
+    cu = np.array([0, 16], np.int32)
+    f = lib.mla_prefill_fwd
+    # missing weights
+    st = f(ctypes.byref(cfg), ctypes.byref(w), 16, 16, cu.ctypes.data, 1, None, None, None, 0, 16, None, 16, 1 << 30, None)
+    assert st == mla.MLA_ERR_INVALID_ARG
+    # non-monotone offsets
+    bad_cu = np.array([0, 8, 4], np.int32)
+    st = f(ctypes.byref(cfg), ctypes.byref(w), 16, 16, bad_cu.ctypes.data, 2, None, None, None, 0, 16, None, 16, 0, None)
+    assert st == mla.MLA_ERR_INVALID_ARG
+    # bf16 with an unsupported head shape
+    c2 = mla.make_config(sh, qk_nope_dim=64)
+    st = f(ctypes.byref(c2), ctypes.byref(w), 16, 16, cu.ctypes.data, 1, None, None, None, 0, 16, None, 16, 0, None)
+    assert st == mla.MLA_ERR_UNSUPPORTED
+    # workspace too small (weights present, fake aligned addresses, nothing is launched)
+    for name, _ in mla.MlaWeights._fields_:
+        setattr(w, name, 4096)
+    w.w_q = None
+    w.w_g = None
+    st = f(ctypes.byref(cfg), ctypes.byref(w), 4096, 4096, cu.ctypes.data, 1, None, 4096, 4096, 64, 4096, None, 4096, 16, None)
+    assert st == mla.MLA_ERR_WORKSPACE
+    # misaligned x
+    st = f(ctypes.byref(cfg), ctypes.byref(w), 4098, 4096, cu.ctypes.data, 1, None, 4096, 4096, 64, 4096, None, 4096, 1 << 40, None)
+    assert st == mla.MLA_ERR_MISALIGNED
+    # decode: fp32 unsupported, bad lengths, bad block size
+    dcfg = mla.make_config(mi.WORKLOADS["dsv3_decode_64"])
+    lens = np.array([100, 0], np.int32)
+    g = lib.mla_decode_absorbed_fwd
+    st = g(ctypes.byref(dcfg), 4096, 4096, 4096, 4096, 10, 64, 4096, 4, 4096, lens.ctypes.data, 2, 4096, 4096, 1 << 30, None)
+    assert st == mla.MLA_ERR_INVALID_ARG
+    lens = np.array([100, 300], np.int32)
+    st = g(ctypes.byref(dcfg), 4096, 4096, 4096, 4096, 10, 64, 4096, 4, 4096, lens.ctypes.data, 2, 4096, 4096, 1 << 30, None)
+    assert st == mla.MLA_ERR_INVALID_ARG       # 300 > max_blocks * block_size
+    st = g(ctypes.byref(dcfg), 4096, 4096, 4096, 4096, 10, 60, 4096, 4, 4096, lens.ctypes.data, 2, 4096, 4096, 1 << 30, None)
+    assert st == mla.MLA_ERR_INVALID_ARG       # block size not a multiple of 16
+    d2 = mla.make_config(mi.WORKLOADS["dsv3_decode_64"], num_heads=48)
+    lens = np.array([100, 200], np.int32)
+    st = g(ctypes.byref(d2), 4096, 4096, 4096, 4096, 10, 64, 4096, 4, 4096, lens.ctypes.data, 2, 4096, 4096, 1 << 30, None)
+    assert st == mla.MLA_ERR_UNSUPPORTED
+    f32 = mla.make_config(mi.WORKLOADS["tiny_fp32_t64"])
+    st = g(ctypes.byref(f32), 4096, 4096, 4096, 4096, 10, 64, 4096, 4, 4096, lens.ctypes.data, 2, 4096, 4096, 1 << 30, None)
+    assert st == mla.MLA_ERR_UNSUPPORTED
+    # norm/rope: rope slices overlapping the norm region, slot mapping in place
+    st = lib.mla_latent_norm_rope(ctypes.byref(cfg), 4096, 576, 4, 576, 512, 4096, 500, 1, 64, 4096, 4096, 16, 4096,
+                                  8192, 576, None, 0, None)
+    assert st == mla.MLA_ERR_INVALID_ARG
+    st = lib.mla_latent_norm_rope(ctypes.byref(cfg), 4096, 576, 4, 576, 512, 4096, 512, 1, 64, 4096, 4096, 16, 4096,
+                                  4096, 576, 4096, 8, None)
+    assert st == mla.MLA_ERR_INVALID_ARG
+    assert mla.MLAError(1, "x", "y").status == 1

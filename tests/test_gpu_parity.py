@@ -1,0 +1,328 @@
+"""GPU parity of libmla against the float64 CPU oracle (through the C ABI).
+
+Tolerances: bf16 outputs within 2e-2 of the oracle as max over output rows of
+max |error| / RMS(oracle row); fp32 within 1e-4 on the same metric; integer and
+placement work (paged slots, untouched poisoned slots) bit-exact.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import mla_inputs as mi
+from oracle import mla as om
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 2e-2
+F32_TOL = 1e-4
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def mla():
+    import latent_attention_forward_amd as m
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    m.load_library()
+    return m
+
+
+DEV = "cuda:0"
+
+
+def dev(a, dtype):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(DEV).to(dtype)
+
+
+def tdtype(shape):
+    return torch.bfloat16 if shape.dtype == "bf16" else torch.float32
+
+
+def run_prefill(mla, sh, case, latent=False, positions=None):
+    dt = tdtype(sh)
+    cfg = mla.make_config(sh)
+    W = {k: dev(v, dt) for k, v in case.w.items()}
+    x = dev(case.x, dt)
+    n = case.x.shape[0]
+    cu = torch.from_numpy(case.cu_seqlens).to(DEV)
+    cos = sin = None
+    if sh.rope.kind != "none":
+        cos, sin = mla.rope_table(cfg, max(int(np.max(np.diff(case.cu_seqlens))), 1) + 1, DEV)
+    out = torch.full((n, sh.hidden), float("nan"), dtype=dt, device=DEV)
+    lat = torch.full((n, sh.kv_lora_rank + sh.qk_rope_dim), float("nan"), dtype=dt, device=DEV) if latent else None
+    mla.prefill_fwd(cfg, W, x, cu, case.cu_seqlens, out, latent_out=lat, rope_cos=cos, rope_sin=sin,
+                    positions=positions)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), (None if lat is None else lat.float().cpu().numpy())
+
+
+# ----------------------------------------------------------------------------- fused norm + RoPE kernel
+def _bf16_ulp(x):
+    x = np.abs(x.astype(np.float32))
+    e = np.floor(np.log2(np.maximum(x, 1e-30)))
+    return np.exp2(e - 7)
+
+
+def test_latent_norm_rope_paged_scatter(mla):
+    _say("case: latent_norm_rope paged scatter")
+    sh = mi.WORKLOADS["dsv3_prefill_4096"]
+    cfg = mla.make_config(sh)
+    rng = np.random.default_rng(5)
+    n = 37
+    src = mi.bf16_round(rng.standard_normal((n, 576)).astype(np.float32) * 3)
+    gamma = mi.bf16_round(1 + 0.1 * rng.standard_normal(512).astype(np.float32))
+    pos = rng.integers(0, 4096, n).astype(np.int32)
+    num_slots = 128
+    slots = rng.permutation(num_slots)[:n].astype(np.int32)
+    slots[3] = -1                      # skipped row
+    cos, sin = mla.rope_table(cfg, 4096, DEV)
+    dst = torch.full((num_slots, 576), float("nan"), dtype=torch.bfloat16, device=DEV)
+    mla.latent_norm_rope(cfg, dev(src, torch.bfloat16), n, 576, 512, dev(gamma, torch.bfloat16), dst,
+                         rope_offset=512, rope_slices=1, rope_slice_stride=64, rope_cos=cos, rope_sin=sin,
+                         positions=torch.from_numpy(pos).to(DEV), slot_mapping=torch.from_numpy(slots).to(DEV),
+                         num_slots=num_slots)
+    torch.cuda.synchronize()
+    got = dst.float().cpu().numpy()
+    oc, osn = om.rope_cos_sin(pos, 64, sh.rope)
+    ref = np.concatenate([om.rms_norm(src[:, :512], gamma, sh.norm_eps), om.apply_rope(src[:, 512:], oc, osn)], 1)
+    for r in range(n):
+        if slots[r] < 0:
+            continue
+        g = got[slots[r]]
+        assert np.all(np.abs(g - ref[r]) <= _bf16_ulp(ref[r]) + 1e-30), r
+    untouched = np.setdiff1d(np.arange(num_slots), slots[slots >= 0])
+    assert np.all(np.isnan(got[untouched]))
+
+
+def test_q_rope_in_place_and_norm_only(mla):
+    _say("case: q rope in place")
+    sh = mi.WORKLOADS["megatron_2x2048"]
+    cfg = mla.make_config(sh)
+    rng = np.random.default_rng(6)
+    n, H = 19, 16
+    q = mi.bf16_round(rng.standard_normal((n, H * 192)).astype(np.float32))
+    pos = np.arange(n, dtype=np.int32) * 97
+    cos, sin = mla.rope_table(cfg, 2048, DEV)
+    t = dev(q, torch.bfloat16)
+    mla.latent_norm_rope(cfg, t, n, H * 192, 0, None, t, rope_offset=128, rope_slices=H, rope_slice_stride=192,
+                         rope_cos=cos, rope_sin=sin, positions=torch.from_numpy(pos).to(DEV))
+    torch.cuda.synchronize()
+    got = t.float().cpu().numpy().reshape(n, H, 192)
+    oc, osn = om.rope_cos_sin(pos, 64, sh.rope)
+    qr = q.reshape(n, H, 192)
+    ref_pe = om.apply_rope(qr[..., 128:], oc[:, None, :], osn[:, None, :])
+    assert np.array_equal(got[..., :128], qr[..., :128])
+    assert np.all(np.abs(got[..., 128:] - ref_pe) <= _bf16_ulp(ref_pe) + 1e-30)
+
+
+# ----------------------------------------------------------------------------- GEMM
+@pytest.mark.parametrize("m,n,k", [(1, 8, 8), (77, 136, 72), (300, 576, 2048), (256, 1024, 512)])
+def test_linear_bf16(mla, m, n, k):
+    _say(f"case: linear bf16 {m}x{n}x{k}")
+    rng = np.random.default_rng(m + n + k)
+    x = mi.bf16_round(rng.standard_normal((m, k)).astype(np.float32))
+    w = mi.bf16_round(0.05 * rng.standard_normal((n, k)).astype(np.float32))
+    cfg = mla.make_config(mi.WORKLOADS["megatron_2x2048"])
+    y = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device=DEV)
+    mla.linear(cfg, dev(x, torch.bfloat16), dev(w, torch.bfloat16), y)
+    torch.cuda.synchronize()
+    ref = x.astype(np.float64) @ w.astype(np.float64).T
+    got = y.float().cpu().numpy()
+    rms = np.sqrt(np.mean(ref * ref, axis=1, keepdims=True))
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-4 * rms)
+
+
+def test_linear_f32(mla):
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((33, 70)).astype(np.float32)
+    w = rng.standard_normal((45, 70)).astype(np.float32)
+    cfg = mla.make_config(mi.WORKLOADS["tiny_fp32_t64"])
+    y = torch.empty(33, 45, dtype=torch.float32, device=DEV)
+    mla.linear(cfg, dev(x, torch.float32), dev(w, torch.float32), y)
+    torch.cuda.synchronize()
+    ref = x.astype(np.float64) @ w.astype(np.float64).T
+    assert om.row_rel_error(ref, y.cpu().numpy()) < 1e-5
+
+
+# ----------------------------------------------------------------------------- attention core
+@pytest.mark.parametrize("lens", [[1], [200], [5, 0, 130, 64, 1, 300]])
+def test_attention_core(mla, lens):
+    _say(f"case: attention core lens={lens}")
+    sh = mi.WORKLOADS["dsv3_prefill_4096"].replace(num_heads=3)
+    rng = np.random.default_rng(len(lens))
+    n = sum(lens)
+    q = mi.bf16_round(rng.standard_normal((n, 3, 192)).astype(np.float32))
+    kv = mi.bf16_round(rng.standard_normal((n, 3, 256)).astype(np.float32))
+    lat = mi.bf16_round(rng.standard_normal((n, 576)).astype(np.float32))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cfg = mla.make_config(sh)
+    attn = torch.full((n, 3, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
+    mla.attention_prefill(cfg, dev(q, torch.bfloat16), dev(kv, torch.bfloat16), dev(lat, torch.bfloat16),
+                          torch.from_numpy(cu).to(DEV), cu, attn)
+    torch.cuda.synchronize()
+    k = np.concatenate([kv[..., :128], np.broadcast_to(lat[:, None, 512:], (n, 3, 64))], -1)
+    ref = om.causal_varlen_attention(q, k, kv[..., 128:], om.softmax_scale(sh), cu)
+    err = om.row_rel_error(ref.reshape(n * 3, 128), attn.float().cpu().numpy().reshape(n * 3, 128))
+    _say(f"  err {err:.3e}")
+    assert err <= BF16_TOL
+
+
+# ----------------------------------------------------------------------------- full prefill, small shapes
+SMALL = {
+    "v3_yarn": (mi.WORKLOADS["dsv3_prefill_4096"].replace(hidden=512, num_heads=4, q_lora_rank=256), [70, 1, 131, 0, 257]),
+    "megatron_direct_q": (mi.WORKLOADS["megatron_2x2048"].replace(hidden=256, num_heads=2), [128, 128]),
+    "kimi_gate_nope": (mi.WORKLOADS["kimi_gated_varlen_8192"].replace(hidden=384, num_heads=3, q_lora_rank=128), [33, 190, 7]),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_prefill_small(mla, name):
+    sh, lens = SMALL[name]
+    _say(f"case: prefill small {name} lens={lens}")
+    case = mi.make_prefill_case(sh, doc_lengths=lens)
+    got, lat = run_prefill(mla, sh, case, latent=True)
+    ref = om.mla_prefill(sh, case.w, case.x, case.cu_seqlens)
+    err = om.row_rel_error(ref["out"], got)
+    lerr = om.row_rel_error(ref["latent"], lat)
+    floor = om.row_rel_error(ref["out"], mi.bf16_round(ref["out"].astype(np.float32)))
+    _say(f"  out err {err:.3e} (bf16 floor {floor:.3e}), latent err {lerr:.3e}")
+    assert err <= BF16_TOL and lerr <= BF16_TOL
+
+
+def test_prefill_tiny_fp32_full(mla):
+    sh = mi.WORKLOADS["tiny_fp32_t64"]
+    _say("case: tiny fp32 layer, T=64")
+    case = mi.make_prefill_case(sh)
+    got, lat = run_prefill(mla, sh, case, latent=True)
+    ref = om.mla_prefill(sh, case.w, case.x, case.cu_seqlens)
+    err = om.row_rel_error(ref["out"], got)
+    _say(f"  err {err:.3e}")
+    assert err <= F32_TOL
+    assert om.row_rel_error(ref["latent"], lat) <= F32_TOL
+
+
+def test_prefill_explicit_positions(mla):
+    """Caller-given positions equal to the per-document defaults give the same bits."""
+    sh, lens = SMALL["v3_yarn"]
+    case = mi.make_prefill_case(sh, doc_lengths=lens)
+    pos = np.concatenate([np.arange(l) for l in lens]).astype(np.int32)
+    a, _ = run_prefill(mla, sh, case)
+    b, _ = run_prefill(mla, sh, case, positions=torch.from_numpy(pos).to(DEV))
+    assert np.array_equal(a, b)
+
+
+def test_prefill_deterministic_and_causal(mla):
+    """Two runs are bit-identical; perturbing tokens after t leaves rows <= t bit-identical."""
+    sh, lens = SMALL["v3_yarn"]
+    lens = [300]
+    case = mi.make_prefill_case(sh, doc_lengths=lens)
+    a, _ = run_prefill(mla, sh, case)
+    b, _ = run_prefill(mla, sh, case)
+    assert np.array_equal(a, b)
+    t = 150
+    case.x[t + 1:] = mi.bf16_round(case.x[t + 1:] * 1.5 + 0.25)
+    c, _ = run_prefill(mla, sh, case)
+    assert np.array_equal(a[: t + 1], c[: t + 1])
+    assert not np.array_equal(a[t + 1:], c[t + 1:])
+
+
+# ----------------------------------------------------------------------------- decode
+def run_decode(mla, sh, dc):
+    cfg = mla.make_config(sh)
+    B = len(dc.seq_lens)
+    out = torch.full((B, sh.num_heads, sh.v_head_dim), float("nan"), dtype=torch.bfloat16, device=DEV)
+    mla.decode_absorbed_fwd(cfg, dev(dc.w_kv_b, torch.bfloat16), dev(dc.q_nope, torch.bfloat16),
+                            dev(dc.q_pe, torch.bfloat16), dev(dc.cache, torch.bfloat16),
+                            torch.from_numpy(dc.block_table).to(DEV), torch.from_numpy(dc.seq_lens).to(DEV),
+                            dc.seq_lens, out)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy()
+
+
+@pytest.mark.parametrize("heads,lens,bs", [(128, [1, 17, 64, 65, 1000, 3000], 64), (32, [5, 300], 16), (96, [129, 700], 32)])
+def test_decode_small(mla, heads, lens, bs):
+    _say(f"case: decode heads={heads} lens={lens} block={bs}")
+    sh = mi.WORKLOADS["dsv3_decode_64"].replace(num_heads=heads)
+    dc = mi.make_decode_case(sh, seq_lens=lens, block_size=bs)
+    got = run_decode(mla, sh, dc)
+    B = len(lens)
+    ra = om.decode_absorbed(sh, dc.w_kv_b, dc.q_nope, dc.q_pe, dc.cache, dc.block_table, dc.seq_lens, bs)
+    rn = om.decode_naive(sh, dc.w_kv_b, dc.q_nope, dc.q_pe, dc.cache, dc.block_table, dc.seq_lens, bs)
+    ea = om.row_rel_error(ra.reshape(B, -1), got.reshape(B, -1))
+    en = om.row_rel_error(rn.reshape(B, -1), got.reshape(B, -1))
+    _say(f"  err vs absorbed {ea:.3e}, vs naive {en:.3e}")
+    assert ea <= BF16_TOL and en <= BF16_TOL
+
+
+def test_decode_bad_block_id_poisons_only_its_sequence(mla):
+    sh = mi.WORKLOADS["dsv3_decode_64"]
+    dc = mi.make_decode_case(sh, seq_lens=[100, 200, 150], block_size=64)
+    dc.block_table[1, 1] = 10 ** 6
+    got = run_decode(mla, sh, dc)
+    assert np.all(np.isnan(got[1]))
+    ok = [0, 2]
+    ra = om.decode_absorbed(sh, dc.w_kv_b, dc.q_nope, dc.q_pe, dc.cache, dc.block_table, dc.seq_lens, 64, batch_idx=ok)
+    assert om.row_rel_error(ra.reshape(2, -1), got[ok].reshape(2, -1)) <= BF16_TOL
+
+
+def test_prefill_latent_feeds_decode(mla):
+    """Prefill writes the latent cache rows; decode of the last token over them
+    equals the last prefill row's attention (through W_o)."""
+    sh = mi.WORKLOADS["dsv3_prefill_4096"].replace(hidden=512, q_lora_rank=256)
+    T = 200
+    case = mi.make_prefill_case(sh, doc_lengths=[T])
+    _, lat = run_prefill(mla, sh, case, latent=True)
+    ref = om.mla_prefill(sh, case.w, case.x, case.cu_seqlens)
+    bs = 64
+    nblk = (T + bs - 1) // bs
+    cache = np.full((nblk, bs, 576), np.nan, np.float32)
+    table = np.arange(nblk, dtype=np.int32)[None, ::-1].copy()
+    for j in range(T):
+        cache[table[0, j // bs], j % bs] = lat[j]
+    q = mi.bf16_round(ref["q"][T - 1].astype(np.float32))[None]
+    dc = mi.DecodeCase(shape=sh, w_kv_b=case.w["w_kv_b"], q_nope=q[..., :128], q_pe=q[..., 128:], cache=cache,
+                       block_table=table, seq_lens=np.array([T], np.int32), block_size=bs)
+    got = run_decode(mla, sh, dc)
+    want = ref["attn"][T - 1].reshape(1, -1)
+    assert om.row_rel_error(want, got.reshape(1, -1)) <= BF16_TOL
+
+
+# ----------------------------------------------------------------------------- full sizes, sampled rows
+FULL = ["megatron_2x2048", "dsv3_prefill_4096", "kimi_gated_varlen_8192"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_prefill_full_size_sampled_rows(mla, name):
+    sh = mi.WORKLOADS[name]
+    _say(f"case: full-size prefill {name}")
+    case = mi.make_prefill_case(sh)
+    got, lat = run_prefill(mla, sh, case, latent=True)
+    cu = case.cu_seqlens
+    rng = np.random.default_rng(0)
+    rows = sorted(set([0, int(cu[-1]) - 1] + [int(c) for c in cu[:-1]] + [int(c) - 1 for c in cu[1:]] +
+                      list(rng.integers(0, int(cu[-1]), 24))))
+    ref = om.mla_prefill_rows(sh, case.w, case.x, cu, rows)
+    err = om.row_rel_error(ref["out"], got[rows])
+    lerr = om.row_rel_error(ref["latent"], lat)
+    _say(f"  sampled rows {len(rows)}: out err {err:.3e}, latent err (all rows) {lerr:.3e}")
+    assert err <= BF16_TOL and lerr <= BF16_TOL
+    assert np.all(np.isfinite(got))
+
+
+def test_decode_full_size(mla):
+    sh = mi.WORKLOADS["dsv3_decode_64"]
+    _say("case: full-size decode, 64 sequences")
+    dc = mi.make_decode_case(sh)
+    got = run_decode(mla, sh, dc)
+    idx = [0, 1, 17, 33, 63] + [int(np.argmax(dc.seq_lens)), int(np.argmin(dc.seq_lens))]
+    ra = om.decode_absorbed(sh, dc.w_kv_b, dc.q_nope, dc.q_pe, dc.cache, dc.block_table, dc.seq_lens, 64, batch_idx=idx)
+    err = om.row_rel_error(ra.reshape(len(idx), -1), got[idx].reshape(len(idx), -1))
+    _say(f"  err {err:.3e}")
+    assert err <= BF16_TOL
+    assert np.all(np.isfinite(got))
