@@ -117,7 +117,7 @@ std::vector<double> rope_frequencies(const mla_config* c) {
 
 // ---------------------------------------------------------------- prefill workspace
 struct PrefillWs {
-  size_t pos, q_lat, q, ckv, latent, kv, attn, total;
+  size_t pos, q_lat32, q_lat, q, ckv32, latent, kpe16, kv, attn, total;
 };
 
 PrefillWs prefill_layout(const mla_config* c, int64_t n) {
@@ -127,10 +127,12 @@ PrefillWs prefill_layout(const mla_config* c, int64_t n) {
   PrefillWs w;
   size_t off = 0;
   w.pos = off; off += align256(n * 4);
+  w.q_lat32 = off; off += align256(n * c->q_lora_rank * 4);   // fp32 down-projection before the norm
   w.q_lat = off; off += align256(n * c->q_lora_rank * es);
   w.q = off; off += align256(n * H * dqk * es);
-  w.ckv = off; off += align256(n * lw * es);
+  w.ckv32 = off; off += align256(n * lw * 4);                  // fp32 [c | k_pe] before norm / RoPE
   w.latent = off; off += align256(n * lw * es);
+  w.kpe16 = off; off += align256(n * c->qk_rope_dim * 2);      // fp16 shared rope key for attention
   w.kv = off; off += align256(n * H * (c->qk_nope_dim + c->v_head_dim) * es);
   w.attn = off; off += align256(n * H * c->v_head_dim * es);
   w.total = off;
@@ -316,14 +318,15 @@ mla_status mla_linear(const mla_config* cfg, const void* x, int64_t ldx, const v
   return s == MLA_OK ? ok() : s;
 }
 
-static mla_status attention_impl(const mla_config* cfg, const void* q, const void* kv, const void* latent,
-                                 int64_t latent_stride, const int32_t* cu_dev, const int32_t* cu_host, int num_seqs,
-                                 int n, void* attn, hipStream_t st) {
+static mla_status attention_impl(const mla_config* cfg, const void* q, const void* kv, const void* kpe,
+                                 int64_t kpe_stride, bool f16_operands, const int32_t* cu_dev,
+                                 const int32_t* cu_host, int num_seqs, int n, void* attn, hipStream_t st) {
   FlashArgs f{};
-  f.q = q; f.kv = kv; f.latent = latent; f.latent_stride = latent_stride; f.cu_dev = cu_dev; f.out = attn;
+  f.q = q; f.kv = kv; f.kpe = kpe; f.kpe_stride = kpe_stride; f.cu_dev = cu_dev; f.out = attn;
   f.n_tokens = n; f.heads = cfg->num_heads; f.nope = cfg->qk_nope_dim; f.rope = cfg->qk_rope_dim;
   f.dv = cfg->v_head_dim; f.kv_lora = cfg->kv_lora_rank; f.scale = scale_of(cfg); f.num_seqs = num_seqs;
-  const hipError_t e = cfg->dtype == MLA_BF16 ? launch_flash_bf16(f, cu_host, num_seqs, st) : launch_flash_f32(f, st);
+  const hipError_t e = cfg->dtype == MLA_BF16 ? launch_flash_mfma(f, f16_operands, cu_host, num_seqs, st)
+                                              : launch_flash_f32(f, st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return MLA_OK;
 }
@@ -342,7 +345,9 @@ mla_status mla_attention_prefill(const mla_config* cfg, const void* q, const voi
   if (latent_stride < cfg->kv_lora_rank + cfg->qk_rope_dim) return fail(MLA_ERR_INVALID_ARG, "latent_stride too small");
   if (cfg->dtype == MLA_BF16 && (!aligned16(q) || !aligned16(kv) || !aligned16(latent) || !aligned16(attn) || latent_stride % 8))
     return fail(MLA_ERR_MISALIGNED, "bf16 attention needs 16-byte aligned tensors and latent_stride % 8 == 0");
-  s = attention_impl(cfg, q, kv, latent, latent_stride, cu_seqlens_dev, cu_seqlens_host, num_seqs, n, attn, (hipStream_t)stream);
+  const void* kpe = (const char*)latent + (size_t)cfg->kv_lora_rank * elem_size(cfg);
+  s = attention_impl(cfg, q, kv, kpe, latent_stride, false, cu_seqlens_dev, cu_seqlens_host, num_seqs, n, attn,
+                     (hipStream_t)stream);
   return s == MLA_OK ? ok() : s;
 }
 
@@ -379,17 +384,17 @@ mla_status mla_prefill_fwd(const mla_config* cfg, const mla_weights* w, const vo
   }
   const hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
-  const size_t es = elem_size(cfg);
-  (void)es;
   const int H = cfg->num_heads, hid = cfg->hidden, rq = cfg->q_lora_rank, rkv = cfg->kv_lora_rank;
   const int dn = cfg->qk_nope_dim, dr = cfg->qk_rope_dim, dv = cfg->v_head_dim, dqk = dn + dr, lw = rkv + dr;
   int32_t* pos = (int32_t*)(ws + L.pos);
+  float* q_lat32 = (float*)(ws + L.q_lat32);
   void* q_lat = ws + L.q_lat;
   void* q = ws + L.q;
-  void* ckv = ws + L.ckv;
+  float* ckv32 = (float*)(ws + L.ckv32);
   void* lat = latent_out ? latent_out : (void*)(ws + L.latent);
   void* kv = ws + L.kv;
   void* attn = ws + L.attn;
+  const bool bf = cfg->dtype == MLA_BF16;
   hipError_t e;
 
   // positions (0..len-1 per document) unless the caller gives them
@@ -398,44 +403,73 @@ mla_status mla_prefill_fwd(const mla_config* cfg, const mla_weights* w, const vo
     if ((e = launch_positions(cu_seqlens_dev, num_seqs, n, pos, st)) != hipSuccess) return hip_fail(e, "positions");
     positions = pos;
   }
-  // query path
+  // Down-projections are kept in fp32 until their norm, so every stored bf16
+  // tensor is rounded once.
+  // Output storage of each GEMM: OUT_ACT (the layer dtype), OUT_F32 (kept for a
+  // following norm), OUT_F16 (attention operands of the bf16 layer).
+  enum { OUT_ACT, OUT_F32, OUT_F16 };
+  auto gemm = [&](const void* a, int64_t lda, const void* b, void* c, int64_t ldc, int m, int nn, int k,
+                  int out_kind, int epi, const void* gate) -> mla_status {
+    GemmArgs g{};
+    g.a = a; g.lda = lda; g.b = b; g.ldb = k; g.c = c; g.ldc = ldc; g.m = m; g.n = nn; g.k = k; g.batch = 1;
+    g.c_f32 = out_kind == OUT_F32 && bf; g.c_f16 = out_kind == OUT_F16 && bf;
+    g.epilogue = epi; g.gate_src = gate; g.ldg = ldc;
+    g.cos_t = rope_cos; g.sin_t = rope_sin; g.table_len = rope_table_len; g.positions = positions;
+    g.rope_head_stride = dqk; g.rope_off = dn;
+    const hipError_t err = bf ? launch_gemm_bf16(g, st) : launch_gemm_f32(g, st);
+    if (err != hipSuccess) return hip_fail(err, "linear launch");
+    return MLA_OK;
+  };
+  auto norm = [&](const void* src, int64_t stride, int width, int norm_dim, const void* gamma, int rope_off,
+                  int rope_slices, int rope_stride, void* dst, int64_t dst_stride, bool src_f32,
+                  f16* aux = nullptr) -> mla_status {
+    NormRopeArgs a{};
+    a.rope_aux = aux; a.rope_aux_stride = dr;
+    a.src = src; a.src_stride = stride; a.n_rows = n; a.row_width = width; a.norm_dim = norm_dim; a.gamma = gamma;
+    a.eps = cfg->norm_eps; a.rope_offset = rope_off; a.rope_slices = rope_slices; a.rope_stride = rope_stride;
+    a.rope_dim = dr; a.cos_t = rope_cos; a.sin_t = rope_sin; a.table_len = rope_table_len; a.positions = positions;
+    a.dst = dst; a.dst_stride = dst_stride;
+    const hipError_t err = launch_norm_rope(a, bf, st, src_f32 && bf);
+    if (err != hipSuccess) return hip_fail(err, "latent norm / rope launch");
+    return MLA_OK;
+  };
+  // bf16: RoPE on q is fused into the q GEMM epilogue; fp32: applied in place after it.
+  // In the bf16 layer the attention operands q, kv and the shared k_pe are kept
+  // in fp16 (rounded once from fp32): bf16 storage of all of them puts the layer
+  // output beyond the parity bound at the 128-head shapes.
+  const int q_epi = (rope && bf) ? EPI_ROPE : EPI_STORE;
+  const int att_kind = bf ? OUT_F16 : OUT_ACT;
+  f16* kpe16 = (f16*)(ws + L.kpe16);
   if (rq > 0) {
-    if ((s = linear_impl(cfg, x, hid, w->w_q_a, q_lat, rq, n, rq, hid, nullptr, 0, st)) != MLA_OK) return s;
-    NormRopeArgs a{};
-    a.src = q_lat; a.src_stride = rq; a.n_rows = n; a.row_width = rq; a.norm_dim = rq; a.gamma = w->q_a_gamma;
-    a.eps = cfg->norm_eps; a.rope_stride = 1; a.dst = q_lat; a.dst_stride = rq;
-    if ((e = launch_norm_rope(a, cfg->dtype == MLA_BF16, st)) != hipSuccess) return hip_fail(e, "q latent norm");
-    if ((s = linear_impl(cfg, q_lat, rq, w->w_q_b, q, (int64_t)H * dqk, n, H * dqk, rq, nullptr, 0, st)) != MLA_OK) return s;
+    void* ql_raw = bf ? (void*)q_lat32 : q_lat;
+    if ((s = gemm(x, hid, w->w_q_a, ql_raw, rq, n, rq, hid, OUT_F32, EPI_STORE, nullptr)) != MLA_OK) return s;
+    if ((s = norm(ql_raw, rq, rq, rq, w->q_a_gamma, 0, 0, 1, q_lat, rq, true)) != MLA_OK) return s;
+    if ((s = gemm(q_lat, rq, w->w_q_b, q, (int64_t)H * dqk, n, H * dqk, rq, att_kind, q_epi, nullptr)) != MLA_OK) return s;
   } else {
-    if ((s = linear_impl(cfg, x, hid, w->w_q, q, (int64_t)H * dqk, n, H * dqk, hid, nullptr, 0, st)) != MLA_OK) return s;
+    if ((s = gemm(x, hid, w->w_q, q, (int64_t)H * dqk, n, H * dqk, hid, att_kind, q_epi, nullptr)) != MLA_OK) return s;
   }
-  if (rope) {   // RoPE on the H rope slices of q, in place
-    NormRopeArgs a{};
-    a.src = q; a.src_stride = (int64_t)H * dqk; a.n_rows = n; a.row_width = H * dqk; a.norm_dim = 0;
-    a.rope_offset = dn; a.rope_slices = H; a.rope_stride = dqk; a.rope_dim = dr;
-    a.cos_t = rope_cos; a.sin_t = rope_sin; a.table_len = rope_table_len; a.positions = positions;
-    a.dst = q; a.dst_stride = (int64_t)H * dqk;
-    if ((e = launch_norm_rope(a, cfg->dtype == MLA_BF16, st)) != hipSuccess) return hip_fail(e, "q rope");
+  if (rope && !bf) {
+    if ((s = norm(q, (int64_t)H * dqk, H * dqk, 0, nullptr, dn, H, dqk, q, (int64_t)H * dqk, false)) != MLA_OK) return s;
   }
   // joint latent: down-projection, latent norm + k_pe RoPE -> [c_n | k_pe']
-  if ((s = linear_impl(cfg, x, hid, w->w_kv_a, ckv, lw, n, lw, hid, nullptr, 0, st)) != MLA_OK) return s;
   {
-    NormRopeArgs a{};
-    a.src = ckv; a.src_stride = lw; a.n_rows = n; a.row_width = lw; a.norm_dim = rkv; a.gamma = w->kv_a_gamma;
-    a.eps = cfg->norm_eps; a.rope_offset = rkv; a.rope_slices = rope ? 1 : 0; a.rope_stride = dr; a.rope_dim = dr;
-    a.cos_t = rope_cos; a.sin_t = rope_sin; a.table_len = rope_table_len; a.positions = positions;
-    a.dst = lat; a.dst_stride = lw;
-    if ((e = launch_norm_rope(a, cfg->dtype == MLA_BF16, st)) != hipSuccess) return hip_fail(e, "kv latent norm rope");
+    void* ckv_raw = bf ? (void*)ckv32 : (void*)(ws + L.ckv32);
+    if ((s = gemm(x, hid, w->w_kv_a, ckv_raw, lw, n, lw, hid, OUT_F32, EPI_STORE, nullptr)) != MLA_OK) return s;
+    if ((s = norm(ckv_raw, lw, lw, rkv, w->kv_a_gamma, rkv, rope ? 1 : 0, dr, lat, lw, true, bf ? kpe16 : nullptr)) != MLA_OK) return s;
   }
   // per-head keys/values from the normalised latent
-  if ((s = linear_impl(cfg, lat, lw, w->w_kv_b, kv, (int64_t)H * (dn + dv), n, H * (dn + dv), rkv, nullptr, 0, st)) != MLA_OK) return s;
+  if ((s = gemm(lat, lw, w->w_kv_b, kv, (int64_t)H * (dn + dv), n, H * (dn + dv), rkv, att_kind, EPI_STORE, nullptr)) != MLA_OK) return s;
   // attention
-  if ((s = attention_impl(cfg, q, kv, lat, lw, cu_seqlens_dev, cu_seqlens_host, num_seqs, n, attn, st)) != MLA_OK) return s;
+  {
+    const void* kpe = bf ? (const void*)kpe16 : (const void*)((const float*)lat + rkv);
+    const int64_t kpe_stride = bf ? dr : lw;
+    if ((s = attention_impl(cfg, q, kv, kpe, kpe_stride, bf, cu_seqlens_dev, cu_seqlens_host, num_seqs, n, attn, st)) != MLA_OK) return s;
+  }
   // optional gate, output projection
   if (cfg->output_gate) {
-    if ((s = linear_impl(cfg, x, hid, w->w_g, attn, (int64_t)H * dv, n, H * dv, hid, attn, (int64_t)H * dv, st)) != MLA_OK) return s;
+    if ((s = gemm(x, hid, w->w_g, attn, (int64_t)H * dv, n, H * dv, hid, OUT_ACT, EPI_GATE, attn)) != MLA_OK) return s;
   }
-  if ((s = linear_impl(cfg, attn, (int64_t)H * dv, w->w_o, out, hid, n, hid, H * dv, nullptr, 0, st)) != MLA_OK) return s;
+  if ((s = gemm(attn, (int64_t)H * dv, w->w_o, out, hid, n, hid, H * dv, OUT_ACT, EPI_STORE, nullptr)) != MLA_OK) return s;
   return ok();
 }
 

@@ -15,9 +15,10 @@
 // in-lane reduction plus one swap with the lane 32 away, and P^T feeds the
 // second MFMA straight from the first MFMA's registers (the key order of the
 // S^T output layout is matched by the transpose reads of V).  The online
-// softmax is fp32 with exp2 and the scale folded in; P is rounded to bf16 for
-// the PV MFMA; the output is normalised in fp32 and rounded once.  d_v = 128
-// is used as is: v is never padded to d_qk.
+// softmax is fp32 with exp2 and the scale folded in; P is rounded to the
+// operand type (bf16, or fp16 inside the prefill layer) for the PV MFMA; the
+// output is normalised in fp32 and rounded once to bf16.  d_v = 128 is used
+// as is: v is never padded to d_qk.
 #include "mla_internal.hpp"
 
 #include <vector>
@@ -27,7 +28,7 @@ namespace mla {
 namespace {
 
 constexpr int FQ = 128, FK = 64;
-constexpr int DN = 128, DQK = 192, DV = 128, RKV = 512;
+constexpr int DN = 128, DQK = 192, DV = 128;
 constexpr int KCH = DQK / 8;          // 16-byte chunks per key row (24)
 constexpr int MAX_TILES = 896;
 
@@ -36,15 +37,25 @@ struct TilePlan {
   uint32_t t[MAX_TILES];              // (document << 16) | query-tile index in the document
 };
 
-__device__ __forceinline__ bf16x8 zero8() { return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0)); }
+template <typename T> struct Vec;
+template <> struct Vec<bf16> { typedef bf16x8 v8; typedef bf16x4 v4; };
+template <> struct Vec<f16> { typedef f16x8 v8; typedef f16x4 v4; };
+
+template <typename V8> __device__ __forceinline__ V8 zero8() { return __builtin_bit_cast(V8, make_uint4(0, 0, 0, 0)); }
+template <typename V4, typename T> __device__ __forceinline__ V4 read_tr(const T* p) {
+  return __builtin_bit_cast(V4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(p)));
+}
 // K tile [64][192]: chunk c (0..23) of key row r at c ^ (r & 7) (stays within its group of 8).
 __device__ __forceinline__ int koff(int r, int c) { return r * DQK + ((c ^ (r & 7)) << 3); }
 // V tile [64][128]: 16 B chunk of column n in key row r at (n/8) ^ ((r & 3) << 1).
 __device__ __forceinline__ int voff(int r, int n) { return r * DV + ((((n >> 3) ^ ((r & 3) << 1))) << 3) + (n & 7); }
 
-__global__ __launch_bounds__(256, 2) void flash_bf16_kernel(FlashArgs a, TilePlan plan) {
-  __shared__ __attribute__((aligned(16))) bf16 sK[2][FK * DQK];
-  __shared__ __attribute__((aligned(16))) bf16 sV[2][FK * DV];
+template <typename T>
+__global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashArgs a, TilePlan plan) {
+  typedef typename Vec<T>::v8 V8;
+  typedef typename Vec<T>::v4 V4;
+  __shared__ __attribute__((aligned(16))) T sK[2][FK * DQK];
+  __shared__ __attribute__((aligned(16))) T sV[2][FK * DV];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int head = blockIdx.x;
@@ -58,9 +69,9 @@ __global__ __launch_bounds__(256, 2) void flash_bf16_kernel(FlashArgs a, TilePla
   const int q1 = min(q0 + FQ, de);
   const int ntiles = (q1 - ds + FK - 1) / FK;
 
-  const bf16* Q = (const bf16*)a.q;
-  const bf16* KV = (const bf16*)a.kv;
-  const bf16* LAT = (const bf16*)a.latent;
+  const T* Q = (const T*)a.q;
+  const T* KV = (const T*)a.kv;
+  const T* KPE = (const T*)a.kpe;
   bf16* O = (bf16*)a.out;
   const int64_t q_row = (int64_t)H * DQK, kv_row = (int64_t)H * (DN + DV);
 
@@ -68,10 +79,10 @@ __global__ __launch_bounds__(256, 2) void flash_bf16_kernel(FlashArgs a, TilePla
   const int qw0 = q0 + wave * 32;
   const int my_q = qw0 + (lane & 31);
   const int hsel = lane >> 5;
-  bf16x8 qreg[DQK / 16];
+  V8 qreg[DQK / 16];
 #pragma unroll
   for (int ks = 0; ks < DQK / 16; ++ks)
-    qreg[ks] = (my_q < q1) ? *(const bf16x8*)(Q + my_q * q_row + head * DQK + ks * 16 + hsel * 8) : zero8();
+    qreg[ks] = (my_q < q1) ? *(const V8*)(Q + my_q * q_row + head * DQK + ks * 16 + hsel * 8) : zero8<V8>();
 
   // Tile loads go straight to LDS (16 B per lane, lane l of a wave fills the
   // l-th 16 B of a 1 KB block).  Each LDS position is mapped back to the
@@ -88,8 +99,8 @@ __global__ __launch_bounds__(256, 2) void flash_bf16_kernel(FlashArgs a, TilePla
       const int r = P / KCH, pc = P - r * KCH;
       const int c = pc ^ (r & 7);
       const int key = (kb + r < q1) ? kb + r : kb;
-      const bf16* src = (c < DN / 8) ? KV + key * kv_row + head * (DN + DV) + c * 8
-                                     : LAT + key * a.latent_stride + RKV + (c - DN / 8) * 8;
+      const T* src = (c < DN / 8) ? KV + key * kv_row + head * (DN + DV) + c * 8
+                                  : KPE + key * a.kpe_stride + (c - DN / 8) * 8;
       lds_dma16(src, &sK[buf][blk * 512]);
     }
 #pragma unroll
@@ -128,7 +139,7 @@ __global__ __launch_bounds__(256, 2) void flash_bf16_kernel(FlashArgs a, TilePla
         for (int e = 0; e < 16; ++e) s[mt][e] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < DQK / 16; ++ks) {
-          const bf16x8 kf = *(const bf16x8*)&sK[buf][koff(mt * 32 + (lane & 31), ks * 2 + hsel)];
+          const V8 kf = *(const V8*)&sK[buf][koff(mt * 32 + (lane & 31), ks * 2 + hsel)];
           s[mt] = mfma32(kf, qreg[ks], s[mt]);
         }
       }
@@ -155,14 +166,14 @@ __global__ __launch_bounds__(256, 2) void flash_bf16_kernel(FlashArgs a, TilePla
       m_run = m_new;
       const float mb = m_use * c2;
       float psum = 0.f;
-      bf16x8 pb[4];
+      V8 pb[4];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const float p = __builtin_amdgcn_exp2f(fmaf(s[mt][e], c2, -mb));
           psum += p;
-          pb[mt * 2 + (e >> 3)][e & 7] = (bf16)p;
+          pb[mt * 2 + (e >> 3)][e & 7] = (T)p;
         }
       l_run = l_run * alpha + psum;
 #pragma unroll
@@ -177,8 +188,8 @@ __global__ __launch_bounds__(256, 2) void flash_bf16_kernel(FlashArgs a, TilePla
 #pragma unroll
         for (int d = 0; d < DV / 32; ++d) {
           const int nb = d * 32 + (grp & 1) * 16 + 4 * (L & 3);
-          const bf16x4 lo = lds_read_tr(&sV[buf][voff(kr, nb)]);
-          const bf16x4 hi = lds_read_tr(&sV[buf][voff(kr + 8, nb)]);
+          const V4 lo = read_tr<V4>(&sV[buf][voff(kr, nb)]);
+          const V4 hi = read_tr<V4>(&sV[buf][voff(kr + 8, nb)]);
           o[d] = mfma32(cat8(lo, hi), pb[j], o[d]);
         }
       }
@@ -219,12 +230,12 @@ __global__ __launch_bounds__(64) void flash_f32_kernel(FlashArgs a) {
   for (int d = lane; d < dqk; d += 64) sq[d] = Q[d];
   __syncthreads();
   const float* KV = (const float*)a.kv;
-  const float* LAT = (const float*)a.latent;
+  const float* KPE = (const float*)a.kpe;
   const int kvw = a.nope + a.dv;
   float m = -INFINITY, l = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
   for (int j = lo; j <= t; ++j) {
     const float* kr = KV + ((int64_t)j * H + h) * kvw;
-    const float* pr = LAT + (int64_t)j * a.latent_stride + a.kv_lora;
+    const float* pr = KPE + (int64_t)j * a.kpe_stride;
     float part = 0.f;
     for (int d = lane; d < dqk; d += 64) part = fmaf(sq[d], d < a.nope ? kr[d] : pr[d - a.nope], part);
     const float s = wave_sum(part) * a.scale;
@@ -248,7 +259,7 @@ __global__ __launch_bounds__(64) void flash_f32_kernel(FlashArgs a) {
 
 }  // namespace
 
-hipError_t launch_flash_bf16(const FlashArgs& a, const int32_t* cu_host, int num_seqs, hipStream_t s) {
+hipError_t launch_flash_mfma(const FlashArgs& a, bool f16_operands, const int32_t* cu_host, int num_seqs, hipStream_t s) {
   // Tile plan: every (document, 128-query tile), longest key range first.
   struct T { int keys; uint32_t id; };
   std::vector<T> tiles;
@@ -264,7 +275,10 @@ hipError_t launch_flash_bf16(const FlashArgs& a, const int32_t* cu_host, int num
     plan.n = n;
     for (int i = 0; i < n; ++i) plan.t[i] = tiles[base + i].id;
     dim3 grid(a.heads, n);
-    flash_bf16_kernel<<<grid, 256, 0, s>>>(a, plan);
+    if (f16_operands)
+      flash_mfma_kernel<f16><<<grid, 256, 0, s>>>(a, plan);
+    else
+      flash_mfma_kernel<bf16><<<grid, 256, 0, s>>>(a, plan);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

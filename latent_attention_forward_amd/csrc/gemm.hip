@@ -40,7 +40,7 @@ __device__ __forceinline__ int2 tile_coords(int pid, int num_m, int num_n) {
   return make_int2(first_m + in_group % gsize, in_group / gsize);
 }
 
-template <bool B_KN, int EPI>
+template <bool B_KN, int EPI, int CT>   // CT: 0 bf16, 1 fp32, 2 fp16 output
 __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) bf16 sA[2][BM * BK];
   __shared__ __attribute__((aligned(16))) bf16 sB[2][BN * BK];
@@ -50,7 +50,6 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmArgs g) {
   const int m0 = tc.x * BM, n0 = tc.y * BN;
   const bf16* A = (const bf16*)g.a + (int64_t)blockIdx.z * g.a_bstride;
   const bf16* B = (const bf16*)g.b + (int64_t)blockIdx.z * g.b_bstride;
-  bf16* C = (bf16*)g.c + (int64_t)blockIdx.z * g.c_bstride;
   const int wm = wave >> 1, wn = wave & 1;
   const int nk = (g.k + BK - 1) / BK;
 
@@ -136,7 +135,35 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmArgs g) {
     __syncthreads();
   }
 
-  // epilogue: lane holds row m = col index of the MFMA output, 4 runs of 4
+  // RoPE epilogue.  Rope slices start at multiples of 64 columns and are 64
+  // wide, so a slice is exactly one wave's 64-column window: pair (i, i + 32)
+  // is register e of N-tile 0 and register e of N-tile 1 in the same lane.
+  if (EPI == EPI_ROPE) {
+    const int c0 = n0 + wn * 64;
+    if (c0 + 64 <= g.n && (c0 % g.rope_head_stride) == g.rope_off) {
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        const int m = m0 + wm * 64 + mi * 32 + (lane & 31);
+        if (m >= g.m) continue;
+        const int pos = g.positions[m];
+        const bool ok = pos >= 0 && pos < g.table_len;
+        const float* cs = g.cos_t + (int64_t)(ok ? pos : 0) * 32;
+        const float* sn = g.sin_t + (int64_t)(ok ? pos : 0) * 32;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = q * 8 + (lane >> 5) * 4 + e;
+            const float x0 = acc[0][mi][q * 4 + e], x1 = acc[1][mi][q * 4 + e];
+            const float c = ok ? cs[i] : __builtin_nanf(""), sv = ok ? sn[i] : __builtin_nanf("");
+            acc[0][mi][q * 4 + e] = x0 * c - x1 * sv;
+            acc[1][mi][q * 4 + e] = x1 * c + x0 * sv;
+          }
+      }
+    }
+  }
+
+  // store: lane holds row m = col index of the MFMA output, 4 runs of 4
   // consecutive n.
   const bf16* G = (const bf16*)g.gate_src + (EPI == EPI_GATE ? (int64_t)blockIdx.z * g.c_bstride : 0);
 #pragma unroll
@@ -157,10 +184,22 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = (float)gs[e] * (1.f / (1.f + __expf(-v[e])));
         }
-        bf16x4 o;
+        if (CT == 1) {
+          float* C = (float*)g.c + (int64_t)blockIdx.z * g.c_bstride;
+          *(float4*)(C + (int64_t)m * g.ldc + n) = make_float4(v[0], v[1], v[2], v[3]);
+        } else if (CT == 2) {
+          f16* C = (f16*)g.c + (int64_t)blockIdx.z * g.c_bstride;
+          f16x4 o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = (bf16)v[e];
-        *(bf16x4*)(C + (int64_t)m * g.ldc + n) = o;
+          for (int e = 0; e < 4; ++e) o[e] = (f16)v[e];
+          *(f16x4*)(C + (int64_t)m * g.ldc + n) = o;
+        } else {
+          bf16* C = (bf16*)g.c + (int64_t)blockIdx.z * g.c_bstride;
+          bf16x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = (bf16)v[e];
+          *(bf16x4*)(C + (int64_t)m * g.ldc + n) = o;
+        }
       }
     }
 }
@@ -206,19 +245,32 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
   if (g.m <= 0 || g.n <= 0 || g.batch <= 0) return hipSuccess;
   const int num_m = (g.m + BM - 1) / BM, num_n = (g.n + BN - 1) / BN;
   dim3 grid(num_m * num_n, 1, g.batch);
+  const int ct = g.c_f32 ? 1 : (g.c_f16 ? 2 : 0);
   if (g.b_kn) {
-    if (g.epilogue == EPI_GATE) return hipErrorInvalidValue;
-    gemm_bf16_kernel<true, EPI_STORE><<<grid, NT, 0, s>>>(g);
+    if (g.epilogue != EPI_STORE || ct != 0) return hipErrorInvalidValue;
+    gemm_bf16_kernel<true, EPI_STORE, 0><<<grid, NT, 0, s>>>(g);
   } else if (g.epilogue == EPI_GATE) {
-    gemm_bf16_kernel<false, EPI_GATE><<<grid, NT, 0, s>>>(g);
+    if (ct != 0) return hipErrorInvalidValue;
+    gemm_bf16_kernel<false, EPI_GATE, 0><<<grid, NT, 0, s>>>(g);
+  } else if (g.epilogue == EPI_ROPE) {
+    if (ct == 1 || g.rope_head_stride % 64 || g.rope_off % 64) return hipErrorInvalidValue;
+    if (ct == 2)
+      gemm_bf16_kernel<false, EPI_ROPE, 2><<<grid, NT, 0, s>>>(g);
+    else
+      gemm_bf16_kernel<false, EPI_ROPE, 0><<<grid, NT, 0, s>>>(g);
+  } else if (ct == 1) {
+    gemm_bf16_kernel<false, EPI_STORE, 1><<<grid, NT, 0, s>>>(g);
+  } else if (ct == 2) {
+    gemm_bf16_kernel<false, EPI_STORE, 2><<<grid, NT, 0, s>>>(g);
   } else {
-    gemm_bf16_kernel<false, EPI_STORE><<<grid, NT, 0, s>>>(g);
+    gemm_bf16_kernel<false, EPI_STORE, 0><<<grid, NT, 0, s>>>(g);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_f32(const GemmArgs& g, hipStream_t s) {
   if (g.m <= 0 || g.n <= 0 || g.batch <= 0) return hipSuccess;
+  if (g.epilogue == EPI_ROPE) return hipErrorInvalidValue;
   dim3 grid((g.n + 15) / 16, (g.m + 15) / 16, g.batch);
   if (g.epilogue == EPI_GATE)
     gemm_f32_kernel<EPI_GATE><<<grid, 256, 0, s>>>(g);

@@ -15,6 +15,9 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 #define MLA_LDS __attribute__((address_space(3)))
 
@@ -49,6 +52,10 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+// fp16 operands, same lane layouts.
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
 
 // LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane
 // L supplies the address of 4 consecutive 16-bit elements ("row" L); the result
@@ -71,6 +78,9 @@ __device__ __forceinline__ void vm_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F7
 __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
+__device__ __forceinline__ f16x8 cat8(f16x4 a, f16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 
 // ---------------------------------------------------------------- launchers
 struct GemmArgs {
@@ -78,11 +88,17 @@ struct GemmArgs {
   const void* b; int64_t ldb; int64_t b_bstride;   // B [n, k] (NT) or [k, n] (NN)
   void* c; int64_t ldc; int64_t c_bstride;         // C [m, n]
   const void* gate_src; int64_t ldg;               // epilogue "gate": c = gate_src * sigmoid(acc)
+  // epilogue "rope": columns [h*rope_head_stride + rope_off, + 64) of each head
+  // are rotated (rotate_half pairs i, i+32) at positions[m]
+  const float* cos_t; const float* sin_t; int table_len; const int32_t* positions;
+  int rope_head_stride; int rope_off;
   int m, n, k, batch;
   bool b_kn;                                       // true: B stored [k, n] (NN)
-  int epilogue;                                    // 0 store, 1 gate
+  bool c_f32;                                      // true: C stored as fp32
+  bool c_f16;                                      // true: C stored as fp16
+  int epilogue;                                    // EPI_*
 };
-enum { EPI_STORE = 0, EPI_GATE = 1 };
+enum { EPI_STORE = 0, EPI_GATE = 1, EPI_ROPE = 2 };
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmArgs& g, hipStream_t s);
@@ -93,20 +109,24 @@ struct NormRopeArgs {
   int rope_offset; int rope_slices; int rope_stride; int rope_dim;
   const float* cos_t; const float* sin_t; int table_len; const int32_t* positions;
   void* dst; int64_t dst_stride; const int32_t* slots; int64_t num_slots;
+  f16* rope_aux; int64_t rope_aux_stride;          // optional fp16 copy of the rotated slice (one slice)
 };
-hipError_t launch_norm_rope(const NormRopeArgs& a, bool bf16_io, hipStream_t s);
+// src/dst element types: bf16 -> bf16, fp32 -> fp32, or fp32 -> bf16 (src_f32 with bf16_io).
+hipError_t launch_norm_rope(const NormRopeArgs& a, bool bf16_io, hipStream_t s, bool src_f32 = false);
 
 hipError_t launch_positions(const int32_t* cu_dev, int num_seqs, int n_tokens, int32_t* pos, hipStream_t s);
 
 struct FlashArgs {
-  const void* q; const void* kv; const void* latent; int64_t latent_stride;
+  const void* q; const void* kv;
+  const void* kpe; int64_t kpe_stride;             // shared rope key: row r at kpe + r * kpe_stride
   const int32_t* cu_dev; void* out;
   int n_tokens; int heads; int nope; int rope; int dv; int kv_lora;
   float scale; int num_seqs;
 };
-// bf16 MFMA kernel (nope 128, rope 64, dv 128).  The tile plan is built from the
-// host offsets inside.
-hipError_t launch_flash_bf16(const FlashArgs& a, const int32_t* cu_host, int num_seqs, hipStream_t s);
+// MFMA kernel (nope 128, rope 64, dv 128) with bf16 or fp16 operands (q, kv,
+// kpe of that type); the output is bf16.  The tile plan is built from the host
+// offsets inside.
+hipError_t launch_flash_mfma(const FlashArgs& a, bool f16_operands, const int32_t* cu_host, int num_seqs, hipStream_t s);
 hipError_t launch_flash_f32(const FlashArgs& a, hipStream_t s);
 
 struct DecodeArgs {

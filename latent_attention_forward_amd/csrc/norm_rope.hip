@@ -13,7 +13,7 @@ namespace {
 
 constexpr int ROWS_PER_BLOCK = 4;
 
-template <typename T>
+template <typename TS, typename T>
 __global__ __launch_bounds__(64 * ROWS_PER_BLOCK) void norm_rope_kernel(NormRopeArgs a) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
@@ -24,13 +24,13 @@ __global__ __launch_bounds__(64 * ROWS_PER_BLOCK) void norm_rope_kernel(NormRope
     if (s < 0 || s >= a.num_slots) return;
     drow = s;
   }
-  const T* src = (const T*)a.src + (int64_t)row * a.src_stride;
+  const TS* src = (const TS*)a.src + (int64_t)row * a.src_stride;
   T* dst = (T*)a.dst + drow * a.dst_stride;
 
   float rinv = 1.f;
   if (a.norm_dim > 0) {
     float ss = 0.f;
-    if (sizeof(T) == 2 && (a.norm_dim & 7) == 0 && ((reinterpret_cast<uintptr_t>(src) & 15) == 0)) {
+    if (sizeof(TS) == 2 && (a.norm_dim & 7) == 0 && ((reinterpret_cast<uintptr_t>(src) & 15) == 0)) {
       for (int c = lane * 8; c < a.norm_dim; c += 64 * 8) {
         const bf16x8 v = *(const bf16x8*)(src + c);
 #pragma unroll
@@ -54,8 +54,10 @@ __global__ __launch_bounds__(64 * ROWS_PER_BLOCK) void norm_rope_kernel(NormRope
   for (int c = lane; c < a.row_width; c += 64) {
     if (in_rope(c)) continue;
     float v = to_f32(src[c]);
-    if (c < a.norm_dim) v = v * rinv * to_f32(((const T*)a.gamma)[c]);
+    if (c < a.norm_dim) v = v * rinv * to_f32(((const T*)a.gamma)[c]);   // gain has the output dtype
     dst[c] = from_f32<T>(v);
+    if (a.rope_aux && c >= a.rope_offset && c < a.rope_offset + a.rope_dim)   // unrotated shared part
+      a.rope_aux[(int64_t)row * a.rope_aux_stride + (c - a.rope_offset)] = (f16)v;
   }
   if (!do_rope) return;
   const int pos = a.positions ? a.positions[row] : 0;
@@ -75,6 +77,11 @@ __global__ __launch_bounds__(64 * ROWS_PER_BLOCK) void norm_rope_kernel(NormRope
     }
     dst[c0] = from_f32<T>(y0);
     dst[c1] = from_f32<T>(y1);
+    if (a.rope_aux) {   // fp16 copy of the rotated slice, rounded once from fp32
+      f16* aux = a.rope_aux + (int64_t)row * a.rope_aux_stride + (int64_t)s * a.rope_dim;
+      aux[i] = (f16)y0;
+      aux[i + half] = (f16)y1;
+    }
   }
 }
 
@@ -92,13 +99,15 @@ __global__ void positions_kernel(const int32_t* cu, int num_seqs, int n, int32_t
 
 }  // namespace
 
-hipError_t launch_norm_rope(const NormRopeArgs& a, bool bf16_io, hipStream_t s) {
+hipError_t launch_norm_rope(const NormRopeArgs& a, bool bf16_io, hipStream_t s, bool src_f32) {
   if (a.n_rows <= 0) return hipSuccess;
   const int blocks = (a.n_rows + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
-  if (bf16_io)
-    norm_rope_kernel<bf16><<<blocks, 64 * ROWS_PER_BLOCK, 0, s>>>(a);
+  if (bf16_io && src_f32)
+    norm_rope_kernel<float, bf16><<<blocks, 64 * ROWS_PER_BLOCK, 0, s>>>(a);
+  else if (bf16_io)
+    norm_rope_kernel<bf16, bf16><<<blocks, 64 * ROWS_PER_BLOCK, 0, s>>>(a);
   else
-    norm_rope_kernel<float><<<blocks, 64 * ROWS_PER_BLOCK, 0, s>>>(a);
+    norm_rope_kernel<float, float><<<blocks, 64 * ROWS_PER_BLOCK, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -35,5 +35,5 @@ from .mla import (  # noqa: F401
     rms_norm, yarn_get_mscale, softmax_scale, rope_inv_freq, rope_cos_sin,
     rotate_half, apply_rope, causal_varlen_attention, mla_prefill, mla_prefill_rows,
     kv_latent, gather_paged, decode_naive, decode_absorbed, prefill_latent_absorbed,
-    row_rel_error,
+    row_rel_error, bf16_excess_error,
 )

@@ -405,6 +405,21 @@ def decode_absorbed(shape, w_kv_b, q_nope, q_pe, cache, block_table, seq_lens, b
 # ----------------------------------------------------------------------------
 # Comparison metric
 # ----------------------------------------------------------------------------
+def bf16_excess_error(ref, got, rtol: float = 2.0 ** -7) -> float:
+    """max over rows of max_k (|got - ref| - rtol |ref|)_+ / RMS_k(ref): the
+    error left after allowing one bfloat16 ulp (2^-7 relative) at each element.
+    A result within atol * RMS(row) + rtol * |ref| everywhere scores <= atol.
+    NaN anywhere in ``got`` gives inf."""
+    ref = _f64(ref).reshape(-1, np.shape(ref)[-1])
+    got = _f64(got).reshape(ref.shape)
+    if not np.all(np.isfinite(got)):
+        return float("inf")
+    rms = np.sqrt(np.mean(ref * ref, axis=-1))
+    rms = np.where(rms > 0, rms, 1.0)
+    ex = np.maximum(np.abs(got - ref) - rtol * np.abs(ref), 0.0)
+    return float(np.max(np.max(ex, axis=-1) / rms))
+
+
 def row_rel_error(ref, got) -> float:
     """max over rows of max_k |got - ref| / RMS_k(ref), rows = last axis.
     NaN anywhere in ``got`` gives inf."""

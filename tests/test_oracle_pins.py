@@ -327,3 +327,16 @@ def test_planted_mistakes_are_caught(monkeypatch):
     monkeypatch.setattr(om, "rotate_half", lambda x: np.concatenate([x[..., x.shape[-1] // 2:], -x[..., :x.shape[-1] // 2]], -1))
     bad = om.mla_prefill(sh, case.w, case.x, case.cu_seqlens)["out"]
     assert not np.allclose(bad, bf, rtol=1e-6)
+
+
+# ----------------------------------------------------------------------------- comparison metrics
+def test_bf16_metrics():
+    rng = np.random.default_rng(9)
+    y = rng.standard_normal((5, 300))
+    yb = mi.bf16_round(y.astype(np.float32)).astype(np.float64)
+    assert om.bf16_excess_error(y, yb) == 0.0          # rounding to bf16 is within one ulp
+    assert 0 < om.row_rel_error(y, yb) < 2e-2
+    bad = y.copy(); bad[2, 7] += 0.1 * np.sqrt(np.mean(y[2] ** 2)) + abs(y[2, 7]) * 2 ** -7
+    assert om.bf16_excess_error(y, bad) > 2e-2
+    nan = yb.copy(); nan[0, 0] = np.nan
+    assert om.bf16_excess_error(y, nan) == float("inf") and om.row_rel_error(y, nan) == float("inf")
