@@ -1,0 +1,323 @@
+#!/usr/bin/env python3
+"""Benchmark of the MLA forward hot path on one MI355X.
+
+One step = one full MLA prefill layer (DeepSeek-V3 shape, 4096 tokens, 128
+heads, YaRN) plus one weight-absorbed decode over the paged latent cache (64
+sequences, lengths U[1024, 8192]).  Prints ONE JSON line.
+
+Metric: "MLA prefill attn TFLOP/s + absorbed decode HBM GB/s, % of MI355X
+peak".  ``value`` is the mean of the two fractions of peak, in percent:
+  prefill attention: algorithmic FLOPs 2 (d_qk + d_v) H sum_d T_d (T_d + 1) / 2
+      per launch / the attention kernel's mean launch time, against the dense
+      bf16/fp16 MFMA peak (2516.6 TFLOP/s);
+  absorbed decode: algorithmic bytes sum_b L_b (r_kv + d_rope) 2 + W_kv_b + q +
+      out + index arrays per call / the mean call time, against 8 TB/s.
+Kernel times are HIP events on the stream the kernels run on.  Between timed
+decode calls a 512 MiB buffer is overwritten so the 256 MB Infinity Cache
+cannot hold the ~380 MB decode working set.
+"""
+import argparse
+import hashlib
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MLA prefill attn TFLOP/s + absorbed decode HBM GB/s, % of MI355X peak"
+PEAK_MFMA_TFLOPS = 2516.6      # dense bf16 / fp16 MFMA, 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {"flash": "flash.hip", "decode": "decode.hip"}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--prefill", default="dsv3_prefill_4096")
+    ap.add_argument("--decode", default="dsv3_decode_64")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=["full", "prefill", "attention", "decode"], default="full",
+                    help="full: the JSON line; the others only run that part's timing loop (for profilers)")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for the CPU baseline")
+    return ap.parse_args()
+
+
+def attention_flops(shape, cu):
+    s = 0
+    for a, b in zip(cu[:-1], cu[1:]):
+        t = int(b) - int(a)
+        s += t * (t + 1) // 2
+    return 2 * (shape.qk_head_dim + shape.v_head_dim) * shape.num_heads * s
+
+
+def layer_flops(shape, n, attn):
+    H, dqk, dv, r, dr = shape.num_heads, shape.qk_head_dim, shape.v_head_dim, shape.kv_lora_rank, shape.qk_rope_dim
+    f = 0
+    if shape.q_lora_rank:
+        f += 2 * n * shape.hidden * shape.q_lora_rank + 2 * n * shape.q_lora_rank * H * dqk
+    else:
+        f += 2 * n * shape.hidden * H * dqk
+    f += 2 * n * shape.hidden * (r + dr) + 2 * n * r * H * (shape.qk_nope_dim + dv)
+    if shape.output_gate:
+        f += 2 * n * shape.hidden * H * dv
+    f += 2 * n * H * dv * shape.hidden
+    return f + attn
+
+
+def decode_bytes(shape, lens, max_blocks):
+    H, r, dr, dn, dv = shape.num_heads, shape.kv_lora_rank, shape.qk_rope_dim, shape.qk_nope_dim, shape.v_head_dim
+    B = len(lens)
+    return (int(sum(lens)) * (r + dr) * 2 + H * (dn + dv) * r * 2 + B * H * (dn + dr) * 2 + B * H * dv * 2
+            + B * max_blocks * 4 + B * 4)
+
+
+def source_hash(name):
+    p = os.path.join(ROOT, "latent_attention_forward_amd", "csrc", KERNEL_SOURCES[name])
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def traffic_for(name):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when it is missing or the kernel source changed since it was taken."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))[name]
+    except (OSError, KeyError, ValueError):
+        return None
+    if t.get("source_sha256_16") != source_hash(name):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(shape_name, dshape_name, budget):
+    """Time the float64 oracle on the host in a child process (its BLAS threads
+    are whatever the environment gives it; the count actually used is
+    reported)."""
+    code = r'''
+import json, sys, time, os
+sys.path.insert(0, %r)
+import numpy as np
+from threadpoolctl import threadpool_info
+import mla_inputs as mi
+from oracle import mla as om
+budget = %f
+sh = mi.WORKLOADS[%r]
+H = sh.num_heads
+rng = np.random.default_rng(0)
+scale = om.softmax_scale(sh)
+# prefill attention: one causal document of T tokens, all heads, grown until the budget is used
+T, tp, fp = 128, 0.0, 0
+while True:
+    q = rng.standard_normal((T, H, 192)); k = rng.standard_normal((T, H, 192)); v = rng.standard_normal((T, H, 128))
+    t0 = time.perf_counter(); om.causal_varlen_attention(q, k, v, scale, [0, T]); dt = time.perf_counter() - t0
+    tp, fp, Tp = dt, 640 * H * T * (T + 1) // 2, T
+    if dt > budget / 6 or T >= 4096:
+        break
+    T *= 2
+# absorbed decode: the first sequences of the decode workload until the budget is used
+dsh = mi.WORKLOADS[%r]
+dc = mi.make_decode_case(dsh)
+nb, bytes_, t_dec = 0, 0, 0.0
+t0 = time.perf_counter()
+while nb < len(dc.seq_lens) and time.perf_counter() - t0 < budget / 3:
+    om.decode_absorbed(dsh, dc.w_kv_b, dc.q_nope, dc.q_pe, dc.cache, dc.block_table, dc.seq_lens, dc.block_size, batch_idx=[nb])
+    nb += 1
+t_dec = time.perf_counter() - t0
+L = dc.seq_lens[:nb]
+bytes_ = int(L.sum()) * 1152 + dsh.num_heads * 256 * 512 * 2 * nb + nb * dsh.num_heads * (192 + 128) * 2
+threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+print(json.dumps({"prefill_tflops": fp / tp / 1e12, "prefill_T": Tp, "prefill_s": tp, "heads": H,
+                  "decode_gbs": bytes_ / t_dec / 1e9, "decode_seqs": nb, "decode_s": t_dec, "threads": threads,
+                  "affinity": len(os.sched_getaffinity(0))}))
+''' % (ROOT, budget, shape_name, dshape_name)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=600)
+    if r.returncode != 0:
+        raise RuntimeError("cpu baseline failed: " + r.stderr[-2000:])
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    frac = 0.5 * (d["prefill_tflops"] / PEAK_MFMA_TFLOPS + d["decode_gbs"] / PEAK_HBM_GBS) * 100
+    return {
+        "value": frac, "unit": "% of MI355X peak (same definition as value)", "cores": d["threads"],
+        "kind": "oracle",
+        "sample": (f"float64 oracle: causal attention of one {d['prefill_T']}-token document x {d['heads']} heads "
+                   f"({d['prefill_s']:.1f} s, {d['prefill_tflops'] * 1e3:.2f} GFLOP/s); absorbed decode of the "
+                   f"first {d['decode_seqs']} sequences of {dshape_name} ({d['decode_s']:.1f} s, "
+                   f"{d['decode_gbs']:.3f} GB/s); host affinity {d['affinity']} cores"),
+        "prefill_attn_tflops": d["prefill_tflops"], "decode_gbs": d["decode_gbs"],
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported by this build "
+              "(the path runs on a single MI355X; see DESIGN.md for how it would shard).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import latent_attention_forward_amd as mla
+    import mla_inputs as mi
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    mla.load_library()
+    stream = torch.cuda.current_stream()
+    tb = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(torch.bfloat16)
+
+    # ------------------------------------------------------------------ prefill inputs
+    sh = mi.WORKLOADS[args.prefill]
+    case = mi.make_prefill_case(sh)
+    cfg = mla.make_config(sh)
+    W = {k: tb(v) for k, v in case.w.items()}
+    x = tb(case.x)
+    n = case.x.shape[0]
+    cuh = case.cu_seqlens
+    cu = torch.from_numpy(cuh).to(dev)
+    maxlen = int(np.max(np.diff(cuh)))
+    cos = sin = None
+    if sh.rope.kind != "none":
+        cos, sin = mla.rope_table(cfg, maxlen, dev)
+    out = torch.empty(n, sh.hidden, dtype=torch.bfloat16, device=dev)
+    lat = torch.empty(n, sh.kv_lora_rank + sh.qk_rope_dim, dtype=torch.bfloat16, device=dev)
+    ws_p = torch.empty(mla.prefill_workspace_size(cfg, n, len(cuh) - 1), dtype=torch.uint8, device=dev)
+    del case
+
+    # ------------------------------------------------------------------ decode inputs
+    dsh = mi.WORKLOADS[args.decode]
+    dc = mi.make_decode_case(dsh)
+    dcfg = mla.make_config(dsh)
+    w_kvb, q_nope, q_pe, cache = tb(dc.w_kv_b), tb(dc.q_nope), tb(dc.q_pe), tb(dc.cache)
+    table = torch.from_numpy(dc.block_table).to(dev)
+    lens_d = torch.from_numpy(dc.seq_lens).to(dev)
+    lens_h = dc.seq_lens.copy()
+    B = len(lens_h)
+    out_d = torch.empty(B, dsh.num_heads, dsh.v_head_dim, dtype=torch.bfloat16, device=dev)
+    ws_d = torch.empty(mla.decode_workspace_size(dcfg, lens_h), dtype=torch.uint8, device=dev)
+    max_blocks = dc.block_table.shape[1]
+    del dc
+
+    def prefill():
+        mla.prefill_fwd(cfg, W, x, cu, cuh, out, latent_out=lat, rope_cos=cos, rope_sin=sin, workspace=ws_p)
+
+    def decode():
+        mla.decode_absorbed_fwd(dcfg, w_kvb, q_nope, q_pe, cache, table, lens_d, lens_h, out_d, workspace=ws_d)
+
+    def step():
+        prefill()
+        decode()
+
+    if args.mode != "full":
+        # profiler runs: only the requested part, warmup + steps launches, no JSON line
+        H = sh.num_heads
+        if args.mode == "attention":
+            g = torch.Generator(device=dev).manual_seed(0)
+            qa = torch.randn(n, H, sh.qk_head_dim, device=dev, generator=g).to(torch.float16)
+            kva = torch.randn(n, H, sh.qk_nope_dim + sh.v_head_dim, device=dev, generator=g).to(torch.float16)
+            kpe = torch.randn(n, sh.qk_rope_dim, device=dev, generator=g).to(torch.float16)
+            attn = torch.empty(n, H, sh.v_head_dim, dtype=torch.bfloat16, device=dev)
+            fn = lambda: mla.attention_prefill(cfg, qa, kva, kpe, cu, cuh, attn)
+        else:
+            fn = prefill if args.mode == "prefill" else decode
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.mode == "decode" else None
+        for i in range(args.warmup + args.steps):
+            if flush is not None:
+                flush.fill_(i & 0xff)
+            fn()
+        torch.cuda.synchronize()
+        print(f"{args.mode}: {args.warmup + args.steps} launches done", flush=True)
+        return
+
+    # ------------------------------------------------------------------ whole steps
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    pe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        pe[i][0].record(stream)
+        prefill()
+        pe[i][1].record(stream)
+        decode()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    prefill_ms = sum(a.elapsed_time(b) for a, b in pe) / args.steps
+
+    # ------------------------------------------------------------------ attention kernel alone
+    # Same kernel and launch shape as inside the layer (fp16 operands), on
+    # operands of the layer's shapes.
+    H = sh.num_heads
+    g = torch.Generator(device=dev).manual_seed(0)
+    qa = torch.randn(n, H, sh.qk_head_dim, device=dev, generator=g).to(torch.float16)
+    kva = torch.randn(n, H, sh.qk_nope_dim + sh.v_head_dim, device=dev, generator=g).to(torch.float16)
+    kpe = torch.randn(n, sh.qk_rope_dim, device=dev, generator=g).to(torch.float16)
+    attn = torch.empty(n, H, sh.v_head_dim, dtype=torch.bfloat16, device=dev)
+    for _ in range(max(2, args.warmup)):
+        mla.attention_prefill(cfg, qa, kva, kpe, cu, cuh, attn)
+    ae = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        ae[i][0].record(stream)
+        mla.attention_prefill(cfg, qa, kva, kpe, cu, cuh, attn)
+        ae[i][1].record(stream)
+    torch.cuda.synchronize()
+    attn_ms = sum(a.elapsed_time(b) for a, b in ae) / args.steps
+    del qa, kva, kpe, attn
+
+    # ------------------------------------------------------------------ decode call alone (cold Infinity Cache)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    de = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for _ in range(2):
+        decode()
+    for i in range(args.steps):
+        flush.fill_(i & 0xff)
+        de[i][0].record(stream)
+        decode()
+        de[i][1].record(stream)
+    torch.cuda.synchronize()
+    dec_ms = sum(a.elapsed_time(b) for a, b in de) / args.steps
+
+    # ------------------------------------------------------------------ figures
+    a_flops = attention_flops(sh, cuh)
+    attn_tflops = a_flops / (attn_ms * 1e-3) / 1e12
+    layer_tflops = layer_flops(sh, n, a_flops) / (prefill_ms * 1e-3) / 1e12
+    d_bytes = decode_bytes(dsh, lens_h, max_blocks)
+    dec_gbs = d_bytes / (dec_ms * 1e-3) / 1e9
+    value = 0.5 * (attn_tflops / PEAK_MFMA_TFLOPS + dec_gbs / PEAK_HBM_GBS) * 100
+
+    rec = {
+        "metric": METRIC, "value": round(value, 3), "unit": "% of MI355X peak (mean of prefill-attention MFMA and absorbed-decode HBM fractions)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) inputs, N(0,0.02) weights, bf16)",
+        "config": {"workload": f"{args.prefill} + {args.decode}", "prefill_tokens": n, "prefill_docs": len(cuh) - 1,
+                   "heads": H, "hidden": sh.hidden, "q_lora_rank": sh.q_lora_rank, "kv_lora_rank": sh.kv_lora_rank,
+                   "decode_batch": B, "decode_keys": int(lens_h.sum()), "decode_block": 64},
+        "prefill_attn_tflops": round(attn_tflops, 2), "prefill_attn_ms": round(attn_ms, 4),
+        "prefill_layer_ms": round(prefill_ms, 4), "prefill_layer_tflops": round(layer_tflops, 2),
+        "decode_ms": round(dec_ms, 4), "decode_hbm_gbs": round(dec_gbs, 1),
+        "wall_s_timed": round(t_wall, 3),
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / PEAK_MFMA_TFLOPS, 4), "traffic": traffic_for("flash"),
+                     "kernel": "flash_mfma_kernel<fp16> (prefill attention)", "flops_per_launch": a_flops},
+        "roofline_decode": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": traffic_for("decode"),
+                            "kernel": "mla_decode_absorbed_fwd (absorb GEMM + split-KV + combine + un-absorb GEMM)",
+                            "bytes_per_call": d_bytes},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(args.prefill, args.decode, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

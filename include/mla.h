@@ -61,7 +61,8 @@ typedef enum mla_status {
   MLA_ERR_HIP = 5            /* a HIP launch or copy failed                            */
 } mla_status;
 
-typedef enum mla_dtype { MLA_BF16 = 0, MLA_F32 = 1 } mla_dtype;
+/* MLA_F16 is accepted only as the operand type of mla_attention_prefill. */
+typedef enum mla_dtype { MLA_BF16 = 0, MLA_F32 = 1, MLA_F16 = 2 } mla_dtype;
 
 /* RoPE variant ("Megatron-LM MLA guide", normalization and position-encoding
  * parameters: rope or yarn; "Kimi-K3 atlas": no rotary embedding). */
@@ -185,18 +186,24 @@ mla_status mla_linear(const mla_config* cfg, const void* x, int64_t ldx, const v
                       void* y, int64_t ldy, int32_t m, int32_t n, int32_t k, void* stream);
 
 /* Causal varlen attention core of the layer (MLA step "A" above) on
- * already-projected tensors, all DEVICE, dtype = cfg.dtype:
+ * already-projected tensors, all DEVICE:
+ *   operand_dtype: type of q, kv and kpe: MLA_BF16 or MLA_F16 for a bf16
+ *          config (the prefill layer itself keeps these operands in fp16),
+ *          MLA_F32 for an fp32 config
  *   q      [N, H, d_nope + d_rope]  per head [q_nope | q_pe] (q_pe rotated)
  *   kv     [N, H, d_nope + d_v]     per head [k_nope | v]
- *   latent [N, latent_stride] whose columns [r_kv, r_kv + d_rope) hold the
- *          shared k_pe (rotated), broadcast to every head
+ *   kpe    the shared rope key (rotated), ONE head broadcast to every head:
+ *          row r at kpe + r * kpe_stride elements (for a latent-cache row
+ *          buffer [N, r_kv + d_rope]: kpe = latent + r_kv, stride r_kv + d_rope)
  *   cu_seqlens_dev / cu_seqlens_host: [num_seqs + 1] offsets (DEVICE / HOST,
  *          same values), documents attend only within themselves, causally
  *          ("Megatron-LM MLA guide", THD packing)
- *   attn   [N, H, d_v] output.  d_v != d_nope + d_rope is handled natively (no
- *          padding of v, unlike the FlashAttention adapters on the pages). */
-mla_status mla_attention_prefill(const mla_config* cfg, const void* q, const void* kv,
-                                 const void* latent, int64_t latent_stride,
+ *   attn   [N, H, d_v] output, cfg.dtype (bf16 for both bf16 operand types).
+ *          d_v != d_nope + d_rope is handled natively (no padding of v, unlike
+ *          the FlashAttention adapters on the pages).
+ *   workspace may be NULL (no scratch is needed). */
+mla_status mla_attention_prefill(const mla_config* cfg, int32_t operand_dtype, const void* q, const void* kv,
+                                 const void* kpe, int64_t kpe_stride,
                                  const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
                                  int32_t num_seqs, void* attn,
                                  void* workspace, size_t workspace_bytes, void* stream);
@@ -231,7 +238,8 @@ mla_status mla_prefill_fwd(const mla_config* cfg, const mla_weights* w, const vo
  *            token (already written to the cache by the caller)
  *   out      [B, H, d_v]: attention output before the output projection.
  *   A block id outside [0, num_blocks) makes that sequence's output NaN; cache
- *   slots past seq_lens are never read.  block_size must be a multiple of 16.
+ *   slots past seq_lens are never read.  block_size must be a power of two
+ *   >= 16.
  *   workspace: DEVICE, >= mla_decode_workspace_size(cfg, seq_lens_host, B). */
 mla_status mla_decode_absorbed_fwd(const mla_config* cfg, const void* w_kv_b,
                                    const void* q_nope, const void* q_pe,

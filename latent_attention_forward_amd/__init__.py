@@ -14,7 +14,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmla.so")
 
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_MISALIGNED, MLA_ERR_HIP = range(6)
-MLA_BF16, MLA_F32 = 0, 1
+MLA_BF16, MLA_F32, MLA_F16 = 0, 1, 2
 MLA_ROPE_NONE, MLA_ROPE_PLAIN, MLA_ROPE_YARN = 0, 1, 2
 
 
@@ -59,7 +59,7 @@ _SIGNATURES = {
     "mla_latent_norm_rope": (_I32, [_CFG, _P, _I64, _I32, _I32, _I32, _P, _I32, _I32, _I32, _P, _P, _I32, _P,
                                     _P, _I64, _P, _I64, _P]),
     "mla_linear": (_I32, [_CFG, _P, _I64, _P, _P, _I64, _I32, _I32, _I32, _P]),
-    "mla_attention_prefill": (_I32, [_CFG, _P, _P, _P, _I64, _P, _P, _I32, _P, _P, _SZ, _P]),
+    "mla_attention_prefill": (_I32, [_CFG, _I32, _P, _P, _P, _I64, _P, _P, _I32, _P, _P, _SZ, _P]),
     "mla_prefill_fwd": (_I32, [_CFG, ctypes.POINTER(MlaWeights), _P, _P, _P, _I32, _P, _P, _P, _I32, _P, _P,
                                _P, _SZ, _P]),
     "mla_decode_absorbed_fwd": (_I32, [_CFG, _P, _P, _P, _P, _I32, _I32, _P, _I32, _P, _P, _I32, _P, _P, _SZ, _P]),
@@ -198,12 +198,18 @@ def linear(cfg: MlaConfig, x, w, y, stream=None):
                           _stream(stream)), "mla_linear")
 
 
-def attention_prefill(cfg: MlaConfig, q, kv, latent, cu_seqlens_dev, cu_seqlens_host: Sequence[int], attn,
-                      stream=None):
+def attention_prefill(cfg: MlaConfig, q, kv, kpe, cu_seqlens_dev, cu_seqlens_host: Sequence[int], attn,
+                      kpe_stride: Optional[int] = None, stream=None):
+    """Attention core.  ``kpe`` is a view whose row r is the shared rope key of
+    token r (e.g. ``latent[:, r_kv:]``); its dtype (bf16 / fp16 / fp32) sets
+    the operand type."""
     import numpy as np
+    import torch
     lib = load_library()
     cuh = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int32))
-    _check(lib.mla_attention_prefill(ctypes.byref(cfg), _ptr(q), _ptr(kv), _ptr(latent), latent.stride(0),
+    op = {torch.bfloat16: MLA_BF16, torch.float16: MLA_F16, torch.float32: MLA_F32}[q.dtype]
+    _check(lib.mla_attention_prefill(ctypes.byref(cfg), op, _ptr(q), _ptr(kv), _ptr(kpe),
+                                     kpe.stride(0) if kpe_stride is None else kpe_stride,
                                      _ptr(cu_seqlens_dev), cuh.ctypes.data, len(cuh) - 1, _ptr(attn), None, 0,
                                      _stream(stream)), "mla_attention_prefill")
 

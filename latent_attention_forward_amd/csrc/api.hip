@@ -47,7 +47,7 @@ mla_status check_config(const mla_config* c) {
       c->v_head_dim <= 0 || c->qk_rope_dim < 0 || c->q_lora_rank < 0)
     return fail(MLA_ERR_INVALID_ARG, "dimensions must be positive (q_lora_rank, qk_rope_dim may be 0)");
   if (c->qk_rope_dim % 2) return fail(MLA_ERR_INVALID_ARG, "qk_rope_dim must be even");
-  if (c->dtype != MLA_BF16 && c->dtype != MLA_F32) return fail(MLA_ERR_INVALID_ARG, "unknown dtype %d", c->dtype);
+  if (c->dtype != MLA_BF16 && c->dtype != MLA_F32) return fail(MLA_ERR_INVALID_ARG, "config dtype must be bf16 or fp32, got %d", c->dtype);
   if (c->rope_kind < MLA_ROPE_NONE || c->rope_kind > MLA_ROPE_YARN)
     return fail(MLA_ERR_INVALID_ARG, "unknown rope_kind %d", c->rope_kind);
   if (c->rope_kind != MLA_ROPE_NONE) {
@@ -156,7 +156,7 @@ mla_status check_cu(const int32_t* cu_host, int num_seqs, int* n_out) {
 constexpr int kDecodeTargetGroups = 256;   // one wave of workgroups on 256 CUs
 
 struct DecodePlan {
-  int chunk, max_chunks;
+  int chunk, max_chunks, items;
   size_t qt, olat, part_o, part_ml, total;
 };
 
@@ -168,18 +168,27 @@ DecodePlan decode_plan(const mla_config* c, const int32_t* lens, int batch, int6
     total += L;
     maxl = std::max(maxl, L);
   }
-  int chunk = 32 * (int)std::max<int64_t>(1, (total + 32LL * kDecodeTargetGroups - 1) / (32LL * kDecodeTargetGroups));
+  // Smallest multiple of the 64-key tile that keeps the workgroup count within
+  // one wave of workgroups; capped so that a chunk spans at most
+  // kDecodeMaxChunkBlocks - 2 cache blocks of the smallest allowed size (16).
+  constexpr int kTile = 64, kMaxChunk = ((kDecodeMaxChunkBlocks - 2) * 16) / kTile * kTile;
+  int chunk = kTile * (int)std::max<int64_t>(1, (total + (int64_t)kTile * kDecodeTargetGroups - 1) /
+                                                   ((int64_t)kTile * kDecodeTargetGroups));
   for (;;) {
+    if (chunk >= kMaxChunk) { chunk = kMaxChunk; break; }
     int64_t groups = 0;
     for (int b = 0; b < batch; ++b) {
       const int64_t L = std::min<int64_t>(std::max(lens[b], 0), key_cap);
       groups += (L + chunk - 1) / chunk;
     }
     if (groups <= kDecodeTargetGroups || chunk >= maxl) break;
-    chunk += 32;
+    chunk += kTile;
   }
   p.chunk = chunk;
   p.max_chunks = (int)((maxl + chunk - 1) / chunk);
+  int64_t items = 0;
+  for (int b = 0; b < batch; ++b) items += (std::min<int64_t>(std::max(lens[b], 0), key_cap) + chunk - 1) / chunk;
+  p.items = (int)items;
   const int64_t H = c->num_heads, R = c->kv_lora_rank;
   size_t off = 0;
   p.qt = off; off += align256((size_t)batch * H * R * 2);
@@ -331,23 +340,26 @@ static mla_status attention_impl(const mla_config* cfg, const void* q, const voi
   return MLA_OK;
 }
 
-mla_status mla_attention_prefill(const mla_config* cfg, const void* q, const void* kv, const void* latent,
-                                 int64_t latent_stride, const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
-                                 int32_t num_seqs, void* attn, void* workspace, size_t workspace_bytes, void* stream) {
+mla_status mla_attention_prefill(const mla_config* cfg, int32_t operand_dtype, const void* q, const void* kv,
+                                 const void* kpe, int64_t kpe_stride, const int32_t* cu_seqlens_dev,
+                                 const int32_t* cu_seqlens_host, int32_t num_seqs, void* attn, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
   (void)workspace; (void)workspace_bytes;
   mla_status s = check_config(cfg);
   if (s != MLA_OK) return s;
   if ((s = check_supported(cfg)) != MLA_OK) return s;
+  const bool ok_type = cfg->dtype == MLA_BF16 ? (operand_dtype == MLA_BF16 || operand_dtype == MLA_F16)
+                                              : operand_dtype == MLA_F32;
+  if (!ok_type) return fail(MLA_ERR_INVALID_ARG, "operand_dtype %d does not match the config dtype", operand_dtype);
   int n = 0;
   if ((s = check_cu(cu_seqlens_host, num_seqs, &n)) != MLA_OK) return s;
   if (n == 0) return ok();
-  if (!q || !kv || !latent || !cu_seqlens_dev || !attn) return fail(MLA_ERR_INVALID_ARG, "q, kv, latent, cu_seqlens_dev and attn are required");
-  if (latent_stride < cfg->kv_lora_rank + cfg->qk_rope_dim) return fail(MLA_ERR_INVALID_ARG, "latent_stride too small");
-  if (cfg->dtype == MLA_BF16 && (!aligned16(q) || !aligned16(kv) || !aligned16(latent) || !aligned16(attn) || latent_stride % 8))
-    return fail(MLA_ERR_MISALIGNED, "bf16 attention needs 16-byte aligned tensors and latent_stride % 8 == 0");
-  const void* kpe = (const char*)latent + (size_t)cfg->kv_lora_rank * elem_size(cfg);
-  s = attention_impl(cfg, q, kv, kpe, latent_stride, false, cu_seqlens_dev, cu_seqlens_host, num_seqs, n, attn,
-                     (hipStream_t)stream);
+  if (!q || !kv || !kpe || !cu_seqlens_dev || !attn) return fail(MLA_ERR_INVALID_ARG, "q, kv, kpe, cu_seqlens_dev and attn are required");
+  if (kpe_stride < cfg->qk_rope_dim) return fail(MLA_ERR_INVALID_ARG, "kpe_stride < d_rope");
+  if (cfg->dtype == MLA_BF16 && (!aligned16(q) || !aligned16(kv) || !aligned16(kpe) || !aligned16(attn) || kpe_stride % 8))
+    return fail(MLA_ERR_MISALIGNED, "bf16 attention needs 16-byte aligned tensors and kpe_stride % 8 == 0");
+  s = attention_impl(cfg, q, kv, kpe, kpe_stride, operand_dtype == MLA_F16, cu_seqlens_dev, cu_seqlens_host,
+                     num_seqs, n, attn, (hipStream_t)stream);
   return s == MLA_OK ? ok() : s;
 }
 
@@ -488,7 +500,8 @@ mla_status mla_decode_absorbed_fwd(const mla_config* cfg, const void* w_kv_b, co
   if (!w_kv_b || !q_nope || !q_pe || !kv_cache || !block_table || !seq_lens_dev || !seq_lens_host || !out)
     return fail(MLA_ERR_INVALID_ARG, "all tensors are required");
   if (num_blocks <= 0 || max_blocks <= 0) return fail(MLA_ERR_INVALID_ARG, "num_blocks and max_blocks must be > 0");
-  if (block_size <= 0 || block_size % 16) return fail(MLA_ERR_INVALID_ARG, "block_size must be a positive multiple of 16");
+  if (block_size < 16 || (block_size & (block_size - 1)))
+    return fail(MLA_ERR_INVALID_ARG, "block_size must be a power of two >= 16");
   for (int b = 0; b < batch; ++b)
     if (seq_lens_host[b] <= 0 || (int64_t)seq_lens_host[b] > (int64_t)max_blocks * block_size)
       return fail(MLA_ERR_INVALID_ARG, "seq_lens[%d] = %d outside [1, max_blocks * block_size]", b, seq_lens_host[b]);
@@ -515,9 +528,12 @@ mla_status mla_decode_absorbed_fwd(const mla_config* cfg, const void* w_kv_b, co
   }
   DecodeArgs d{};
   d.qt = qt; d.q_pe = (const bf16*)q_pe; d.cache = (const bf16*)kv_cache; d.block_table = block_table;
-  d.max_blocks = max_blocks; d.num_blocks = num_blocks; d.block_size = block_size; d.seq_lens = seq_lens_dev;
+  int lbs = 0;
+  while ((1 << lbs) < block_size) ++lbs;
+  d.max_blocks = max_blocks; d.num_blocks = num_blocks; d.log2_block = lbs; d.seq_lens = seq_lens_dev;
   d.part_o = (float*)(ws + P.part_o); d.part_ml = (float*)(ws + P.part_ml); d.o_lat = olat;
-  d.batch = batch; d.heads = H; d.chunk = P.chunk; d.max_chunks = P.max_chunks; d.scale = scale_of(cfg);
+  d.batch = batch; d.heads = H; d.chunk = P.chunk; d.max_chunks = P.max_chunks; d.num_items = P.items;
+  d.scale = scale_of(cfg);
   if ((e = launch_decode_split(d, st)) != hipSuccess) return hip_fail(e, "decode split");
   if ((e = launch_decode_combine(d, st)) != hipSuccess) return hip_fail(e, "decode combine");
   // un-absorb W_UV: out[b, h, :] = W_kv_b[h*(dn+dv) + dn : +dv, :] . o_lat[b, h, :]

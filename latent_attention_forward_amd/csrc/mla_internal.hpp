@@ -74,6 +74,14 @@ __device__ __forceinline__ void lds_dma16(const void* gsrc, void* lds_base) {
   __builtin_amdgcn_global_load_lds(gsrc, (MLA_LDS void*)(lds_base), 16, 0, 0);
 }
 __device__ __forceinline__ void vm_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+// Wait until at most N vector-memory instructions are outstanding (gfx9
+// s_waitcnt encoding: vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt left at
+// their maxima).  Loads complete in issue order, so this waits for all but the
+// N most recent.
+template <int N> __device__ __forceinline__ void vm_wait_keep() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
 
 __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -129,16 +137,20 @@ struct FlashArgs {
 hipError_t launch_flash_mfma(const FlashArgs& a, bool f16_operands, const int32_t* cu_host, int num_seqs, hipStream_t s);
 hipError_t launch_flash_f32(const FlashArgs& a, hipStream_t s);
 
+// Most paged-cache blocks one decode chunk may span (its block ids are staged in LDS).
+constexpr int kDecodeMaxChunkBlocks = 512;
+
 struct DecodeArgs {
   const bf16* qt;         // [B, H, 512] absorbed query
   const bf16* q_pe;       // [B, H, 64]
   const bf16* cache;      // [num_blocks, block_size, 576]
-  const int32_t* block_table; int max_blocks; int num_blocks; int block_size;
+  const int32_t* block_table; int max_blocks; int num_blocks; int log2_block;
   const int32_t* seq_lens;
   float* part_o;          // [B, max_chunks, H, 512]
   float* part_ml;         // [B, max_chunks, H, 2]
   bf16* o_lat;            // [B, H, 512]
   int batch; int heads; int chunk; int max_chunks;
+  int num_items;          // sum over sequences of ceil(len / chunk) (host lengths)
   float scale;
 };
 hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s);

@@ -129,7 +129,7 @@ def test_device_calls_reject_bad_arguments_before_launch(lib):
     st = g(ctypes.byref(dcfg), 4096, 4096, 4096, 4096, 10, 64, 4096, 4, 4096, lens.ctypes.data, 2, 4096, 4096, 1 << 30, None)
     assert st == mla.MLA_ERR_INVALID_ARG       # 300 > max_blocks * block_size
     st = g(ctypes.byref(dcfg), 4096, 4096, 4096, 4096, 10, 60, 4096, 4, 4096, lens.ctypes.data, 2, 4096, 4096, 1 << 30, None)
-    assert st == mla.MLA_ERR_INVALID_ARG       # block size not a multiple of 16
+    assert st == mla.MLA_ERR_INVALID_ARG       # block size not a power of two
     d2 = mla.make_config(mi.WORKLOADS["dsv3_decode_64"], num_heads=48)
     lens = np.array([100, 200], np.int32)
     st = g(ctypes.byref(d2), 4096, 4096, 4096, 4096, 10, 64, 4096, 4, 4096, lens.ctypes.data, 2, 4096, 4096, 1 << 30, None)

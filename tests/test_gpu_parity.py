@@ -168,6 +168,7 @@ def test_linear_f32(mla):
 # ----------------------------------------------------------------------------- attention core
 @pytest.mark.parametrize("lens", [[1], [200], [5, 0, 130, 64, 1, 300]])
 def test_attention_core(mla, lens):
+    """bf16 operands from a latent-cache buffer (the public attention entry point)."""
     _say(f"case: attention core lens={lens}")
     sh = mi.WORKLOADS["dsv3_prefill_4096"].replace(num_heads=3)
     rng = np.random.default_rng(len(lens))
@@ -178,12 +179,34 @@ def test_attention_core(mla, lens):
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     cfg = mla.make_config(sh)
     attn = torch.full((n, 3, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
-    mla.attention_prefill(cfg, dev(q, torch.bfloat16), dev(kv, torch.bfloat16), dev(lat, torch.bfloat16),
+    tl = dev(lat, torch.bfloat16)
+    mla.attention_prefill(cfg, dev(q, torch.bfloat16), dev(kv, torch.bfloat16), tl[:, 512:],
                           torch.from_numpy(cu).to(DEV), cu, attn)
     torch.cuda.synchronize()
     k = np.concatenate([kv[..., :128], np.broadcast_to(lat[:, None, 512:], (n, 3, 64))], -1)
     ref = om.causal_varlen_attention(q, k, kv[..., 128:], om.softmax_scale(sh), cu)
     bf16_check(ref.reshape(n * 3, 128), attn.float().cpu().numpy().reshape(n * 3, 128), "attn")
+
+
+def test_attention_core_fp16_operands(mla):
+    """fp16 operands (as inside the prefill layer), with a dense k_pe buffer."""
+    _say("case: attention core fp16 operands")
+    sh = mi.WORKLOADS["kimi_gated_varlen_8192"].replace(num_heads=2)
+    lens = [257, 3, 64]
+    rng = np.random.default_rng(3)
+    n = sum(lens)
+    f16 = lambda a: np.asarray(a, np.float16).astype(np.float32)
+    q = f16(rng.standard_normal((n, 2, 192)))
+    kv = f16(rng.standard_normal((n, 2, 256)))
+    kpe = f16(rng.standard_normal((n, 64)))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    attn = torch.full((n, 2, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
+    mla.attention_prefill(mla.make_config(sh), dev(q, torch.float16), dev(kv, torch.float16), dev(kpe, torch.float16),
+                          torch.from_numpy(cu).to(DEV), cu, attn)
+    torch.cuda.synchronize()
+    k = np.concatenate([kv[..., :128], np.broadcast_to(kpe[:, None, :], (n, 2, 64))], -1)
+    ref = om.causal_varlen_attention(q, k, kv[..., 128:], om.softmax_scale(sh), cu)
+    bf16_check(ref.reshape(n * 2, 128), attn.float().cpu().numpy().reshape(n * 2, 128), "attn fp16 operands")
 
 
 # ----------------------------------------------------------------------------- full prefill, small shapes
