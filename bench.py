@@ -13,8 +13,10 @@ peak".  ``value`` is the mean of the two fractions of peak, in percent:
   absorbed decode: algorithmic bytes sum_b L_b (r_kv + d_rope) 2 + W_kv_b + q +
       out + index arrays per call / the mean call time, against 8 TB/s.
 Kernel times are HIP events on the stream the kernels run on.  Between timed
-decode calls a 512 MiB buffer is overwritten so the 256 MB Infinity Cache
-cannot hold the ~380 MB decode working set.
+decode calls a 512 MiB buffer is read, so the 256 MB Infinity Cache holds none
+of the ~370 MB decode working set (a read leaves clean lines; overwriting the
+buffer instead would charge the decode for writing back 256 MB of dirty
+lines).
 """
 import argparse
 import hashlib
@@ -225,10 +227,11 @@ def main():
             fn = lambda: mla.attention_prefill(cfg, qa, kva, kpe, cu, cuh, attn)
         else:
             fn = prefill if args.mode == "prefill" else decode
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.mode == "decode" else None
+        flush = torch.zeros(512 << 20, dtype=torch.uint8, device=dev) if args.mode == "decode" else None
+        sink = torch.zeros(1, dtype=torch.int64, device=dev)
         for i in range(args.warmup + args.steps):
             if flush is not None:
-                flush.fill_(i & 0xff)
+                sink.copy_(flush.view(torch.int64).sum())
             fn()
         torch.cuda.synchronize()
         print(f"{args.mode}: {args.warmup + args.steps} launches done", flush=True)
@@ -274,12 +277,13 @@ def main():
     del qa, kva, kpe, attn
 
     # ------------------------------------------------------------------ decode call alone (cold Infinity Cache)
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = torch.zeros(512 << 20, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int64, device=dev)
     de = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for _ in range(2):
         decode()
     for i in range(args.steps):
-        flush.fill_(i & 0xff)
+        sink.copy_(flush.view(torch.int64).sum())
         de[i][0].record(stream)
         decode()
         de[i][1].record(stream)

@@ -170,20 +170,24 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
 #pragma unroll
   for (int q = 0; q < 2; ++q) base_t[q] = rt * RC + ((((q * 4 + (grp & 1) * 2 + xb) ^ swt)) << 3) + 4 * (L4 & 1);
 
-  // Tile loads: with blocks of >= 32 tokens a 32-key tile lies in one block,
-  // so its rows are contiguous and only the block id is looked up.
+  // Tile loads.  A full tile in one block (blocks of >= 32 tokens) is 32
+  // contiguous cache rows, so each lane's BPW source offsets are fixed for the
+  // whole chunk.  The chunk's last, partial tile and blocks of 16 tokens take
+  // the per-row path (rows past the chunk are clamped to its first key, whose
+  // probability is masked to 0).
+  int doff[BPW];
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    const int P = (wave + NW * i) * 64 + lane;
+    const int r = P / CCH, pc = P - r * CCH;
+    doff[i] = r * RC + ((pc ^ csw(r)) << 3);
+  }
   auto issue_tile = [&](int t, int buf) {
     const int kb = k0 + t * DKT;
-    if (lbs >= 5) {
-      const int64_t base = ((int64_t)sBlk[(kb >> lbs) - blk0] << lbs) + (kb & bmask);
-#pragma unroll 1
-      for (int i = 0; i < BPW; ++i) {
-        const int blk = wave + NW * i;
-        const int P = blk * 64 + lane;
-        const int r = P / CCH, pc = P - r * CCH;
-        const int rr = (kb + r < k1) ? r : 0;             // clamped rows are masked out
-        lds_dma16(a.cache + (base + rr) * RC + ((pc ^ csw(r)) << 3), &sC[buf][blk * 512]);
-      }
+    if (lbs >= 5 && kb + DKT <= k1) {
+      const bf16* tb = a.cache + (((int64_t)sBlk[(kb >> lbs) - blk0] << lbs) + (kb & bmask)) * RC;
+#pragma unroll
+      for (int i = 0; i < BPW; ++i) lds_dma16(tb + doff[i], &sC[buf][(wave + NW * i) * 512]);
     } else {
 #pragma unroll 1
       for (int i = 0; i < BPW; ++i) {
@@ -220,7 +224,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
   for (int t = 0; t < NBUF - 1; ++t)
     if (t < nt) issue_tile(t, t);
   wait_tile(min(NBUF - 2, nt - 1));
-  __syncthreads();
+  wg_barrier();
   for (int t = 0; t < nt; ++t) {
     const int buf = t % NBUF;
     const int kb = k0 + t * DKT;
@@ -301,7 +305,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
     }
     // tile t + 1 must have landed; newer tiles may still be in flight
     wait_tile(min(NBUF - 2, nt - 2 - t));
-    __syncthreads();
+    wg_barrier();
   }
 
   if (exact_path) {

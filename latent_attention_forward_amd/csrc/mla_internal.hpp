@@ -83,6 +83,13 @@ template <int N> __device__ __forceinline__ void vm_wait_keep() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
+// Workgroup barrier without the release fence of __syncthreads() (which makes
+// the compiler wait for every outstanding memory operation, in-flight LDS DMA
+// included).  Callers wait for their own DMA explicitly and consume every LDS
+// read before the barrier; the asm memory clobber keeps memory operations from
+// moving across it.
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
