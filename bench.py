@@ -34,7 +34,10 @@ METRIC = "MLA prefill attn TFLOP/s + absorbed decode HBM GB/s, % of MI355X peak"
 PEAK_MFMA_TFLOPS = 2516.6      # dense bf16 / fp16 MFMA, 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = {"flash": "flash.hip", "decode": "decode.hip"}
+COPY_BYTES = 256 << 20
+# sources whose change invalidates a committed counter figure
+KERNEL_SOURCES = {"flash": ["flash.hip", "mla_internal.hpp"],
+                  "decode": ["decode.hip", "gemm.hip", "api.hip", "mla_internal.hpp"]}
 
 
 def parse():
@@ -45,7 +48,7 @@ def parse():
     ap.add_argument("--prefill", default="dsv3_prefill_4096")
     ap.add_argument("--decode", default="dsv3_decode_64")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["full", "prefill", "attention", "decode"], default="full",
+    ap.add_argument("--mode", choices=["full", "prefill", "attention", "decode", "copy"], default="full",
                     help="full: the JSON line; the others only run that part's timing loop (for profilers)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for the CPU baseline")
     return ap.parse_args()
@@ -81,8 +84,10 @@ def decode_bytes(shape, lens, max_blocks):
 
 
 def source_hash(name):
-    p = os.path.join(ROOT, "latent_attention_forward_amd", "csrc", KERNEL_SOURCES[name])
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[name]:
+        h.update(open(os.path.join(ROOT, "latent_attention_forward_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_for(name):
@@ -225,6 +230,11 @@ def main():
             kpe = torch.randn(n, sh.qk_rope_dim, device=dev, generator=g).to(torch.float16)
             attn = torch.empty(n, H, sh.v_head_dim, dtype=torch.bfloat16, device=dev)
             fn = lambda: mla.attention_prefill(cfg, qa, kva, kpe, cu, cuh, attn)
+        elif args.mode == "copy":
+            # known-size device copy: calibrates the FETCH_SIZE / WRITE_SIZE counters
+            src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
+            dst = torch.empty_like(src)
+            fn = lambda: dst.copy_(src)
         else:
             fn = prefill if args.mode == "prefill" else decode
         flush = torch.zeros(512 << 20, dtype=torch.uint8, device=dev) if args.mode == "decode" else None

@@ -34,7 +34,11 @@
  *     (MLA_ERR_MISALIGNED otherwise).
  *   - Dtypes: cfg.dtype MLA_BF16 (bf16 storage, fp32 accumulation and fp32
  *     softmax/norm arithmetic) or MLA_F32 (fp32 everywhere).  Norm gains use the
- *     weight dtype; RoPE tables are fp32; index arrays are int32.
+ *     weight dtype; RoPE tables are fp32; index arrays are int32.  Inside the
+ *     bf16 prefill layer the attention operands (q, kv, the shared k_pe) are
+ *     kept in the workspace as fp16, which has three more mantissa bits than
+ *     bf16 and ample range for them; everything the caller passes or receives
+ *     stays bf16.
  *   - Shapes supported by the bf16 kernels: d_nope = 128, d_rope = 64,
  *     d_v = 128, r_kv = 512 (the DeepSeek-V3 / Kimi head shape); other shapes
  *     return MLA_ERR_UNSUPPORTED for bf16.  The fp32 kernels take any

@@ -318,15 +318,64 @@ def test_megatron_unit_test_config_shapes_and_identity():
 
 
 # ----------------------------------------------------------------------------- planted mistakes
-def test_planted_mistakes_are_caught(monkeypatch):
-    """A wrong sign in rotate_half, or a transposed kv_b split, must break the
-    brute-force or identity pins (checks that the pins have teeth)."""
-    sh = tiny_shape()
-    case = mi.make_prefill_case(sh, doc_lengths=[5])
+def _mask_one_ahead(q, k, v, scale, cu_seqlens, rows=None):
+    """Mutant attention: every query also sees the next key of its document."""
+    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    out = np.empty(q.shape[:2] + (v.shape[-1],))
+    cu = np.asarray(cu_seqlens)
+    for d in range(len(cu) - 1):
+        a, b = int(cu[d]), int(cu[d + 1])
+        for t in range(a, b):
+            e = min(t + 2, b)
+            s = scale * np.einsum("hd,lhd->hl", q[t], k[a:e])
+            p = np.exp(s - s.max(-1, keepdims=True))
+            out[t] = np.einsum("hl,lhd->hd", p / p.sum(-1, keepdims=True), v[a:e])
+    return out
+
+
+_PLANTED = {
+    # wrong sign in rotate_half
+    "rope_sign": ("rotate_half", lambda orig: (lambda x: np.concatenate(
+        [x[..., x.shape[-1] // 2:], -x[..., :x.shape[-1] // 2]], -1))),
+    # RMSNorm divides by the root of the sum instead of the mean
+    "rmsnorm_sum": ("rms_norm", lambda orig: (lambda x, g, eps: orig(x, g, eps) / np.sqrt(x.shape[-1]))),
+    # the shared rope key dropped from the scores (cos = sin = 0 zeroes q_pe)
+    "rope_term_dropped": ("apply_rope", lambda orig: (lambda x, c, s: 0.0 * x)),
+    # causal mask off by one
+    "mask_off_by_one": ("causal_varlen_attention", lambda orig: _mask_one_ahead),
+    # softmax scale inverted
+    "scale_inverted": ("softmax_scale", lambda orig: (lambda sh: 1.0 / orig(sh))),
+}
+
+
+@pytest.mark.parametrize("mistake", sorted(_PLANTED))
+def test_planted_mistakes_are_caught(monkeypatch, mistake):
+    """Each plausible mistake planted in the oracle (on the CPU) makes it
+    disagree with the scalar brute force, so the brute-force pin has teeth.
+    The unmutated oracle agrees with it (checked first)."""
+    sh = tiny_shape(num_docs=2, total_tokens=7)
+    case = mi.make_prefill_case(sh, doc_lengths=[4, 3])
     bf = np.array(brute.prefill(sh, case.w, case.x, case.cu_seqlens))
-    monkeypatch.setattr(om, "rotate_half", lambda x: np.concatenate([x[..., x.shape[-1] // 2:], -x[..., :x.shape[-1] // 2]], -1))
+    good = om.mla_prefill(sh, case.w, case.x, case.cu_seqlens)["out"]
+    assert np.allclose(good, bf, rtol=1e-11, atol=1e-13)
+    name, make = _PLANTED[mistake]
+    monkeypatch.setattr(om, name, make(getattr(om, name)))
     bad = om.mla_prefill(sh, case.w, case.x, case.cu_seqlens)["out"]
-    assert not np.allclose(bad, bf, rtol=1e-6)
+    assert not np.allclose(bad, bf, rtol=1e-6, atol=1e-9)
+
+
+def test_planted_kv_split_swap_is_caught(monkeypatch):
+    """Taking W_UK from the v rows of kv_b (and W_UV from the k_nope rows)
+    makes the absorbed decode disagree with the naive decode, which splits the
+    decompressed kv itself."""
+    sh = mi.WORKLOADS["dsv3_decode_64"].replace(num_heads=2)
+    dc = mi.make_decode_case(sh, batch=2, len_lo=3, len_hi=40, block_size=16)
+    args = (sh, dc.w_kv_b, dc.q_nope, dc.q_pe, dc.cache, dc.block_table, dc.seq_lens, 16)
+    n = om.decode_naive(*args)
+    assert np.allclose(om.decode_absorbed(*args), n, rtol=1e-10, atol=1e-12)
+    orig = om._split_kv_b
+    monkeypatch.setattr(om, "_split_kv_b", lambda shape, w: orig(shape, w)[::-1])
+    assert not np.allclose(om.decode_absorbed(*args), n, rtol=1e-6, atol=1e-9)
 
 
 # ----------------------------------------------------------------------------- comparison metrics
