@@ -330,6 +330,11 @@ mla_status mla_linear(const mla_config* cfg, const void* x, int64_t ldx, const v
 static mla_status attention_impl(const mla_config* cfg, const void* q, const void* kv, const void* kpe,
                                  int64_t kpe_stride, bool f16_operands, const int32_t* cu_dev,
                                  const int32_t* cu_host, int num_seqs, int n, void* attn, hipStream_t st) {
+  // the MFMA kernel addresses the 64 key rows of a tile with 32-bit byte offsets
+  if (cfg->dtype == MLA_BF16 &&
+      (64 * kpe_stride * 2 >= ((int64_t)1 << 31) ||
+       64 * (int64_t)cfg->num_heads * (cfg->qk_nope_dim + cfg->v_head_dim) * 2 >= ((int64_t)1 << 31)))
+    return fail(MLA_ERR_UNSUPPORTED, "64 rows of kv or kpe must span less than 2 GiB");
   FlashArgs f{};
   f.q = q; f.kv = kv; f.kpe = kpe; f.kpe_stride = kpe_stride; f.cu_dev = cu_dev; f.out = attn;
   f.n_tokens = n; f.heads = cfg->num_heads; f.nope = cfg->qk_nope_dim; f.rope = cfg->qk_rope_dim;

@@ -3,22 +3,31 @@
 // One 256-thread workgroup computes 128 query rows of one head of one packed
 // document; each of its 4 waves owns 32 query rows.  Keys are walked in tiles
 // of 64 from the document start to the last query of the tile (causal).  The
-// key tile [k_nope_h (from kv) | k_pe (the one shared rope head, from the
-// latent rows)] and the value tile v_h are copied into LDS by asynchronous
-// global->LDS loads, double buffered, so tile t+1 streams in while tile t is
-// multiplied.
+// key tile [k_nope_h (from kv) | k_pe (the one shared rope head)] and the value
+// tile v_h are copied into LDS by asynchronous global->LDS loads, double
+// buffered, so tile t+1 streams in while tile t is multiplied.  Each lane's
+// source offsets inside a tile are computed once; a tile only moves two
+// uniform base pointers.
 //
-// Contractions are v_mfma_f32_32x32x16_bf16 in the transposed orientation:
+// Contractions are 32x32x16 MFMAs in the transposed orientation:
 //   S^T[key, query]  = K[key, :] . Q[query, :]      (A = K from LDS, B = Q^T from registers)
 //   O^T[dv, query]  += V^T[dv, key] . P^T[key, query] (A = V^T by LDS transpose read, B = P^T)
 // so every lane holds one query row: the softmax max / sum need only an
 // in-lane reduction plus one swap with the lane 32 away, and P^T feeds the
 // second MFMA straight from the first MFMA's registers (the key order of the
-// S^T output layout is matched by the transpose reads of V).  The online
-// softmax is fp32 with exp2 and the scale folded in; P is rounded to the
-// operand type (bf16, or fp16 inside the prefill layer) for the PV MFMA; the
-// output is normalised in fp32 and rounded once to bf16.  d_v = 128 is used
+// S^T output layout is matched by the transpose reads of V).  LDS operand
+// reads are issued several MFMAs ahead of their use.
+//
+// Softmax: fp32, exp2 with the scale folded in.  The exponent origin m is
+// moved only when a score exceeds it by more than 2^8 (in base-2 units), so
+// most tiles skip rescaling the accumulators; P = 2^(s - m) <= 256 is rounded
+// to the operand type (bf16, or fp16 inside the prefill layer) for the PV
+// MFMA.  O / l is formed in fp32 and rounded once to bf16.  d_v = 128 is used
 // as is: v is never padded to d_qk.
+//
+// Work order: the workgroups of one head are kept on one XCD (workgroup i runs
+// on XCD i mod 8), all of that head's query tiles back to back, so the causal
+// tiles that stream the same k/v rows at the same time share that XCD's L2.
 #include "mla_internal.hpp"
 
 #include <vector>
@@ -28,39 +37,70 @@ namespace mla {
 namespace {
 
 constexpr int FQ = 128, FK = 64;
-constexpr int DN = 128, DQK = 192, DV = 128;
-constexpr int KCH = DQK / 8;          // 16-byte chunks per key row (24)
-constexpr int MAX_TILES = 896;
+constexpr int DN = 128, DR = 64, DQK = 192, DV = 128;
+constexpr int MAX_TILES = 880;
+constexpr float kRescaleSlack = 8.f;  // base-2 headroom before the exponent origin moves
 
 struct TilePlan {
-  int n;
+  int n;                              // query tiles per head in this launch
+  int heads_per_xcd;                  // ceil(H / 8)
   uint32_t t[MAX_TILES];              // (document << 16) | query-tile index in the document
 };
 
 template <typename T> struct Vec;
 template <> struct Vec<bf16> { typedef bf16x8 v8; typedef bf16x4 v4; };
 template <> struct Vec<f16> { typedef f16x8 v8; typedef f16x4 v4; };
+template <int B> struct BufC { static constexpr int value = B; };
 
 template <typename V8> __device__ __forceinline__ V8 zero8() { return __builtin_bit_cast(V8, make_uint4(0, 0, 0, 0)); }
 template <typename V4, typename T> __device__ __forceinline__ V4 read_tr(const T* p) {
   return __builtin_bit_cast(V4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(p)));
 }
-// K tile [64][192]: chunk c (0..23) of key row r at c ^ (r & 7) (stays within its group of 8).
-__device__ __forceinline__ int koff(int r, int c) { return r * DQK + ((c ^ (r & 7)) << 3); }
-// V tile [64][128]: 16 B chunk of column n in key row r at (n/8) ^ ((r & 3) << 1).
-__device__ __forceinline__ int voff(int r, int n) { return r * DV + ((((n >> 3) ^ ((r & 3) << 1))) << 3) + (n & 7); }
+// acc + sum of the 8 values of v, accumulated in fp32 (two-element dot
+// products with (1, 1)): the row sum of exactly the P values the PV MFMA uses.
+__device__ __forceinline__ float sum8(f16x8 v, float acc) {
+  const f16x2 one = {(f16)1.f, (f16)1.f};
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
+  return __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
+}
+__device__ __forceinline__ float sum8(bf16x8 v, float acc) {
+  const bf16x2 one = {(bf16)1.f, (bf16)1.f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
+}
+// LDS tiles, 16-byte chunks XOR-swizzled by key row so that the rows one
+// operand read touches spread over the banks:
+//   k_nope [64][128]: chunk c (0..15) of row r at c ^ (r & 7)
+//   k_pe   [64][64]:  chunk c (0..7)  of row r at c ^ (r & 7)
+//   v      [64][128]: chunk c (0..15) of row r at c ^ ((r & 3) << 2), so the
+//                     four rows a transpose read takes land in four different
+//                     64-byte bank groups
+__device__ __forceinline__ int kn_off(int r, int c) { return r * DN + ((c ^ (r & 7)) << 3); }
+__device__ __forceinline__ int kr_off(int r, int c) { return r * DR + ((c ^ (r & 7)) << 3); }
+__device__ __forceinline__ int vsw(int r, int c) { return c ^ ((r & 3) << 2); }
+__device__ __forceinline__ int voff(int r, int n) { return r * DV + (vsw(r, n >> 3) << 3) + (n & 7); }
 
 template <typename T>
 __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashArgs a, TilePlan plan) {
   typedef typename Vec<T>::v8 V8;
   typedef typename Vec<T>::v4 V4;
-  __shared__ __attribute__((aligned(16))) T sK[2][FK * DQK];
+  __shared__ __attribute__((aligned(16))) T sKn[2][FK * DN];
+  __shared__ __attribute__((aligned(16))) T sKr[2][FK * DR];
   __shared__ __attribute__((aligned(16))) T sV[2][FK * DV];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int head = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = a.heads;
-  const uint32_t td = plan.t[blockIdx.y];
+  // workgroup -> (head, tile): XCD x = blockIdx % 8 takes heads x, x+8, ...
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int hj = slot / plan.n, ti = slot - hj * plan.n;
+  const int head = xcd + 8 * hj;
+  if (head >= H) return;
+  const uint32_t td = plan.t[ti];
   const int doc = (int)(td >> 16), tix = (int)(td & 0xffff);
   const int ds = max(0, min(a.cu_dev[doc], a.n_tokens));
   const int de = max(ds, min(a.cu_dev[doc + 1], a.n_tokens));
@@ -84,65 +124,116 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashArgs a, TilePla
   for (int ks = 0; ks < DQK / 16; ++ks)
     qreg[ks] = (my_q < q1) ? *(const V8*)(Q + my_q * q_row + head * DQK + ks * 16 + hsel * 8) : zero8<V8>();
 
-  // Tile loads go straight to LDS (16 B per lane, lane l of a wave fills the
-  // l-th 16 B of a 1 KB block).  Each LDS position is mapped back to the
-  // (key row, logical chunk) that the swizzled layout keeps there.  Keys past
-  // the last query of the tile are clamped to the tile's first key: they are
-  // masked out of the softmax (their probability is exactly 0) and are never
-  // read out of bounds.
-  auto issue_tile = [&](int t, int buf) {
+  // ---- global->LDS copies.  Lane l of a wave fills the l-th 16 bytes of a
+  // 1 KB block; each LDS position is mapped back to the (key row, logical
+  // chunk) that the swizzled layout keeps there.  Per-lane byte offsets
+  // relative to the tile's first key are fixed for the whole walk (the host
+  // bounds them to 32 bits).
+  uint32_t o_kn[4], o_kr[2], o_v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int P = (wave + 4 * i) * 64 + lane;
+    const int r = P >> 4;
+    o_kn[i] = (uint32_t)((r * kv_row + (((P & 15) ^ (r & 7)) << 3)) * sizeof(T));
+    o_v[i] = (uint32_t)((r * kv_row + DN + (vsw(r, P & 15) << 3)) * sizeof(T));
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int P = (wave + 4 * i) * 64 + lane;
+    const int r = P >> 3;
+    o_kr[i] = (uint32_t)((r * a.kpe_stride + (((P & 7) ^ (r & 7)) << 3)) * sizeof(T));
+  }
+  const T* kv_head = KV + head * (DN + DV);
+  auto issue_tile = [&](int t, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     const int kb = ds + t * FK;
+    if (kb + FK <= q1) {
+      const T* kvb = kv_head + (int64_t)kb * kv_row;
+      const T* kpb = KPE + (int64_t)kb * a.kpe_stride;
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {                       // K: 24 blocks of 64 chunks
-      const int blk = wave + 4 * i;
-      const int P = blk * 64 + lane;
-      const int r = P / KCH, pc = P - r * KCH;
-      const int c = pc ^ (r & 7);
-      const int key = (kb + r < q1) ? kb + r : kb;
-      const T* src = (c < DN / 8) ? KV + key * kv_row + head * (DN + DV) + c * 8
-                                  : KPE + key * a.kpe_stride + (c - DN / 8) * 8;
-      lds_dma16(src, &sK[buf][blk * 512]);
-    }
+      for (int i = 0; i < 4; ++i) lds_dma16_sv(kvb, o_kn[i], &sKn[buf][(wave + 4 * i) * 512]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {                       // V: 16 blocks of 64 chunks
-      const int blk = wave + 4 * i;
-      const int P = blk * 64 + lane;
-      const int r = P >> 4, pc = P & 15;
-      const int c = pc ^ ((r & 3) << 1);
-      const int key = (kb + r < q1) ? kb + r : kb;
-      lds_dma16(KV + key * kv_row + head * (DN + DV) + DN + c * 8, &sV[buf][blk * 512]);
+      for (int i = 0; i < 2; ++i) lds_dma16_sv(kpb, o_kr[i], &sKr[buf][(wave + 4 * i) * 512]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lds_dma16_sv(kvb, o_v[i], &sV[buf][(wave + 4 * i) * 512]);
+    } else {
+      // last, partial tile: keys at or past q1 read the tile's first key
+      // instead (they are masked out of the softmax, probability exactly 0)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int P = (wave + 4 * i) * 64 + lane;
+        const int r = P >> 4;
+        const int key = (kb + r < q1) ? kb + r : kb;
+        lds_dma16_raw(kv_head + (int64_t)key * kv_row + (((P & 15) ^ (r & 7)) << 3), &sKn[buf][(wave + 4 * i) * 512]);
+        lds_dma16_raw(kv_head + (int64_t)key * kv_row + DN + (vsw(r, P & 15) << 3), &sV[buf][(wave + 4 * i) * 512]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int P = (wave + 4 * i) * 64 + lane;
+        const int r = P >> 3;
+        const int key = (kb + r < q1) ? kb + r : kb;
+        lds_dma16_raw(KPE + (int64_t)key * a.kpe_stride + (((P & 7) ^ (r & 7)) << 3), &sKr[buf][(wave + 4 * i) * 512]);
+      }
     }
   };
 
   const float c2 = a.scale * kLog2e;     // scores to base-2 exponent units
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_ref = -INFINITY, l_run = 0.f;  // exponent origin (base-2 units), running sum
   f32x16 o[DV / 32];
 #pragma unroll
   for (int d = 0; d < DV / 32; ++d)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[d][e] = 0.f;
 
-  issue_tile(0, 0);
-  vm_wait_all();
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
+  // S operand i (0..23): key block mt = i & 1, k-step ks = i >> 1
+  const int krow = lane & 31;
+  auto kread = [&](int i, auto bufc) -> V8 {
+    constexpr int buf = decltype(bufc)::value;
+    const int row = (i & 1) * 32 + krow, ks = i >> 1;
+    if (ks < DN / 16) return *(const V8*)&sKn[buf][kn_off(row, (ks << 1) | hsel)];
+    return *(const V8*)&sKr[buf][kr_off(row, ((ks - DN / 16) << 1) | hsel)];
+  };
+  // PV operand i (0..15): key group j = i >> 2 (16 keys), dv block d = i & 3
+  const int grp = lane >> 4, L16 = lane & 15;
+  auto vread = [&](int i, auto bufc) -> V8 {
+    constexpr int buf = decltype(bufc)::value;
+    const int j = i >> 2, d = i & 3;
+    const int kr = (j >> 1) * 32 + (j & 1) * 16 + (grp >> 1) * 4 + (L16 >> 2);
+    const int nb = d * 32 + (grp & 1) * 16 + 4 * (L16 & 3);
+    const V4 lo = read_tr<V4>(&sV[buf][voff(kr, nb)]);
+    const V4 hi = read_tr<V4>(&sV[buf][voff(kr + 8, nb)]);
+    return cat8(lo, hi);
+  };
+  constexpr int SD = 4;   // S operand reads in flight
+  constexpr int PD = 3;   // PV operands in flight
+
+  auto step = [&](int t, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     const int kb = ds + t * FK;
-    if (t + 1 < ntiles) issue_tile(t + 1, buf ^ 1);
+    if (t + 1 < ntiles) issue_tile(t + 1, BufC<buf ^ 1>{});
     const bool active = (qw0 < q1) && (kb <= qw0 + 31);
     if (active) {
-      // ---- S^T for 64 keys (2 tiles of 32) x 32 queries
+      // ---- S^T for 64 keys (2 blocks of 32) x 32 queries, operands read SD ahead
       f32x16 s[2];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[mt][e] = 0.f;
+      V8 kf[SD];
 #pragma unroll
-        for (int ks = 0; ks < DQK / 16; ++ks) {
-          const V8 kf = *(const V8*)&sK[buf][koff(mt * 32 + (lane & 31), ks * 2 + hsel)];
-          s[mt] = mfma32(kf, qreg[ks], s[mt]);
-        }
+      for (int i = 0; i < SD; ++i) kf[i] = kread(i, bufc);
+#pragma unroll
+      for (int i = 0; i < 24; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        const V8 cur = kf[i % SD];
+        if (i + SD < 24) kf[i % SD] = kread(i + SD, bufc);
+        s[i & 1] = mfma32(cur, qreg[i >> 1], s[i & 1]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      // first PV operands, independent of the softmax
+      V8 vf[PD];
+#pragma unroll
+      for (int i = 0; i < PD; ++i) vf[i] = vread(i, bufc);
       // ---- causal mask (only tiles that reach past this wave's first query)
       if (kb + FK - 1 > qw0) {
 #pragma unroll
@@ -159,43 +250,48 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashArgs a, TilePla
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mt][e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
-      m_run = m_new;
-      const float mb = m_use * c2;
-      float psum = 0.f;
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c2;
+      if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRescaleSlack) != 0) {
+        const float m_new = fmaxf(m_ref, mx);
+        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+        m_ref = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
+      }
+      const float mb = (m_ref == -INFINITY) ? 0.f : m_ref;
       V8 pb[4];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[mt][e], c2, -mb));
-          psum += p;
-          pb[mt * 2 + (e >> 3)][e & 7] = (T)p;
-        }
-      l_run = l_run * alpha + psum;
+        for (int e = 0; e < 16; ++e)
+          pb[mt * 2 + (e >> 3)][e & 7] = (T)__builtin_amdgcn_exp2f(fmaf(s[mt][e], c2, -mb));
+      float ps0 = sum8(pb[0], 0.f), ps1 = sum8(pb[1], 0.f);
+      ps0 = sum8(pb[2], ps0);
+      ps1 = sum8(pb[3], ps1);
+      l_run += ps0 + ps1;
+      // ---- O^T += V^T P^T ; step j covers keys (j/2)*32 + (j%2)*16 + {h*4+0..3, 8+h*4+0..3}
 #pragma unroll
-      for (int d = 0; d < DV / 32; ++d)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
-      // ---- O^T += V^T P^T ; step j covers keys mt*32 + hf*16 + {h*4+0..3, 8+h*4+0..3}
-      const int grp = lane >> 4, L = lane & 15;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int kr = (j >> 1) * 32 + (j & 1) * 16 + (grp >> 1) * 4 + (L >> 2);
-#pragma unroll
-        for (int d = 0; d < DV / 32; ++d) {
-          const int nb = d * 32 + (grp & 1) * 16 + 4 * (L & 3);
-          const V4 lo = read_tr<V4>(&sV[buf][voff(kr, nb)]);
-          const V4 hi = read_tr<V4>(&sV[buf][voff(kr + 8, nb)]);
-          o[d] = mfma32(cat8(lo, hi), pb[j], o[d]);
-        }
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        const V8 vv = vf[i % PD];
+        if (i + PD < 16) vf[i % PD] = vread(i + PD, bufc);
+        o[i & 3] = mfma32(vv, pb[i >> 2], o[i & 3]);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    vm_wait_all();
-    __syncthreads();
+    if (t + 1 < ntiles) vm_wait_all();
+    wg_barrier();
+  };
+
+  issue_tile(0, BufC<0>{});
+  vm_wait_all();
+  __syncthreads();
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, BufC<0>{});
+    if (t + 1 < ntiles) step(t + 1, BufC<1>{});
   }
 
   // ---- normalise and store: lane holds query my_q, dv rows d*32 + qd*8 + h*4 + [0,4)
@@ -260,7 +356,8 @@ __global__ __launch_bounds__(64) void flash_f32_kernel(FlashArgs a) {
 }  // namespace
 
 hipError_t launch_flash_mfma(const FlashArgs& a, bool f16_operands, const int32_t* cu_host, int num_seqs, hipStream_t s) {
-  // Tile plan: every (document, 128-query tile), longest key range first.
+  // Tile plan: every (document, 128-query tile), longest key range first; each
+  // head walks the whole list on its XCD.
   struct T { int keys; uint32_t id; };
   std::vector<T> tiles;
   for (int d = 0; d < num_seqs; ++d) {
@@ -270,11 +367,14 @@ hipError_t launch_flash_mfma(const FlashArgs& a, bool f16_operands, const int32_
   }
   std::stable_sort(tiles.begin(), tiles.end(), [](const T& x, const T& y) { return x.keys > y.keys; });
   TilePlan plan;
+  plan.heads_per_xcd = (a.heads + 7) / 8;
   for (size_t base = 0; base < tiles.size(); base += MAX_TILES) {
     const int n = (int)std::min<size_t>(MAX_TILES, tiles.size() - base);
     plan.n = n;
     for (int i = 0; i < n; ++i) plan.t[i] = tiles[base + i].id;
-    dim3 grid(a.heads, n);
+    const int64_t blocks = (int64_t)8 * plan.heads_per_xcd * n;
+    if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+    dim3 grid((unsigned)blocks);
     if (f16_operands)
       flash_mfma_kernel<f16><<<grid, 256, 0, s>>>(a, plan);
     else

@@ -18,6 +18,8 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16;
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 #define MLA_LDS __attribute__((address_space(3)))
 
@@ -72,6 +74,23 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
 // across the wave.  Completion is awaited with vm_wait_all() before a barrier.
 __device__ __forceinline__ void lds_dma16(const void* gsrc, void* lds_base) {
   __builtin_amdgcn_global_load_lds(gsrc, (MLA_LDS void*)(lds_base), 16, 0, 0);
+}
+// The same copy issued from inline asm.  The compiler does not see it as an LDS
+// write, so it inserts no wait for it before later LDS reads (it would wait for
+// every outstanding copy, including ones into other buffers); the caller must
+// order the copy against the reads of its destination itself, with
+// vm_wait_all() / vm_wait_keep<N>() and a barrier.  The instruction has no
+// register result.
+__device__ __forceinline__ void lds_dma16_raw(const void* gsrc, const void* lds_base) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(MLA_LDS const void*)(lds_base));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gsrc), "s"(m) : "memory", "m0");
+}
+// As lds_dma16_raw, with the address split into a wave-uniform base (SGPR
+// pair) and a per-lane 32-bit byte offset (the SADDR form), so moving a tile
+// costs no per-lane address arithmetic.
+__device__ __forceinline__ void lds_dma16_sv(const void* base, uint32_t off_bytes, const void* lds_base) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(MLA_LDS const void*)(lds_base));
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off_bytes), "s"(base), "s"(m) : "memory", "m0");
 }
 __device__ __forceinline__ void vm_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 // Wait until at most N vector-memory instructions are outstanding (gfx9
