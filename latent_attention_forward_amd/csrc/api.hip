@@ -153,48 +153,41 @@ mla_status check_cu(const int32_t* cu_host, int num_seqs, int* n_out) {
 }
 
 // ---------------------------------------------------------------- decode plan
-constexpr int kDecodeTargetGroups = 256;   // one wave of workgroups on 256 CUs
+constexpr int kDecodeTargetGroups = 256;   // one workgroup per CU
 
 struct DecodePlan {
-  int chunk, max_chunks, items;
+  int quota, groups, max_slots;
   size_t qt, olat, part_o, part_ml, total;
 };
 
+// The keys of all sequences, one after another, are dealt to workgroups in
+// runs of `quota` keys (a multiple of 64; at most as many blocks of the
+// smallest allowed size, 16, as a workgroup can stage).  Sequence b, starting
+// at st_b in that order, collects partials in slots 0 .. (st_b + L_b - 1) /
+// quota - st_b / quota.
 DecodePlan decode_plan(const mla_config* c, const int32_t* lens, int batch, int64_t key_cap) {
   DecodePlan p{};
-  int64_t total = 0, maxl = 1;
+  int64_t total = 0;
+  for (int b = 0; b < batch; ++b) total += std::min<int64_t>(std::max(lens[b], 0), key_cap);
+  constexpr int kTile = 64, kMaxQuota = ((kDecodeMaxChunkBlocks - 2) * 16 - kTile) / kTile * kTile;
+  int64_t quota = kTile * std::max<int64_t>(1, (total + (int64_t)kTile * kDecodeTargetGroups - 1) /
+                                                   ((int64_t)kTile * kDecodeTargetGroups));
+  quota = std::min<int64_t>(quota, kMaxQuota);
+  p.quota = (int)quota;
+  p.groups = (int)((total + quota - 1) / quota);
+  int64_t st = 0, max_slots = 1;
   for (int b = 0; b < batch; ++b) {
     const int64_t L = std::min<int64_t>(std::max(lens[b], 0), key_cap);
-    total += L;
-    maxl = std::max(maxl, L);
+    if (L > 0) max_slots = std::max<int64_t>(max_slots, (st + L - 1) / quota - st / quota + 1);
+    st += L;
   }
-  // Smallest multiple of the 64-key tile that keeps the workgroup count within
-  // one wave of workgroups; capped so that a chunk spans at most
-  // kDecodeMaxChunkBlocks - 2 cache blocks of the smallest allowed size (16).
-  constexpr int kTile = 64, kMaxChunk = ((kDecodeMaxChunkBlocks - 2) * 16) / kTile * kTile;
-  int chunk = kTile * (int)std::max<int64_t>(1, (total + (int64_t)kTile * kDecodeTargetGroups - 1) /
-                                                   ((int64_t)kTile * kDecodeTargetGroups));
-  for (;;) {
-    if (chunk >= kMaxChunk) { chunk = kMaxChunk; break; }
-    int64_t groups = 0;
-    for (int b = 0; b < batch; ++b) {
-      const int64_t L = std::min<int64_t>(std::max(lens[b], 0), key_cap);
-      groups += (L + chunk - 1) / chunk;
-    }
-    if (groups <= kDecodeTargetGroups || chunk >= maxl) break;
-    chunk += kTile;
-  }
-  p.chunk = chunk;
-  p.max_chunks = (int)((maxl + chunk - 1) / chunk);
-  int64_t items = 0;
-  for (int b = 0; b < batch; ++b) items += (std::min<int64_t>(std::max(lens[b], 0), key_cap) + chunk - 1) / chunk;
-  p.items = (int)items;
+  p.max_slots = (int)max_slots;
   const int64_t H = c->num_heads, R = c->kv_lora_rank;
   size_t off = 0;
   p.qt = off; off += align256((size_t)batch * H * R * 2);
   p.olat = off; off += align256((size_t)batch * H * R * 2);
-  p.part_o = off; off += align256((size_t)batch * p.max_chunks * H * R * 4);
-  p.part_ml = off; off += align256((size_t)batch * p.max_chunks * H * 2 * 4);
+  p.part_o = off; off += align256((size_t)batch * p.max_slots * H * R * 2);
+  p.part_ml = off; off += align256((size_t)batch * p.max_slots * H * 2 * 4);
   p.total = off;
   return p;
 }
@@ -536,8 +529,8 @@ mla_status mla_decode_absorbed_fwd(const mla_config* cfg, const void* w_kv_b, co
   int lbs = 0;
   while ((1 << lbs) < block_size) ++lbs;
   d.max_blocks = max_blocks; d.num_blocks = num_blocks; d.log2_block = lbs; d.seq_lens = seq_lens_dev;
-  d.part_o = (float*)(ws + P.part_o); d.part_ml = (float*)(ws + P.part_ml); d.o_lat = olat;
-  d.batch = batch; d.heads = H; d.chunk = P.chunk; d.max_chunks = P.max_chunks; d.num_items = P.items;
+  d.part_o = (f16*)(ws + P.part_o); d.part_ml = (float*)(ws + P.part_ml); d.o_lat = olat;
+  d.batch = batch; d.heads = H; d.quota = P.quota; d.max_slots = P.max_slots; d.num_items = P.groups;
   d.scale = scale_of(cfg);
   if ((e = launch_decode_split(d, st)) != hipSuccess) return hip_fail(e, "decode split");
   if ((e = launch_decode_combine(d, st)) != hipSuccess) return hip_fail(e, "decode combine");

@@ -1,26 +1,36 @@
 // Weight-absorbed MLA decode over the paged latent cache: split-KV attention in
 // the 576-wide latent space and the log-sum-exp combine of the splits.
 //
-// Split kernel: one workgroup per (sequence, chunk of keys) computes, for every
-// head at once, the partial softmax state of its keys.  Each of its waves owns
-// 32 heads (v_mfma_f32_32x32x16_bf16, one wave per SIMD so that the 32 x 512
-// fp32 accumulator and the query operand both stay in registers).  A tile of
-// 64 cached rows [c_n (512) | k_pe' (64)] is copied into LDS once per
-// workgroup (asynchronous global->LDS loads, double buffered) and used twice:
+// Work split: the keys of all sequences, taken one sequence after another,
+// form one long sequence; workgroup g takes the keys [g R, (g+1) R) of it (R,
+// the quota, a multiple of 64 chosen so that about one workgroup per CU
+// results), cut at each sequence boundary into segments.  A cut that falls
+// inside a sequence is moved to the nearest multiple of 64 keys of that
+// sequence (both workgroups sharing it round it the same way), so every
+// workgroup gets R +- 64 keys whatever the length mix.  Segment (g, b) writes
+// its partial result to slot g - floor(start_b / R) of sequence b.
+//
+// Split kernel: for every head at once, the partial softmax state of a
+// segment's keys.  Each wave owns 32 heads (v_mfma_f32_32x32x16_bf16, one wave
+// per SIMD so that the 32 x 512 fp32 accumulator and the query operand both
+// stay in registers).  A tile of 32 cached rows [c_n (512) | k_pe' (64)] is
+// copied into LDS once per workgroup (asynchronous global->LDS loads, three
+// tiles in flight) and used twice:
 //   S^T[key, head]  = C[key, :] . Qc[head, :]        (A = C rows, B = absorbed query)
 //   O^T[dim, head] += C^T[dim, key] . P^T[key, head] (A = C^T by LDS transpose read)
 // so each cached row is read from HBM exactly once per query group.  The
 // absorbed query Qc = [W_UK^T q_nope | q_pe] stays in registers as the MFMA B
-// operand for the whole chunk.  The chunk's block ids are staged in LDS first,
-// so issuing a tile's loads never waits on a dependent global load.
+// operand for the whole segment.  The segment's block ids are staged in LDS
+// first, so issuing a tile's loads never waits on a dependent global load.
 //
-// Softmax origin: the exponent origin of each head is the max of the chunk's
-// first tile and is never moved, so the accumulators are never rescaled.
-// Later scores may exceed it by up to 64 in log2 units (probabilities up to
-// 2^64, exact in fp32 and in the bf16 exponent range).  A wave that meets a
-// larger excursion recomputes its heads for the chunk with an fp32 online
-// softmax (decode_chunk_exact) instead.  Partial outputs are unnormalised fp32
-// with the origin and the sum per head.
+// Softmax origin: the exponent origin of each head is the max of the
+// segment's first tile and is never moved, so the accumulators are never
+// rescaled.  Later scores may exceed it by up to 64 in log2 units
+// (probabilities up to 2^64, exact in fp32 and in the bf16 exponent range).  A
+// wave that meets a larger excursion recomputes its heads for the segment with
+// an fp32 online softmax (decode_chunk_exact) instead.  Partial outputs are
+// stored normalised (O / l, |O / l| <= max |c|) in fp16, with the origin and
+// the sum per head in fp32.
 #include "mla_internal.hpp"
 
 namespace mla {
@@ -40,12 +50,11 @@ __device__ __forceinline__ int csw(int r) { return ((r & 3) << 1) | ((r >> 2) & 
 // fp32 online softmax over keys [k0, k1) of sequence b for heads [h0, h0 + 32),
 // one wave, reading the cache from global memory; writes the partials.  Used
 // only by a wave whose scores left the range of its fixed exponent origin.
-__device__ __forceinline__ void decode_chunk_exact(const DecodeArgs& a, int b, int c, int h0, int k0,
-                                                             int k1) {
+__device__ __forceinline__ void decode_chunk_exact(const DecodeArgs& a, int b, int slot, int h0, int k0, int k1) {
   const int lane = threadIdx.x & 63;
   const int H = a.heads, lbs = a.log2_block, bmask = (1 << lbs) - 1;
   const float c2 = a.scale * kLog2e;
-  const int64_t part = ((int64_t)b * a.max_chunks + c) * H;
+  const int64_t part = ((int64_t)b * a.max_slots + slot) * H;
   for (int h = h0; h < h0 + 32; ++h) {
     const bf16* qt = a.qt + ((int64_t)b * H + h) * RK;
     const bf16* qp = a.q_pe + ((int64_t)b * H + h) * DRP;
@@ -72,9 +81,10 @@ __device__ __forceinline__ void decode_chunk_exact(const DecodeArgs& a, int b, i
       for (int e = 0; e < 8; ++e) acc[e] = acc[e] * al + p * (float)cr[lane * 8 + e];
       m = mn;
     }
-    float* po = a.part_o + (part + h) * RK + lane * 8;
+    f16* po = a.part_o + (part + h) * RK + lane * 8;
+    const float inv = 1.f / l;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) po[e] = acc[e];
+    for (int e = 0; e < 8; ++e) po[e] = (f16)(acc[e] * inv);
     if (lane == 0) {
       a.part_ml[(part + h) * 2 + 0] = m;
       a.part_ml[(part + h) * 2 + 1] = l;
@@ -94,38 +104,52 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = a.heads;
   const int lbs = a.log2_block, bmask = (1 << lbs) - 1;
-  // Work item blockIdx.x -> (sequence b, chunk c): items are numbered sequence
-  // by sequence, so consecutive workgroups (dealt round-robin to the XCDs)
-  // spread every sequence's chunks over all XCDs.
-  __shared__ int s_item[2];
+  // This workgroup's keys [S0, S1) of the concatenated sequence: find the
+  // first sequence that reaches past S0 (wave 0, a prefix sum of the lengths).
+  const int cap = a.max_blocks << lbs;
+  const int64_t R = a.quota;
+  const int64_t S0 = (int64_t)blockIdx.x * R, S1 = S0 + R;
+  __shared__ long long s_first[2];
   if (wave == 0) {
-    if (lane == 0) { s_item[0] = -1; s_item[1] = 0; }
-    int seen = 0;
-    const int id = blockIdx.x;
+    if (lane == 0) { s_first[0] = a.batch; s_first[1] = 0; }
+    long long seen = 0;
     for (int b0 = 0; b0 < a.batch; b0 += 64) {
       const int bb = b0 + lane;
-      int n = 0;
-      if (bb < a.batch) n = (min(a.seq_lens[bb], a.max_blocks << lbs) + a.chunk - 1) / a.chunk;
-      int incl = n;
+      const long long n = (bb < a.batch) ? (long long)max(0, min(a.seq_lens[bb], cap)) : 0;
+      long long incl = n;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
-        const int v = __shfl_up(incl, o, 64);
+        const long long v = __shfl_up(incl, o, 64);
         if (lane >= o) incl += v;
       }
-      if (id >= seen + incl - n && id < seen + incl) { s_item[0] = bb; s_item[1] = id - (seen + incl - n); }
+      if (n > 0 && seen + incl - n <= S0 && S0 < seen + incl) { s_first[0] = bb; s_first[1] = seen + incl - n; }
       seen += __shfl(incl, 63, 64);
-      if (seen > id) break;
+      if (seen > S0) break;
     }
   }
   __syncthreads();
-  const int b = s_item[0], c = s_item[1];
-  if (b < 0) return;
-  const int L = min(a.seq_lens[b], a.max_blocks << lbs);
-  const int k0 = c * a.chunk;
-  if (k0 >= L) return;
-  const int k1 = min(k0 + a.chunk, L);
+  int b = (int)s_first[0];
+  int64_t st = s_first[1];
+  for (; b < a.batch && st < S1; st += max(0, min(a.seq_lens[b], cap)), ++b) {
+  __syncthreads();                         // the previous segment is done with sBlk and the tiles
+  // Lane-dependent values are rebuilt per segment from an opaque copy of the
+  // thread id, so none of them is kept live across the segment loop.
+  int tid_s = tid;
+  asm volatile("" : "+v"(tid_s));
+  const int tid = tid_s, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int L = max(0, min(a.seq_lens[b], cap));
+  // cut points inside the sequence move to the nearest multiple of 64 keys
+  auto cut = [&](int64_t x) -> int {
+    return x <= 0 ? 0 : (x >= L ? L : (int)min<int64_t>(L, ((x + 32) >> 6) << 6));
+  };
+  const int k0 = cut(S0 - st), k1 = cut(S1 - st);
+  const int slot = (int)(blockIdx.x - st / R);
+  const int64_t part = ((int64_t)b * a.max_slots + slot) * H;
+  if (k0 >= k1) {                          // empty after the cut: weight 0 in the combine
+    for (int i = tid; i < H; i += NTH) { a.part_ml[(part + i) * 2] = -INFINITY; a.part_ml[(part + i) * 2 + 1] = 0.f; }
+    continue;
+  }
   const int nt = (k1 - k0 + DKT - 1) / DKT;
-  const int64_t part = ((int64_t)b * a.max_chunks + c) * H;
 
   // the chunk's block ids; an id outside the pool poisons this sequence's output
   const int blk0 = k0 >> lbs;
@@ -137,9 +161,9 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
     sBlk[i] = v;
   }
   if (__syncthreads_or(bad)) {
-    for (int i = tid; i < H * RK; i += NTH) a.part_o[part * RK + i] = __builtin_nanf("");
+    for (int i = tid; i < H * RK; i += NTH) a.part_o[part * RK + i] = (f16)__builtin_nanf("");
     for (int i = tid; i < H; i += NTH) { a.part_ml[(part + i) * 2] = 0.f; a.part_ml[(part + i) * 2 + 1] = __builtin_nanf(""); }
-    return;
+    continue;
   }
 
   const int hsel = lane >> 5;
@@ -154,6 +178,9 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
       qreg[ks] = (d < RK) ? *(const bf16x8*)(qt + d) : *(const bf16x8*)(qp + d - RK);
     }
   }
+  // the query must have landed before the tile copies go out: the copies are
+  // issued from inline asm and the waits inside the tile loop only track them
+  vm_wait_all();
 
   // Lane-constant parts of the swizzled LDS addresses (elements); the rest of
   // every address is a compile-time offset.
@@ -175,19 +202,21 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
   // whole chunk.  The chunk's last, partial tile and blocks of 16 tokens take
   // the per-row path (rows past the chunk are clamped to its first key, whose
   // probability is masked to 0).
-  int doff[BPW];
+  uint32_t doff[BPW];                      // byte offsets inside a tile of 32 contiguous rows
 #pragma unroll
   for (int i = 0; i < BPW; ++i) {
     const int P = (wave + NW * i) * 64 + lane;
     const int r = P / CCH, pc = P - r * CCH;
-    doff[i] = r * RC + ((pc ^ csw(r)) << 3);
+    doff[i] = (uint32_t)((r * RC + ((pc ^ csw(r)) << 3)) * 2);
   }
+  const uint32_t dst0 = lds_addr_of(&sC[0][0]) + (uint32_t)wave * 1024u;   // this wave's first block
   auto issue_tile = [&](int t, int buf) {
     const int kb = k0 + t * DKT;
+    const uint32_t dst = dst0 + (uint32_t)buf * (DKT * RC * 2);
     if (lbs >= 5 && kb + DKT <= k1) {
-      const bf16* tb = a.cache + (((int64_t)sBlk[(kb >> lbs) - blk0] << lbs) + (kb & bmask)) * RC;
+      const bf16* tb = uniform_ptr(a.cache + (((int64_t)sBlk[(kb >> lbs) - blk0] << lbs) + (kb & bmask)) * RC);
 #pragma unroll
-      for (int i = 0; i < BPW; ++i) lds_dma16(tb + doff[i], &sC[buf][(wave + NW * i) * 512]);
+      for (int i = 0; i < BPW; ++i) lds_dma16_sv_m0(tb, doff[i], dst + i * NW * 1024);
     } else {
 #pragma unroll 1
       for (int i = 0; i < BPW; ++i) {
@@ -196,7 +225,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
         const int r = P / CCH, pc = P - r * CCH;
         const int key = (kb + r < k1) ? kb + r : k0;
         const int64_t row = ((int64_t)sBlk[(key >> lbs) - blk0] << lbs) + (key & bmask);
-        lds_dma16(a.cache + row * RC + ((pc ^ csw(r)) << 3), &sC[buf][blk * 512]);
+        lds_dma16_m0(a.cache + row * RC + ((pc ^ csw(r)) << 3), dst + i * NW * 1024);
       }
     }
   };
@@ -309,40 +338,63 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
   }
 
   if (exact_path) {
-    decode_chunk_exact(a, b, c, wave * 32, k0, k1);
-    return;
+    decode_chunk_exact(a, b, slot, wave * 32, k0, k1);
+  } else {
+    // lane holds head my_h, dims d*32 + q*8 + hsel*4 + [0,4); stored as O / l in fp16
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float inv = 1.f / l_tot;
+    f16* po = a.part_o + (part + my_h) * RK;
+#pragma unroll
+    for (int d = 0; d < RK / 32; ++d)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (f16)(o[d][q * 4 + e] * inv);
+        *(f16x4*)(po + d * 32 + q * 8 + hsel * 4) = v;
+      }
+    if (hsel == 0) {
+      a.part_ml[(part + my_h) * 2 + 0] = m_ref;
+      a.part_ml[(part + my_h) * 2 + 1] = l_tot;
+    }
   }
-  // lane holds head my_h, dims d*32 + q*8 + hsel*4 + [0,4)
-  float* po = a.part_o + (part + my_h) * RK;
-#pragma unroll
-  for (int d = 0; d < RK / 32; ++d)
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      *(float4*)(po + d * 32 + q * 8 + hsel * 4) = make_float4(o[d][q * 4], o[d][q * 4 + 1], o[d][q * 4 + 2], o[d][q * 4 + 3]);
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  if (hsel == 0) {
-    a.part_ml[(part + my_h) * 2 + 0] = m_ref;
-    a.part_ml[(part + my_h) * 2 + 1] = l_tot;
   }
 }
 
-// Combine: o_lat[b, h, :] = sum_c w_c o_c / sum_c w_c l_c with w_c = 2^((m_c - M) * c2).
+// Combine: o_lat[b, h, :] = sum_s w_s l_s (O_s / l_s) / sum_s w_s l_s over the
+// sequence's slots s, with w_s = 2^((m_s - M) * c2); slots emptied by a cut
+// (l_s = 0) are skipped.
 __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int H = a.heads;
-  const int L = min(a.seq_lens[b], a.max_blocks << a.log2_block);
-  const int nch = min((L + a.chunk - 1) / a.chunk, a.max_chunks);
+  const int cap = a.max_blocks << a.log2_block;
+  // start of sequence b in the concatenated key sequence
+  __shared__ long long s_part[2];
+  long long st = 0;
+  for (int i = tid; i < b; i += 128) st += max(0, min(a.seq_lens[i], cap));
+  st = wave_sum_ll(st);
+  if ((tid & 63) == 0) s_part[tid >> 6] = st;
+  __syncthreads();
+  st = s_part[0] + s_part[1];
+  const int L = max(0, min(a.seq_lens[b], cap));
+  const int64_t R = a.quota;
+  const int nslot = L > 0 ? (int)((st + L - 1) / R - st / R + 1) : 0;
   const float c2 = a.scale * kLog2e;
   float M = -INFINITY;
-  for (int c = 0; c < nch; ++c) M = fmaxf(M, a.part_ml[(((int64_t)b * a.max_chunks + c) * H + h) * 2]);
+  for (int sl = 0; sl < nslot; ++sl) {
+    const int64_t part = ((int64_t)b * a.max_slots + sl) * H + h;
+    if (a.part_ml[part * 2 + 1] != 0.f) M = fmaxf(M, a.part_ml[part * 2]);
+  }
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float lsum = 0.f;
-  for (int c = 0; c < nch; ++c) {
-    const int64_t part = ((int64_t)b * a.max_chunks + c) * H + h;
-    const float w = __builtin_amdgcn_exp2f((a.part_ml[part * 2] - M) * c2);
-    lsum += w * a.part_ml[part * 2 + 1];
-    const float4 v = *(const float4*)(a.part_o + part * RK + tid * 4);
-    acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
+  for (int sl = 0; sl < nslot; ++sl) {
+    const int64_t part = ((int64_t)b * a.max_slots + sl) * H + h;
+    const float l = a.part_ml[part * 2 + 1];
+    if (l == 0.f) continue;
+    const float w = __builtin_amdgcn_exp2f((a.part_ml[part * 2] - M) * c2) * l;
+    lsum += w;
+    const f16x4 v = *(const f16x4*)(a.part_o + part * RK + tid * 4);
+    acc.x += w * (float)v[0]; acc.y += w * (float)v[1]; acc.z += w * (float)v[2]; acc.w += w * (float)v[3];
   }
   const float inv = 1.f / lsum;
   bf16x4 r;

@@ -37,6 +37,11 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
+__device__ __forceinline__ long long wave_sum_ll(long long v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -69,6 +74,18 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
   return __builtin_bit_cast(bf16x4, r);
 }
 
+// A pointer the caller knows to be the same in every lane, moved to SGPRs.
+template <typename T> __device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// 32-bit LDS address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)(uintptr_t)(MLA_LDS const void*)(p);
+}
+
 // Asynchronous global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4).
 // The destination of lane l is lds_base + 16 * l; lds_base must be uniform
 // across the wave.  Completion is awaited with vm_wait_all() before a barrier.
@@ -91,6 +108,16 @@ __device__ __forceinline__ void lds_dma16_raw(const void* gsrc, const void* lds_
 __device__ __forceinline__ void lds_dma16_sv(const void* base, uint32_t off_bytes, const void* lds_base) {
   const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(MLA_LDS const void*)(lds_base));
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off_bytes), "s"(base), "s"(m) : "memory", "m0");
+}
+// As lds_dma16_sv with the LDS destination given as a wave-uniform 32-bit LDS
+// address (the M0 value).
+__device__ __forceinline__ void lds_dma16_sv_m0(const void* base, uint32_t off_bytes, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off_bytes), "s"(base), "s"(lds_addr) : "memory", "m0");
+}
+// As lds_dma16_raw with the LDS destination given as a wave-uniform 32-bit
+// LDS address.
+__device__ __forceinline__ void lds_dma16_m0(const void* gsrc, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gsrc), "s"(lds_addr) : "memory", "m0");
 }
 __device__ __forceinline__ void vm_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 // Wait until at most N vector-memory instructions are outstanding (gfx9
@@ -163,7 +190,7 @@ struct FlashArgs {
 hipError_t launch_flash_mfma(const FlashArgs& a, bool f16_operands, const int32_t* cu_host, int num_seqs, hipStream_t s);
 hipError_t launch_flash_f32(const FlashArgs& a, hipStream_t s);
 
-// Most paged-cache blocks one decode chunk may span (its block ids are staged in LDS).
+// Most paged-cache blocks one decode segment may span (its block ids are staged in LDS).
 constexpr int kDecodeMaxChunkBlocks = 512;
 
 struct DecodeArgs {
@@ -172,13 +199,16 @@ struct DecodeArgs {
   const bf16* cache;      // [num_blocks, block_size, 576]
   const int32_t* block_table; int max_blocks; int num_blocks; int log2_block;
   const int32_t* seq_lens;
-  float* part_o;          // [B, max_chunks, H, 512]
-  float* part_ml;         // [B, max_chunks, H, 2]
+  f16* part_o;            // [B, max_slots, H, 512] partial outputs, normalised (O / l)
+  float* part_ml;         // [B, max_slots, H, 2] exponent origin and sum (sum 0: empty slot)
   bf16* o_lat;            // [B, H, 512]
-  int batch; int heads; int chunk; int max_chunks;
-  int num_items;          // sum over sequences of ceil(len / chunk) (host lengths)
+  int batch; int heads;
+  int quota;              // keys per workgroup of the concatenated key sequence (multiple of 64)
+  int max_slots;          // partial slots per sequence
+  int num_items;          // workgroups of the split kernel
   float scale;
 };
+
 hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t s);
 
