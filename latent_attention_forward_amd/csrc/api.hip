@@ -157,7 +157,7 @@ constexpr int kDecodeTargetGroups = 256;   // one workgroup per CU
 
 struct DecodePlan {
   int quota, groups, max_slots;
-  size_t qt, olat, part_o, part_ml, total;
+  size_t qt, part_o, part_ml, total;
 };
 
 // The keys of all sequences, one after another, are dealt to workgroups in
@@ -185,7 +185,6 @@ DecodePlan decode_plan(const mla_config* c, const int32_t* lens, int batch, int6
   const int64_t H = c->num_heads, R = c->kv_lora_rank;
   size_t off = 0;
   p.qt = off; off += align256((size_t)batch * H * R * 2);
-  p.olat = off; off += align256((size_t)batch * H * R * 2);
   p.part_o = off; off += align256((size_t)batch * p.max_slots * H * R * 2);
   p.part_ml = off; off += align256((size_t)batch * p.max_slots * H * 2 * 4);
   p.total = off;
@@ -513,7 +512,6 @@ mla_status mla_decode_absorbed_fwd(const mla_config* cfg, const void* w_kv_b, co
   char* ws = (char*)workspace;
   const int dn = cfg->qk_nope_dim, dv = cfg->v_head_dim, R = cfg->kv_lora_rank;
   bf16* qt = (bf16*)(ws + P.qt);
-  bf16* olat = (bf16*)(ws + P.olat);
   hipError_t e;
   // absorb W_UK into the query: qt[b, h, :] = q_nope[b, h, :] . W_kv_b[h*(dn+dv) + 0:dn, :]
   {
@@ -529,20 +527,14 @@ mla_status mla_decode_absorbed_fwd(const mla_config* cfg, const void* w_kv_b, co
   int lbs = 0;
   while ((1 << lbs) < block_size) ++lbs;
   d.max_blocks = max_blocks; d.num_blocks = num_blocks; d.log2_block = lbs; d.seq_lens = seq_lens_dev;
-  d.part_o = (f16*)(ws + P.part_o); d.part_ml = (float*)(ws + P.part_ml); d.o_lat = olat;
+  d.part_o = (f16*)(ws + P.part_o); d.part_ml = (float*)(ws + P.part_ml);
   d.batch = batch; d.heads = H; d.quota = P.quota; d.max_slots = P.max_slots; d.num_items = P.groups;
   d.scale = scale_of(cfg);
   if ((e = launch_decode_split(d, st)) != hipSuccess) return hip_fail(e, "decode split");
-  if ((e = launch_decode_combine(d, st)) != hipSuccess) return hip_fail(e, "decode combine");
-  // un-absorb W_UV: out[b, h, :] = W_kv_b[h*(dn+dv) + dn : +dv, :] . o_lat[b, h, :]
-  {
-    GemmArgs g{};
-    g.a = olat; g.lda = (int64_t)H * R; g.a_bstride = R;
-    g.b = (const bf16*)w_kv_b + (int64_t)dn * R; g.ldb = R; g.b_bstride = (int64_t)(dn + dv) * R; g.b_kn = false;
-    g.c = out; g.ldc = (int64_t)H * dv; g.c_bstride = dv;
-    g.m = batch; g.n = dv; g.k = R; g.batch = H; g.epilogue = EPI_STORE;
-    if ((e = launch_gemm_bf16(g, st)) != hipSuccess) return hip_fail(e, "un-absorb");
-  }
+  // combine the splits and un-absorb W_UV: out[b, h, :] = W_kv_b[h*(dn+dv) + dn : +dv, :] . o_lat[b, h, :]
+  d.w_uv = (const bf16*)w_kv_b + (int64_t)dn * R; d.w_uv_hstride = (int64_t)(dn + dv) * R;
+  d.out = (bf16*)out; d.dv = dv;
+  if ((e = launch_decode_combine_unabsorb(d, st)) != hipSuccess) return hip_fail(e, "decode combine");
   return ok();
 }
 

@@ -1,5 +1,6 @@
 // Weight-absorbed MLA decode over the paged latent cache: split-KV attention in
-// the 576-wide latent space and the log-sum-exp combine of the splits.
+// the 576-wide latent space, then the log-sum-exp combine of the splits fused
+// with the W_UV un-absorb.
 //
 // Work split: the keys of all sequences, taken one sequence after another,
 // form one long sequence; workgroup g takes the keys [g R, (g+1) R) of it (R,
@@ -108,7 +109,12 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
   // first sequence that reaches past S0 (wave 0, a prefix sum of the lengths).
   const int cap = a.max_blocks << lbs;
   const int64_t R = a.quota;
-  const int64_t S0 = (int64_t)blockIdx.x * R, S1 = S0 + R;
+  // Work item of this workgroup.  Workgroup x runs on XCD x % 8; consecutive
+  // items, which mostly share a sequence and so its query, go to one XCD so
+  // that the query is read from that XCD's L2 after the first of them.
+  const int G = gridDim.x, g8 = G >> 3, r8 = G & 7, xc = blockIdx.x & 7;
+  const int item = xc * g8 + min(xc, r8) + (int)(blockIdx.x >> 3);
+  const int64_t S0 = (int64_t)item * R, S1 = S0 + R;
   __shared__ long long s_first[2];
   if (wave == 0) {
     if (lane == 0) { s_first[0] = a.batch; s_first[1] = 0; }
@@ -143,7 +149,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
     return x <= 0 ? 0 : (x >= L ? L : (int)min<int64_t>(L, ((x + 32) >> 6) << 6));
   };
   const int k0 = cut(S0 - st), k1 = cut(S1 - st);
-  const int slot = (int)(blockIdx.x - st / R);
+  const int slot = (int)(item - st / R);
   const int64_t part = ((int64_t)b * a.max_slots + slot) * H;
   if (k0 >= k1) {                          // empty after the cut: weight 0 in the combine
     for (int i = tid; i < H; i += NTH) { a.part_ml[(part + i) * 2] = -INFINITY; a.part_ml[(part + i) * 2 + 1] = 0.f; }
@@ -168,19 +174,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
 
   const int hsel = lane >> 5;
   const int my_h = wave * 32 + (lane & 31);
-  bf16x8 qreg[RC / 16];
-  {
-    const bf16* qt = a.qt + ((int64_t)b * H + my_h) * RK;
-    const bf16* qp = a.q_pe + ((int64_t)b * H + my_h) * DRP;
-#pragma unroll
-    for (int ks = 0; ks < RC / 16; ++ks) {
-      const int d = ks * 16 + hsel * 8;
-      qreg[ks] = (d < RK) ? *(const bf16x8*)(qt + d) : *(const bf16x8*)(qp + d - RK);
-    }
-  }
-  // the query must have landed before the tile copies go out: the copies are
-  // issued from inline asm and the waits inside the tile loop only track them
-  vm_wait_all();
+  bf16x8 qreg[RC / 16];                  // absorbed query, loaded behind the first tiles
 
   // Lane-constant parts of the swizzled LDS addresses (elements); the rest of
   // every address is a compile-time offset.
@@ -239,111 +233,132 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[d][e] = 0.f;
 
-  // NBUF - 1 tiles in flight: tile t + NBUF - 1 is requested while tile t is
-  // multiplied.  Each wave issues BPW loads per tile; before a barrier it waits
-  // until the next tile's loads are done and keeps the newer tiles' pending.
-  static_assert(NBUF == 4, "wait_tile is written for 3 tiles in flight");
-  constexpr int KEEP2 = (2 * BPW < 64) ? 2 * BPW : BPW;   // vmcnt holds at most 63
-  auto wait_tile = [&](int newer) {          // newer: tiles issued after the awaited one
-    if (newer >= 2) vm_wait_keep<KEEP2>();
-    else if (newer == 1) vm_wait_keep<BPW>();
-    else vm_wait_all();
+  // Pipelined tile loop.  In iteration t the scores of tile t + 1 are formed
+  // on the MFMA unit (accumulated in VGPRs, inline asm) while the softmax of
+  // tile t runs on the VALU between those MFMAs; then PV(t) accumulates into
+  // the AGPR-resident output.  Tile t + 3 is requested at the start of
+  // iteration t (ring of NBUF = 4 LDS buffers); at its end tile t + 2 must
+  // have landed (the copies of tile t + 3, BPW per wave, may still fly).
+  static_assert(NBUF == 4, "the pipeline is written for a ring of 4 tiles");
+  auto s_tile = [&](f32x16& s, int buf, auto&& group) __attribute__((always_inline)) {
+    const bf16* sb = sC[buf];
+    constexpr int NS = RC / 16, D = 4;
+    auto addr = [&](int i) { return sb + base_s[i & 3] + (i >> 2) * 64; };
+    bf16x8 cf[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) cf[i] = *(const bf16x8*)addr(i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const bf16x8 cur = cf[i % D];
+      if (i + D < NS) cf[i % D] = *(const bf16x8*)addr(i + D);
+      if (i == 0) mfma32_vacc0(s, cur, qreg[0]);
+      else mfma32_vacc(s, cur, qreg[i]);
+      group(i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mfma_result_wait();                  // the VALU reads s next
   };
+  // softmax of one tile: prep (mask, max, excursion check), then 16 probabilities
+  // in groups interleaved with the next tile's MFMAs
+  float mb = 0.f;
+  bf16x8 pb[2];
+  auto prep = [&](f32x16& s, int t) __attribute__((always_inline)) {
+    const int kb = k0 + t * DKT;
+    if (kb + DKT > k1) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (kb + (e >> 2) * 8 + hsel * 4 + (e & 3) >= k1) s[e] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    if (t == 0) m_ref = mx;                       // the first tile holds at least one key
+    exact_path |= __builtin_amdgcn_ballot_w64((mx - m_ref) * c2 > kMaxExcursion) != 0;
+    mb = m_ref * c2;
+  };
+  auto group_of = [&](f32x16& s) {
+    return [&](int i) __attribute__((always_inline)) {
+      if (i % 2 == 1 && i < 33) {                 // 16 groups of one probability
+        const int e = i >> 1;
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[e], c2, -mb));
+        l_run += p;
+        pb[e >> 3][e & 7] = (bf16)p;
+      }
+    };
+  };
+  auto no_group = [](int) {};
+  // O^T += C^T P^T; step j covers keys j*16 + {h*4 + [0,4), 8 + h*4 + [0,4)}
+  auto pv_tile = [&](int buf) __attribute__((always_inline)) {
+    const bf16* sb = sC[buf];
+    constexpr int NP = 2 * (RK / 32), D = 4;
+    auto taddr = [&](int i) { const int j = i / (RK / 32), d = i % (RK / 32);
+                              return sb + base_t[d & 1] + (j * 16) * RC + (d >> 1) * 64; };
+    bf16x4 lo[D], hi[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) { lo[i] = lds_read_tr(taddr(i)); hi[i] = lds_read_tr(taddr(i) + 8 * RC); }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const bf16x8 cur = cat8(lo[i % D], hi[i % D]);
+      if (i + D < NP) { lo[i % D] = lds_read_tr(taddr(i + D)); hi[i % D] = lds_read_tr(taddr(i + D) + 8 * RC); }
+      const int j = i / (RK / 32), d = i % (RK / 32);
+      o[d] = mfma32(cur, pb[j], o[d]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto step = [&](int t, f32x16& s_cur, f32x16& s_nxt) __attribute__((always_inline)) {
+    if (t + 3 < nt) issue_tile(t + 3, (t + 3) % NBUF);
+    prep(s_cur, t);
+    if (t + 1 < nt) {
+      s_tile(s_nxt, (t + 1) % NBUF, group_of(s_cur));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 36; ++i) group_of(s_cur)(i);
+    }
+    pv_tile(t % NBUF);
+    if (t + 3 < nt) vm_wait_keep<BPW>();   // tile t + 2 landed, t + 3 may fly
+    else vm_wait_all();
+    wg_barrier();
+  };
+
 #pragma unroll
   for (int t = 0; t < NBUF - 1; ++t)
     if (t < nt) issue_tile(t, t);
-  wait_tile(min(NBUF - 2, nt - 1));
-  wg_barrier();
-  for (int t = 0; t < nt; ++t) {
-    const int buf = t % NBUF;
-    const int kb = k0 + t * DKT;
-    if (t + NBUF - 1 < nt) issue_tile(t + NBUF - 1, (t + NBUF - 1) % NBUF);
-    {
-      const bf16* sb = sC[buf];
-      constexpr int MT = DKT / 32;
-      f32x16 s[MT];
+  // The query, behind the first tiles.  Everything in flight has landed before
+  // the loop starts: the tile copies are issued from inline asm, so the waits
+  // inside the loop count only them.
+  {
+    const bf16* qt = a.qt + ((int64_t)b * H + my_h) * RK;
+    const bf16* qp = a.q_pe + ((int64_t)b * H + my_h) * DRP;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[mt][e] = 0.f;
-      {
-        // software-pipelined operand reads: step i = (mt, ks) reads 4 steps ahead
-        constexpr int NS = MT * (RC / 16), D = 4;
-        auto addr = [&](int i) { const int mt = i / (RC / 16), ks = i % (RC / 16);
-                                 return sb + base_s[ks & 3] + mt * 32 * RC + (ks >> 2) * 64; };
-        bf16x8 cf[D];
-#pragma unroll
-        for (int i = 0; i < D; ++i) cf[i] = *(const bf16x8*)addr(i);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < NS; ++i) {
-          const bf16x8 cur = cf[i % D];
-          if (i + D < NS) cf[i % D] = *(const bf16x8*)addr(i + D);
-          const int mt = i / (RC / 16), ks = i % (RC / 16);
-          s[mt] = mfma32(cur, qreg[ks], s[mt]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      // lane holds head my_h, keys mt*32 + (e/4)*8 + hsel*4 + e%4
-      if (kb + DKT > k1) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            if (kb + mt * 32 + (e >> 2) * 8 + hsel * 4 + (e & 3) >= k1) s[mt][e] = -INFINITY;
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mt][e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      if (t == 0) m_ref = mx;                       // the first tile holds at least one key
-      exact_path |= __builtin_amdgcn_ballot_w64((mx - m_ref) * c2 > kMaxExcursion) != 0;
-      {
-        const float mb = m_ref * c2;
-        bf16x8 pb[2 * MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(s[mt][e], c2, -mb));
-            l_run += p;
-            pb[mt * 2 + (e >> 3)][e & 7] = (bf16)p;
-          }
-        // O^T += C^T P^T; step j covers keys (j/2)*32 + (j%2)*16 + {h*4 + [0,4), 8 + h*4 + [0,4)}
-        {
-          // software-pipelined transpose reads: step i = (j, d) reads 4 steps ahead
-          constexpr int NP = 2 * MT * (RK / 32), D = 4;
-          auto taddr = [&](int i) { const int j = i / (RK / 32), d = i % (RK / 32);
-                                    return sb + base_t[d & 1] + ((j >> 1) * 32 + (j & 1) * 16) * RC + (d >> 1) * 64; };
-          bf16x4 lo[D], hi[D];
-#pragma unroll
-          for (int i = 0; i < D; ++i) { lo[i] = lds_read_tr(taddr(i)); hi[i] = lds_read_tr(taddr(i) + 8 * RC); }
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int i = 0; i < NP; ++i) {
-            const bf16x8 cur = cat8(lo[i % D], hi[i % D]);
-            if (i + D < NP) { lo[i % D] = lds_read_tr(taddr(i + D)); hi[i % D] = lds_read_tr(taddr(i + D) + 8 * RC); }
-            const int j = i / (RK / 32), d = i % (RK / 32);
-            o[d] = mfma32(cur, pb[j], o[d]);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        }
-      }
+    for (int ks = 0; ks < RC / 16; ++ks) {
+      const int d = ks * 16 + hsel * 8;
+      qreg[ks] = (d < RK) ? *(const bf16x8*)(qt + d) : *(const bf16x8*)(qp + d - RK);
     }
-    // tile t + 1 must have landed; newer tiles may still be in flight
-    wait_tile(min(NBUF - 2, nt - 2 - t));
-    wg_barrier();
+  }
+  vm_wait_all();
+  wg_barrier();
+  f32x16 sa, sbv;
+  s_tile(sa, 0, no_group);
+  for (int t = 0; t < nt; ++t) {
+    step(t, sa, sbv);
+    sa = sbv;                             // the next tile's scores become the current ones
   }
 
   if (exact_path) {
     decode_chunk_exact(a, b, slot, wave * 32, k0, k1);
   } else {
-    // lane holds head my_h, dims d*32 + q*8 + hsel*4 + [0,4); stored as O / l in fp16
+    // Lane holds head my_h, dims d*32 + q*8 + hsel*4 + [0,4).  O / l goes in
+    // fp16 through this wave's 32 KB of the (now idle) tile buffers, as 32 rows
+    // of 1 KB with 16 B chunk c of row r at c ^ (r & 15), and leaves as one 1 KB
+    // row per store.
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     const float inv = 1.f / l_tot;
-    f16* po = a.part_o + (part + my_h) * RK;
+    char* wb = (char*)&sC[0][0] + wave * (32 * RK * 2);
+    const int hl = lane & 31;
 #pragma unroll
     for (int d = 0; d < RK / 32; ++d)
 #pragma unroll
@@ -351,8 +366,12 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
         f16x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = (f16)(o[d][q * 4 + e] * inv);
-        *(f16x4*)(po + d * 32 + q * 8 + hsel * 4) = v;
+        *(f16x4*)(wb + hl * (RK * 2) + (((d * 4 + q) ^ (hl & 15)) << 4) + hsel * 8) = v;
       }
+    f16* po = a.part_o + (part + wave * 32) * RK + lane * 8;
+#pragma unroll
+    for (int r = 0; r < 32; ++r)
+      *(f16x8*)(po + r * RK) = *(const f16x8*)(wb + r * (RK * 2) + ((lane ^ (r & 15)) << 4));
     if (hsel == 0) {
       a.part_ml[(part + my_h) * 2 + 0] = m_ref;
       a.part_ml[(part + my_h) * 2 + 1] = l_tot;
@@ -361,45 +380,157 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
   }
 }
 
-// Combine: o_lat[b, h, :] = sum_s w_s l_s (O_s / l_s) / sum_s w_s l_s over the
-// sequence's slots s, with w_s = 2^((m_s - M) * c2); slots emptied by a cut
-// (l_s = 0) are skipped.
-__global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int H = a.heads;
+// Combine and un-absorb, fused.  Workgroup (h, block of 16 sequences):
+//  1. o_lat[b, h, :] = sum_s w_s l_s (O_s / l_s) / sum_s w_s l_s over the
+//     sequence's slots s, with w_s = 2^((m_s - M) * c2); slots emptied by a
+//     cut (l_s = 0) are skipped.  Rounded to bf16 into LDS; each wave takes 4
+//     sequences, two at a time with all their slots loaded before any is used,
+//     8 latent dims per lane.
+//  2. out[b, h, :] = W_UV[h] . o_lat[b, h, :] for the 16 sequences at once:
+//     O^T[dv, b] = W_UV[h][dv, :] . o_lat[b, :]^T on 16x16x32 MFMAs, each wave
+//     32 output dims.  Its W_UV rows are requested while step 1 runs.
+// The workgroups of one head run on one XCD (x = h), so W_UV[h] is read from
+// HBM about once.
+constexpr int CB = 16;                     // sequences per combine workgroup
+constexpr int CMAXS = 8;                   // slots per sequence loaded at once
+__global__ __launch_bounds__(256, 2) void decode_combine_unabsorb_kernel(DecodeArgs a) {
+  // latent rows of the block: 16 B chunk c of row j at c ^ (j & 15), so the
+  // 16 rows one MFMA operand read touches spread over the banks
+  __shared__ __attribute__((aligned(16))) bf16 sO[CB * RK];
+  __shared__ int s_ns[CB];
+  __shared__ long long s_red[4];
+  const int h = blockIdx.x, b0 = blockIdx.y * CB;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int H = a.heads, B = a.batch;
   const int cap = a.max_blocks << a.log2_block;
-  // start of sequence b in the concatenated key sequence
-  __shared__ long long s_part[2];
-  long long st = 0;
-  for (int i = tid; i < b; i += 128) st += max(0, min(a.seq_lens[i], cap));
-  st = wave_sum_ll(st);
-  if ((tid & 63) == 0) s_part[tid >> 6] = st;
-  __syncthreads();
-  st = s_part[0] + s_part[1];
-  const int L = max(0, min(a.seq_lens[b], cap));
   const int64_t R = a.quota;
-  const int nslot = L > 0 ? (int)((st + L - 1) / R - st / R + 1) : 0;
+  // start of sequence b0 in the concatenated key order, then the slot counts
+  // of b0 .. b0 + 15
+  long long part_sum = 0;
+  for (int i = tid; i < b0; i += 256) part_sum += max(0, min(a.seq_lens[i], cap));
+  part_sum = wave_sum_ll(part_sum);
+  if (lane == 0) s_red[wave] = part_sum;
+  __syncthreads();
+  if (wave == 0) {
+    const long long base = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+    const int b = b0 + lane;
+    long long n = (lane < CB && b < B) ? (long long)max(0, min(a.seq_lens[b], cap)) : 0;
+    long long incl = n;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const long long v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    const long long st = base + incl - n;
+    if (lane < CB) s_ns[lane] = n > 0 ? (int)((st + n - 1) / R - st / R + 1) : 0;
+  }
+  __syncthreads();
+
   const float c2 = a.scale * kLog2e;
-  float M = -INFINITY;
-  for (int sl = 0; sl < nslot; ++sl) {
-    const int64_t part = ((int64_t)b * a.max_slots + sl) * H + h;
-    if (a.part_ml[part * 2 + 1] != 0.f) M = fmaxf(M, a.part_ml[part * 2]);
+  // A operand of the un-absorb: lane holds row 32 w + 16 mt + lane % 16 of
+  // W_UV[h], k = 32 ks + (lane / 16) * 8 + [0, 8)
+  const int r16 = lane & 15, kq = lane >> 4;
+  bf16x8 wf[2][RK / 32];
+  for (int j2 = 0; j2 < 2; ++j2) {
+    float mv[2][CMAXS], lv[2][CMAXS];
+    f16x8 pv[2][CMAXS];
+    int nslot[2];
+    int64_t part0[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int j = wave * 4 + j2 * 2 + u, b = b0 + j;
+      nslot[u] = s_ns[j];                                // 0 past the batch
+      part0[u] = (int64_t)b * a.max_slots * H + h;     // slot s at part0 + s * H
+#pragma unroll
+      for (int sl = 0; sl < CMAXS; ++sl) {
+        if (sl < nslot[u]) {
+          const int64_t part = part0[u] + (int64_t)sl * H;
+          const float2 ml = *(const float2*)(a.part_ml + part * 2);
+          mv[u][sl] = ml.x;
+          lv[u][sl] = ml.y;
+          pv[u][sl] = *(const f16x8*)(a.part_o + part * RK + lane * 8);
+        } else {
+          mv[u][sl] = -INFINITY;
+          lv[u][sl] = 0.f;
+        }
+      }
+    }
+    if (j2 == 0) {                         // behind the first partials, ahead of the second
+      const bf16* wr = a.w_uv + (int64_t)h * a.w_uv_hstride + (int64_t)(32 * wave + r16) * RK + kq * 8;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < RK / 32; ++ks) wf[mt][ks] = *(const bf16x8*)(wr + mt * 16 * RK + ks * 32);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int j = wave * 4 + j2 * 2 + u;
+      float M = -INFINITY;
+#pragma unroll
+      for (int sl = 0; sl < CMAXS; ++sl)
+        if (lv[u][sl] != 0.f) M = fmaxf(M, mv[u][sl]);
+      for (int sl = CMAXS; sl < nslot[u]; ++sl) {
+        const int64_t part = part0[u] + (int64_t)sl * H;
+        if (a.part_ml[part * 2 + 1] != 0.f) M = fmaxf(M, a.part_ml[part * 2]);
+      }
+      float acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+      float lsum = 0.f;
+#pragma unroll
+      for (int sl = 0; sl < CMAXS; ++sl) {
+        if (lv[u][sl] != 0.f) {
+          const float w = __builtin_amdgcn_exp2f((mv[u][sl] - M) * c2) * lv[u][sl];
+          lsum += w;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] += w * (float)pv[u][sl][e];
+        }
+      }
+      for (int sl = CMAXS; sl < nslot[u]; ++sl) {
+        const int64_t part = part0[u] + (int64_t)sl * H;
+        const float l = a.part_ml[part * 2 + 1];
+        if (l == 0.f) continue;
+        const float w = __builtin_amdgcn_exp2f((a.part_ml[part * 2] - M) * c2) * l;
+        lsum += w;
+        const f16x8 v = *(const f16x8*)(a.part_o + part * RK + lane * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += w * (float)v[e];
+      }
+      // sequences past the batch and empty ones leave a zero row
+      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+      bf16x8 r;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r[e] = (bf16)(acc[e] * inv);
+      *(bf16x8*)&sO[j * RK + ((lane ^ (j & 15)) << 3)] = r;
+    }
   }
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float lsum = 0.f;
-  for (int sl = 0; sl < nslot; ++sl) {
-    const int64_t part = ((int64_t)b * a.max_slots + sl) * H + h;
-    const float l = a.part_ml[part * 2 + 1];
-    if (l == 0.f) continue;
-    const float w = __builtin_amdgcn_exp2f((a.part_ml[part * 2] - M) * c2) * l;
-    lsum += w;
-    const f16x4 v = *(const f16x4*)(a.part_o + part * RK + tid * 4);
-    acc.x += w * (float)v[0]; acc.y += w * (float)v[1]; acc.z += w * (float)v[2]; acc.w += w * (float)v[3];
+  __syncthreads();
+
+  // O^T[dv, b]: wave w takes output dims 32 w .. 32 w + 31 (dv = 128); the B
+  // operand lane holds sequence b0 + lane % 16, k = 32 ks + (lane / 16) * 8
+  f32x4 o[2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[mt][e] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < RK / 32; ++ks) {
+    const bf16x8 Bv = *(const bf16x8*)&sO[r16 * RK + (((ks * 4 + kq) ^ r16) << 3)];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) o[mt] = mfma16(wf[mt][ks], Bv, o[mt]);
   }
-  const float inv = 1.f / lsum;
-  bf16x4 r;
-  r[0] = (bf16)(acc.x * inv); r[1] = (bf16)(acc.y * inv); r[2] = (bf16)(acc.z * inv); r[3] = (bf16)(acc.w * inv);
-  *(bf16x4*)(a.o_lat + ((int64_t)b * H + h) * RK + tid * 4) = r;
+  // lane holds sequence b0 + lane % 16, dims 32 w + 16 mt + (lane / 16) * 4 + [0, 4)
+  const int b = b0 + r16;
+  if (b < B) {
+    bf16* orow = a.out + ((int64_t)b * H + h) * a.dv + 32 * wave + kq * 4;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      bf16x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (bf16)o[mt][e];
+      *(bf16x4*)(orow + mt * 16) = v;
+    }
+  }
 }
 
 }  // namespace
@@ -417,9 +548,10 @@ hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t s) {
-  dim3 grid(a.heads, a.batch);
-  decode_combine_kernel<<<grid, 128, 0, s>>>(a);
+hipError_t launch_decode_combine_unabsorb(const DecodeArgs& a, hipStream_t s) {
+  if (a.dv != 128) return hipErrorInvalidValue;
+  dim3 grid(a.heads, (a.batch + CB - 1) / CB);
+  decode_combine_unabsorb_kernel<<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -64,6 +64,20 @@ __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+// 32x32x16 bf16 MFMA with the accumulator held in VGPRs whatever form the
+// compiler picks for the other MFMAs of the kernel (inline asm; the first of a
+// chain starts from 0).  Back-to-back MFMAs accumulating into the same
+// registers need no wait states; before the VALU reads the result, call
+// mfma_result_wait().
+__device__ __forceinline__ void mfma32_vacc(f32x16& c, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32_vacc0(f32x16& c, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+}
+// Wait states between an MFMA writing VGPRs and a VALU instruction reading them.
+__device__ __forceinline__ void mfma_result_wait() { asm volatile("s_nop 15"); }
+
 // LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane
 // L supplies the address of 4 consecutive 16-bit elements ("row" L); the result
 // of lane i is element i%4 of rows i/4, i/4+4, i/4+8, i/4+12.
@@ -201,7 +215,10 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   f16* part_o;            // [B, max_slots, H, 512] partial outputs, normalised (O / l)
   float* part_ml;         // [B, max_slots, H, 2] exponent origin and sum (sum 0: empty slot)
-  bf16* o_lat;            // [B, H, 512]
+  const bf16* w_uv;       // W_UV of head h: rows [dv] of 512 at w_uv + h * w_uv_hstride
+  int64_t w_uv_hstride;
+  bf16* out;              // [B, H, dv]
+  int dv;
   int batch; int heads;
   int quota;              // keys per workgroup of the concatenated key sequence (multiple of 64)
   int max_slots;          // partial slots per sequence
@@ -210,6 +227,6 @@ struct DecodeArgs {
 };
 
 hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s);
-hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_combine_unabsorb(const DecodeArgs& a, hipStream_t s);
 
 }  // namespace mla
