@@ -513,15 +513,6 @@ mla_status mla_decode_absorbed_fwd(const mla_config* cfg, const void* w_kv_b, co
   const int dn = cfg->qk_nope_dim, dv = cfg->v_head_dim, R = cfg->kv_lora_rank;
   bf16* qt = (bf16*)(ws + P.qt);
   hipError_t e;
-  // absorb W_UK into the query: qt[b, h, :] = q_nope[b, h, :] . W_kv_b[h*(dn+dv) + 0:dn, :]
-  {
-    GemmArgs g{};
-    g.a = q_nope; g.lda = (int64_t)H * dn; g.a_bstride = dn;
-    g.b = w_kv_b; g.ldb = R; g.b_bstride = (int64_t)(dn + dv) * R; g.b_kn = true;
-    g.c = qt; g.ldc = (int64_t)H * R; g.c_bstride = R;
-    g.m = batch; g.n = R; g.k = dn; g.batch = H; g.epilogue = EPI_STORE;
-    if ((e = launch_gemm_bf16(g, st)) != hipSuccess) return hip_fail(e, "absorb q");
-  }
   DecodeArgs d{};
   d.qt = qt; d.q_pe = (const bf16*)q_pe; d.cache = (const bf16*)kv_cache; d.block_table = block_table;
   int lbs = 0;
@@ -530,6 +521,9 @@ mla_status mla_decode_absorbed_fwd(const mla_config* cfg, const void* w_kv_b, co
   d.part_o = (f16*)(ws + P.part_o); d.part_ml = (float*)(ws + P.part_ml);
   d.batch = batch; d.heads = H; d.quota = P.quota; d.max_slots = P.max_slots; d.num_items = P.groups;
   d.scale = scale_of(cfg);
+  // absorb W_UK into the query: qt[b, h, :] = q_nope[b, h, :] . W_kv_b[h*(dn+dv) + 0:dn, :]
+  d.q_nope = (const bf16*)q_nope; d.w_uk = (const bf16*)w_kv_b; d.w_uv_hstride = (int64_t)(dn + dv) * R;
+  if ((e = launch_decode_absorb_q(d, st)) != hipSuccess) return hip_fail(e, "absorb q");
   if ((e = launch_decode_split(d, st)) != hipSuccess) return hip_fail(e, "decode split");
   // combine the splits and un-absorb W_UV: out[b, h, :] = W_kv_b[h*(dn+dv) + dn : +dv, :] . o_lat[b, h, :]
   d.w_uv = (const bf16*)w_kv_b + (int64_t)dn * R; d.w_uv_hstride = (int64_t)(dn + dv) * R;

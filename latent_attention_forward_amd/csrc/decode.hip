@@ -380,6 +380,82 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
   }
 }
 
+// Query absorption: qt[b, h, :] = W_UK[h]^T q_nope[b, h, :] for every
+// sequence, with W_UK[h] the [128, 512] block of W_kv_b rows of head h.
+// Workgroup (128 latent columns c0.., head h): the [128 x 128] slab of W_UK[h]
+// is copied to LDS (16 B chunk c of row k at c ^ 2 (k & 3)) and read back
+// transposed as the A operand of 32x32x16 MFMAs, D^T[col, b] = W^T[col, :] .
+// q^T[:, b]; wave w takes columns c0 + 32 w .. + 31 for all sequences, 32 at a
+// time, with the q_nope rows read straight from HBM as the B operand.
+constexpr int ADN = 128, ANC = 128;        // contraction (d_nope), columns per workgroup
+__global__ __launch_bounds__(256) void absorb_q_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16 sW[ADN * ANC];
+  const int c0 = blockIdx.x * ANC, h = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int H = a.heads, B = a.batch;
+  {
+    const bf16* src = a.w_uk + (int64_t)h * a.w_uv_hstride + c0;   // row k at + k * RK
+    const uint32_t sb = lds_addr_of(&sW[0]);
+#pragma unroll
+    for (int i = 0; i < ADN * ANC / 8 / 256; ++i) {
+      const int P = i * 256 + tid, k = P >> 4, pc = P & 15;
+      lds_dma16_m0(src + (int64_t)k * RK + ((pc ^ ((k & 3) << 1)) << 3), sb + (uint32_t)(i * 256 + wave * 64) * 16);
+    }
+  }
+  // B operand: lane holds sequence m0 + lane % 32, d_nope (lane / 32) * 8 + 16 ks + [0, 8)
+  const int col = lane & 31, hsel = lane >> 5;
+  auto load_q = [&](bf16x8 (&qb)[ADN / 16], int m0) {
+    const int b = m0 + col;
+    const bf16* q = a.q_nope + ((int64_t)b * H + h) * ADN + hsel * 8;
+#pragma unroll
+    for (int ks = 0; ks < ADN / 16; ++ks) {
+      if (b < B) qb[ks] = *(const bf16x8*)(q + ks * 16);
+      else
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qb[ks][e] = (bf16)0.f;
+    }
+  };
+  bf16x8 qb[ADN / 16];
+  load_q(qb, 0);
+  vm_wait_all();                           // the slab copies, issued from inline asm
+  __syncthreads();
+  // A operand by transpose reads: lane group g = lane / 16 reads rows
+  // 16 ks + (g / 2) * 8 + [0, 8) of columns 32 w + (g % 2) * 16 + [0, 16)
+  const int g = lane >> 4, L = lane & 15;
+  const int n = wave * 32 + (g & 1) * 16 + 4 * (L & 3);
+  bf16x8 wa[ADN / 16];
+#pragma unroll
+  for (int ks = 0; ks < ADN / 16; ++ks) {
+    bf16x4 v[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int k = ks * 16 + (g >> 1) * 8 + u * 4 + (L >> 2);
+      v[u] = lds_read_tr(&sW[k * ANC + ((((n >> 3) ^ ((k & 3) << 1))) << 3) + (n & 7)]);
+    }
+    wa[ks] = cat8(v[0], v[1]);
+  }
+  for (int m0 = 0; m0 < B; m0 += 32) {
+    f32x16 acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < ADN / 16; ++ks) acc = mfma32(wa[ks], qb[ks], acc);
+    if (m0 + 32 < B) load_q(qb, m0 + 32);
+    // lane holds sequence m0 + lane % 32, columns (i / 4) * 8 + hsel * 4 + i % 4
+    const int b = m0 + col;
+    if (b < B) {
+      bf16* dst = (bf16*)a.qt + ((int64_t)b * H + h) * RK + c0 + wave * 32 + hsel * 4;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (bf16)acc[q * 4 + e];
+        *(bf16x4*)(dst + q * 8) = v;
+      }
+    }
+  }
+}
+
 // Combine and un-absorb, fused.  Workgroup (h, block of 16 sequences):
 //  1. o_lat[b, h, :] = sum_s w_s l_s (O_s / l_s) / sum_s w_s l_s over the
 //     sequence's slots s, with w_s = 2^((m_s - M) * c2); slots emptied by a
@@ -534,6 +610,11 @@ __global__ __launch_bounds__(256, 2) void decode_combine_unabsorb_kernel(DecodeA
 }
 
 }  // namespace
+
+hipError_t launch_decode_absorb_q(const DecodeArgs& a, hipStream_t s) {
+  absorb_q_kernel<<<dim3(RK / ANC, a.heads), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
 
 hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s) {
   if (a.num_items <= 0) return hipSuccess;

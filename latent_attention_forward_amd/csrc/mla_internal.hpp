@@ -209,6 +209,8 @@ constexpr int kDecodeMaxChunkBlocks = 512;
 
 struct DecodeArgs {
   const bf16* qt;         // [B, H, 512] absorbed query
+  const bf16* q_nope;     // [B, H, 128]
+  const bf16* w_uk;       // W_UK of head h: rows [128] of 512 at w_uk + h * w_uv_hstride
   const bf16* q_pe;       // [B, H, 64]
   const bf16* cache;      // [num_blocks, block_size, 576]
   const int32_t* block_table; int max_blocks; int num_blocks; int log2_block;
@@ -226,6 +228,7 @@ struct DecodeArgs {
   float scale;
 };
 
+hipError_t launch_decode_absorb_q(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_combine_unabsorb(const DecodeArgs& a, hipStream_t s);
 
