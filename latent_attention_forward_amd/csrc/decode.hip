@@ -248,22 +248,23 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
 #pragma unroll
     for (int i = 0; i < D; ++i) cf[i] = *(const bf16x8*)addr(i);
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
+    static_for<0, NS>([&](auto I) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value;
       const bf16x8 cur = cf[i % D];
-      if (i + D < NS) cf[i % D] = *(const bf16x8*)addr(i + D);
-      if (i == 0) mfma32_vacc0(s, cur, qreg[0]);
+      if constexpr (i + D < NS) cf[i % D] = *(const bf16x8*)addr(i + D);
+      if constexpr (i == 0) mfma32_vacc0(s, cur, qreg[0]);
       else mfma32_vacc(s, cur, qreg[i]);
-      group(i);
+      group(I);
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
     mfma_result_wait();                  // the VALU reads s next
   };
   // softmax of one tile: prep (mask, max, excursion check), then 16 probabilities
   // in groups interleaved with the next tile's MFMAs
   float mb = 0.f;
   bf16x8 pb[2];
-  auto prep = [&](f32x16& s, int t) __attribute__((always_inline)) {
+  float mx_part = 0.f;
+  auto prep_a = [&](f32x16& s, int t) __attribute__((always_inline)) {   // mask, lane max
     const int kb = k0 + t * DKT;
     if (kb + DKT > k1) {
 #pragma unroll
@@ -273,23 +274,21 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
     float mx = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    mx_part = mx;
+  };
+  auto prep_b = [&](int t) __attribute__((always_inline)) {   // head max, origin, excursion check
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx_part), __float_as_uint(mx_part), false, false);
+    const float mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     if (t == 0) m_ref = mx;                       // the first tile holds at least one key
     exact_path |= __builtin_amdgcn_ballot_w64((mx - m_ref) * c2 > kMaxExcursion) != 0;
     mb = m_ref * c2;
   };
-  auto group_of = [&](f32x16& s) {
-    return [&](int i) __attribute__((always_inline)) {
-      if (i % 2 == 1 && i < 33) {                 // 16 groups of one probability
-        const int e = i >> 1;
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[e], c2, -mb));
-        l_run += p;
-        pb[e >> 3][e & 7] = (bf16)p;
-      }
-    };
+  auto prob = [&](f32x16& s, int e) __attribute__((always_inline)) {
+    const float p = __builtin_amdgcn_exp2f(fmaf(s[e], c2, -mb));
+    l_run += p;
+    pb[e >> 3][e & 7] = (bf16)p;
   };
-  auto no_group = [](int) {};
+  auto no_group = [](auto) {};
   // O^T += C^T P^T; step j covers keys j*16 + {h*4 + [0,4), 8 + h*4 + [0,4)}
   auto pv_tile = [&](int buf) __attribute__((always_inline)) {
     const bf16* sb = sC[buf];
@@ -309,14 +308,40 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  // Iteration t: the MFMAs of S(t + 1) carry, between them, the softmax
+  // preparation of tile t (MFMAs 0 and 1), its 16 probabilities (odd MFMAs 3
+  // to 33) and the copies of tile t + 3 (spread evenly over MFMAs 4 to 33, so
+  // that the address unit the four waves share keeps up with them; the source
+  // block is read from LDS at MFMA 0), so the MFMA unit waits for none of them.
   auto step = [&](int t, f32x16& s_cur, f32x16& s_nxt) __attribute__((always_inline)) {
-    if (t + 3 < nt) issue_tile(t + 3, (t + 3) % NBUF);
-    prep(s_cur, t);
+    const int kn = k0 + (t + 3) * DKT;
+    const bool issue = t + 3 < nt, fast = lbs >= 5 && kn + DKT <= k1;
+    const uint32_t dstn = dst0 + (uint32_t)((t + 3) % NBUF) * (DKT * RC * 2);
+    if (issue && !fast) issue_tile(t + 3, (t + 3) % NBUF);
     if (t + 1 < nt) {
-      s_tile(s_nxt, (t + 1) % NBUF, group_of(s_cur));
+      const bf16* tb = nullptr;
+      s_tile(s_nxt, (t + 1) % NBUF, [&](auto I) __attribute__((always_inline)) {
+        constexpr int i = decltype(I)::value;
+        if constexpr (i == 0) {
+          prep_a(s_cur, t);
+          if (issue && fast) tb = uniform_ptr(a.cache + (((int64_t)sBlk[(kn >> lbs) - blk0] << lbs) + (kn & bmask)) * RC);
+        }
+        if constexpr (i == 1) prep_b(t);
+        if constexpr (i >= 3 && i <= 33 && (i & 1)) prob(s_cur, (i - 3) >> 1);
+        if constexpr (i >= 4 && i < 34) {            // copy k at MFMA 4 + floor(30 k / BPW)
+          constexpr int ka = ((i - 4) * BPW + 29) / 30;
+          if constexpr (ka < BPW && 4 + ka * 30 / BPW == i)
+            if (issue && fast) lds_dma16_sv_m0(tb, doff[ka], dstn + ka * NW * 1024);
+          if constexpr (ka + 1 < BPW && 4 + (ka + 1) * 30 / BPW == i)
+            if (issue && fast) lds_dma16_sv_m0(tb, doff[ka + 1], dstn + (ka + 1) * NW * 1024);
+        }
+      });
     } else {
+      if (issue && fast) issue_tile(t + 3, (t + 3) % NBUF);
+      prep_a(s_cur, t);
+      prep_b(t);
 #pragma unroll
-      for (int i = 0; i < 36; ++i) group_of(s_cur)(i);
+      for (int e = 0; e < 16; ++e) prob(s_cur, e);
     }
     pv_tile(t % NBUF);
     if (t + 3 < nt) vm_wait_keep<BPW>();   // tile t + 2 landed, t + 3 may fly

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stddef.h>
+#include <type_traits>
 
 #include "mla.h"
 
@@ -68,12 +69,16 @@ __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
 // compiler picks for the other MFMAs of the kernel (inline asm; the first of a
 // chain starts from 0).  Back-to-back MFMAs accumulating into the same
 // registers need no wait states; before the VALU reads the result, call
-// mfma_result_wait().
+// mfma_result_wait().  The compiler does not see an MFMA in the asm, so it
+// inserts no wait states between a VALU write of an operand (for instance a
+// copy out of an AGPR it parked the operand in) and the MFMA's read of it:
+// the asm carries them itself (they pass while the chain's previous MFMA is
+// still running).
 __device__ __forceinline__ void mfma32_vacc(f32x16& c, bf16x8 a, bf16x8 b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma32_vacc0(f32x16& c, bf16x8 a, bf16x8 b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
 }
 // Wait states between an MFMA writing VGPRs and a VALU instruction reading them.
 __device__ __forceinline__ void mfma_result_wait() { asm volatile("s_nop 15"); }
@@ -149,12 +154,23 @@ template <int N> __device__ __forceinline__ void vm_wait_keep() {
 // read before the barrier; the asm memory clobber keeps memory operations from
 // moving across it.
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// Wait until this wave's LDS operations (stores included) have completed.
+__device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 __device__ __forceinline__ f16x8 cat8(f16x4 a, f16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Calls f(std::integral_constant<int, i>) for i = B .. E - 1, so that the index
+// is a constant expression in the body whatever the loop unroller decides.
+template <int B, int E, typename F> __device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 // ---------------------------------------------------------------- launchers
