@@ -37,7 +37,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_BYTES = 256 << 20
 # sources whose change invalidates a committed counter figure
 KERNEL_SOURCES = {"flash": ["flash.hip", "mla_internal.hpp"],
-                  "decode": ["decode.hip", "gemm.hip", "api.hip", "mla_internal.hpp"]}
+                  "decode": ["decode.hip", "api.hip", "mla_internal.hpp"]}
 
 
 def parse():
@@ -325,7 +325,7 @@ def main():
                      "kernel": "flash_mfma_kernel<fp16> (prefill attention)", "flops_per_launch": a_flops},
         "roofline_decode": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": traffic_for("decode"),
-                            "kernel": "mla_decode_absorbed_fwd (absorb GEMM + split-KV + combine + un-absorb GEMM)",
+                            "kernel": "mla_decode_absorbed_fwd (query absorption + split-KV attention + fused combine and un-absorb)",
                             "bytes_per_call": d_bytes},
     }
     if not args.no_cpu_baseline:
