@@ -160,15 +160,22 @@ struct DecodePlan {
   size_t qt, part_o, part_ml, total;
 };
 
-// The keys of all sequences, one after another, are dealt to workgroups in
-// runs of `quota` keys (a multiple of 64; at most as many blocks of the
-// smallest allowed size, 16, as a workgroup can stage).  Sequence b, starting
-// at st_b in that order, collects partials in slots 0 .. (st_b + L_b - 1) /
-// quota - st_b / quota.
+// The keys of all sequences, one after another, each sequence preceded by
+// kDecodeSegmentCost placeholder keys, are dealt to workgroups in runs of
+// `quota` keys (a multiple of 64; at most as many blocks of the smallest
+// allowed size, 16, as a workgroup can stage).  The placeholders charge the
+// workgroup that starts a sequence for the fixed cost of one more segment
+// (staging, query load, pipeline fill, partial stores), so workgroups that
+// span a sequence end take fewer keys.  Sequence b, whose first key sits at
+// r_b in that order, collects partials in slots 0 .. (r_b + L_b - 1) / quota -
+// r_b / quota.
 DecodePlan decode_plan(const mla_config* c, const int32_t* lens, int batch, int64_t key_cap) {
   DecodePlan p{};
   int64_t total = 0;
-  for (int b = 0; b < batch; ++b) total += std::min<int64_t>(std::max(lens[b], 0), key_cap);
+  for (int b = 0; b < batch; ++b) {
+    const int64_t L = std::min<int64_t>(std::max(lens[b], 0), key_cap);
+    if (L > 0) total += L + kDecodeSegmentCost;
+  }
   constexpr int kTile = 64, kMaxQuota = ((kDecodeMaxChunkBlocks - 2) * 16 - kTile) / kTile * kTile;
   int64_t quota = kTile * std::max<int64_t>(1, (total + (int64_t)kTile * kDecodeTargetGroups - 1) /
                                                    ((int64_t)kTile * kDecodeTargetGroups));
@@ -178,8 +185,10 @@ DecodePlan decode_plan(const mla_config* c, const int32_t* lens, int batch, int6
   int64_t st = 0, max_slots = 1;
   for (int b = 0; b < batch; ++b) {
     const int64_t L = std::min<int64_t>(std::max(lens[b], 0), key_cap);
-    if (L > 0) max_slots = std::max<int64_t>(max_slots, (st + L - 1) / quota - st / quota + 1);
-    st += L;
+    if (L == 0) continue;
+    const int64_t r0 = st + kDecodeSegmentCost;
+    max_slots = std::max<int64_t>(max_slots, (r0 + L - 1) / quota - r0 / quota + 1);
+    st = r0 + L;
   }
   p.max_slots = (int)max_slots;
   const int64_t H = c->num_heads, R = c->kv_lora_rank;

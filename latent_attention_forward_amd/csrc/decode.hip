@@ -3,13 +3,16 @@
 // with the W_UV un-absorb.
 //
 // Work split: the keys of all sequences, taken one sequence after another,
-// form one long sequence; workgroup g takes the keys [g R, (g+1) R) of it (R,
-// the quota, a multiple of 64 chosen so that about one workgroup per CU
-// results), cut at each sequence boundary into segments.  A cut that falls
+// each preceded by kDecodeSegmentCost placeholder keys (the fixed cost of a
+// segment, charged to the workgroup that starts the sequence), form one long
+// sequence; workgroup g takes the keys [g R, (g+1) R) of it (R, the quota, a
+// multiple of 64 chosen so that about one workgroup per CU results), cut at
+// each sequence boundary into segments.  A cut that falls
 // inside a sequence is moved to the nearest multiple of 64 keys of that
 // sequence (both workgroups sharing it round it the same way), so every
-// workgroup gets R +- 64 keys whatever the length mix.  Segment (g, b) writes
-// its partial result to slot g - floor(start_b / R) of sequence b.
+// workgroup gets R +- 64 keys of work whatever the length mix.  Segment (g, b)
+// writes its partial result to slot g - floor(r_b / R) of sequence b, r_b the
+// position of b's first key.
 //
 // Split kernel: for every head at once, the partial softmax state of a
 // segment's keys.  Each wave owns 32 heads (v_mfma_f32_32x32x16_bf16, one wave
@@ -116,12 +119,18 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
   const int item = xc * g8 + min(xc, r8) + (int)(blockIdx.x >> 3);
   const int64_t S0 = (int64_t)item * R, S1 = S0 + R;
   __shared__ long long s_first[2];
+  // length of sequence b in the work order (its keys plus the placeholders)
+  auto seg_len = [&](int bq) -> long long {
+    const int Lq = max(0, min(a.seq_lens[bq], cap));
+    return Lq > 0 ? (long long)Lq + kDecodeSegmentCost : 0;
+  };
   if (wave == 0) {
     if (lane == 0) { s_first[0] = a.batch; s_first[1] = 0; }
     long long seen = 0;
     for (int b0 = 0; b0 < a.batch; b0 += 64) {
       const int bb = b0 + lane;
-      const long long n = (bb < a.batch) ? (long long)max(0, min(a.seq_lens[bb], cap)) : 0;
+      const int Lb = (bb < a.batch) ? max(0, min(a.seq_lens[bb], cap)) : 0;
+      const long long n = Lb > 0 ? (long long)Lb + kDecodeSegmentCost : 0;
       long long incl = n;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -136,7 +145,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
   __syncthreads();
   int b = (int)s_first[0];
   int64_t st = s_first[1];
-  for (; b < a.batch && st < S1; st += max(0, min(a.seq_lens[b], cap)), ++b) {
+  for (; b < a.batch && st < S1; st += seg_len(b), ++b) {
   __syncthreads();                         // the previous segment is done with sBlk and the tiles
   // Lane-dependent values are rebuilt per segment from an opaque copy of the
   // thread id, so none of them is kept live across the segment loop.
@@ -144,12 +153,14 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
   asm volatile("" : "+v"(tid_s));
   const int tid = tid_s, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int L = max(0, min(a.seq_lens[b], cap));
+  const int64_t r0 = st + kDecodeSegmentCost;   // work-order position of key 0 of b
+  if (L == 0 || S1 <= r0) continue;             // none of b's keys fall to this workgroup
   // cut points inside the sequence move to the nearest multiple of 64 keys
   auto cut = [&](int64_t x) -> int {
     return x <= 0 ? 0 : (x >= L ? L : (int)min<int64_t>(L, ((x + 32) >> 6) << 6));
   };
-  const int k0 = cut(S0 - st), k1 = cut(S1 - st);
-  const int slot = (int)(item - st / R);
+  const int k0 = cut(S0 - r0), k1 = cut(S1 - r0);
+  const int slot = (int)(item - r0 / R);
   const int64_t part = ((int64_t)b * a.max_slots + slot) * H;
   if (k0 >= k1) {                          // empty after the cut: weight 0 in the combine
     for (int i = tid; i < H; i += NTH) { a.part_ml[(part + i) * 2] = -INFINITY; a.part_ml[(part + i) * 2 + 1] = 0.f; }
@@ -508,22 +519,26 @@ __global__ __launch_bounds__(256, 2) void decode_combine_unabsorb_kernel(DecodeA
   // start of sequence b0 in the concatenated key order, then the slot counts
   // of b0 .. b0 + 15
   long long part_sum = 0;
-  for (int i = tid; i < b0; i += 256) part_sum += max(0, min(a.seq_lens[i], cap));
+  for (int i = tid; i < b0; i += 256) {
+    const int Li = max(0, min(a.seq_lens[i], cap));
+    part_sum += Li > 0 ? (long long)Li + kDecodeSegmentCost : 0;
+  }
   part_sum = wave_sum_ll(part_sum);
   if (lane == 0) s_red[wave] = part_sum;
   __syncthreads();
   if (wave == 0) {
     const long long base = s_red[0] + s_red[1] + s_red[2] + s_red[3];
     const int b = b0 + lane;
-    long long n = (lane < CB && b < B) ? (long long)max(0, min(a.seq_lens[b], cap)) : 0;
+    const int Lb = (lane < CB && b < B) ? max(0, min(a.seq_lens[b], cap)) : 0;
+    const long long n = Lb > 0 ? (long long)Lb + kDecodeSegmentCost : 0;
     long long incl = n;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const long long v = __shfl_up(incl, o, 64);
       if (lane >= o) incl += v;
     }
-    const long long st = base + incl - n;
-    if (lane < CB) s_ns[lane] = n > 0 ? (int)((st + n - 1) / R - st / R + 1) : 0;
+    const long long r0 = base + incl - n + kDecodeSegmentCost;   // work-order position of key 0
+    if (lane < CB) s_ns[lane] = Lb > 0 ? (int)((r0 + Lb - 1) / R - r0 / R + 1) : 0;
   }
   __syncthreads();
 

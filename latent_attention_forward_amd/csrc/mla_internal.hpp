@@ -222,6 +222,9 @@ hipError_t launch_flash_f32(const FlashArgs& a, hipStream_t s);
 
 // Most paged-cache blocks one decode segment may span (its block ids are staged in LDS).
 constexpr int kDecodeMaxChunkBlocks = 512;
+// Placeholder keys ahead of each sequence in the decode work order: the work
+// of one more segment for the workgroup that starts it, in keys.
+constexpr int kDecodeSegmentCost = 256;
 
 struct DecodeArgs {
   const bf16* qt;         // [B, H, 512] absorbed query
