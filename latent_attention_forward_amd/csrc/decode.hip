@@ -46,10 +46,14 @@ constexpr int RC = 576, RK = 512, DRP = 64;
 constexpr int CCH = RC / 8;                // 16 B chunks per cached row (72)
 constexpr float kMaxExcursion = 64.f;      // log2 units above the origin
 
-// Cache tile [64 keys][576]: chunk c of row r at c ^ sw(r).  sw maps any 8
-// consecutive rows to distinct values (row reads of the score MFMA) and any 4
-// rows 4a..4a+3 to distinct 32 B pairs (transpose reads of the PV MFMA).
-__device__ __forceinline__ int csw(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// Cache tile [32 keys][576]: chunk c of row r at c ^ sw(r), sw(r) a
+// permutation of row bits 1..3.  A row is 4.5 x 256 B, so rows of one parity
+// start at the same bank; sw spreads the 16 rows that one 16-lane phase of a
+// score-operand read (ds_read_b128) touches over all 64 banks, and keeps the
+// transpose reads of the PV operand (rows 4a .. 4a + 3 and 4a + 4 .. 4a + 7
+// in one 32-lane phase) on distinct banks too.  sw(r + 8) = sw(r) ^ 2 and
+// sw(r + 16) = sw(r).
+__device__ __forceinline__ int csw(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 1) | (((r >> 3) & 1) << 1); }
 
 // fp32 online softmax over keys [k0, k1) of sequence b for heads [h0, h0 + 32),
 // one wave, reading the cache from global memory; writes the partials.  Used
@@ -190,17 +194,21 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
   // Lane-constant parts of the swizzled LDS addresses (elements); the rest of
   // every address is a compile-time offset.
   //  score read (mt, ks): row mt*32 + lane%32, chunk ks*2 + hsel
-  const int rs = lane & 31, sws = csw(rs & 7);
+  const int rs = lane & 31, sws = csw(rs);
   int base_s[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) base_s[q] = rs * RC + ((((q * 2 + hsel) ^ sws)) << 3);
-  //  transpose read (j, half, d): row (j/2)*32 + (j%2)*16 + half*8 + rt, column d*32 + (g&1)*16 + 4*(L%4)
+  //  transpose read (j, half, d): row j*16 + half*8 + rt, column d*32 + (g&1)*16 + 4*(L%4);
+  //  the rows of half 1 carry the swizzle of rt ^ 8
   const int grp = lane >> 4, L4 = lane & 15;
-  const int rt = (grp >> 1) * 4 + (L4 >> 2), swt = csw(rt & 7);
+  const int rt = (grp >> 1) * 4 + (L4 >> 2), swt = csw(rt);
   const int xb = (L4 >> 1) & 1;
-  int base_t[2];
+  int base_t[2], base_th[2];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) base_t[q] = rt * RC + ((((q * 4 + (grp & 1) * 2 + xb) ^ swt)) << 3) + 4 * (L4 & 1);
+  for (int q = 0; q < 2; ++q) {
+    base_t[q] = rt * RC + ((((q * 4 + (grp & 1) * 2 + xb) ^ swt)) << 3) + 4 * (L4 & 1);
+    base_th[q] = (rt + 8) * RC + ((((q * 4 + (grp & 1) * 2 + xb) ^ csw(rt + 8))) << 3) + 4 * (L4 & 1);
+  }
 
   // Tile loads.  A full tile in one block (blocks of >= 32 tokens) is 32
   // contiguous cache rows, so each lane's BPW source offsets are fixed for the
@@ -306,14 +314,16 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
     constexpr int NP = 2 * (RK / 32), D = 4;
     auto taddr = [&](int i) { const int j = i / (RK / 32), d = i % (RK / 32);
                               return sb + base_t[d & 1] + (j * 16) * RC + (d >> 1) * 64; };
+    auto thaddr = [&](int i) { const int j = i / (RK / 32), d = i % (RK / 32);
+                               return sb + base_th[d & 1] + (j * 16) * RC + (d >> 1) * 64; };
     bf16x4 lo[D], hi[D];
 #pragma unroll
-    for (int i = 0; i < D; ++i) { lo[i] = lds_read_tr(taddr(i)); hi[i] = lds_read_tr(taddr(i) + 8 * RC); }
+    for (int i = 0; i < D; ++i) { lo[i] = lds_read_tr(taddr(i)); hi[i] = lds_read_tr(thaddr(i)); }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const bf16x8 cur = cat8(lo[i % D], hi[i % D]);
-      if (i + D < NP) { lo[i % D] = lds_read_tr(taddr(i + D)); hi[i % D] = lds_read_tr(taddr(i + D) + 8 * RC); }
+      if (i + D < NP) { lo[i % D] = lds_read_tr(taddr(i + D)); hi[i % D] = lds_read_tr(thaddr(i + D)); }
       const int j = i / (RK / 32), d = i % (RK / 32);
       o[d] = mfma32(cur, pb[j], o[d]);
       __builtin_amdgcn_sched_barrier(0);
