@@ -74,13 +74,15 @@ __device__ __forceinline__ float sum8(bf16x8 v, float acc) {
 }
 // LDS tiles, 16-byte chunks XOR-swizzled by key row so that the rows one
 // operand read touches spread over the banks:
-//   k_nope [64][128]: chunk c (0..15) of row r at c ^ (r & 7)
-//   k_pe   [64][64]:  chunk c (0..7)  of row r at c ^ (r & 7)
+//   k_nope [64][128]: chunk c (0..15) of row r at c ^ (r & 15)
+//   k_pe   [64][64]:  chunk c (0..7)  of row r at c ^ ((r >> 1) & 7)
 //   v      [64][128]: chunk c (0..15) of row r at c ^ ((r & 3) << 2), so the
 //                     four rows a transpose read takes land in four different
 //                     64-byte bank groups
-__device__ __forceinline__ int kn_off(int r, int c) { return r * DN + ((c ^ (r & 7)) << 3); }
-__device__ __forceinline__ int kr_off(int r, int c) { return r * DR + ((c ^ (r & 7)) << 3); }
+__device__ __forceinline__ int ksw_n(int r) { return r & 15; }
+__device__ __forceinline__ int ksw_r(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int kn_off(int r, int c) { return r * DN + ((c ^ ksw_n(r)) << 3); }
+__device__ __forceinline__ int kr_off(int r, int c) { return r * DR + ((c ^ ksw_r(r)) << 3); }
 __device__ __forceinline__ int vsw(int r, int c) { return c ^ ((r & 3) << 2); }
 __device__ __forceinline__ int voff(int r, int n) { return r * DV + (vsw(r, n >> 3) << 3) + (n & 7); }
 
@@ -134,16 +136,23 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashArgs a, TilePla
   for (int i = 0; i < 4; ++i) {
     const int P = (wave + 4 * i) * 64 + lane;
     const int r = P >> 4;
-    o_kn[i] = (uint32_t)((r * kv_row + (((P & 15) ^ (r & 7)) << 3)) * sizeof(T));
+    o_kn[i] = (uint32_t)((r * kv_row + (((P & 15) ^ ksw_n(r)) << 3)) * sizeof(T));
     o_v[i] = (uint32_t)((r * kv_row + DN + (vsw(r, P & 15) << 3)) * sizeof(T));
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int P = (wave + 4 * i) * 64 + lane;
     const int r = P >> 3;
-    o_kr[i] = (uint32_t)((r * a.kpe_stride + (((P & 7) ^ (r & 7)) << 3)) * sizeof(T));
+    o_kr[i] = (uint32_t)((r * a.kpe_stride + (((P & 7) ^ ksw_r(r)) << 3)) * sizeof(T));
   }
   const T* kv_head = KV + head * (DN + DV);
+  // copy k (0..9) of a full tile: k_nope blocks 0-3, k_pe blocks 4-5, v blocks 6-9
+  auto issue_part = [&](const T* kvb, const T* kpb, int k, auto bufc) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
+    if (k < 4) lds_dma16_sv(kvb, o_kn[k], &sKn[buf][(wave + 4 * k) * 512]);
+    else if (k < 6) lds_dma16_sv(kpb, o_kr[k - 4], &sKr[buf][(wave + 4 * (k - 4)) * 512]);
+    else lds_dma16_sv(kvb, o_v[k - 6], &sV[buf][(wave + 4 * (k - 6)) * 512]);
+  };
   auto issue_tile = [&](int t, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
     const int kb = ds + t * FK;
@@ -164,7 +173,7 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashArgs a, TilePla
         const int P = (wave + 4 * i) * 64 + lane;
         const int r = P >> 4;
         const int key = (kb + r < q1) ? kb + r : kb;
-        lds_dma16_raw(kv_head + (int64_t)key * kv_row + (((P & 15) ^ (r & 7)) << 3), &sKn[buf][(wave + 4 * i) * 512]);
+        lds_dma16_raw(kv_head + (int64_t)key * kv_row + (((P & 15) ^ ksw_n(r)) << 3), &sKn[buf][(wave + 4 * i) * 512]);
         lds_dma16_raw(kv_head + (int64_t)key * kv_row + DN + (vsw(r, P & 15) << 3), &sV[buf][(wave + 4 * i) * 512]);
       }
 #pragma unroll
@@ -172,7 +181,7 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashArgs a, TilePla
         const int P = (wave + 4 * i) * 64 + lane;
         const int r = P >> 3;
         const int key = (kb + r < q1) ? kb + r : kb;
-        lds_dma16_raw(KPE + (int64_t)key * a.kpe_stride + (((P & 7) ^ (r & 7)) << 3), &sKr[buf][(wave + 4 * i) * 512]);
+        lds_dma16_raw(KPE + (int64_t)key * a.kpe_stride + (((P & 7) ^ ksw_r(r)) << 3), &sKr[buf][(wave + 4 * i) * 512]);
       }
     }
   };
@@ -207,11 +216,18 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashArgs a, TilePla
   constexpr int SD = 4;   // S operand reads in flight
   constexpr int PD = 3;   // PV operands in flight
 
+  // The copies of tile t + 1 go out between the score MFMAs of tile t (one
+  // per other MFMA) rather than all at once after the barrier, where the
+  // copies of all eight waves of the CU queue at the address unit together.
   auto step = [&](int t, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
     const int kb = ds + t * FK;
-    if (t + 1 < ntiles) issue_tile(t + 1, BufC<buf ^ 1>{});
+    const int kn = kb + FK;
     const bool active = (qw0 < q1) && (kb <= qw0 + 31);
+    const bool spread = active && t + 1 < ntiles && kn + FK <= q1;
+    if (t + 1 < ntiles && !spread) issue_tile(t + 1, BufC<buf ^ 1>{});
+    const T* kvn = kv_head + (int64_t)kn * kv_row;
+    const T* kpn = KPE + (int64_t)kn * a.kpe_stride;
     if (active) {
       // ---- S^T for 64 keys (2 blocks of 32) x 32 queries, operands read SD ahead
       f32x16 s[2];
@@ -228,6 +244,7 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashArgs a, TilePla
         const V8 cur = kf[i % SD];
         if (i + SD < 24) kf[i % SD] = kread(i + SD, bufc);
         s[i & 1] = mfma32(cur, qreg[i >> 1], s[i & 1]);
+        if ((i & 1) && i < 20 && spread) issue_part(uniform_ptr(kvn), uniform_ptr(kpn), i >> 1, BufC<buf ^ 1>{});
       }
       __builtin_amdgcn_sched_barrier(0);
       // first PV operands, independent of the softmax
