@@ -194,23 +194,36 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashArgs a, TilePla
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[d][e] = 0.f;
 
-  // S operand i (0..23): key block mt = i & 1, k-step ks = i >> 1
+  // LDS operand addresses: a lane-constant part per operand column, computed
+  // once (the swizzles depend only on the lane's row within 16 or 4 rows), plus
+  // compile-time row offsets, so an operand read costs no address arithmetic.
+  // S operand i (0..23): key block mt = i & 1 (rows + 32, same swizzle), k-step ks = i >> 1
   const int krow = lane & 31;
+  int kbase[DN / 16], rbase[DR / 16];
+#pragma unroll
+  for (int ks = 0; ks < DN / 16; ++ks) kbase[ks] = kn_off(krow, (ks << 1) | hsel);
+#pragma unroll
+  for (int ks = 0; ks < DR / 16; ++ks) rbase[ks] = kr_off(krow, (ks << 1) | hsel);
   auto kread = [&](int i, auto bufc) -> V8 {
     constexpr int buf = decltype(bufc)::value;
-    const int row = (i & 1) * 32 + krow, ks = i >> 1;
-    if (ks < DN / 16) return *(const V8*)&sKn[buf][kn_off(row, (ks << 1) | hsel)];
-    return *(const V8*)&sKr[buf][kr_off(row, ((ks - DN / 16) << 1) | hsel)];
+    const int mt = i & 1, ks = i >> 1;
+    if (ks < DN / 16) return *(const V8*)&sKn[buf][kbase[ks] + mt * 32 * DN];
+    return *(const V8*)&sKr[buf][rbase[ks - DN / 16] + mt * 32 * DR];
   };
-  // PV operand i (0..15): key group j = i >> 2 (16 keys), dv block d = i & 3
+  // PV operand i (0..15): key group j = i >> 2 (16 keys: rows (j/2)*32 + (j%2)*16
+  // + 4 (g/2) + L/4, and + 8), dv block d = i & 3; the V swizzle depends on the
+  // row only through row & 3, the same for every j and both halves
   const int grp = lane >> 4, L16 = lane & 15;
+  int vbase[DV / 32];
+#pragma unroll
+  for (int d = 0; d < DV / 32; ++d)
+    vbase[d] = voff((grp >> 1) * 4 + (L16 >> 2), d * 32 + (grp & 1) * 16 + 4 * (L16 & 3));
   auto vread = [&](int i, auto bufc) -> V8 {
     constexpr int buf = decltype(bufc)::value;
     const int j = i >> 2, d = i & 3;
-    const int kr = (j >> 1) * 32 + (j & 1) * 16 + (grp >> 1) * 4 + (L16 >> 2);
-    const int nb = d * 32 + (grp & 1) * 16 + 4 * (L16 & 3);
-    const V4 lo = read_tr<V4>(&sV[buf][voff(kr, nb)]);
-    const V4 hi = read_tr<V4>(&sV[buf][voff(kr + 8, nb)]);
+    const int r0 = ((j >> 1) * 32 + (j & 1) * 16) * DV;
+    const V4 lo = read_tr<V4>(&sV[buf][vbase[d] + r0]);
+    const V4 hi = read_tr<V4>(&sV[buf][vbase[d] + r0 + 8 * DV]);
     return cat8(lo, hi);
   };
   constexpr int SD = 4;   // S operand reads in flight
