@@ -19,11 +19,13 @@
 // reads are issued several MFMAs ahead of their use.
 //
 // Softmax: fp32, exp2 with the scale folded in.  The exponent origin m is
-// moved only when a score exceeds it by more than 2^8 (in base-2 units), so
-// most tiles skip rescaling the accumulators; P = 2^(s - m) <= 256 is rounded
-// to the operand type (bf16, or fp16 inside the prefill layer) for the PV
-// MFMA.  O / l is formed in fp32 and rounded once to bf16.  d_v = 128 is used
-// as is: v is never padded to d_qk.
+// kept as long as every lane's sum of P = 2^(s - m) over a tile stays at or
+// below 2^15 (so no P exceeds it): most tiles need neither the tile's max nor
+// a rescale of the accumulators.  Otherwise (and on a wave's first tile) the
+// max is taken and m moves when a score exceeds it by more than 8 in base-2
+// units.  P is rounded to the operand type (bf16, or fp16 inside the prefill
+// layer) for the PV MFMA; O / l is formed in fp32 and rounded once to bf16.
+// d_v = 128 is used as is: v is never padded to d_qk.
 //
 // Work order: the workgroups of one head are kept on one XCD (workgroup i runs
 // on XCD i mod 8), all of that head's query tiles back to back, so the causal
@@ -40,6 +42,7 @@ constexpr int FQ = 128, FK = 64;
 constexpr int DN = 128, DR = 64, DQK = 192, DV = 128;
 constexpr int MAX_TILES = 880;
 constexpr float kRescaleSlack = 8.f;  // base-2 headroom before the exponent origin moves
+constexpr float kPSumMax = 32768.f;   // a lane's sum of P (32 keys) accepted against the current origin
 
 struct TilePlan {
   int n;                              // query tiles per head in this launch
@@ -274,34 +277,50 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashArgs a, TilePla
             if (key > my_q) s[mt][e] = -INFINITY;
           }
       }
-      // ---- online softmax (one query per lane, keys split across lane and lane^32)
-      float mx = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mt][e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c2;
-      if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRescaleSlack) != 0) {
-        const float m_new = fmaxf(m_ref, mx);
-        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-        m_ref = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int d = 0; d < DV / 32; ++d)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
-      }
-      const float mb = (m_ref == -INFINITY) ? 0.f : m_ref;
+      // ---- online softmax (one query per lane, keys split across lane and lane^32).
+      // Once every lane has an exponent origin, P is formed against it
+      // directly and accepted if no lane's sum of P exceeds 2^15 (then every P
+      // is at most 2^15, exact in range for the operand type); otherwise, and
+      // on a wave's first tile, the tile's max is taken and the origin moved
+      // (by the slack rule, which then always applies) before P is formed.
       V8 pb[4];
+      auto probs = [&](float mb) __attribute__((always_inline)) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          pb[mt * 2 + (e >> 3)][e & 7] = (T)__builtin_amdgcn_exp2f(fmaf(s[mt][e], c2, -mb));
-      float ps0 = sum8(pb[0], 0.f), ps1 = sum8(pb[1], 0.f);
-      ps0 = sum8(pb[2], ps0);
-      ps1 = sum8(pb[3], ps1);
-      l_run += ps0 + ps1;
+          for (int e = 0; e < 16; ++e)
+            pb[mt * 2 + (e >> 3)][e & 7] = (T)__builtin_amdgcn_exp2f(fmaf(s[mt][e], c2, -mb));
+        float ps0 = sum8(pb[0], 0.f), ps1 = sum8(pb[1], 0.f);
+        ps0 = sum8(pb[2], ps0);
+        ps1 = sum8(pb[3], ps1);
+        return ps0 + ps1;
+      };
+      float ps = 0.f;
+      bool redo = __builtin_amdgcn_ballot_w64(m_ref == -INFINITY) != 0;
+      if (!redo) {
+        ps = probs(m_ref);
+        redo = __builtin_amdgcn_ballot_w64(!(ps <= kPSumMax)) != 0;
+      }
+      if (redo) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mt][e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c2;
+        if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRescaleSlack) != 0) {
+          const float m_new = fmaxf(m_ref, mx);
+          const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+          m_ref = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
+        }
+        ps = probs((m_ref == -INFINITY) ? 0.f : m_ref);
+      }
+      l_run += ps;
       // ---- O^T += V^T P^T ; step j covers keys (j/2)*32 + (j%2)*16 + {h*4+0..3, 8+h*4+0..3}
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
