@@ -502,34 +502,36 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(DecodeArgs a) {
   }
 }
 
-// Combine and un-absorb, fused.  Workgroup (h, block of 16 sequences):
+// Combine and un-absorb, fused.  Workgroup (h, block of 32 sequences), 8
+// waves:
 //  1. o_lat[b, h, :] = sum_s w_s l_s (O_s / l_s) / sum_s w_s l_s over the
 //     sequence's slots s, with w_s = 2^((m_s - M) * c2); slots emptied by a
 //     cut (l_s = 0) are skipped.  Rounded to bf16 into LDS; each wave takes 4
 //     sequences, two at a time with all their slots loaded before any is used,
 //     8 latent dims per lane.
-//  2. out[b, h, :] = W_UV[h] . o_lat[b, h, :] for the 16 sequences at once:
+//  2. out[b, h, :] = W_UV[h] . o_lat[b, h, :] for the 32 sequences at once:
 //     O^T[dv, b] = W_UV[h][dv, :] . o_lat[b, :]^T on 16x16x32 MFMAs, each wave
-//     32 output dims.  Its W_UV rows are requested while step 1 runs.
-// The workgroups of one head run on one XCD (x = h), so W_UV[h] is read from
-// HBM about once.
-constexpr int CB = 16;                     // sequences per combine workgroup
+//     16 output dims for both blocks of 16 sequences.  Its W_UV rows are
+//     requested while step 1 runs.
+// W_UV[h] (128 KB) is read once per 32 sequences; the workgroups of one head
+// run on one XCD (x = h), so it comes from HBM about once.
+constexpr int CB = 32;                     // sequences per combine workgroup
 constexpr int CMAXS = 8;                   // slots per sequence loaded at once
-__global__ __launch_bounds__(256, 2) void decode_combine_unabsorb_kernel(DecodeArgs a) {
+constexpr int CNW = 8;                     // waves per combine workgroup
+__global__ __launch_bounds__(CNW * 64, 1) void decode_combine_unabsorb_kernel(DecodeArgs a) {
   // latent rows of the block: 16 B chunk c of row j at c ^ (j & 15), so the
   // 16 rows one MFMA operand read touches spread over the banks
   __shared__ __attribute__((aligned(16))) bf16 sO[CB * RK];
   __shared__ int s_ns[CB];
-  __shared__ long long s_red[4];
+  __shared__ long long s_red[CNW];
   const int h = blockIdx.x, b0 = blockIdx.y * CB;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = a.heads, B = a.batch;
   const int cap = a.max_blocks << a.log2_block;
   const int64_t R = a.quota;
-  // start of sequence b0 in the concatenated key order, then the slot counts
-  // of b0 .. b0 + 15
+  // work-order position of sequence b0, then the slot counts of b0 .. b0 + 31
   long long part_sum = 0;
-  for (int i = tid; i < b0; i += 256) {
+  for (int i = tid; i < b0; i += CNW * 64) {
     const int Li = max(0, min(a.seq_lens[i], cap));
     part_sum += Li > 0 ? (long long)Li + kDecodeSegmentCost : 0;
   }
@@ -537,7 +539,9 @@ __global__ __launch_bounds__(256, 2) void decode_combine_unabsorb_kernel(DecodeA
   if (lane == 0) s_red[wave] = part_sum;
   __syncthreads();
   if (wave == 0) {
-    const long long base = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+    long long base = 0;
+#pragma unroll
+    for (int w = 0; w < CNW; ++w) base += s_red[w];
     const int b = b0 + lane;
     const int Lb = (lane < CB && b < B) ? max(0, min(a.seq_lens[b], cap)) : 0;
     const long long n = Lb > 0 ? (long long)Lb + kDecodeSegmentCost : 0;
@@ -553,10 +557,10 @@ __global__ __launch_bounds__(256, 2) void decode_combine_unabsorb_kernel(DecodeA
   __syncthreads();
 
   const float c2 = a.scale * kLog2e;
-  // A operand of the un-absorb: lane holds row 32 w + 16 mt + lane % 16 of
-  // W_UV[h], k = 32 ks + (lane / 16) * 8 + [0, 8)
+  // A operand of the un-absorb: lane holds row 16 w + lane % 16 of W_UV[h],
+  // k = 32 ks + (lane / 16) * 8 + [0, 8)
   const int r16 = lane & 15, kq = lane >> 4;
-  bf16x8 wf[2][RK / 32];
+  bf16x8 wf[RK / 32];
   for (int j2 = 0; j2 < 2; ++j2) {
     float mv[2][CMAXS], lv[2][CMAXS];
     f16x8 pv[2][CMAXS];
@@ -566,7 +570,7 @@ __global__ __launch_bounds__(256, 2) void decode_combine_unabsorb_kernel(DecodeA
     for (int u = 0; u < 2; ++u) {
       const int j = wave * 4 + j2 * 2 + u, b = b0 + j;
       nslot[u] = s_ns[j];                                // 0 past the batch
-      part0[u] = (int64_t)b * a.max_slots * H + h;     // slot s at part0 + s * H
+      part0[u] = (int64_t)b * a.max_slots * H + h;       // slot s at part0 + s * H
 #pragma unroll
       for (int sl = 0; sl < CMAXS; ++sl) {
         if (sl < nslot[u]) {
@@ -582,11 +586,9 @@ __global__ __launch_bounds__(256, 2) void decode_combine_unabsorb_kernel(DecodeA
       }
     }
     if (j2 == 0) {                         // behind the first partials, ahead of the second
-      const bf16* wr = a.w_uv + (int64_t)h * a.w_uv_hstride + (int64_t)(32 * wave + r16) * RK + kq * 8;
+      const bf16* wr = a.w_uv + (int64_t)h * a.w_uv_hstride + (int64_t)(16 * wave + r16) * RK + kq * 8;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int ks = 0; ks < RK / 32; ++ks) wf[mt][ks] = *(const bf16x8*)(wr + mt * 16 * RK + ks * 32);
+      for (int ks = 0; ks < RK / 32; ++ks) wf[ks] = *(const bf16x8*)(wr + ks * 32);
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -632,29 +634,31 @@ __global__ __launch_bounds__(256, 2) void decode_combine_unabsorb_kernel(DecodeA
   }
   __syncthreads();
 
-  // O^T[dv, b]: wave w takes output dims 32 w .. 32 w + 31 (dv = 128); the B
-  // operand lane holds sequence b0 + lane % 16, k = 32 ks + (lane / 16) * 8
+  // O^T[dv, b]: wave w takes output dims 16 w .. 16 w + 15 (dv = 128) for
+  // sequence blocks n = 0, 1; the B operand lane holds sequence b0 + 16 n +
+  // lane % 16, k = 32 ks + (lane / 16) * 8
   f32x4 o[2];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int n = 0; n < 2; ++n)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o[mt][e] = 0.f;
+    for (int e = 0; e < 4; ++e) o[n][e] = 0.f;
 #pragma unroll
-  for (int ks = 0; ks < RK / 32; ++ks) {
-    const bf16x8 Bv = *(const bf16x8*)&sO[r16 * RK + (((ks * 4 + kq) ^ r16) << 3)];
+  for (int ks = 0; ks < RK / 32; ++ks)
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) o[mt] = mfma16(wf[mt][ks], Bv, o[mt]);
-  }
-  // lane holds sequence b0 + lane % 16, dims 32 w + 16 mt + (lane / 16) * 4 + [0, 4)
-  const int b = b0 + r16;
-  if (b < B) {
-    bf16* orow = a.out + ((int64_t)b * H + h) * a.dv + 32 * wave + kq * 4;
+    for (int n = 0; n < 2; ++n) {
+      const int j = n * 16 + r16;
+      const bf16x8 Bv = *(const bf16x8*)&sO[j * RK + (((ks * 4 + kq) ^ (j & 15)) << 3)];
+      o[n] = mfma16(wf[ks], Bv, o[n]);
+    }
+  // lane holds sequence b0 + 16 n + lane % 16, dims 16 w + (lane / 16) * 4 + [0, 4)
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+  for (int n = 0; n < 2; ++n) {
+    const int b = b0 + n * 16 + r16;
+    if (b < B) {
       bf16x4 v;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = (bf16)o[mt][e];
-      *(bf16x4*)(orow + mt * 16) = v;
+      for (int e = 0; e < 4; ++e) v[e] = (bf16)o[n][e];
+      *(bf16x4*)(a.out + ((int64_t)b * H + h) * a.dv + 16 * wave + kq * 4) = v;
     }
   }
 }
@@ -682,7 +686,7 @@ hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s) {
 hipError_t launch_decode_combine_unabsorb(const DecodeArgs& a, hipStream_t s) {
   if (a.dv != 128) return hipErrorInvalidValue;
   dim3 grid(a.heads, (a.batch + CB - 1) / CB);
-  decode_combine_unabsorb_kernel<<<grid, 256, 0, s>>>(a);
+  decode_combine_unabsorb_kernel<<<grid, CNW * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 
