@@ -245,6 +245,9 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashArgs a, TilePla
     const T* kvn = kv_head + (int64_t)kn * kv_row;
     const T* kpn = KPE + (int64_t)kn * a.kpe_stride;
     if (active) {
+      // MFMA phases run at a raised wave priority, so that when the other wave
+      // on this SIMD is in its softmax the MFMAs issue first
+      __builtin_amdgcn_s_setprio(2);
       // ---- S^T for 64 keys (2 blocks of 32) x 32 queries, operands read SD ahead
       f32x16 s[2];
 #pragma unroll
@@ -277,6 +280,7 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashArgs a, TilePla
             if (key > my_q) s[mt][e] = -INFINITY;
           }
       }
+      __builtin_amdgcn_s_setprio(0);
       // ---- online softmax (one query per lane, keys split across lane and lane^32).
       // Once every lane has an exponent origin, P is formed against it
       // directly and accepted if no lane's sum of P exceeds 2^15 (then every P
@@ -321,6 +325,7 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashArgs a, TilePla
         ps = probs((m_ref == -INFINITY) ? 0.f : m_ref);
       }
       l_run += ps;
+      __builtin_amdgcn_s_setprio(2);
       // ---- O^T += V^T P^T ; step j covers keys (j/2)*32 + (j%2)*16 + {h*4+0..3, 8+h*4+0..3}
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -331,6 +336,7 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashArgs a, TilePla
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
     if (t + 1 < ntiles) vm_wait_all();
     wg_barrier();
   };
