@@ -28,8 +28,9 @@
 // d_v = 128 is used as is: v is never padded to d_qk.
 //
 // Work order: the workgroups of one head are kept on one XCD (workgroup i runs
-// on XCD i mod 8), all of that head's query tiles back to back, so the causal
-// tiles that stream the same k/v rows at the same time share that XCD's L2.
+// on XCD i mod 8), so the tiles that stream the same k/v rows share that XCD's
+// L2; each XCD takes its tiles longest first across all its heads, so that
+// the last workgroups to start are short ones.
 #include "mla_internal.hpp"
 
 #include <vector>
@@ -100,9 +101,11 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashArgs a, TilePla
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = a.heads;
-  // workgroup -> (head, tile): XCD x = blockIdx % 8 takes heads x, x+8, ...
+  // workgroup -> (head, tile): XCD x = blockIdx % 8 takes heads x, x+8, ...;
+  // within an XCD the tiles go out longest first across all its heads (tile
+  // index major), so no long tile starts late
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int hj = slot / plan.n, ti = slot - hj * plan.n;
+  const int ti = slot / plan.heads_per_xcd, hj = slot - ti * plan.heads_per_xcd;
   const int head = xcd + 8 * hj;
   if (head >= H) return;
   const uint32_t td = plan.t[ti];
