@@ -108,6 +108,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
   constexpr int BPW = BLOCKS / NW;
   __shared__ __attribute__((aligned(16))) bf16 sC[NBUF][DKT * RC];
   __shared__ int sBlk[kDecodeMaxChunkBlocks];
+  __shared__ int s_badw[NW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = a.heads;
@@ -172,24 +173,55 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
   }
   const int nt = (k1 - k0 + DKT - 1) / DKT;
 
-  // the chunk's block ids; an id outside the pool poisons this sequence's output
+  // The chunk's block ids are requested first, then the absorbed query; the
+  // ids are waited for (loads complete in order) while the query is still in
+  // flight.  An id outside the pool poisons this sequence's output.
   const int blk0 = k0 >> lbs;
   const int nblk = ((k1 - 1) >> lbs) - blk0 + 1;
-  int bad = 0;
-  for (int i = tid; i < nblk; i += NTH) {
-    const int v = a.block_table[(int64_t)b * a.max_blocks + blk0 + i];
-    bad |= (v < 0 || v >= a.num_blocks);
-    sBlk[i] = v;
+  constexpr int TBL = (kDecodeMaxChunkBlocks + NTH - 1) / NTH;
+  int tv[TBL];
+#pragma unroll
+  for (int u = 0; u < TBL; ++u) {
+    const int i = tid + u * NTH;
+    tv[u] = i < nblk ? a.block_table[(int64_t)b * a.max_blocks + blk0 + i] : 0;
   }
-  if (__syncthreads_or(bad)) {
+  __builtin_amdgcn_sched_barrier(0);
+  const int hsel = lane >> 5;
+  const int my_h = wave * 32 + (lane & 31);
+  bf16x8 qreg[RC / 16];                  // absorbed query, in registers for the whole segment
+  {
+    const bf16* qt = a.qt + ((int64_t)b * H + my_h) * RK;
+    const bf16* qp = a.q_pe + ((int64_t)b * H + my_h) * DRP;
+#pragma unroll
+    for (int ks = 0; ks < RC / 16; ++ks) {
+      const int d = ks * 16 + hsel * 8;
+      qreg[ks] = (d < RK) ? *(const bf16x8*)(qt + d) : *(const bf16x8*)(qp + d - RK);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  int bad = 0;
+#pragma unroll
+  for (int u = 0; u < TBL; ++u) {
+    const int i = tid + u * NTH;
+    if (i < nblk) {
+      bad |= (tv[u] < 0 || tv[u] >= a.num_blocks);
+      sBlk[i] = tv[u];
+    }
+  }
+  // workgroup OR of the flags, one word per wave (no zeroing needed), behind
+  // an LDS-only wait so that the query stays in flight
+  const bool wbad = __builtin_amdgcn_ballot_w64(bad != 0) != 0;
+  if (lane == 0) s_badw[wave] = wbad;
+  lds_wait_all();
+  wg_barrier();
+  int anybad = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) anybad |= s_badw[w];
+  if (anybad) {
     for (int i = tid; i < H * RK; i += NTH) a.part_o[part * RK + i] = (f16)__builtin_nanf("");
     for (int i = tid; i < H; i += NTH) { a.part_ml[(part + i) * 2] = 0.f; a.part_ml[(part + i) * 2 + 1] = __builtin_nanf(""); }
     continue;
   }
-
-  const int hsel = lane >> 5;
-  const int my_h = wave * 32 + (lane & 31);
-  bf16x8 qreg[RC / 16];                  // absorbed query, loaded behind the first tiles
 
   // Lane-constant parts of the swizzled LDS addresses (elements); the rest of
   // every address is a compile-time offset.
@@ -302,8 +334,12 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
     exact_path |= __builtin_amdgcn_ballot_w64((mx - m_ref) * c2 > kMaxExcursion) != 0;
     mb = m_ref * c2;
   };
+  // The opaque statement keeps each probability between the MFMAs it was
+  // placed among: without it the compiler sinks all of them past the branches
+  // of the copy issue, into one block of VALU work that stalls the MFMA chain.
   auto prob = [&](f32x16& s, int e) __attribute__((always_inline)) {
-    const float p = __builtin_amdgcn_exp2f(fmaf(s[e], c2, -mb));
+    float p = __builtin_amdgcn_exp2f(fmaf(s[e], c2, -mb));
+    asm volatile("" : "+v"(p));
     l_run += p;
     pb[e >> 3][e & 7] = (bf16)p;
   };
@@ -370,23 +406,17 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
     wg_barrier();
   };
 
-#pragma unroll
-  for (int t = 0; t < NBUF - 1; ++t)
-    if (t < nt) issue_tile(t, t);
-  // The query, behind the first tiles.  Everything in flight has landed before
-  // the loop starts: the tile copies are issued from inline asm, so the waits
-  // inside the loop count only them.
-  {
-    const bf16* qt = a.qt + ((int64_t)b * H + my_h) * RK;
-    const bf16* qp = a.q_pe + ((int64_t)b * H + my_h) * DRP;
-#pragma unroll
-    for (int ks = 0; ks < RC / 16; ++ks) {
-      const int d = ks * 16 + hsel * 8;
-      qreg[ks] = (d < RK) ? *(const bf16x8*)(qt + d) : *(const bf16x8*)(qp + d - RK);
-    }
-  }
+  // Tiles 0 and 1 and the query land before the loop starts; tile 2 is
+  // requested after that, so the waits inside the loop count only tile
+  // copies (the compiler's own waits for the query are all met here: the
+  // empty statements use every query register).
+  issue_tile(0, 0);
+  if (1 < nt) issue_tile(1, 1);
   vm_wait_all();
+#pragma unroll
+  for (int ks = 0; ks < RC / 16; ++ks) asm volatile("" : : "v"(qreg[ks]));
   wg_barrier();
+  if (2 < nt) issue_tile(2, 2);
   f32x16 sa, sbv;
   s_tile(sa, 0, no_group);
   for (int t = 0; t < nt; ++t) {
