@@ -38,7 +38,7 @@ import numpy as np
 __all__ = [
     "MLAShape", "RopeSpec", "WORKLOADS", "bf16_round", "bf16_bits",
     "bf16_from_bits", "make_prefill_case", "make_decode_case", "PrefillCase",
-    "DecodeCase", "doc_lengths_for",
+    "DecodeCase", "doc_lengths_for", "ChunkCase", "make_chunk_case",
 ]
 
 
@@ -261,3 +261,55 @@ def make_decode_case(shape: MLAShape, batch: int = 64, len_lo: int = 1024, len_h
                 cache[table[b, last], used:, :] = np.nan
     return DecodeCase(shape=shape, w_kv_b=w_kv_b, q_nope=q_nope, q_pe=q_pe, cache=cache,
                       block_table=table, seq_lens=lens.astype(np.int32), block_size=block_size)
+
+
+@dataclasses.dataclass
+class ChunkCase:
+    """New tokens of sequences whose first tokens are already cached."""
+    shape: MLAShape
+    x: np.ndarray                   # [N, hidden] new tokens, packed by cu_seqlens
+    w: Dict[str, Optional[np.ndarray]]
+    cu_seqlens: np.ndarray          # [S+1] int32 (new tokens)
+    prefix_lens: np.ndarray         # [S] int32 cached tokens per sequence
+    cache: np.ndarray               # [n_blocks, block_size, kv_lora+rope] the cached latent rows
+    block_table: np.ndarray         # [S, max_blocks] int32, -1 for unused entries
+    block_size: int
+
+
+def make_chunk_case(shape: MLAShape, chunk_lens: Sequence[int], prefix_lens: Sequence[int],
+                    block_size: int = 64, max_blocks: Optional[int] = None, poison_tail: bool = True,
+                    seed: Optional[int] = None) -> ChunkCase:
+    """Seeded inputs of a prefill chunk over a cached prefix: the layer inputs
+    of ``make_prefill_case`` for the new tokens (documents = ``chunk_lens``),
+    then, from a second stream seeded with seed + 1000, the block permutation
+    and the cached latent rows (N(0, 1), the scale of a normalised latent and
+    of the shared rope key), bf16 for bf16 workloads.  Each sequence's blocks
+    hold only its prefix; slots past it are NaN when ``poison_tail`` is set
+    (they must never be read).  A sequence with prefix 0 owns no block."""
+    base = make_prefill_case(shape, doc_lengths=chunk_lens, seed=seed)
+    pre = np.asarray(prefix_lens, dtype=np.int64)
+    assert len(pre) == len(chunk_lens)
+    rng = np.random.Generator(np.random.PCG64((shape.seed if seed is None else seed) + 1000))
+    width = shape.kv_lora_rank + shape.qk_rope_dim
+    nblk = (pre + block_size - 1) // block_size
+    pool = max(1, int(nblk.sum()))
+    mb = max(1, int(nblk.max())) if max_blocks is None else max_blocks
+    assert mb >= int(nblk.max())
+    perm = rng.permutation(pool).astype(np.int32)                               # 1
+    table = np.full((len(pre), mb), -1, dtype=np.int32)
+    o = 0
+    for b in range(len(pre)):
+        table[b, : nblk[b]] = perm[o: o + nblk[b]]
+        o += nblk[b]
+    cache = _normal(rng, (pool, block_size, width), 1.0)                        # 2
+    if shape.dtype == "bf16":
+        cache = bf16_round(cache)
+    if poison_tail:
+        used = np.zeros(pool, dtype=np.int64)
+        for b in range(len(pre)):
+            for i in range(nblk[b]):
+                used[table[b, i]] = min(block_size, int(pre[b]) - i * block_size)
+        for blk in range(pool):
+            cache[blk, used[blk]:, :] = np.nan
+    return ChunkCase(shape=shape, x=base.x, w=base.w, cu_seqlens=base.cu_seqlens,
+                     prefix_lens=pre.astype(np.int32), cache=cache, block_table=table, block_size=block_size)

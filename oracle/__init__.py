@@ -16,11 +16,13 @@ Everything is float64 NumPy (``mla.py``) or pure-Python scalar loops
 * "kimi_vl.py - KimiVL (DeepSeek-V3 architecture) attention adapter", sections
   "Q projection and KV compression" and "concatenating the final Q and K".
 * "MiniMind: attention forward pass", section 3 (RMSNorm in fp32, rotate_half
-  RoPE), section 5 (scaled dot product, causal mask, fp32 softmax), section 7
+  RoPE), section 5 (scaled dot product, causal mask, fp32 softmax, and the mask
+  of a forward with a cache: only the new T x T block is triangular), section 7
   (merge heads, output projection).
 * "Megatron-LM MLA guide", sections on projection dimensions, YaRN parameters,
-  softmax scale, THD packing and the inference section (latent cache and weight
-  absorption).
+  softmax scale, THD packing and the inference section (latent cache, weight
+  absorption for decode-only steps, decompression of the cached latents for
+  prefill and mixed steps).
 * "Kimi-K3 atlas: Gated MLA" (mla-init, mla-forward, rmsnorm excerpts): the
   unrotated shared key part and the full-rank output gate.
 
@@ -35,5 +37,5 @@ from .mla import (  # noqa: F401
     rms_norm, yarn_get_mscale, softmax_scale, rope_inv_freq, rope_cos_sin,
     rotate_half, apply_rope, causal_varlen_attention, mla_prefill, mla_prefill_rows,
     kv_latent, gather_paged, decode_naive, decode_absorbed, prefill_latent_absorbed,
-    row_rel_error, bf16_excess_error,
+    row_rel_error, bf16_excess_error, prefix_causal_attention, mla_prefill_with_prefix,
 )

@@ -403,6 +403,95 @@ def decode_absorbed(shape, w_kv_b, q_nope, q_pe, cache, block_table, seq_lens, b
 
 
 # ----------------------------------------------------------------------------
+# Prefill of a new chunk over a cached prefix
+# ----------------------------------------------------------------------------
+def prefix_causal_attention(q, k, v, scale: float, prefix: int, rows: Optional[Sequence[int]] = None):
+    """Attention of T new queries over P cached + T new keys of one sequence.
+
+    q [T, H, d_qk], k [P + T, H, d_qk], v [P + T, H, d_v] -> [T, H, d_v].
+    With ``rows``, q holds only the queries rows[0], rows[1], ... (indices in
+    0 .. T-1) and the result has len(rows) rows.  Query i stands at
+    position P + i; it sees every cached key and the new keys up to itself:
+    keys j <= P + i.  This is the causal mask of "MiniMind: attention forward
+    pass" section 5 for a forward with a cache: the upper triangle is masked
+    only inside the last T x T block of the score matrix, every column of the
+    history stays visible, and a single query (T = 1) is masked nowhere.
+
+    Pinned by: P = 0 equals ``causal_varlen_attention``; a full causal run
+    over P + T tokens restricted to its last T rows equals this with the first
+    P keys as the prefix; T = 1 equals the non-absorbed decode.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    t = k.shape[0] - prefix
+    sel = np.arange(t) if rows is None else np.asarray(rows, dtype=np.int64)
+    assert q.shape[0] == len(sel) and v.shape[0] == k.shape[0] and np.all((sel >= 0) & (sel < t))
+    out = np.empty((len(sel), q.shape[1], v.shape[-1]), dtype=F64)
+    for r, i in enumerate(sel):
+        last = prefix + int(i)                                   # last visible key
+        s = scale * np.einsum("hd,lhd->hl", q[r], k[: last + 1])
+        p = _softmax_rows(s)
+        out[r] = np.einsum("hl,lhd->hd", p, v[: last + 1])
+    return out
+
+
+def mla_prefill_with_prefix(shape, w: Dict[str, np.ndarray], x, cu_seqlens, prefix_lens, cache, block_table,
+                            block_size: int, rows: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
+    """The MLA layer for new tokens of sequences whose first tokens are
+    already in the paged latent cache (chunked prefill, mixed prefill/decode).
+
+    x [N, hidden] holds the new tokens packed by ``cu_seqlens``; sequence s
+    has ``prefix_lens[s]`` = P_s cached tokens, read from the pool ``cache``
+    [n_blocks, block_size, r_kv + d_rope] through ``block_table`` (rows
+    [c_n | k_pe'] as the decode path stores them).  New token i of s stands at
+    position P_s + i (its q_pe and k_pe are rotated there).  The cached
+    latents are decompressed with the same kv up-projection as the new
+    tokens' ("Megatron-LM MLA guide", inference section: prefill and mixed
+    steps decompress k/v from the cached latents, only decode-only steps use
+    the absorbed form), keys [k_nope_h | k_pe'] over P_s + T_s tokens, and
+    query i attends to keys 0 .. P_s + i (``prefix_causal_attention``).  Gate
+    and output projection as in ``mla_prefill``.
+
+    ``rows`` restricts the returned query rows (global indices into x).
+    Returns the output, the new tokens' latent rows and the attention result.
+    """
+    x = _f64(x)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    pre = np.asarray(prefix_lens, dtype=np.int64)
+    n = x.shape[0]
+    H, nope, dr, dv, r = shape.num_heads, shape.qk_nope_dim, shape.qk_rope_dim, shape.v_head_dim, shape.kv_lora_rank
+    pos = np.empty(n, dtype=np.int64)
+    for d in range(len(cu) - 1):
+        pos[cu[d]: cu[d + 1]] = pre[d] + np.arange(cu[d + 1] - cu[d])
+    sel = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    lat = kv_latent(shape, w, x, pos)                                  # new tokens' cache rows
+    q = _q_proj(shape, w, x[sel]).reshape(len(sel), H, nope + dr)
+    q_nope, q_pe = q[..., :nope], q[..., nope:]
+    if shape.rope.kind != "none":
+        cos, sin = rope_cos_sin(pos[sel], dr, shape.rope)
+        q_pe = apply_rope(q_pe, cos[:, None, :], sin[:, None, :])
+    qf = np.concatenate([q_nope, q_pe], axis=-1)
+    W = _f64(w["w_kv_b"])
+    sc = softmax_scale(shape)
+    A = np.empty((len(sel), H, dv), dtype=F64)
+    doc = np.searchsorted(cu, sel, side="right") - 1
+    for d in range(len(cu) - 1):
+        mine = np.nonzero(doc == d)[0]
+        if len(mine) == 0:
+            continue
+        a, b = int(cu[d]), int(cu[d + 1])
+        ctx = np.concatenate([gather_paged(cache, block_table, d, int(pre[d]), block_size), lat[a:b]], axis=0)
+        kv = (ctx[:, :r] @ W.T).reshape(-1, H, nope + dv)
+        k = np.concatenate([kv[..., :nope], np.broadcast_to(ctx[:, None, r:], (ctx.shape[0], H, dr))], axis=-1)
+        A[mine] = prefix_causal_attention(qf[mine], k, kv[..., nope:], sc, int(pre[d]), rows=sel[mine] - a)
+    A2 = A.reshape(len(sel), H * dv)
+    if shape.output_gate:
+        g = x[sel] @ _f64(w["w_g"]).T
+        A2 = A2 * (1.0 / (1.0 + np.exp(-g)))
+    out = A2 @ _f64(w["w_o"]).T
+    return {"out": out, "attn": A2, "latent": lat, "q": qf, "positions": pos}
+
+
+# ----------------------------------------------------------------------------
 # Comparison metric
 # ----------------------------------------------------------------------------
 def bf16_excess_error(ref, got, rtol: float = 2.0 ** -7) -> float:

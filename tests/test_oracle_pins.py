@@ -389,3 +389,94 @@ def test_bf16_metrics():
     assert om.bf16_excess_error(y, bad) > 2e-2
     nan = yb.copy(); nan[0, 0] = np.nan
     assert om.bf16_excess_error(y, nan) == float("inf") and om.row_rel_error(y, nan) == float("inf")
+
+
+# ----------------------------------------------------------------------------- chunk over a cached prefix
+def test_prefix_attention_zero_prefix_is_causal_and_tail_of_full_run():
+    rng = np.random.default_rng(21)
+    P, T, H = 7, 5, 3
+    q = rng.standard_normal((P + T, H, 6))
+    k = rng.standard_normal((P + T, H, 6))
+    v = rng.standard_normal((P + T, H, 4))
+    full = om.causal_varlen_attention(q, k, v, 0.4, [0, P + T])
+    # no prefix: the plain causal run
+    assert np.allclose(om.prefix_causal_attention(q[:T], k[:T], v[:T], 0.4, 0),
+                       om.causal_varlen_attention(q[:T], k[:T], v[:T], 0.4, [0, T]), rtol=1e-13, atol=1e-15)
+    # the last T queries of a causal run over P + T tokens, with the first P as the prefix
+    got = om.prefix_causal_attention(q[P:], k, v, 0.4, P)
+    assert np.allclose(got, full[P:], rtol=1e-13, atol=1e-15)
+    # a query sees every cached key: perturbing any future new key leaves it unchanged
+    k2 = k.copy(); k2[P + 3:] += 5.0
+    got2 = om.prefix_causal_attention(q[P:], k2, v, 0.4, P)
+    assert np.array_equal(got2[:3], got[:3]) and not np.allclose(got2[3:], got[3:])
+
+
+def _paged_f64(rows, block_size, rng):
+    """Store rows [L, W] (float64) in a shuffled pool of blocks; returns cache, table row."""
+    nb = (len(rows) + block_size - 1) // block_size
+    perm = rng.permutation(nb + 2)[:nb]                # two spare blocks stay NaN
+    cache = np.full((nb + 2, block_size, rows.shape[1]), np.nan)
+    for i in range(nb):
+        part = rows[i * block_size:(i + 1) * block_size]
+        cache[perm[i], :len(part)] = part
+    return cache, perm
+
+
+@pytest.mark.parametrize("rope", ["plain", "yarn", "none"])
+def test_chunk_layer_equals_tail_of_full_prefill(rope):
+    """Two sequences prefilled whole (oracle prefill) versus their first P
+    tokens taken from a paged cache and the rest prefilled as a chunk: the
+    chunk's outputs and latent rows equal the whole run's last rows."""
+    spec = {"plain": mi.RopeSpec(kind="plain", theta=500.0),
+            "yarn": mi.RopeSpec(kind="yarn", theta=500.0, factor=4.0, original_max_pos=8, beta_fast=4.0,
+                                beta_slow=1.0, mscale=1.0, mscale_all_dim=1.0),
+            "none": mi.RopeSpec(kind="none")}[rope]
+    sh = tiny_shape(rope=spec, output_gate=(rope == "none"))
+    P, T = [6, 3], [4, 5]
+    full_case = mi.make_prefill_case(sh, doc_lengths=[P[0] + T[0], P[1] + T[1]], seed=5)
+    ref = om.mla_prefill(sh, full_case.w, full_case.x, full_case.cu_seqlens)
+    rng = np.random.default_rng(3)
+    bs = 4
+    cu_full = full_case.cu_seqlens
+    caches, tables = [], []
+    for d in range(2):
+        c, t = _paged_f64(ref["latent"][cu_full[d]: cu_full[d] + P[d]], bs, rng)
+        caches.append(c); tables.append(t)
+    # one pool: sequence 1's blocks after sequence 0's
+    off = caches[0].shape[0]
+    cache = np.concatenate(caches, axis=0)
+    mb = max(len(t) for t in tables)
+    table = np.full((2, mb), -1, dtype=np.int64)
+    table[0, :len(tables[0])] = tables[0]
+    table[1, :len(tables[1])] = tables[1] + off
+    new_rows = np.concatenate([np.arange(cu_full[d] + P[d], cu_full[d + 1]) for d in range(2)])
+    x_new = full_case.x[new_rows]
+    cu_new = np.array([0, T[0], T[0] + T[1]])
+    got = om.mla_prefill_with_prefix(sh, full_case.w, x_new, cu_new, P, cache, table, bs)
+    assert np.allclose(got["out"], ref["out"][new_rows], rtol=1e-11, atol=1e-13)
+    assert np.allclose(got["latent"], ref["latent"][new_rows], rtol=1e-12, atol=1e-14)
+    assert np.array_equal(got["positions"], [6, 7, 8, 9, 3, 4, 5, 6, 7])
+    # the rows variant returns the same rows
+    part = om.mla_prefill_with_prefix(sh, full_case.w, x_new, cu_new, P, cache, table, bs, rows=[8, 0, 4])
+    assert np.allclose(part["out"], got["out"][[8, 0, 4]], rtol=1e-13, atol=1e-15)
+
+
+def test_chunk_single_query_equals_decode():
+    """T = 1 per sequence: the new token attends to all P + 1 keys, which is
+    the non-absorbed decode over the cache with the token's own row added."""
+    sh = tiny_shape(rope=mi.RopeSpec(kind="plain", theta=100.0))
+    c = mi.make_chunk_case(sh, [1, 1, 1], [5, 1, 9], block_size=4, poison_tail=False, seed=7)
+    got = om.mla_prefill_with_prefix(sh, c.w, c.x, c.cu_seqlens, c.prefix_lens, c.cache, c.block_table, 4)
+    H, nope, dr, dv = sh.num_heads, sh.qk_nope_dim, sh.qk_rope_dim, sh.v_head_dim
+    # append each token's own latent row to its sequence (one fresh block each)
+    pool = np.concatenate([c.cache.astype(np.float64), np.zeros((3, 4, c.cache.shape[2]))], axis=0)
+    table = np.concatenate([c.block_table.astype(np.int64), np.full((3, 1), -1)], axis=1)
+    lens = c.prefix_lens.astype(np.int64) + 1
+    for b in range(3):
+        P = int(c.prefix_lens[b])
+        if P % 4 == 0:
+            table[b, P // 4] = c.cache.shape[0] + b
+        pool[table[b, P // 4], P % 4] = got["latent"][b]
+    A = om.decode_naive(sh, c.w["w_kv_b"], got["q"][:, :, :nope], got["q"][:, :, nope:], pool, table, lens, 4)
+    assert np.allclose(got["attn"].reshape(3, H, dv), A, rtol=1e-12, atol=1e-14)
+    assert not np.any(np.isnan(got["out"]))
