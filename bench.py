@@ -47,8 +47,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--prefill", default="dsv3_prefill_4096")
     ap.add_argument("--decode", default="dsv3_decode_64")
+    ap.add_argument("--chunk", default="dsv3_chunk_4x1024_p4096",
+                    help="chunked-prefill workload reported beside the metric ('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["full", "prefill", "attention", "decode", "copy"], default="full",
+    ap.add_argument("--mode", choices=["full", "prefill", "attention", "decode", "copy", "chunk", "chunk_attention"],
+                    default="full",
                     help="full: the JSON line; the others only run that part's timing loop (for profilers)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for the CPU baseline")
     return ap.parse_args()
@@ -59,6 +62,19 @@ def attention_flops(shape, cu):
     for a, b in zip(cu[:-1], cu[1:]):
         t = int(b) - int(a)
         s += t * (t + 1) // 2
+    return 2 * (shape.qk_head_dim + shape.v_head_dim) * shape.num_heads * s
+
+
+# Chunked prefill over a cached prefix: (layer shape, new tokens per sequence,
+# cached tokens per sequence).  DeepSeek-V3 shape, four sequences each
+# continuing 4096 cached tokens with a 1024-token chunk.
+CHUNK_WORKLOADS = {"dsv3_chunk_4x1024_p4096": ("dsv3_prefill_4096", [1024] * 4, [4096] * 4)}
+
+
+def prefix_attention_flops(shape, chunks, prefixes):
+    s = 0
+    for t, p in zip(chunks, prefixes):
+        s += t * p + t * (t + 1) // 2          # query i sees p + i + 1 keys
     return 2 * (shape.qk_head_dim + shape.v_head_dim) * shape.num_heads * s
 
 
@@ -210,6 +226,49 @@ def main():
     max_blocks = dc.block_table.shape[1]
     del dc
 
+    # ------------------------------------------------------------------ chunked prefill inputs
+    chunk = None
+    if args.chunk != "none":
+        cname, cch, cpre = CHUNK_WORKLOADS[args.chunk]
+        csh = mi.WORKLOADS[cname]
+        cc = mi.make_chunk_case(csh, cch, cpre, block_size=64)
+        ccfg = mla.make_config(csh)
+        cW = W if cname == args.prefill else {k: tb(v) for k, v in cc.w.items()}
+        c_n = cc.x.shape[0]
+        ccu_h, cpre_h = cc.cu_seqlens, cc.prefix_lens
+        ccos, csin = cos, sin
+        longest = int(np.max(cpre_h + np.diff(ccu_h)))
+        if csh.rope.kind != "none":
+            ccos, csin = mla.rope_table(ccfg, longest, dev)
+        chunk = dict(
+            name=args.chunk, sh=csh, cfg=ccfg, W=cW, x=tb(cc.x), cu=torch.from_numpy(ccu_h).to(dev), cu_h=ccu_h,
+            pre=torch.from_numpy(cpre_h).to(dev), pre_h=cpre_h, cache=tb(cc.cache),
+            table=torch.from_numpy(cc.block_table).to(dev), cos=ccos, sin=csin, chunks=cch, prefixes=cpre,
+            out=torch.empty(c_n, csh.hidden, dtype=torch.bfloat16, device=dev),
+            lat=torch.empty(c_n, csh.kv_lora_rank + csh.qk_rope_dim, dtype=torch.bfloat16, device=dev),
+            ws=torch.empty(mla.prefill_chunk_workspace_size(ccfg, ccu_h, cpre_h), dtype=torch.uint8, device=dev))
+        del cc
+
+    def chunk_layer():
+        c = chunk
+        mla.prefill_chunk_fwd(c["cfg"], c["W"], c["x"], c["cu"], c["cu_h"], c["pre"], c["pre_h"], c["cache"],
+                              c["table"], c["out"], latent_out=c["lat"], rope_cos=c["cos"], rope_sin=c["sin"],
+                              workspace=c["ws"])
+
+    def chunk_attention_operands():
+        # fp16 operands of the chunk layer's attention shapes (keys = context rows)
+        c = chunk
+        csh = c["sh"]
+        ck_h = np.concatenate([[0], np.cumsum(np.asarray(c["prefixes"]) + np.asarray(c["chunks"]))]).astype(np.int32)
+        g = torch.Generator(device=dev).manual_seed(1)
+        Hc, nq, nk = csh.num_heads, int(c["cu_h"][-1]), int(ck_h[-1])
+        qa = torch.randn(nq, Hc, csh.qk_head_dim, device=dev, generator=g).to(torch.float16)
+        kva = torch.randn(nk, Hc, csh.qk_nope_dim + csh.v_head_dim, device=dev, generator=g).to(torch.float16)
+        kpe = torch.randn(nk, csh.qk_rope_dim, device=dev, generator=g).to(torch.float16)
+        attn = torch.empty(nq, Hc, csh.v_head_dim, dtype=torch.bfloat16, device=dev)
+        ck = torch.from_numpy(ck_h).to(dev)
+        return lambda: mla.attention_prefix(c["cfg"], qa, kva, kpe, c["cu"], c["cu_h"], ck, ck_h, attn)
+
     def prefill():
         mla.prefill_fwd(cfg, W, x, cu, cuh, out, latent_out=lat, rope_cos=cos, rope_sin=sin, workspace=ws_p)
 
@@ -230,6 +289,10 @@ def main():
             kpe = torch.randn(n, sh.qk_rope_dim, device=dev, generator=g).to(torch.float16)
             attn = torch.empty(n, H, sh.v_head_dim, dtype=torch.bfloat16, device=dev)
             fn = lambda: mla.attention_prefill(cfg, qa, kva, kpe, cu, cuh, attn)
+        elif args.mode == "chunk_attention":
+            fn = chunk_attention_operands()
+        elif args.mode == "chunk":
+            fn = chunk_layer
         elif args.mode == "copy":
             # known-size device copy: calibrates the FETCH_SIZE / WRITE_SIZE counters
             src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
@@ -300,6 +363,37 @@ def main():
     torch.cuda.synchronize()
     dec_ms = sum(a.elapsed_time(b) for a, b in de) / args.steps
 
+    # ------------------------------------------------------------------ chunked prefill (reported beside the metric)
+    chunk_rec = None
+    if chunk is not None:
+        def timed(fn, k):
+            for _ in range(2):
+                fn()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(k)]
+            for i in range(k):
+                ev[i][0].record(stream)
+                fn()
+                ev[i][1].record(stream)
+            torch.cuda.synchronize()
+            return sum(a.elapsed_time(b) for a, b in ev) / k
+        c_layer_ms = timed(chunk_layer, args.steps)
+        c_attn_ms = timed(chunk_attention_operands(), args.steps)
+        csh = chunk["sh"]
+        c_aflops = prefix_attention_flops(csh, chunk["chunks"], chunk["prefixes"])
+        c_tflops = c_aflops / (c_attn_ms * 1e-3) / 1e12
+        # layer FLOPs: the new tokens' projections, the up-projection of every context row, the attention
+        n_new, n_ctx = int(chunk["cu_h"][-1]), int(sum(chunk["chunks"]) + sum(chunk["prefixes"]))
+        c_lflops = (layer_flops(csh, n_new, c_aflops)
+                    + 2 * (n_ctx - n_new) * csh.kv_lora_rank * csh.num_heads * (csh.qk_nope_dim + csh.v_head_dim))
+        chunk_rec = {"workload": chunk["name"], "new_tokens": n_new, "context_tokens": n_ctx,
+                     "layer_ms": round(c_layer_ms, 4), "layer_tflops": round(c_lflops / (c_layer_ms * 1e-3) / 1e12, 2),
+                     "attn_ms": round(c_attn_ms, 4), "attn_tflops": round(c_tflops, 2),
+                     "roofline": {"bound": "mfma", "achieved": round(c_tflops, 2), "peak": PEAK_MFMA_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": round(c_tflops / PEAK_MFMA_TFLOPS, 4),
+                                  "kernel": "flash_mfma_kernel<fp16> (queries over cached + new keys)",
+                                  "flops_per_launch": c_aflops}}
+        del chunk
+
     # ------------------------------------------------------------------ figures
     a_flops = attention_flops(sh, cuh)
     attn_tflops = a_flops / (attn_ms * 1e-3) / 1e12
@@ -328,6 +422,8 @@ def main():
                             "kernel": "mla_decode_absorbed_fwd (query absorption + split-KV attention + fused combine and un-absorb)",
                             "bytes_per_call": d_bytes},
     }
+    if chunk_rec is not None:
+        rec["chunked_prefill"] = chunk_rec
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(args.prefill, args.decode, args.cpu_budget)
     print(json.dumps(rec), flush=True)

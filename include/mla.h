@@ -143,6 +143,11 @@ mla_status mla_rope_table(const mla_config* cfg, int32_t max_pos, float* cos_out
  * tokens in num_seqs documents. */
 size_t mla_prefill_workspace_size(const mla_config* cfg, int32_t num_tokens, int32_t num_seqs);
 
+/* Workspace (device bytes) needed by mla_prefill_chunk_fwd; both arrays are
+ * HOST arrays (cu_seqlens [num_seqs + 1], prefix_lens [num_seqs]). */
+size_t mla_prefill_chunk_workspace_size(const mla_config* cfg, const int32_t* cu_seqlens_host,
+                                        const int32_t* prefix_lens_host, int32_t num_seqs);
+
 /* Workspace (device bytes) needed by mla_decode_absorbed_fwd; seq_lens_host
  * is a HOST array of batch lengths. */
 size_t mla_decode_workspace_size(const mla_config* cfg, const int32_t* seq_lens_host, int32_t batch);
@@ -212,6 +217,22 @@ mla_status mla_attention_prefill(const mla_config* cfg, int32_t operand_dtype, c
                                  int32_t num_seqs, void* attn,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* The attention core for new queries over longer key sequences (a chunk of
+ * new tokens over a cached prefix): document d has queries [cu_q[d],
+ * cu_q[d+1]) and keys [cu_k[d], cu_k[d+1]), at least as many keys as
+ * queries, aligned at the end, so query t of d sees the keys of d up to row
+ * cu_k[d+1] - (cu_q[d+1] - t): every key before the document's queries and
+ * the queries' own keys up to itself ("MiniMind: attention forward pass",
+ * section 5, the mask with a cache).  cu_q == cu_k gives
+ * mla_attention_prefill.  Operands and output as for mla_attention_prefill,
+ * with kv and kpe indexed by key rows (cu_k_host[num_seqs] of them).
+ * MLA_ERR_INVALID_ARG when a document has fewer keys than queries. */
+mla_status mla_attention_prefix(const mla_config* cfg, int32_t operand_dtype, const void* q, const void* kv,
+                                const void* kpe, int64_t kpe_stride,
+                                const int32_t* cu_q_dev, const int32_t* cu_q_host,
+                                const int32_t* cu_k_dev, const int32_t* cu_k_host,
+                                int32_t num_seqs, void* attn, void* stream);
+
 /* The full MLA prefill layer on packed documents.
  *   x [N, hidden] DEVICE; N = cu_seqlens_host[num_seqs].
  *   positions_dev: DEVICE [N] RoPE positions, or NULL for 0..len-1 within each
@@ -228,6 +249,44 @@ mla_status mla_prefill_fwd(const mla_config* cfg, const mla_weights* w, const vo
                            const float* rope_cos, const float* rope_sin, int32_t rope_table_len,
                            void* out, void* latent_out,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* The MLA prefill layer for new tokens of sequences whose first tokens are
+ * already in the paged latent cache (chunked prefill, mixed prefill/decode).
+ * The cached latent rows are decompressed with the kv up-projection, as the
+ * new tokens' are ("Megatron-LM MLA guide", inference section: prefill and
+ * mixed steps decompress the cached latents; only decode-only steps absorb),
+ * and new token i of sequence s, at position prefix_lens[s] + i, attends to
+ * every cached token of s and to the new tokens of s up to itself (the mask of
+ * a forward with a cache, "MiniMind: attention forward pass", section 5).
+ *   x [N, hidden] DEVICE: the new tokens, packed by cu_seqlens (DEVICE / HOST,
+ *     [num_seqs + 1], same values); N = cu_seqlens_host[num_seqs].
+ *   prefix_lens_dev / prefix_lens_host: [num_seqs] cached tokens per sequence
+ *     (DEVICE / HOST, same values, each >= 0; 0 = a plain causal prefill).
+ *   kv_cache [num_blocks, block_size, r_kv + d_rope] in cfg.dtype, rows
+ *     [c_n | k_pe'] as mla_latent_norm_rope / latent_out store them; cached
+ *     token j of sequence s lives in slot block_table[s, j / block_size] *
+ *     block_size + j % block_size.  block_table [num_seqs, max_blocks].
+ *     May be NULL when every prefix is 0.  block_size: a power of two.
+ *     A block id outside [0, num_blocks) makes that sequence's outputs NaN;
+ *     slots past a prefix are never read.  The new tokens are NOT written to
+ *     the cache: latent_out receives their rows for the caller to store.
+ *   rope_cos/rope_sin: as for mla_prefill_fwd (positions up to the longest
+ *     prefix + chunk must be in the table).
+ *   out [N, hidden], latent_out NULL or [N, r_kv + d_rope], as for
+ *     mla_prefill_fwd.
+ *   workspace: DEVICE, >= mla_prefill_chunk_workspace_size(cfg, cu_seqlens_host,
+ *     prefix_lens_host, num_seqs).
+ * Errors: MLA_ERR_INVALID_ARG for a negative prefix, a prefix beyond
+ * max_blocks * block_size, or missing cache arguments with a non-zero
+ * prefix; MLA_ERR_UNSUPPORTED past 2^31 - 1 context rows. */
+mla_status mla_prefill_chunk_fwd(const mla_config* cfg, const mla_weights* w, const void* x,
+                                 const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                 const int32_t* prefix_lens_dev, const int32_t* prefix_lens_host,
+                                 const void* kv_cache, int32_t num_blocks, int32_t block_size,
+                                 const int32_t* block_table, int32_t max_blocks,
+                                 const float* rope_cos, const float* rope_sin, int32_t rope_table_len,
+                                 void* out, void* latent_out,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* Weight-absorbed MLA decode over a paged latent cache ("Megatron-LM MLA
  * guide", inference section: kv up-projection split per head into up_k and

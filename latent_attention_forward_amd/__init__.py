@@ -63,6 +63,10 @@ _SIGNATURES = {
     "mla_prefill_fwd": (_I32, [_CFG, ctypes.POINTER(MlaWeights), _P, _P, _P, _I32, _P, _P, _P, _I32, _P, _P,
                                _P, _SZ, _P]),
     "mla_decode_absorbed_fwd": (_I32, [_CFG, _P, _P, _P, _P, _I32, _I32, _P, _I32, _P, _P, _I32, _P, _P, _SZ, _P]),
+    "mla_prefill_chunk_workspace_size": (_SZ, [_CFG, _P, _P, _I32]),
+    "mla_attention_prefix": (_I32, [_CFG, _I32, _P, _P, _P, _I64, _P, _P, _P, _P, _I32, _P, _P]),
+    "mla_prefill_chunk_fwd": (_I32, [_CFG, ctypes.POINTER(MlaWeights), _P, _P, _P, _I32, _P, _P, _P, _I32, _I32, _P,
+                                     _I32, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
 }
 
 _lib = None
@@ -214,6 +218,22 @@ def attention_prefill(cfg: MlaConfig, q, kv, kpe, cu_seqlens_dev, cu_seqlens_hos
                                      _stream(stream)), "mla_attention_prefill")
 
 
+def attention_prefix(cfg: MlaConfig, q, kv, kpe, cu_q_dev, cu_q_host: Sequence[int], cu_k_dev,
+                     cu_k_host: Sequence[int], attn, kpe_stride: Optional[int] = None, stream=None):
+    """Attention core of new queries over longer key sequences (aligned at
+    the end).  ``q`` rows follow ``cu_q``, ``kv`` and ``kpe`` rows ``cu_k``."""
+    import numpy as np
+    import torch
+    lib = load_library()
+    cqh = np.ascontiguousarray(np.asarray(cu_q_host, dtype=np.int32))
+    ckh = np.ascontiguousarray(np.asarray(cu_k_host, dtype=np.int32))
+    op = {torch.bfloat16: MLA_BF16, torch.float16: MLA_F16, torch.float32: MLA_F32}[q.dtype]
+    _check(lib.mla_attention_prefix(ctypes.byref(cfg), op, _ptr(q), _ptr(kv), _ptr(kpe),
+                                    kpe.stride(0) if kpe_stride is None else kpe_stride, _ptr(cu_q_dev),
+                                    cqh.ctypes.data, _ptr(cu_k_dev), ckh.ctypes.data, len(cqh) - 1, _ptr(attn),
+                                    _stream(stream)), "mla_attention_prefix")
+
+
 def make_weights(w: Dict[str, object]) -> MlaWeights:
     mw = MlaWeights()
     for name, _ in MlaWeights._fields_:
@@ -252,4 +272,36 @@ def decode_absorbed_fwd(cfg: MlaConfig, w_kv_b, q_nope, q_pe, kv_cache, block_ta
                                        num_blocks, block_size, _ptr(block_table), block_table.shape[1],
                                        _ptr(seq_lens_dev), lens.ctypes.data, len(lens), _ptr(out), _ptr(ws),
                                        ws.numel(), _stream(stream)), "mla_decode_absorbed_fwd")
+    return ws
+
+
+def prefill_chunk_workspace_size(cfg: MlaConfig, cu_seqlens_host: Sequence[int], prefix_lens_host: Sequence[int]) -> int:
+    import numpy as np
+    cuh = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int32))
+    pre = np.ascontiguousarray(np.asarray(prefix_lens_host, dtype=np.int32))
+    return int(load_library().mla_prefill_chunk_workspace_size(ctypes.byref(cfg), cuh.ctypes.data, pre.ctypes.data,
+                                                                len(cuh) - 1))
+
+
+def prefill_chunk_fwd(cfg: MlaConfig, weights: Dict[str, object], x, cu_seqlens_dev, cu_seqlens_host: Sequence[int],
+                      prefix_lens_dev, prefix_lens_host: Sequence[int], kv_cache, block_table, out,
+                      latent_out=None, rope_cos=None, rope_sin=None, workspace=None, stream=None):
+    """Prefill of new tokens over a cached latent prefix.  ``kv_cache`` is
+    [num_blocks, block_size, r_kv + d_rope] (or None when every prefix is 0),
+    ``block_table`` [num_seqs, max_blocks] int32."""
+    import numpy as np
+    lib = load_library()
+    cuh = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int32))
+    pre = np.ascontiguousarray(np.asarray(prefix_lens_host, dtype=np.int32))
+    s = len(cuh) - 1
+    ws = _workspace(prefill_chunk_workspace_size(cfg, cuh, pre), x.device, workspace)
+    mw = make_weights(weights)
+    table_len = 0 if rope_cos is None else rope_cos.shape[0]
+    nb, bs = (0, 0) if kv_cache is None else (kv_cache.shape[0], kv_cache.shape[1])
+    mb = 0 if block_table is None else block_table.shape[1]
+    _check(lib.mla_prefill_chunk_fwd(ctypes.byref(cfg), ctypes.byref(mw), _ptr(x), _ptr(cu_seqlens_dev),
+                                     cuh.ctypes.data, s, _ptr(prefix_lens_dev), pre.ctypes.data, _ptr(kv_cache), nb,
+                                     bs, _ptr(block_table), mb, _ptr(rope_cos), _ptr(rope_sin), table_len, _ptr(out),
+                                     _ptr(latent_out), _ptr(ws), ws.numel(), _stream(stream)),
+           "mla_prefill_chunk_fwd")
     return ws

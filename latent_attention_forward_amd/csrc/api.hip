@@ -117,10 +117,12 @@ std::vector<double> rope_frequencies(const mla_config* c) {
 
 // ---------------------------------------------------------------- prefill workspace
 struct PrefillWs {
-  size_t pos, q_lat32, q_lat, q, ckv32, latent, kpe16, kv, attn, total;
+  size_t pos, q_lat32, q_lat, q, ckv32, latent, kpe16, kv, attn, ctx, kpe16ctx, cuk, total;
 };
 
-PrefillWs prefill_layout(const mla_config* c, int64_t n) {
+// n new tokens; n_ctx >= 0 for a chunk over a cached prefix (context rows of
+// all sequences, num_seqs sequences), else -1.
+PrefillWs prefill_layout(const mla_config* c, int64_t n, int64_t n_ctx = -1, int64_t num_seqs = 0) {
   const size_t es = elem_size(c);
   const int64_t H = c->num_heads, dqk = c->qk_nope_dim + c->qk_rope_dim;
   const int64_t lw = c->kv_lora_rank + c->qk_rope_dim;
@@ -133,8 +135,15 @@ PrefillWs prefill_layout(const mla_config* c, int64_t n) {
   w.ckv32 = off; off += align256(n * lw * 4);                  // fp32 [c | k_pe] before norm / RoPE
   w.latent = off; off += align256(n * lw * es);
   w.kpe16 = off; off += align256(n * c->qk_rope_dim * 2);      // fp16 shared rope key for attention
-  w.kv = off; off += align256(n * H * (c->qk_nope_dim + c->v_head_dim) * es);
+  const int64_t kv_rows = n_ctx >= 0 ? n_ctx : n;
+  w.kv = off; off += align256(kv_rows * H * (c->qk_nope_dim + c->v_head_dim) * es);
   w.attn = off; off += align256(n * H * c->v_head_dim * es);
+  w.ctx = w.kpe16ctx = w.cuk = off;
+  if (n_ctx >= 0) {
+    w.ctx = off; off += align256(n_ctx * lw * es);                     // context latent rows
+    w.kpe16ctx = off; off += align256(n_ctx * c->qk_rope_dim * 2);     // their fp16 rope keys
+    w.cuk = off; off += align256((num_seqs + 1) * 4);                  // context row offsets
+  }
   w.total = off;
   return w;
 }
@@ -256,6 +265,15 @@ size_t mla_prefill_workspace_size(const mla_config* cfg, int32_t num_tokens, int
   return prefill_layout(cfg, num_tokens).total;
 }
 
+size_t mla_prefill_chunk_workspace_size(const mla_config* cfg, const int32_t* cu_seqlens_host,
+                                        const int32_t* prefix_lens_host, int32_t num_seqs) {
+  if (check_config(cfg) != MLA_OK || !cu_seqlens_host || !prefix_lens_host || num_seqs <= 0) return 0;
+  int64_t n_ctx = 0;
+  for (int i = 0; i < num_seqs; ++i)
+    n_ctx += std::max(0, prefix_lens_host[i]) + std::max(0, cu_seqlens_host[i + 1] - cu_seqlens_host[i]);
+  return prefill_layout(cfg, cu_seqlens_host[num_seqs], n_ctx, num_seqs).total;
+}
+
 size_t mla_decode_workspace_size(const mla_config* cfg, const int32_t* seq_lens_host, int32_t batch) {
   if (check_config(cfg) != MLA_OK || !seq_lens_host || batch <= 0) return 0;
   return decode_plan(cfg, seq_lens_host, batch, INT32_MAX).total;
@@ -328,9 +346,14 @@ mla_status mla_linear(const mla_config* cfg, const void* x, int64_t ldx, const v
   return s == MLA_OK ? ok() : s;
 }
 
+// Attention core.  cuk_dev / cuk_host (both or neither): key rows per document
+// when they differ from the query rows (a chunk over a cached prefix), n_keys
+// the rows of kv and kpe.
 static mla_status attention_impl(const mla_config* cfg, const void* q, const void* kv, const void* kpe,
                                  int64_t kpe_stride, bool f16_operands, const int32_t* cu_dev,
-                                 const int32_t* cu_host, int num_seqs, int n, void* attn, hipStream_t st) {
+                                 const int32_t* cu_host, int num_seqs, int n, void* attn, hipStream_t st,
+                                 const int32_t* cuk_dev = nullptr, const int32_t* cuk_host = nullptr,
+                                 int n_keys = -1) {
   // the MFMA kernel addresses the 64 key rows of a tile with 32-bit byte offsets
   if (cfg->dtype == MLA_BF16 &&
       (64 * kpe_stride * 2 >= ((int64_t)1 << 31) ||
@@ -340,7 +363,8 @@ static mla_status attention_impl(const mla_config* cfg, const void* q, const voi
   f.q = q; f.kv = kv; f.kpe = kpe; f.kpe_stride = kpe_stride; f.cu_dev = cu_dev; f.out = attn;
   f.n_tokens = n; f.heads = cfg->num_heads; f.nope = cfg->qk_nope_dim; f.rope = cfg->qk_rope_dim;
   f.dv = cfg->v_head_dim; f.kv_lora = cfg->kv_lora_rank; f.scale = scale_of(cfg); f.num_seqs = num_seqs;
-  const hipError_t e = cfg->dtype == MLA_BF16 ? launch_flash_mfma(f, f16_operands, cu_host, num_seqs, st)
+  f.cuk_dev = cuk_dev; f.n_keys = cuk_dev ? n_keys : n;
+  const hipError_t e = cfg->dtype == MLA_BF16 ? launch_flash_mfma(f, f16_operands, cu_host, cuk_host, num_seqs, st)
                                               : launch_flash_f32(f, st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return MLA_OK;
@@ -369,6 +393,59 @@ mla_status mla_attention_prefill(const mla_config* cfg, int32_t operand_dtype, c
   return s == MLA_OK ? ok() : s;
 }
 
+// A chunk of new tokens over a cached prefix (see mla_prefill_chunk_fwd).
+struct ChunkIn {
+  const int32_t* prefix_dev;
+  const void* cache; int num_blocks; int log2_block; const int32_t* block_table; int max_blocks;
+  int n_ctx; int max_ctx_len;
+  std::vector<int32_t> cuk_host;                     // context row offsets, for the attention plan
+};
+
+static mla_status check_weights(const mla_config* cfg, const mla_weights* w) {
+  if (!w) return fail(MLA_ERR_INVALID_ARG, "weights are NULL");
+  if (cfg->q_lora_rank > 0 && (!w->w_q_a || !w->q_a_gamma || !w->w_q_b))
+    return fail(MLA_ERR_INVALID_ARG, "q_lora_rank > 0 needs w_q_a, q_a_gamma, w_q_b");
+  if (cfg->q_lora_rank == 0 && !w->w_q) return fail(MLA_ERR_INVALID_ARG, "q_lora_rank == 0 needs w_q");
+  if (!w->w_kv_a || !w->kv_a_gamma || !w->w_kv_b || !w->w_o) return fail(MLA_ERR_INVALID_ARG, "w_kv_a, kv_a_gamma, w_kv_b, w_o are required");
+  if (cfg->output_gate && !w->w_g) return fail(MLA_ERR_INVALID_ARG, "output_gate needs w_g");
+  return MLA_OK;
+}
+
+static mla_status prefill_core(const mla_config* cfg, const mla_weights* w, const void* x, const int32_t* cu_seqlens_dev,
+                               const int32_t* cu_seqlens_host, int32_t num_seqs, int n, const int32_t* positions_dev,
+                               const float* rope_cos, const float* rope_sin, int32_t rope_table_len, void* out,
+                               void* latent_out, void* workspace, size_t workspace_bytes, void* stream,
+                               const ChunkIn* chunk);
+
+mla_status mla_attention_prefix(const mla_config* cfg, int32_t operand_dtype, const void* q, const void* kv,
+                                const void* kpe, int64_t kpe_stride, const int32_t* cu_q_dev, const int32_t* cu_q_host,
+                                const int32_t* cu_k_dev, const int32_t* cu_k_host, int32_t num_seqs, void* attn,
+                                void* stream) {
+  mla_status s = check_config(cfg);
+  if (s != MLA_OK) return s;
+  if ((s = check_supported(cfg)) != MLA_OK) return s;
+  const bool ok_type = cfg->dtype == MLA_BF16 ? (operand_dtype == MLA_BF16 || operand_dtype == MLA_F16)
+                                              : operand_dtype == MLA_F32;
+  if (!ok_type) return fail(MLA_ERR_INVALID_ARG, "operand_dtype %d does not match the config dtype", operand_dtype);
+  int n = 0, nk = 0;
+  if ((s = check_cu(cu_q_host, num_seqs, &n)) != MLA_OK) return s;
+  if (!cu_k_host) return fail(MLA_ERR_INVALID_ARG, "cu_k_host is NULL");
+  if (cu_k_host[0] != 0) return fail(MLA_ERR_INVALID_ARG, "cu_k[0] must be 0");
+  for (int i = 0; i < num_seqs; ++i)
+    if (cu_k_host[i + 1] - cu_k_host[i] < cu_q_host[i + 1] - cu_q_host[i])
+      return fail(MLA_ERR_INVALID_ARG, "document %d has fewer keys than queries", i);
+  nk = cu_k_host[num_seqs];
+  if (n == 0) return ok();
+  if (!q || !kv || !kpe || !cu_q_dev || !cu_k_dev || !attn)
+    return fail(MLA_ERR_INVALID_ARG, "q, kv, kpe, both device offset arrays and attn are required");
+  if (kpe_stride < cfg->qk_rope_dim) return fail(MLA_ERR_INVALID_ARG, "kpe_stride < d_rope");
+  if (cfg->dtype == MLA_BF16 && (!aligned16(q) || !aligned16(kv) || !aligned16(kpe) || !aligned16(attn) || kpe_stride % 8))
+    return fail(MLA_ERR_MISALIGNED, "bf16 attention needs 16-byte aligned tensors and kpe_stride % 8 == 0");
+  s = attention_impl(cfg, q, kv, kpe, kpe_stride, operand_dtype == MLA_F16, cu_q_dev, cu_q_host, num_seqs, n, attn,
+                     (hipStream_t)stream, cu_k_dev, cu_k_host, nk);
+  return s == MLA_OK ? ok() : s;
+}
+
 mla_status mla_prefill_fwd(const mla_config* cfg, const mla_weights* w, const void* x, const int32_t* cu_seqlens_dev,
                            const int32_t* cu_seqlens_host, int32_t num_seqs, const int32_t* positions_dev,
                            const float* rope_cos, const float* rope_sin, int32_t rope_table_len, void* out,
@@ -376,20 +453,78 @@ mla_status mla_prefill_fwd(const mla_config* cfg, const mla_weights* w, const vo
   mla_status s = check_config(cfg);
   if (s != MLA_OK) return s;
   if ((s = check_supported(cfg)) != MLA_OK) return s;
-  if (!w) return fail(MLA_ERR_INVALID_ARG, "weights are NULL");
+  if ((s = check_weights(cfg, w)) != MLA_OK) return s;
   int n = 0;
   if ((s = check_cu(cu_seqlens_host, num_seqs, &n)) != MLA_OK) return s;
   if (n == 0) return ok();
   if (!x || !out || !cu_seqlens_dev) return fail(MLA_ERR_INVALID_ARG, "x, out and cu_seqlens_dev are required");
-  if (cfg->q_lora_rank > 0 && (!w->w_q_a || !w->q_a_gamma || !w->w_q_b))
-    return fail(MLA_ERR_INVALID_ARG, "q_lora_rank > 0 needs w_q_a, q_a_gamma, w_q_b");
-  if (cfg->q_lora_rank == 0 && !w->w_q) return fail(MLA_ERR_INVALID_ARG, "q_lora_rank == 0 needs w_q");
-  if (!w->w_kv_a || !w->kv_a_gamma || !w->w_kv_b || !w->w_o) return fail(MLA_ERR_INVALID_ARG, "w_kv_a, kv_a_gamma, w_kv_b, w_o are required");
-  if (cfg->output_gate && !w->w_g) return fail(MLA_ERR_INVALID_ARG, "output_gate needs w_g");
+  s = prefill_core(cfg, w, x, cu_seqlens_dev, cu_seqlens_host, num_seqs, n, positions_dev, rope_cos, rope_sin,
+                   rope_table_len, out, latent_out, workspace, workspace_bytes, stream, nullptr);
+  return s == MLA_OK ? ok() : s;
+}
+
+mla_status mla_prefill_chunk_fwd(const mla_config* cfg, const mla_weights* w, const void* x,
+                                 const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                 const int32_t* prefix_lens_dev, const int32_t* prefix_lens_host,
+                                 const void* kv_cache, int32_t num_blocks, int32_t block_size,
+                                 const int32_t* block_table, int32_t max_blocks, const float* rope_cos,
+                                 const float* rope_sin, int32_t rope_table_len, void* out, void* latent_out,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  mla_status s = check_config(cfg);
+  if (s != MLA_OK) return s;
+  if ((s = check_supported(cfg)) != MLA_OK) return s;
+  if ((s = check_weights(cfg, w)) != MLA_OK) return s;
+  int n = 0;
+  if ((s = check_cu(cu_seqlens_host, num_seqs, &n)) != MLA_OK) return s;
+  if (n == 0) return ok();
+  if (!x || !out || !cu_seqlens_dev || !prefix_lens_dev || !prefix_lens_host)
+    return fail(MLA_ERR_INVALID_ARG, "x, out, cu_seqlens_dev and both prefix_lens arrays are required");
+  ChunkIn c{};
+  c.prefix_dev = prefix_lens_dev;
+  c.cuk_host.assign(num_seqs + 1, 0);
+  int64_t n_ctx = 0, max_prefix = 0;
+  int max_len = 0;
+  for (int i = 0; i < num_seqs; ++i) {
+    const int64_t P = prefix_lens_host[i];
+    if (P < 0) return fail(MLA_ERR_INVALID_ARG, "prefix_lens[%d] = %lld < 0", i, (long long)P);
+    const int64_t len = P + cu_seqlens_host[i + 1] - cu_seqlens_host[i];
+    n_ctx += len;
+    if (n_ctx >= INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "more than 2^31 - 1 context rows");
+    c.cuk_host[i + 1] = (int32_t)n_ctx;
+    max_prefix = std::max(max_prefix, P);
+    max_len = std::max<int>(max_len, (int)len);
+  }
+  c.n_ctx = (int)n_ctx;
+  c.max_ctx_len = max_len;
+  if (max_prefix > 0) {
+    if (!kv_cache || !block_table) return fail(MLA_ERR_INVALID_ARG, "a cached prefix needs kv_cache and block_table");
+    if (num_blocks <= 0 || max_blocks <= 0) return fail(MLA_ERR_INVALID_ARG, "num_blocks and max_blocks must be > 0");
+    if (block_size <= 0 || (block_size & (block_size - 1))) return fail(MLA_ERR_INVALID_ARG, "block_size must be a power of two");
+    if (max_prefix > (int64_t)max_blocks * block_size)
+      return fail(MLA_ERR_INVALID_ARG, "a prefix is longer than max_blocks * block_size");
+    if (cfg->dtype == MLA_BF16 && !aligned16(kv_cache)) return fail(MLA_ERR_MISALIGNED, "kv_cache must be 16-byte aligned");
+    if (cfg->dtype == MLA_F32 && ((uintptr_t)kv_cache & 15)) return fail(MLA_ERR_MISALIGNED, "kv_cache must be 16-byte aligned");
+  }
+  const int lw = cfg->kv_lora_rank + cfg->qk_rope_dim;
+  if ((lw * (int)elem_size(cfg)) % 16) return fail(MLA_ERR_UNSUPPORTED, "latent rows must be a multiple of 16 bytes");
+  c.cache = kv_cache; c.num_blocks = num_blocks; c.block_table = block_table; c.max_blocks = max_blocks;
+  c.log2_block = 0;
+  while (max_prefix > 0 && (1 << c.log2_block) < block_size) ++c.log2_block;
+  s = prefill_core(cfg, w, x, cu_seqlens_dev, cu_seqlens_host, num_seqs, n, nullptr, rope_cos, rope_sin,
+                   rope_table_len, out, latent_out, workspace, workspace_bytes, stream, &c);
+  return s == MLA_OK ? ok() : s;
+}
+
+static mla_status prefill_core(const mla_config* cfg, const mla_weights* w, const void* x, const int32_t* cu_seqlens_dev,
+                               const int32_t* cu_seqlens_host, int32_t num_seqs, int n, const int32_t* positions_dev,
+                               const float* rope_cos, const float* rope_sin, int32_t rope_table_len, void* out,
+                               void* latent_out, void* workspace, size_t workspace_bytes, void* stream,
+                               const ChunkIn* chunk) {
+  mla_status s = MLA_OK;
   const bool rope = cfg->rope_kind != MLA_ROPE_NONE;
   if (rope && (!rope_cos || !rope_sin || rope_table_len <= 0))
     return fail(MLA_ERR_INVALID_ARG, "RoPE needs device cos/sin tables and their length");
-  const PrefillWs L = prefill_layout(cfg, n);
+  const PrefillWs L = chunk ? prefill_layout(cfg, n, chunk->n_ctx, num_seqs) : prefill_layout(cfg, n);
   if (!workspace || workspace_bytes < L.total)
     return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, workspace_bytes);
   if (cfg->dtype == MLA_BF16) {
@@ -415,10 +550,12 @@ mla_status mla_prefill_fwd(const mla_config* cfg, const mla_weights* w, const vo
   const bool bf = cfg->dtype == MLA_BF16;
   hipError_t e;
 
-  // positions (0..len-1 per document) unless the caller gives them
+  // positions (0..len-1 per document, after the cached prefix of a chunk)
+  // unless the caller gives them
   const int32_t* positions = positions_dev;
   if (rope && !positions) {
-    if ((e = launch_positions(cu_seqlens_dev, num_seqs, n, pos, st)) != hipSuccess) return hip_fail(e, "positions");
+    if ((e = launch_positions(cu_seqlens_dev, num_seqs, n, pos, st, chunk ? chunk->prefix_dev : nullptr)) != hipSuccess)
+      return hip_fail(e, "positions");
     positions = pos;
   }
   // Down-projections are kept in fp32 until their norm, so every stored bf16
@@ -475,20 +612,48 @@ mla_status mla_prefill_fwd(const mla_config* cfg, const mla_weights* w, const vo
     if ((s = gemm(x, hid, w->w_kv_a, ckv_raw, lw, n, lw, hid, OUT_F32, EPI_STORE, nullptr)) != MLA_OK) return s;
     if ((s = norm(ckv_raw, lw, lw, rkv, w->kv_a_gamma, rkv, rope ? 1 : 0, dr, lat, lw, true, bf ? kpe16 : nullptr)) != MLA_OK) return s;
   }
+  // The rows keys and values are formed from: the new tokens' latent rows, or
+  // for a chunk each sequence's cached prefix rows followed by its new rows.
+  const void* kv_src = lat;
+  const f16* kpe_src16 = kpe16;
+  int kv_rows = n;
+  const int32_t* cuk_dev = nullptr;
+  if (chunk) {
+    int32_t* cuk = (int32_t*)(ws + L.cuk);
+    if ((e = launch_chunk_offsets(cu_seqlens_dev, chunk->prefix_dev, num_seqs, cuk, st)) != hipSuccess)
+      return hip_fail(e, "chunk offsets");
+    ChunkGatherArgs g{};
+    g.cu = cu_seqlens_dev; g.prefix = chunk->prefix_dev; g.cuk = cuk;
+    g.cache = chunk->cache; g.block_table = chunk->block_table; g.max_blocks = chunk->max_blocks;
+    g.num_blocks = chunk->num_blocks; g.log2_block = chunk->log2_block;
+    g.lat = lat; g.ctx = ws + L.ctx;
+    g.kpe16_new = bf ? kpe16 : nullptr; g.kpe16_ctx = bf ? (f16*)(ws + L.kpe16ctx) : nullptr;
+    g.row_width = lw; g.rope_dim = dr; g.n_ctx = chunk->n_ctx; g.n_new = n;
+    if ((e = launch_gather_context(g, bf, chunk->max_ctx_len, num_seqs, st)) != hipSuccess)
+      return hip_fail(e, "context gather");
+    kv_src = ws + L.ctx;
+    kpe_src16 = (const f16*)(ws + L.kpe16ctx);
+    kv_rows = chunk->n_ctx;
+    cuk_dev = cuk;
+  }
   // per-head keys/values from the normalised latent
-  if ((s = gemm(lat, lw, w->w_kv_b, kv, (int64_t)H * (dn + dv), n, H * (dn + dv), rkv, att_kind, EPI_STORE, nullptr)) != MLA_OK) return s;
+  if ((s = gemm(kv_src, lw, w->w_kv_b, kv, (int64_t)H * (dn + dv), kv_rows, H * (dn + dv), rkv, att_kind, EPI_STORE,
+                nullptr)) != MLA_OK)
+    return s;
   // attention
   {
-    const void* kpe = bf ? (const void*)kpe16 : (const void*)((const float*)lat + rkv);
+    const void* kpe = bf ? (const void*)kpe_src16 : (const void*)((const float*)kv_src + rkv);
     const int64_t kpe_stride = bf ? dr : lw;
-    if ((s = attention_impl(cfg, q, kv, kpe, kpe_stride, bf, cu_seqlens_dev, cu_seqlens_host, num_seqs, n, attn, st)) != MLA_OK) return s;
+    if ((s = attention_impl(cfg, q, kv, kpe, kpe_stride, bf, cu_seqlens_dev, cu_seqlens_host, num_seqs, n, attn, st,
+                            cuk_dev, chunk ? chunk->cuk_host.data() : nullptr, kv_rows)) != MLA_OK)
+      return s;
   }
   // optional gate, output projection
   if (cfg->output_gate) {
     if ((s = gemm(x, hid, w->w_g, attn, (int64_t)H * dv, n, H * dv, hid, OUT_ACT, EPI_GATE, attn)) != MLA_OK) return s;
   }
   if ((s = gemm(attn, (int64_t)H * dv, w->w_o, out, hid, n, hid, H * dv, OUT_ACT, EPI_STORE, nullptr)) != MLA_OK) return s;
-  return ok();
+  return MLA_OK;
 }
 
 mla_status mla_decode_absorbed_fwd(const mla_config* cfg, const void* w_kv_b, const void* q_nope, const void* q_pe,

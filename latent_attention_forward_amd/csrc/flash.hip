@@ -30,7 +30,11 @@
 // Work order: the workgroups of one head are kept on one XCD (workgroup i runs
 // on XCD i mod 8), so the tiles that stream the same k/v rows share that XCD's
 // L2; each XCD takes its tiles longest first across all its heads, so that
-// the last workgroups to start are short ones.
+// the last workgroups to start are short ones.  Documents go one after
+// another (longest first).  When the queries follow a cached prefix (keys
+// offset per document, see FlashArgs), every tile of a document streams the
+// whole prefix, and the tiles of one head are issued in groups that run
+// together instead.
 #include "mla_internal.hpp"
 
 #include <vector>
@@ -48,8 +52,12 @@ constexpr float kPSumMax = 32768.f;   // a lane's sum of P (32 keys) accepted ag
 struct TilePlan {
   int n;                              // query tiles per head in this launch
   int heads_per_xcd;                  // ceil(H / 8)
+  int group;                          // tiles of one head issued back to back (see the work order)
   uint32_t t[MAX_TILES];              // (document << 16) | query-tile index in the document
 };
+// Tiles per group when the queries follow a cached prefix: all of a group's
+// tiles stream the prefix keys, so they run together on one XCD.
+constexpr int kPrefixTileGroup = 8;
 
 template <typename T> struct Vec;
 template <> struct Vec<bf16> { typedef bf16x8 v8; typedef bf16x4 v4; };
@@ -102,20 +110,34 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashArgs a, TilePla
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = a.heads;
   // workgroup -> (head, tile): XCD x = blockIdx % 8 takes heads x, x+8, ...;
-  // within an XCD the tiles go out longest first across all its heads (tile
-  // index major), so no long tile starts late
+  // within an XCD the plan's tiles go out in groups of plan.group, each group
+  // head by head and the group's tiles of one head back to back (a group of 1:
+  // tile index major across all the XCD's heads)
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int ti = slot / plan.heads_per_xcd, hj = slot - ti * plan.heads_per_xcd;
+  const int hpx = plan.heads_per_xcd, tg = plan.group;
+  const int gbase = slot / (tg * hpx) * tg, gs = min(tg, plan.n - gbase);
+  const int rem = slot - gbase * hpx;
+  const int hj = rem / gs, ti = gbase + rem - hj * gs;
   const int head = xcd + 8 * hj;
   if (head >= H) return;
   const uint32_t td = plan.t[ti];
   const int doc = (int)(td >> 16), tix = (int)(td & 0xffff);
   const int ds = max(0, min(a.cu_dev[doc], a.n_tokens));
   const int de = max(ds, min(a.cu_dev[doc + 1], a.n_tokens));
+  // keys of the document: rows [kst, ...); query row t sees keys up to t + koff
+  int kst = ds, koff = 0;
+  if (a.cuk_dev) {
+    const int k_s = max(0, min(a.cuk_dev[doc], a.n_keys));
+    const int k_e = max(k_s, min(a.cuk_dev[doc + 1], a.n_keys));
+    if (k_e - k_s < de - ds) return;       // fewer keys than queries: rejected by the host
+    kst = k_s;
+    koff = k_e - de;
+  }
   const int q0 = ds + tix * FQ;
   if (q0 >= de) return;
   const int q1 = min(q0 + FQ, de);
-  const int ntiles = (q1 - ds + FK - 1) / FK;
+  const int kend = q1 + koff;              // keys [kst, kend) are seen by some query of the tile
+  const int ntiles = (kend - kst + FK - 1) / FK;
 
   const T* Q = (const T*)a.q;
   const T* KV = (const T*)a.kv;
@@ -161,8 +183,8 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashArgs a, TilePla
   };
   auto issue_tile = [&](int t, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
-    const int kb = ds + t * FK;
-    if (kb + FK <= q1) {
+    const int kb = kst + t * FK;
+    if (kb + FK <= kend) {
       const T* kvb = kv_head + (int64_t)kb * kv_row;
       const T* kpb = KPE + (int64_t)kb * a.kpe_stride;
 #pragma unroll
@@ -172,13 +194,13 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashArgs a, TilePla
 #pragma unroll
       for (int i = 0; i < 4; ++i) lds_dma16_sv(kvb, o_v[i], &sV[buf][(wave + 4 * i) * 512]);
     } else {
-      // last, partial tile: keys at or past q1 read the tile's first key
+      // last, partial tile: keys at or past kend read the tile's first key
       // instead (they are masked out of the softmax, probability exactly 0)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int P = (wave + 4 * i) * 64 + lane;
         const int r = P >> 4;
-        const int key = (kb + r < q1) ? kb + r : kb;
+        const int key = (kb + r < kend) ? kb + r : kb;
         lds_dma16_raw(kv_head + (int64_t)key * kv_row + (((P & 15) ^ ksw_n(r)) << 3), &sKn[buf][(wave + 4 * i) * 512]);
         lds_dma16_raw(kv_head + (int64_t)key * kv_row + DN + (vsw(r, P & 15) << 3), &sV[buf][(wave + 4 * i) * 512]);
       }
@@ -186,7 +208,7 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashArgs a, TilePla
       for (int i = 0; i < 2; ++i) {
         const int P = (wave + 4 * i) * 64 + lane;
         const int r = P >> 3;
-        const int key = (kb + r < q1) ? kb + r : kb;
+        const int key = (kb + r < kend) ? kb + r : kb;
         lds_dma16_raw(KPE + (int64_t)key * a.kpe_stride + (((P & 7) ^ ksw_r(r)) << 3), &sKr[buf][(wave + 4 * i) * 512]);
       }
     }
@@ -240,10 +262,10 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashArgs a, TilePla
   // copies of all eight waves of the CU queue at the address unit together.
   auto step = [&](int t, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
-    const int kb = ds + t * FK;
+    const int kb = kst + t * FK;
     const int kn = kb + FK;
-    const bool active = (qw0 < q1) && (kb <= qw0 + 31);
-    const bool spread = active && t + 1 < ntiles && kn + FK <= q1;
+    const bool active = (qw0 < q1) && (kb <= qw0 + 31 + koff);
+    const bool spread = active && t + 1 < ntiles && kn + FK <= kend;
     if (t + 1 < ntiles && !spread) issue_tile(t + 1, BufC<buf ^ 1>{});
     const T* kvn = kv_head + (int64_t)kn * kv_row;
     const T* kpn = KPE + (int64_t)kn * a.kpe_stride;
@@ -274,13 +296,13 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashArgs a, TilePla
 #pragma unroll
       for (int i = 0; i < PD; ++i) vf[i] = vread(i, bufc);
       // ---- causal mask (only tiles that reach past this wave's first query)
-      if (kb + FK - 1 > qw0) {
+      if (kb + FK - 1 > qw0 + koff) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int key = kb + mt * 32 + (e >> 2) * 8 + hsel * 4 + (e & 3);
-            if (key > my_q) s[mt][e] = -INFINITY;
+            if (key > my_q + koff) s[mt][e] = -INFINITY;
           }
       }
       __builtin_amdgcn_s_setprio(0);
@@ -379,7 +401,13 @@ __global__ __launch_bounds__(64) void flash_f32_kernel(FlashArgs a) {
   // document of t
   int d = 0;
   while (d + 1 < a.num_seqs && cu[d + 1] <= t) ++d;
-  const int lo = max(0, cu[d]);
+  // keys lo .. hi: the document's own tokens up to t, or with separate key
+  // rows, everything up to t's place counted from the end of both
+  int lo = max(0, cu[d]), hi = t;
+  if (a.cuk_dev) {
+    lo = max(0, a.cuk_dev[d]);
+    hi = min(t + a.cuk_dev[d + 1] - cu[d + 1], a.n_keys - 1);
+  }
   const float* Q = (const float*)a.q + ((int64_t)t * H + h) * dqk;
   for (int d = lane; d < dqk; d += 64) sq[d] = Q[d];
   __syncthreads();
@@ -387,7 +415,7 @@ __global__ __launch_bounds__(64) void flash_f32_kernel(FlashArgs a) {
   const float* KPE = (const float*)a.kpe;
   const int kvw = a.nope + a.dv;
   float m = -INFINITY, l = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int j = lo; j <= t; ++j) {
+  for (int j = lo; j <= hi; ++j) {
     const float* kr = KV + ((int64_t)j * H + h) * kvw;
     const float* pr = KPE + (int64_t)j * a.kpe_stride;
     float part = 0.f;
@@ -413,19 +441,38 @@ __global__ __launch_bounds__(64) void flash_f32_kernel(FlashArgs a) {
 
 }  // namespace
 
-hipError_t launch_flash_mfma(const FlashArgs& a, bool f16_operands, const int32_t* cu_host, int num_seqs, hipStream_t s) {
+hipError_t launch_flash_mfma(const FlashArgs& a, bool f16_operands, const int32_t* cu_host, const int32_t* cuk_host,
+                             int num_seqs, hipStream_t s) {
   // Tile plan: every (document, 128-query tile), longest key range first; each
   // head walks the whole list on its XCD.
   struct T { int keys; uint32_t id; };
   std::vector<T> tiles;
+  int64_t prefix_total = 0;
   for (int d = 0; d < num_seqs; ++d) {
     const int len = cu_host[d + 1] - cu_host[d];
+    const int prefix = cuk_host ? (cuk_host[d + 1] - cuk_host[d]) - len : 0;
+    prefix_total += prefix;
     const int nt = (len + FQ - 1) / FQ;
-    for (int i = 0; i < nt; ++i) tiles.push_back({std::min((i + 1) * FQ, len), ((uint32_t)d << 16) | (uint32_t)i});
+    for (int i = 0; i < nt; ++i)
+      tiles.push_back({prefix + std::min((i + 1) * FQ, len), ((uint32_t)d << 16) | (uint32_t)i});
   }
-  std::stable_sort(tiles.begin(), tiles.end(), [](const T& x, const T& y) { return x.keys > y.keys; });
+  // Documents in decreasing order of their longest tile, each document's
+  // tiles longest first.  Tile-major across the XCD's heads (a group of 1):
+  // the few tiles of one head in flight together share their keys in the L2,
+  // and the longest tiles start first.  Queries after a cached prefix all
+  // stream the same long key prefix: groups of kPrefixTileGroup consecutive
+  // tiles go out head by head, so those tiles run together.
+  std::vector<int> doc_max(num_seqs, 0);
+  for (const T& t : tiles) doc_max[t.id >> 16] = std::max(doc_max[t.id >> 16], t.keys);
+  std::stable_sort(tiles.begin(), tiles.end(), [&](const T& x, const T& y) {
+    const int dx = (int)(x.id >> 16), dy = (int)(y.id >> 16);
+    if (doc_max[dx] != doc_max[dy]) return doc_max[dx] > doc_max[dy];
+    if (dx != dy) return dx < dy;
+    return x.keys > y.keys;
+  });
   TilePlan plan;
   plan.heads_per_xcd = (a.heads + 7) / 8;
+  plan.group = prefix_total > 0 ? kPrefixTileGroup : 1;
   for (size_t base = 0; base < tiles.size(); base += MAX_TILES) {
     const int n = (int)std::min<size_t>(MAX_TILES, tiles.size() - base);
     plan.n = n;

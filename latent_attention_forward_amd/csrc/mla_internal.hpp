@@ -205,19 +205,43 @@ struct NormRopeArgs {
 // src/dst element types: bf16 -> bf16, fp32 -> fp32, or fp32 -> bf16 (src_f32 with bf16_io).
 hipError_t launch_norm_rope(const NormRopeArgs& a, bool bf16_io, hipStream_t s, bool src_f32 = false);
 
-hipError_t launch_positions(const int32_t* cu_dev, int num_seqs, int n_tokens, int32_t* pos, hipStream_t s);
+// pos[t] = t - cu[d] (+ prefix[d] when prefix_dev is given) for t in document d.
+hipError_t launch_positions(const int32_t* cu_dev, int num_seqs, int n_tokens, int32_t* pos, hipStream_t s,
+                            const int32_t* prefix_dev = nullptr);
+
+// A chunk over a cached prefix: context rows of sequence s are rows
+// [cuk[s], cuk[s+1]) of ctx, its prefix[s] cached rows then its new rows.
+struct ChunkGatherArgs {
+  const int32_t* cu; const int32_t* prefix; const int32_t* cuk;
+  const void* cache; const int32_t* block_table; int max_blocks; int num_blocks; int log2_block;
+  const void* lat;                       // new rows [N, row_width]
+  void* ctx;                             // [n_ctx, row_width]
+  const f16* kpe16_new; f16* kpe16_ctx;  // fp16 rope keys (bf16 rows only; NULL otherwise)
+  int row_width; int rope_dim; int n_ctx; int n_new;
+};
+hipError_t launch_chunk_offsets(const int32_t* cu_dev, const int32_t* prefix_dev, int num_seqs, int32_t* cuk,
+                                hipStream_t s);
+hipError_t launch_gather_context(const ChunkGatherArgs& g, bool bf16_rows, int max_ctx_len, int num_seqs,
+                                 hipStream_t s);
 
 struct FlashArgs {
   const void* q; const void* kv;
   const void* kpe; int64_t kpe_stride;             // shared rope key: row r at kpe + r * kpe_stride
   const int32_t* cu_dev; void* out;
+  // Key rows of each document when they are not its query rows (a chunk over
+  // a cached prefix): document d's keys are rows [cuk[d], cuk[d+1]) of kv and
+  // kpe, aligned at the end, so query row t of d sees keys up to
+  // t + cuk[d+1] - cu[d+1].  NULL: the keys are the query rows (causal).
+  const int32_t* cuk_dev; int n_keys;
   int n_tokens; int heads; int nope; int rope; int dv; int kv_lora;
   float scale; int num_seqs;
 };
 // MFMA kernel (nope 128, rope 64, dv 128) with bf16 or fp16 operands (q, kv,
 // kpe of that type); the output is bf16.  The tile plan is built from the host
 // offsets inside.
-hipError_t launch_flash_mfma(const FlashArgs& a, bool f16_operands, const int32_t* cu_host, int num_seqs, hipStream_t s);
+// cuk_host: the key offsets when a.cuk_dev is set (for the plan), else NULL.
+hipError_t launch_flash_mfma(const FlashArgs& a, bool f16_operands, const int32_t* cu_host, const int32_t* cuk_host,
+                             int num_seqs, hipStream_t s);
 hipError_t launch_flash_f32(const FlashArgs& a, hipStream_t s);
 
 // Most paged-cache blocks one decode segment may span (its block ids are staged in LDS).

@@ -86,7 +86,7 @@ __global__ __launch_bounds__(64 * ROWS_PER_BLOCK) void norm_rope_kernel(NormRope
 }
 
 // positions[t] = t - start of t's document, one thread per token.
-__global__ void positions_kernel(const int32_t* cu, int num_seqs, int n, int32_t* pos) {
+__global__ void positions_kernel(const int32_t* cu, int num_seqs, int n, int32_t* pos, const int32_t* prefix) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= n) return;
   int lo = 0, hi = num_seqs;       // find d with cu[d] <= t < cu[d+1]
@@ -94,7 +94,7 @@ __global__ void positions_kernel(const int32_t* cu, int num_seqs, int n, int32_t
     const int mid = (lo + hi) >> 1;
     if (cu[mid] <= t) lo = mid; else hi = mid;
   }
-  pos[t] = t - cu[lo];
+  pos[t] = t - cu[lo] + (prefix ? prefix[lo] : 0);
 }
 
 }  // namespace
@@ -111,9 +111,10 @@ hipError_t launch_norm_rope(const NormRopeArgs& a, bool bf16_io, hipStream_t s, 
   return hipGetLastError();
 }
 
-hipError_t launch_positions(const int32_t* cu_dev, int num_seqs, int n_tokens, int32_t* pos, hipStream_t s) {
+hipError_t launch_positions(const int32_t* cu_dev, int num_seqs, int n_tokens, int32_t* pos, hipStream_t s,
+                            const int32_t* prefix_dev) {
   if (n_tokens <= 0) return hipSuccess;
-  positions_kernel<<<(n_tokens + 255) / 256, 256, 0, s>>>(cu_dev, num_seqs, n_tokens, pos);
+  positions_kernel<<<(n_tokens + 255) / 256, 256, 0, s>>>(cu_dev, num_seqs, n_tokens, pos, prefix_dev);
   return hipGetLastError();
 }
 
