@@ -97,6 +97,9 @@ class MLAShape:
     rope: RopeSpec
     output_gate: bool = False
     norm_eps: float = 1e-6
+    rope_interleave: bool = False   # RoPE on interleaved pairs (2i, 2i+1)
+    o_groups: int = 0               # > 0: grouped low-rank output projection W_o_b . blockdiag(W_o_a)
+    o_lora_rank: int = 0
     # token layout
     num_docs: int = 1
     total_tokens: int = 0
@@ -211,6 +214,12 @@ def make_prefill_case(shape: MLAShape, doc_lengths: Optional[Sequence[int]] = No
         lens = doc_lengths_for(shape, rng)                                      # 10
     else:
         lens = np.asarray(doc_lengths, dtype=np.int64)
+    if shape.o_groups:
+        fg = h * shape.v_head_dim // shape.o_groups
+        w["w_o_a"] = _normal(rng, (shape.o_groups * shape.o_lora_rank, fg), 0.02)          # 11
+        w["w_o_b"] = _normal(rng, (shape.hidden, shape.o_groups * shape.o_lora_rank), 0.02)  # 12
+    else:
+        w["w_o_a"] = w["w_o_b"] = None
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     if shape.dtype == "bf16":
         x = bf16_round(x)

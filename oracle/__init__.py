@@ -38,4 +38,5 @@ from .mla import (  # noqa: F401
     rotate_half, apply_rope, causal_varlen_attention, mla_prefill, mla_prefill_rows,
     kv_latent, gather_paged, decode_naive, decode_absorbed, prefill_latent_absorbed,
     row_rel_error, bf16_excess_error, prefix_causal_attention, mla_prefill_with_prefix,
+    apply_rope_interleaved,
 )

@@ -144,6 +144,54 @@ def apply_rope(x, cos, sin):
     return x * c + rotate_half(x) * s
 
 
+def apply_rope_interleaved(x, cos, sin):
+    """RoPE on interleaved pairs: features (2i, 2i+1) rotate together by
+    position * theta_i, results in place.  The "CSDN walkthrough of HF
+    DeepseekV3Attention" (``forward``) branches on ``rope_interleave`` to a
+    variant for interleaved weights and does not print it; this is the
+    reading taken (pairing only, layout kept).
+
+    Pinned by: equal to ``apply_rope`` on the features regrouped from
+    interleaved to half-split order (and back); the layer with interleaved
+    pairs equals the layer with rotate_half pairs and the rope rows of the
+    query and key weights regrouped the same way."""
+    x = _f64(x)
+    x0, x1 = x[..., 0::2], x[..., 1::2]
+    y = np.empty_like(x)
+    y[..., 0::2] = x0 * cos - x1 * sin
+    y[..., 1::2] = x1 * cos + x0 * sin
+    return y
+
+
+def _rope(shape, x, cos, sin):
+    """The layer's RoPE: interleaved pairs when the shape asks for them."""
+    if getattr(shape, "rope_interleave", False):
+        return apply_rope_interleaved(x, cos, sin)
+    return apply_rope(x, cos, sin)
+
+
+def _out_proj(shape, w, A2):
+    """Output projection of the attention rows A2 [N, H d_v].  Plain: A2 W_o^T.
+    Grouped low rank ("Megatron-LM MLA guide", output_projection_groups and
+    output_projection_lora_rank, the grouped low-rank output projection wo_a;
+    the page gives only these two settings, so the rest is a reading): the
+    H d_v features split into G consecutive groups, group g projected to
+    rank r_o by its own block of W_o_a ([G r_o, H d_v / G], rows g r_o ..),
+    the G results concatenated and projected to hidden by W_o_b
+    ([hidden, G r_o]).
+
+    Pinned by: equal to a plain projection with W_o = W_o_b blockdiag(W_o_a)."""
+    G = getattr(shape, "o_groups", 0)
+    if not G:
+        return A2 @ _f64(w["w_o"]).T
+    r = shape.o_lora_rank
+    n, f = A2.shape
+    fg = f // G
+    Wa = _f64(w["w_o_a"]).reshape(G, r, fg)
+    t = np.concatenate([A2[:, g * fg:(g + 1) * fg] @ Wa[g].T for g in range(G)], axis=1)
+    return t @ _f64(w["w_o_b"]).T
+
+
 # ----------------------------------------------------------------------------
 # Attention
 # ----------------------------------------------------------------------------
@@ -236,7 +284,7 @@ def kv_latent(shape, w, x, positions):
     c_n = rms_norm(c, w["kv_a_gamma"], shape.norm_eps)
     if shape.rope.kind != "none":
         cos, sin = rope_cos_sin(positions, shape.qk_rope_dim, shape.rope)
-        k_pe = apply_rope(k_pe, cos, sin)
+        k_pe = _rope(shape, k_pe, cos, sin)
     return np.concatenate([c_n, k_pe], axis=-1)
 
 
@@ -274,7 +322,7 @@ def mla_prefill(shape, w: Dict[str, np.ndarray], x, cu_seqlens) -> Dict[str, np.
     q_nope, q_pe = q[..., :nope], q[..., nope:]
     if shape.rope.kind != "none":
         cos, sin = rope_cos_sin(pos, dr, shape.rope)
-        q_pe = apply_rope(q_pe, cos[:, None, :], sin[:, None, :])
+        q_pe = _rope(shape, q_pe, cos[:, None, :], sin[:, None, :])
     qf = np.concatenate([q_nope, q_pe], axis=-1)
     kf = np.concatenate([k_nope, np.broadcast_to(k_pe[:, None, :], (n, H, dr))], axis=-1)
     A = causal_varlen_attention(qf, kf, v, softmax_scale(shape), cu_seqlens)
@@ -282,7 +330,7 @@ def mla_prefill(shape, w: Dict[str, np.ndarray], x, cu_seqlens) -> Dict[str, np.
     if shape.output_gate:
         g = x @ _f64(w["w_g"]).T
         A2 = A2 * (1.0 / (1.0 + np.exp(-g)))
-    out = A2 @ _f64(w["w_o"]).T
+    out = _out_proj(shape, w, A2)
     return {"out": out, "q": qf, "latent": lat, "kv": kv, "attn": A2, "positions": pos}
 
 
@@ -303,7 +351,7 @@ def mla_prefill_rows(shape, w, x, cu_seqlens, rows: Sequence[int]) -> Dict[str, 
     q_nope, q_pe = q[..., :nope], q[..., nope:]
     if shape.rope.kind != "none":
         cos, sin = rope_cos_sin(pos[rows], dr, shape.rope)
-        q_pe = apply_rope(q_pe, cos[:, None, :], sin[:, None, :])
+        q_pe = _rope(shape, q_pe, cos[:, None, :], sin[:, None, :])
     qf = np.empty((n, H, nope + dr), dtype=F64)
     qf[rows] = np.concatenate([q_nope, q_pe], axis=-1)
     kf = np.concatenate([k_nope, np.broadcast_to(k_pe[:, None, :], (n, H, dr))], axis=-1)
@@ -312,7 +360,7 @@ def mla_prefill_rows(shape, w, x, cu_seqlens, rows: Sequence[int]) -> Dict[str, 
     if shape.output_gate:
         g = x[rows] @ _f64(w["w_g"]).T
         A2 = A2 * (1.0 / (1.0 + np.exp(-g)))
-    out = A2 @ _f64(w["w_o"]).T
+    out = _out_proj(shape, w, A2)
     return {"out": out, "attn": A2, "latent": lat, "q": qf[rows], "kv": kv}
 
 
@@ -468,7 +516,7 @@ def mla_prefill_with_prefix(shape, w: Dict[str, np.ndarray], x, cu_seqlens, pref
     q_nope, q_pe = q[..., :nope], q[..., nope:]
     if shape.rope.kind != "none":
         cos, sin = rope_cos_sin(pos[sel], dr, shape.rope)
-        q_pe = apply_rope(q_pe, cos[:, None, :], sin[:, None, :])
+        q_pe = _rope(shape, q_pe, cos[:, None, :], sin[:, None, :])
     qf = np.concatenate([q_nope, q_pe], axis=-1)
     W = _f64(w["w_kv_b"])
     sc = softmax_scale(shape)
@@ -487,7 +535,7 @@ def mla_prefill_with_prefix(shape, w: Dict[str, np.ndarray], x, cu_seqlens, pref
     if shape.output_gate:
         g = x[sel] @ _f64(w["w_g"]).T
         A2 = A2 * (1.0 / (1.0 + np.exp(-g)))
-    out = A2 @ _f64(w["w_o"]).T
+    out = _out_proj(shape, w, A2)
     return {"out": out, "attn": A2, "latent": lat, "q": qf, "positions": pos}
 
 

@@ -480,3 +480,66 @@ def test_chunk_single_query_equals_decode():
     A = om.decode_naive(sh, c.w["w_kv_b"], got["q"][:, :, :nope], got["q"][:, :, nope:], pool, table, lens, 4)
     assert np.allclose(got["attn"].reshape(3, H, dv), A, rtol=1e-12, atol=1e-14)
     assert not np.any(np.isnan(got["out"]))
+
+
+# ----------------------------------------------------------------------------- interleaved RoPE, grouped output projection
+def _il_to_half(d):
+    """Index map: half-split position j takes interleaved feature perm[j]."""
+    return np.concatenate([np.arange(0, d, 2), np.arange(1, d, 2)])
+
+
+def test_interleaved_rope_is_rotate_half_on_regrouped_features():
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((5, 3, 16))
+    c, s = om.rope_cos_sin(np.arange(5), 16, _plain(77.0))
+    perm = _il_to_half(16)
+    got = om.apply_rope_interleaved(x, c[:, None, :], s[:, None, :])
+    want_half = om.apply_rope(x[..., perm], c[:, None, :], s[:, None, :])
+    back = np.empty_like(want_half)
+    back[..., perm] = want_half
+    assert np.allclose(got, back, rtol=1e-14, atol=1e-15)
+    # norm preserved, position 0 the identity
+    assert np.allclose(np.linalg.norm(got, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
+    assert np.array_equal(om.apply_rope_interleaved(x[:1], c[:1, None, :], s[:1, None, :]), x[:1])
+
+
+@pytest.mark.parametrize("rope", ["plain", "yarn"])
+def test_interleaved_layer_equals_rotate_half_layer_with_regrouped_weights(rope):
+    """"Interleaved weights": the layer with interleaved pairs equals the
+    rotate_half layer whose query and key rope rows are regrouped."""
+    spec = {"plain": mi.RopeSpec(kind="plain", theta=500.0),
+            "yarn": mi.RopeSpec(kind="yarn", theta=500.0, factor=4.0, original_max_pos=8, beta_fast=4.0,
+                                beta_slow=1.0, mscale=1.0, mscale_all_dim=1.0)}[rope]
+    sh_il = tiny_shape(rope=spec, rope_interleave=True, num_heads=3, qk_rope_dim=6)
+    sh_h = sh_il.replace(rope_interleave=False)
+    case = mi.make_prefill_case(sh_il, doc_lengths=[6, 4], seed=9)
+    dn, dr, r = sh_il.qk_nope_dim, sh_il.qk_rope_dim, sh_il.kv_lora_rank
+    perm = _il_to_half(dr)
+    w2 = dict(case.w)
+    Wqb = case.w["w_q_b"].reshape(sh_il.num_heads, dn + dr, -1).copy()
+    Wqb[:, dn:, :] = Wqb[:, dn + perm, :]
+    w2["w_q_b"] = Wqb.reshape(case.w["w_q_b"].shape)
+    Wkva = case.w["w_kv_a"].copy()
+    Wkva[r:, :] = case.w["w_kv_a"][r + perm, :]
+    w2["w_kv_a"] = Wkva
+    a = om.mla_prefill(sh_il, case.w, case.x, case.cu_seqlens)
+    b = om.mla_prefill(sh_h, w2, case.x, case.cu_seqlens)
+    assert np.allclose(a["out"], b["out"], rtol=1e-12, atol=1e-14)
+    assert np.allclose(a["latent"][:, r + perm], b["latent"][:, r:], rtol=1e-12, atol=1e-14)
+    # and the pairing matters: without regrouping the outputs differ
+    c_ = om.mla_prefill(sh_h, case.w, case.x, case.cu_seqlens)
+    assert not np.allclose(a["out"], c_["out"], rtol=1e-6)
+
+
+def test_grouped_low_rank_output_projection_equals_its_product():
+    sh = tiny_shape(num_heads=4, v_head_dim=3, o_groups=2, o_lora_rank=5, output_gate=True)
+    case = mi.make_prefill_case(sh, doc_lengths=[7], seed=4)
+    got = om.mla_prefill(sh, case.w, case.x, case.cu_seqlens)
+    G, r = 2, 5
+    fg = sh.num_heads * sh.v_head_dim // G
+    Wa = case.w["w_o_a"].astype(np.float64).reshape(G, r, fg)
+    Wb = case.w["w_o_b"].astype(np.float64)
+    W_o = np.concatenate([Wb[:, g * r:(g + 1) * r] @ Wa[g] for g in range(G)], axis=1)
+    w2 = dict(case.w); w2["w_o"] = W_o
+    want = om.mla_prefill(sh.replace(o_groups=0, o_lora_rank=0), w2, case.x, case.cu_seqlens)
+    assert np.allclose(got["out"], want["out"], rtol=1e-12, atol=1e-14)
