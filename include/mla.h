@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 1
+#define MLA_ABI_VERSION 2
 
 typedef enum mla_status {
   MLA_OK = 0,
@@ -95,6 +95,18 @@ typedef struct mla_config {
   double yarn_beta_slow;
   double yarn_mscale;
   double yarn_mscale_all_dim;
+  /* Layout / config variants (0 = the DeepSeek-V3 defaults above). */
+  int32_t rope_interleave;   /* 1 => RoPE rotates interleaved pairs (2i, 2i+1) in place
+                              * instead of (i, i + d_rope/2): the "interleaved weights"
+                              * branch of the forward in the "CSDN walkthrough of HF
+                              * DeepseekV3Attention"                                    */
+  int32_t o_groups;          /* > 0 => grouped low-rank output projection ("Megatron-LM
+                              * MLA guide", output_projection_groups): the H*d_v
+                              * attention features split into o_groups consecutive
+                              * groups, group g projected to o_lora_rank by its block of
+                              * w_o_a, the groups' results concatenated and projected to
+                              * hidden by w_o_b; w_o unused                            */
+  int32_t o_lora_rank;       /* output_projection_lora_rank (o_groups > 0)            */
 } mla_config;
 
 /* Device pointers to the layer weights, nn.Linear layout, dtype = cfg.dtype. */
@@ -108,6 +120,9 @@ typedef struct mla_weights {
   const void* w_kv_b;      /* [H*(d_nope+d_v), r_kv]; rows of head h: [k_nope | v]    */
   const void* w_o;         /* [hidden, H*d_v]                                         */
   const void* w_g;         /* [H*d_v, hidden] (output_gate, else NULL)                */
+  const void* w_o_a;       /* [o_groups*o_lora_rank, H*d_v/o_groups] (o_groups > 0): rows
+                            * g*o_lora_rank .. of group g                               */
+  const void* w_o_b;       /* [hidden, o_groups*o_lora_rank] (o_groups > 0)           */
 } mla_weights;
 
 /* ---------------------------------------------------------------- host-only */

@@ -33,12 +33,14 @@ class MlaConfig(ctypes.Structure):
         ("norm_eps", ctypes.c_float), ("softmax_scale", ctypes.c_float),
         ("rope_theta", ctypes.c_double), ("yarn_factor", ctypes.c_double), ("yarn_beta_fast", ctypes.c_double),
         ("yarn_beta_slow", ctypes.c_double), ("yarn_mscale", ctypes.c_double), ("yarn_mscale_all_dim", ctypes.c_double),
+        ("rope_interleave", ctypes.c_int32), ("o_groups", ctypes.c_int32), ("o_lora_rank", ctypes.c_int32),
     ]
 
 
 class MlaWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("w_q_a", "q_a_gamma", "w_q_b", "w_q", "w_kv_a", "kv_a_gamma", "w_kv_b", "w_o", "w_g")]
+                ("w_q_a", "q_a_gamma", "w_q_b", "w_q", "w_kv_a", "kv_a_gamma", "w_kv_b", "w_o", "w_g", "w_o_a",
+                 "w_o_b")]
 
 
 _P = ctypes.c_void_p
@@ -107,7 +109,8 @@ def make_config(shape=None, *, softmax_scale: float = 0.0, **kw) -> MlaConfig:
     ``mla_inputs.MLAShape`` (hidden, num_heads, q_lora_rank, kv_lora_rank,
     qk_nope_dim, qk_rope_dim, v_head_dim, dtype "bf16"/"f32", rope (kind,
     theta, factor, original_max_pos, beta_fast, beta_slow, mscale,
-    mscale_all_dim), output_gate, norm_eps), or from keyword arguments."""
+    mscale_all_dim), output_gate, norm_eps, and optionally rope_interleave,
+    o_groups, o_lora_rank), or from keyword arguments."""
     c = MlaConfig()
     if shape is not None:
         r = shape.rope
@@ -121,6 +124,9 @@ def make_config(shape=None, *, softmax_scale: float = 0.0, **kw) -> MlaConfig:
         c.yarn_mscale, c.yarn_mscale_all_dim = r.mscale, r.mscale_all_dim
         c.output_gate = int(shape.output_gate)
         c.norm_eps = shape.norm_eps
+        c.rope_interleave = int(getattr(shape, "rope_interleave", False))
+        c.o_groups = int(getattr(shape, "o_groups", 0))
+        c.o_lora_rank = int(getattr(shape, "o_lora_rank", 0))
     for k, v in kw.items():
         setattr(c, k, v)
     c.softmax_scale = softmax_scale

@@ -62,6 +62,13 @@ mla_status check_config(const mla_config* c) {
   if (!(c->norm_eps >= 0.f) || !std::isfinite(c->norm_eps)) return fail(MLA_ERR_INVALID_ARG, "norm_eps must be finite and >= 0");
   if (!std::isfinite(c->softmax_scale)) return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite");
   if (c->output_gate != 0 && c->output_gate != 1) return fail(MLA_ERR_INVALID_ARG, "output_gate must be 0 or 1");
+  if (c->rope_interleave != 0 && c->rope_interleave != 1) return fail(MLA_ERR_INVALID_ARG, "rope_interleave must be 0 or 1");
+  if (c->o_groups < 0) return fail(MLA_ERR_INVALID_ARG, "o_groups must be >= 0");
+  if (c->o_groups > 0) {
+    if (c->o_lora_rank <= 0) return fail(MLA_ERR_INVALID_ARG, "o_groups > 0 needs o_lora_rank > 0");
+    if (((int64_t)c->num_heads * c->v_head_dim) % c->o_groups)
+      return fail(MLA_ERR_INVALID_ARG, "o_groups must divide num_heads * v_head_dim");
+  }
   return MLA_OK;
 }
 
@@ -72,6 +79,8 @@ mla_status check_supported(const mla_config* c) {
       return fail(MLA_ERR_UNSUPPORTED, "bf16 kernels need d_nope=128, d_rope=64, d_v=128, r_kv=512");
     if (c->hidden % 8 || c->q_lora_rank % 8)
       return fail(MLA_ERR_UNSUPPORTED, "bf16 kernels need hidden and q_lora_rank multiples of 8");
+    if (c->o_groups > 0 && ((c->num_heads * c->v_head_dim / c->o_groups) % 8 || c->o_lora_rank % 8))
+      return fail(MLA_ERR_UNSUPPORTED, "bf16 kernels need the output group width and o_lora_rank multiples of 8");
   } else {
     if (c->qk_nope_dim + c->qk_rope_dim > 512 || c->v_head_dim > 256 || c->qk_rope_dim > 128 || c->kv_lora_rank > 1024)
       return fail(MLA_ERR_UNSUPPORTED, "fp32 kernels need d_nope+d_rope <= 512, d_v <= 256, d_rope <= 128, r_kv <= 1024");
@@ -117,7 +126,7 @@ std::vector<double> rope_frequencies(const mla_config* c) {
 
 // ---------------------------------------------------------------- prefill workspace
 struct PrefillWs {
-  size_t pos, q_lat32, q_lat, q, ckv32, latent, kpe16, kv, attn, ctx, kpe16ctx, cuk, total;
+  size_t pos, q_lat32, q_lat, q, ckv32, latent, kpe16, kv, attn, ot, ctx, kpe16ctx, cuk, total;
 };
 
 // n new tokens; n_ctx >= 0 for a chunk over a cached prefix (context rows of
@@ -138,6 +147,8 @@ PrefillWs prefill_layout(const mla_config* c, int64_t n, int64_t n_ctx = -1, int
   const int64_t kv_rows = n_ctx >= 0 ? n_ctx : n;
   w.kv = off; off += align256(kv_rows * H * (c->qk_nope_dim + c->v_head_dim) * es);
   w.attn = off; off += align256(n * H * c->v_head_dim * es);
+  w.ot = off;
+  if (c->o_groups > 0) off += align256(n * (int64_t)c->o_groups * c->o_lora_rank * es);   // grouped low-rank o-proj
   w.ctx = w.kpe16ctx = w.cuk = off;
   if (n_ctx >= 0) {
     w.ctx = off; off += align256(n_ctx * lw * es);                     // context latent rows
@@ -309,7 +320,7 @@ mla_status mla_latent_norm_rope(const mla_config* cfg, const void* src, int64_t 
   if (slot_mapping && src == dst) return fail(MLA_ERR_INVALID_ARG, "in-place update cannot use a slot mapping");
   NormRopeArgs a{};
   a.src = src; a.src_stride = src_row_stride; a.n_rows = n_rows; a.row_width = row_width;
-  a.norm_dim = norm_dim; a.gamma = gamma; a.eps = cfg->norm_eps;
+  a.norm_dim = norm_dim; a.gamma = gamma; a.eps = cfg->norm_eps; a.interleave = cfg->rope_interleave;
   a.rope_offset = rope_offset; a.rope_slices = rope ? rope_slices : 0;
   a.rope_stride = std::max(rope_slice_stride, cfg->qk_rope_dim); a.rope_dim = cfg->qk_rope_dim;
   a.cos_t = rope_cos; a.sin_t = rope_sin; a.table_len = rope_table_len; a.positions = positions;
@@ -406,8 +417,12 @@ static mla_status check_weights(const mla_config* cfg, const mla_weights* w) {
   if (cfg->q_lora_rank > 0 && (!w->w_q_a || !w->q_a_gamma || !w->w_q_b))
     return fail(MLA_ERR_INVALID_ARG, "q_lora_rank > 0 needs w_q_a, q_a_gamma, w_q_b");
   if (cfg->q_lora_rank == 0 && !w->w_q) return fail(MLA_ERR_INVALID_ARG, "q_lora_rank == 0 needs w_q");
-  if (!w->w_kv_a || !w->kv_a_gamma || !w->w_kv_b || !w->w_o) return fail(MLA_ERR_INVALID_ARG, "w_kv_a, kv_a_gamma, w_kv_b, w_o are required");
+  if (!w->w_kv_a || !w->kv_a_gamma || !w->w_kv_b) return fail(MLA_ERR_INVALID_ARG, "w_kv_a, kv_a_gamma, w_kv_b are required");
+  if (cfg->o_groups == 0 && !w->w_o) return fail(MLA_ERR_INVALID_ARG, "w_o is required");
+  if (cfg->o_groups > 0 && (!w->w_o_a || !w->w_o_b)) return fail(MLA_ERR_INVALID_ARG, "o_groups > 0 needs w_o_a and w_o_b");
   if (cfg->output_gate && !w->w_g) return fail(MLA_ERR_INVALID_ARG, "output_gate needs w_g");
+  if (cfg->dtype == MLA_BF16 && ((w->w_o_a && !aligned16(w->w_o_a)) || (w->w_o_b && !aligned16(w->w_o_b))))
+    return fail(MLA_ERR_MISALIGNED, "bf16 weights must be 16-byte aligned");
   return MLA_OK;
 }
 
@@ -570,7 +585,7 @@ static mla_status prefill_core(const mla_config* cfg, const mla_weights* w, cons
     g.c_f32 = out_kind == OUT_F32 && bf; g.c_f16 = out_kind == OUT_F16 && bf;
     g.epilogue = epi; g.gate_src = gate; g.ldg = ldc;
     g.cos_t = rope_cos; g.sin_t = rope_sin; g.table_len = rope_table_len; g.positions = positions;
-    g.rope_head_stride = dqk; g.rope_off = dn;
+    g.rope_head_stride = dqk; g.rope_off = dn; g.rope_interleave = cfg->rope_interleave;
     const hipError_t err = bf ? launch_gemm_bf16(g, st) : launch_gemm_f32(g, st);
     if (err != hipSuccess) return hip_fail(err, "linear launch");
     return MLA_OK;
@@ -579,7 +594,7 @@ static mla_status prefill_core(const mla_config* cfg, const mla_weights* w, cons
                   int rope_slices, int rope_stride, void* dst, int64_t dst_stride, bool src_f32,
                   f16* aux = nullptr) -> mla_status {
     NormRopeArgs a{};
-    a.rope_aux = aux; a.rope_aux_stride = dr;
+    a.rope_aux = aux; a.rope_aux_stride = dr; a.interleave = cfg->rope_interleave;
     a.src = src; a.src_stride = stride; a.n_rows = n; a.row_width = width; a.norm_dim = norm_dim; a.gamma = gamma;
     a.eps = cfg->norm_eps; a.rope_offset = rope_off; a.rope_slices = rope_slices; a.rope_stride = rope_stride;
     a.rope_dim = dr; a.cos_t = rope_cos; a.sin_t = rope_sin; a.table_len = rope_table_len; a.positions = positions;
@@ -652,7 +667,23 @@ static mla_status prefill_core(const mla_config* cfg, const mla_weights* w, cons
   if (cfg->output_gate) {
     if ((s = gemm(x, hid, w->w_g, attn, (int64_t)H * dv, n, H * dv, hid, OUT_ACT, EPI_GATE, attn)) != MLA_OK) return s;
   }
-  if ((s = gemm(attn, (int64_t)H * dv, w->w_o, out, hid, n, hid, H * dv, OUT_ACT, EPI_STORE, nullptr)) != MLA_OK) return s;
+  if (cfg->o_groups > 0) {
+    // grouped low-rank output projection: group g of the attention features
+    // [n, H d_v / G] times its block of W_o_a -> columns g r_o .. of ot, then
+    // ot W_o_b^T
+    const int G = cfg->o_groups, ro = cfg->o_lora_rank, fg = H * dv / G;
+    void* ot = ws + L.ot;
+    GemmArgs g{};
+    g.a = attn; g.lda = (int64_t)H * dv; g.a_bstride = fg;
+    g.b = w->w_o_a; g.ldb = fg; g.b_bstride = (int64_t)ro * fg;
+    g.c = ot; g.ldc = (int64_t)G * ro; g.c_bstride = ro;
+    g.m = n; g.n = ro; g.k = fg; g.batch = G; g.epilogue = EPI_STORE;
+    e = bf ? launch_gemm_bf16(g, st) : launch_gemm_f32(g, st);
+    if (e != hipSuccess) return hip_fail(e, "grouped output projection launch");
+    if ((s = gemm(ot, (int64_t)G * ro, w->w_o_b, out, hid, n, hid, G * ro, OUT_ACT, EPI_STORE, nullptr)) != MLA_OK) return s;
+  } else {
+    if ((s = gemm(attn, (int64_t)H * dv, w->w_o, out, hid, n, hid, H * dv, OUT_ACT, EPI_STORE, nullptr)) != MLA_OK) return s;
+  }
   return MLA_OK;
 }
 

@@ -149,16 +149,33 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmArgs g) {
         const bool ok = pos >= 0 && pos < g.table_len;
         const float* cs = g.cos_t + (int64_t)(ok ? pos : 0) * 32;
         const float* sn = g.sin_t + (int64_t)(ok ? pos : 0) * 32;
+        if (!g.rope_interleave) {
+          // rotate_half pairs (i, i + 32): column i in acc[0], i + 32 in acc[1]
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+          for (int q = 0; q < 4; ++q)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = q * 8 + (lane >> 5) * 4 + e;
-            const float x0 = acc[0][mi][q * 4 + e], x1 = acc[1][mi][q * 4 + e];
-            const float c = ok ? cs[i] : __builtin_nanf(""), sv = ok ? sn[i] : __builtin_nanf("");
-            acc[0][mi][q * 4 + e] = x0 * c - x1 * sv;
-            acc[1][mi][q * 4 + e] = x1 * c + x0 * sv;
-          }
+            for (int e = 0; e < 4; ++e) {
+              const int i = q * 8 + (lane >> 5) * 4 + e;
+              const float x0 = acc[0][mi][q * 4 + e], x1 = acc[1][mi][q * 4 + e];
+              const float c = ok ? cs[i] : __builtin_nanf(""), sv = ok ? sn[i] : __builtin_nanf("");
+              acc[0][mi][q * 4 + e] = x0 * c - x1 * sv;
+              acc[1][mi][q * 4 + e] = x1 * c + x0 * sv;
+            }
+        } else {
+          // interleaved pairs (2i, 2i + 1): both columns in one lane's run of 4
+#pragma unroll
+          for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+              for (int e = 0; e < 4; e += 2) {
+                const int i = (ni * 32 + q * 8 + (lane >> 5) * 4 + e) >> 1;
+                const float x0 = acc[ni][mi][q * 4 + e], x1 = acc[ni][mi][q * 4 + e + 1];
+                const float c = ok ? cs[i] : __builtin_nanf(""), sv = ok ? sn[i] : __builtin_nanf("");
+                acc[ni][mi][q * 4 + e] = x0 * c - x1 * sv;
+                acc[ni][mi][q * 4 + e + 1] = x1 * c + x0 * sv;
+              }
+        }
       }
     }
   }

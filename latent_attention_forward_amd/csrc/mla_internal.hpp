@@ -180,9 +180,10 @@ struct GemmArgs {
   void* c; int64_t ldc; int64_t c_bstride;         // C [m, n]
   const void* gate_src; int64_t ldg;               // epilogue "gate": c = gate_src * sigmoid(acc)
   // epilogue "rope": columns [h*rope_head_stride + rope_off, + 64) of each head
-  // are rotated (rotate_half pairs i, i+32) at positions[m]
+  // are rotated at positions[m]: rotate_half pairs (i, i+32), or interleaved
+  // pairs (2i, 2i+1) with rope_interleave
   const float* cos_t; const float* sin_t; int table_len; const int32_t* positions;
-  int rope_head_stride; int rope_off;
+  int rope_head_stride; int rope_off; int rope_interleave;
   int m, n, k, batch;
   bool b_kn;                                       // true: B stored [k, n] (NN)
   bool c_f32;                                      // true: C stored as fp32
@@ -201,6 +202,7 @@ struct NormRopeArgs {
   const float* cos_t; const float* sin_t; int table_len; const int32_t* positions;
   void* dst; int64_t dst_stride; const int32_t* slots; int64_t num_slots;
   f16* rope_aux; int64_t rope_aux_stride;          // optional fp16 copy of the rotated slice (one slice)
+  int interleave;                                  // pairs (2i, 2i+1) instead of (i, i + d/2)
 };
 // src/dst element types: bf16 -> bf16, fp32 -> fp32, or fp32 -> bf16 (src_f32 with bf16_io).
 hipError_t launch_norm_rope(const NormRopeArgs& a, bool bf16_io, hipStream_t s, bool src_f32 = false);

@@ -65,7 +65,9 @@ __global__ __launch_bounds__(64 * ROWS_PER_BLOCK) void norm_rope_kernel(NormRope
   const int pairs = a.rope_slices * half;
   for (int p = lane; p < pairs; p += 64) {
     const int s = p / half, i = p - s * half;
-    const int c0 = a.rope_offset + s * a.rope_stride + i, c1 = c0 + half;
+    // pair (i, i + half), or (2i, 2i + 1) for interleaved pairs
+    const int l0 = a.interleave ? 2 * i : i, l1 = a.interleave ? 2 * i + 1 : i + half;
+    const int c0 = a.rope_offset + s * a.rope_stride + l0, c1 = a.rope_offset + s * a.rope_stride + l1;
     const float x0 = to_f32(src[c0]), x1 = to_f32(src[c1]);
     float y0, y1;
     if (pos_ok) {
@@ -79,8 +81,8 @@ __global__ __launch_bounds__(64 * ROWS_PER_BLOCK) void norm_rope_kernel(NormRope
     dst[c1] = from_f32<T>(y1);
     if (a.rope_aux) {   // fp16 copy of the rotated slice, rounded once from fp32
       f16* aux = a.rope_aux + (int64_t)row * a.rope_aux_stride + (int64_t)s * a.rope_dim;
-      aux[i] = (f16)y0;
-      aux[i + half] = (f16)y1;
+      aux[l0] = (f16)y0;
+      aux[l1] = (f16)y1;
     }
   }
 }

@@ -37,7 +37,7 @@ def test_header_symbols_exported(lib):
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(mla.exported_symbols())
-    assert lib.mla_abi_version() == 1
+    assert lib.mla_abi_version() == 2
 
 
 def test_config_validation(lib):
@@ -46,12 +46,18 @@ def test_config_validation(lib):
     bad = [
         dict(qk_rope_dim=63), dict(num_heads=0), dict(dtype=7), dict(rope_kind=9),
         dict(yarn_beta_fast=0.5), dict(rope_theta=0.0), dict(output_gate=3), dict(kv_lora_rank=-1),
+        dict(rope_interleave=2), dict(o_groups=-1), dict(o_groups=8, o_lora_rank=0), dict(o_groups=3, o_lora_rank=64),
     ]
     for kw in bad:
         c = mla.make_config(mi.WORKLOADS["dsv3_prefill_4096"], **kw)
         assert lib.mla_validate_config(ctypes.byref(c)) == mla.MLA_ERR_INVALID_ARG, kw
         assert lib.mla_last_error().decode()
     assert lib.mla_validate_config(None) == mla.MLA_ERR_INVALID_ARG
+    for kw in (dict(rope_interleave=1), dict(o_groups=8, o_lora_rank=1024)):
+        c = mla.make_config(mi.WORKLOADS["dsv3_prefill_4096"], **kw)
+        assert lib.mla_validate_config(ctypes.byref(c)) == mla.MLA_OK, kw
+    # the ctypes mirror of the config has the C layout: its size includes the appended variant fields
+    assert ctypes.sizeof(mla.MlaConfig) == 120 and ctypes.sizeof(mla.MlaWeights) == 11 * 8
 
 
 def test_softmax_scale_matches_oracle(lib):
