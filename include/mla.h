@@ -97,9 +97,9 @@ typedef struct mla_config {
   double yarn_mscale_all_dim;
   /* Layout / config variants (0 = the DeepSeek-V3 defaults above). */
   int32_t rope_interleave;   /* 1 => RoPE rotates interleaved pairs (2i, 2i+1) in place
-                              * instead of (i, i + d_rope/2): the "interleaved weights"
-                              * branch of the forward in the "CSDN walkthrough of HF
-                              * DeepseekV3Attention"                                    */
+                              * instead of (i, i + d_rope/2): the rope_interleave branch
+                              * of the forward in the "CSDN walkthrough of HF
+                              * DeepseekV3Attention", for weights with interleaved pairs                                    */
   int32_t o_groups;          /* > 0 => grouped low-rank output projection ("Megatron-LM
                               * MLA guide", output_projection_groups): the H*d_v
                               * attention features split into o_groups consecutive

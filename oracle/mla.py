@@ -148,7 +148,8 @@ def apply_rope_interleaved(x, cos, sin):
     """RoPE on interleaved pairs: features (2i, 2i+1) rotate together by
     position * theta_i, results in place.  The "CSDN walkthrough of HF
     DeepseekV3Attention" (``forward``) branches on ``rope_interleave`` to a
-    variant for interleaved weights and does not print it; this is the
+    variant, for weights whose rope features come in interleaved pairs, that
+    it does not print; this is the
     reading taken (pairing only, layout kept).
 
     Pinned by: equal to ``apply_rope`` on the features regrouped from
