@@ -505,8 +505,9 @@ def test_interleaved_rope_is_rotate_half_on_regrouped_features():
 
 @pytest.mark.parametrize("rope", ["plain", "yarn"])
 def test_interleaved_layer_equals_rotate_half_layer_with_regrouped_weights(rope):
-    """"Interleaved weights": the layer with interleaved pairs equals the
-    rotate_half layer whose query and key rope rows are regrouped."""
+    """With weights laid out for interleaved pairs, the layer with interleaved
+    pairs equals the rotate_half layer whose query and key rope rows are
+    regrouped."""
     spec = {"plain": mi.RopeSpec(kind="plain", theta=500.0),
             "yarn": mi.RopeSpec(kind="yarn", theta=500.0, factor=4.0, original_max_pos=8, beta_fast=4.0,
                                 beta_slow=1.0, mscale=1.0, mscale_all_dim=1.0)}[rope]
