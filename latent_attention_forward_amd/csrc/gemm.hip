@@ -221,6 +221,208 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmArgs g) {
     }
 }
 
+// Large bf16 GEMMs (the projections whose grid fills the GPU many times):
+// 256x256 output tile per 256-thread workgroup, one wave per SIMD, each wave a
+// 128x128 quadrant (4x4 MFMA tiles, the fp32 accumulators in AGPRs).  K steps
+// of 32; the operand tiles go global->LDS with global_load_lds_dwordx4 (no
+// register staging), 4 LDS stages with 3 in flight, one barrier per step.
+// Per step and CU: 1024 MFMA cycles per SIMD against 64 KB of operand reads
+// and 32 KB of copies in LDS (~768 cycles at 128 B/clk).
+// LDS tile [256 rows][32 k]: 4 chunks of 16 B per row, chunk c of row r at
+// c ^ ((r >> 2) & 3), so the 16 rows one 16-lane phase of an operand read
+// touches (4 rows per 256 B of banks) land on distinct banks.
+constexpr int GBM = 256, GBN = 256, GBK = 32, GSTAGES = 4;
+__device__ __forceinline__ int gsw(int r, int c) { return r * GBK + ((c ^ ((r >> 2) & 3)) << 3); }
+
+template <int EPI, int CT>   // CT: 0 bf16, 2 fp16 output
+__global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g) {
+  // operand stages, then (after the K loop) the 256x256 output tile in 16-bit
+  // values: row r of 512 B with 16-byte chunk c at c ^ (r & 31)
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * GSTAGES * GBM * GBK];
+  bf16 (*sX)[GBM * GBK] = (bf16 (*)[GBM * GBK])smem;                          // activation rows (m)
+  bf16 (*sW)[GBN * GBK] = (bf16 (*)[GBN * GBK])(smem + GSTAGES * GBM * GBK);  // weight rows (n)
+  static_assert(2 * GSTAGES * GBM * GBK >= GBM * GBN, "the output tile reuses the operand stages");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int num_m = (g.m + GBM - 1) / GBM, num_n = (g.n + GBN - 1) / GBN;
+  const int2 tc = tile_coords(blockIdx.x, num_m, num_n);
+  const int m0 = tc.x * GBM, n0 = tc.y * GBN;
+  const bf16* A = (const bf16*)g.a + (int64_t)blockIdx.z * g.a_bstride + (int64_t)m0 * g.lda;
+  const bf16* B = (const bf16*)g.b + (int64_t)blockIdx.z * g.b_bstride + (int64_t)n0 * g.ldb;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nk = g.k / GBK;
+
+  // Copies: instruction i of wave w fills the 1 KB block w + 4 i (16 rows) of a
+  // tile; lane l takes row P / 4 and logical chunk (P % 4) ^ swizzle, P = 64
+  // (w + 4 i) + l.  Rows past the matrix read its last row (never stored).
+  uint32_t offx[4], offw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int P = (wave + 4 * i) * 64 + lane, r = P >> 2, c = (P & 3) ^ ((r >> 2) & 3);
+    const int rx = min(m0 + r, g.m - 1) - m0, rw = min(n0 + r, g.n - 1) - n0;
+    offx[i] = (uint32_t)(((int64_t)rx * g.lda + c * 8) * 2);
+    offw[i] = (uint32_t)(((int64_t)rw * g.ldb + c * 8) * 2);
+  }
+  // LDS byte address of this wave's first block in stage 0 of each operand
+  const uint32_t lx = lds_addr_of(&sX[0][0]) + (uint32_t)wave * 1024u;
+  const uint32_t lw = lds_addr_of(&sW[0][0]) + (uint32_t)wave * 1024u;
+  auto issue = [&](int kt) {
+    const uint32_t st = (uint32_t)(kt % GSTAGES) * (GBM * GBK * 2);
+    const bf16* ax = uniform_ptr(A + kt * GBK);
+    const bf16* bw = uniform_ptr(B + kt * GBK);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_dma16_sv_m0(ax, offx[i], lx + st + i * 4096u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_dma16_sv_m0(bw, offw[i], lw + st + i * 4096u);
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  // operand reads: tile row wm*128 + mi*32 + lane%32 (x) / wn*128 + ni*32 + lane%32 (w),
+  // chunk 2 ks + lane/32; the swizzle depends on the row only through bits 2-3,
+  // the same for every mi / ni
+  const int r32 = lane & 31, hs = lane >> 5;
+  int xoff[2], woff[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    xoff[ks] = gsw(wm * 128 + r32, 2 * ks + hs);
+    woff[ks] = gsw(wn * 128 + r32, 2 * ks + hs);
+  }
+  auto compute = [&](int st) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 x[4], w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = *(const bf16x8*)&sX[st][xoff[ks] + i * 32 * GBK];
+        w[i] = *(const bf16x8*)&sW[st][woff[ks] + i * 32 * GBK];
+      }
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) acc[ni][mi] = mfma32(w[ni], x[mi], acc[ni][mi]);
+    }
+  };
+
+#pragma unroll
+  for (int t = 0; t < GSTAGES - 1; ++t)
+    if (t < nk) issue(t);
+  for (int kt = 0; kt < nk; ++kt) {
+    // step kt's copies have landed (later steps' may still fly), for every wave
+    const int ahead = min(nk - 1 - kt, GSTAGES - 2);
+    if (ahead >= 2) vm_wait_keep<16>();
+    else if (ahead == 1) vm_wait_keep<8>();
+    else vm_wait_all();
+    wg_barrier();
+    // the stage step kt + 3 reuses was last read in step kt - 1, which every
+    // wave has finished (barrier above)
+    if (kt + GSTAGES - 1 < nk) issue(kt + GSTAGES - 1);
+    compute(kt % GSTAGES);
+  }
+
+  // RoPE epilogue: rope slices are 64 columns starting at multiples of 64, so
+  // a slice is N-tiles (2p, 2p+1) of a wave: rotate_half pair (i, i + 32) is
+  // register e of tile 2p and of tile 2p+1 in the same lane; interleaved pairs
+  // (2i, 2i+1) are neighbours in a lane's run of 4.
+  if (EPI == EPI_ROPE) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int c0 = n0 + wn * 128 + p * 64;
+      if (c0 + 64 > g.n || (c0 % g.rope_head_stride) != g.rope_off) continue;
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) {
+        const int m = m0 + wm * 128 + mi * 32 + r32;
+        if (m >= g.m) continue;
+        const int pos = g.positions[m];
+        const bool ok = pos >= 0 && pos < g.table_len;
+        const float* cs = g.cos_t + (int64_t)(ok ? pos : 0) * 32;
+        const float* sn = g.sin_t + (int64_t)(ok ? pos : 0) * 32;
+        if (!g.rope_interleave) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int i = q * 8 + hs * 4 + e;
+              const float x0 = acc[2 * p][mi][q * 4 + e], x1 = acc[2 * p + 1][mi][q * 4 + e];
+              const float c = ok ? cs[i] : __builtin_nanf(""), sv = ok ? sn[i] : __builtin_nanf("");
+              acc[2 * p][mi][q * 4 + e] = x0 * c - x1 * sv;
+              acc[2 * p + 1][mi][q * 4 + e] = x1 * c + x0 * sv;
+            }
+        } else {
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+              for (int e = 0; e < 4; e += 2) {
+                const int i = (t * 32 + q * 8 + hs * 4 + e) >> 1;
+                const float x0 = acc[2 * p + t][mi][q * 4 + e], x1 = acc[2 * p + t][mi][q * 4 + e + 1];
+                const float c = ok ? cs[i] : __builtin_nanf(""), sv = ok ? sn[i] : __builtin_nanf("");
+                acc[2 * p + t][mi][q * 4 + e] = x0 * c - x1 * sv;
+                acc[2 * p + t][mi][q * 4 + e + 1] = x1 * c + x0 * sv;
+              }
+        }
+      }
+    }
+  }
+
+  // Store through LDS: the lane holds output row wm*128 + mi*32 + lane%32 and,
+  // per N-tile, 4 runs of 4 consecutive columns; those go to the LDS tile, and
+  // the tile leaves as whole rows, 16 bytes per lane, consecutive lanes on
+  // consecutive addresses.
+  const bf16* G = (const bf16*)g.gate_src + (EPI == EPI_GATE ? (int64_t)blockIdx.z * g.c_bstride : 0);
+  lds_wait_all();
+  wg_barrier();                            // every wave is done with the operand stages
+  char* tile = (char*)smem;
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      const int ml = wm * 128 + mi * 32 + r32;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int nl = wn * 128 + ni * 32 + q * 8 + hs * 4;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[ni][mi][q * 4 + e];
+        if (EPI == EPI_GATE) {
+          const int m = min(m0 + ml, g.m - 1), n = min(n0 + nl, g.n - 4);
+          const bf16x4 gs = *(const bf16x4*)(G + (int64_t)m * g.ldg + n);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (float)gs[e] * (1.f / (1.f + __expf(-v[e])));
+        }
+        char* dst = tile + ml * 512 + ((((nl >> 3) ^ (ml & 31))) << 4) + ((nl >> 2) & 1) * 8;
+        if (CT == 2) {
+          f16x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = (f16)v[e];
+          *(f16x4*)dst = o;
+        } else {
+          bf16x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = (bf16)v[e];
+          *(bf16x4*)dst = o;
+        }
+      }
+    }
+  lds_wait_all();
+  wg_barrier();
+  char* C = (char*)g.c + ((int64_t)blockIdx.z * g.c_bstride) * 2;
+#pragma unroll 4
+  for (int i = 0; i < GBM * GBN * 2 / 16 / 256; ++i) {
+    const int id = i * 256 + tid, r = id >> 5, c = id & 31;
+    const int m = m0 + r, n = n0 + c * 8;
+    if (m < g.m && n < g.n)
+      *(uint4*)(C + ((int64_t)m * g.ldc + n) * 2) = *(const uint4*)(tile + r * 512 + ((c ^ (r & 31)) << 4));
+  }
+}
+
 // fp32 kernel for the fp32 dtype: 16x16 outputs per 256-thread block, K tiles of
 // 16 through LDS, one output per thread.
 template <int EPI>
@@ -263,6 +465,31 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
   const int num_m = (g.m + BM - 1) / BM, num_n = (g.n + BN - 1) / BN;
   dim3 grid(num_m * num_n, 1, g.batch);
   const int ct = g.c_f32 ? 1 : (g.c_f16 ? 2 : 0);
+  // the 256x256 kernel when its grid covers every CU at least once and the
+  // operands suit its copies (K a multiple of 32, 16-byte rows and batch
+  // strides, 256 rows of an operand within 32-bit byte offsets)
+  {
+    const int64_t bm = (g.m + GBM - 1) / GBM, bn = (g.n + GBN - 1) / GBN;
+    const bool fits = !g.b_kn && ct != 1 && g.k >= GBK && g.k % GBK == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 &&
+                      g.a_bstride % 8 == 0 && g.b_bstride % 8 == 0 && (int64_t)GBM * g.lda * 2 < ((int64_t)1 << 31) &&
+                      (int64_t)GBN * g.ldb * 2 < ((int64_t)1 << 31) &&
+                      (g.epilogue != EPI_ROPE || (g.rope_head_stride % 64 == 0 && g.rope_off % 64 == 0));
+    if (fits && bm * bn * g.batch >= 256) {
+      dim3 gb((unsigned)(bm * bn), 1, g.batch);
+      if (g.epilogue == EPI_GATE) {
+        if (ct != 0) return hipErrorInvalidValue;
+        gemm_bf16_big_kernel<EPI_GATE, 0><<<gb, 256, 0, s>>>(g);
+      } else if (g.epilogue == EPI_ROPE) {
+        if (ct == 2) gemm_bf16_big_kernel<EPI_ROPE, 2><<<gb, 256, 0, s>>>(g);
+        else gemm_bf16_big_kernel<EPI_ROPE, 0><<<gb, 256, 0, s>>>(g);
+      } else if (ct == 2) {
+        gemm_bf16_big_kernel<EPI_STORE, 2><<<gb, 256, 0, s>>>(g);
+      } else {
+        gemm_bf16_big_kernel<EPI_STORE, 0><<<gb, 256, 0, s>>>(g);
+      }
+      return hipGetLastError();
+    }
+  }
   if (g.b_kn) {
     if (g.epilogue != EPI_STORE || ct != 0) return hipErrorInvalidValue;
     gemm_bf16_kernel<true, EPI_STORE, 0><<<grid, NT, 0, s>>>(g);

@@ -137,7 +137,9 @@ def test_q_rope_in_place_and_norm_only(mla):
 
 
 # ----------------------------------------------------------------------------- GEMM
-@pytest.mark.parametrize("m,n,k", [(1, 8, 8), (77, 136, 72), (300, 576, 2048), (256, 1024, 512)])
+@pytest.mark.parametrize("m,n,k", [(1, 8, 8), (77, 136, 72), (300, 576, 2048), (256, 1024, 512),
+                                   # 256x256-tile kernel: ragged m and n, 1 and 3 K steps, long K
+                                   (1000, 16400, 2048), (1024, 16384, 32), (1100, 16384, 96), (4096, 7168, 512)])
 def test_linear_bf16(mla, m, n, k):
     _say(f"case: linear bf16 {m}x{n}x{k}")
     rng = np.random.default_rng(m + n + k)
