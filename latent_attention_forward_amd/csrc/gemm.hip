@@ -266,14 +266,15 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g) {
   // LDS byte address of this wave's first block in stage 0 of each operand
   const uint32_t lx = lds_addr_of(&sX[0][0]) + (uint32_t)wave * 1024u;
   const uint32_t lw = lds_addr_of(&sW[0][0]) + (uint32_t)wave * 1024u;
-  auto issue = [&](int kt) {
+  // copy j (0..7) of step kt: x blocks for j < 4, w blocks for j >= 4
+  auto issue_part = [&](int kt, int j) __attribute__((always_inline)) {
     const uint32_t st = (uint32_t)(kt % GSTAGES) * (GBM * GBK * 2);
-    const bf16* ax = uniform_ptr(A + kt * GBK);
-    const bf16* bw = uniform_ptr(B + kt * GBK);
+    if (j < 4) lds_dma16_sv_m0(uniform_ptr(A + kt * GBK), offx[j], lx + st + j * 4096u);
+    else lds_dma16_sv_m0(uniform_ptr(B + kt * GBK), offw[j - 4], lw + st + (j - 4) * 4096u);
+  };
+  auto issue = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lds_dma16_sv_m0(ax, offx[i], lx + st + i * 4096u);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lds_dma16_sv_m0(bw, offw[i], lw + st + i * 4096u);
+    for (int j = 0; j < 8; ++j) issue_part(kt, j);
   };
 
   f32x16 acc[4][4];
@@ -294,7 +295,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g) {
     xoff[ks] = gsw(wm * 128 + r32, 2 * ks + hs);
     woff[ks] = gsw(wn * 128 + r32, 2 * ks + hs);
   }
-  auto compute = [&](int st) {
+  // The copies of step kiss (when >= 0) go out one per 4 MFMAs: issued all at
+  // once, right after the barrier, the four waves' copies queue at the address
+  // unit they share for ~400 cycles.
+  auto compute = [&](int st, int kiss) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       bf16x8 x[4], w[4];
@@ -304,9 +308,13 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g) {
         w[i] = *(const bf16x8*)&sW[st][woff[ks] + i * 32 * GBK];
       }
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
+      for (int ni = 0; ni < 4; ++ni) {
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) acc[ni][mi] = mfma32(w[ni], x[mi], acc[ni][mi]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (kiss >= 0) issue_part(kiss, ks * 4 + ni);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
 
@@ -322,8 +330,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g) {
     wg_barrier();
     // the stage step kt + 3 reuses was last read in step kt - 1, which every
     // wave has finished (barrier above)
-    if (kt + GSTAGES - 1 < nk) issue(kt + GSTAGES - 1);
-    compute(kt % GSTAGES);
+    compute(kt % GSTAGES, kt + GSTAGES - 1 < nk ? kt + GSTAGES - 1 : -1);
   }
 
   // RoPE epilogue: rope slices are 64 columns starting at multiples of 64, so
