@@ -37,7 +37,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_BYTES = 256 << 20
 # sources whose change invalidates a committed counter figure
 KERNEL_SOURCES = {"flash": ["flash.hip", "mla_internal.hpp"],
-                  "decode": ["decode.hip", "api.hip", "mla_internal.hpp"]}
+                  "decode": ["decode.hip", "api.hip", "mla_internal.hpp"],
+                  "chunk": ["flash.hip", "mla_internal.hpp"]}
 
 
 def parse():
@@ -338,7 +339,9 @@ def main():
     kva = torch.randn(n, H, sh.qk_nope_dim + sh.v_head_dim, device=dev, generator=g).to(torch.float16)
     kpe = torch.randn(n, sh.qk_rope_dim, device=dev, generator=g).to(torch.float16)
     attn = torch.empty(n, H, sh.v_head_dim, dtype=torch.bfloat16, device=dev)
-    for _ in range(max(2, args.warmup)):
+    # warm-up launches bring the GPU to the kernel's steady state after the
+    # layer steps (power and clock state, caches)
+    for _ in range(max(20, args.warmup)):
         mla.attention_prefill(cfg, qa, kva, kpe, cu, cuh, attn)
     ae = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for i in range(args.steps):
@@ -353,7 +356,11 @@ def main():
     flush = torch.zeros(512 << 20, dtype=torch.uint8, device=dev)
     sink = torch.zeros(1, dtype=torch.int64, device=dev)
     de = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for _ in range(2):
+    # decode in its own steady state: 20 warm-up calls, each after the flush as
+    # the timed ones (2 warm-up calls after the attention loop measured 139-149
+    # us against 134 us here)
+    for _ in range(20):
+        sink.copy_(flush.view(torch.int64).sum())
         decode()
     for i in range(args.steps):
         sink.copy_(flush.view(torch.int64).sum())
@@ -367,7 +374,7 @@ def main():
     chunk_rec = None
     if chunk is not None:
         def timed(fn, k):
-            for _ in range(2):
+            for _ in range(10):
                 fn()
             ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(k)]
             for i in range(k):
@@ -390,6 +397,7 @@ def main():
                      "attn_ms": round(c_attn_ms, 4), "attn_tflops": round(c_tflops, 2),
                      "roofline": {"bound": "mfma", "achieved": round(c_tflops, 2), "peak": PEAK_MFMA_TFLOPS,
                                   "unit": "TFLOP/s", "frac": round(c_tflops / PEAK_MFMA_TFLOPS, 4),
+                                  "traffic": traffic_for("chunk"),
                                   "kernel": "flash_mfma_kernel<fp16> (queries over cached + new keys)",
                                   "flops_per_launch": c_aflops}}
         del chunk
