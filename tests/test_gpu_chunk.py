@@ -59,6 +59,9 @@ SMALL = {
                           [128, 33], [256, 1], 16),
     "kimi_gate_nope": (mi.WORKLOADS["kimi_gated_varlen_8192"].replace(hidden=384, num_heads=3, q_lora_rank=128),
                        [33, 190], [200, 17], 32),
+    # many sequences with mixed prefixes, 16-token blocks
+    "v3_many_small_blocks": (mi.WORKLOADS["dsv3_prefill_4096"].replace(hidden=512, num_heads=2, q_lora_rank=256),
+                             [1, 2, 129, 64, 7, 300, 1, 50], [0, 1, 15, 16, 17, 1000, 4095, 127], 16),
 }
 
 

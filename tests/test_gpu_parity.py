@@ -280,7 +280,9 @@ def run_decode(mla, sh, dc):
     return out.float().cpu().numpy()
 
 
-@pytest.mark.parametrize("heads,lens,bs", [(128, [1, 17, 64, 65, 1000, 3000], 64), (32, [5, 300], 16), (96, [129, 700], 32)])
+@pytest.mark.parametrize("heads,lens,bs", [(128, [1, 17, 64, 65, 1000, 3000], 64), (32, [5, 300], 16), (96, [129, 700], 32),
+                                           # long sequences on small blocks; one sequence spanning many workgroups
+                                           (64, [8192, 31, 4000], 16), (128, [30000], 64), (128, [1] * 40 + [2048], 32)])
 def test_decode_small(mla, heads, lens, bs):
     _say(f"case: decode heads={heads} lens={lens} block={bs}")
     sh = mi.WORKLOADS["dsv3_decode_64"].replace(num_heads=heads)
