@@ -182,7 +182,7 @@ struct DecodePlan {
 
 // The keys of all sequences, one after another, each sequence preceded by
 // kDecodeSegmentCost placeholder keys, are dealt to workgroups in runs of
-// `quota` keys (a multiple of 64; at most as many blocks of the smallest
+// `quota` keys (a multiple of 32; at most as many blocks of the smallest
 // allowed size, 16, as a workgroup can stage).  The placeholders charge the
 // workgroup that starts a sequence for the fixed cost of one more segment
 // (staging, query load, pipeline fill, partial stores), so workgroups that
@@ -196,7 +196,7 @@ DecodePlan decode_plan(const mla_config* c, const int32_t* lens, int batch, int6
     const int64_t L = std::min<int64_t>(std::max(lens[b], 0), key_cap);
     if (L > 0) total += L + kDecodeSegmentCost;
   }
-  constexpr int kTile = 64, kMaxQuota = ((kDecodeMaxChunkBlocks - 2) * 16 - kTile) / kTile * kTile;
+  constexpr int kTile = 32, kMaxQuota = ((kDecodeMaxChunkBlocks - 2) * 16 - kTile) / kTile * kTile;
   int64_t quota = kTile * std::max<int64_t>(1, (total + (int64_t)kTile * kDecodeTargetGroups - 1) /
                                                    ((int64_t)kTile * kDecodeTargetGroups));
   quota = std::min<int64_t>(quota, kMaxQuota);

@@ -6,11 +6,11 @@
 // each preceded by kDecodeSegmentCost placeholder keys (the fixed cost of a
 // segment, charged to the workgroup that starts the sequence), form one long
 // sequence; workgroup g takes the keys [g R, (g+1) R) of it (R, the quota, a
-// multiple of 64 chosen so that about one workgroup per CU results), cut at
+// multiple of 32 chosen so that about one workgroup per CU results), cut at
 // each sequence boundary into segments.  A cut that falls
-// inside a sequence is moved to the nearest multiple of 64 keys of that
+// inside a sequence is moved to the nearest multiple of 32 keys of that
 // sequence (both workgroups sharing it round it the same way), so every
-// workgroup gets R +- 64 keys of work whatever the length mix.  Segment (g, b)
+// workgroup gets R +- 32 keys of work whatever the length mix.  Segment (g, b)
 // writes its partial result to slot g - floor(r_b / R) of sequence b, r_b the
 // position of b's first key.
 //
@@ -160,9 +160,9 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
   const int L = max(0, min(a.seq_lens[b], cap));
   const int64_t r0 = st + kDecodeSegmentCost;   // work-order position of key 0 of b
   if (L == 0 || S1 <= r0) continue;             // none of b's keys fall to this workgroup
-  // cut points inside the sequence move to the nearest multiple of 64 keys
+  // cut points inside the sequence move to the nearest multiple of 32 keys (one tile)
   auto cut = [&](int64_t x) -> int {
-    return x <= 0 ? 0 : (x >= L ? L : (int)min<int64_t>(L, ((x + 32) >> 6) << 6));
+    return x <= 0 ? 0 : (x >= L ? L : (int)min<int64_t>(L, ((x + 16) >> 5) << 5));
   };
   const int k0 = cut(S0 - r0), k1 = cut(S1 - r0);
   const int slot = (int)(item - r0 / R);

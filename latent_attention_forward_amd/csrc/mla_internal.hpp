@@ -267,7 +267,7 @@ struct DecodeArgs {
   bf16* out;              // [B, H, dv]
   int dv;
   int batch; int heads;
-  int quota;              // keys per workgroup of the concatenated key sequence (multiple of 64)
+  int quota;              // keys per workgroup of the concatenated key sequence (multiple of 32)
   int max_slots;          // partial slots per sequence
   int num_items;          // workgroups of the split kernel
   float scale;
