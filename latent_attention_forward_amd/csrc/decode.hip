@@ -462,11 +462,18 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
 // is copied to LDS (16 B chunk c of row k at c ^ 2 (k & 3)) and read back
 // transposed as the A operand of 32x32x16 MFMAs, D^T[col, b] = W^T[col, :] .
 // q^T[:, b]; wave w takes columns c0 + 32 w .. + 31 for all sequences, 32 at a
-// time, with the q_nope rows read straight from HBM as the B operand.
+// time, with the q_nope rows read straight from HBM as the B operand.  Each
+// block of 32 sequences goes through LDS and leaves as whole 256 B row pieces.
+// The four column blocks of a head run on one XCD (workgroup i on XCD i % 8),
+// so the head's q_nope rows come from HBM once.
 constexpr int ADN = 128, ANC = 128;        // contraction (d_nope), columns per workgroup
 __global__ __launch_bounds__(256) void absorb_q_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 sW[ADN * ANC];
-  const int c0 = blockIdx.x * ANC, h = blockIdx.y;
+  // output block [32 sequences][128 columns]: 16 B chunk c of row r at c ^ (r & 15)
+  __shared__ __attribute__((aligned(16))) bf16 sOut[32 * ANC];
+  constexpr int NCB = RK / ANC;            // column blocks per head
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int c0 = (slot % NCB) * ANC, h = xcd + 8 * (slot / NCB);
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = a.heads, B = a.batch;
   {
@@ -517,17 +524,22 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(DecodeArgs a) {
 #pragma unroll
     for (int ks = 0; ks < ADN / 16; ++ks) acc = mfma32(wa[ks], qb[ks], acc);
     if (m0 + 32 < B) load_q(qb, m0 + 32);
-    // lane holds sequence m0 + lane % 32, columns (i / 4) * 8 + hsel * 4 + i % 4
-    const int b = m0 + col;
-    if (b < B) {
-      bf16* dst = (bf16*)a.qt + ((int64_t)b * H + h) * RK + c0 + wave * 32 + hsel * 4;
+    // lane holds sequence m0 + lane % 32, columns 32 w + (i / 4) * 8 + hsel * 4 + i % 4
+    if (m0 > 0) __syncthreads();           // the previous block has left sOut
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        bf16x4 v;
+    for (int q = 0; q < 4; ++q) {
+      bf16x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (bf16)acc[q * 4 + e];
-        *(bf16x4*)(dst + q * 8) = v;
-      }
+      for (int e = 0; e < 4; ++e) v[e] = (bf16)acc[q * 4 + e];
+      *(bf16x4*)&sOut[col * ANC + (((wave * 4 + q) ^ (col & 15)) << 3) + hsel * 4] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int r = (tid >> 4) + 16 * u, c = tid & 15, b = m0 + r;
+      if (b < B)
+        *(bf16x8*)((bf16*)a.qt + ((int64_t)b * H + h) * RK + c0 + c * 8) =
+            *(const bf16x8*)&sOut[r * ANC + ((c ^ (r & 15)) << 3)];
     }
   }
 }
@@ -696,7 +708,9 @@ __global__ __launch_bounds__(CNW * 64, 1) void decode_combine_unabsorb_kernel(De
 }  // namespace
 
 hipError_t launch_decode_absorb_q(const DecodeArgs& a, hipStream_t s) {
-  absorb_q_kernel<<<dim3(RK / ANC, a.heads), 256, 0, s>>>(a);
+  // one workgroup per (column block, head); XCD x takes heads x, x + 8, ...
+  if (a.heads % 8) return hipErrorInvalidValue;
+  absorb_q_kernel<<<(RK / ANC) * a.heads, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
