@@ -49,6 +49,8 @@ __global__ __launch_bounds__(256) void gather_context_kernel(ChunkGatherArgs g) 
   const int s = blockIdx.y, r0 = blockIdx.x * GR;
   const int cs = g.cuk[s], ce = g.cuk[s + 1];
   const int P = max(0, g.prefix[s]), a = g.cu[s];
+  // new row of context row j (j >= P): a + j - P, valid inside [0, n_new)
+  auto new_ok = [&](int j) { return a + j - P >= 0 && a + j - P < g.n_new; };
   const int len = min(ce, g.n_ctx) - cs;
   if (cs < 0 || r0 >= len) return;
   const int rows = min(GR, len - r0);
@@ -67,7 +69,7 @@ __global__ __launch_bounds__(256) void gather_context_kernel(ChunkGatherArgs g) 
     if (j < P) {
       const int blk = block_of(j);
       if (blk >= 0) src = (const T*)g.cache + (((int64_t)blk << g.log2_block) + (j & bmask)) * lw;
-    } else if (a + j - P < g.n_new) {
+    } else if (new_ok(j)) {
       src = (const T*)g.lat + (int64_t)(a + j - P) * lw;
     }
     const bool bad = src == nullptr;
@@ -91,7 +93,7 @@ __global__ __launch_bounds__(256) void gather_context_kernel(ChunkGatherArgs g) 
           const bf16* row = (const bf16*)g.cache + (((int64_t)blk << g.log2_block) + (j & bmask)) * lw;
           v = (f16)(float)row[lw - dr + c];        // bf16 -> fp16, exact in fp16's normal range
         }
-      } else if (a + j - P < g.n_new) {
+      } else if (new_ok(j)) {
         v = g.kpe16_new[(int64_t)(a + j - P) * dr + c];
       }
       g.kpe16_ctx[(int64_t)(cs + j) * dr + c] = v;
