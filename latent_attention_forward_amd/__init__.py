@@ -169,8 +169,22 @@ def decode_workspace_size(cfg: MlaConfig, seq_lens_host) -> int:
 
 
 # --------------------------------------------------------------------------- device calls
-def _ptr(t) -> Optional[int]:
-    return None if t is None else t.data_ptr()
+def _ptr(t, rows: bool = False) -> Optional[int]:
+    """Device address of a tensor argument.  The library takes raw device
+    pointers, so a host tensor, or a layout the call does not describe, is
+    refused here rather than read wrongly: the tensor must live on a GPU and
+    be contiguous (with ``rows``, only its last dimension must be contiguous:
+    the call takes the row stride as an argument)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor arguments of the library calls must be GPU tensors")
+    if rows:
+        if t.dim() > 0 and t.stride(-1) != 1:
+            raise ValueError("a row-strided tensor argument needs a contiguous last dimension")
+    elif not t.is_contiguous():
+        raise ValueError("tensor arguments of the library calls must be contiguous")
+    return t.data_ptr()
 
 
 def _stream(stream) -> Optional[int]:
@@ -193,9 +207,9 @@ def latent_norm_rope(cfg: MlaConfig, src, n_rows: int, row_width: int, norm_dim:
     lib = load_library()
     table_len = 0 if rope_cos is None else rope_cos.shape[0]
     st = lib.mla_latent_norm_rope(
-        ctypes.byref(cfg), _ptr(src), src.stride(0) if src_row_stride is None else src_row_stride, n_rows,
+        ctypes.byref(cfg), _ptr(src, rows=True), src.stride(0) if src_row_stride is None else src_row_stride, n_rows,
         row_width, norm_dim, _ptr(gamma), rope_offset, rope_slices, rope_slice_stride, _ptr(rope_cos),
-        _ptr(rope_sin), table_len, _ptr(positions), _ptr(dst),
+        _ptr(rope_sin), table_len, _ptr(positions), _ptr(dst, rows=True),
         dst.stride(0) if dst_row_stride is None else dst_row_stride, _ptr(slot_mapping), num_slots, _stream(stream))
     _check(st, "mla_latent_norm_rope")
 
@@ -204,7 +218,7 @@ def linear(cfg: MlaConfig, x, w, y, stream=None):
     lib = load_library()
     m, k = x.shape
     n = w.shape[0]
-    _check(lib.mla_linear(ctypes.byref(cfg), _ptr(x), x.stride(0), _ptr(w), _ptr(y), y.stride(0), m, n, k,
+    _check(lib.mla_linear(ctypes.byref(cfg), _ptr(x, rows=True), x.stride(0), _ptr(w), _ptr(y, rows=True), y.stride(0), m, n, k,
                           _stream(stream)), "mla_linear")
 
 
@@ -218,7 +232,7 @@ def attention_prefill(cfg: MlaConfig, q, kv, kpe, cu_seqlens_dev, cu_seqlens_hos
     lib = load_library()
     cuh = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int32))
     op = {torch.bfloat16: MLA_BF16, torch.float16: MLA_F16, torch.float32: MLA_F32}[q.dtype]
-    _check(lib.mla_attention_prefill(ctypes.byref(cfg), op, _ptr(q), _ptr(kv), _ptr(kpe),
+    _check(lib.mla_attention_prefill(ctypes.byref(cfg), op, _ptr(q), _ptr(kv), _ptr(kpe, rows=True),
                                      kpe.stride(0) if kpe_stride is None else kpe_stride,
                                      _ptr(cu_seqlens_dev), cuh.ctypes.data, len(cuh) - 1, _ptr(attn), None, 0,
                                      _stream(stream)), "mla_attention_prefill")
@@ -234,7 +248,7 @@ def attention_prefix(cfg: MlaConfig, q, kv, kpe, cu_q_dev, cu_q_host: Sequence[i
     cqh = np.ascontiguousarray(np.asarray(cu_q_host, dtype=np.int32))
     ckh = np.ascontiguousarray(np.asarray(cu_k_host, dtype=np.int32))
     op = {torch.bfloat16: MLA_BF16, torch.float16: MLA_F16, torch.float32: MLA_F32}[q.dtype]
-    _check(lib.mla_attention_prefix(ctypes.byref(cfg), op, _ptr(q), _ptr(kv), _ptr(kpe),
+    _check(lib.mla_attention_prefix(ctypes.byref(cfg), op, _ptr(q), _ptr(kv), _ptr(kpe, rows=True),
                                     kpe.stride(0) if kpe_stride is None else kpe_stride, _ptr(cu_q_dev),
                                     cqh.ctypes.data, _ptr(cu_k_dev), ckh.ctypes.data, len(cqh) - 1, _ptr(attn),
                                     _stream(stream)), "mla_attention_prefix")
@@ -244,7 +258,7 @@ def make_weights(w: Dict[str, object]) -> MlaWeights:
     mw = MlaWeights()
     for name, _ in MlaWeights._fields_:
         t = w.get(name)
-        setattr(mw, name, None if t is None else t.data_ptr())
+        setattr(mw, name, _ptr(t))
     return mw
 
 

@@ -151,3 +151,14 @@ def test_device_calls_reject_bad_arguments_before_launch(lib):
                                   4096, 576, 4096, 8, None)
     assert st == mla.MLA_ERR_INVALID_ARG
     assert mla.MLAError(1, "x", "y").status == 1
+
+
+def test_binding_refuses_host_tensors():
+    """The binding passes raw device addresses: a host tensor is refused before
+    any call, never handed to a kernel."""
+    torch = pytest.importorskip("torch")
+    with pytest.raises(ValueError):
+        mla._ptr(torch.zeros(4))
+    with pytest.raises(ValueError):
+        mla._ptr(torch.zeros(4, 4), rows=True)
+    assert mla._ptr(None) is None
