@@ -16,10 +16,11 @@ namespace {
 
 constexpr int BM = 128, BN = 128, BK = 64, NT = 256;
 
-// K-contiguous tile [rows][64]: 8 chunks of 16 B per row, chunk c of row r is
-// stored at chunk c ^ (r & 7) so that 8 consecutive rows read at the same
-// logical chunk hit 8 different 16 B bank groups.
-__device__ __forceinline__ int kmaj(int r, int c) { return r * BK + ((c ^ (r & 7)) << 3); }
+// K-contiguous tile [rows][64]: 8 chunks of 16 B per row (128 B), so rows of
+// one parity start at the same bank.  Chunk c of row r is stored at chunk
+// c ^ ((r >> 1) & 7): the 16 consecutive rows that one 16-lane phase of an
+// operand read (ds_read_b128, same logical chunk) touches cover all 64 banks.
+__device__ __forceinline__ int kmaj(int r, int c) { return r * BK + ((c ^ ((r >> 1) & 7)) << 3); }
 // N-contiguous tile [64 k][128 n] for the transposed (NN) operand: 16 chunks per
 // row, chunk c of row k stored at c ^ ((k & 3) << 1).  A transpose read touches
 // 4 consecutive k rows x 32 B; the swizzle spreads them over 128 B.
