@@ -299,19 +299,23 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g) {
   // The copies of step kiss (when >= 0) go out one per 4 MFMAs: issued all at
   // once, right after the barrier, the four waves' copies queue at the address
   // unit they share for ~400 cycles.
+  // Both k halves' operands are requested up front, so the MFMAs of the
+  // second half find theirs in registers instead of waiting on LDS.
   auto compute = [&](int st, int kiss) {
+    bf16x8 x[2][4], w[2][4];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 x[4], w[4];
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        x[i] = *(const bf16x8*)&sX[st][xoff[ks] + i * 32 * GBK];
-        w[i] = *(const bf16x8*)&sW[st][woff[ks] + i * 32 * GBK];
+        x[ks][i] = *(const bf16x8*)&sX[st][xoff[ks] + i * 32 * GBK];
+        w[ks][i] = *(const bf16x8*)&sW[st][woff[ks] + i * 32 * GBK];
       }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni) {
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) acc[ni][mi] = mfma32(w[ni], x[mi], acc[ni][mi]);
+        for (int mi = 0; mi < 4; ++mi) acc[ni][mi] = mfma32(w[ks][ni], x[ks][mi], acc[ni][mi]);
         __builtin_amdgcn_sched_barrier(0);
         if (kiss >= 0) issue_part(kiss, ks * 4 + ni);
         __builtin_amdgcn_sched_barrier(0);
