@@ -180,7 +180,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported by this build "
-              "(the path runs on a single MI355X; see DESIGN.md for how it would shard).", file=sys.stderr)
+              "(the path runs on a single MI355X; sharding across GPUs is not built).", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
