@@ -179,7 +179,7 @@ print(json.dumps({"prefill_tflops": fp / tp / 1e12, "prefill_T": Tp, "prefill_s"
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported by this build "
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
               "(the path runs on a single MI355X; sharding across GPUs is not built).", file=sys.stderr)
         sys.exit(2)
     import numpy as np
