@@ -136,6 +136,33 @@ def test_q_rope_in_place_and_norm_only(mla):
     assert np.all(np.abs(got[..., 128:] - ref_pe) <= _bf16_ulp(ref_pe) + 1e-30)
 
 
+
+def test_rope_position_outside_table_gives_nan_rows(mla):
+    """A position outside [0, rope_table_len) writes NaN into that row's rope
+    slices only; the other columns of the row and every other row are exact."""
+    _say("case: rope positions outside the table")
+    sh = mi.WORKLOADS["megatron_2x2048"]
+    cfg = mla.make_config(sh)
+    rng = np.random.default_rng(7)
+    n, H, T = 6, 4, 256
+    q = mi.bf16_round(rng.standard_normal((n, H * 192)).astype(np.float32))
+    pos = np.array([0, -1, 5, T, T - 1, 100000], dtype=np.int32)
+    cos, sin = mla.rope_table(cfg, T, DEV)
+    t = dev(q, torch.bfloat16)
+    mla.latent_norm_rope(cfg, t, n, H * 192, 0, None, t, rope_offset=128, rope_slices=H, rope_slice_stride=192,
+                         rope_cos=cos, rope_sin=sin, positions=torch.from_numpy(pos).to(DEV))
+    torch.cuda.synchronize()
+    got = t.float().cpu().numpy().reshape(n, H, 192)
+    qr = q.reshape(n, H, 192)
+    assert np.array_equal(got[..., :128], qr[..., :128])
+    bad = (pos < 0) | (pos >= T)
+    assert np.all(np.isnan(got[bad][..., 128:]))
+    good = np.flatnonzero(~bad)
+    oc, osn = om.rope_cos_sin(pos[good], 64, sh.rope)
+    ref_pe = om.apply_rope(qr[good][..., 128:], oc[:, None, :], osn[:, None, :])
+    assert np.all(np.abs(got[good][..., 128:] - ref_pe) <= _bf16_ulp(ref_pe) + 1e-30)
+
+
 # ----------------------------------------------------------------------------- GEMM
 @pytest.mark.parametrize("m,n,k", [(1, 8, 8), (77, 136, 72), (300, 576, 2048), (256, 1024, 512),
                                    # 256x256-tile kernel: ragged m and n, 1 and 3 K steps, long K
