@@ -376,6 +376,23 @@ def test_prefill_full_size_sampled_rows(mla, name):
     assert np.all(np.isfinite(got))
 
 
+
+def test_decode_quota_clamp_over_two_million_keys(mla):
+    """More cached keys than 256 workgroups can take at the largest quota a
+    workgroup can stage (8128 keys): the split plan clamps the quota and runs
+    more than 256 workgroups.  68 sequences x 30600 keys (2.08 M keys, a 2.4 GB
+    cache); sampled sequences against the oracle."""
+    sh = mi.WORKLOADS["dsv3_decode_64"]
+    lens = [30600] * 68
+    _say(f"case: decode of {len(lens)} x {lens[0]} keys (quota clamp)")
+    dc = mi.make_decode_case(sh, seq_lens=lens, block_size=64)
+    got = run_decode(mla, sh, dc)
+    idx = [0, 33, 67]
+    ra = om.decode_absorbed(sh, dc.w_kv_b, dc.q_nope, dc.q_pe, dc.cache, dc.block_table, dc.seq_lens, 64, batch_idx=idx)
+    bf16_check(ra.reshape(len(idx), -1), got[idx].reshape(len(idx), -1), "out")
+    assert np.all(np.isfinite(got))
+
+
 def test_decode_full_size(mla):
     sh = mi.WORKLOADS["dsv3_decode_64"]
     _say("case: full-size decode, 64 sequences")
