@@ -217,6 +217,34 @@ def test_attention_core(mla, lens):
     bf16_check(ref.reshape(n * 3, 128), attn.float().cpu().numpy().reshape(n * 3, 128), "attn")
 
 
+
+def test_attention_core_one_long_document(mla):
+    """One 40000-token document (313 query tiles, up to 625 key tiles per
+    workgroup) plus a short one after it, 2 heads; sampled query rows against
+    the oracle, all rows finite."""
+    lens = [40000, 77]
+    _say(f"case: attention core lens={lens}")
+    sh = mi.WORKLOADS["dsv3_prefill_4096"].replace(num_heads=2)
+    rng = np.random.default_rng(11)
+    n = sum(lens)
+    q = mi.bf16_round(rng.standard_normal((n, 2, 192)).astype(np.float32))
+    kv = mi.bf16_round(rng.standard_normal((n, 2, 256)).astype(np.float32))
+    lat = mi.bf16_round(rng.standard_normal((n, 576)).astype(np.float32))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cfg = mla.make_config(sh)
+    attn = torch.full((n, 2, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
+    tl = dev(lat, torch.bfloat16)
+    mla.attention_prefill(cfg, dev(q, torch.bfloat16), dev(kv, torch.bfloat16), tl[:, 512:],
+                          torch.from_numpy(cu).to(DEV), cu, attn)
+    torch.cuda.synchronize()
+    got = attn.float().cpu().numpy()
+    assert np.all(np.isfinite(got))
+    rows = [0, 1, 127, 128, 20001, 39871, 39999, 40000, 40076]
+    k = np.concatenate([kv[..., :128], np.broadcast_to(lat[:, None, 512:], (n, 2, 64))], -1)
+    ref = om.causal_varlen_attention(q, k, kv[..., 128:], om.softmax_scale(sh), cu, rows=rows)
+    bf16_check(ref.reshape(len(rows), -1), got[rows].reshape(len(rows), -1), "sampled rows")
+
+
 def test_attention_core_fp16_operands(mla):
     """fp16 operands (as inside the prefill layer), with a dense k_pe buffer."""
     _say("case: attention core fp16 operands")
