@@ -27,11 +27,13 @@ Everything is float64 NumPy (``mla.py``) or pure-Python scalar loops
   unrotated shared key part and the full-rank output gate.
 
 Parity status of each function is listed in its docstring ("pinned by ...").
-Two readings are not pinned by anything on the pages, because the pages cite the
-YaRN paper without printing its formulas: the constant of the YaRN attention
-factor (``yarn_get_mscale``) and the ramp of the YaRN frequency blend
-(``rope_inv_freq`` for kind "yarn").  Their structural properties are pinned
-(identity at factor 1, wavelength limits); the constants are "parity unpinned".
+The pages cite the YaRN paper for the attention factor (``yarn_get_mscale``)
+and the frequency blend (``rope_inv_freq`` for kind "yarn") without printing
+either formula; the paper's forms are taken, and the values they give at the
+DeepSeek-V3 shape (attention factor, softmax scale, the ramp between pair
+indices 10 and 23) are pinned, together with their structural properties
+(identity at factor 1, wavelength limits).  That a trained DeepSeek-V3 uses
+exactly these constants is not claimed: no page prints a value to check.
 """
 from .mla import (  # noqa: F401
     rms_norm, yarn_get_mscale, softmax_scale, rope_inv_freq, rope_cos_sin,

@@ -52,8 +52,11 @@ def yarn_get_mscale(scale: float, mscale: float) -> float:
     "Megatron-LM MLA guide" (MLA overview / softmax scale) states
     softmax_scale = mscale * mscale / sqrt(q_head_dim).  The pages do not print
     the function; the YaRN paper's form is 0.1 * m * ln(s) + 1 for s > 1, and
-    1 otherwise.  Parity unpinned for the 0.1 constant (not on the pages);
-    pinned: s <= 1 gives 1, and m = 0 gives 1.
+    1 otherwise.  Pinned: s <= 1 gives 1, m = 0 gives 1, and the values this
+    form gives at the DeepSeek-V3 shape (1.3688879454113936 for s = 40, m = 1;
+    softmax scale 0.1352337788608801), which a base-10 logarithm, a single
+    factor or the rope-side mscale would miss.  The 0.1 itself is the paper's
+    constant; no page prints it.
     """
     if scale <= 1.0:
         return 1.0
@@ -543,11 +546,12 @@ def mla_prefill_with_prefix(shape, w: Dict[str, np.ndarray], x, cu_seqlens, pref
 # ----------------------------------------------------------------------------
 # Comparison metric
 # ----------------------------------------------------------------------------
-def bf16_excess_error(ref, got, rtol: float = 2.0 ** -7) -> float:
+def bf16_excess_error(ref, got, rtol: float = 2.0 ** -8) -> float:
     """max over rows of max_k (|got - ref| - rtol |ref|)_+ / RMS_k(ref): the
-    error left after allowing one bfloat16 ulp (2^-7 relative) at each element.
-    A result within atol * RMS(row) + rtol * |ref| everywhere scores <= atol.
-    NaN anywhere in ``got`` gives inf."""
+    error left after allowing, at each element, the rounding of a correctly
+    rounded bfloat16 result (half an ulp, at most 2^-8 of |ref|).  A result
+    within atol * RMS(row) + rtol * |ref| everywhere scores <= atol; the exact
+    answer rounded to bfloat16 scores 0.  NaN anywhere in ``got`` gives inf."""
     ref = _f64(ref).reshape(-1, np.shape(ref)[-1])
     got = _f64(got).reshape(ref.shape)
     if not np.all(np.isfinite(got)):

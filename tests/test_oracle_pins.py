@@ -114,6 +114,94 @@ def test_yarn_wavelength_limits():
     assert np.all(np.diff(ratio) <= 1e-15) and ratio.min() >= 1 / y.factor - 1e-15
 
 
+def _yarn(**kw):
+    return mi.RopeSpec(**{**mi.YARN_V3.__dict__, **kw})
+
+
+def _check_yarn_values():
+    """Values the YaRN reading fixes at the DeepSeek-V3 shape (s = 40,
+    original context 4096, beta_fast 32, beta_slow 1, d_rope 64, base 10000).
+
+    Attention factor: the "CSDN walkthrough of HF DeepseekV3Attention"
+    (``__init__``) squares mscale(s, mscale_all_dim) into the softmax scaling,
+    citing the YaRN paper's equations 21-22, whose factor is 0.1 m ln s + 1;
+    the "Megatron-LM MLA guide" (softmax scale) states mscale^2 / sqrt(q_head_dim).
+      mscale(40, 1) = 1 + 0.1 ln 40 = 1.3688879454113936
+      scale = 1.3688879454113936^2 / sqrt(192) = 0.1352337788608801
+    The softmax takes mscale_all_dim only; mscale (the rope-side parameter)
+    only enters the cos/sin amplitude mscale(s, mscale) / mscale(s, mscale_all_dim):
+      mscale = 0.707, mscale_all_dim = 1: scale unchanged, amplitude 0.9210423553163399
+      mscale_all_dim = 0.707:            scale 1.2608037774058554^2 / sqrt(192) = 0.11472138679292612
+    Frequency ramp (pairs turning b times over the original context sit at
+    index d ln(L / (2 pi b)) / (2 ln base): 10.47 for b = 32, 22.51 for b = 1,
+    so low = 10, high = 23): the ratio theta'_i / theta_i is 1 for i <= 10,
+    1/40 for i >= 23, and 1 - (39/40)(i - 10)/13 between, e.g. 0.925 at i = 11,
+    0.55 at i = 16, 0.1 at i = 22."""
+    def close(a, b, rtol=4e-16):
+        assert abs(a - b) <= rtol * abs(b), (a, b)
+
+    close(om.yarn_get_mscale(40.0, 1.0), 1.3688879454113936)
+    v3 = mi.WORKLOADS["dsv3_prefill_4096"]
+    close(om.softmax_scale(v3), 0.1352337788608801)
+    close(om.softmax_scale(v3.replace(rope=_yarn(mscale=0.707))), 0.1352337788608801)
+    close(om.softmax_scale(v3.replace(rope=_yarn(mscale_all_dim=0.707))), 0.11472138679292612)
+    c, s = om.rope_cos_sin([0], 64, _yarn(mscale=0.707))
+    assert np.allclose(c, 0.9210423553163399, rtol=4e-16, atol=0) and np.all(s == 0)
+    c, s = om.rope_cos_sin([0], 64, mi.YARN_V3)
+    assert np.array_equal(c, np.ones_like(c))
+    ratio = om.rope_inv_freq(64, mi.YARN_V3) / om.rope_inv_freq(64, _plain())
+    assert np.array_equal(ratio[:11], np.ones(11))
+    assert np.allclose(ratio[23:], 1 / 40, rtol=1e-15, atol=0)
+    for i, want in ((11, 0.925), (16, 0.55), (22, 0.1)):
+        close(ratio[i], want, rtol=1e-14)
+    assert np.allclose(ratio[11:23], 1 - (39 / 40) * (np.arange(11, 23) - 10) / 13, rtol=1e-14, atol=0)
+
+
+def test_yarn_attention_factor_and_ramp_values():
+    _check_yarn_values()
+
+
+_YARN_MISTAKES = {
+    # the factor with a base-10 logarithm
+    "log10": ("yarn_get_mscale", lambda s, m: 1.0 if s <= 1 else 0.1 * m * math.log10(s) + 1.0),
+    # the factor applied once instead of squared
+    "single_mscale": ("softmax_scale", lambda sh: sh.qk_head_dim ** -0.5 * om.yarn_get_mscale(sh.rope.factor, sh.rope.mscale_all_dim)),
+    # the rope-side mscale in place of mscale_all_dim
+    "mscale_for_all_dim": ("softmax_scale", lambda sh: sh.qk_head_dim ** -0.5 * om.yarn_get_mscale(sh.rope.factor, sh.rope.mscale) ** 2),
+    # the ramp taken over wavelength ratios r = L / lambda instead of pair indices
+    "ramp_in_r": ("rope_inv_freq", lambda d, rope: _ramp_in_r(d, rope)),
+    # the ramp indices rounded the other way (ceil for beta_fast, floor for beta_slow)
+    "ramp_rounding": ("rope_inv_freq", lambda d, rope: _ramp_rounded_inward(d, rope)),
+}
+
+
+def _ramp_in_r(d, rope):
+    inv = rope.theta ** (-2.0 * np.arange(d // 2) / d)
+    if rope.kind != "yarn":
+        return inv
+    r = rope.original_max_pos * inv / (2 * math.pi)
+    g = np.clip((r - rope.beta_slow) / (rope.beta_fast - rope.beta_slow), 0, 1)   # 1: keep
+    return inv * g + inv / rope.factor * (1 - g)
+
+
+def _ramp_rounded_inward(d, rope):
+    inv = rope.theta ** (-2.0 * np.arange(d // 2) / d)
+    if rope.kind != "yarn":
+        return inv
+    idx = lambda b: d * math.log(rope.original_max_pos / (b * 2 * math.pi)) / (2 * math.log(rope.theta))
+    lo, hi = math.ceil(idx(rope.beta_fast)), math.floor(idx(rope.beta_slow))
+    g = np.clip((np.arange(d // 2) - lo) / (hi - lo), 0, 1)
+    return inv * (1 - g) + inv / rope.factor * g
+
+
+@pytest.mark.parametrize("mistake", list(_YARN_MISTAKES))
+def test_yarn_pins_catch_planted_mistakes(monkeypatch, mistake):
+    name, fn = _YARN_MISTAKES[mistake]
+    monkeypatch.setattr(om, name, fn)
+    with pytest.raises(AssertionError):
+        _check_yarn_values()
+
+
 def test_softmax_scale_readings():
     ws = mi.WORKLOADS
     assert om.softmax_scale(ws["tiny_fp32_t64"]) == 48 ** -0.5
@@ -383,10 +471,15 @@ def test_bf16_metrics():
     rng = np.random.default_rng(9)
     y = rng.standard_normal((5, 300))
     yb = mi.bf16_round(y.astype(np.float32)).astype(np.float64)
-    assert om.bf16_excess_error(y, yb) == 0.0          # rounding to bf16 is within one ulp
+    assert om.bf16_excess_error(y, yb) == 0.0          # a correctly rounded result is within half an ulp
     assert 0 < om.row_rel_error(y, yb) < 2e-2
     bad = y.copy(); bad[2, 7] += 0.1 * np.sqrt(np.mean(y[2] ** 2)) + abs(y[2, 7]) * 2 ** -7
     assert om.bf16_excess_error(y, bad) > 2e-2
+    # the next bfloat16 value past the correctly rounded one is counted: at
+    # 1.5 (ulp 2^-7) it lies 2^-7 away, 2^-8 of it beyond the allowance
+    one = np.full((1, 4), 1.5)
+    nxt = one.copy(); nxt[0, 1] = 1.5 + 2.0 ** -7
+    assert om.bf16_excess_error(one, nxt) == (2.0 ** -7 - 2.0 ** -8 * 1.5) / 1.5
     nan = yb.copy(); nan[0, 0] = np.nan
     assert om.bf16_excess_error(y, nan) == float("inf") and om.row_rel_error(y, nan) == float("inf")
 
