@@ -36,9 +36,15 @@
  *     softmax/norm arithmetic) or MLA_F32 (fp32 everywhere).  Norm gains use the
  *     weight dtype; RoPE tables are fp32; index arrays are int32.  Inside the
  *     bf16 prefill layer the attention operands (q, kv, the shared k_pe) are
- *     kept in the workspace as fp16, which has three more mantissa bits than
- *     bf16 and ample range for them; everything the caller passes or receives
- *     stays bf16.
+ *     held in the workspace in the type cfg.attn_operand selects:
+ *     MLA_ATTN_F16 (the default, 0): fp16, three more mantissa bits than bf16,
+ *       which the DeepSeek-V3-shaped layer needs to stay within the parity
+ *       bound; its range is |x| <= 65504, and a q, kv or k_pe value beyond it
+ *       SATURATES to +-65504 (NaN stays NaN), so this mode is for layers whose
+ *       activations stay in that range (the attention output is a convex
+ *       combination of v, so it then does too);
+ *     MLA_ATTN_BF16: bf16 operands, the full bf16 range, less precise.
+ *     Everything the caller passes or receives stays bf16.
  *   - Shapes supported by the bf16 kernels: d_nope = 128, d_rope = 64,
  *     d_v = 128, r_kv = 512 (the DeepSeek-V3 / Kimi head shape); other shapes
  *     return MLA_ERR_UNSUPPORTED for bf16.  The fp32 kernels take any
@@ -54,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 2
+#define MLA_ABI_VERSION 3
 
 typedef enum mla_status {
   MLA_OK = 0,
@@ -65,8 +71,12 @@ typedef enum mla_status {
   MLA_ERR_HIP = 5            /* a HIP launch or copy failed                            */
 } mla_status;
 
-/* MLA_F16 is accepted only as the operand type of mla_attention_prefill. */
+/* MLA_F16 is accepted only as the operand type of mla_attention_prefill and
+ * mla_attention_prefix. */
 typedef enum mla_dtype { MLA_BF16 = 0, MLA_F32 = 1, MLA_F16 = 2 } mla_dtype;
+
+/* Element type of the attention operands inside the bf16 prefill layer. */
+typedef enum mla_attn_operand { MLA_ATTN_F16 = 0, MLA_ATTN_BF16 = 1 } mla_attn_operand;
 
 /* RoPE variant ("Megatron-LM MLA guide", normalization and position-encoding
  * parameters: rope or yarn; "Kimi-K3 atlas": no rotary embedding). */
@@ -107,6 +117,10 @@ typedef struct mla_config {
                               * w_o_a, the groups' results concatenated and projected to
                               * hidden by w_o_b; w_o unused                            */
   int32_t o_lora_rank;       /* output_projection_lora_rank (o_groups > 0)            */
+  int32_t attn_operand;      /* bf16 layers: mla_attn_operand, the element type of the
+                              * attention operands q, kv and k_pe inside mla_prefill_fwd
+                              * and mla_prefill_chunk_fwd (see Dtypes above); must be 0
+                              * for MLA_F32                                            */
 } mla_config;
 
 /* Device pointers to the layer weights, nn.Linear layout, dtype = cfg.dtype. */

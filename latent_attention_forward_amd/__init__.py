@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libmla.so")
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_MISALIGNED, MLA_ERR_HIP = range(6)
 MLA_BF16, MLA_F32, MLA_F16 = 0, 1, 2
 MLA_ROPE_NONE, MLA_ROPE_PLAIN, MLA_ROPE_YARN = 0, 1, 2
+MLA_ATTN_F16, MLA_ATTN_BF16 = 0, 1
 
 
 class MLAError(RuntimeError):
@@ -34,6 +35,7 @@ class MlaConfig(ctypes.Structure):
         ("rope_theta", ctypes.c_double), ("yarn_factor", ctypes.c_double), ("yarn_beta_fast", ctypes.c_double),
         ("yarn_beta_slow", ctypes.c_double), ("yarn_mscale", ctypes.c_double), ("yarn_mscale_all_dim", ctypes.c_double),
         ("rope_interleave", ctypes.c_int32), ("o_groups", ctypes.c_int32), ("o_lora_rank", ctypes.c_int32),
+        ("attn_operand", ctypes.c_int32),
     ]
 
 
@@ -110,7 +112,8 @@ def make_config(shape=None, *, softmax_scale: float = 0.0, **kw) -> MlaConfig:
     qk_nope_dim, qk_rope_dim, v_head_dim, dtype "bf16"/"f32", rope (kind,
     theta, factor, original_max_pos, beta_fast, beta_slow, mscale,
     mscale_all_dim), output_gate, norm_eps, and optionally rope_interleave,
-    o_groups, o_lora_rank), or from keyword arguments."""
+    o_groups, o_lora_rank, attn_operand "f16"/"bf16"), or from keyword
+    arguments."""
     c = MlaConfig()
     if shape is not None:
         r = shape.rope
@@ -127,6 +130,7 @@ def make_config(shape=None, *, softmax_scale: float = 0.0, **kw) -> MlaConfig:
         c.rope_interleave = int(getattr(shape, "rope_interleave", False))
         c.o_groups = int(getattr(shape, "o_groups", 0))
         c.o_lora_rank = int(getattr(shape, "o_lora_rank", 0))
+        c.attn_operand = MLA_ATTN_BF16 if getattr(shape, "attn_operand", "f16") == "bf16" else MLA_ATTN_F16
     for k, v in kw.items():
         setattr(c, k, v)
     c.softmax_scale = softmax_scale
@@ -169,16 +173,19 @@ def decode_workspace_size(cfg: MlaConfig, seq_lens_host) -> int:
 
 
 # --------------------------------------------------------------------------- device calls
-def _ptr(t, rows: bool = False) -> Optional[int]:
+def _ptr(t, rows: bool = False, dtype=None, name: str = "tensor") -> Optional[int]:
     """Device address of a tensor argument.  The library takes raw device
-    pointers, so a host tensor, or a layout the call does not describe, is
-    refused here rather than read wrongly: the tensor must live on a GPU and
-    be contiguous (with ``rows``, only its last dimension must be contiguous:
-    the call takes the row stride as an argument)."""
+    pointers, so a host tensor, an element type other than the one the call
+    reads (``dtype``), or a layout the call does not describe, is refused here
+    rather than read wrongly: the tensor must live on a GPU and be contiguous
+    (with ``rows``, only its last dimension must be contiguous: the call takes
+    the row stride as an argument)."""
     if t is None:
         return None
     if not t.is_cuda:
         raise ValueError("tensor arguments of the library calls must be GPU tensors")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if rows:
         if t.dim() > 0 and t.stride(-1) != 1:
             raise ValueError("a row-strided tensor argument needs a contiguous last dimension")
@@ -193,11 +200,39 @@ def _stream(stream) -> Optional[int]:
     return s.cuda_stream
 
 
-def _workspace(nbytes: int, device, workspace=None):
+def _i32():
+    import torch
+    return torch.int32
+
+
+def _act(cfg: MlaConfig):
+    """Element type of the activations, weights and outputs of a config."""
+    import torch
+    return torch.bfloat16 if cfg.dtype == MLA_BF16 else torch.float32
+
+
+def _workspace(nbytes: int, device, workspace=None, stream=None):
+    """The caller's workspace, or a new one.  A new workspace is allocated on
+    torch's current stream; when the kernels run on another stream it is
+    recorded there, so the caching allocator does not hand the memory out
+    again while they may still use it."""
     import torch
     if workspace is not None:
         return workspace
-    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    if stream is not None and stream != torch.cuda.current_stream(device):
+        ws.record_stream(stream)
+    return ws
+
+
+def _f32():
+    import torch
+    return torch.float32
+
+
+def _resolve_stream(stream):
+    import torch
+    return torch.cuda.current_stream() if stream is None else stream
 
 
 def latent_norm_rope(cfg: MlaConfig, src, n_rows: int, row_width: int, norm_dim: int, gamma, dst,
@@ -205,36 +240,53 @@ def latent_norm_rope(cfg: MlaConfig, src, n_rows: int, row_width: int, norm_dim:
                      rope_cos=None, rope_sin=None, positions=None, slot_mapping=None, num_slots: int = 0,
                      src_row_stride: Optional[int] = None, dst_row_stride: Optional[int] = None, stream=None):
     lib = load_library()
+    act, i32, f32 = _act(cfg), _i32(), _f32()
     table_len = 0 if rope_cos is None else rope_cos.shape[0]
     st = lib.mla_latent_norm_rope(
-        ctypes.byref(cfg), _ptr(src, rows=True), src.stride(0) if src_row_stride is None else src_row_stride, n_rows,
-        row_width, norm_dim, _ptr(gamma), rope_offset, rope_slices, rope_slice_stride, _ptr(rope_cos),
-        _ptr(rope_sin), table_len, _ptr(positions), _ptr(dst, rows=True),
-        dst.stride(0) if dst_row_stride is None else dst_row_stride, _ptr(slot_mapping), num_slots, _stream(stream))
+        ctypes.byref(cfg), _ptr(src, True, act, "src"), src.stride(0) if src_row_stride is None else src_row_stride,
+        n_rows, row_width, norm_dim, _ptr(gamma, dtype=act, name="gamma"), rope_offset, rope_slices,
+        rope_slice_stride, _ptr(rope_cos, dtype=f32, name="rope_cos"), _ptr(rope_sin, dtype=f32, name="rope_sin"),
+        table_len, _ptr(positions, dtype=i32, name="positions"), _ptr(dst, True, act, "dst"),
+        dst.stride(0) if dst_row_stride is None else dst_row_stride,
+        _ptr(slot_mapping, dtype=i32, name="slot_mapping"), num_slots, _stream(stream))
     _check(st, "mla_latent_norm_rope")
 
 
 def linear(cfg: MlaConfig, x, w, y, stream=None):
     lib = load_library()
+    act = _act(cfg)
     m, k = x.shape
     n = w.shape[0]
-    _check(lib.mla_linear(ctypes.byref(cfg), _ptr(x, rows=True), x.stride(0), _ptr(w), _ptr(y, rows=True), y.stride(0), m, n, k,
-                          _stream(stream)), "mla_linear")
+    _check(lib.mla_linear(ctypes.byref(cfg), _ptr(x, True, act, "x"), x.stride(0), _ptr(w, dtype=act, name="w"),
+                          _ptr(y, True, act, "y"), y.stride(0), m, n, k, _stream(stream)), "mla_linear")
+
+
+def _operand_type(cfg: MlaConfig, q, kv, kpe):
+    """Operand type code of an attention call: q, kv and kpe must share one
+    element type (bf16 or fp16 for a bf16 config, fp32 for an fp32 config)."""
+    import torch
+    codes = {torch.bfloat16: MLA_BF16, torch.float16: MLA_F16, torch.float32: MLA_F32}
+    if q.dtype not in codes:
+        raise ValueError(f"attention operands must be bf16, fp16 or fp32, got {q.dtype}")
+    for name, t in (("kv", kv), ("kpe", kpe)):
+        if t.dtype != q.dtype:
+            raise ValueError(f"{name} must have the dtype of q ({q.dtype}), got {t.dtype}")
+    return codes[q.dtype]
 
 
 def attention_prefill(cfg: MlaConfig, q, kv, kpe, cu_seqlens_dev, cu_seqlens_host: Sequence[int], attn,
                       kpe_stride: Optional[int] = None, stream=None):
     """Attention core.  ``kpe`` is a view whose row r is the shared rope key of
-    token r (e.g. ``latent[:, r_kv:]``); its dtype (bf16 / fp16 / fp32) sets
-    the operand type."""
+    token r (e.g. ``latent[:, r_kv:]``); its dtype (bf16 / fp16 / fp32, the
+    same as q and kv) sets the operand type."""
     import numpy as np
-    import torch
     lib = load_library()
     cuh = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int32))
-    op = {torch.bfloat16: MLA_BF16, torch.float16: MLA_F16, torch.float32: MLA_F32}[q.dtype]
+    op = _operand_type(cfg, q, kv, kpe)
     _check(lib.mla_attention_prefill(ctypes.byref(cfg), op, _ptr(q), _ptr(kv), _ptr(kpe, rows=True),
                                      kpe.stride(0) if kpe_stride is None else kpe_stride,
-                                     _ptr(cu_seqlens_dev), cuh.ctypes.data, len(cuh) - 1, _ptr(attn), None, 0,
+                                     _ptr(cu_seqlens_dev, dtype=_i32(), name="cu_seqlens_dev"), cuh.ctypes.data,
+                                     len(cuh) - 1, _ptr(attn, dtype=_act(cfg), name="attn"), None, 0,
                                      _stream(stream)), "mla_attention_prefill")
 
 
@@ -243,22 +295,26 @@ def attention_prefix(cfg: MlaConfig, q, kv, kpe, cu_q_dev, cu_q_host: Sequence[i
     """Attention core of new queries over longer key sequences (aligned at
     the end).  ``q`` rows follow ``cu_q``, ``kv`` and ``kpe`` rows ``cu_k``."""
     import numpy as np
-    import torch
     lib = load_library()
     cqh = np.ascontiguousarray(np.asarray(cu_q_host, dtype=np.int32))
     ckh = np.ascontiguousarray(np.asarray(cu_k_host, dtype=np.int32))
-    op = {torch.bfloat16: MLA_BF16, torch.float16: MLA_F16, torch.float32: MLA_F32}[q.dtype]
+    op = _operand_type(cfg, q, kv, kpe)
+    i32 = _i32()
     _check(lib.mla_attention_prefix(ctypes.byref(cfg), op, _ptr(q), _ptr(kv), _ptr(kpe, rows=True),
-                                    kpe.stride(0) if kpe_stride is None else kpe_stride, _ptr(cu_q_dev),
-                                    cqh.ctypes.data, _ptr(cu_k_dev), ckh.ctypes.data, len(cqh) - 1, _ptr(attn),
-                                    _stream(stream)), "mla_attention_prefix")
+                                    kpe.stride(0) if kpe_stride is None else kpe_stride,
+                                    _ptr(cu_q_dev, dtype=i32, name="cu_q_dev"), cqh.ctypes.data,
+                                    _ptr(cu_k_dev, dtype=i32, name="cu_k_dev"), ckh.ctypes.data, len(cqh) - 1,
+                                    _ptr(attn, dtype=_act(cfg), name="attn"), _stream(stream)),
+           "mla_attention_prefix")
 
 
-def make_weights(w: Dict[str, object]) -> MlaWeights:
+def make_weights(w: Dict[str, object], dtype=None) -> MlaWeights:
+    """``MlaWeights`` from a dict of device tensors (absent names are NULL);
+    with ``dtype`` every weight must have that element type."""
     mw = MlaWeights()
     for name, _ in MlaWeights._fields_:
         t = w.get(name)
-        setattr(mw, name, _ptr(t))
+        setattr(mw, name, _ptr(t, dtype=dtype, name=name))
     return mw
 
 
@@ -268,15 +324,21 @@ def prefill_fwd(cfg: MlaConfig, weights: Dict[str, object], x, cu_seqlens_dev, c
     to device tensors (None for absent ones)."""
     import numpy as np
     lib = load_library()
+    act, i32, f32 = _act(cfg), _i32(), _f32()
     cuh = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int32))
     n, s = int(cuh[-1]), len(cuh) - 1
     ws_bytes = prefill_workspace_size(cfg, n, s)
-    ws = _workspace(ws_bytes, x.device, workspace)
-    mw = make_weights(weights)
+    st = _resolve_stream(stream)
+    ws = _workspace(ws_bytes, x.device, workspace, st)
+    mw = make_weights(weights, act)
     table_len = 0 if rope_cos is None else rope_cos.shape[0]
-    _check(lib.mla_prefill_fwd(ctypes.byref(cfg), ctypes.byref(mw), _ptr(x), _ptr(cu_seqlens_dev), cuh.ctypes.data,
-                               s, _ptr(positions), _ptr(rope_cos), _ptr(rope_sin), table_len, _ptr(out),
-                               _ptr(latent_out), _ptr(ws), ws.numel(), _stream(stream)), "mla_prefill_fwd")
+    _check(lib.mla_prefill_fwd(ctypes.byref(cfg), ctypes.byref(mw), _ptr(x, dtype=act, name="x"),
+                               _ptr(cu_seqlens_dev, dtype=i32, name="cu_seqlens_dev"), cuh.ctypes.data, s,
+                               _ptr(positions, dtype=i32, name="positions"),
+                               _ptr(rope_cos, dtype=f32, name="rope_cos"), _ptr(rope_sin, dtype=f32, name="rope_sin"),
+                               table_len, _ptr(out, dtype=act, name="out"),
+                               _ptr(latent_out, dtype=act, name="latent_out"), _ptr(ws), ws.numel(),
+                               st.cuda_stream), "mla_prefill_fwd")
     return ws
 
 
@@ -284,14 +346,19 @@ def decode_absorbed_fwd(cfg: MlaConfig, w_kv_b, q_nope, q_pe, kv_cache, block_ta
                         seq_lens_host: Sequence[int], out, workspace=None, stream=None):
     import numpy as np
     lib = load_library()
+    act, i32 = _act(cfg), _i32()
     lens = np.ascontiguousarray(np.asarray(seq_lens_host, dtype=np.int32))
     ws_bytes = decode_workspace_size(cfg, lens)
-    ws = _workspace(ws_bytes, q_nope.device, workspace)
+    st = _resolve_stream(stream)
+    ws = _workspace(ws_bytes, q_nope.device, workspace, st)
     num_blocks, block_size = kv_cache.shape[0], kv_cache.shape[1]
-    _check(lib.mla_decode_absorbed_fwd(ctypes.byref(cfg), _ptr(w_kv_b), _ptr(q_nope), _ptr(q_pe), _ptr(kv_cache),
-                                       num_blocks, block_size, _ptr(block_table), block_table.shape[1],
-                                       _ptr(seq_lens_dev), lens.ctypes.data, len(lens), _ptr(out), _ptr(ws),
-                                       ws.numel(), _stream(stream)), "mla_decode_absorbed_fwd")
+    _check(lib.mla_decode_absorbed_fwd(ctypes.byref(cfg), _ptr(w_kv_b, dtype=act, name="w_kv_b"),
+                                       _ptr(q_nope, dtype=act, name="q_nope"), _ptr(q_pe, dtype=act, name="q_pe"),
+                                       _ptr(kv_cache, dtype=act, name="kv_cache"), num_blocks, block_size,
+                                       _ptr(block_table, dtype=i32, name="block_table"), block_table.shape[1],
+                                       _ptr(seq_lens_dev, dtype=i32, name="seq_lens_dev"), lens.ctypes.data,
+                                       len(lens), _ptr(out, dtype=act, name="out"), _ptr(ws), ws.numel(),
+                                       st.cuda_stream), "mla_decode_absorbed_fwd")
     return ws
 
 
@@ -311,17 +378,24 @@ def prefill_chunk_fwd(cfg: MlaConfig, weights: Dict[str, object], x, cu_seqlens_
     ``block_table`` [num_seqs, max_blocks] int32."""
     import numpy as np
     lib = load_library()
+    act, i32, f32 = _act(cfg), _i32(), _f32()
     cuh = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int32))
     pre = np.ascontiguousarray(np.asarray(prefix_lens_host, dtype=np.int32))
     s = len(cuh) - 1
-    ws = _workspace(prefill_chunk_workspace_size(cfg, cuh, pre), x.device, workspace)
-    mw = make_weights(weights)
+    st = _resolve_stream(stream)
+    ws = _workspace(prefill_chunk_workspace_size(cfg, cuh, pre), x.device, workspace, st)
+    mw = make_weights(weights, act)
     table_len = 0 if rope_cos is None else rope_cos.shape[0]
     nb, bs = (0, 0) if kv_cache is None else (kv_cache.shape[0], kv_cache.shape[1])
     mb = 0 if block_table is None else block_table.shape[1]
-    _check(lib.mla_prefill_chunk_fwd(ctypes.byref(cfg), ctypes.byref(mw), _ptr(x), _ptr(cu_seqlens_dev),
-                                     cuh.ctypes.data, s, _ptr(prefix_lens_dev), pre.ctypes.data, _ptr(kv_cache), nb,
-                                     bs, _ptr(block_table), mb, _ptr(rope_cos), _ptr(rope_sin), table_len, _ptr(out),
-                                     _ptr(latent_out), _ptr(ws), ws.numel(), _stream(stream)),
+    _check(lib.mla_prefill_chunk_fwd(ctypes.byref(cfg), ctypes.byref(mw), _ptr(x, dtype=act, name="x"),
+                                     _ptr(cu_seqlens_dev, dtype=i32, name="cu_seqlens_dev"), cuh.ctypes.data, s,
+                                     _ptr(prefix_lens_dev, dtype=i32, name="prefix_lens_dev"), pre.ctypes.data,
+                                     _ptr(kv_cache, dtype=act, name="kv_cache"), nb, bs,
+                                     _ptr(block_table, dtype=i32, name="block_table"), mb,
+                                     _ptr(rope_cos, dtype=f32, name="rope_cos"),
+                                     _ptr(rope_sin, dtype=f32, name="rope_sin"), table_len,
+                                     _ptr(out, dtype=act, name="out"), _ptr(latent_out, dtype=act, name="latent_out"),
+                                     _ptr(ws), ws.numel(), st.cuda_stream),
            "mla_prefill_chunk_fwd")
     return ws

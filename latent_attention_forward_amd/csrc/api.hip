@@ -64,6 +64,10 @@ mla_status check_config(const mla_config* c) {
   if (c->output_gate != 0 && c->output_gate != 1) return fail(MLA_ERR_INVALID_ARG, "output_gate must be 0 or 1");
   if (c->rope_interleave != 0 && c->rope_interleave != 1) return fail(MLA_ERR_INVALID_ARG, "rope_interleave must be 0 or 1");
   if (c->o_groups < 0) return fail(MLA_ERR_INVALID_ARG, "o_groups must be >= 0");
+  if (c->attn_operand != MLA_ATTN_F16 && c->attn_operand != MLA_ATTN_BF16)
+    return fail(MLA_ERR_INVALID_ARG, "attn_operand must be MLA_ATTN_F16 or MLA_ATTN_BF16");
+  if (c->dtype == MLA_F32 && c->attn_operand != 0)
+    return fail(MLA_ERR_INVALID_ARG, "attn_operand must be 0 for an fp32 config");
   if (c->o_groups > 0) {
     if (c->o_lora_rank <= 0) return fail(MLA_ERR_INVALID_ARG, "o_groups > 0 needs o_lora_rank > 0");
     if (((int64_t)c->num_heads * c->v_head_dim) % c->o_groups)
@@ -604,11 +608,13 @@ static mla_status prefill_core(const mla_config* cfg, const mla_weights* w, cons
     return MLA_OK;
   };
   // bf16: RoPE on q is fused into the q GEMM epilogue; fp32: applied in place after it.
-  // In the bf16 layer the attention operands q, kv and the shared k_pe are kept
-  // in fp16 (rounded once from fp32): bf16 storage of all of them puts the layer
-  // output beyond the parity bound at the 128-head shapes.
+  // In the bf16 layer the attention operands q, kv and the shared k_pe are
+  // rounded once from fp32 to the type cfg->attn_operand selects: fp16 (k_pe
+  // gets an fp16 copy of its own; values beyond the fp16 range saturate) or
+  // bf16 (k_pe is read from the latent rows).
+  const bool f16op = bf && cfg->attn_operand == MLA_ATTN_F16;
   const int q_epi = (rope && bf) ? EPI_ROPE : EPI_STORE;
-  const int att_kind = bf ? OUT_F16 : OUT_ACT;
+  const int att_kind = f16op ? OUT_F16 : OUT_ACT;
   f16* kpe16 = (f16*)(ws + L.kpe16);
   if (rq > 0) {
     void* ql_raw = bf ? (void*)q_lat32 : q_lat;
@@ -625,7 +631,7 @@ static mla_status prefill_core(const mla_config* cfg, const mla_weights* w, cons
   {
     void* ckv_raw = bf ? (void*)ckv32 : (void*)(ws + L.ckv32);
     if ((s = gemm(x, hid, w->w_kv_a, ckv_raw, lw, n, lw, hid, OUT_F32, EPI_STORE, nullptr)) != MLA_OK) return s;
-    if ((s = norm(ckv_raw, lw, lw, rkv, w->kv_a_gamma, rkv, rope ? 1 : 0, dr, lat, lw, true, bf ? kpe16 : nullptr)) != MLA_OK) return s;
+    if ((s = norm(ckv_raw, lw, lw, rkv, w->kv_a_gamma, rkv, rope ? 1 : 0, dr, lat, lw, true, f16op ? kpe16 : nullptr)) != MLA_OK) return s;
   }
   // The rows keys and values are formed from: the new tokens' latent rows, or
   // for a chunk each sequence's cached prefix rows followed by its new rows.
@@ -642,7 +648,7 @@ static mla_status prefill_core(const mla_config* cfg, const mla_weights* w, cons
     g.cache = chunk->cache; g.block_table = chunk->block_table; g.max_blocks = chunk->max_blocks;
     g.num_blocks = chunk->num_blocks; g.log2_block = chunk->log2_block;
     g.lat = lat; g.ctx = ws + L.ctx;
-    g.kpe16_new = bf ? kpe16 : nullptr; g.kpe16_ctx = bf ? (f16*)(ws + L.kpe16ctx) : nullptr;
+    g.kpe16_new = f16op ? kpe16 : nullptr; g.kpe16_ctx = f16op ? (f16*)(ws + L.kpe16ctx) : nullptr;
     g.row_width = lw; g.rope_dim = dr; g.n_ctx = chunk->n_ctx; g.n_new = n;
     if ((e = launch_gather_context(g, bf, chunk->max_ctx_len, num_seqs, st)) != hipSuccess)
       return hip_fail(e, "context gather");
@@ -657,9 +663,9 @@ static mla_status prefill_core(const mla_config* cfg, const mla_weights* w, cons
     return s;
   // attention
   {
-    const void* kpe = bf ? (const void*)kpe_src16 : (const void*)((const float*)kv_src + rkv);
-    const int64_t kpe_stride = bf ? dr : lw;
-    if ((s = attention_impl(cfg, q, kv, kpe, kpe_stride, bf, cu_seqlens_dev, cu_seqlens_host, num_seqs, n, attn, st,
+    const void* kpe = f16op ? (const void*)kpe_src16 : (const void*)((const char*)kv_src + (size_t)rkv * elem_size(cfg));
+    const int64_t kpe_stride = f16op ? dr : lw;
+    if ((s = attention_impl(cfg, q, kv, kpe, kpe_stride, f16op, cu_seqlens_dev, cu_seqlens_host, num_seqs, n, attn, st,
                             cuk_dev, chunk ? chunk->cuk_host.data() : nullptr, kv_rows)) != MLA_OK)
       return s;
   }
@@ -704,6 +710,9 @@ mla_status mla_decode_absorbed_fwd(const mla_config* cfg, const void* w_kv_b, co
   if (num_blocks <= 0 || max_blocks <= 0) return fail(MLA_ERR_INVALID_ARG, "num_blocks and max_blocks must be > 0");
   if (block_size < 16 || (block_size & (block_size - 1)))
     return fail(MLA_ERR_INVALID_ARG, "block_size must be a power of two >= 16");
+  // the kernels hold a sequence's key count (up to max_blocks * block_size) in 32 bits
+  if ((int64_t)max_blocks * block_size >= ((int64_t)1 << 31))
+    return fail(MLA_ERR_UNSUPPORTED, "max_blocks * block_size must be below 2^31");
   for (int b = 0; b < batch; ++b)
     if (seq_lens_host[b] <= 0 || (int64_t)seq_lens_host[b] > (int64_t)max_blocks * block_size)
       return fail(MLA_ERR_INVALID_ARG, "seq_lens[%d] = %d outside [1, max_blocks * block_size]", b, seq_lens_host[b]);

@@ -91,7 +91,7 @@ __global__ __launch_bounds__(256) void gather_context_kernel(ChunkGatherArgs g) 
         const int blk = block_of(j);
         if (blk >= 0) {
           const bf16* row = (const bf16*)g.cache + (((int64_t)blk << g.log2_block) + (j & bmask)) * lw;
-          v = (f16)(float)row[lw - dr + c];        // bf16 -> fp16, exact in fp16's normal range
+          v = to_f16_sat((float)row[lw - dr + c]);   // bf16 -> fp16, exact in fp16's normal range
         }
       } else if (new_ok(j)) {
         v = g.kpe16_new[(int64_t)(a + j - P) * dr + c];

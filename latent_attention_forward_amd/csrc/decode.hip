@@ -165,7 +165,11 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
     return x <= 0 ? 0 : (x >= L ? L : (int)min<int64_t>(L, ((x + 16) >> 5) << 5));
   };
   const int k0 = cut(S0 - r0), k1 = cut(S1 - r0);
-  const int slot = (int)(item - r0 / R);
+  const int64_t slot64 = item - r0 / R;
+  // the host planned max_slots from its copy of the lengths; a device length
+  // that disagrees with it must not move a store outside the partial buffers
+  if (slot64 < 0 || slot64 >= a.max_slots) continue;
+  const int slot = (int)slot64;
   const int64_t part = ((int64_t)b * a.max_slots + slot) * H;
   if (k0 >= k1) {                          // empty after the cut: weight 0 in the combine
     for (int i = tid; i < H; i += NTH) { a.part_ml[(part + i) * 2] = -INFINITY; a.part_ml[(part + i) * 2 + 1] = 0.f; }
@@ -340,9 +344,11 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
   auto prob = [&](f32x16& s, int e) __attribute__((always_inline)) {
     float p = __builtin_amdgcn_exp2f(fmaf(s[e], c2, -mb));
     asm volatile("" : "+v"(p));
-    l_run += p;
     pb[e >> 3][e & 7] = (bf16)p;
   };
+  // The softmax denominator sums the same bf16-rounded probabilities the PV
+  // MFMA multiplies, so that rounding P scales numerator and denominator alike.
+  auto psum = [&]() __attribute__((always_inline)) { l_run = sum8(pb[1], sum8(pb[0], l_run)); };
   auto no_group = [](auto) {};
   // O^T += C^T P^T; step j covers keys j*16 + {h*4 + [0,4), 8 + h*4 + [0,4)}
   auto pv_tile = [&](int buf) __attribute__((always_inline)) {
@@ -385,6 +391,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
         }
         if constexpr (i == 1) prep_b(t);
         if constexpr (i >= 3 && i <= 33 && (i & 1)) prob(s_cur, (i - 3) >> 1);
+        if constexpr (i == 35) psum();
         if constexpr (i >= 4 && i < 34) {            // copy k at MFMA 4 + floor(30 k / BPW)
           constexpr int ka = ((i - 4) * BPW + 29) / 30;
           if constexpr (ka < BPW && 4 + ka * 30 / BPW == i)
@@ -399,6 +406,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
       prep_b(t);
 #pragma unroll
       for (int e = 0; e < 16; ++e) prob(s_cur, e);
+      psum();
     }
     pv_tile(t % NBUF);
     if (t + 3 < nt) vm_wait_keep<BPW>();   // tile t + 2 landed, t + 3 may fly
@@ -548,13 +556,14 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(DecodeArgs a) {
 // waves:
 //  1. o_lat[b, h, :] = sum_s w_s l_s (O_s / l_s) / sum_s w_s l_s over the
 //     sequence's slots s, with w_s = 2^((m_s - M) * c2); slots emptied by a
-//     cut (l_s = 0) are skipped.  Rounded to bf16 into LDS; each wave takes 4
-//     sequences, two at a time with all their slots loaded before any is used,
-//     8 latent dims per lane.
+//     cut (l_s = 0) are skipped.  Stored into LDS as two bf16 parts, hi =
+//     bf16(o_lat) and lo = bf16(o_lat - hi), which carry o_lat to about 16
+//     significant bits; each wave takes 4 sequences, two at a time with all
+//     their slots loaded before any is used, 8 latent dims per lane.
 //  2. out[b, h, :] = W_UV[h] . o_lat[b, h, :] for the 32 sequences at once:
-//     O^T[dv, b] = W_UV[h][dv, :] . o_lat[b, :]^T on 16x16x32 MFMAs, each wave
-//     16 output dims for both blocks of 16 sequences.  Its W_UV rows are
-//     requested while step 1 runs.
+//     O^T[dv, b] = W_UV[h][dv, :] . (hi + lo)[b, :]^T on 16x16x32 MFMAs (two
+//     per step, one per part), each wave 16 output dims for both blocks of 16
+//     sequences.  Its W_UV rows are requested while step 1 runs.
 // W_UV[h] (128 KB) is read once per 32 sequences; the workgroups of one head
 // run on one XCD (x = h), so it comes from HBM about once.
 constexpr int CB = 32;                     // sequences per combine workgroup
@@ -563,7 +572,7 @@ constexpr int CNW = 8;                     // waves per combine workgroup
 __global__ __launch_bounds__(CNW * 64, 1) void decode_combine_unabsorb_kernel(DecodeArgs a) {
   // latent rows of the block: 16 B chunk c of row j at c ^ (j & 15), so the
   // 16 rows one MFMA operand read touches spread over the banks
-  __shared__ __attribute__((aligned(16))) bf16 sO[CB * RK];
+  __shared__ __attribute__((aligned(16))) bf16 sO[2][CB * RK];
   __shared__ int s_ns[CB];
   __shared__ long long s_red[CNW];
   const int h = blockIdx.x, b0 = blockIdx.y * CB;
@@ -594,7 +603,8 @@ __global__ __launch_bounds__(CNW * 64, 1) void decode_combine_unabsorb_kernel(De
       if (lane >= o) incl += v;
     }
     const long long r0 = base + incl - n + kDecodeSegmentCost;   // work-order position of key 0
-    if (lane < CB) s_ns[lane] = Lb > 0 ? (int)((r0 + Lb - 1) / R - r0 / R + 1) : 0;
+    // slot count, bounded by the slots the host planned (see the split kernel)
+    if (lane < CB) s_ns[lane] = Lb > 0 ? (int)min<long long>((r0 + Lb - 1) / R - r0 / R + 1, a.max_slots) : 0;
   }
   __syncthreads();
 
@@ -668,10 +678,15 @@ __global__ __launch_bounds__(CNW * 64, 1) void decode_combine_unabsorb_kernel(De
       }
       // sequences past the batch and empty ones leave a zero row
       const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-      bf16x8 r;
+      bf16x8 rh, rl;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) r[e] = (bf16)(acc[e] * inv);
-      *(bf16x8*)&sO[j * RK + ((lane ^ (j & 15)) << 3)] = r;
+      for (int e = 0; e < 8; ++e) {
+        const float v = acc[e] * inv;
+        rh[e] = (bf16)v;
+        rl[e] = (bf16)(v - (float)rh[e]);
+      }
+      *(bf16x8*)&sO[0][j * RK + ((lane ^ (j & 15)) << 3)] = rh;
+      *(bf16x8*)&sO[1][j * RK + ((lane ^ (j & 15)) << 3)] = rl;
     }
   }
   __syncthreads();
@@ -689,8 +704,9 @@ __global__ __launch_bounds__(CNW * 64, 1) void decode_combine_unabsorb_kernel(De
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
       const int j = n * 16 + r16;
-      const bf16x8 Bv = *(const bf16x8*)&sO[j * RK + (((ks * 4 + kq) ^ (j & 15)) << 3)];
-      o[n] = mfma16(wf[ks], Bv, o[n]);
+      const int off = j * RK + (((ks * 4 + kq) ^ (j & 15)) << 3);
+      o[n] = mfma16(wf[ks], *(const bf16x8*)&sO[0][off], o[n]);
+      o[n] = mfma16(wf[ks], *(const bf16x8*)&sO[1][off], o[n]);
     }
   // lane holds sequence b0 + 16 n + lane % 16, dims 16 w + (lane / 16) * 4 + [0, 4)
 #pragma unroll

@@ -68,22 +68,6 @@ template <typename V8> __device__ __forceinline__ V8 zero8() { return __builtin_
 template <typename V4, typename T> __device__ __forceinline__ V4 read_tr(const T* p) {
   return __builtin_bit_cast(V4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(p)));
 }
-// acc + sum of the 8 values of v, accumulated in fp32 (two-element dot
-// products with (1, 1)): the row sum of exactly the P values the PV MFMA uses.
-__device__ __forceinline__ float sum8(f16x8 v, float acc) {
-  const f16x2 one = {(f16)1.f, (f16)1.f};
-  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
-  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
-  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
-  return __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
-}
-__device__ __forceinline__ float sum8(bf16x8 v, float acc) {
-  const bf16x2 one = {(bf16)1.f, (bf16)1.f};
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
-}
 // LDS tiles, 16-byte chunks XOR-swizzled by key row so that the rows one
 // operand read touches spread over the banks:
 //   k_nope [64][128]: chunk c (0..15) of row r at c ^ (r & 15)

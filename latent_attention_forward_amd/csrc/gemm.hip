@@ -209,7 +209,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmArgs g) {
           f16* C = (f16*)g.c + (int64_t)blockIdx.z * g.c_bstride;
           f16x4 o;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = (f16)v[e];
+          for (int e = 0; e < 4; ++e) o[e] = to_f16_sat(v[e]);
           *(f16x4*)(C + (int64_t)m * g.ldc + n) = o;
         } else {
           bf16* C = (bf16*)g.c + (int64_t)blockIdx.z * g.c_bstride;
@@ -413,7 +413,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g) {
         if (CT == 2) {
           f16x4 o;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = (f16)v[e];
+          for (int e = 0; e < 4; ++e) o[e] = to_f16_sat(v[e]);
           *(f16x4*)dst = o;
         } else {
           bf16x4 o;

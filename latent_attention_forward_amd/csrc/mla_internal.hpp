@@ -164,6 +164,30 @@ __device__ __forceinline__ f16x8 cat8(f16x4 a, f16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// fp32 -> fp16 with values beyond the fp16 range saturated to +-65504 (a
+// plain conversion would give +-inf); NaN stays NaN.
+__device__ __forceinline__ f16 to_f16_sat(float v) {
+  return (f16)(__builtin_fabsf(v) > 65504.f ? __builtin_copysignf(65504.f, v) : v);
+}
+
+// acc + sum of the 8 values of v, accumulated in fp32 (two-element dot
+// products with (1, 1)): the sum of exactly the rounded values an MFMA takes
+// as its operand.
+__device__ __forceinline__ float sum8(f16x8 v, float acc) {
+  const f16x2 one = {(f16)1.f, (f16)1.f};
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
+  return __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
+}
+__device__ __forceinline__ float sum8(bf16x8 v, float acc) {
+  const bf16x2 one = {(bf16)1.f, (bf16)1.f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
+}
+
 // Calls f(std::integral_constant<int, i>) for i = B .. E - 1, so that the index
 // is a constant expression in the body whatever the loop unroller decides.
 template <int B, int E, typename F> __device__ __forceinline__ void static_for(F&& f) {

@@ -37,7 +37,7 @@ def test_header_symbols_exported(lib):
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(mla.exported_symbols())
-    assert lib.mla_abi_version() == 2
+    assert lib.mla_abi_version() == 3
 
 
 def test_config_validation(lib):
@@ -47,13 +47,14 @@ def test_config_validation(lib):
         dict(qk_rope_dim=63), dict(num_heads=0), dict(dtype=7), dict(rope_kind=9),
         dict(yarn_beta_fast=0.5), dict(rope_theta=0.0), dict(output_gate=3), dict(kv_lora_rank=-1),
         dict(rope_interleave=2), dict(o_groups=-1), dict(o_groups=8, o_lora_rank=0), dict(o_groups=3, o_lora_rank=64),
+        dict(attn_operand=2), dict(attn_operand=-1), dict(dtype=mla.MLA_F32, attn_operand=mla.MLA_ATTN_BF16),
     ]
     for kw in bad:
         c = mla.make_config(mi.WORKLOADS["dsv3_prefill_4096"], **kw)
         assert lib.mla_validate_config(ctypes.byref(c)) == mla.MLA_ERR_INVALID_ARG, kw
         assert lib.mla_last_error().decode()
     assert lib.mla_validate_config(None) == mla.MLA_ERR_INVALID_ARG
-    for kw in (dict(rope_interleave=1), dict(o_groups=8, o_lora_rank=1024)):
+    for kw in (dict(rope_interleave=1), dict(o_groups=8, o_lora_rank=1024), dict(attn_operand=mla.MLA_ATTN_BF16)):
         c = mla.make_config(mi.WORKLOADS["dsv3_prefill_4096"], **kw)
         assert lib.mla_validate_config(ctypes.byref(c)) == mla.MLA_OK, kw
     # the ctypes mirror of the config has the C layout: its size includes the appended variant fields
@@ -67,6 +68,8 @@ def test_softmax_scale_matches_oracle(lib):
         assert got == np.float32(om.softmax_scale(sh)), name
     c = mla.make_config(mi.WORKLOADS["megatron_2x2048"], softmax_scale=0.5)
     assert mla.softmax_scale(c) == 0.5
+    # the DeepSeek-V3 YaRN value (1 + 0.1 ln 40)^2 / sqrt(192), rounded to float32
+    assert mla.softmax_scale(mla.make_config(mi.WORKLOADS["dsv3_prefill_4096"])) == np.float32(0.1352337788608801)
 
 
 @pytest.mark.parametrize("name", ["tiny_fp32_t64", "megatron_2x2048", "dsv3_prefill_4096"])
@@ -162,3 +165,22 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         mla._ptr(torch.zeros(4, 4), rows=True)
     assert mla._ptr(None) is None
+
+
+@pytest.mark.parametrize("lens", [[1], [5, 300], [1024, 8192, 4000, 17], [30600] * 68, [8192] * 300,
+                                  list(range(1, 200, 7))])
+def test_decode_plan_matches_workspace_size(lib, lens):
+    """The library's decode workspace equals what the split plan (restated in
+    tests/decode_plan.py) needs, and every segment the plan makes is a
+    non-empty-or-cut key range of its sequence that covers it exactly once."""
+    import decode_plan as dp
+    cfg = mla.make_config(mi.WORKLOADS["dsv3_decode_64"])
+    assert mla.decode_workspace_size(cfg, lens) == dp.workspace_bytes(lens, 128, 512)
+    quota, groups, segs = dp.plan(lens)
+    assert quota % 32 == 0 and quota <= dp.MAX_QUOTA
+    for L, s in zip(lens, segs):
+        cover = [k for k0, k1, _ in s for k in range(k0, k1)]
+        assert cover == list(range(L))
+        assert [slot for _, _, slot in s] == list(range(len(s)))
+        # a segment spans at most the blocks of 16 tokens one workgroup stages
+        assert all(k1 - k0 <= (dp.MAX_CHUNK_BLOCKS - 1) * 16 for k0, k1, _ in s)

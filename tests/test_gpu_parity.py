@@ -1,12 +1,15 @@
 """GPU parity of libmla against the float64 CPU oracle (through the C ABI).
 
 Tolerances
-  bf16 outputs: every element within 2e-2 * RMS(oracle row) + 2^-7 * |oracle|,
+  bf16 outputs: every element within 2e-2 * RMS(oracle row) + 2^-8 * |oracle|,
       i.e. the stated 2e-2 max-abs bound relative to the output RMS, on top of
-      one bfloat16 ulp of the element itself (``bf16_excess_error`` <= 2e-2).
-      The strict max-abs / row-RMS figure (``row_rel_error``) is printed next
-      to it: for these workloads the exact answer rounded to bf16 already
-      reaches 1.9e-2 on it, so it cannot be the bound on a bf16 output.
+      the half ulp by which a correctly rounded bfloat16 result may differ
+      from the exact one (``bf16_excess_error`` <= 2e-2; the exact answer
+      rounded to bf16 scores 0).  The strict max-abs / row-RMS figure
+      (``row_rel_error``) is printed next to it with the format floor (the
+      exact answer rounded to bf16, same metric): for these workloads the
+      floor alone reaches 1.9e-2, so the strict figure cannot be the bound on
+      a bf16 output; the gap between the two is what the pipeline adds.
   fp32 outputs: max |error| / row RMS <= 1e-4.
   integer and placement work (paged slots, untouched poisoned slots): bit-exact.
 """
@@ -25,13 +28,16 @@ BF16_TOL = 2e-2
 F32_TOL = 1e-4
 
 
-def bf16_check(ref, got, label=""):
-    """Assert the bf16 bound and print the strict figure and the format floor."""
+def bf16_check(ref, got, label="", tol=BF16_TOL):
+    """Assert the bf16 bound and print the strict figure and the format floor.
+    Returns (excess, strict, floor)."""
     ex = om.bf16_excess_error(ref, got)
     strict = om.row_rel_error(ref, got)
     floor = om.row_rel_error(ref, mi.bf16_round(np.asarray(ref, np.float32)))
-    _say(f"  {label}: excess over 1 ulp {ex:.3e} | strict max-abs/row-RMS {strict:.3e} (bf16 floor {floor:.3e})")
-    assert ex <= BF16_TOL, (label, ex)
+    _say(f"  {label}: excess over half an ulp {ex:.3e} | strict max-abs/row-RMS {strict:.3e} "
+         f"(bf16 floor {floor:.3e}, gap {strict - floor:.3e})")
+    assert ex <= tol, (label, ex)
+    return ex, strict, floor
 
 
 def _say(msg):
@@ -59,9 +65,13 @@ def tdtype(shape):
     return torch.bfloat16 if shape.dtype == "bf16" else torch.float32
 
 
-def run_prefill(mla, sh, case, latent=False, positions=None):
+def run_prefill(mla, sh, case, latent=False, positions=None, operand=None):
+    """The prefill layer through the C ABI; ``operand`` "bf16" selects bf16
+    attention operands (default: fp16)."""
     dt = tdtype(sh)
     cfg = mla.make_config(sh)
+    if operand == "bf16":
+        cfg.attn_operand = mla.MLA_ATTN_BF16
     W = {k: dev(v, dt) for k, v in case.w.items()}
     x = dev(case.x, dt)
     n = case.x.shape[0]
@@ -388,21 +398,41 @@ FULL = ["megatron_2x2048", "dsv3_prefill_4096", "kimi_gated_varlen_8192"]
 
 
 @pytest.mark.parametrize("name", FULL)
-def test_prefill_full_size_sampled_rows(mla, name):
+def test_prefill_full_size_sampled_rows(mla, name, operand="f16"):
+    """Full-size layer: every document's first and last rows plus 256 seeded
+    random rows against the oracle, every latent row, all rows finite."""
     sh = mi.WORKLOADS[name]
-    _say(f"case: full-size prefill {name}")
+    _say(f"case: full-size prefill {name}, {operand} attention operands")
     case = mi.make_prefill_case(sh)
-    got, lat = run_prefill(mla, sh, case, latent=True)
+    got, lat = run_prefill(mla, sh, case, latent=True, operand=operand)
     cu = case.cu_seqlens
     rng = np.random.default_rng(0)
     rows = sorted(set([0, int(cu[-1]) - 1] + [int(c) for c in cu[:-1]] + [int(c) - 1 for c in cu[1:]] +
-                      list(rng.integers(0, int(cu[-1]), 24))))
+                      [int(r) for r in rng.choice(int(cu[-1]), 256, replace=False)]))
     ref = om.mla_prefill_rows(sh, case.w, case.x, cu, rows)
     _say(f"  sampled rows: {len(rows)}")
     bf16_check(ref["out"], got[rows], "out (sampled rows)")
     bf16_check(ref["latent"], lat, "latent (all rows)")
     assert np.all(np.isfinite(got))
 
+
+@pytest.mark.parametrize("name", ["megatron_2x2048", "dsv3_prefill_4096"])
+def test_prefill_full_size_bf16_operands(mla, name):
+    """The layer with bf16 attention operands at full size.  Its error is
+    printed; at 16 heads it is within the bound, at the DeepSeek-V3 shape
+    (128 heads, 4096 tokens) it is not (about 2.5e-2), which is why fp16
+    operands are the default.  Asserted: the 16-head bound, and finite
+    output with an error below 4e-2 at 128 heads."""
+    sh = mi.WORKLOADS[name]
+    _say(f"case: full-size prefill {name}, bf16 attention operands")
+    case = mi.make_prefill_case(sh)
+    got, _ = run_prefill(mla, sh, case, operand="bf16")
+    cu = case.cu_seqlens
+    rng = np.random.default_rng(0)
+    rows = sorted(set([0, int(cu[-1]) - 1] + [int(r) for r in rng.choice(int(cu[-1]), 256, replace=False)]))
+    ref = om.mla_prefill_rows(sh, case.w, case.x, cu, rows)
+    bf16_check(ref["out"], got[rows], "out (sampled rows)", tol=BF16_TOL if sh.num_heads <= 16 else 4e-2)
+    assert np.all(np.isfinite(got))
 
 
 def test_decode_quota_clamp_over_two_million_keys(mla):
@@ -422,11 +452,153 @@ def test_decode_quota_clamp_over_two_million_keys(mla):
 
 
 def test_decode_full_size(mla):
+    """All 64 sequences of the DeepSeek-V3 decode workload against the
+    absorbed oracle; the strict error is printed beside the format floor."""
     sh = mi.WORKLOADS["dsv3_decode_64"]
     _say("case: full-size decode, 64 sequences")
     dc = mi.make_decode_case(sh)
     got = run_decode(mla, sh, dc)
-    idx = [0, 1, 17, 33, 63] + [int(np.argmax(dc.seq_lens)), int(np.argmin(dc.seq_lens))]
-    ra = om.decode_absorbed(sh, dc.w_kv_b, dc.q_nope, dc.q_pe, dc.cache, dc.block_table, dc.seq_lens, 64, batch_idx=idx)
-    bf16_check(ra.reshape(len(idx), -1), got[idx].reshape(len(idx), -1), "out")
+    B = len(dc.seq_lens)
+    ra = om.decode_absorbed(sh, dc.w_kv_b, dc.q_nope, dc.q_pe, dc.cache, dc.block_table, dc.seq_lens, 64)
+    bf16_check(ra.reshape(B, -1), got.reshape(B, -1), "out (all 64 sequences)")
     assert np.all(np.isfinite(got))
+
+
+# ----------------------------------------------------------------------------- branches of the softmax
+@pytest.mark.parametrize("operand", ["bf16", "f16"])
+def test_attention_scores_rising_along_keys_move_the_origin(mla, operand):
+    """Queries and keys aligned with one direction, keys growing along the
+    sequence: late queries meet scores 20-40 log2 units above their first key
+    tile's maximum, so the flash kernel rejects tiles against its exponent
+    origin, moves the origin and rescales its accumulators (a branch that
+    random inputs never reach).  Compared element by element with the oracle."""
+    _say(f"case: attention with rising scores, {operand} operands")
+    sh = mi.WORKLOADS["dsv3_prefill_4096"].replace(num_heads=2)
+    H, lens = 2, [700, 300]
+    n = sum(lens)
+    rng = np.random.default_rng(13)
+    u = rng.standard_normal(192)
+    u /= np.linalg.norm(u)
+    pos = np.concatenate([np.arange(l) for l in lens]).astype(np.float64)
+    rnd = (lambda a: mi.bf16_round(a.astype(np.float32))) if operand == "bf16" else \
+        (lambda a: np.asarray(a, np.float16).astype(np.float32))
+    q = rnd(20.0 * u[None, None, :] + 0.5 * rng.standard_normal((n, H, 192)))
+    kn = (pos / 64.0)[:, None, None] * u[None, None, :128] + 0.5 * rng.standard_normal((n, H, 128))
+    kv = rnd(np.concatenate([kn, rng.standard_normal((n, H, 128))], -1))
+    kpe = rnd((pos / 64.0)[:, None] * u[None, 128:] + 0.5 * rng.standard_normal((n, 64)))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    k = np.concatenate([kv[..., :128], np.broadcast_to(kpe[:, None, :], (n, H, 64))], -1)
+    scale = om.softmax_scale(sh)
+    # the inputs reach the branch: some query's best key lies more than 20
+    # log2 units above the best key of its first 64-key tile
+    s = np.einsum("qhd,khd->hqk", q[:700].astype(np.float64), k[:700].astype(np.float64)) * scale / np.log(2)
+    s = np.where(np.tril(np.ones((700, 700), bool))[None], s, -np.inf)
+    excursion = np.max(s, -1) - np.max(s[..., :64], -1)
+    _say(f"  largest excursion over the first tile: {excursion.max():.1f} log2 units")
+    assert excursion.max() > 20
+    td = torch.float16 if operand == "f16" else torch.bfloat16
+    attn = torch.full((n, H, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
+    mla.attention_prefill(mla.make_config(sh), dev(q, td), dev(kv, td), dev(kpe, td),
+                          torch.from_numpy(cu).to(DEV), cu, attn)
+    torch.cuda.synchronize()
+    ref = om.causal_varlen_attention(q, k, kv[..., 128:], scale, cu)
+    bf16_check(ref.reshape(n * H, 128), attn.float().cpu().numpy().reshape(n * H, 128), "attn")
+
+
+def test_decode_dominant_late_key_takes_the_exact_path(mla):
+    """A cached key whose shared rope part is 8 times the query's rope part of
+    head 5 scores more than 64 log2 units above the first tile of its segment
+    for that head: the split kernel discards that wave's fixed-origin result
+    and recomputes its 32 heads with a per-key online softmax.  The keys are
+    planted inside segments (not in their first tile) by the split plan; all
+    64 sequences are compared with the absorbed and the naive oracle."""
+    import decode_plan as dp
+    sh = mi.WORKLOADS["dsv3_decode_64"]
+    lens = [2000 + 37 * b for b in range(64)]
+    _say("case: decode with dominant late keys (exact fallback)")
+    dc = mi.make_decode_case(sh, seq_lens=lens, block_size=64)
+    quota, _, segs = dp.plan(lens)
+    h0, planted = 5, []
+    for b in (3, 17, 40):
+        k0, k1, _ = segs[b][1]                      # a segment in the middle of the sequence
+        j = k0 + (k1 - k0) // 2
+        assert j - k0 >= dp.TILE                    # not in the segment's first tile
+        blk, off = dc.block_table[b, j // 64], j % 64
+        dc.cache[blk, off, 512:] = mi.bf16_round(8.0 * dc.q_pe[b, h0])
+        planted.append((b, j))
+    c2 = om.softmax_scale(sh) / np.log(2)
+    for b, j in planted:                            # the planted score is far above the segment's first tile
+        rows = om.gather_paged(dc.cache, dc.block_table, b, int(dc.seq_lens[b]), 64).astype(np.float64)
+        W = dc.w_kv_b.astype(np.float64).reshape(128, 256, 512)[h0, :128]
+        qt = dc.q_nope[b, h0].astype(np.float64) @ W
+        sc = (rows[:, :512] @ qt + rows[:, 512:] @ dc.q_pe[b, h0].astype(np.float64)) * c2
+        k0 = [s for s in segs[b] if s[0] <= j < s[1]][0][0]
+        _say(f"  sequence {b}: key {j} is {sc[j] - sc[k0:k0 + dp.TILE].max():.0f} log2 units above its segment's first tile")
+        assert sc[j] - sc[k0:k0 + dp.TILE].max() > 64
+    B = len(lens)
+    cfg = mla.make_config(sh)
+    args = (dev(dc.w_kv_b, torch.bfloat16), dev(dc.q_nope, torch.bfloat16), dev(dc.q_pe, torch.bfloat16),
+            dev(dc.cache, torch.bfloat16), torch.from_numpy(dc.block_table).to(DEV),
+            torch.from_numpy(dc.seq_lens).to(DEV), dc.seq_lens)
+    out = torch.full((B, sh.num_heads, sh.v_head_dim), float("nan"), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(mla.decode_workspace_size(cfg, dc.seq_lens), dtype=torch.uint8, device=DEV)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    mla.decode_absorbed_fwd(cfg, *args, out, workspace=ws)
+    e0.record()
+    mla.decode_absorbed_fwd(cfg, *args, out, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    _say(f"  call with the exact fallback in 3 waves: {e0.elapsed_time(e1) * 1e3:.0f} us")
+    got = out.float().cpu().numpy()
+    ra = om.decode_absorbed(sh, dc.w_kv_b, dc.q_nope, dc.q_pe, dc.cache, dc.block_table, dc.seq_lens, 64)
+    bf16_check(ra.reshape(B, -1), got.reshape(B, -1), "all sequences vs absorbed oracle")
+    idx = [b for b, _ in planted]
+    rn = om.decode_naive(sh, dc.w_kv_b, dc.q_nope, dc.q_pe, dc.cache, dc.block_table, dc.seq_lens, 64, batch_idx=idx)
+    bf16_check(rn.reshape(len(idx), -1), got[idx].reshape(len(idx), -1), "planted sequences vs naive oracle")
+
+
+# ----------------------------------------------------------------------------- operand range
+def test_prefill_values_beyond_fp16_range(mla):
+    """V rows of W_kv_b scaled by 2^17 make v reach about 2e5, beyond fp16's
+    65504.  With bf16 attention operands the layer matches the oracle; with
+    fp16 operands (the default) v saturates to +-65504 as documented and the
+    output stays finite."""
+    sh, lens = SMALL["v3_yarn"]
+    _say("case: prefill with v beyond the fp16 range")
+    case = mi.make_prefill_case(sh, doc_lengths=lens)
+    w = case.w["w_kv_b"].reshape(sh.num_heads, 256, -1).copy()
+    w[:, 128:] *= 2.0 ** 17
+    case.w["w_kv_b"] = w.reshape(sh.num_heads * 256, -1)
+    ref = om.mla_prefill(sh, case.w, case.x, case.cu_seqlens)
+    kv = (ref["latent"][:, :512] @ case.w["w_kv_b"].astype(np.float64).T).reshape(-1, sh.num_heads, 256)
+    _say(f"  largest |v|: {np.abs(kv[..., 128:]).max():.3g}")
+    assert np.abs(kv[..., 128:]).max() > 65504
+    got, _ = run_prefill(mla, sh, case, operand="bf16")
+    bf16_check(ref["out"], got, "out, bf16 operands")
+    got16, _ = run_prefill(mla, sh, case)
+    assert np.all(np.isfinite(got16))
+
+
+def test_latent_norm_rope_unaligned_layout(mla):
+    """Column splits that are not multiples of 8 elements (norm over 36
+    columns, a 64-wide rope slice at column 36, 4 copied columns after it,
+    row strides of 100 and 104) take the element-wise kernel: same results."""
+    _say("case: latent_norm_rope with an unaligned layout")
+    sh = mi.WORKLOADS["dsv3_prefill_4096"]
+    cfg = mla.make_config(sh)
+    rng = np.random.default_rng(8)
+    n, w = 29, 104
+    src = mi.bf16_round(rng.standard_normal((n, w)).astype(np.float32) * 2)
+    gamma = mi.bf16_round(1 + 0.1 * rng.standard_normal(36).astype(np.float32))
+    pos = rng.integers(0, 4096, n).astype(np.int32)
+    cos, sin = mla.rope_table(cfg, 4096, DEV)
+    dst = torch.full((n, w), float("nan"), dtype=torch.bfloat16, device=DEV)
+    mla.latent_norm_rope(cfg, dev(src, torch.bfloat16), n, 104, 36, dev(gamma, torch.bfloat16), dst,
+                         rope_offset=36, rope_slices=1, rope_slice_stride=64, rope_cos=cos, rope_sin=sin,
+                         positions=torch.from_numpy(pos).to(DEV))
+    torch.cuda.synchronize()
+    got = dst.float().cpu().numpy()
+    oc, osn = om.rope_cos_sin(pos, 64, sh.rope)
+    ref = np.concatenate([om.rms_norm(src[:, :36], gamma, sh.norm_eps), om.apply_rope(src[:, 36:100], oc, osn),
+                          src[:, 100:]], 1)
+    assert np.all(np.abs(got - ref) <= _bf16_ulp(ref) + 1e-30)
