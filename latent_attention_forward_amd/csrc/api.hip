@@ -218,8 +218,10 @@ DecodePlan decode_plan(const mla_config* c, const int32_t* lens, int batch, int6
   const int64_t H = c->num_heads, R = c->kv_lora_rank;
   size_t off = 0;
   p.qt = off; off += align256((size_t)batch * H * R * 2);
-  p.part_o = off; off += align256((size_t)batch * p.max_slots * H * R * 2);
-  p.part_ml = off; off += align256((size_t)batch * p.max_slots * H * 2 * 4);
+  // one partial entry per (workgroup, sequence) segment, at index g + b
+  const size_t parts = (size_t)p.groups + (size_t)batch;
+  p.part_o = off; off += align256(parts * H * R * 2);
+  p.part_ml = off; off += align256(parts * H * 2 * 4);
   p.total = off;
   return p;
 }
@@ -693,11 +695,11 @@ static mla_status prefill_core(const mla_config* cfg, const mla_weights* w, cons
   return MLA_OK;
 }
 
-mla_status mla_decode_absorbed_fwd(const mla_config* cfg, const void* w_kv_b, const void* q_nope, const void* q_pe,
-                                   const void* kv_cache, int32_t num_blocks, int32_t block_size,
-                                   const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens_dev,
-                                   const int32_t* seq_lens_host, int32_t batch, void* out, void* workspace,
-                                   size_t workspace_bytes, void* stream) {
+// Argument checks and split plan of the absorbed decode (host only).
+static mla_status decode_check(const mla_config* cfg, const void* w_kv_b, const void* q_nope, const void* q_pe,
+                               const void* kv_cache, int32_t num_blocks, int32_t block_size,
+                               const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens_dev,
+                               const int32_t* seq_lens_host, int32_t batch, void* out, DecodePlan* plan) {
   mla_status s = check_config(cfg);
   if (s != MLA_OK) return s;
   if (cfg->dtype != MLA_BF16) return fail(MLA_ERR_UNSUPPORTED, "absorbed decode is compiled for bf16 only");
@@ -716,15 +718,20 @@ mla_status mla_decode_absorbed_fwd(const mla_config* cfg, const void* w_kv_b, co
   for (int b = 0; b < batch; ++b)
     if (seq_lens_host[b] <= 0 || (int64_t)seq_lens_host[b] > (int64_t)max_blocks * block_size)
       return fail(MLA_ERR_INVALID_ARG, "seq_lens[%d] = %d outside [1, max_blocks * block_size]", b, seq_lens_host[b]);
-  const void* ptrs[] = {w_kv_b, q_nope, q_pe, kv_cache, out, workspace};
+  const void* ptrs[] = {w_kv_b, q_nope, q_pe, kv_cache, out};
   for (const void* p : ptrs)
-    if (p && !aligned16(p)) return fail(MLA_ERR_MISALIGNED, "decode needs 16-byte aligned tensors");
-  const DecodePlan P = decode_plan(cfg, seq_lens_host, batch, (int64_t)max_blocks * block_size);
-  if (!workspace || workspace_bytes < P.total)
-    return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", P.total, workspace_bytes);
-  const hipStream_t st = (hipStream_t)stream;
-  char* ws = (char*)workspace;
-  const int dn = cfg->qk_nope_dim, dv = cfg->v_head_dim, R = cfg->kv_lora_rank;
+    if (!aligned16(p)) return fail(MLA_ERR_MISALIGNED, "decode needs 16-byte aligned tensors");
+  *plan = decode_plan(cfg, seq_lens_host, batch, (int64_t)max_blocks * block_size);
+  return MLA_OK;
+}
+
+// Launch sequence of the absorbed decode over a checked plan; ws holds at
+// least P.total bytes (a caller workspace or the static scratch).
+static mla_status decode_launch(const mla_config* cfg, const DecodePlan& P, const void* w_kv_b, const void* q_nope,
+                                const void* q_pe, const void* kv_cache, int32_t num_blocks, int32_t block_size,
+                                const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens_dev,
+                                int32_t batch, void* out, char* ws, hipStream_t st) {
+  const int H = cfg->num_heads, dn = cfg->qk_nope_dim, dv = cfg->v_head_dim, R = cfg->kv_lora_rank;
   bf16* qt = (bf16*)(ws + P.qt);
   hipError_t e;
   DecodeArgs d{};
@@ -743,7 +750,24 @@ mla_status mla_decode_absorbed_fwd(const mla_config* cfg, const void* w_kv_b, co
   d.w_uv = (const bf16*)w_kv_b + (int64_t)dn * R; d.w_uv_hstride = (int64_t)(dn + dv) * R;
   d.out = (bf16*)out; d.dv = dv;
   if ((e = launch_decode_combine_unabsorb(d, st)) != hipSuccess) return hip_fail(e, "decode combine");
-  return ok();
+  return MLA_OK;
+}
+
+mla_status mla_decode_absorbed_fwd(const mla_config* cfg, const void* w_kv_b, const void* q_nope, const void* q_pe,
+                                   const void* kv_cache, int32_t num_blocks, int32_t block_size,
+                                   const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens_dev,
+                                   const int32_t* seq_lens_host, int32_t batch, void* out, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  DecodePlan P;
+  mla_status s = decode_check(cfg, w_kv_b, q_nope, q_pe, kv_cache, num_blocks, block_size, block_table, max_blocks,
+                              seq_lens_dev, seq_lens_host, batch, out, &P);
+  if (s != MLA_OK) return s;
+  if (workspace && !aligned16(workspace)) return fail(MLA_ERR_MISALIGNED, "decode needs a 16-byte aligned workspace");
+  if (!workspace || workspace_bytes < P.total)
+    return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", P.total, workspace_bytes);
+  s = decode_launch(cfg, P, w_kv_b, q_nope, q_pe, kv_cache, num_blocks, block_size, block_table, max_blocks,
+                    seq_lens_dev, batch, out, (char*)workspace, (hipStream_t)stream);
+  return s == MLA_OK ? ok() : s;
 }
 
 }  // extern "C"

@@ -11,8 +11,8 @@
 // inside a sequence is moved to the nearest multiple of 32 keys of that
 // sequence (both workgroups sharing it round it the same way), so every
 // workgroup gets R +- 32 keys of work whatever the length mix.  Segment (g, b)
-// writes its partial result to slot g - floor(r_b / R) of sequence b, r_b the
-// position of b's first key.
+// is slot g - floor(r_b / R) of sequence b (r_b the position of b's first
+// key) and writes its partial result to entry g + b of the partial buffers.
 //
 // Split kernel: for every head at once, the partial softmax state of a
 // segment's keys.  Each wave owns 32 heads (v_mfma_f32_32x32x16_bf16, one wave
@@ -58,11 +58,10 @@ __device__ __forceinline__ int csw(int r) { return (((r >> 1) & 1) << 2) | ((r >
 // fp32 online softmax over keys [k0, k1) of sequence b for heads [h0, h0 + 32),
 // one wave, reading the cache from global memory; writes the partials.  Used
 // only by a wave whose scores left the range of its fixed exponent origin.
-__device__ __forceinline__ void decode_chunk_exact(const DecodeArgs& a, int b, int slot, int h0, int k0, int k1) {
+__device__ __forceinline__ void decode_chunk_exact(const DecodeArgs& a, int b, int64_t part, int h0, int k0, int k1) {
   const int lane = threadIdx.x & 63;
   const int H = a.heads, lbs = a.log2_block, bmask = (1 << lbs) - 1;
   const float c2 = a.scale * kLog2e;
-  const int64_t part = ((int64_t)b * a.max_slots + slot) * H;
   for (int h = h0; h < h0 + 32; ++h) {
     const bf16* qt = a.qt + ((int64_t)b * H + h) * RK;
     const bf16* qp = a.q_pe + ((int64_t)b * H + h) * DRP;
@@ -165,12 +164,9 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
     return x <= 0 ? 0 : (x >= L ? L : (int)min<int64_t>(L, ((x + 16) >> 5) << 5));
   };
   const int k0 = cut(S0 - r0), k1 = cut(S1 - r0);
-  const int64_t slot64 = item - r0 / R;
-  // the host planned max_slots from its copy of the lengths; a device length
-  // that disagrees with it must not move a store outside the partial buffers
-  if (slot64 < 0 || slot64 >= a.max_slots) continue;
-  const int slot = (int)slot64;
-  const int64_t part = ((int64_t)b * a.max_slots + slot) * H;
+  // entry item + b of the partial buffers (num_items + batch entries, item <
+  // num_items and b < batch by the loops): in bounds whatever the lengths
+  const int64_t part = ((int64_t)item + b) * H;
   if (k0 >= k1) {                          // empty after the cut: weight 0 in the combine
     for (int i = tid; i < H; i += NTH) { a.part_ml[(part + i) * 2] = -INFINITY; a.part_ml[(part + i) * 2 + 1] = 0.f; }
     continue;
@@ -433,7 +429,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
   }
 
   if (exact_path) {
-    decode_chunk_exact(a, b, slot, wave * 32, k0, k1);
+    decode_chunk_exact(a, b, part, wave * 32, k0, k1);
   } else {
     // Lane holds head my_h, dims d*32 + q*8 + hsel*4 + [0,4).  O / l goes in
     // fp16 through this wave's 32 KB of the (now idle) tile buffers, as 32 rows
@@ -574,6 +570,7 @@ __global__ __launch_bounds__(CNW * 64, 1) void decode_combine_unabsorb_kernel(De
   // 16 rows one MFMA operand read touches spread over the banks
   __shared__ __attribute__((aligned(16))) bf16 sO[2][CB * RK];
   __shared__ int s_ns[CB];
+  __shared__ int s_base[CB];
   __shared__ long long s_red[CNW];
   const int h = blockIdx.x, b0 = blockIdx.y * CB;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -603,8 +600,14 @@ __global__ __launch_bounds__(CNW * 64, 1) void decode_combine_unabsorb_kernel(De
       if (lane >= o) incl += v;
     }
     const long long r0 = base + incl - n + kDecodeSegmentCost;   // work-order position of key 0
-    // slot count, bounded by the slots the host planned (see the split kernel)
-    if (lane < CB) s_ns[lane] = Lb > 0 ? (int)min<long long>((r0 + Lb - 1) / R - r0 / R + 1, a.max_slots) : 0;
+    // slot count and first partial entry (r0 / R + b, see the split kernel),
+    // the count bounded so that every entry read lies in the buffers
+    if (lane < CB) {
+      const long long base = r0 / R + b;
+      const long long ns = Lb > 0 ? (r0 + Lb - 1) / R - r0 / R + 1 : 0;
+      s_base[lane] = (int)min<long long>(base, (long long)a.num_items + B);
+      s_ns[lane] = (int)max<long long>(0, min<long long>(ns, (long long)a.num_items + B - base));
+    }
   }
   __syncthreads();
 
@@ -622,7 +625,7 @@ __global__ __launch_bounds__(CNW * 64, 1) void decode_combine_unabsorb_kernel(De
     for (int u = 0; u < 2; ++u) {
       const int j = wave * 4 + j2 * 2 + u, b = b0 + j;
       nslot[u] = s_ns[j];                                // 0 past the batch
-      part0[u] = (int64_t)b * a.max_slots * H + h;       // slot s at part0 + s * H
+      part0[u] = (int64_t)s_base[j] * H + h;             // slot s at part0 + s * H
 #pragma unroll
       for (int sl = 0; sl < CMAXS; ++sl) {
         if (sl < nslot[u]) {

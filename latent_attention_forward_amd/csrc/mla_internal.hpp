@@ -284,15 +284,18 @@ struct DecodeArgs {
   const bf16* cache;      // [num_blocks, block_size, 576]
   const int32_t* block_table; int max_blocks; int num_blocks; int log2_block;
   const int32_t* seq_lens;
-  f16* part_o;            // [B, max_slots, H, 512] partial outputs, normalised (O / l)
-  float* part_ml;         // [B, max_slots, H, 2] exponent origin and sum (sum 0: empty slot)
+  // Partial results, one entry per (workgroup g, sequence b) segment at index
+  // g + b (injective: the workgroups that touch sequence b + 1 start at or
+  // after the last one that touches b), so [num_items + B] entries:
+  f16* part_o;            // [num_items + B, H, 512] partial outputs, normalised (O / l)
+  float* part_ml;         // [num_items + B, H, 2] exponent origin and sum (sum 0: empty slot)
   const bf16* w_uv;       // W_UV of head h: rows [dv] of 512 at w_uv + h * w_uv_hstride
   int64_t w_uv_hstride;
   bf16* out;              // [B, H, dv]
   int dv;
   int batch; int heads;
   int quota;              // keys per workgroup of the concatenated key sequence (multiple of 32)
-  int max_slots;          // partial slots per sequence
+  int max_slots;          // most segments of one sequence (host plan)
   int num_items;          // workgroups of the split kernel
   float scale;
 };

@@ -56,9 +56,25 @@ def max_slots(lens):
 
 
 def workspace_bytes(lens, heads, kv_lora_rank):
-    """Workspace the plan needs: the absorbed query [B, H, r_kv] bf16, the
-    partial outputs [B, slots, H, r_kv] fp16 and their (max, sum) pairs
-    [B, slots, H, 2] fp32, each region rounded up to 256 bytes."""
+    """Workspace the plan needs: the absorbed query [B, H, r_kv] bf16, then
+    one partial entry per (workgroup g, sequence b) segment at index g + b
+    (so groups + B entries): outputs [., H, r_kv] fp16 and (max, sum) pairs
+    [., H, 2] fp32, each region rounded up to 256 bytes."""
     a = lambda x: (x + 255) // 256 * 256
-    B, S = len(lens), max_slots(lens)
-    return a(B * heads * kv_lora_rank * 2) + a(B * S * heads * kv_lora_rank * 2) + a(B * S * heads * 2 * 4)
+    _, groups, _ = plan(lens)
+    B, P = len(lens), groups + len(lens)
+    return a(B * heads * kv_lora_rank * 2) + a(P * heads * kv_lora_rank * 2) + a(P * heads * 2 * 4)
+
+
+def entries(lens):
+    """Partial-buffer entry of every segment: (b, slot) -> g + b.  Distinct
+    for distinct segments, all below groups + B."""
+    quota, groups, segs = plan(lens)
+    out = {}
+    st = 0
+    for b, L in enumerate(lens):
+        r0 = st + SEGMENT_COST
+        for _, _, slot in segs[b]:
+            out[(b, slot)] = r0 // quota + slot + b
+        st = r0 + L
+    return out, groups + len(lens)

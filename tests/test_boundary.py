@@ -184,3 +184,5 @@ def test_decode_plan_matches_workspace_size(lib, lens):
         assert [slot for _, _, slot in s] == list(range(len(s)))
         # a segment spans at most the blocks of 16 tokens one workgroup stages
         assert all(k1 - k0 <= (dp.MAX_CHUNK_BLOCKS - 1) * 16 for k0, k1, _ in s)
+    ent, n_ent = dp.entries(lens)
+    assert len(set(ent.values())) == len(ent) and max(ent.values()) < n_ent
