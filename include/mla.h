@@ -341,6 +341,27 @@ mla_status mla_decode_absorbed_fwd(const mla_config* cfg, const void* w_kv_b,
                                    int32_t batch, void* out,
                                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* mla_decode_absorbed_fwd without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments, kernels and
+ * results as mla_decode_absorbed_fwd; its scratch (absorbed query, partial
+ * results) lives in a static device array of 64 MiB that every GPU the
+ * library runs on holds for the life of the process.  The call allocates
+ * nothing: its first call on a device only looks the array's address up.
+ * A batch whose plan needs more scratch than that (mla_decode_workspace_size
+ * > 64 MiB) returns MLA_ERR_WORKSPACE before anything is enqueued.  All calls
+ * on one GPU share the array: calls that overlap in time on one GPU (on
+ * different streams, or from different threads without ordering) race and
+ * give undefined results; calls ordered on one stream do not.  Nothing in the
+ * array needs clearing between calls: each call writes every part it
+ * reads. */
+mla_status mla_decode_absorbed_fwd_noalloc(const mla_config* cfg, const void* w_kv_b,
+                                           const void* q_nope, const void* q_pe,
+                                           const void* kv_cache, int32_t num_blocks, int32_t block_size,
+                                           const int32_t* block_table, int32_t max_blocks,
+                                           const int32_t* seq_lens_dev, const int32_t* seq_lens_host,
+                                           int32_t batch, void* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -67,6 +67,7 @@ _SIGNATURES = {
     "mla_prefill_fwd": (_I32, [_CFG, ctypes.POINTER(MlaWeights), _P, _P, _P, _I32, _P, _P, _P, _I32, _P, _P,
                                _P, _SZ, _P]),
     "mla_decode_absorbed_fwd": (_I32, [_CFG, _P, _P, _P, _P, _I32, _I32, _P, _I32, _P, _P, _I32, _P, _P, _SZ, _P]),
+    "mla_decode_absorbed_fwd_noalloc": (_I32, [_CFG, _P, _P, _P, _P, _I32, _I32, _P, _I32, _P, _P, _I32, _P, _P]),
     "mla_prefill_chunk_workspace_size": (_SZ, [_CFG, _P, _P, _I32]),
     "mla_attention_prefix": (_I32, [_CFG, _I32, _P, _P, _P, _I64, _P, _P, _P, _P, _I32, _P, _P]),
     "mla_prefill_chunk_fwd": (_I32, [_CFG, ctypes.POINTER(MlaWeights), _P, _P, _P, _I32, _P, _P, _P, _I32, _I32, _P,
@@ -360,6 +361,25 @@ def decode_absorbed_fwd(cfg: MlaConfig, w_kv_b, q_nope, q_pe, kv_cache, block_ta
                                        len(lens), _ptr(out, dtype=act, name="out"), _ptr(ws), ws.numel(),
                                        st.cuda_stream), "mla_decode_absorbed_fwd")
     return ws
+
+
+def decode_absorbed_fwd_noalloc(cfg: MlaConfig, w_kv_b, q_nope, q_pe, kv_cache, block_table, seq_lens_dev,
+                                seq_lens_host: Sequence[int], out, stream=None):
+    """``decode_absorbed_fwd`` with the library's static scratch instead of a
+    workspace: allocates nothing (see ``mla_decode_absorbed_fwd_noalloc``)."""
+    import numpy as np
+    lib = load_library()
+    act, i32 = _act(cfg), _i32()
+    lens = np.ascontiguousarray(np.asarray(seq_lens_host, dtype=np.int32))
+    num_blocks, block_size = kv_cache.shape[0], kv_cache.shape[1]
+    _check(lib.mla_decode_absorbed_fwd_noalloc(ctypes.byref(cfg), _ptr(w_kv_b, dtype=act, name="w_kv_b"),
+                                               _ptr(q_nope, dtype=act, name="q_nope"),
+                                               _ptr(q_pe, dtype=act, name="q_pe"),
+                                               _ptr(kv_cache, dtype=act, name="kv_cache"), num_blocks, block_size,
+                                               _ptr(block_table, dtype=i32, name="block_table"), block_table.shape[1],
+                                               _ptr(seq_lens_dev, dtype=i32, name="seq_lens_dev"), lens.ctypes.data,
+                                               len(lens), _ptr(out, dtype=act, name="out"), _stream(stream)),
+           "mla_decode_absorbed_fwd_noalloc")
 
 
 def prefill_chunk_workspace_size(cfg: MlaConfig, cu_seqlens_host: Sequence[int], prefix_lens_host: Sequence[int]) -> int:

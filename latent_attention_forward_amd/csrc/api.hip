@@ -9,6 +9,7 @@
 #include <string>
 #include <vector>
 #include <algorithm>
+#include <mutex>
 
 using namespace mla;
 
@@ -224,6 +225,51 @@ DecodePlan decode_plan(const mla_config* c, const int32_t* lens, int batch, int6
   p.part_ml = off; off += align256(parts * H * 2 * 4);
   p.total = off;
   return p;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- static scratch
+// Device memory of mla_decode_absorbed_fwd_noalloc, for callers that cannot
+// allocate.  Each GPU the library runs on holds its own copy of the array for
+// the life of the process.  In host code the array's name stands for the
+// host-side shadow, not a device address: the device address is obtained once
+// per device with hipGetSymbolAddress (with that device current) and only that
+// address is passed to kernels.
+static constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+static constexpr int kMaxDevices = 64;
+
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the scratch array on the device `stream` belongs to (the
+// current device for the null stream).
+mla_status static_scratch(hipStream_t stream, char** out) {
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "device of the stream");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MLA_ERR_UNSUPPORTED, "device %d beyond the %d the scratch table holds", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return hip_fail(e, "current device");
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e, "select the stream's device");
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess && e2 != hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return hip_fail(e, "address of the static scratch");
+    if (!p) return fail(MLA_ERR_HIP, "address of the static scratch is NULL");
+    g_scratch_ptr[dev] = (char*)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MLA_OK;
 }
 
 }  // namespace
@@ -767,6 +813,25 @@ mla_status mla_decode_absorbed_fwd(const mla_config* cfg, const void* w_kv_b, co
     return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", P.total, workspace_bytes);
   s = decode_launch(cfg, P, w_kv_b, q_nope, q_pe, kv_cache, num_blocks, block_size, block_table, max_blocks,
                     seq_lens_dev, batch, out, (char*)workspace, (hipStream_t)stream);
+  return s == MLA_OK ? ok() : s;
+}
+
+mla_status mla_decode_absorbed_fwd_noalloc(const mla_config* cfg, const void* w_kv_b, const void* q_nope,
+                                           const void* q_pe, const void* kv_cache, int32_t num_blocks,
+                                           int32_t block_size, const int32_t* block_table, int32_t max_blocks,
+                                           const int32_t* seq_lens_dev, const int32_t* seq_lens_host,
+                                           int32_t batch, void* out, void* stream) {
+  DecodePlan P;
+  mla_status s = decode_check(cfg, w_kv_b, q_nope, q_pe, kv_cache, num_blocks, block_size, block_table, max_blocks,
+                              seq_lens_dev, seq_lens_host, batch, out, &P);
+  if (s != MLA_OK) return s;
+  if (P.total > kStaticScratchBytes)
+    return fail(MLA_ERR_WORKSPACE, "this batch needs %zu bytes of scratch; the static scratch holds %zu "
+                "(use mla_decode_absorbed_fwd with a workspace)", P.total, kStaticScratchBytes);
+  char* ws = nullptr;
+  if ((s = static_scratch((hipStream_t)stream, &ws)) != MLA_OK) return s;
+  s = decode_launch(cfg, P, w_kv_b, q_nope, q_pe, kv_cache, num_blocks, block_size, block_table, max_blocks,
+                    seq_lens_dev, batch, out, ws, (hipStream_t)stream);
   return s == MLA_OK ? ok() : s;
 }
 

@@ -146,6 +146,16 @@ def test_device_calls_reject_bad_arguments_before_launch(lib):
     f32 = mla.make_config(mi.WORKLOADS["tiny_fp32_t64"])
     st = g(ctypes.byref(f32), 4096, 4096, 4096, 4096, 10, 64, 4096, 4, 4096, lens.ctypes.data, 2, 4096, 4096, 1 << 30, None)
     assert st == mla.MLA_ERR_UNSUPPORTED
+    # decode without a workspace: a batch whose plan needs more than the 64 MiB
+    # static scratch is refused before anything runs
+    big = np.full(300, 8192, np.int32)
+    assert mla.decode_workspace_size(dcfg, big) > 64 << 20
+    st = lib.mla_decode_absorbed_fwd_noalloc(ctypes.byref(dcfg), 4096, 4096, 4096, 4096, 10, 64, 4096, 128, 4096,
+                                             big.ctypes.data, 300, 4096, None)
+    assert st == mla.MLA_ERR_WORKSPACE and b"static scratch" in lib.mla_last_error()
+    st = lib.mla_decode_absorbed_fwd_noalloc(ctypes.byref(dcfg), 4096, 4096, 4096, 4096, 10, 60, 4096, 4, 4096,
+                                             lens.ctypes.data, 2, 4096, None)
+    assert st == mla.MLA_ERR_INVALID_ARG       # the same argument checks as with a workspace
     # norm/rope: rope slices overlapping the norm region, slot mapping in place
     st = lib.mla_latent_norm_rope(ctypes.byref(cfg), 4096, 576, 4, 576, 512, 4096, 500, 1, 64, 4096, 4096, 16, 4096,
                                   8192, 576, None, 0, None)
