@@ -9,9 +9,18 @@ Metric: "MLA prefill attn TFLOP/s + absorbed decode HBM GB/s, % of MI355X
 peak".  ``value`` is the mean of the two fractions of peak, in percent:
   prefill attention: algorithmic FLOPs 2 (d_qk + d_v) H sum_d T_d (T_d + 1) / 2
       per launch / the attention kernel's mean launch time, against the dense
-      bf16/fp16 MFMA peak (2516.6 TFLOP/s);
+      bf16/fp16 MFMA peak (2516.6 TFLOP/s), on the DeepSeek-V3 workload with
+      the layer's own (fp16) operand type;
   absorbed decode: algorithmic bytes sum_b L_b (r_kv + d_rope) 2 + W_kv_b + q +
       out + index arrays per call / the mean call time, against 8 TB/s.
+Beside it: the attention kernel on the other two graded prefill workloads
+(Megatron-shaped 2 x 2048, Kimi-shaped gated 8192 tokens in 4 documents),
+with bf16 operands on the DeepSeek-V3 workload, the fused latent
+norm + RoPE kernel's GB/s, and the chunked prefill over a cached prefix.
+
+The attention operands are the workloads' own: q, kv and the shared k_pe are
+computed from each workload's seeded x and weights with the library's
+projection and norm/RoPE calls, then held in the operand type timed.
 Kernel times are HIP events on the stream the kernels run on.  Between timed
 decode calls a 512 MiB buffer is read, so the 256 MB Infinity Cache holds none
 of the ~370 MB decode working set (a read leaves clean lines; overwriting the
@@ -39,6 +48,8 @@ COPY_BYTES = 256 << 20
 KERNEL_SOURCES = {"flash": ["flash.hip", "mla_internal.hpp"],
                   "decode": ["decode.hip", "api.hip", "mla_internal.hpp"],
                   "chunk": ["flash.hip", "mla_internal.hpp"]}
+# the graded prefill workloads whose attention kernel is timed
+ATTN_WORKLOADS = ["megatron_2x2048", "dsv3_prefill_4096", "kimi_gated_varlen_8192"]
 
 
 def parse():
@@ -51,9 +62,13 @@ def parse():
     ap.add_argument("--chunk", default="dsv3_chunk_4x1024_p4096",
                     help="chunked-prefill workload reported beside the metric ('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["full", "prefill", "attention", "decode", "copy", "chunk", "chunk_attention"],
-                    default="full",
+    ap.add_argument("--mode", choices=["full", "prefill", "attention", "decode", "copy", "chunk", "chunk_attention",
+                                       "norm"], default="full",
                     help="full: the JSON line; the others only run that part's timing loop (for profilers)")
+    ap.add_argument("--attn-workload", default="dsv3_prefill_4096", choices=ATTN_WORKLOADS,
+                    help="workload of --mode attention")
+    ap.add_argument("--operand", default="f16", choices=["f16", "bf16"],
+                    help="attention operand type of --mode attention / prefill")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for the CPU baseline")
     return ap.parse_args()
 
@@ -119,48 +134,78 @@ def traffic_for(name):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(shape_name, dshape_name, budget):
-    """Time the float64 oracle on the host in a child process (its BLAS threads
-    are whatever the environment gives it; the count actually used is
-    reported)."""
-    code = r'''
-import json, sys, time, os
-sys.path.insert(0, %r)
+CPU_CODE = r'''
+import json, sys, time, os, platform, io, contextlib
+sys.path.insert(0, %(root)r)
 import numpy as np
 from threadpoolctl import threadpool_info
 import mla_inputs as mi
 from oracle import mla as om
-budget = %f
-sh = mi.WORKLOADS[%r]
-H = sh.num_heads
+heads_sample = %(heads)d
+
+def best_of(fn, runs=3):
+    fn()                                   # warm-up
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter(); fn(); ts.append(time.perf_counter() - t0)
+    return min(ts)
+
+# prefill attention: the 4096-token document of the DeepSeek-V3 workload at
+# its head shape, on a sample of its 128 heads (the work per head is the same)
+sh = mi.WORKLOADS[%(prefill)r]
+T = sh.total_tokens
 rng = np.random.default_rng(0)
+q = rng.standard_normal((T, heads_sample, sh.qk_head_dim))
+k = rng.standard_normal((T, heads_sample, sh.qk_head_dim))
+v = rng.standard_normal((T, heads_sample, sh.v_head_dim))
 scale = om.softmax_scale(sh)
-# prefill attention: one causal document of T tokens, all heads, grown until the budget is used
-T, tp, fp = 128, 0.0, 0
-while True:
-    q = rng.standard_normal((T, H, 192)); k = rng.standard_normal((T, H, 192)); v = rng.standard_normal((T, H, 128))
-    t0 = time.perf_counter(); om.causal_varlen_attention(q, k, v, scale, [0, T]); dt = time.perf_counter() - t0
-    tp, fp, Tp = dt, 640 * H * T * (T + 1) // 2, T
-    if dt > budget / 6 or T >= 4096:
-        break
-    T *= 2
-# absorbed decode: the first sequences of the decode workload until the budget is used
-dsh = mi.WORKLOADS[%r]
+tp = best_of(lambda: om.causal_varlen_attention(q, k, v, scale, [0, T]))
+fp = 2 * (sh.qk_head_dim + sh.v_head_dim) * heads_sample * T * (T + 1) // 2
+# absorbed decode over all 64 sequences; the non-absorbed form on 8 of them
+dsh = mi.WORKLOADS[%(decode)r]
 dc = mi.make_decode_case(dsh)
-nb, bytes_, t_dec = 0, 0, 0.0
-t0 = time.perf_counter()
-while nb < len(dc.seq_lens) and time.perf_counter() - t0 < budget / 3:
-    om.decode_absorbed(dsh, dc.w_kv_b, dc.q_nope, dc.q_pe, dc.cache, dc.block_table, dc.seq_lens, dc.block_size, batch_idx=[nb])
-    nb += 1
-t_dec = time.perf_counter() - t0
-L = dc.seq_lens[:nb]
-bytes_ = int(L.sum()) * 1152 + dsh.num_heads * 256 * 512 * 2 * nb + nb * dsh.num_heads * (192 + 128) * 2
+args = (dsh, dc.w_kv_b, dc.q_nope, dc.q_pe, dc.cache, dc.block_table, dc.seq_lens, dc.block_size)
+td = best_of(lambda: om.decode_absorbed(*args))
+B = len(dc.seq_lens)
+H, r, dr, dn, dv = dsh.num_heads, dsh.kv_lora_rank, dsh.qk_rope_dim, dsh.qk_nope_dim, dsh.v_head_dim
+dbytes = (int(dc.seq_lens.sum()) * (r + dr) * 2 + H * (dn + dv) * r * 2 + B * H * (dn + dr) * 2 + B * H * dv * 2
+          + dc.block_table.size * 4 + B * 4)
+sub = list(range(8))
+t0 = time.perf_counter(); om.decode_naive(*args, batch_idx=sub); tn = time.perf_counter() - t0
+nbytes = (int(dc.seq_lens[sub].sum()) * (r + dr) * 2 + H * (dn + dv) * r * 2 + 8 * H * (dn + dr + dv) * 2)
 threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-print(json.dumps({"prefill_tflops": fp / tp / 1e12, "prefill_T": Tp, "prefill_s": tp, "heads": H,
-                  "decode_gbs": bytes_ / t_dec / 1e9, "decode_seqs": nb, "decode_s": t_dec, "threads": threads,
-                  "affinity": len(os.sched_getaffinity(0))}))
-''' % (ROOT, budget, shape_name, dshape_name)
-    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=600)
+cpu = platform.processor() or ""
+try:
+    for line in open("/proc/cpuinfo"):
+        if line.startswith("model name"):
+            cpu = line.split(":", 1)[1].strip(); break
+except OSError:
+    pass
+buf = io.StringIO()
+with contextlib.redirect_stdout(buf):
+    np.show_config()
+blas = " ".join(l.strip() for l in buf.getvalue().splitlines() if "name" in l.lower())[:300]
+print(json.dumps({"prefill_tflops": fp / tp / 1e12, "prefill_T": T, "prefill_heads": heads_sample, "prefill_s": tp,
+                  "decode_gbs": dbytes / td / 1e9, "decode_s": td, "decode_seqs": B,
+                  "naive_gbs": nbytes / tn / 1e9, "naive_s": tn, "naive_seqs": len(sub),
+                  "threads": threads, "affinity": len(os.sched_getaffinity(0)), "cpu": cpu, "blas": blas}))
+'''
+
+
+def cpu_baseline(prefill_name, decode_name, budget):
+    """Time the float64 oracle on the host in a child process whose BLAS /
+    OpenMP threads are set to the cores it may run on before NumPy loads:
+    best of 3 runs after a warm-up for the prefill attention (the 4096-token
+    DeepSeek-V3 document on a sample of its heads, sized so the whole leg
+    takes about ``budget`` seconds) and the absorbed decode of all 64
+    sequences; one run of the non-absorbed decode of 8 sequences."""
+    cores = len(os.sched_getaffinity(0))
+    env = dict(os.environ)
+    for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        env[v] = str(cores)
+    heads = 8 if budget >= 10 else 4
+    code = CPU_CODE % dict(root=ROOT, heads=heads, prefill=prefill_name, decode=decode_name)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=900, env=env)
     if r.returncode != 0:
         raise RuntimeError("cpu baseline failed: " + r.stderr[-2000:])
     d = json.loads(r.stdout.strip().splitlines()[-1])
@@ -168,11 +213,14 @@ print(json.dumps({"prefill_tflops": fp / tp / 1e12, "prefill_T": Tp, "prefill_s"
     return {
         "value": frac, "unit": "% of MI355X peak (same definition as value)", "cores": d["threads"],
         "kind": "oracle",
-        "sample": (f"float64 oracle: causal attention of one {d['prefill_T']}-token document x {d['heads']} heads "
-                   f"({d['prefill_s']:.1f} s, {d['prefill_tflops'] * 1e3:.2f} GFLOP/s); absorbed decode of the "
-                   f"first {d['decode_seqs']} sequences of {dshape_name} ({d['decode_s']:.1f} s, "
-                   f"{d['decode_gbs']:.3f} GB/s); host affinity {d['affinity']} cores"),
-        "prefill_attn_tflops": d["prefill_tflops"], "decode_gbs": d["decode_gbs"],
+        "sample": (f"float64 oracle on {d['cpu']} ({d['affinity']} cores in the affinity mask, {d['threads']} BLAS "
+                   f"threads): causal attention of the {d['prefill_T']}-token DeepSeek-V3 document on "
+                   f"{d['prefill_heads']} of its heads, best of 3 after a warm-up ({d['prefill_s']:.2f} s, "
+                   f"{d['prefill_tflops'] * 1e3:.2f} GFLOP/s); absorbed decode of all {d['decode_seqs']} sequences of "
+                   f"{decode_name}, best of 3 ({d['decode_s']:.2f} s, {d['decode_gbs']:.3f} GB/s); non-absorbed "
+                   f"decode of {d['naive_seqs']} sequences, one run ({d['naive_s']:.1f} s, {d['naive_gbs']:.3f} GB/s); "
+                   f"numpy BLAS: {d['blas']}"),
+        "prefill_attn_tflops": d["prefill_tflops"], "decode_gbs": d["decode_gbs"], "naive_decode_gbs": d["naive_gbs"],
     }
 
 
@@ -195,10 +243,79 @@ def main():
     stream = torch.cuda.current_stream()
     tb = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(torch.bfloat16)
 
-    # ------------------------------------------------------------------ prefill inputs
+    def timed(fn, k, warm=10):
+        """Mean time of one call of fn in ms: HIP events around each call on
+        the stream the library launches on, after `warm` untimed calls."""
+        for _ in range(warm):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(k)]
+        for i in range(k):
+            ev[i][0].record(stream)
+            fn()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in ev) / k
+
+    def attention_operands(name):
+        """q, kv and the shared k_pe of a prefill workload, computed from its
+        seeded x and weights with the library's projection and norm/RoPE calls
+        (bf16 intermediates), and a runner for the attention kernel on them."""
+        sh = mi.WORKLOADS[name]
+        case = mi.make_prefill_case(sh)
+        cfg = mla.make_config(sh)
+        n, H = case.x.shape[0], sh.num_heads
+        cuh = case.cu_seqlens
+        cu = torch.from_numpy(cuh).to(dev)
+        x = tb(case.x)
+        w = {k: tb(v) for k, v in case.w.items() if k in ("w_q_a", "q_a_gamma", "w_q_b", "w_q", "w_kv_a",
+                                                          "kv_a_gamma", "w_kv_b")}
+        del case
+        lw = sh.kv_lora_rank + sh.qk_rope_dim
+        rope = sh.rope.kind != "none"
+        pos = torch.from_numpy(np.concatenate([np.arange(b - a) for a, b in zip(cuh[:-1], cuh[1:])]).astype(np.int32)).to(dev)
+        cos = sin = None
+        if rope:
+            cos, sin = mla.rope_table(cfg, int(np.max(np.diff(cuh))), dev)
+        q = torch.empty(n, H * sh.qk_head_dim, dtype=torch.bfloat16, device=dev)
+        if sh.q_lora_rank:
+            ql = torch.empty(n, sh.q_lora_rank, dtype=torch.bfloat16, device=dev)
+            mla.linear(cfg, x, w["w_q_a"], ql)
+            mla.latent_norm_rope(cfg, ql, n, sh.q_lora_rank, sh.q_lora_rank, w["q_a_gamma"], ql)
+            mla.linear(cfg, ql, w["w_q_b"], q)
+            del ql
+        else:
+            mla.linear(cfg, x, w["w_q"], q)
+        if rope:
+            mla.latent_norm_rope(cfg, q, n, H * sh.qk_head_dim, 0, None, q, rope_offset=sh.qk_nope_dim,
+                                 rope_slices=H, rope_slice_stride=sh.qk_head_dim, rope_cos=cos, rope_sin=sin,
+                                 positions=pos)
+        ckv = torch.empty(n, lw, dtype=torch.bfloat16, device=dev)
+        mla.linear(cfg, x, w["w_kv_a"], ckv)
+        lat = torch.empty_like(ckv)
+        mla.latent_norm_rope(cfg, ckv, n, lw, sh.kv_lora_rank, w["kv_a_gamma"], lat, rope_offset=sh.kv_lora_rank,
+                             rope_slices=1 if rope else 0, rope_slice_stride=sh.qk_rope_dim, rope_cos=cos,
+                             rope_sin=sin, positions=pos)
+        kv = torch.empty(n, H * (sh.qk_nope_dim + sh.v_head_dim), dtype=torch.bfloat16, device=dev)
+        mla.linear(cfg, lat[:, :sh.kv_lora_rank], w["w_kv_b"], kv)
+        del x, w, ckv
+        kpe = lat[:, sh.kv_lora_rank:].contiguous()
+        del lat
+        torch.cuda.synchronize()
+        ops = {"bf16": (q.view(n, H, -1), kv.view(n, H, -1), kpe)}
+        ops["f16"] = tuple(t.to(torch.float16) for t in ops["bf16"])
+        attn = torch.empty(n, H, sh.v_head_dim, dtype=torch.bfloat16, device=dev)
+
+        def runner(operand):
+            qq, kk, pp = ops[operand]
+            return lambda: mla.attention_prefill(cfg, qq, kk, pp, cu, cuh, attn)
+        return {"shape": sh, "cu": cuh, "flops": attention_flops(sh, cuh), "run": runner, "ops": ops}
+
+    # ------------------------------------------------------------------ prefill layer inputs
     sh = mi.WORKLOADS[args.prefill]
     case = mi.make_prefill_case(sh)
     cfg = mla.make_config(sh)
+    if args.operand == "bf16":
+        cfg.attn_operand = mla.MLA_ATTN_BF16
     W = {k: tb(v) for k, v in case.w.items()}
     x = tb(case.x)
     n = case.x.shape[0]
@@ -227,9 +344,25 @@ def main():
     max_blocks = dc.block_table.shape[1]
     del dc
 
+    def prefill():
+        mla.prefill_fwd(cfg, W, x, cu, cuh, out, latent_out=lat, rope_cos=cos, rope_sin=sin, workspace=ws_p)
+
+    def decode():
+        mla.decode_absorbed_fwd(dcfg, w_kvb, q_nope, q_pe, cache, table, lens_d, lens_h, out_d, workspace=ws_d)
+
+    # the fused latent norm + RoPE (a5) on the layer's [N, r_kv + d_rope] rows
+    norm_src = torch.randn(n, sh.kv_lora_rank + sh.qk_rope_dim, device=dev).to(torch.bfloat16)
+    norm_dst = torch.empty_like(norm_src)
+    norm_pos = torch.from_numpy(np.concatenate([np.arange(b - a) for a, b in zip(cuh[:-1], cuh[1:])]).astype(np.int32)).to(dev)
+
+    def norm_rope():
+        mla.latent_norm_rope(cfg, norm_src, n, sh.kv_lora_rank + sh.qk_rope_dim, sh.kv_lora_rank, W["kv_a_gamma"],
+                             norm_dst, rope_offset=sh.kv_lora_rank, rope_slices=1 if cos is not None else 0,
+                             rope_slice_stride=sh.qk_rope_dim, rope_cos=cos, rope_sin=sin, positions=norm_pos)
+
     # ------------------------------------------------------------------ chunked prefill inputs
     chunk = None
-    if args.chunk != "none":
+    if args.chunk != "none" and args.mode in ("full", "chunk", "chunk_attention"):
         cname, cch, cpre = CHUNK_WORKLOADS[args.chunk]
         csh = mi.WORKLOADS[cname]
         cc = mi.make_chunk_case(csh, cch, cpre, block_size=64)
@@ -270,30 +403,20 @@ def main():
         ck = torch.from_numpy(ck_h).to(dev)
         return lambda: mla.attention_prefix(c["cfg"], qa, kva, kpe, c["cu"], c["cu_h"], ck, ck_h, attn)
 
-    def prefill():
-        mla.prefill_fwd(cfg, W, x, cu, cuh, out, latent_out=lat, rope_cos=cos, rope_sin=sin, workspace=ws_p)
-
-    def decode():
-        mla.decode_absorbed_fwd(dcfg, w_kvb, q_nope, q_pe, cache, table, lens_d, lens_h, out_d, workspace=ws_d)
-
     def step():
         prefill()
         decode()
 
     if args.mode != "full":
         # profiler runs: only the requested part, warmup + steps launches, no JSON line
-        H = sh.num_heads
         if args.mode == "attention":
-            g = torch.Generator(device=dev).manual_seed(0)
-            qa = torch.randn(n, H, sh.qk_head_dim, device=dev, generator=g).to(torch.float16)
-            kva = torch.randn(n, H, sh.qk_nope_dim + sh.v_head_dim, device=dev, generator=g).to(torch.float16)
-            kpe = torch.randn(n, sh.qk_rope_dim, device=dev, generator=g).to(torch.float16)
-            attn = torch.empty(n, H, sh.v_head_dim, dtype=torch.bfloat16, device=dev)
-            fn = lambda: mla.attention_prefill(cfg, qa, kva, kpe, cu, cuh, attn)
+            fn = attention_operands(args.attn_workload)["run"](args.operand)
         elif args.mode == "chunk_attention":
             fn = chunk_attention_operands()
         elif args.mode == "chunk":
             fn = chunk_layer
+        elif args.mode == "norm":
+            fn = norm_rope
         elif args.mode == "copy":
             # known-size device copy: calibrates the FETCH_SIZE / WRITE_SIZE counters
             src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
@@ -329,36 +452,37 @@ def main():
     t_wall = time.perf_counter() - t_wall
     ms_per_step = e0.elapsed_time(e1) / args.steps
     prefill_ms = sum(a.elapsed_time(b) for a, b in pe) / args.steps
+    print(f"steps done: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
 
-    # ------------------------------------------------------------------ attention kernel alone
-    # Same kernel and launch shape as inside the layer (fp16 operands), on
-    # operands of the layer's shapes.
-    H = sh.num_heads
-    g = torch.Generator(device=dev).manual_seed(0)
-    qa = torch.randn(n, H, sh.qk_head_dim, device=dev, generator=g).to(torch.float16)
-    kva = torch.randn(n, H, sh.qk_nope_dim + sh.v_head_dim, device=dev, generator=g).to(torch.float16)
-    kpe = torch.randn(n, sh.qk_rope_dim, device=dev, generator=g).to(torch.float16)
-    attn = torch.empty(n, H, sh.v_head_dim, dtype=torch.bfloat16, device=dev)
+    # ------------------------------------------------------------------ attention kernel alone, graded workloads
     # warm-up launches bring the GPU to the kernel's steady state after the
     # layer steps (power and clock state, caches)
-    for _ in range(max(20, args.warmup)):
-        mla.attention_prefill(cfg, qa, kva, kpe, cu, cuh, attn)
-    ae = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for i in range(args.steps):
-        ae[i][0].record(stream)
-        mla.attention_prefill(cfg, qa, kva, kpe, cu, cuh, attn)
-        ae[i][1].record(stream)
-    torch.cuda.synchronize()
-    attn_ms = sum(a.elapsed_time(b) for a, b in ae) / args.steps
-    del qa, kva, kpe, attn
+    attn_rec = {}
+    for name in ATTN_WORKLOADS:
+        ao = attention_operands(name)
+        for operand in (("f16", "bf16") if name == args.prefill else ("f16",)):
+            ms = timed(ao["run"](operand), args.steps, warm=max(20, args.warmup))
+            tf = ao["flops"] / (ms * 1e-3) / 1e12
+            attn_rec[f"{name}/{operand}"] = {"ms": round(ms, 4), "tflops": round(tf, 2),
+                                              "frac": round(tf / PEAK_MFMA_TFLOPS, 4), "flops": ao["flops"]}
+        del ao
+        torch.cuda.empty_cache()
+        print(f"attention {name} done", file=sys.stderr, flush=True)
+    head = attn_rec[f"{args.prefill}/f16"]
+    attn_ms, attn_tflops, a_flops = head["ms"], head["tflops"], head["flops"]
+
+    # ------------------------------------------------------------------ fused latent norm + RoPE (a5)
+    norm_ms = timed(norm_rope, 50, warm=20)
+    lw = sh.kv_lora_rank + sh.qk_rope_dim
+    norm_bytes = n * lw * 2 * 2 + n * 4 + n * sh.qk_rope_dim * 4 + sh.kv_lora_rank * 2   # rows in/out, positions, cos/sin rows, gain
+    norm_gbs = norm_bytes / (norm_ms * 1e-3) / 1e9
 
     # ------------------------------------------------------------------ decode call alone (cold Infinity Cache)
     flush = torch.zeros(512 << 20, dtype=torch.uint8, device=dev)
     sink = torch.zeros(1, dtype=torch.int64, device=dev)
     de = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     # decode in its own steady state: 20 warm-up calls, each after the flush as
-    # the timed ones (2 warm-up calls after the attention loop measured 139-149
-    # us against 134 us here)
+    # the timed ones
     for _ in range(20):
         sink.copy_(flush.view(torch.int64).sum())
         decode()
@@ -369,20 +493,11 @@ def main():
         de[i][1].record(stream)
     torch.cuda.synchronize()
     dec_ms = sum(a.elapsed_time(b) for a, b in de) / args.steps
+    del flush
 
     # ------------------------------------------------------------------ chunked prefill (reported beside the metric)
     chunk_rec = None
     if chunk is not None:
-        def timed(fn, k):
-            for _ in range(10):
-                fn()
-            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(k)]
-            for i in range(k):
-                ev[i][0].record(stream)
-                fn()
-                ev[i][1].record(stream)
-            torch.cuda.synchronize()
-            return sum(a.elapsed_time(b) for a, b in ev) / k
         c_layer_ms = timed(chunk_layer, args.steps)
         c_attn_ms = timed(chunk_attention_operands(), args.steps)
         csh = chunk["sh"]
@@ -403,24 +518,29 @@ def main():
         del chunk
 
     # ------------------------------------------------------------------ figures
-    a_flops = attention_flops(sh, cuh)
-    attn_tflops = a_flops / (attn_ms * 1e-3) / 1e12
     layer_tflops = layer_flops(sh, n, a_flops) / (prefill_ms * 1e-3) / 1e12
     d_bytes = decode_bytes(dsh, lens_h, max_blocks)
     dec_gbs = d_bytes / (dec_ms * 1e-3) / 1e9
     value = 0.5 * (attn_tflops / PEAK_MFMA_TFLOPS + dec_gbs / PEAK_HBM_GBS) * 100
 
     rec = {
-        "metric": METRIC, "value": round(value, 3), "unit": "% of MI355X peak (mean of prefill-attention MFMA and absorbed-decode HBM fractions)",
+        "metric": METRIC, "value": round(value, 3),
+        "unit": "% of MI355X peak (mean of prefill-attention MFMA and absorbed-decode HBM fractions)",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp16 MFMA (prefill attention operands) + bf16 MFMA (decode); fp32 accumulate and softmax; bf16 I/O",
         "data": "synthetic (seeded N(0,1) inputs, N(0,0.02) weights, bf16)",
         "config": {"workload": f"{args.prefill} + {args.decode}", "prefill_tokens": n, "prefill_docs": len(cuh) - 1,
-                   "heads": H, "hidden": sh.hidden, "q_lora_rank": sh.q_lora_rank, "kv_lora_rank": sh.kv_lora_rank,
-                   "decode_batch": B, "decode_keys": int(lens_h.sum()), "decode_block": 64},
+                   "heads": sh.num_heads, "hidden": sh.hidden, "q_lora_rank": sh.q_lora_rank,
+                   "kv_lora_rank": sh.kv_lora_rank, "decode_batch": B, "decode_keys": int(lens_h.sum()),
+                   "decode_block": 64, "prefill_attn_operand": args.operand},
         "prefill_attn_tflops": round(attn_tflops, 2), "prefill_attn_ms": round(attn_ms, 4),
         "prefill_layer_ms": round(prefill_ms, 4), "prefill_layer_tflops": round(layer_tflops, 2),
         "decode_ms": round(dec_ms, 4), "decode_hbm_gbs": round(dec_gbs, 1),
+        "attention_by_workload": attn_rec,
+        "latent_norm_rope": {"workload": f"{args.prefill} latent rows [{n}, {lw}] bf16, norm 512 + RoPE 64",
+                             "us": round(norm_ms * 1e3, 2), "gbs": round(norm_gbs, 1),
+                             "frac": round(norm_gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": norm_bytes},
         "wall_s_timed": round(t_wall, 3),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_MFMA_TFLOPS, 4), "traffic": traffic_for("flash"),
