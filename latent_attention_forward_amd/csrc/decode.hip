@@ -462,20 +462,24 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(DecodeArgs a) 
 
 // Query absorption: qt[b, h, :] = W_UK[h]^T q_nope[b, h, :] for every
 // sequence, with W_UK[h] the [128, 512] block of W_kv_b rows of head h.
-// Workgroup (128 latent columns c0.., head h): the [128 x 128] slab of W_UK[h]
-// is copied to LDS (16 B chunk c of row k at c ^ 2 (k & 3)) and read back
-// transposed as the A operand of 32x32x16 MFMAs, D^T[col, b] = W^T[col, :] .
-// q^T[:, b]; wave w takes columns c0 + 32 w .. + 31 for all sequences, 32 at a
-// time, with the q_nope rows read straight from HBM as the B operand.  Each
-// block of 32 sequences goes through LDS and leaves as whole 256 B row pieces.
-// The four column blocks of a head run on one XCD (workgroup i on XCD i % 8),
-// so the head's q_nope rows come from HBM once.
-constexpr int ADN = 128, ANC = 128;        // contraction (d_nope), columns per workgroup
-__global__ __launch_bounds__(256) void absorb_q_kernel(DecodeArgs a) {
+// Workgroup (256 latent columns c0.., head h), one per CU: the [128 x 256]
+// slab of W_UK[h] (64 KB) is copied to LDS (16 B chunk c of row k at
+// c ^ 2 (k & 3)) and read back transposed as the A operand of 32x32x16
+// MFMAs, D^T[col, b] = W^T[col, :] . q^T[:, b]; wave w takes columns c0 + 64 w
+// .. + 63 (two blocks of 32) for every sequence, 64 at a time (two blocks of
+// 32), with the q_nope rows read straight from memory as the B operand.  The
+// slab copy and the first 64 sequences' query loads are issued before
+// anything waits.  Each block of 64 sequences leaves through LDS as whole
+// 512 B row pieces.  The two column halves of a head run on one XCD
+// (workgroup i on XCD i % 8), so the head's q_nope rows come from HBM once.
+constexpr int ADN = 128, ANC = 256;        // contraction (d_nope), columns per workgroup
+constexpr int ASB = 64;                    // sequences per block
+__global__ __launch_bounds__(256, 1) void absorb_q_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 sW[ADN * ANC];
-  // output block [32 sequences][128 columns]: 16 B chunk c of row r at c ^ (r & 15)
-  __shared__ __attribute__((aligned(16))) bf16 sOut[32 * ANC];
+  // output block [64 sequences][256 columns]: 16 B chunk c of row r at c ^ (r & 31)
+  __shared__ __attribute__((aligned(16))) bf16 sOut[ASB * ANC];
   constexpr int NCB = RK / ANC;            // column blocks per head
+  constexpr int CPR = ANC / 8;             // 16 B chunks per slab row
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int c0 = (slot % NCB) * ANC, h = xcd + 8 * (slot / NCB);
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -484,66 +488,88 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(DecodeArgs a) {
     const bf16* src = a.w_uk + (int64_t)h * a.w_uv_hstride + c0;   // row k at + k * RK
     const uint32_t sb = lds_addr_of(&sW[0]);
 #pragma unroll
-    for (int i = 0; i < ADN * ANC / 8 / 256; ++i) {
-      const int P = i * 256 + tid, k = P >> 4, pc = P & 15;
+    for (int i = 0; i < ADN * CPR / 256; ++i) {
+      const int P = i * 256 + tid, k = P / CPR, pc = P % CPR;
       lds_dma16_m0(src + (int64_t)k * RK + ((pc ^ ((k & 3) << 1)) << 3), sb + (uint32_t)(i * 256 + wave * 64) * 16);
     }
   }
-  // B operand: lane holds sequence m0 + lane % 32, d_nope (lane / 32) * 8 + 16 ks + [0, 8)
+  // B operand of sequence block j: lane holds sequence m0 + 32 j + lane % 32,
+  // d_nope (lane / 32) * 8 + 16 ks + [0, 8)
   const int col = lane & 31, hsel = lane >> 5;
-  auto load_q = [&](bf16x8 (&qb)[ADN / 16], int m0) {
-    const int b = m0 + col;
-    const bf16* q = a.q_nope + ((int64_t)b * H + h) * ADN + hsel * 8;
+  auto load_q = [&](bf16x8 (&qb)[2][ADN / 16], int m0) {
 #pragma unroll
-    for (int ks = 0; ks < ADN / 16; ++ks) {
-      if (b < B) qb[ks] = *(const bf16x8*)(q + ks * 16);
-      else
+    for (int j = 0; j < 2; ++j) {
+      const int b = m0 + 32 * j + col;
+      const bf16* q = a.q_nope + ((int64_t)b * H + h) * ADN + hsel * 8;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qb[ks][e] = (bf16)0.f;
+      for (int ks = 0; ks < ADN / 16; ++ks) {
+        if (b < B) qb[j][ks] = *(const bf16x8*)(q + ks * 16);
+        else
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qb[j][ks][e] = (bf16)0.f;
+      }
     }
   };
-  bf16x8 qb[ADN / 16];
+  bf16x8 qb[2][ADN / 16];
   load_q(qb, 0);
-  vm_wait_all();                           // the slab copies, issued from inline asm
+  vm_wait_all();                           // the slab copies (inline asm) and the queries
   __syncthreads();
-  // A operand by transpose reads: lane group g = lane / 16 reads rows
-  // 16 ks + (g / 2) * 8 + [0, 8) of columns 32 w + (g % 2) * 16 + [0, 16)
+  // A operand of column block i by transpose reads: lane group g = lane / 16
+  // reads rows 16 ks + (g / 2) * 8 + [0, 8) of columns 64 w + 32 i + (g % 2) * 16 + [0, 16)
   const int g = lane >> 4, L = lane & 15;
-  const int n = wave * 32 + (g & 1) * 16 + 4 * (L & 3);
-  bf16x8 wa[ADN / 16];
+  bf16x8 wa[2][ADN / 16];
 #pragma unroll
-  for (int ks = 0; ks < ADN / 16; ++ks) {
-    bf16x4 v[2];
+  for (int i = 0; i < 2; ++i) {
+    const int n = wave * 64 + i * 32 + (g & 1) * 16 + 4 * (L & 3);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int k = ks * 16 + (g >> 1) * 8 + u * 4 + (L >> 2);
-      v[u] = lds_read_tr(&sW[k * ANC + ((((n >> 3) ^ ((k & 3) << 1))) << 3) + (n & 7)]);
+    for (int ks = 0; ks < ADN / 16; ++ks) {
+      bf16x4 v[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int k = ks * 16 + (g >> 1) * 8 + u * 4 + (L >> 2);
+        v[u] = lds_read_tr(&sW[k * ANC + ((((n >> 3) ^ ((k & 3) << 1))) << 3) + (n & 7)]);
+      }
+      wa[i][ks] = cat8(v[0], v[1]);
     }
-    wa[ks] = cat8(v[0], v[1]);
   }
-  for (int m0 = 0; m0 < B; m0 += 32) {
-    f32x16 acc;
+  for (int mb = 0; mb < B; mb += ASB) {
+    f32x16 acc[2][2];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int ks = 0; ks < ADN / 16; ++ks) acc = mfma32(wa[ks], qb[ks], acc);
-    if (m0 + 32 < B) load_q(qb, m0 + 32);
-    // lane holds sequence m0 + lane % 32, columns 32 w + (i / 4) * 8 + hsel * 4 + i % 4
-    if (m0 > 0) __syncthreads();           // the previous block has left sOut
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      bf16x4 v;
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = (bf16)acc[q * 4 + e];
-      *(bf16x4*)&sOut[col * ANC + (((wave * 4 + q) ^ (col & 15)) << 3) + hsel * 4] = v;
+    for (int ks = 0; ks < ADN / 16; ++ks)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(wa[i][ks], qb[j][ks], acc[i][j]);
+    if (mb + ASB < B) load_q(qb, mb + ASB);
+    // lane holds sequence mb + 32 j + lane % 32, columns 64 w + 32 i + (e / 4) * 8 + hsel * 4 + e % 4
+    if (mb > 0) __syncthreads();           // the previous block has left sOut
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = 32 * j + col;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          bf16x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (bf16)acc[i][j][q * 4 + e];
+          const int chunk = wave * 8 + i * 4 + q;
+          *(bf16x4*)&sOut[r * ANC + ((chunk ^ (r & 31)) << 3) + hsel * 4] = v;
+        }
     }
     __syncthreads();
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int r = (tid >> 4) + 16 * u, c = tid & 15, b = m0 + r;
+    for (int u = 0; u < ASB * CPR / 256; ++u) {
+      const int id = u * 256 + tid, rr = id / CPR, c = id % CPR, b = mb + rr;
       if (b < B)
         *(bf16x8*)((bf16*)a.qt + ((int64_t)b * H + h) * RK + c0 + c * 8) =
-            *(const bf16x8*)&sOut[r * ANC + ((c ^ (r & 15)) << 3)];
+            *(const bf16x8*)&sOut[rr * ANC + ((c ^ (rr & 31)) << 3)];
     }
   }
 }
@@ -554,8 +580,8 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(DecodeArgs a) {
 //     sequence's slots s, with w_s = 2^((m_s - M) * c2); slots emptied by a
 //     cut (l_s = 0) are skipped.  Stored into LDS as two bf16 parts, hi =
 //     bf16(o_lat) and lo = bf16(o_lat - hi), which carry o_lat to about 16
-//     significant bits; each wave takes 4 sequences, two at a time with all
-//     their slots loaded before any is used, 8 latent dims per lane.
+//     significant bits; each wave takes 4 sequences, with all their slots
+//     (up to CMAXS each) loaded before any is used, 8 latent dims per lane.
 //  2. out[b, h, :] = W_UV[h] . o_lat[b, h, :] for the 32 sequences at once:
 //     O^T[dv, b] = W_UV[h][dv, :] . (hi + lo)[b, :]^T on 16x16x32 MFMAs (two
 //     per step, one per part), each wave 16 output dims for both blocks of 16
@@ -616,81 +642,86 @@ __global__ __launch_bounds__(CNW * 64, 1) void decode_combine_unabsorb_kernel(De
   // k = 32 ks + (lane / 16) * 8 + [0, 8)
   const int r16 = lane & 15, kq = lane >> 4;
   bf16x8 wf[RK / 32];
-  for (int j2 = 0; j2 < 2; ++j2) {
-    float mv[2][CMAXS], lv[2][CMAXS];
-    f16x8 pv[2][CMAXS];
-    int nslot[2];
-    int64_t part0[2];
+  // all partials of the wave's 4 sequences, then its W_UV rows, are requested
+  // before any of them is used: one memory round trip.  The (origin, sum)
+  // pairs are loaded one per lane (lane 8 u + s: slot s of the wave's u-th
+  // sequence) and read back as wave-uniform values.
+  constexpr int SPW = CB / CNW;            // sequences per wave
+  static_assert(SPW * CMAXS <= 64, "one (origin, sum) pair per lane");
+  f16x8 pv[SPW][CMAXS];
+  int nslot[SPW];
+  int64_t part0[SPW];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int j = wave * 4 + j2 * 2 + u, b = b0 + j;
-      nslot[u] = s_ns[j];                                // 0 past the batch
-      part0[u] = (int64_t)s_base[j] * H + h;             // slot s at part0 + s * H
+  for (int u = 0; u < SPW; ++u) {
+    const int j = wave * SPW + u;
+    nslot[u] = s_ns[j];                                  // 0 past the batch
+    part0[u] = (int64_t)s_base[j] * H + h;               // slot s at part0 + s * H
 #pragma unroll
-      for (int sl = 0; sl < CMAXS; ++sl) {
-        if (sl < nslot[u]) {
-          const int64_t part = part0[u] + (int64_t)sl * H;
-          const float2 ml = *(const float2*)(a.part_ml + part * 2);
-          mv[u][sl] = ml.x;
-          lv[u][sl] = ml.y;
-          pv[u][sl] = *(const f16x8*)(a.part_o + part * RK + lane * 8);
-        } else {
-          mv[u][sl] = -INFINITY;
-          lv[u][sl] = 0.f;
-        }
-      }
+    for (int sl = 0; sl < CMAXS; ++sl)
+      if (sl < nslot[u]) pv[u][sl] = *(const f16x8*)(a.part_o + (part0[u] + (int64_t)sl * H) * RK + lane * 8);
+  }
+  float2 ml_lane = make_float2(-INFINITY, 0.f);
+  {
+    const int u = lane / CMAXS, sl = lane % CMAXS;
+    if (u < SPW && sl < s_ns[wave * SPW + u])
+      ml_lane = *(const float2*)(a.part_ml + ((int64_t)s_base[wave * SPW + u] * H + h + (int64_t)sl * H) * 2);
+  }
+  {
+    const bf16* wr = a.w_uv + (int64_t)h * a.w_uv_hstride + (int64_t)(16 * wave + r16) * RK + kq * 8;
+#pragma unroll
+    for (int ks = 0; ks < RK / 32; ++ks) wf[ks] = *(const bf16x8*)(wr + ks * 32);
+  }
+#pragma unroll
+  for (int u = 0; u < SPW; ++u) {
+    const int j = wave * SPW + u;
+    float mv[CMAXS], lv[CMAXS];
+#pragma unroll
+    for (int sl = 0; sl < CMAXS; ++sl) {
+      mv[sl] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ml_lane.x), u * CMAXS + sl));
+      lv[sl] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ml_lane.y), u * CMAXS + sl));
     }
-    if (j2 == 0) {                         // behind the first partials, ahead of the second
-      const bf16* wr = a.w_uv + (int64_t)h * a.w_uv_hstride + (int64_t)(16 * wave + r16) * RK + kq * 8;
+    float M = -INFINITY;
 #pragma unroll
-      for (int ks = 0; ks < RK / 32; ++ks) wf[ks] = *(const bf16x8*)(wr + ks * 32);
+    for (int sl = 0; sl < CMAXS; ++sl)
+      if (lv[sl] != 0.f) M = fmaxf(M, mv[sl]);
+    for (int sl = CMAXS; sl < nslot[u]; ++sl) {
+      const int64_t part = part0[u] + (int64_t)sl * H;
+      if (a.part_ml[part * 2 + 1] != 0.f) M = fmaxf(M, a.part_ml[part * 2]);
     }
+    float acc[8];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int j = wave * 4 + j2 * 2 + u;
-      float M = -INFINITY;
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    float lsum = 0.f;
 #pragma unroll
-      for (int sl = 0; sl < CMAXS; ++sl)
-        if (lv[u][sl] != 0.f) M = fmaxf(M, mv[u][sl]);
-      for (int sl = CMAXS; sl < nslot[u]; ++sl) {
-        const int64_t part = part0[u] + (int64_t)sl * H;
-        if (a.part_ml[part * 2 + 1] != 0.f) M = fmaxf(M, a.part_ml[part * 2]);
-      }
-      float acc[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-      float lsum = 0.f;
-#pragma unroll
-      for (int sl = 0; sl < CMAXS; ++sl) {
-        if (lv[u][sl] != 0.f) {
-          const float w = __builtin_amdgcn_exp2f((mv[u][sl] - M) * c2) * lv[u][sl];
-          lsum += w;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[e] += w * (float)pv[u][sl][e];
-        }
-      }
-      for (int sl = CMAXS; sl < nslot[u]; ++sl) {
-        const int64_t part = part0[u] + (int64_t)sl * H;
-        const float l = a.part_ml[part * 2 + 1];
-        if (l == 0.f) continue;
-        const float w = __builtin_amdgcn_exp2f((a.part_ml[part * 2] - M) * c2) * l;
+    for (int sl = 0; sl < CMAXS; ++sl) {
+      if (lv[sl] != 0.f) {
+        const float w = __builtin_amdgcn_exp2f((mv[sl] - M) * c2) * lv[sl];
         lsum += w;
-        const f16x8 v = *(const f16x8*)(a.part_o + part * RK + lane * 8);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += w * (float)v[e];
+        for (int e = 0; e < 8; ++e) acc[e] += w * (float)pv[u][sl][e];
       }
-      // sequences past the batch and empty ones leave a zero row
-      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-      bf16x8 rh, rl;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float v = acc[e] * inv;
-        rh[e] = (bf16)v;
-        rl[e] = (bf16)(v - (float)rh[e]);
-      }
-      *(bf16x8*)&sO[0][j * RK + ((lane ^ (j & 15)) << 3)] = rh;
-      *(bf16x8*)&sO[1][j * RK + ((lane ^ (j & 15)) << 3)] = rl;
     }
+    for (int sl = CMAXS; sl < nslot[u]; ++sl) {
+      const int64_t part = part0[u] + (int64_t)sl * H;
+      const float l = a.part_ml[part * 2 + 1];
+      if (l == 0.f) continue;
+      const float w = __builtin_amdgcn_exp2f((a.part_ml[part * 2] - M) * c2) * l;
+      lsum += w;
+      const f16x8 v = *(const f16x8*)(a.part_o + part * RK + lane * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += w * (float)v[e];
+    }
+    // sequences past the batch and empty ones leave a zero row
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    bf16x8 rh, rl;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = acc[e] * inv;
+      rh[e] = (bf16)v;
+      rl[e] = (bf16)(v - (float)rh[e]);
+    }
+    *(bf16x8*)&sO[0][j * RK + ((lane ^ (j & 15)) << 3)] = rh;
+    *(bf16x8*)&sO[1][j * RK + ((lane ^ (j & 15)) << 3)] = rl;
   }
   __syncthreads();
 
