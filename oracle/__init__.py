@@ -7,8 +7,8 @@ library (no kernels, headers, tables or helpers); the only module both sides use
 is ``mla_inputs``, which draws the seeded inputs and holds none of the method's
 arithmetic.
 
-Everything is float64 NumPy (``mla.py``) or pure-Python scalar loops
-(``brute.py``), written from the pages' statement of the layer:
+Everything is float64 NumPy (``mla.py``, ``fp8.py``) or pure-Python scalar
+loops (``brute.py``), written from the pages' statement of the layer:
 
 * "CSDN walkthrough of HF DeepseekV3Attention" (``__init__`` and ``forward``
   listing): projections, latent RMSNorm, split, RoPE on the 64-wide slice with a
@@ -25,6 +25,10 @@ Everything is float64 NumPy (``mla.py``) or pure-Python scalar loops
   prefill and mixed steps).
 * "Kimi-K3 atlas: Gated MLA" (mla-init, mla-forward, rmsnorm excerpts): the
   unrotated shared key part and the full-rank output gate.
+* The FP8 latent cache (``fp8.py``): the pages name FP8 / MXFP8 only as a
+  recipe ("Megatron-LM MLA guide", parameter section); the element format is
+  the published OCP 8-bit floating point E4M3 with the OCP Microscaling
+  conversion rule (round to nearest even, saturate at 448).
 
 Parity status of each function is listed in its docstring ("pinned by ...").
 The pages cite the YaRN paper for the attention factor (``yarn_get_mscale``)
@@ -41,4 +45,7 @@ from .mla import (  # noqa: F401
     kv_latent, gather_paged, decode_naive, decode_absorbed, prefill_latent_absorbed,
     row_rel_error, bf16_excess_error, prefix_causal_attention, mla_prefill_with_prefix,
     apply_rope_interleaved,
+)
+from .fp8 import (  # noqa: F401
+    e4m3_value, e4m3_encode, cache_inverse_scale, cache_quantize_fp8, cache_dequantize_fp8, decode_absorbed_fp8,
 )
