@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 3
+#define MLA_ABI_VERSION 4
 
 typedef enum mla_status {
   MLA_OK = 0,
@@ -180,6 +180,10 @@ size_t mla_prefill_chunk_workspace_size(const mla_config* cfg, const int32_t* cu
 /* Workspace (device bytes) needed by mla_decode_absorbed_fwd; seq_lens_host
  * is a HOST array of batch lengths. */
 size_t mla_decode_workspace_size(const mla_config* cfg, const int32_t* seq_lens_host, int32_t batch);
+
+/* Workspace (device bytes) needed by mla_decode_absorbed_fp8_fwd (its split
+ * works on tiles of 64 keys; the plan differs from the bf16 decode's). */
+size_t mla_decode_fp8_workspace_size(const mla_config* cfg, const int32_t* seq_lens_host, int32_t batch);
 
 const char* mla_status_string(mla_status s);
 /* Message for the last failed call on this thread ("" if none). */
@@ -361,6 +365,51 @@ mla_status mla_decode_absorbed_fwd_noalloc(const mla_config* cfg, const void* w_
                                            const int32_t* block_table, int32_t max_blocks,
                                            const int32_t* seq_lens_dev, const int32_t* seq_lens_host,
                                            int32_t batch, void* out, void* stream);
+
+/* ---------------------------------------------------- FP8 (E4M3) latent cache
+ * The pages name FP8 only as the MXFP8 recipe of "Megatron-LM MLA guide"
+ * (parameter section: use_fused_mla_q_uproj, fp8_dot_product_attention) and
+ * give no cache format.  The format here: each latent-cache row [c_n | k_pe']
+ * stored as r_kv + d_rope codes of the OCP 8-bit floating point E4M3 type
+ * (sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals, largest
+ * finite 448, S.1111.111 = NaN), with ONE float32 scale for the whole cache:
+ * value = code * scale.  Half the bytes of the bf16 cache. */
+
+/* Converts bf16 latent-cache rows to E4M3 codes:
+ *   dst[r, c] = E4M3(fl32(src[r, c] * fl32(1 / scale)))
+ * rounding to nearest, ties to even, magnitudes above 448 saturated to 448
+ * (the OCP Microscaling conversion rule); a NaN gives a NaN code.
+ *   src  DEVICE bf16 [n_rows, src_row_stride] (elements), 16-byte aligned
+ *   dst  DEVICE uint8 [n_rows, dst_row_stride] (bytes), 8-byte aligned
+ *   row_width, src_row_stride, dst_row_stride: multiples of 8
+ *   (MLA_ERR_MISALIGNED otherwise), strides >= row_width.
+ *   scale: positive and finite (MLA_ERR_INVALID_ARG otherwise).
+ * Quantising a paged cache [num_blocks, block_size, 576] is one call with
+ * n_rows = num_blocks * block_size and row_width = 576.  The layout is the
+ * caller's: rows are converted where they are, slot for slot. */
+mla_status mla_cache_quantize_fp8(const void* src, int64_t src_row_stride, int64_t n_rows, int32_t row_width,
+                                  float scale, void* dst, int64_t dst_row_stride, void* stream);
+
+/* mla_decode_absorbed_fwd over an E4M3 latent cache (same arguments, bf16
+ * queries, weights and output; "Megatron-LM MLA guide", inference section, as
+ * for the bf16 decode).  The result approximates the absorbed decode over the
+ * dequantised cache (code * cache_scale): inside, the absorbed query and the
+ * probabilities are rounded to MXFP8 (blocks of 32 values sharing a
+ * power-of-two scale, E4M3 elements) and both contractions run on fp8 MFMAs
+ * with fp32 accumulation.
+ *   kv_cache_fp8 [num_blocks, block_size, r_kv + d_rope] uint8 codes (as
+ *            mla_cache_quantize_fp8 writes them), 16-byte aligned
+ *   cache_scale: the cache's scale, positive and finite
+ *   workspace: DEVICE, >= mla_decode_fp8_workspace_size(cfg, seq_lens_host, B).
+ * Other arguments, errors and guarantees as for mla_decode_absorbed_fwd. */
+mla_status mla_decode_absorbed_fp8_fwd(const mla_config* cfg, const void* w_kv_b,
+                                       const void* q_nope, const void* q_pe,
+                                       const void* kv_cache_fp8, float cache_scale,
+                                       int32_t num_blocks, int32_t block_size,
+                                       const int32_t* block_table, int32_t max_blocks,
+                                       const int32_t* seq_lens_dev, const int32_t* seq_lens_host,
+                                       int32_t batch, void* out,
+                                       void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -69,6 +69,10 @@ _SIGNATURES = {
     "mla_decode_absorbed_fwd": (_I32, [_CFG, _P, _P, _P, _P, _I32, _I32, _P, _I32, _P, _P, _I32, _P, _P, _SZ, _P]),
     "mla_decode_absorbed_fwd_noalloc": (_I32, [_CFG, _P, _P, _P, _P, _I32, _I32, _P, _I32, _P, _P, _I32, _P, _P]),
     "mla_prefill_chunk_workspace_size": (_SZ, [_CFG, _P, _P, _I32]),
+    "mla_decode_fp8_workspace_size": (_SZ, [_CFG, _P, _I32]),
+    "mla_cache_quantize_fp8": (_I32, [_P, _I64, _I64, _I32, ctypes.c_float, _P, _I64, _P]),
+    "mla_decode_absorbed_fp8_fwd": (_I32, [_CFG, _P, _P, _P, _P, ctypes.c_float, _I32, _I32, _P, _I32, _P, _P, _I32,
+                                           _P, _P, _SZ, _P]),
     "mla_attention_prefix": (_I32, [_CFG, _I32, _P, _P, _P, _I64, _P, _P, _P, _P, _I32, _P, _P]),
     "mla_prefill_chunk_fwd": (_I32, [_CFG, ctypes.POINTER(MlaWeights), _P, _P, _P, _I32, _P, _P, _P, _I32, _I32, _P,
                                      _I32, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
@@ -380,6 +384,51 @@ def decode_absorbed_fwd_noalloc(cfg: MlaConfig, w_kv_b, q_nope, q_pe, kv_cache, 
                                                _ptr(seq_lens_dev, dtype=i32, name="seq_lens_dev"), lens.ctypes.data,
                                                len(lens), _ptr(out, dtype=act, name="out"), _stream(stream)),
            "mla_decode_absorbed_fwd_noalloc")
+
+
+def decode_fp8_workspace_size(cfg: MlaConfig, seq_lens_host) -> int:
+    import numpy as np
+    lens = np.ascontiguousarray(np.asarray(seq_lens_host, dtype=np.int32))
+    return int(load_library().mla_decode_fp8_workspace_size(ctypes.byref(cfg), lens.ctypes.data, len(lens)))
+
+
+def cache_quantize_fp8(src, scale: float, dst, stream=None):
+    """E4M3 codes of the bf16 rows of ``src`` ([..., width], row-strided
+    along the first dimensions as one contiguous block of rows) into ``dst``
+    (uint8, same shape); see ``mla_cache_quantize_fp8``."""
+    import torch
+    if src.shape != dst.shape:
+        raise ValueError("src and dst must have the same shape")
+    width = src.shape[-1]
+    rows = src.numel() // width if width else 0
+    _check(load_library().mla_cache_quantize_fp8(_ptr(src, dtype=torch.bfloat16, name="src"), width, rows, width,
+                                                 float(scale), _ptr(dst, dtype=torch.uint8, name="dst"), width,
+                                                 _stream(stream)), "mla_cache_quantize_fp8")
+
+
+def decode_absorbed_fp8_fwd(cfg: MlaConfig, w_kv_b, q_nope, q_pe, kv_cache_fp8, cache_scale: float, block_table,
+                            seq_lens_dev, seq_lens_host: Sequence[int], out, workspace=None, stream=None):
+    """``decode_absorbed_fwd`` over an E4M3 cache (uint8 codes
+    [num_blocks, block_size, r_kv + d_rope], value = code * cache_scale)."""
+    import numpy as np
+    import torch
+    lib = load_library()
+    act, i32 = _act(cfg), _i32()
+    lens = np.ascontiguousarray(np.asarray(seq_lens_host, dtype=np.int32))
+    ws_bytes = decode_fp8_workspace_size(cfg, lens)
+    st = _resolve_stream(stream)
+    ws = _workspace(ws_bytes, q_nope.device, workspace, st)
+    num_blocks, block_size = kv_cache_fp8.shape[0], kv_cache_fp8.shape[1]
+    _check(lib.mla_decode_absorbed_fp8_fwd(ctypes.byref(cfg), _ptr(w_kv_b, dtype=act, name="w_kv_b"),
+                                           _ptr(q_nope, dtype=act, name="q_nope"),
+                                           _ptr(q_pe, dtype=act, name="q_pe"),
+                                           _ptr(kv_cache_fp8, dtype=torch.uint8, name="kv_cache_fp8"),
+                                           float(cache_scale), num_blocks, block_size,
+                                           _ptr(block_table, dtype=i32, name="block_table"), block_table.shape[1],
+                                           _ptr(seq_lens_dev, dtype=i32, name="seq_lens_dev"), lens.ctypes.data,
+                                           len(lens), _ptr(out, dtype=act, name="out"), _ptr(ws), ws.numel(),
+                                           st.cuda_stream), "mla_decode_absorbed_fp8_fwd")
+    return ws
 
 
 def prefill_chunk_workspace_size(cfg: MlaConfig, cu_seqlens_host: Sequence[int], prefix_lens_host: Sequence[int]) -> int:

@@ -187,21 +187,24 @@ struct DecodePlan {
 
 // The keys of all sequences, one after another, each sequence preceded by
 // kDecodeSegmentCost placeholder keys, are dealt to workgroups in runs of
-// `quota` keys (a multiple of 32; at most as many blocks of the smallest
-// allowed size, 16, as a workgroup can stage).  The placeholders charge the
-// workgroup that starts a sequence for the fixed cost of one more segment
+// `quota` keys (a multiple of the split kernel's tile, 32 keys for the bf16
+// cache and 64 for the E4M3 cache; the cuts inside a sequence move to the
+// nearest tile boundary, so a workgroup's keys, quota + one tile at most, span
+// no more blocks of the smallest allowed size, 16, than it can stage).  The
+// placeholders charge the workgroup that starts a sequence for the fixed cost
+// of one more segment
 // (staging, query load, pipeline fill, partial stores), so workgroups that
 // span a sequence end take fewer keys.  Sequence b, whose first key sits at
 // r_b in that order, collects partials in slots 0 .. (r_b + L_b - 1) / quota -
 // r_b / quota.
-DecodePlan decode_plan(const mla_config* c, const int32_t* lens, int batch, int64_t key_cap) {
+DecodePlan decode_plan(const mla_config* c, const int32_t* lens, int batch, int64_t key_cap, int tile = 32) {
   DecodePlan p{};
   int64_t total = 0;
   for (int b = 0; b < batch; ++b) {
     const int64_t L = std::min<int64_t>(std::max(lens[b], 0), key_cap);
     if (L > 0) total += L + kDecodeSegmentCost;
   }
-  constexpr int kTile = 32, kMaxQuota = ((kDecodeMaxChunkBlocks - 2) * 16 - kTile) / kTile * kTile;
+  const int kTile = tile, kMaxQuota = ((kDecodeMaxChunkBlocks - 2) * 16 - kTile) / kTile * kTile;
   int64_t quota = kTile * std::max<int64_t>(1, (total + (int64_t)kTile * kDecodeTargetGroups - 1) /
                                                    ((int64_t)kTile * kDecodeTargetGroups));
   quota = std::min<int64_t>(quota, kMaxQuota);
@@ -340,6 +343,11 @@ size_t mla_prefill_chunk_workspace_size(const mla_config* cfg, const int32_t* cu
 size_t mla_decode_workspace_size(const mla_config* cfg, const int32_t* seq_lens_host, int32_t batch) {
   if (check_config(cfg) != MLA_OK || !seq_lens_host || batch <= 0) return 0;
   return decode_plan(cfg, seq_lens_host, batch, INT32_MAX).total;
+}
+
+size_t mla_decode_fp8_workspace_size(const mla_config* cfg, const int32_t* seq_lens_host, int32_t batch) {
+  if (check_config(cfg) != MLA_OK || !seq_lens_host || batch <= 0) return 0;
+  return decode_plan(cfg, seq_lens_host, batch, INT32_MAX, 64).total;
 }
 
 mla_status mla_latent_norm_rope(const mla_config* cfg, const void* src, int64_t src_row_stride, int32_t n_rows,
@@ -745,7 +753,8 @@ static mla_status prefill_core(const mla_config* cfg, const mla_weights* w, cons
 static mla_status decode_check(const mla_config* cfg, const void* w_kv_b, const void* q_nope, const void* q_pe,
                                const void* kv_cache, int32_t num_blocks, int32_t block_size,
                                const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens_dev,
-                               const int32_t* seq_lens_host, int32_t batch, void* out, DecodePlan* plan) {
+                               const int32_t* seq_lens_host, int32_t batch, void* out, DecodePlan* plan,
+                               int tile = 32) {
   mla_status s = check_config(cfg);
   if (s != MLA_OK) return s;
   if (cfg->dtype != MLA_BF16) return fail(MLA_ERR_UNSUPPORTED, "absorbed decode is compiled for bf16 only");
@@ -767,7 +776,7 @@ static mla_status decode_check(const mla_config* cfg, const void* w_kv_b, const 
   const void* ptrs[] = {w_kv_b, q_nope, q_pe, kv_cache, out};
   for (const void* p : ptrs)
     if (!aligned16(p)) return fail(MLA_ERR_MISALIGNED, "decode needs 16-byte aligned tensors");
-  *plan = decode_plan(cfg, seq_lens_host, batch, (int64_t)max_blocks * block_size);
+  *plan = decode_plan(cfg, seq_lens_host, batch, (int64_t)max_blocks * block_size, tile);
   return MLA_OK;
 }
 
@@ -776,7 +785,8 @@ static mla_status decode_check(const mla_config* cfg, const void* w_kv_b, const 
 static mla_status decode_launch(const mla_config* cfg, const DecodePlan& P, const void* w_kv_b, const void* q_nope,
                                 const void* q_pe, const void* kv_cache, int32_t num_blocks, int32_t block_size,
                                 const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens_dev,
-                                int32_t batch, void* out, char* ws, hipStream_t st) {
+                                int32_t batch, void* out, char* ws, hipStream_t st, bool fp8_cache = false,
+                                float cache_scale = 1.f) {
   const int H = cfg->num_heads, dn = cfg->qk_nope_dim, dv = cfg->v_head_dim, R = cfg->kv_lora_rank;
   bf16* qt = (bf16*)(ws + P.qt);
   hipError_t e;
@@ -791,7 +801,12 @@ static mla_status decode_launch(const mla_config* cfg, const DecodePlan& P, cons
   // absorb W_UK into the query: qt[b, h, :] = q_nope[b, h, :] . W_kv_b[h*(dn+dv) + 0:dn, :]
   d.q_nope = (const bf16*)q_nope; d.w_uk = (const bf16*)w_kv_b; d.w_uv_hstride = (int64_t)(dn + dv) * R;
   if ((e = launch_decode_absorb_q(d, st)) != hipSuccess) return hip_fail(e, "absorb q");
-  if ((e = launch_decode_split(d, st)) != hipSuccess) return hip_fail(e, "decode split");
+  if (fp8_cache) {
+    d.cache = nullptr; d.cache8 = (const uint8_t*)kv_cache; d.cache_scale = cache_scale;
+    if ((e = launch_decode_split_fp8(d, st)) != hipSuccess) return hip_fail(e, "decode split (fp8 cache)");
+  } else if ((e = launch_decode_split(d, st)) != hipSuccess) {
+    return hip_fail(e, "decode split");
+  }
   // combine the splits and un-absorb W_UV: out[b, h, :] = W_kv_b[h*(dn+dv) + dn : +dv, :] . o_lat[b, h, :]
   d.w_uv = (const bf16*)w_kv_b + (int64_t)dn * R; d.w_uv_hstride = (int64_t)(dn + dv) * R;
   d.out = (bf16*)out; d.dv = dv;
@@ -833,6 +848,47 @@ mla_status mla_decode_absorbed_fwd_noalloc(const mla_config* cfg, const void* w_
   s = decode_launch(cfg, P, w_kv_b, q_nope, q_pe, kv_cache, num_blocks, block_size, block_table, max_blocks,
                     seq_lens_dev, batch, out, ws, (hipStream_t)stream);
   return s == MLA_OK ? ok() : s;
+}
+
+mla_status mla_decode_absorbed_fp8_fwd(const mla_config* cfg, const void* w_kv_b, const void* q_nope,
+                                       const void* q_pe, const void* kv_cache_fp8, float cache_scale,
+                                       int32_t num_blocks, int32_t block_size, const int32_t* block_table,
+                                       int32_t max_blocks, const int32_t* seq_lens_dev,
+                                       const int32_t* seq_lens_host, int32_t batch, void* out, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  DecodePlan P;
+  mla_status s = decode_check(cfg, w_kv_b, q_nope, q_pe, kv_cache_fp8, num_blocks, block_size, block_table,
+                              max_blocks, seq_lens_dev, seq_lens_host, batch, out, &P, 64);
+  if (s != MLA_OK) return s;
+  if (!(cache_scale > 0.f) || !std::isfinite(cache_scale))
+    return fail(MLA_ERR_INVALID_ARG, "cache_scale must be a positive finite number");
+  if (workspace && !aligned16(workspace)) return fail(MLA_ERR_MISALIGNED, "decode needs a 16-byte aligned workspace");
+  if (!workspace || workspace_bytes < P.total)
+    return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", P.total, workspace_bytes);
+  s = decode_launch(cfg, P, w_kv_b, q_nope, q_pe, kv_cache_fp8, num_blocks, block_size, block_table, max_blocks,
+                    seq_lens_dev, batch, out, (char*)workspace, (hipStream_t)stream, true, cache_scale);
+  return s == MLA_OK ? ok() : s;
+}
+
+mla_status mla_cache_quantize_fp8(const void* src, int64_t src_row_stride, int64_t n_rows, int32_t row_width,
+                                  float scale, void* dst, int64_t dst_row_stride, void* stream) {
+  if (n_rows < 0 || row_width <= 0) return fail(MLA_ERR_INVALID_ARG, "n_rows >= 0 and row_width > 0 required");
+  if (n_rows == 0) return ok();
+  if (!src || !dst) return fail(MLA_ERR_INVALID_ARG, "src and dst are required");
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(MLA_ERR_INVALID_ARG, "scale must be a positive finite number");
+  if (row_width % 8 || src_row_stride < row_width || dst_row_stride < row_width || src_row_stride % 8 ||
+      dst_row_stride % 8)
+    return fail(MLA_ERR_MISALIGNED, "row_width and both strides must be multiples of 8 (strides >= row_width)");
+  if (!aligned16(src) || ((uintptr_t)dst & 7))
+    return fail(MLA_ERR_MISALIGNED, "src must be 16-byte aligned and dst 8-byte aligned");
+  CacheQuantArgs q{};
+  q.src = (const bf16*)src; q.src_stride = src_row_stride;
+  q.dst = (uint8_t*)dst; q.dst_stride = dst_row_stride;
+  q.rows = n_rows; q.width = row_width;
+  q.inv = 1.0f / scale;
+  const hipError_t e = launch_cache_quant_fp8(q, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "cache quantisation");
+  return ok();
 }
 
 }  // extern "C"

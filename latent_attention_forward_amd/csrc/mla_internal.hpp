@@ -298,10 +298,26 @@ struct DecodeArgs {
   int max_slots;          // most segments of one sequence (host plan)
   int num_items;          // workgroups of the split kernel
   float scale;
+  // E4M3 latent cache (the fp8 decode): codes [num_blocks, block_size, 576],
+  // value = code * cache_scale
+  const uint8_t* cache8;
+  float cache_scale;
 };
 
 hipError_t launch_decode_absorb_q(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_combine_unabsorb(const DecodeArgs& a, hipStream_t s);
+// Split kernel of the decode over an E4M3 cache (64-key tiles, fp8 MFMAs);
+// same partial-buffer contract as launch_decode_split.
+hipError_t launch_decode_split_fp8(const DecodeArgs& a, hipStream_t s);
+
+// bf16 rows -> E4M3 codes: dst = E4M3(fl32(x * inv)), saturating at +-448.
+struct CacheQuantArgs {
+  const bf16* src; int64_t src_stride;   // elements
+  uint8_t* dst; int64_t dst_stride;      // bytes
+  int64_t rows; int width;               // width: a multiple of 8
+  float inv;
+};
+hipError_t launch_cache_quant_fp8(const CacheQuantArgs& a, hipStream_t s);
 
 }  // namespace mla

@@ -37,7 +37,7 @@ def test_header_symbols_exported(lib):
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(mla.exported_symbols())
-    assert lib.mla_abi_version() == 3
+    assert lib.mla_abi_version() == 4
 
 
 def test_config_validation(lib):
@@ -156,6 +156,25 @@ def test_device_calls_reject_bad_arguments_before_launch(lib):
     st = lib.mla_decode_absorbed_fwd_noalloc(ctypes.byref(dcfg), 4096, 4096, 4096, 4096, 10, 60, 4096, 4, 4096,
                                              lens.ctypes.data, 2, 4096, None)
     assert st == mla.MLA_ERR_INVALID_ARG       # the same argument checks as with a workspace
+    # fp8 decode: the same checks, then the cache scale; cache quantisation
+    lens = np.array([100, 200], np.int32)
+    h = lib.mla_decode_absorbed_fp8_fwd
+    st = h(ctypes.byref(dcfg), 4096, 4096, 4096, 4096, 1.0, 10, 60, 4096, 4, 4096, lens.ctypes.data, 2, 4096, 4096,
+           1 << 30, None)
+    assert st == mla.MLA_ERR_INVALID_ARG       # block size not a power of two
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        st = h(ctypes.byref(dcfg), 4096, 4096, 4096, 4096, bad, 10, 64, 4096, 4, 4096, lens.ctypes.data, 2, 4096,
+               4096, 1 << 30, None)
+        assert st == mla.MLA_ERR_INVALID_ARG and b"cache_scale" in lib.mla_last_error()
+    st = h(ctypes.byref(dcfg), 4096, 4096, 4096, 4096, 1.0, 10, 64, 4096, 4, 4096, lens.ctypes.data, 2, 4096, 4096,
+           16, None)
+    assert st == mla.MLA_ERR_WORKSPACE
+    q = lib.mla_cache_quantize_fp8
+    assert q(4096, 576, 10, 576, 0.0, 8192, 576, None) == mla.MLA_ERR_INVALID_ARG
+    assert q(4096, 576, 10, 570, 1.0, 8192, 576, None) == mla.MLA_ERR_MISALIGNED
+    assert q(4096, 576, 10, 576, 1.0, 8196, 576, None) == mla.MLA_ERR_MISALIGNED
+    assert q(4096, 576, 10, 576, 1.0, None, 576, None) == mla.MLA_ERR_INVALID_ARG
+    assert q(4096, 576, 0, 576, 1.0, 8192, 576, None) == mla.MLA_OK   # nothing to convert
     # norm/rope: rope slices overlapping the norm region, slot mapping in place
     st = lib.mla_latent_norm_rope(ctypes.byref(cfg), 4096, 576, 4, 576, 512, 4096, 500, 1, 64, 4096, 4096, 16, 4096,
                                   8192, 576, None, 0, None)
@@ -186,13 +205,17 @@ def test_decode_plan_matches_workspace_size(lib, lens):
     import decode_plan as dp
     cfg = mla.make_config(mi.WORKLOADS["dsv3_decode_64"])
     assert mla.decode_workspace_size(cfg, lens) == dp.workspace_bytes(lens, 128, 512)
-    quota, groups, segs = dp.plan(lens)
-    assert quota % 32 == 0 and quota <= dp.MAX_QUOTA
-    for L, s in zip(lens, segs):
-        cover = [k for k0, k1, _ in s for k in range(k0, k1)]
-        assert cover == list(range(L))
-        assert [slot for _, _, slot in s] == list(range(len(s)))
-        # a segment spans at most the blocks of 16 tokens one workgroup stages
-        assert all(k1 - k0 <= (dp.MAX_CHUNK_BLOCKS - 1) * 16 for k0, k1, _ in s)
-    ent, n_ent = dp.entries(lens)
-    assert len(set(ent.values())) == len(ent) and max(ent.values()) < n_ent
+    assert mla.decode_fp8_workspace_size(cfg, lens) == dp.workspace_bytes(lens, 128, 512, tile=64)
+    for tile in (32, 64):
+        quota, groups, segs = dp.plan(lens, tile)
+        assert quota % tile == 0 and quota <= dp.max_quota(tile)
+        for L, s in zip(lens, segs):
+            cover = [k for k0, k1, _ in s for k in range(k0, k1)]
+            assert cover == list(range(L))
+            assert [slot for _, _, slot in s] == list(range(len(s)))
+            # tiles start on multiples of the tile inside the sequence
+            assert all(k0 % tile == 0 for k0, k1, _ in s if k1 > k0)
+            # a segment spans at most the blocks of 16 tokens one workgroup stages
+            assert all((k1 - 1) // 16 - k0 // 16 + 1 <= dp.MAX_CHUNK_BLOCKS for k0, k1, _ in s if k1 > k0)
+        ent, n_ent = dp.entries(lens, tile)
+        assert len(set(ent.values())) == len(ent) and max(ent.values()) < n_ent
