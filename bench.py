@@ -47,6 +47,7 @@ COPY_BYTES = 256 << 20
 # sources whose change invalidates a committed counter figure
 KERNEL_SOURCES = {"flash": ["flash.hip", "mla_internal.hpp"],
                   "decode": ["decode.hip", "api.hip", "mla_internal.hpp"],
+                  "decode_fp8": ["decode_fp8.hip", "decode.hip", "api.hip", "mla_internal.hpp"],
                   "chunk": ["flash.hip", "mla_internal.hpp"]}
 # the graded prefill workloads whose attention kernel is timed
 ATTN_WORKLOADS = ["megatron_2x2048", "dsv3_prefill_4096", "kimi_gated_varlen_8192"]
@@ -62,8 +63,8 @@ def parse():
     ap.add_argument("--chunk", default="dsv3_chunk_4x1024_p4096",
                     help="chunked-prefill workload reported beside the metric ('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["full", "prefill", "attention", "decode", "copy", "chunk", "chunk_attention",
-                                       "norm"], default="full",
+    ap.add_argument("--mode", choices=["full", "prefill", "attention", "decode", "decode_fp8", "copy", "chunk",
+                                       "chunk_attention", "norm"], default="full",
                     help="full: the JSON line; the others only run that part's timing loop (for profilers)")
     ap.add_argument("--attn-workload", default="dsv3_prefill_4096", choices=ATTN_WORKLOADS,
                     help="workload of --mode attention")
@@ -344,8 +345,18 @@ def main():
     max_blocks = dc.block_table.shape[1]
     del dc
 
+    # the same cache in E4M3 (one scale), converted by the library
+    FP8_SCALE = 1.0 / 32.0
+    cache8 = torch.empty(cache.shape, dtype=torch.uint8, device=dev)
+    mla.cache_quantize_fp8(cache, FP8_SCALE, cache8)
+    ws_d8 = torch.empty(mla.decode_fp8_workspace_size(dcfg, lens_h), dtype=torch.uint8, device=dev)
+
     def prefill():
         mla.prefill_fwd(cfg, W, x, cu, cuh, out, latent_out=lat, rope_cos=cos, rope_sin=sin, workspace=ws_p)
+
+    def decode_fp8():
+        mla.decode_absorbed_fp8_fwd(dcfg, w_kvb, q_nope, q_pe, cache8, FP8_SCALE, table, lens_d, lens_h, out_d,
+                                    workspace=ws_d8)
 
     def decode():
         mla.decode_absorbed_fwd(dcfg, w_kvb, q_nope, q_pe, cache, table, lens_d, lens_h, out_d, workspace=ws_d)
@@ -422,9 +433,11 @@ def main():
             src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
             dst = torch.empty_like(src)
             fn = lambda: dst.copy_(src)
+        elif args.mode == "decode_fp8":
+            fn = decode_fp8
         else:
             fn = prefill if args.mode == "prefill" else decode
-        flush = torch.zeros(512 << 20, dtype=torch.uint8, device=dev) if args.mode == "decode" else None
+        flush = torch.zeros(512 << 20, dtype=torch.uint8, device=dev) if args.mode in ("decode", "decode_fp8") else None
         sink = torch.zeros(1, dtype=torch.int64, device=dev)
         for i in range(args.warmup + args.steps):
             if flush is not None:
@@ -493,6 +506,17 @@ def main():
         de[i][1].record(stream)
     torch.cuda.synchronize()
     dec_ms = sum(a.elapsed_time(b) for a, b in de) / args.steps
+    # the decode over the E4M3 copy of the cache, timed the same way
+    for _ in range(20):
+        sink.copy_(flush.view(torch.int64).sum())
+        decode_fp8()
+    for i in range(args.steps):
+        sink.copy_(flush.view(torch.int64).sum())
+        de[i][0].record(stream)
+        decode_fp8()
+        de[i][1].record(stream)
+    torch.cuda.synchronize()
+    dec8_ms = sum(a.elapsed_time(b) for a, b in de) / args.steps
     del flush
 
     # ------------------------------------------------------------------ chunked prefill (reported beside the metric)
@@ -521,6 +545,8 @@ def main():
     layer_tflops = layer_flops(sh, n, a_flops) / (prefill_ms * 1e-3) / 1e12
     d_bytes = decode_bytes(dsh, lens_h, max_blocks)
     dec_gbs = d_bytes / (dec_ms * 1e-3) / 1e9
+    d8_bytes = d_bytes - int(lens_h.sum()) * (dsh.kv_lora_rank + dsh.qk_rope_dim)   # one byte per cached value
+    dec8_gbs = d8_bytes / (dec8_ms * 1e-3) / 1e9
     value = 0.5 * (attn_tflops / PEAK_MFMA_TFLOPS + dec_gbs / PEAK_HBM_GBS) * 100
 
     rec = {
@@ -550,6 +576,12 @@ def main():
                             "kernel": "mla_decode_absorbed_fwd (query absorption + split-KV attention + fused combine and un-absorb)",
                             "bytes_per_call": d_bytes},
     }
+    rec["decode_fp8_cache"] = {
+        "workload": f"{args.decode} with the cache in E4M3 (scale {FP8_SCALE}), mla_decode_absorbed_fp8_fwd",
+        "ms": round(dec8_ms, 4), "speedup_vs_bf16_cache": round(dec_ms / dec8_ms, 3),
+        "roofline": {"bound": "hbm", "achieved": round(dec8_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(dec8_gbs / PEAK_HBM_GBS, 4), "traffic": traffic_for("decode_fp8"),
+                     "bytes_per_call": d8_bytes}}
     if chunk_rec is not None:
         rec["chunked_prefill"] = chunk_rec
     if not args.no_cpu_baseline:

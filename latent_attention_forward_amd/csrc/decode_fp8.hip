@@ -68,12 +68,19 @@ template <int BYTE> __device__ __forceinline__ float fp8_value(int word) {
 // score chain stays in VGPRs while the AGPRs hold the 32 x 512 output.  The
 // asm carries the wait states for VALU-written operands and scales.
 __device__ __forceinline__ void mfma_f8_vacc(f32x16& c, const i32x8& a, const i32x8& b, int sa, int sb) {
-  asm volatile("s_nop 4\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+  asm volatile("s_nop 2\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
                : "+v"(c) : "v"(a), "v"(b), "v"(sa), "v"(sb));
 }
 __device__ __forceinline__ void mfma_f8_vacc0(f32x16& c, const i32x8& a, const i32x8& b, int sa, int sb) {
-  asm volatile("s_nop 4\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %4 op_sel_hi:[0,0,0]"
+  asm volatile("s_nop 2\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %4 op_sel_hi:[0,0,0]"
                : "=&v"(c) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+}
+// The same MFMA accumulating in AGPRs (the 32 x 512 output).  As asm it stays
+// where it is written: the compiler would sink the builtin past the step's
+// wait and barrier and issue every operand read of the tile first.
+__device__ __forceinline__ void mfma_f8_aacc(f32x16& c, const i32x8& a, const i32x8& b, int sa, int sb) {
+  asm volatile("s_nop 2\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+               : "+a"(c) : "v"(a), "v"(b), "v"(sa), "v"(sb));
 }
 // Wait states between the 16-pass MFMA writing VGPRs and a VALU read of them.
 __device__ __forceinline__ void mfma16p_result_wait() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"); }
@@ -86,6 +93,8 @@ __device__ __forceinline__ int pack4_fp8(float a, float b, float c, float d) {
 __device__ __forceinline__ float sat448(float v) {
   return __builtin_fabsf(v) > 448.f ? __builtin_copysignf(448.f, v) : v;
 }
+// The same clamp for finite values (one v_med3).
+__device__ __forceinline__ float clamp448(float v) { return __builtin_amdgcn_fmed3f(v, -448.f, 448.f); }
 
 // max of v over this lane and its partner lane l ^ 32
 __device__ __forceinline__ float pair_max(float v) {
@@ -114,10 +123,10 @@ __device__ __forceinline__ void mx_pair(const float (&v)[32], int half, i32x8& c
   const float i1 = __uint_as_float((uint32_t)(254 - s1) << 23);
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    codes[w] = pack4_fp8(sat448(v[4 * w] * i0), sat448(v[4 * w + 1] * i0), sat448(v[4 * w + 2] * i0),
-                         sat448(v[4 * w + 3] * i0));
-    codes[4 + w] = pack4_fp8(sat448(v[16 + 4 * w] * i1), sat448(v[17 + 4 * w] * i1), sat448(v[18 + 4 * w] * i1),
-                             sat448(v[19 + 4 * w] * i1));
+    codes[w] = pack4_fp8(clamp448(v[4 * w] * i0), clamp448(v[4 * w + 1] * i0), clamp448(v[4 * w + 2] * i0),
+                         clamp448(v[4 * w + 3] * i0));
+    codes[4 + w] = pack4_fp8(clamp448(v[16 + 4 * w] * i1), clamp448(v[17 + 4 * w] * i1),
+                             clamp448(v[18 + 4 * w] * i1), clamp448(v[19 + 4 * w] * i1));
   }
   scale_byte = half ? s1 : s0;
 }
@@ -441,6 +450,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_fp8_kernel(DecodeArgs
       }
       l_run = fmaf(acc, __builtin_amdgcn_ldexpf(1.f, (int)eb[mt]), l_run);
     }
+    asm volatile("" : "+v"(l_run));       // computed here, between the PV MFMAs
   };
   auto no_group = [](auto) {};
   // O^T += C^T P^T over the 64 keys: 16 dim blocks, each one MFMA with the
@@ -467,7 +477,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_fp8_kernel(DecodeArgs
       constexpr int d = decltype(I)::value;
       const i32x8 cur = vf[d % D];
       if constexpr (d + D < NP) vf[d % D] = rd(d + D);
-      o[d] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur, pb, o[d], 0, 0, 0, one_scale, 0, psc);
+      mfma_f8_aacc(o[d], cur, pb, one_scale, psc);
       group(I);
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -524,6 +534,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_fp8_kernel(DecodeArgs
     sa[0] = sbv[0];
     sa[1] = sbv[1];
   }
+  mfma16p_result_wait();                  // the output accumulators are read next
 
   if (exact_path) {
     decode_chunk_exact_fp8(a, b, part, wave * 32, k0, k1);
