@@ -48,4 +48,5 @@ from .mla import (  # noqa: F401
 )
 from .fp8 import (  # noqa: F401
     e4m3_value, e4m3_encode, cache_inverse_scale, cache_quantize_fp8, cache_dequantize_fp8, decode_absorbed_fp8,
+    mx_scale_exponent, mxfp8_quantize, mxfp8_dequantize, q_uproj_rope, q_uproj_rope_mxfp8,
 )

@@ -33,12 +33,23 @@ normal, smallest normal and subnormal, the NaN code), by exhaustive
 round-trips of the 254 finite codes, by brute-force nearest-value search with
 the even tie break, and by planted mistakes (bias 8, truncation, ties away
 from zero, no saturation) that fail those pins.
+
+MXFP8 (the query up-projection the Megatron-LM MLA guide names,
+``use_fused_mla_q_uproj``: query up-projection, per-head RoPE and MXFP8
+quantisation in one kernel): the OCP Microscaling conversion of a block of
+32 consecutive values V_i: shared scale X = 2^(floor(log2(max_i |V_i|)) - emax)
+with emax = 8 for E4M3 (its largest binade), stored as the E8M0 byte
+(exponent + 127), elements E4M3(V_i / X) with the saturating conversion above;
+a block of zeros takes the smallest scale, 2^-127.  Pinned by values the rule
+fixes (amax 1 -> scale 2^-8, element 1 -> 256), the exact round trip of
+representable blocks, invariance under powers of two, the half-ulp error
+bound, and planted mistakes (emax 7, ceil instead of floor, no saturation).
 """
 from typing import Optional, Sequence
 
 import numpy as np
 
-from .mla import decode_absorbed
+from .mla import _f64, _rope, decode_absorbed, rope_cos_sin
 
 E4M3_MAX = 448.0
 E4M3_NAN = 0x7F
@@ -126,3 +137,62 @@ def decode_absorbed_fp8(shape, w_kv_b, q_nope, q_pe, cache_codes, scale: float, 
     dequantised rows."""
     return decode_absorbed(shape, w_kv_b, q_nope, q_pe, cache_dequantize_fp8(cache_codes, scale), block_table,
                            seq_lens, block_size, batch_idx=batch_idx, return_latent=return_latent)
+
+
+# ----------------------------------------------------------------------------
+# MXFP8 (OCP Microscaling, E4M3 elements, blocks of 32)
+# ----------------------------------------------------------------------------
+MX_BLOCK = 32
+E4M3_EMAX = 8
+
+
+def mx_scale_exponent(amax) -> np.ndarray:
+    """floor(log2 amax) - 8, within the E8M0 range [-127, 127]; -127 for a
+    zero block."""
+    a = np.asarray(amax, dtype=np.float64)
+    e = np.full(a.shape, -127, dtype=np.int64)
+    nz = a > 0
+    e[nz] = np.floor(np.log2(a[nz])).astype(np.int64) - E4M3_EMAX
+    return np.clip(e, -127, 127)
+
+
+def mxfp8_quantize(x):
+    """(codes, scale_bytes) of x [..., n], n a multiple of 32: blocks of 32
+    consecutive values along the last axis.  scale_bytes = exponent + 127."""
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[-1]
+    assert n % MX_BLOCK == 0
+    b = x.reshape(*x.shape[:-1], n // MX_BLOCK, MX_BLOCK)
+    e = mx_scale_exponent(np.abs(b).max(-1))
+    codes = e4m3_encode(b / np.ldexp(1.0, e)[..., None])
+    return codes.reshape(x.shape), (e + 127).astype(np.uint8)
+
+
+def mxfp8_dequantize(codes, scale_bytes) -> np.ndarray:
+    c = np.asarray(codes)
+    v = e4m3_value(c).reshape(*c.shape[:-1], c.shape[-1] // MX_BLOCK, MX_BLOCK)
+    e = np.asarray(scale_bytes).astype(np.int64) - 127
+    return (v * np.ldexp(1.0, e)[..., None]).reshape(c.shape)
+
+
+def q_uproj_rope(shape, w_q_b, q_latent, positions) -> np.ndarray:
+    """q = q_latent W_qb^T viewed [N, H, d_nope + d_rope], the rope part of
+    every head rotated at the token's position ("CSDN walkthrough of HF
+    DeepseekV3Attention", forward: q_b_proj, split, apply_rotary_pos_emb on
+    q_pe); not rotated for rope kind "none".  Returns [N, H * d_qk], float64."""
+    H, nope, dr = shape.num_heads, shape.qk_nope_dim, shape.qk_rope_dim
+    q = (_f64(q_latent) @ _f64(w_q_b).T).reshape(-1, H, nope + dr)
+    if shape.rope.kind != "none":
+        cos, sin = rope_cos_sin(np.asarray(positions), dr, shape.rope)
+        q = np.concatenate([q[..., :nope], _rope(shape, q[..., nope:], cos[:, None, :], sin[:, None, :])], -1)
+    return q.reshape(q.shape[0], -1)
+
+
+def q_uproj_rope_mxfp8(shape, w_q_b, q_latent, positions):
+    """The fused query up-projection of the Megatron-LM MLA guide's
+    ``use_fused_mla_q_uproj``: ``q_uproj_rope`` quantised to MXFP8 along each
+    row (blocks of 32 within a head, as d_qk = 192 is 6 blocks).  Returns
+    (codes [N, H d_qk], scale bytes [N, H d_qk / 32], q float64)."""
+    q = q_uproj_rope(shape, w_q_b, q_latent, positions)
+    codes, scales = mxfp8_quantize(q)
+    return codes, scales, q

@@ -156,3 +156,91 @@ def test_decode_over_representable_cache_is_the_bf16_decode():
     got = of.decode_absorbed_fp8(sh, w, qn, qp, q, scale, table, lens, bs)
     ref = om.decode_absorbed(sh, w, qn, qp, cache, table, lens, bs)
     assert np.array_equal(got, ref)
+
+
+# ----------------------------------------------------------------------------- MXFP8
+MX_VALUES = [  # (block contents, expected scale byte, expected codes of the first values)
+    ([1.0, 0.5, -0.25], 119, [0x78, 0x70, 0xE8]),          # amax 1: X = 2^-8, 1 -> 256, 0.5 -> 128, -0.25 -> -64
+    ([448.0, 1.0], 127, [0x7E, 0x38]),                     # amax 448: X = 1
+    ([500.0, -3.0], 127, [0x7E, 0xC4]),                    # amax 500: X = 1, 500 saturates to 448
+    ([3.0, 1.0], 120, [0x7C, 0x70]),                       # amax 3: X = 2^-7, 3 -> 384, 1 -> 128
+    ([0.0, 0.0], 0, [0x00, 0x00]),                         # zero block: smallest scale
+]
+
+
+def _mx_pins(quantize, dequantize):
+    bad = []
+    for vals, sb, codes in MX_VALUES:
+        x = np.zeros(32)
+        x[: len(vals)] = vals
+        c, s = quantize(x)
+        if int(s[0]) != sb or [int(v) for v in c[: len(codes)]] != codes:
+            bad.append(f"values {vals}")
+    rng = np.random.default_rng(2)
+    # blocks on the grid (top element in the top binade) survive exactly
+    cds = rng.integers(0, 0x7E, size=(200, 32)).astype(np.uint8)
+    cds[:, 0] = rng.integers(0x78, 0x7F, size=200)
+    cds ^= rng.integers(0, 2, size=cds.shape).astype(np.uint8) << 7
+    e = rng.integers(-20, 20, size=200)
+    x = of.e4m3_value(cds) * np.ldexp(1.0, e)[:, None]
+    c, s = quantize(x)
+    if not (np.array_equal(c, cds) and np.array_equal(s.ravel().astype(int), e + 127)):
+        bad.append("round trip")
+    # power-of-two invariance and the half-ulp error bound on random blocks
+    y = rng.standard_normal((300, 64)) * np.exp(rng.uniform(-8, 8, size=(300, 1)))
+    c1, s1 = quantize(y)
+    c2, s2 = quantize(y * 2.0 ** 5)
+    if not (np.array_equal(c1, c2) and np.array_equal(s2.astype(int), s1.astype(int) + 5)):
+        bad.append("invariance")
+    X = np.repeat(np.ldexp(1.0, s1.astype(int) - 127), 32, axis=-1)
+    err = np.abs(dequantize(c1, s1) - y)
+    # half an ulp (relative 2^-4, or 2^-10 X among the subnormals), plus what
+    # saturation takes off the elements above 448 X (at most |y| < 512 X)
+    sat = np.maximum(0.0, np.abs(y) - 448.0 * X)
+    if not (np.all(err <= 2.0 ** -4 * np.abs(y) + 2.0 ** -10 * X * (1 + 1e-12) + sat)
+            and np.all(np.abs(y) < 512.0 * X)):
+        bad.append("error bound")
+    return bad
+
+
+def test_mxfp8_pins():
+    assert _mx_pins(of.mxfp8_quantize, of.mxfp8_dequantize) == []
+
+
+def _mx_with(scale_rule, saturate=True):
+    def quantize(x):
+        x = np.asarray(x, np.float64)
+        b = x.reshape(*x.shape[:-1], -1, 32)
+        a = np.abs(b).max(-1)
+        e = np.where(a > 0, scale_rule(np.where(a > 0, a, 1.0)), -127).astype(np.int64)
+        e = np.clip(e, -127, 127)
+        y = b / np.ldexp(1.0, e)[..., None]
+        c = of.e4m3_encode(y)
+        if not saturate:
+            c = np.where(np.abs(y) > 464, np.uint8(0x7F), c)
+        return c.reshape(x.shape), (e + 127).astype(np.uint8)
+    return quantize
+
+
+@pytest.mark.parametrize("quantize", [
+    _mx_with(lambda a: np.floor(np.log2(a)) - 7),
+    _mx_with(lambda a: np.ceil(np.log2(a)) - 8),
+    _mx_with(lambda a: np.floor(np.log2(a)) - 8, saturate=False),
+], ids=["emax7", "ceil", "no_saturation"])
+def test_mxfp8_pins_catch_planted_mistakes(quantize):
+    assert _mx_pins(quantize, of.mxfp8_dequantize)
+
+
+def test_q_uproj_rope_is_the_layer_query():
+    """The fused up-projection's q equals the query of the pinned layer oracle
+    (q_b of the normalised query latent, RoPE on each head's rope part)."""
+    sh = mi.WORKLOADS["tiny_fp32_t64"]
+    case = mi.make_prefill_case(sh, doc_lengths=[20, 44])
+    ref = om.mla_prefill(sh, case.w, case.x, case.cu_seqlens)
+    lat = om.rms_norm(np.asarray(case.x, np.float64) @ np.asarray(case.w["w_q_a"], np.float64).T,
+                      case.w["q_a_gamma"], sh.norm_eps)
+    q = of.q_uproj_rope(sh, case.w["w_q_b"], lat, ref["positions"])
+    assert np.allclose(q, ref["q"].reshape(q.shape), rtol=1e-12, atol=1e-12)
+    codes, scales, q2 = of.q_uproj_rope_mxfp8(sh, case.w["w_q_b"], lat, ref["positions"])
+    assert codes.shape == q.shape and scales.shape == (q.shape[0], q.shape[1] // 32)
+    assert np.array_equal(q2, q)
