@@ -484,6 +484,23 @@ def main():
     head = attn_rec[f"{args.prefill}/f16"]
     attn_ms, attn_tflops, a_flops = head["ms"], head["tflops"], head["flops"]
 
+    # ------------------------------------------------------------------ fused query up-projection + RoPE + MXFP8
+    mxq = None
+    if sh.q_lora_rank > 0:
+        Hq, dqk = sh.num_heads, sh.qk_nope_dim + sh.qk_rope_dim
+        g = torch.Generator(device=dev).manual_seed(5)
+        qlat = torch.randn(n, sh.q_lora_rank, device=dev, generator=g).to(torch.bfloat16)
+        qc = torch.empty(n, Hq * dqk, dtype=torch.uint8, device=dev)
+        qs = torch.empty(n, Hq * dqk // 32, dtype=torch.uint8, device=dev)
+        qpos = torch.from_numpy(np.concatenate([np.arange(b - a) for a, b in zip(cuh[:-1], cuh[1:])]).astype(np.int32)).to(dev)
+        mx_ms = timed(lambda: mla.q_uproj_rope_mxfp8(cfg, qlat, W["w_q_b"], qpos if cos is not None else None, cos,
+                                                     sin, qc, qs), args.steps, warm=10)
+        mx_flops = 2.0 * n * sh.q_lora_rank * Hq * dqk
+        mxq = {"workload": f"{args.prefill} query latent [{n}, {sh.q_lora_rank}] -> [{n}, {Hq * dqk}] E4M3 + E8M0",
+               "us": round(mx_ms * 1e3, 1), "tflops": round(mx_flops / (mx_ms * 1e-3) / 1e12, 1),
+               "frac": round(mx_flops / (mx_ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4), "flops": mx_flops}
+        del qlat, qc, qs
+
     # ------------------------------------------------------------------ fused latent norm + RoPE (a5)
     norm_ms = timed(norm_rope, 50, warm=20)
     lw = sh.kv_lora_rank + sh.qk_rope_dim
@@ -576,6 +593,8 @@ def main():
                             "kernel": "mla_decode_absorbed_fwd (query absorption + split-KV attention + fused combine and un-absorb)",
                             "bytes_per_call": d_bytes},
     }
+    if mxq is not None:
+        rec["q_uproj_rope_mxfp8"] = mxq
     rec["decode_fp8_cache"] = {
         "workload": f"{args.decode} with the cache in E4M3 (scale {FP8_SCALE}), mla_decode_absorbed_fp8_fwd",
         "ms": round(dec8_ms, 4), "speedup_vs_bf16_cache": round(dec_ms / dec8_ms, 3),

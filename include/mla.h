@@ -390,6 +390,33 @@ mla_status mla_decode_absorbed_fwd_noalloc(const mla_config* cfg, const void* w_
 mla_status mla_cache_quantize_fp8(const void* src, int64_t src_row_stride, int64_t n_rows, int32_t row_width,
                                   float scale, void* dst, int64_t dst_row_stride, void* stream);
 
+/* The fused query up-projection of "Megatron-LM MLA guide" (parameter
+ * section, use_fused_mla_q_uproj: query up-projection, per-head RoPE and MXFP8
+ * quantisation in one kernel):
+ *   q = q_latent W_qb^T viewed [N, H, d_nope + d_rope], the rope part of each
+ *       head rotated at positions[t] (plain or YaRN tables, rotate_half or
+ *       interleaved pairs as cfg says; no rotation for MLA_ROPE_NONE)
+ *   quantised to MXFP8 along each row, blocks of 32 consecutive columns (a
+ *   head of d_qk = 192 is 6 blocks), by the OCP Microscaling rule for E4M3:
+ *   shared scale X = 2^(floor(log2 max|q_i|) - 8), elements E4M3(q_i / X),
+ *   round to nearest even, saturating at 448; a zero block takes X = 2^-127.
+ *   q_latent  DEVICE bf16 [N, ldq] (the normalised query latent, RMSNorm_q
+ *             applied), 16-byte aligned, ldq a multiple of 8
+ *   w_q_b     DEVICE bf16 [H * d_qk, q_lora_rank]
+ *   positions DEVICE int32 [N]; rope_cos/rope_sin DEVICE tables of
+ *             mla_rope_table with rope_table_len rows (unused for
+ *             MLA_ROPE_NONE); a position outside the table gives NaN values
+ *   q_codes   DEVICE uint8 [N, H * d_qk] E4M3 codes, 16-byte aligned
+ *   q_scales  DEVICE uint8 [N, H * d_qk / 32] E8M0 bytes (exponent + 127),
+ *             8-byte aligned
+ * The product is accumulated in fp32 and rounded once, to MXFP8.  bf16
+ * configs with a query latent (q_lora_rank > 0, a multiple of 32) and the
+ * supported head shape only (MLA_ERR_INVALID_ARG / MLA_ERR_UNSUPPORTED). */
+mla_status mla_q_uproj_rope_mxfp8(const mla_config* cfg, const void* q_latent, int64_t ldq, int32_t n_tokens,
+                                  const void* w_q_b, const int32_t* positions, const float* rope_cos,
+                                  const float* rope_sin, int32_t rope_table_len, void* q_codes, void* q_scales,
+                                  void* stream);
+
 /* mla_decode_absorbed_fwd over an E4M3 latent cache (same arguments, bf16
  * queries, weights and output; "Megatron-LM MLA guide", inference section, as
  * for the bf16 decode).  The result approximates the absorbed decode over the

@@ -70,6 +70,7 @@ _SIGNATURES = {
     "mla_decode_absorbed_fwd_noalloc": (_I32, [_CFG, _P, _P, _P, _P, _I32, _I32, _P, _I32, _P, _P, _I32, _P, _P]),
     "mla_prefill_chunk_workspace_size": (_SZ, [_CFG, _P, _P, _I32]),
     "mla_decode_fp8_workspace_size": (_SZ, [_CFG, _P, _I32]),
+    "mla_q_uproj_rope_mxfp8": (_I32, [_CFG, _P, _I64, _I32, _P, _P, _P, _P, _I32, _P, _P, _P]),
     "mla_cache_quantize_fp8": (_I32, [_P, _I64, _I64, _I32, ctypes.c_float, _P, _I64, _P]),
     "mla_decode_absorbed_fp8_fwd": (_I32, [_CFG, _P, _P, _P, _P, ctypes.c_float, _I32, _I32, _P, _I32, _P, _P, _I32,
                                            _P, _P, _SZ, _P]),
@@ -404,6 +405,23 @@ def cache_quantize_fp8(src, scale: float, dst, stream=None):
     _check(load_library().mla_cache_quantize_fp8(_ptr(src, dtype=torch.bfloat16, name="src"), width, rows, width,
                                                  float(scale), _ptr(dst, dtype=torch.uint8, name="dst"), width,
                                                  _stream(stream)), "mla_cache_quantize_fp8")
+
+
+def q_uproj_rope_mxfp8(cfg: MlaConfig, q_latent, w_q_b, positions, rope_cos, rope_sin, q_codes, q_scales,
+                       stream=None):
+    """Fused query up-projection + RoPE + MXFP8 (``mla_q_uproj_rope_mxfp8``):
+    q_latent [N, q_lora_rank] bf16, w_q_b bf16, positions int32 [N] (None
+    without RoPE), q_codes uint8 [N, H d_qk], q_scales uint8 [N, H d_qk / 32]."""
+    import torch
+    act, i32 = _act(cfg), _i32()
+    n = q_latent.shape[0]
+    table_len = rope_cos.shape[0] if rope_cos is not None else 0
+    _check(load_library().mla_q_uproj_rope_mxfp8(
+        ctypes.byref(cfg), _ptr(q_latent, rows=True, dtype=act, name="q_latent"), q_latent.stride(0), n,
+        _ptr(w_q_b, dtype=act, name="w_q_b"), _ptr(positions, dtype=i32, name="positions"),
+        _ptr(rope_cos, dtype=torch.float32, name="rope_cos"), _ptr(rope_sin, dtype=torch.float32, name="rope_sin"),
+        table_len, _ptr(q_codes, dtype=torch.uint8, name="q_codes"), _ptr(q_scales, dtype=torch.uint8, name="q_scales"),
+        _stream(stream)), "mla_q_uproj_rope_mxfp8")
 
 
 def decode_absorbed_fp8_fwd(cfg: MlaConfig, w_kv_b, q_nope, q_pe, kv_cache_fp8, cache_scale: float, block_table,

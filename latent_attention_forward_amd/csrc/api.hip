@@ -870,6 +870,38 @@ mla_status mla_decode_absorbed_fp8_fwd(const mla_config* cfg, const void* w_kv_b
   return s == MLA_OK ? ok() : s;
 }
 
+mla_status mla_q_uproj_rope_mxfp8(const mla_config* cfg, const void* q_latent, int64_t ldq, int32_t n_tokens,
+                                  const void* w_q_b, const int32_t* positions, const float* rope_cos,
+                                  const float* rope_sin, int32_t rope_table_len, void* q_codes, void* q_scales,
+                                  void* stream) {
+  mla_status s = check_config(cfg);
+  if (s != MLA_OK) return s;
+  if (cfg->dtype != MLA_BF16) return fail(MLA_ERR_UNSUPPORTED, "the MXFP8 query projection is compiled for bf16 only");
+  if ((s = check_supported(cfg)) != MLA_OK) return s;
+  if (cfg->q_lora_rank <= 0) return fail(MLA_ERR_INVALID_ARG, "the fused query up-projection needs a query latent (q_lora_rank > 0)");
+  if (n_tokens < 0) return fail(MLA_ERR_INVALID_ARG, "n_tokens must be >= 0");
+  if (n_tokens == 0) return ok();
+  const bool rope = cfg->rope_kind != MLA_ROPE_NONE;
+  if (!q_latent || !w_q_b || !q_codes || !q_scales) return fail(MLA_ERR_INVALID_ARG, "q_latent, w_q_b, q_codes and q_scales are required");
+  if (rope && (!positions || !rope_cos || !rope_sin || rope_table_len <= 0))
+    return fail(MLA_ERR_INVALID_ARG, "positions and the RoPE tables are required with RoPE");
+  const int R = cfg->q_lora_rank, H = cfg->num_heads, dqk = cfg->qk_nope_dim + cfg->qk_rope_dim;
+  if (ldq < R) return fail(MLA_ERR_INVALID_ARG, "ldq >= q_lora_rank required");
+  if (!aligned16(q_latent) || !aligned16(w_q_b) || !aligned16(q_codes) || ((uintptr_t)q_scales & 7) || ldq % 8)
+    return fail(MLA_ERR_MISALIGNED, "q_latent, w_q_b, q_codes need 16-byte alignment, q_scales 8, ldq a multiple of 8");
+  if (R % 32) return fail(MLA_ERR_UNSUPPORTED, "q_lora_rank must be a multiple of 32");
+  GemmArgs g{};
+  g.a = q_latent; g.lda = ldq; g.b = w_q_b; g.ldb = R; g.c = q_codes; g.ldc = (int64_t)H * dqk;
+  g.m = n_tokens; g.n = H * dqk; g.k = R; g.batch = 1;
+  g.c_mx = true; g.c_scale = q_scales; g.ld_scale = (int64_t)H * dqk / 32;
+  g.epilogue = rope ? EPI_ROPE : EPI_STORE;
+  g.cos_t = rope_cos; g.sin_t = rope_sin; g.table_len = rope_table_len; g.positions = positions;
+  g.rope_head_stride = dqk; g.rope_off = cfg->qk_nope_dim; g.rope_interleave = cfg->rope_interleave;
+  const hipError_t e = launch_gemm_bf16(g, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "MXFP8 query projection");
+  return ok();
+}
+
 mla_status mla_cache_quantize_fp8(const void* src, int64_t src_row_stride, int64_t n_rows, int32_t row_width,
                                   float scale, void* dst, int64_t dst_row_stride, void* stream) {
   if (n_rows < 0 || row_width <= 0) return fail(MLA_ERR_INVALID_ARG, "n_rows >= 0 and row_width > 0 required");

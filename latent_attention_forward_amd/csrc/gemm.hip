@@ -235,7 +235,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmArgs g) {
 constexpr int GBM = 256, GBN = 256, GBK = 32, GSTAGES = 4;
 __device__ __forceinline__ int gsw(int r, int c) { return r * GBK + ((c ^ ((r >> 2) & 3)) << 3); }
 
-template <int EPI, int CT>   // CT: 0 bf16, 2 fp16 output
+template <int EPI, int CT>   // CT: 0 bf16, 2 fp16, 3 MXFP8 (E4M3 codes + E8M0 block scales) output
 __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g) {
   // operand stages, then (after the K loop) the 256x256 output tile in 16-bit
   // values: row r of 512 B with 16-byte chunk c at c ^ (r & 31)
@@ -384,6 +384,64 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g) {
     }
   }
 
+  if constexpr (CT == 3) {
+    // MXFP8 output: an MX block is the 32 columns of one N-tile in one row,
+    // 16 of them in this lane and 16 in lane l ^ 32 (same row): shared scale
+    // 2^(floor(log2 amax) - 8) as an E8M0 byte, E4M3 codes saturating at
+    // 448.  Codes go to an LDS tile [256 rows][256 B] (16 B chunk c of row r at
+    // c ^ (r & 15)), scale bytes to [256 rows][8], then out as whole rows.
+    lds_wait_all();
+    wg_barrier();                          // every wave is done with the operand stages
+    uint8_t* tile8 = (uint8_t*)smem;
+    uint8_t* tsc = tile8 + GBM * GBN;
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) {
+        const int ml = wm * 128 + mi * 32 + r32;
+        float amax = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, __builtin_fabsf(acc[ni][mi][e]));
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(amax), __float_as_uint(amax), false, false);
+        amax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        const int sb = max(0, min(254, (int)((__float_as_uint(amax) >> 23) & 255) - 8));
+        const float inv = __uint_as_float((uint32_t)(254 - sb) << 23);   // 2^(127 - sb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int nl = wn * 128 + ni * 32 + q * 8 + hs * 4;
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            y[e] = acc[ni][mi][q * 4 + e] * inv;
+            y[e] = __builtin_fabsf(y[e]) > 448.f ? __builtin_copysignf(448.f, y[e]) : y[e];
+          }
+          int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+          w = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
+          *(int*)(tile8 + ml * 256 + ((((nl >> 4) ^ (ml & 15))) << 4) + (nl & 15)) = w;
+        }
+        if (hs == 0) tsc[ml * 8 + wn * 4 + ni] = (uint8_t)sb;
+      }
+    lds_wait_all();
+    wg_barrier();
+    uint8_t* C8 = (uint8_t*)g.c + (int64_t)blockIdx.z * g.c_bstride;
+#pragma unroll 4
+    for (int i = 0; i < GBM * GBN / 16 / 256; ++i) {
+      const int id = i * 256 + tid, r = id >> 4, c = id & 15;
+      const int m = m0 + r, n = n0 + c * 16;
+      if (m < g.m && n < g.n)
+        *(uint4*)(C8 + (int64_t)m * g.ldc + n) = *(const uint4*)(tile8 + r * 256 + ((c ^ (r & 15)) << 4));
+    }
+    {
+      const int r = tid, m = m0 + r;
+      uint8_t* S = (uint8_t*)g.c_scale + (int64_t)m * g.ld_scale + n0 / 32;
+      if (m < g.m)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (n0 + 32 * j < g.n) S[j] = tsc[r * 8 + j];
+    }
+    return;
+  }
+
   // Store through LDS: the lane holds output row wm*128 + mi*32 + lane%32 and,
   // per N-tile, 4 runs of 4 consecutive columns; those go to the LDS tile, and
   // the tile leaves as whole rows, 16 bytes per lane, consecutive lanes on
@@ -477,6 +535,19 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
   const int num_m = (g.m + BM - 1) / BM, num_n = (g.n + BN - 1) / BN;
   dim3 grid(num_m * num_n, 1, g.batch);
   const int ct = g.c_f32 ? 1 : (g.c_f16 ? 2 : 0);
+  // MXFP8 output: the 256x256 kernel whatever the grid size
+  if (g.c_mx) {
+    const bool ok = !g.b_kn && g.k >= GBK && g.k % GBK == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 && g.n % 32 == 0 &&
+                    g.ldc % 16 == 0 && g.a_bstride % 8 == 0 && g.b_bstride % 8 == 0 &&
+                    (int64_t)GBM * g.lda * 2 < ((int64_t)1 << 31) && (int64_t)GBN * g.ldb * 2 < ((int64_t)1 << 31) &&
+                    (g.epilogue == EPI_STORE ||
+                     (g.epilogue == EPI_ROPE && g.rope_head_stride % 64 == 0 && g.rope_off % 64 == 0));
+    if (!ok) return hipErrorInvalidValue;
+    dim3 gb((unsigned)(((g.m + GBM - 1) / GBM) * ((g.n + GBN - 1) / GBN)), 1, g.batch);
+    if (g.epilogue == EPI_ROPE) gemm_bf16_big_kernel<EPI_ROPE, 3><<<gb, 256, 0, s>>>(g);
+    else gemm_bf16_big_kernel<EPI_STORE, 3><<<gb, 256, 0, s>>>(g);
+    return hipGetLastError();
+  }
   // the 256x256 kernel when its grid covers every CU at least once and the
   // operands suit its copies (K a multiple of 32, 16-byte rows and batch
   // strides, 256 rows of an operand within 32-bit byte offsets)

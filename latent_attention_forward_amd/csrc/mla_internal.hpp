@@ -213,6 +213,10 @@ struct GemmArgs {
   bool c_f32;                                      // true: C stored as fp32
   bool c_f16;                                      // true: C stored as fp16
   int epilogue;                                    // EPI_*
+  // MXFP8 output (after the epilogue): C holds E4M3 codes (ldc in bytes) and
+  // c_scale one E8M0 byte per 32 consecutive columns of a row (row stride
+  // ld_scale bytes); n a multiple of 32
+  bool c_mx; void* c_scale; int64_t ld_scale;
 };
 enum { EPI_STORE = 0, EPI_GATE = 1, EPI_ROPE = 2 };
 

@@ -251,3 +251,69 @@ def test_decode_fp8_dominant_key_takes_the_exact_path(mla):
     ex = om.bf16_excess_error(ref.reshape(B, -1), got.reshape(B, -1))
     _say(f"  all sequences: excess over half an ulp {ex:.3e}")
     assert ex <= EXACT_TOL
+
+
+# ----------------------------------------------------------------------------- MXFP8 query projection
+EPS = 2.0 ** -14
+
+
+def _mx_compare(q, got_c, got_s):
+    """Codes and scales of the GPU against the oracle's MXFP8 rule applied to
+    the float64 q: equal wherever the decision is clear; where the float64
+    value lies within 2^-14 (relative) + 2^-12 X (absolute) of a rounding
+    midpoint, or a block's max within a relative 2^-14 of a power of two, the
+    fp32 product may fall on either side and either neighbour is accepted.
+    Returns (elements excused, blocks excused)."""
+    n, w = q.shape
+    b = q.reshape(n, w // 32, 32)
+    amax = np.abs(b).max(-1)
+    e_lo, e_hi = of.mx_scale_exponent(amax * (1 - EPS)), of.mx_scale_exponent(amax * (1 + EPS))
+    gs = got_s.astype(np.int64) - 127
+    near_s = e_lo != e_hi
+    assert np.array_equal(gs[~near_s], e_lo[~near_s]), "scale mismatch away from a power of two"
+    assert np.all((gs[near_s] == e_lo[near_s]) | (gs[near_s] == e_hi[near_s]))
+    y = b / np.ldexp(1.0, gs)[..., None]                       # the GPU's own block scale
+    # -0 and +0 are the same value (a tiny element's sign may differ)
+    z = lambda c: np.where(c == 0x80, np.uint8(0), c)
+    want = z(of.e4m3_encode(y))
+    # relative, and absolute: the fp32 sum of K = 1536 products is off by
+    # about 1e-6 of the row's values, ~1e-4 in units of X (the block max is
+    # 2^8..2^9 of those units), which moves small elements across a midpoint
+    d = EPS * np.abs(y) + 2.0 ** -12
+    lo, hi = z(of.e4m3_encode(y - d)), z(of.e4m3_encode(y + d))
+    gc = z(got_c.reshape(b.shape))
+    ok = (gc == want) | ((lo != hi) & ((gc == lo) | (gc == hi)))
+    bad = np.argwhere(~ok)
+    assert len(bad) == 0, (len(bad), [(float(y[tuple(i)]), int(gc[tuple(i)]), int(want[tuple(i)])) for i in bad[:6]])
+    return int(((gc != want) & ok).sum()), int(near_s.sum())
+
+
+@pytest.mark.parametrize("name,n", [("dsv3_prefill_4096", 300), ("kimi_gated_varlen_8192", 257),
+                                    ("dsv3_prefill_4096", 4096)])
+def test_q_uproj_rope_mxfp8(mla, name, n):
+    sh = mi.WORKLOADS[name]
+    _say(f"case: MXFP8 query projection {name}, {n} tokens")
+    rng = np.random.default_rng(21)
+    R, H, dqk = sh.q_lora_rank, sh.num_heads, sh.qk_head_dim
+    lat = mi.bf16_round(rng.standard_normal((n, R)).astype(np.float32))
+    w = mi.bf16_round((rng.standard_normal((H * dqk, R)) * 0.02).astype(np.float32))
+    pos = rng.integers(0, 5000, size=n).astype(np.int32)
+    cfg = mla.make_config(sh)
+    rope = sh.rope.kind != "none"
+    cos = sin = None
+    if rope:
+        cos, sin = mla.rope_table(cfg, 5000, DEV)
+    codes = torch.zeros((n, H * dqk), dtype=torch.uint8, device=DEV)
+    scales = torch.full((n, H * dqk // 32), 0xFF, dtype=torch.uint8, device=DEV)
+    mla.q_uproj_rope_mxfp8(cfg, dev(lat, torch.bfloat16), dev(w, torch.bfloat16),
+                           torch.from_numpy(pos).to(DEV) if rope else None, cos, sin, codes, scales)
+    torch.cuda.synchronize()
+    got_c, got_s = codes.cpu().numpy(), scales.cpu().numpy()
+    assert not np.any(got_s == 0xFF)                          # every scale written (0xFF is not an E8M0 value here)
+    rows = np.arange(n) if n <= 512 else np.sort(rng.choice(n, 128, replace=False))
+    q = of.q_uproj_rope(sh, w, lat[rows], pos[rows])
+    ne, nb = _mx_compare(q, got_c[rows], got_s[rows])
+    _say(f"  {len(rows)} rows: codes off by one near a midpoint {ne} of {q.size}, blocks near a power of two {nb}")
+    deq = of.mxfp8_dequantize(got_c[rows], got_s[rows])
+    err = np.abs(deq - q).max() / np.abs(q).max()
+    _say(f"  max |dequantised - q| / max |q| = {err:.3e}")
