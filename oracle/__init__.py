@@ -7,7 +7,7 @@ library (no kernels, headers, tables or helpers); the only module both sides use
 is ``mla_inputs``, which draws the seeded inputs and holds none of the method's
 arithmetic.
 
-Everything is float64 NumPy (``mla.py``, ``fp8.py``) or pure-Python scalar
+Everything is float64 NumPy (``mla.py``, ``fp8.py``, ``backward.py``) or pure-Python scalar
 loops (``brute.py``), written from the pages' statement of the layer:
 
 * "CSDN walkthrough of HF DeepseekV3Attention" (``__init__`` and ``forward``
@@ -45,6 +45,9 @@ from .mla import (  # noqa: F401
     kv_latent, gather_paged, decode_naive, decode_absorbed, prefill_latent_absorbed,
     row_rel_error, bf16_excess_error, prefix_causal_attention, mla_prefill_with_prefix,
     apply_rope_interleaved,
+)
+from .backward import (  # noqa: F401
+    attention_backward, attention_core_backward, rms_norm_backward, rope_backward, mla_prefill_backward,
 )
 from .fp8 import (  # noqa: F401
     e4m3_value, e4m3_encode, cache_inverse_scale, cache_quantize_fp8, cache_dequantize_fp8, decode_absorbed_fp8,
