@@ -63,8 +63,8 @@ def parse():
     ap.add_argument("--chunk", default="dsv3_chunk_4x1024_p4096",
                     help="chunked-prefill workload reported beside the metric ('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["full", "prefill", "attention", "decode", "decode_fp8", "copy", "chunk",
-                                       "chunk_attention", "norm"], default="full",
+    ap.add_argument("--mode", choices=["full", "prefill", "attention", "attention_bwd", "decode", "decode_fp8", "copy",
+                                       "chunk", "chunk_attention", "norm"], default="full",
                     help="full: the JSON line; the others only run that part's timing loop (for profilers)")
     ap.add_argument("--attn-workload", default="dsv3_prefill_4096", choices=ATTN_WORKLOADS,
                     help="workload of --mode attention")
@@ -80,6 +80,14 @@ def attention_flops(shape, cu):
         t = int(b) - int(a)
         s += t * (t + 1) // 2
     return 2 * (shape.qk_head_dim + shape.v_head_dim) * shape.num_heads * s
+
+
+def attention_bwd_flops(shape, cu):
+    """Algorithmic FLOPs of the attention backward: per causal (query, key,
+    head) pair the score recompute and dq, dk (2 d_qk each), dP and dv (2 d_v
+    each), two FLOPs per multiply-add."""
+    dqk, dv = shape.qk_head_dim, shape.v_head_dim
+    return attention_flops(shape, cu) // (dqk + dv) * (3 * dqk + 2 * dv)
 
 
 # Chunked prefill over a cached prefix: (layer shape, new tokens per sequence,
@@ -309,7 +317,22 @@ def main():
         def runner(operand):
             qq, kk, pp = ops[operand]
             return lambda: mla.attention_prefill(cfg, qq, kk, pp, cu, cuh, attn)
-        return {"shape": sh, "cu": cuh, "flops": attention_flops(sh, cuh), "run": runner, "ops": ops}
+
+        def backward():
+            """The attention backward on the bf16 operands, with the forward's
+            bf16 output and a seeded N(0, 1) output gradient."""
+            qq, kk, pp = ops["bf16"]
+            runner("bf16")()
+            o = attn.clone()
+            g = torch.Generator(device=dev).manual_seed(7)
+            do = torch.randn(o.shape, device=dev, generator=g).to(torch.bfloat16)
+            dq = torch.empty(qq.shape, dtype=torch.float32, device=dev)
+            dkv = torch.empty(kk.shape, dtype=torch.float32, device=dev)
+            dkpe = torch.empty(pp.shape, dtype=torch.float32, device=dev)
+            ws = torch.empty(mla.attention_bwd_workspace_size(cfg, n), dtype=torch.uint8, device=dev)
+            return lambda: mla.attention_prefill_bwd(cfg, qq, kk, pp, cu, cuh, o, do, dq, dkv, dkpe, workspace=ws)
+        return {"shape": sh, "cu": cuh, "flops": attention_flops(sh, cuh), "run": runner, "ops": ops,
+                "bwd": backward, "bwd_flops": attention_bwd_flops(sh, cuh)}
 
     # ------------------------------------------------------------------ prefill layer inputs
     sh = mi.WORKLOADS[args.prefill]
@@ -422,6 +445,8 @@ def main():
         # profiler runs: only the requested part, warmup + steps launches, no JSON line
         if args.mode == "attention":
             fn = attention_operands(args.attn_workload)["run"](args.operand)
+        elif args.mode == "attention_bwd":
+            fn = attention_operands(args.attn_workload)["bwd"]()
         elif args.mode == "chunk_attention":
             fn = chunk_attention_operands()
         elif args.mode == "chunk":
@@ -471,6 +496,7 @@ def main():
     # warm-up launches bring the GPU to the kernel's steady state after the
     # layer steps (power and clock state, caches)
     attn_rec = {}
+    bwd_rec = None
     for name in ATTN_WORKLOADS:
         ao = attention_operands(name)
         for operand in (("f16", "bf16") if name == args.prefill else ("f16",)):
@@ -478,6 +504,14 @@ def main():
             tf = ao["flops"] / (ms * 1e-3) / 1e12
             attn_rec[f"{name}/{operand}"] = {"ms": round(ms, 4), "tflops": round(tf, 2),
                                               "frac": round(tf / PEAK_MFMA_TFLOPS, 4), "flops": ao["flops"]}
+        if name == args.prefill:
+            # the attention backward on the same workload (bf16 operands, fp32 gradients)
+            b_ms = timed(ao["bwd"](), args.steps, warm=10)
+            b_tf = ao["bwd_flops"] / (b_ms * 1e-3) / 1e12
+            bwd_rec = {"workload": f"{name}, bf16 operands, fp32 dq / dkv / dkpe", "ms": round(b_ms, 4),
+                       "tflops": round(b_tf, 2), "frac": round(b_tf / PEAK_MFMA_TFLOPS, 4),
+                       "flops_per_launch": ao["bwd_flops"],
+                       "kernel": "mla_attention_prefill_bwd (stats, dq and dk/dv passes + k_pe head sum)"}
         del ao
         torch.cuda.empty_cache()
         print(f"attention {name} done", file=sys.stderr, flush=True)
@@ -603,6 +637,8 @@ def main():
                      "bytes_per_call": d8_bytes}}
     if chunk_rec is not None:
         rec["chunked_prefill"] = chunk_rec
+    if bwd_rec is not None:
+        rec["attention_backward"] = bwd_rec
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(args.prefill, args.decode, args.cpu_budget)
     print(json.dumps(rec), flush=True)

@@ -366,6 +366,37 @@ mla_status mla_decode_absorbed_fwd_noalloc(const mla_config* cfg, const void* w_
                                            const int32_t* seq_lens_dev, const int32_t* seq_lens_host,
                                            int32_t batch, void* out, void* stream);
 
+/* ------------------------------------------------------------------- backward
+ * Backward of the attention core of mla_attention_prefill ("Megatron-LM MLA
+ * guide", training section: the layer is trained end to end; gradients reach
+ * the query, the per-head k_nope and v of the latent and the one shared k_pe).
+ * With S = scale [q_nope|q_pe] [k_nope|k_pe]^T per head, causal within each
+ * document, P = softmax(S), O = P v and the output gradient dO:
+ *   dv = P^T dO, dP = dO v^T, dS = P * (dP - rowsum(dO * O)),
+ *   dq = scale dS k, dk = scale dS^T q, dk_pe = sum over heads of dk's rope part.
+ * bf16 config and head shape only (d_nope 128, d_rope 64, d_v 128).
+ *   q, kv, kpe, kpe_stride, cu_seqlens: the forward's bf16 operands, as for
+ *          mla_attention_prefill (MLA_BF16 operands)
+ *   out    [N, H, d_v] bf16, the forward's output for these operands; D =
+ *          rowsum(dO * out) is formed from it as given
+ *   dout   [N, H, d_v] bf16, the gradient of the output
+ *   dq     [N, H, d_nope + d_rope] fp32, dkv [N, H, d_nope + d_v] fp32
+ *          (per head [dk_nope | dv]), dkpe [N, d_rope] fp32 — all DEVICE,
+ *          16-byte aligned, written completely
+ *   workspace: DEVICE, >= mla_attention_bwd_workspace_size(cfg, N) bytes.
+ * The forward's softmax statistics are recomputed (one extra QK^T pass); P
+ * and dS are rounded to bf16 as MFMA operands, accumulation is fp32.
+ * Errors: MLA_ERR_UNSUPPORTED for another dtype or head shape, more than
+ * 65535 documents or a document longer than 65535 * 128 tokens;
+ * MLA_ERR_INVALID_ARG for a missing pointer or bad offsets; MLA_ERR_MISALIGNED;
+ * MLA_ERR_WORKSPACE for a missing or short workspace.  N = 0 is a no-op. */
+size_t mla_attention_bwd_workspace_size(const mla_config* cfg, int32_t num_tokens);
+mla_status mla_attention_prefill_bwd(const mla_config* cfg, const void* q, const void* kv, const void* kpe,
+                                     int64_t kpe_stride, const int32_t* cu_seqlens_dev,
+                                     const int32_t* cu_seqlens_host, int32_t num_seqs, const void* out,
+                                     const void* dout, void* dq, void* dkv, void* dkpe, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------- FP8 (E4M3) latent cache
  * The pages name FP8 only as the MXFP8 recipe of "Megatron-LM MLA guide"
  * (parameter section: use_fused_mla_q_uproj, fp8_dot_product_attention) and

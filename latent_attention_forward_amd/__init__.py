@@ -70,6 +70,8 @@ _SIGNATURES = {
     "mla_decode_absorbed_fwd_noalloc": (_I32, [_CFG, _P, _P, _P, _P, _I32, _I32, _P, _I32, _P, _P, _I32, _P, _P]),
     "mla_prefill_chunk_workspace_size": (_SZ, [_CFG, _P, _P, _I32]),
     "mla_decode_fp8_workspace_size": (_SZ, [_CFG, _P, _I32]),
+    "mla_attention_bwd_workspace_size": (_SZ, [_CFG, _I32]),
+    "mla_attention_prefill_bwd": (_I32, [_CFG, _P, _P, _P, _I64, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mla_q_uproj_rope_mxfp8": (_I32, [_CFG, _P, _I64, _I32, _P, _P, _P, _P, _I32, _P, _P, _P]),
     "mla_cache_quantize_fp8": (_I32, [_P, _I64, _I64, _I32, ctypes.c_float, _P, _I64, _P]),
     "mla_decode_absorbed_fp8_fwd": (_I32, [_CFG, _P, _P, _P, _P, ctypes.c_float, _I32, _I32, _P, _I32, _P, _P, _I32,
@@ -405,6 +407,33 @@ def cache_quantize_fp8(src, scale: float, dst, stream=None):
     _check(load_library().mla_cache_quantize_fp8(_ptr(src, dtype=torch.bfloat16, name="src"), width, rows, width,
                                                  float(scale), _ptr(dst, dtype=torch.uint8, name="dst"), width,
                                                  _stream(stream)), "mla_cache_quantize_fp8")
+
+
+def attention_bwd_workspace_size(cfg: MlaConfig, num_tokens: int) -> int:
+    """Bytes of workspace ``mla_attention_prefill_bwd`` needs for N tokens."""
+    return int(load_library().mla_attention_bwd_workspace_size(ctypes.byref(cfg), int(num_tokens)))
+
+
+def attention_prefill_bwd(cfg: MlaConfig, q, kv, kpe, cu_seqlens_dev, cu_seqlens_host: Sequence[int], out, dout,
+                          dq, dkv, dkpe, workspace=None, stream=None):
+    """Backward of the attention core (``mla_attention_prefill_bwd``): bf16
+    q [N, H, 192], kv [N, H, 256], kpe [N, 64] (row-strided), out and dout
+    [N, H, 128]; fp32 dq [N, H, 192], dkv [N, H, 256], dkpe [N, 64]."""
+    import numpy as np
+    import torch
+    lib = load_library()
+    cuh = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int32))
+    n = int(cuh[-1])
+    st = _resolve_stream(stream)
+    ws = _workspace(int(lib.mla_attention_bwd_workspace_size(ctypes.byref(cfg), n)), q.device, workspace, st)
+    bf, f32 = torch.bfloat16, torch.float32
+    _check(lib.mla_attention_prefill_bwd(
+        ctypes.byref(cfg), _ptr(q, dtype=bf, name="q"), _ptr(kv, dtype=bf, name="kv"),
+        _ptr(kpe, rows=True, dtype=bf, name="kpe"), kpe.stride(0), _ptr(cu_seqlens_dev, dtype=_i32(), name="cu"),
+        cuh.ctypes.data, len(cuh) - 1, _ptr(out, dtype=bf, name="out"), _ptr(dout, dtype=bf, name="dout"),
+        _ptr(dq, dtype=f32, name="dq"), _ptr(dkv, dtype=f32, name="dkv"), _ptr(dkpe, dtype=f32, name="dkpe"),
+        _ptr(ws), ws.numel(), st.cuda_stream), "mla_attention_prefill_bwd")
+    return ws
 
 
 def q_uproj_rope_mxfp8(cfg: MlaConfig, q_latent, w_q_b, positions, rope_cos, rope_sin, q_codes, q_scales,

@@ -870,6 +870,52 @@ mla_status mla_decode_absorbed_fp8_fwd(const mla_config* cfg, const void* w_kv_b
   return s == MLA_OK ? ok() : s;
 }
 
+size_t mla_attention_bwd_workspace_size(const mla_config* cfg, int32_t num_tokens) {
+  if (check_config(cfg) != MLA_OK || num_tokens < 0) return 0;
+  const size_t n = (size_t)num_tokens, H = (size_t)cfg->num_heads;
+  return align256(n * H * 4) * 2 + align256(n * H * (size_t)cfg->qk_rope_dim * 4);
+}
+
+mla_status mla_attention_prefill_bwd(const mla_config* cfg, const void* q, const void* kv, const void* kpe,
+                                     int64_t kpe_stride, const int32_t* cu_seqlens_dev,
+                                     const int32_t* cu_seqlens_host, int32_t num_seqs, const void* out,
+                                     const void* dout, void* dq, void* dkv, void* dkpe, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  mla_status s = check_config(cfg);
+  if (s != MLA_OK) return s;
+  if (cfg->dtype != MLA_BF16) return fail(MLA_ERR_UNSUPPORTED, "the attention backward is compiled for bf16 only");
+  if ((s = check_supported(cfg)) != MLA_OK) return s;
+  int n = 0;
+  if ((s = check_cu(cu_seqlens_host, num_seqs, &n)) != MLA_OK) return s;
+  if (n == 0) return ok();
+  if (num_seqs > 65535) return fail(MLA_ERR_UNSUPPORTED, "the attention backward takes at most 65535 documents");
+  for (int d = 0; d < num_seqs; ++d)
+    if (cu_seqlens_host[d + 1] - cu_seqlens_host[d] > 65535 * 128)
+      return fail(MLA_ERR_UNSUPPORTED, "the attention backward takes documents of at most 65535 * 128 tokens");
+  if (!q || !kv || !kpe || !cu_seqlens_dev || !out || !dout || !dq || !dkv || !dkpe)
+    return fail(MLA_ERR_INVALID_ARG, "q, kv, kpe, cu_seqlens_dev, out, dout, dq, dkv and dkpe are required");
+  if (kpe_stride < cfg->qk_rope_dim) return fail(MLA_ERR_INVALID_ARG, "kpe_stride < d_rope");
+  const void* ptrs[] = {q, kv, kpe, out, dout, dq, dkv, dkpe};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(MLA_ERR_MISALIGNED, "the attention backward needs 16-byte aligned tensors");
+  if (kpe_stride % 8) return fail(MLA_ERR_MISALIGNED, "kpe_stride must be a multiple of 8");
+  const size_t need = mla_attention_bwd_workspace_size(cfg, n);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace))
+    return fail(MLA_ERR_WORKSPACE, "an aligned workspace of %zu bytes is needed", need);
+  const size_t H = (size_t)cfg->num_heads;
+  char* ws = (char*)workspace;
+  AttnBwdArgs a{};
+  a.q = q; a.kv = kv; a.kpe = kpe; a.kpe_stride = kpe_stride; a.o = out; a.dout = dout;
+  a.cu_dev = cu_seqlens_dev; a.n_tokens = n; a.heads = cfg->num_heads; a.scale = scale_of(cfg);
+  a.lse = (float*)ws;
+  a.dsum = (float*)(ws + align256((size_t)n * H * 4));
+  a.dkr = (float*)(ws + 2 * align256((size_t)n * H * 4));
+  a.dq = (float*)dq; a.dkv = (float*)dkv; a.dkpe = (float*)dkpe;
+  const hipError_t e = launch_attention_bwd(a, cu_seqlens_host, num_seqs, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attention backward launch");
+  return ok();
+}
+
 mla_status mla_q_uproj_rope_mxfp8(const mla_config* cfg, const void* q_latent, int64_t ldq, int32_t n_tokens,
                                   const void* w_q_b, const int32_t* positions, const float* rope_cos,
                                   const float* rope_sin, int32_t rope_table_len, void* q_codes, void* q_scales,

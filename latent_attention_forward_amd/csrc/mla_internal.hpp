@@ -274,6 +274,17 @@ hipError_t launch_flash_mfma(const FlashArgs& a, bool f16_operands, const int32_
                              int num_seqs, hipStream_t s);
 hipError_t launch_flash_f32(const FlashArgs& a, hipStream_t s);
 
+// Backward of the bf16 attention core (nope 128, rope 64, dv 128): bf16
+// operands, fp32 gradients; lse / dsum / dkr are scratch.
+struct AttnBwdArgs {
+  const void* q; const void* kv; const void* kpe; int64_t kpe_stride;
+  const void* o; const void* dout;
+  const int32_t* cu_dev; int n_tokens; int heads; float scale;
+  float* lse; float* dsum; float* dkr;                 // [N, H], [N, H], [N, H, 64]
+  float* dq; float* dkv; float* dkpe;                  // [N, H, 192], [N, H, 256], [N, 64]
+};
+hipError_t launch_attention_bwd(const AttnBwdArgs& a, const int32_t* cu_host, int num_seqs, hipStream_t s);
+
 // Most paged-cache blocks one decode segment may span (its block ids are staged in LDS).
 constexpr int kDecodeMaxChunkBlocks = 512;
 // Placeholder keys ahead of each sequence in the decode work order: the work

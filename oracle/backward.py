@@ -32,11 +32,16 @@ import numpy as np
 from .mla import (_f64, _out_proj, _positions, _rope, _softmax_rows, rms_norm, rope_cos_sin, softmax_scale)
 
 
-def attention_backward(q, k, v, scale: float, cu_seqlens, dout):
+def attention_backward(q, k, v, scale: float, cu_seqlens, dout, out=None):
     """(dq, dk, dv, lse) of ``causal_varlen_attention(q, k, v, scale, cu)``
     for the output gradient dout [N, H, d_v]; k is per head here.  lse is the
-    natural-log log-sum-exp of each (row, head)'s scaled scores."""
+    natural-log log-sum-exp of each (row, head)'s scaled scores.
+
+    ``out`` is the forward output as handed to the backward (for instance
+    stored in bf16 by the forward); D = rowsum(dout * out) is formed from it.
+    None recomputes it exactly, giving the true gradient."""
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    out = None if out is None else _f64(out)
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     n, h, _ = q.shape
     dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
@@ -59,6 +64,8 @@ def attention_backward(q, k, v, scale: float, cu_seqlens, dout):
         o = np.matmul(p, vd)
         dvd = np.matmul(np.transpose(p, (0, 2, 1)), gd)
         dp = np.matmul(gd, np.transpose(vd, (0, 2, 1)))
+        if out is not None:
+            o = np.transpose(out[a:b], (1, 0, 2))
         D = np.sum(gd * o, axis=-1, keepdims=True)
         ds = p * (dp - D)
         dq[a:b] = np.transpose(scale * np.matmul(ds, kd), (1, 0, 2))
@@ -186,13 +193,14 @@ def mla_prefill_backward(shape, w: Dict[str, np.ndarray], x, cu_seqlens, dout) -
     return grads
 
 
-def attention_core_backward(q, kv, kpe, scale: float, cu_seqlens, dout, nope: int):
+def attention_core_backward(q, kv, kpe, scale: float, cu_seqlens, dout, nope: int, out=None):
     """Backward of the attention core as the library computes it: q
     [N, H, nope + rope], kv [N, H, nope + d_v] = per head [k_nope | v], kpe
-    [N, rope] the one shared key part.  Returns (dq [N, H, nope + rope], dkv
+    [N, rope] the one shared key part, ``out`` the forward output the caller
+    hands over (None: exact).  Returns (dq [N, H, nope + rope], dkv
     [N, H, nope + d_v], dkpe [N, rope] summed over heads, lse [N, H])."""
     q, kv, kpe = _f64(q), _f64(kv), _f64(kpe)
     n, H, _ = q.shape
     k = np.concatenate([kv[..., :nope], np.broadcast_to(kpe[:, None, :], (n, H, kpe.shape[-1]))], axis=-1)
-    dq, dk, dv, lse = attention_backward(q, k, kv[..., nope:], scale, cu_seqlens, dout)
+    dq, dk, dv, lse = attention_backward(q, k, kv[..., nope:], scale, cu_seqlens, dout, out)
     return dq, np.concatenate([dk[..., :nope], dv], axis=-1), np.sum(dk[..., nope:], axis=1), lse

@@ -175,6 +175,22 @@ def test_device_calls_reject_bad_arguments_before_launch(lib):
     assert q(4096, 576, 10, 576, 1.0, 8196, 576, None) == mla.MLA_ERR_MISALIGNED
     assert q(4096, 576, 10, 576, 1.0, None, 576, None) == mla.MLA_ERR_INVALID_ARG
     assert q(4096, 576, 0, 576, 1.0, 8192, 576, None) == mla.MLA_OK   # nothing to convert
+    # attention backward: dtype, missing pointers, alignment, workspace
+    b = lib.mla_attention_prefill_bwd
+    cu2 = np.array([0, 100, 300], np.int32)
+    args = lambda **kw: [kw.get(k, 4096) for k in ("q", "kv", "kpe")] + [kw.get("kpe_stride", 576), 4096,
+                                                                          cu2.ctypes.data, 2] + \
+        [kw.get(k, 4096) for k in ("out", "dout", "dq", "dkv", "dkpe", "ws")] + [kw.get("wsb", 1 << 30), None]
+    assert b(ctypes.byref(f32), *args()) == mla.MLA_ERR_UNSUPPORTED
+    assert b(ctypes.byref(cfg), *args(dout=None)) == mla.MLA_ERR_INVALID_ARG
+    assert b(ctypes.byref(cfg), *args(kpe_stride=32)) == mla.MLA_ERR_INVALID_ARG
+    assert b(ctypes.byref(cfg), *args(dq=4100)) == mla.MLA_ERR_MISALIGNED
+    assert b(ctypes.byref(cfg), *args(kpe_stride=580)) == mla.MLA_ERR_MISALIGNED
+    assert b(ctypes.byref(cfg), *args(wsb=16)) == mla.MLA_ERR_WORKSPACE
+    assert mla.attention_bwd_workspace_size(cfg, 300) == 2 * 153600 + 300 * 128 * 64 * 4
+    empty = np.array([0, 0], np.int32)
+    assert b(ctypes.byref(cfg), None, None, None, 576, None, empty.ctypes.data, 1, None, None, None, None, None,
+             None, 0, None) == mla.MLA_OK
     # norm/rope: rope slices overlapping the norm region, slot mapping in place
     st = lib.mla_latent_norm_rope(ctypes.byref(cfg), 4096, 576, 4, 576, 512, 4096, 500, 1, 64, 4096, 4096, 16, 4096,
                                   8192, 576, None, 0, None)

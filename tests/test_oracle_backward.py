@@ -109,6 +109,34 @@ def test_attention_core_gradients_match_finite_differences():
     assert np.allclose(lse[10], np.log(np.sum(np.exp(s), axis=-1)))
 
 
+def test_attention_backward_with_given_output_moves_linearly_in_D():
+    """The backward formed with a forward output other than the exact one
+    (as stored in bf16 by a forward): D = rowsum(dO * out) enters
+    dS = P (dP - D) linearly, so with out' = out + delta and
+    dD = rowsum(dO * delta): dq' - dq = -scale dD (P k), the forward attention
+    with k in place of v; dk' - dk = -scale P^T (dD q), the dv formula with q
+    in place of dO's values; dv unchanged."""
+    rng = np.random.default_rng(11)
+    n, H, dqk, dv_ = 23, 2, 10, 6
+    cu = np.array([0, 1, 9, 23])
+    q, k, v = rng.standard_normal((n, H, dqk)), rng.standard_normal((n, H, dqk)), rng.standard_normal((n, H, dv_))
+    dout = rng.standard_normal((n, H, dv_))
+    scale = 0.4
+    exact = ob.attention_backward(q, k, v, scale, cu, dout)
+    o = om.causal_varlen_attention(q, k, v, scale, cu)
+    same = ob.attention_backward(q, k, v, scale, cu, dout, out=o)
+    for a, b in zip(exact, same):
+        assert np.allclose(a, b, rtol=1e-13, atol=1e-13)
+    delta = 1e-2 * rng.standard_normal(o.shape)
+    dq2, dk2, dv2, _ = ob.attention_backward(q, k, v, scale, cu, dout, out=o + delta)
+    dD = np.sum(dout * delta, axis=-1)
+    pk = om.causal_varlen_attention(q, k, k, scale, cu)
+    assert np.allclose(dq2 - exact[0], -scale * dD[..., None] * pk, rtol=1e-10, atol=1e-12)
+    _, _, ptq, _ = ob.attention_backward(q, k, q, scale, cu, dD[..., None] * q)
+    assert np.allclose(dk2 - exact[1], -scale * ptq, rtol=1e-10, atol=1e-12)
+    assert np.array_equal(dv2, exact[2])
+
+
 # ----------------------------------------------------------------------------- planted mistakes
 def _planted(monkeypatch, which):
     if which == "no_D_term":
