@@ -63,8 +63,8 @@ def parse():
     ap.add_argument("--chunk", default="dsv3_chunk_4x1024_p4096",
                     help="chunked-prefill workload reported beside the metric ('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["full", "prefill", "attention", "attention_bwd", "decode", "decode_fp8", "copy",
-                                       "chunk", "chunk_attention", "norm"], default="full",
+    ap.add_argument("--mode", choices=["full", "prefill", "prefill_bwd", "attention", "attention_bwd", "decode",
+                                       "decode_fp8", "copy", "chunk", "chunk_attention", "norm"], default="full",
                     help="full: the JSON line; the others only run that part's timing loop (for profilers)")
     ap.add_argument("--attn-workload", default="dsv3_prefill_4096", choices=ATTN_WORKLOADS,
                     help="workload of --mode attention")
@@ -437,6 +437,20 @@ def main():
         ck = torch.from_numpy(ck_h).to(dev)
         return lambda: mla.attention_prefix(c["cfg"], qa, kva, kpe, c["cu"], c["cu_h"], ck, ck_h, attn)
 
+    # the layer backward on the same layer (seeded N(0, 1) output gradient)
+    lbw = {}
+
+    def prefill_bwd():
+        if not lbw:
+            g = torch.Generator(device=dev).manual_seed(11)
+            lbw["dout"] = torch.randn(n, sh.hidden, device=dev, generator=g).to(torch.bfloat16)
+            lbw["dx"] = torch.empty(n, sh.hidden, dtype=torch.float32, device=dev)
+            lbw["grads"] = {k: torch.empty(v.shape, dtype=torch.float32, device=dev) for k, v in W.items()
+                            if v is not None and not (k == "w_o" and sh.o_groups)}
+            lbw["ws"] = torch.empty(mla.prefill_bwd_workspace_size(cfg, n), dtype=torch.uint8, device=dev)
+        mla.prefill_bwd(cfg, W, x, cu, cuh, lbw["dout"], lbw["dx"], lbw["grads"], rope_cos=cos, rope_sin=sin,
+                        workspace=lbw["ws"])
+
     def step():
         prefill()
         decode()
@@ -460,6 +474,8 @@ def main():
             fn = lambda: dst.copy_(src)
         elif args.mode == "decode_fp8":
             fn = decode_fp8
+        elif args.mode == "prefill_bwd":
+            fn = prefill_bwd
         else:
             fn = prefill if args.mode == "prefill" else decode
         flush = torch.zeros(512 << 20, dtype=torch.uint8, device=dev) if args.mode in ("decode", "decode_fp8") else None
@@ -517,6 +533,18 @@ def main():
         print(f"attention {name} done", file=sys.stderr, flush=True)
     head = attn_rec[f"{args.prefill}/f16"]
     attn_ms, attn_tflops, a_flops = head["ms"], head["tflops"], head["flops"]
+
+    # ------------------------------------------------------------------ layer backward (recompute + chain rule)
+    lb_ms = timed(prefill_bwd, max(3, args.steps // 4), warm=2)
+    lb_flops = 2 * layer_flops(sh, n, 0) + attention_bwd_flops(sh, cuh)
+    lbw.clear()
+    torch.cuda.empty_cache()
+    layer_bwd_rec = {"workload": f"{args.prefill}, bf16, fp32 dx and weight gradients", "ms": round(lb_ms, 3),
+                     "tflops": round(lb_flops / (lb_ms * 1e-3) / 1e12, 2),
+                     "frac": round(lb_flops / (lb_ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
+                     "flops_per_call": lb_flops,
+                     "flops_counted": "dX and dW of every projection (twice the forward's) + the attention backward; "
+                                      "the forward recompute inside the call is not counted"}
 
     # ------------------------------------------------------------------ fused query up-projection + RoPE + MXFP8
     mxq = None
@@ -639,6 +667,7 @@ def main():
         rec["chunked_prefill"] = chunk_rec
     if bwd_rec is not None:
         rec["attention_backward"] = bwd_rec
+    rec["layer_backward"] = layer_bwd_rec
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(args.prefill, args.decode, args.cpu_budget)
     print(json.dumps(rec), flush=True)

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 4
+#define MLA_ABI_VERSION 5
 
 typedef enum mla_status {
   MLA_OK = 0,
@@ -396,6 +396,57 @@ mla_status mla_attention_prefill_bwd(const mla_config* cfg, const void* q, const
                                      const int32_t* cu_seqlens_host, int32_t num_seqs, const void* out,
                                      const void* dout, void* dq, void* dkv, void* dkpe, void* workspace,
                                      size_t workspace_bytes, void* stream);
+
+/* Gradients of the layer's weights (mla_prefill_bwd): fp32 DEVICE arrays of
+ * the shapes of the mla_weights fields of the same name, 16-byte aligned;
+ * those the configuration does not use are NULL. */
+typedef struct mla_weight_grads {
+  float* w_q_a;
+  float* q_a_gamma;
+  float* w_q_b;
+  float* w_q;
+  float* w_kv_a;
+  float* kv_a_gamma;
+  float* w_kv_b;
+  float* w_o;
+  float* w_g;
+  float* w_o_a;
+  float* w_o_b;
+} mla_weight_grads;
+
+/* Backward of the whole prefill layer ("Megatron-LM MLA guide", training
+ * section: the layer is trained end to end, its weight gradients including
+ * the ones backward_dw produces; the pages print no backward formulas, so it
+ * is the chain rule through the forward of mla_prefill_fwd):
+ *   output projection (plain or grouped low-rank): dW = dout^T A2, dA2;
+ *   gate: dA = dA2 sigmoid(g), dg = dA2 A sigmoid(g) (1 - sigmoid(g)), dW_g;
+ *   attention core: mla_attention_prefill_bwd;
+ *   RoPE: the rotation by -theta of the q and k_pe gradients;
+ *   kv up-projection: dW_kv_b = dkv^T c_n, dc_n = dkv W_kv_b (through the
+ *     latent: every head's k_nope / v gradient reaches the one latent row);
+ *   RMSNorm: dx = g dy / r - x mean(g dy x) / r^3, dgamma = sum_rows dy x / r;
+ *   down-projections: dW = dY^T x, and dx = sum of dY W over the projections
+ *     that read x.
+ * The forward is recomputed inside the call (activation recomputation), with
+ * bf16 attention operands whatever cfg->attn_operand says.  bf16 config only.
+ *   w, x, cu_seqlens, positions, rope tables: as for mla_prefill_fwd
+ *   dout   [N, hidden] bf16 DEVICE, the gradient of the layer output
+ *   dx     [N, hidden] fp32 DEVICE, written (not accumulated)
+ *   dw     the weight gradients (fp32, written, not accumulated)
+ *   workspace: DEVICE, >= mla_prefill_bwd_workspace_size(cfg, N) bytes.
+ * Gradients are fp32 sums of products of bf16 operands: every GEMM operand,
+ * the attention's P and dS, and the gradients between the steps are rounded
+ * to bf16 once.
+ * Errors: MLA_ERR_UNSUPPORTED for an fp32 config or an unsupported head
+ * shape; MLA_ERR_INVALID_ARG for a missing tensor (any weight gradient the
+ * configuration uses included); MLA_ERR_MISALIGNED; MLA_ERR_WORKSPACE.  N = 0
+ * is a no-op. */
+size_t mla_prefill_bwd_workspace_size(const mla_config* cfg, int32_t num_tokens);
+mla_status mla_prefill_bwd(const mla_config* cfg, const mla_weights* w, const void* x, const int32_t* cu_seqlens_dev,
+                           const int32_t* cu_seqlens_host, int32_t num_seqs, const int32_t* positions_dev,
+                           const float* rope_cos, const float* rope_sin, int32_t rope_table_len, const void* dout,
+                           float* dx, const mla_weight_grads* dw, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /* ---------------------------------------------------- FP8 (E4M3) latent cache
  * The pages name FP8 only as the MXFP8 recipe of "Megatron-LM MLA guide"

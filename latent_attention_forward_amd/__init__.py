@@ -45,6 +45,10 @@ class MlaWeights(ctypes.Structure):
                  "w_o_b")]
 
 
+class MlaWeightGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n, _ in MlaWeights._fields_]
+
+
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
@@ -71,6 +75,9 @@ _SIGNATURES = {
     "mla_prefill_chunk_workspace_size": (_SZ, [_CFG, _P, _P, _I32]),
     "mla_decode_fp8_workspace_size": (_SZ, [_CFG, _P, _I32]),
     "mla_attention_bwd_workspace_size": (_SZ, [_CFG, _I32]),
+    "mla_prefill_bwd_workspace_size": (_SZ, [_CFG, _I32]),
+    "mla_prefill_bwd": (_I32, [_CFG, ctypes.POINTER(MlaWeights), _P, _P, _P, _I32, _P, _P, _P, _I32, _P, _P,
+                               ctypes.POINTER(MlaWeightGrads), _P, _SZ, _P]),
     "mla_attention_prefill_bwd": (_I32, [_CFG, _P, _P, _P, _I64, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mla_q_uproj_rope_mxfp8": (_I32, [_CFG, _P, _I64, _I32, _P, _P, _P, _P, _I32, _P, _P, _P]),
     "mla_cache_quantize_fp8": (_I32, [_P, _I64, _I64, _I32, ctypes.c_float, _P, _I64, _P]),
@@ -347,6 +354,39 @@ def prefill_fwd(cfg: MlaConfig, weights: Dict[str, object], x, cu_seqlens_dev, c
                                table_len, _ptr(out, dtype=act, name="out"),
                                _ptr(latent_out, dtype=act, name="latent_out"), _ptr(ws), ws.numel(),
                                st.cuda_stream), "mla_prefill_fwd")
+    return ws
+
+
+def prefill_bwd_workspace_size(cfg: MlaConfig, num_tokens: int) -> int:
+    """Bytes of workspace ``mla_prefill_bwd`` needs for N tokens."""
+    return int(load_library().mla_prefill_bwd_workspace_size(ctypes.byref(cfg), int(num_tokens)))
+
+
+def prefill_bwd(cfg: MlaConfig, weights: Dict[str, object], x, cu_seqlens_dev, cu_seqlens_host: Sequence[int],
+                dout, dx, grads: Dict[str, object], positions=None, rope_cos=None, rope_sin=None, workspace=None,
+                stream=None):
+    """Backward of the prefill layer (``mla_prefill_bwd``): bf16 x, dout
+    [N, hidden] and weights as for ``prefill_fwd``; fp32 dx [N, hidden] and
+    ``grads``, a dict of fp32 device tensors named and shaped as the weights
+    the configuration uses."""
+    import numpy as np
+    lib = load_library()
+    act, i32, f32 = _act(cfg), _i32(), _f32()
+    cuh = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int32))
+    n, s = int(cuh[-1]), len(cuh) - 1
+    st = _resolve_stream(stream)
+    ws = _workspace(prefill_bwd_workspace_size(cfg, n), x.device, workspace, st)
+    mw = make_weights(weights, act)
+    mg = MlaWeightGrads()
+    for name, _ in MlaWeightGrads._fields_:
+        setattr(mg, name, _ptr(grads.get(name), dtype=f32, name="d" + name))
+    table_len = 0 if rope_cos is None else rope_cos.shape[0]
+    _check(lib.mla_prefill_bwd(ctypes.byref(cfg), ctypes.byref(mw), _ptr(x, dtype=act, name="x"),
+                               _ptr(cu_seqlens_dev, dtype=i32, name="cu_seqlens_dev"), cuh.ctypes.data, s,
+                               _ptr(positions, dtype=i32, name="positions"),
+                               _ptr(rope_cos, dtype=f32, name="rope_cos"), _ptr(rope_sin, dtype=f32, name="rope_sin"),
+                               table_len, _ptr(dout, dtype=act, name="dout"), _ptr(dx, dtype=f32, name="dx"),
+                               ctypes.byref(mg), _ptr(ws), ws.numel(), st.cuda_stream), "mla_prefill_bwd")
     return ws
 
 

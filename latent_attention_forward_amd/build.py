@@ -11,7 +11,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libmla.so")
-SOURCES = ["api.hip", "gemm.hip", "norm_rope.hip", "flash.hip", "decode.hip", "decode_fp8.hip", "attn_bwd.hip", "chunk.hip"]
+SOURCES = ["api.hip", "gemm.hip", "norm_rope.hip", "flash.hip", "decode.hip", "decode_fp8.hip", "attn_bwd.hip", "layer_bwd.hip", "chunk.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -916,6 +916,291 @@ mla_status mla_attention_prefill_bwd(const mla_config* cfg, const void* q, const
   return ok();
 }
 
+// ---------------------------------------------------------------- layer backward
+namespace {
+struct LayerBwdWs {
+  size_t pos, q_lat32, q_lat, q, ckv32, lat, kv, attn, gpre, a2, ot, dt, da2, da, dg, dq32, dkv32, dkpe32, abw,
+      dq16, dkv16, dckv, dcn32, dqln32, dql16, rinv, part, tr, total;
+  int64_t npad;
+};
+
+LayerBwdWs layer_bwd_layout(const mla_config* c, int64_t n) {
+  const int64_t H = c->num_heads, rq = c->q_lora_rank, rkv = c->kv_lora_rank, dr = c->qk_rope_dim;
+  const int64_t dqk = c->qk_nope_dim + dr, dkv = c->qk_nope_dim + c->v_head_dim, F = H * c->v_head_dim;
+  const int64_t lw = rkv + dr, gro = c->o_groups > 0 ? (int64_t)c->o_groups * c->o_lora_rank : 0;
+  LayerBwdWs w{};
+  w.npad = (n + 63) / 64 * 64;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off += align256(bytes); return o; };
+  w.pos = take(n * 4);
+  w.q_lat32 = take(n * rq * 4);
+  w.q_lat = take(n * rq * 2);
+  w.q = take(n * H * dqk * 2);
+  w.ckv32 = take(n * lw * 4);
+  w.lat = take(n * lw * 2);
+  w.kv = take(n * H * dkv * 2);
+  w.attn = take(n * F * 2);
+  w.gpre = take(c->output_gate ? n * F * 4 : 0);
+  w.a2 = take(c->output_gate ? n * F * 2 : 0);
+  w.ot = take(n * gro * 2);
+  w.dt = take(n * gro * 2);
+  w.da2 = take(n * F * 4);
+  w.da = take(n * F * 2);
+  w.dg = take(c->output_gate ? n * F * 2 : 0);
+  w.dq32 = take(n * H * dqk * 4);
+  w.dkv32 = take(n * H * dkv * 4);
+  w.dkpe32 = take(n * dr * 4);
+  w.abw = take(mla_attention_bwd_workspace_size(c, (int32_t)n));
+  w.dq16 = take(n * H * dqk * 2);
+  w.dkv16 = take(n * H * dkv * 2);
+  w.dckv = take(n * lw * 2);
+  w.dcn32 = take(n * rkv * 4);
+  w.dqln32 = take(n * rq * 4);
+  w.dql16 = take(n * rq * 2);
+  w.rinv = take(n * 4);
+  w.part = take((n + 255) / 256 * std::max(rkv, rq) * 4);
+  const int64_t tcols = std::max({(int64_t)c->hidden, F, H * dkv, H * dqk, lw, rq, gro});
+  w.tr = take(tcols * w.npad * 2);
+  w.total = off;
+  return w;
+}
+}  // namespace
+
+size_t mla_prefill_bwd_workspace_size(const mla_config* cfg, int32_t num_tokens) {
+  if (check_config(cfg) != MLA_OK || num_tokens < 0) return 0;
+  return layer_bwd_layout(cfg, num_tokens).total;
+}
+
+mla_status mla_prefill_bwd(const mla_config* cfg, const mla_weights* w, const void* x, const int32_t* cu_seqlens_dev,
+                           const int32_t* cu_seqlens_host, int32_t num_seqs, const int32_t* positions_dev,
+                           const float* rope_cos, const float* rope_sin, int32_t rope_table_len, const void* dout,
+                           float* dx, const mla_weight_grads* dw, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  mla_status s = check_config(cfg);
+  if (s != MLA_OK) return s;
+  if (cfg->dtype != MLA_BF16) return fail(MLA_ERR_UNSUPPORTED, "the layer backward is compiled for bf16 only");
+  if ((s = check_supported(cfg)) != MLA_OK) return s;
+  if ((s = check_weights(cfg, w)) != MLA_OK) return s;
+  int n = 0;
+  if ((s = check_cu(cu_seqlens_host, num_seqs, &n)) != MLA_OK) return s;
+  if (n == 0) return ok();
+  if (!x || !dout || !dx || !cu_seqlens_dev || !dw)
+    return fail(MLA_ERR_INVALID_ARG, "x, dout, dx, dw and cu_seqlens_dev are required");
+  const bool rope = cfg->rope_kind != MLA_ROPE_NONE;
+  if (rope && (!rope_cos || !rope_sin || rope_table_len <= 0))
+    return fail(MLA_ERR_INVALID_ARG, "RoPE needs device cos/sin tables and their length");
+  const int H = cfg->num_heads, hid = cfg->hidden, rq = cfg->q_lora_rank, rkv = cfg->kv_lora_rank;
+  const int dn = cfg->qk_nope_dim, dr = cfg->qk_rope_dim, dv = cfg->v_head_dim, dqk = dn + dr, lw = rkv + dr;
+  const int dkvw = dn + dv, F = H * dv, G = cfg->o_groups, ro = cfg->o_lora_rank, gro = G > 0 ? G * ro : 0;
+  const int fg = G > 0 ? F / G : 0;
+  // the weight gradients this configuration needs
+  struct Need { const void* have; const char* name; };
+  const Need need[] = {
+      {rq > 0 ? dw->w_q_a : (void*)1, "w_q_a"}, {rq > 0 ? dw->q_a_gamma : (void*)1, "q_a_gamma"},
+      {rq > 0 ? dw->w_q_b : (void*)1, "w_q_b"}, {rq == 0 ? dw->w_q : (void*)1, "w_q"},
+      {dw->w_kv_a, "w_kv_a"}, {dw->kv_a_gamma, "kv_a_gamma"}, {dw->w_kv_b, "w_kv_b"},
+      {G == 0 ? dw->w_o : (void*)1, "w_o"}, {cfg->output_gate ? dw->w_g : (void*)1, "w_g"},
+      {G > 0 ? dw->w_o_a : (void*)1, "w_o_a"}, {G > 0 ? dw->w_o_b : (void*)1, "w_o_b"}};
+  for (const Need& q : need)
+    if (!q.have) return fail(MLA_ERR_INVALID_ARG, "the gradient of %s is required by this configuration", q.name);
+  {
+    const void* ptrs[] = {x, dout, dx, w->w_kv_a, w->kv_a_gamma, w->w_kv_b, workspace};
+    for (const void* p : ptrs)
+      if (p && !aligned16(p)) return fail(MLA_ERR_MISALIGNED, "the layer backward needs 16-byte aligned tensors");
+    const void* opt[] = {w->w_q_a, w->w_q_b, w->w_q, w->w_o, w->w_g, w->w_o_a, w->w_o_b, dw->w_q_a, dw->w_q_b,
+                         dw->w_q, dw->w_kv_a, dw->w_kv_b, dw->w_o, dw->w_g, dw->w_o_a, dw->w_o_b};
+    for (const void* p : opt)
+      if (p && !aligned16(p)) return fail(MLA_ERR_MISALIGNED, "the layer backward needs 16-byte aligned tensors");
+  }
+  const LayerBwdWs L = layer_bwd_layout(cfg, n);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, workspace_bytes);
+  const hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  auto at = [&](size_t off) { return (void*)(ws + off); };
+  bf16* tr = (bf16*)at(L.tr);
+  const int64_t npad = L.npad;
+  hipError_t e;
+
+  const int32_t* positions = positions_dev;
+  if (rope && !positions) {
+    if ((e = launch_positions(cu_seqlens_dev, num_seqs, n, (int32_t*)at(L.pos), st)) != hipSuccess)
+      return hip_fail(e, "positions");
+    positions = (const int32_t*)at(L.pos);
+  }
+  // y = a b^T (b [n, k]) or, nn, y = a b (b [k, n]); fp32 or bf16 output
+  auto gemm = [&](const void* a, int64_t lda, const void* b, int64_t ldb, void* c, int64_t ldc, int m, int nn, int k,
+                  bool nn_layout, bool f32_out, bool acc, int epi = EPI_STORE, int batch = 1, int64_t abs = 0,
+                  int64_t bbs = 0, int64_t cbs = 0) -> mla_status {
+    GemmArgs g{};
+    g.a = a; g.lda = lda; g.a_bstride = abs; g.b = b; g.ldb = ldb; g.b_bstride = bbs; g.c = c; g.ldc = ldc;
+    g.c_bstride = cbs; g.m = m; g.n = nn; g.k = k; g.batch = batch; g.b_kn = nn_layout; g.c_f32 = f32_out;
+    g.c_acc = acc; g.epilogue = epi;
+    g.cos_t = rope_cos; g.sin_t = rope_sin; g.table_len = rope_table_len; g.positions = positions;
+    g.rope_head_stride = dqk; g.rope_off = dn; g.rope_interleave = cfg->rope_interleave;
+    const hipError_t err = launch_gemm_bf16(g, st);
+    return err == hipSuccess ? MLA_OK : hip_fail(err, "layer backward GEMM");
+  };
+  // dW [cols(dy), cols(xin)] = dy^T xin over the n tokens: dy transposed (and
+  // rounded to bf16) into the K-major buffer, then an NN product
+  auto weight_grad = [&](const void* dy, bool dy_f32, int64_t ld_dy, int dy_cols, const void* xin, int64_t ld_x,
+                         int x_cols, float* out, int batch = 1, int64_t abs = 0, int64_t bbs = 0,
+                         int64_t cbs = 0, int m_rows = -1, int n_cols = -1) -> mla_status {
+    const hipError_t err = launch_transpose_bf16(dy, dy_f32, ld_dy, n, dy_cols, tr, npad, (int)npad, st);
+    if (err != hipSuccess) return hip_fail(err, "transpose");
+    return gemm(tr, npad, xin, ld_x, out, n_cols > 0 ? n_cols : x_cols, m_rows > 0 ? m_rows : dy_cols,
+                n_cols > 0 ? n_cols : x_cols, n, true, true, false, EPI_STORE, batch, abs, bbs, cbs);
+  };
+  auto norm = [&](const void* src, int64_t stride, int width, int norm_dim, const void* gamma, int rope_off,
+                  int rope_slices, void* dst, int64_t dst_stride) -> mla_status {
+    NormRopeArgs a{};
+    a.interleave = cfg->rope_interleave;
+    a.src = src; a.src_stride = stride; a.n_rows = n; a.row_width = width; a.norm_dim = norm_dim; a.gamma = gamma;
+    a.eps = cfg->norm_eps; a.rope_offset = rope_off; a.rope_slices = rope_slices; a.rope_stride = dr;
+    a.rope_dim = dr; a.cos_t = rope_cos; a.sin_t = rope_sin; a.table_len = rope_table_len; a.positions = positions;
+    a.dst = dst; a.dst_stride = dst_stride;
+    const hipError_t err = launch_norm_rope(a, true, st, true);
+    return err == hipSuccess ? MLA_OK : hip_fail(err, "latent norm / rope launch");
+  };
+  auto rope_back = [&](const float* src, int64_t ld_src, int width, bf16* dst, int64_t ld_dst, int rope_off,
+                       int slices, int stride) -> mla_status {
+    RopeBackArgs a{};
+    a.src = src; a.ld_src = ld_src; a.n_rows = n; a.width = width; a.dst = dst; a.ld_dst = ld_dst;
+    a.rope_off = rope_off; a.rope_slices = rope ? slices : 0; a.rope_stride = stride; a.rope_dim = dr;
+    a.interleave = cfg->rope_interleave; a.cos_t = rope_cos; a.sin_t = rope_sin; a.table_len = rope_table_len;
+    a.positions = positions;
+    const hipError_t err = launch_rope_back(a, st);
+    return err == hipSuccess ? MLA_OK : hip_fail(err, "rope backward");
+  };
+  auto norm_back = [&](const float* xin, int64_t ld_x, const float* dy, int64_t ld_dy, const void* gamma, int width,
+                       bf16* dxo, int64_t ld_dx, float* dgamma) -> mla_status {
+    RmsNormBwdArgs a{};
+    a.x = xin; a.ld_x = ld_x; a.dy = dy; a.ld_dy = ld_dy; a.gamma = gamma; a.n_rows = n; a.width = width;
+    a.eps = cfg->norm_eps; a.dx = dxo; a.ld_dx = ld_dx; a.rinv = (float*)at(L.rinv);
+    const hipError_t err = launch_rms_norm_bwd(a, (float*)at(L.part), dgamma, st);
+    return err == hipSuccess ? MLA_OK : hip_fail(err, "rmsnorm backward");
+  };
+
+  // ---- forward, recomputed (bf16 attention operands)
+  bf16* q = (bf16*)at(L.q);
+  bf16* lat = (bf16*)at(L.lat);
+  bf16* kv = (bf16*)at(L.kv);
+  bf16* attn = (bf16*)at(L.attn);
+  float* q_lat32 = (float*)at(L.q_lat32);
+  bf16* q_lat = (bf16*)at(L.q_lat);
+  float* ckv32 = (float*)at(L.ckv32);
+  const int q_epi = rope ? EPI_ROPE : EPI_STORE;
+  if (rq > 0) {
+    if ((s = gemm(x, hid, w->w_q_a, hid, q_lat32, rq, n, rq, hid, false, true, false)) != MLA_OK) return s;
+    if ((s = norm(q_lat32, rq, rq, rq, w->q_a_gamma, 0, 0, q_lat, rq)) != MLA_OK) return s;
+    if ((s = gemm(q_lat, rq, w->w_q_b, rq, q, (int64_t)H * dqk, n, H * dqk, rq, false, false, false, q_epi)) != MLA_OK)
+      return s;
+  } else {
+    if ((s = gemm(x, hid, w->w_q, hid, q, (int64_t)H * dqk, n, H * dqk, hid, false, false, false, q_epi)) != MLA_OK)
+      return s;
+  }
+  if ((s = gemm(x, hid, w->w_kv_a, hid, ckv32, lw, n, lw, hid, false, true, false)) != MLA_OK) return s;
+  if ((s = norm(ckv32, lw, lw, rkv, w->kv_a_gamma, rkv, rope ? 1 : 0, lat, lw)) != MLA_OK) return s;
+  if ((s = gemm(lat, lw, w->w_kv_b, rkv, kv, (int64_t)H * dkvw, n, H * dkvw, rkv, false, false, false)) != MLA_OK)
+    return s;
+  if ((s = attention_impl(cfg, q, kv, lat + rkv, lw, false, cu_seqlens_dev, cu_seqlens_host, num_seqs, n, attn, st)) !=
+      MLA_OK)
+    return s;
+  const bf16* a2 = attn;                         // the output projection's input
+  float* gpre = (float*)at(L.gpre);
+  if (cfg->output_gate) {
+    if ((s = gemm(x, hid, w->w_g, hid, gpre, F, n, F, hid, false, true, false)) != MLA_OK) return s;
+    if ((e = launch_gate_fwd(attn, gpre, (bf16*)at(L.a2), (int64_t)n * F, st)) != hipSuccess) return hip_fail(e, "gate");
+    a2 = (const bf16*)at(L.a2);
+  }
+  bf16* ot = (bf16*)at(L.ot);
+  if (G > 0) {
+    if ((s = gemm(a2, F, w->w_o_a, fg, ot, gro, n, ro, fg, false, false, false, EPI_STORE, G, fg, (int64_t)ro * fg,
+                  ro)) != MLA_OK)
+      return s;
+  }
+
+  // ---- output projection
+  float* da2 = (float*)at(L.da2);
+  if (G > 0) {
+    bf16* dt = (bf16*)at(L.dt);
+    if ((s = weight_grad(dout, false, hid, hid, ot, gro, gro, dw->w_o_b)) != MLA_OK) return s;
+    if ((s = gemm(dout, hid, w->w_o_b, gro, dt, gro, n, gro, hid, true, false, false)) != MLA_OK) return s;
+    // dW_o_a[g] = dt_g^T a2_g (groups batched over the transposed dt)
+    if ((e = launch_transpose_bf16(dt, false, gro, n, gro, tr, npad, (int)npad, st)) != hipSuccess)
+      return hip_fail(e, "transpose");
+    if ((s = gemm(tr, npad, a2, F, dw->w_o_a, fg, ro, fg, n, true, true, false, EPI_STORE, G, (int64_t)ro * npad, fg,
+                  (int64_t)ro * fg)) != MLA_OK)
+      return s;
+    if ((s = gemm(dt, gro, w->w_o_a, fg, da2, F, n, fg, ro, true, true, false, EPI_STORE, G, ro, (int64_t)ro * fg,
+                  fg)) != MLA_OK)
+      return s;
+  } else {
+    if ((s = weight_grad(dout, false, hid, hid, a2, F, F, dw->w_o)) != MLA_OK) return s;
+    if ((s = gemm(dout, hid, w->w_o, F, da2, F, n, F, hid, true, true, false)) != MLA_OK) return s;
+  }
+  // ---- gate
+  bf16* da = (bf16*)at(L.da);
+  bf16* dgp = (bf16*)at(L.dg);
+  if (cfg->output_gate) {
+    if ((e = launch_gate_bwd(da2, attn, gpre, da, dgp, (int64_t)n * F, st)) != hipSuccess) return hip_fail(e, "gate backward");
+  } else {
+    RopeBackArgs a{};
+    a.src = da2; a.ld_src = F; a.n_rows = n; a.width = F; a.dst = da; a.ld_dst = F;
+    if ((e = launch_rope_back(a, st)) != hipSuccess) return hip_fail(e, "convert");
+  }
+  // ---- attention core
+  float* dq32 = (float*)at(L.dq32);
+  float* dkv32 = (float*)at(L.dkv32);
+  float* dkpe32 = (float*)at(L.dkpe32);
+  {
+    AttnBwdArgs a{};
+    char* aw = (char*)at(L.abw);
+    a.q = q; a.kv = kv; a.kpe = lat + rkv; a.kpe_stride = lw; a.o = attn; a.dout = da;
+    a.cu_dev = cu_seqlens_dev; a.n_tokens = n; a.heads = H; a.scale = scale_of(cfg);
+    a.lse = (float*)aw;
+    a.dsum = (float*)(aw + align256((size_t)n * H * 4));
+    a.dkr = (float*)(aw + 2 * align256((size_t)n * H * 4));
+    a.dq = dq32; a.dkv = dkv32; a.dkpe = dkpe32;
+    if ((e = launch_attention_bwd(a, cu_seqlens_host, num_seqs, st)) != hipSuccess) return hip_fail(e, "attention backward");
+  }
+  // ---- RoPE backward, bf16 gradients
+  bf16* dq16 = (bf16*)at(L.dq16);
+  bf16* dkv16 = (bf16*)at(L.dkv16);
+  bf16* dckv = (bf16*)at(L.dckv);
+  if ((s = rope_back(dq32, (int64_t)H * dqk, H * dqk, dq16, (int64_t)H * dqk, dn, H, dqk)) != MLA_OK) return s;
+  if ((s = rope_back(dkv32, (int64_t)H * dkvw, H * dkvw, dkv16, (int64_t)H * dkvw, 0, 0, dr)) != MLA_OK) return s;
+  if ((s = rope_back(dkpe32, dr, dr, dckv + rkv, lw, 0, 1, dr)) != MLA_OK) return s;
+  // ---- kv up-projection, latent norm, joint down-projection
+  float* dcn32 = (float*)at(L.dcn32);
+  if ((s = weight_grad(dkv16, false, (int64_t)H * dkvw, H * dkvw, lat, lw, rkv, dw->w_kv_b)) != MLA_OK) return s;
+  if ((s = gemm(dkv16, (int64_t)H * dkvw, w->w_kv_b, rkv, dcn32, rkv, n, rkv, H * dkvw, true, true, false)) != MLA_OK)
+    return s;
+  if ((s = norm_back(ckv32, lw, dcn32, rkv, w->kv_a_gamma, rkv, dckv, lw, dw->kv_a_gamma)) != MLA_OK) return s;
+  if ((s = weight_grad(dckv, false, lw, lw, x, hid, hid, dw->w_kv_a)) != MLA_OK) return s;
+  if ((s = gemm(dckv, lw, w->w_kv_a, hid, dx, hid, n, hid, lw, true, true, false)) != MLA_OK) return s;
+  // ---- query path
+  if (rq > 0) {
+    float* dqln32 = (float*)at(L.dqln32);
+    bf16* dql16 = (bf16*)at(L.dql16);
+    if ((s = weight_grad(dq16, false, (int64_t)H * dqk, H * dqk, q_lat, rq, rq, dw->w_q_b)) != MLA_OK) return s;
+    if ((s = gemm(dq16, (int64_t)H * dqk, w->w_q_b, rq, dqln32, rq, n, rq, H * dqk, true, true, false)) != MLA_OK)
+      return s;
+    if ((s = norm_back(q_lat32, rq, dqln32, rq, w->q_a_gamma, rq, dql16, rq, dw->q_a_gamma)) != MLA_OK) return s;
+    if ((s = weight_grad(dql16, false, rq, rq, x, hid, hid, dw->w_q_a)) != MLA_OK) return s;
+    if ((s = gemm(dql16, rq, w->w_q_a, hid, dx, hid, n, hid, rq, true, true, true)) != MLA_OK) return s;
+  } else {
+    if ((s = weight_grad(dq16, false, (int64_t)H * dqk, H * dqk, x, hid, hid, dw->w_q)) != MLA_OK) return s;
+    if ((s = gemm(dq16, (int64_t)H * dqk, w->w_q, hid, dx, hid, n, hid, H * dqk, true, true, true)) != MLA_OK) return s;
+  }
+  // ---- gate projection
+  if (cfg->output_gate) {
+    if ((s = weight_grad(dgp, false, F, F, x, hid, hid, dw->w_g)) != MLA_OK) return s;
+    if ((s = gemm(dgp, F, w->w_g, hid, dx, hid, n, hid, F, true, true, true)) != MLA_OK) return s;
+  }
+  return ok();
+}
+
 mla_status mla_q_uproj_rope_mxfp8(const mla_config* cfg, const void* q_latent, int64_t ldq, int32_t n_tokens,
                                   const void* w_q_b, const int32_t* positions, const float* rope_cos,
                                   const float* rope_sin, int32_t rope_table_len, void* q_codes, void* q_scales,

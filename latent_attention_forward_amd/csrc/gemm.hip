@@ -204,7 +204,12 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmArgs g) {
         }
         if (CT == 1) {
           float* C = (float*)g.c + (int64_t)blockIdx.z * g.c_bstride;
-          *(float4*)(C + (int64_t)m * g.ldc + n) = make_float4(v[0], v[1], v[2], v[3]);
+          float4* cp = (float4*)(C + (int64_t)m * g.ldc + n);
+          if (g.c_acc) {
+            const float4 o = *cp;
+            v[0] += o.x; v[1] += o.y; v[2] += o.z; v[3] += o.w;
+          }
+          *cp = make_float4(v[0], v[1], v[2], v[3]);
         } else if (CT == 2) {
           f16* C = (f16*)g.c + (int64_t)blockIdx.z * g.c_bstride;
           f16x4 o;
@@ -535,6 +540,7 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
   const int num_m = (g.m + BM - 1) / BM, num_n = (g.n + BN - 1) / BN;
   dim3 grid(num_m * num_n, 1, g.batch);
   const int ct = g.c_f32 ? 1 : (g.c_f16 ? 2 : 0);
+  if (g.c_acc && (ct != 1 || g.c_mx)) return hipErrorInvalidValue;   // accumulation is for fp32 outputs
   // MXFP8 output: the 256x256 kernel whatever the grid size
   if (g.c_mx) {
     const bool ok = !g.b_kn && g.k >= GBK && g.k % GBK == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 && g.n % 32 == 0 &&
@@ -574,8 +580,9 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
     }
   }
   if (g.b_kn) {
-    if (g.epilogue != EPI_STORE || ct != 0) return hipErrorInvalidValue;
-    gemm_bf16_kernel<true, EPI_STORE, 0><<<grid, NT, 0, s>>>(g);
+    if (g.epilogue != EPI_STORE || ct == 2) return hipErrorInvalidValue;
+    if (ct == 1) gemm_bf16_kernel<true, EPI_STORE, 1><<<grid, NT, 0, s>>>(g);
+    else gemm_bf16_kernel<true, EPI_STORE, 0><<<grid, NT, 0, s>>>(g);
   } else if (g.epilogue == EPI_GATE) {
     if (ct != 0) return hipErrorInvalidValue;
     gemm_bf16_kernel<false, EPI_GATE, 0><<<grid, NT, 0, s>>>(g);

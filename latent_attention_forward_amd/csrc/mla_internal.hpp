@@ -217,6 +217,7 @@ struct GemmArgs {
   // c_scale one E8M0 byte per 32 consecutive columns of a row (row stride
   // ld_scale bytes); n a multiple of 32
   bool c_mx; void* c_scale; int64_t ld_scale;
+  bool c_acc;                                      // fp32 C (128x128 kernel): C += result instead of C = result
 };
 enum { EPI_STORE = 0, EPI_GATE = 1, EPI_ROPE = 2 };
 
@@ -284,6 +285,33 @@ struct AttnBwdArgs {
   float* dq; float* dkv; float* dkpe;                  // [N, H, 192], [N, H, 256], [N, 64]
 };
 hipError_t launch_attention_bwd(const AttnBwdArgs& a, const int32_t* cu_host, int num_seqs, hipStream_t s);
+
+// ---------------------------------------------------------------- layer backward helpers
+// dst[c, r] = src[r, c] (bf16 or fp32 source, rounded to bf16), zero for
+// rows <= r < rows_pad.
+hipError_t launch_transpose_bf16(const void* src, bool src_f32, int64_t ld_src, int rows, int cols, bf16* dst,
+                                 int64_t ld_dst, int rows_pad, hipStream_t s);
+// a2 = a * sigmoid(g), and the gate's backward (dA, dg) from dA2; n elements, dense.
+hipError_t launch_gate_fwd(const bf16* a, const float* g, bf16* a2, int64_t n, hipStream_t s);
+hipError_t launch_gate_bwd(const float* da2, const bf16* a, const float* g, bf16* da, bf16* dg, int64_t n,
+                           hipStream_t s);
+struct RopeBackArgs {
+  const float* src; int64_t ld_src; int n_rows; int width;
+  bf16* dst; int64_t ld_dst;
+  int rope_off; int rope_slices; int rope_stride; int rope_dim; int interleave;
+  const float* cos_t; const float* sin_t; int table_len; const int32_t* positions;
+};
+// dst = bf16(src) with the rope columns rotated by -theta (no rotation with rope_slices = 0).
+hipError_t launch_rope_back(const RopeBackArgs& a, hipStream_t s);
+struct RmsNormBwdArgs {
+  const float* x; int64_t ld_x;                    // the norm's fp32 input
+  const float* dy; int64_t ld_dy;                  // gradient of its output
+  const void* gamma; int n_rows; int width; float eps;
+  bf16* dx; int64_t ld_dx;                         // gradient of its input
+  float* rinv;                                     // [n_rows] 1 / r (scratch)
+};
+// dx and dgamma [width]; partials: (n_rows + 255) / 256 * width floats of scratch.
+hipError_t launch_rms_norm_bwd(const RmsNormBwdArgs& a, float* partials, float* dgamma, hipStream_t s);
 
 // Most paged-cache blocks one decode segment may span (its block ids are staged in LDS).
 constexpr int kDecodeMaxChunkBlocks = 512;

@@ -37,7 +37,7 @@ def test_header_symbols_exported(lib):
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(mla.exported_symbols())
-    assert lib.mla_abi_version() == 4
+    assert lib.mla_abi_version() == 5
 
 
 def test_config_validation(lib):
@@ -191,6 +191,21 @@ def test_device_calls_reject_bad_arguments_before_launch(lib):
     empty = np.array([0, 0], np.int32)
     assert b(ctypes.byref(cfg), None, None, None, 576, None, empty.ctypes.data, 1, None, None, None, None, None,
              None, 0, None) == mla.MLA_OK
+    # layer backward: fp32 config, a missing weight gradient, workspace
+    lb = lib.mla_prefill_bwd
+    for name, _ in mla.MlaWeights._fields_:
+        setattr(w, name, 4096)
+    w.w_q = w.w_g = w.w_o_a = w.w_o_b = None
+    dw = mla.MlaWeightGrads()
+    for name, _ in mla.MlaWeightGrads._fields_:
+        setattr(dw, name, 4096)
+    lb_args = lambda c, g, wsb: [ctypes.byref(c), ctypes.byref(w), 4096, 4096, cu.ctypes.data, 1, None, 4096, 4096,
+                                 64, 4096, 4096, ctypes.byref(g), 4096, wsb, None]
+    assert lb(*lb_args(f32, dw, 1 << 40)) == mla.MLA_ERR_UNSUPPORTED
+    assert lb(*lb_args(cfg, dw, 16)) == mla.MLA_ERR_WORKSPACE
+    dw.w_kv_b = None
+    assert lb(*lb_args(cfg, dw, 1 << 40)) == mla.MLA_ERR_INVALID_ARG and b"w_kv_b" in lib.mla_last_error()
+    assert mla.prefill_bwd_workspace_size(cfg, 4096) > mla.attention_bwd_workspace_size(cfg, 4096)
     # norm/rope: rope slices overlapping the norm region, slot mapping in place
     st = lib.mla_latent_norm_rope(ctypes.byref(cfg), 4096, 576, 4, 576, 512, 4096, 500, 1, 64, 4096, 4096, 16, 4096,
                                   8192, 576, None, 0, None)
