@@ -8,7 +8,7 @@
 //   dq = scale dS k,  dk = scale dS^T q,  dk_pe = sum over heads of dk's
 //   64-wide shared part.
 // Three passes, each on 32x32x16 bf16 MFMAs:
-//   1. stats: per (query, head) the log-sum-exp of the scaled scores in
+//   1. stats: per (head, query) the log-sum-exp of the scaled scores in
 //      base-2 units (the forward's softmax statistics, recomputed: one QK^T
 //      pass) and D;
 //   2. dq, query-major (workgroup = 128 queries of one head, keys in tiles of
@@ -19,9 +19,23 @@
 //      dK^T += Q^T dS, dO^T and Q^T by transposing LDS reads.
 // P and dS are rounded to bf16 as MFMA operands.  Every lane owns one query
 // (pass 2) or one key (pass 3) column, so the per-row statistics are per lane.
-// Tiles are staged through LDS with rows padded by 16 bytes (row stride 400
-// or 272 B), which keeps the 16 rows of a row read and the 4 rows of a
-// transposing read on different banks.
+//
+// The streamed tiles go global -> LDS by asynchronous copies
+// (global_load_lds), double buffered: tile t + 1 is requested right after the
+// barrier that opens tile t, so it lands while tile t is multiplied; one
+// barrier per tile.  Rows past the document end are copied from its last row
+// (finite values; their scores are masked).  In LDS a 128-wide part is stored
+// as rows of 16 chunks of 16 bytes, chunk c of row r at c ^ swn(r), the
+// 64-wide part as rows of 8 chunks at c ^ swr(r): with a 64-bank model both
+// are free of bank conflicts for the row reads of an MFMA operand (16 rows,
+// one chunk, per 16-lane phase) and for the transposing reads (4 rows x 32
+// bytes per 16 lanes, 4 rows x 64 bytes per 32 lanes).
+//
+// Work order: workgroup b runs on XCD b mod 8; the heads are dealt to the
+// XCDs (head h on XCD h mod 8), and an XCD takes its heads one after another,
+// the tiles of a head longest first, so the workgroups that run together on
+// an XCD stream the same head's rows from its L2.  With fewer than 8 heads
+// the workgroups take (head, tile) pairs head fastest instead.
 #include "mla_internal.hpp"
 
 #include <vector>
@@ -31,14 +45,15 @@ namespace mla {
 namespace {
 
 constexpr int DN = 128, DR = 64, DQK = 192, DV = 128;
-constexpr int QP = DQK + 8;          // padded row of a q / k tile (elements)
-constexpr int VP = DV + 8;           // padded row of a v / dO tile
 constexpr int BT = 128;              // rows (queries or keys) per workgroup
 constexpr int ST = 64;               // rows of the streamed tile
 constexpr int MAX_ITEMS = 880;
+constexpr int SD = 4;                // row-read operands in flight
+constexpr int PD = 3;                // transposing-read operands in flight
 
 struct BwdPlan {
-  int n;                             // work items in this launch
+  int n;                             // tiles per head in this launch
+  int by_xcd;                        // heads dealt to XCDs (else workgroup b: head b % H, tile b / H)
   uint32_t t[MAX_ITEMS];             // (document << 16) | 128-row tile index in the document
 };
 
@@ -47,53 +62,99 @@ struct BwdArgs {
   const bf16* o; const bf16* dout;
   const int32_t* cu; int n_tokens; int heads;
   float scale;                       // softmax scale
-  float* lse;                        // [N, H] base-2 log-sum-exp of scale * q.k
-  float* dsum;                       // [N, H] D = rowsum(dO * O)
+  float* lse;                        // [H, N] base-2 log-sum-exp of scale * q.k
+  float* dsum;                       // [H, N] D = rowsum(dO * O)
   float* dq;                         // [N, H, 192]
   float* dkv;                        // [N, H, 256] = [dk_nope | dv]
   float* dkr;                        // [N, H, 64] per-head gradient of the shared key part
   float* dkpe;                       // [N, 64]
 };
 
+// chunk swizzles (bits of the row permuted; see the header)
+__device__ __forceinline__ int swn(int r) { return ((r & 1) << 3) | ((r & 2) << 1) | ((r >> 1) & 2) | ((r >> 3) & 1); }
+__device__ __forceinline__ int swr(int r) { return ((r & 2) << 1) | ((r >> 1) & 2) | ((r >> 3) & 1); }
+// element offsets of (row, column) in a 128-wide and a 64-wide tile
+__device__ __forceinline__ int offn(int r, int col) { return r * 128 + (((col >> 3) ^ swn(r)) << 3) + (col & 7); }
+__device__ __forceinline__ int offr(int r, int col) { return r * 64 + (((col >> 3) ^ swr(r)) << 3) + (col & 7); }
+
 __device__ __forceinline__ bf16x8 zero8b() { return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0)); }
 
-// transposing read of a padded row-major tile X[row][col] (stride P elements):
-// lane i of a 16-lane group receives X[r0 + j][c0 + i] for j = 0..3 (see
-// lds_read_tr); a lane L addresses &X[r0 + L/4][c0 + 4 (L%4)]
-template <int P>
+// 4-byte asynchronous global -> LDS copy (lane l lands at lds_base + 4 l);
+// awaited like the 16-byte copies.
+__device__ __forceinline__ void lds_dma4_raw(const void* gsrc, const void* lds_base) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(MLA_LDS const void*)(lds_base));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" : : "v"(gsrc), "s"(m) : "memory", "m0");
+}
+
+// Transposing read of a swizzled tile: the A operand of 32 columns
+// c0 .. c0 + 31 (rows of the MFMA) and 16 K rows r0 .. r0 + 15 taken in the
+// order {4h + j, 8 + 4h + j}, h = lane / 32: the row order of a score tile's
+// C layout.  Within a 16-lane group, lane L addresses row r0 + 4 (group / 2)
+// + L / 4, columns c0 + 16 (group % 2) + 4 (L % 4) .. + 3 (see lds_read_tr).
+template <bool WIDE>
 __device__ __forceinline__ bf16x8 tr_operand(const bf16* tile, int r0, int c0, int lane) {
-  // A operand of 32 columns (rows of the MFMA) c0 .. c0 + 31 and 16 K rows
-  // r0 .. r0 + 15 in the order {4h + j, 8 + 4h + j}, h = lane / 32: the key
-  // (or query) order of a score tile's C layout
   const int grp = lane >> 4, L16 = lane & 15;
   const int row = r0 + (grp >> 1) * 4 + (L16 >> 2);
   const int col = c0 + (grp & 1) * 16 + 4 * (L16 & 3);
-  const bf16x4 lo = lds_read_tr(tile + row * P + col);
-  const bf16x4 hi = lds_read_tr(tile + (row + 8) * P + col);
+  const bf16x4 lo = lds_read_tr(tile + (WIDE ? offn(row, col) : offr(row, col)));
+  const bf16x4 hi = lds_read_tr(tile + (WIDE ? offn(row + 8, col) : offr(row + 8, col)));
   return cat8(lo, hi);
 }
 
-// Copies rows [r0, r0 + nrows) of a [*, width] bf16 source (row stride
-// src_stride elements, rows past `valid` replaced by zeros) into a padded LDS
-// tile (stride P), 8 elements per thread and step.
-template <int P>
-__device__ __forceinline__ void load_tile(bf16* tile, const bf16* src, int64_t src_stride, int r0, int nrows,
-                                          int valid, int width, int col0 = 0) {
-  const int cpr = width / 8;
-  for (int i = threadIdx.x; i < nrows * cpr; i += 256) {
-    const int r = i / cpr, c = i - r * cpr;
-    bf16x8 v = zero8b();
-    if (r0 + r < valid) v = *(const bf16x8*)(src + (int64_t)(r0 + r) * src_stride + c * 8);
-    *(bf16x8*)(tile + r * P + col0 + c * 8) = v;
+// Which (head, tile) a workgroup takes; false when it has none.
+__device__ __forceinline__ bool work_item(const BwdPlan& plan, int H, int& h, uint32_t& td) {
+  if (!plan.by_xcd) {
+    h = (int)(blockIdx.x % (unsigned)H);
+    td = plan.t[blockIdx.x / (unsigned)H];
+    return true;
   }
+  const int x = blockIdx.x & 7, s = blockIdx.x >> 3;
+  const int hl = s / plan.n, ti = s - hl * plan.n;
+  h = x + 8 * hl;
+  if (h >= H) return false;
+  td = plan.t[ti];
+  return true;
 }
+
+// Per-lane copy sources of a 64-row tile [64][W] (W = 128: 16 copies of 1 KB,
+// 4 per wave; W = 64: 8 copies, 2 per wave): copy i of wave w fills LDS chunk
+// positions P = (w + 4 i) 64 + lane, i.e. row P / (W / 8), physical chunk
+// P % (W / 8), which holds logical chunk physical ^ swizzle(row).  The row
+// bits the swizzle reads do not depend on i, so a lane's chunk is the same in
+// all of its copies and its rows step by 2048 / W.
+template <int W>
+struct TileCopy {
+  static constexpr int NC = W == 128 ? 4 : 2;
+  static constexpr int STEP = 2048 / W;
+  int row0;                          // tile row of the first copy
+  int col_bytes;                     // byte offset of the logical chunk in the row
+  __device__ __forceinline__ void init(int wave, int lane) {
+    const int P = wave * 64 + lane;
+    row0 = P / (W / 8);
+    const int pc = P % (W / 8);
+    col_bytes = (pc ^ (W == 128 ? swn(row0) : swr(row0))) << 4;
+  }
+  // rows at or past `valid` repeat row valid - 1
+  __device__ __forceinline__ void issue(const bf16* base, int64_t row_bytes, int valid, bf16* tile, int wave) const {
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int r = min(row0 + i * STEP, valid - 1);
+      lds_dma16_sv(base, (uint32_t)(r * row_bytes + col_bytes), tile + (wave + 4 * i) * 512);
+    }
+  }
+};
+
+template <int B> struct BufC { static constexpr int value = B; };
 
 // ----------------------------------------------------------------------------- pass 1
 __global__ __launch_bounds__(256, 2) void bwd_stats_kernel(BwdArgs a, BwdPlan plan) {
-  __shared__ __attribute__((aligned(16))) bf16 sK[ST * QP];
+  __shared__ __attribute__((aligned(16))) bf16 sKn[2][ST * DN];
+  __shared__ __attribute__((aligned(16))) bf16 sKr[2][ST * DR];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h = blockIdx.y, H = a.heads;
-  const uint32_t td = plan.t[blockIdx.x];
+  const int H = a.heads;
+  int h;
+  uint32_t td;
+  if (!work_item(plan, H, h, td)) return;
   const int doc = (int)(td >> 16), tix = (int)(td & 0xffff);
   const int ds = a.cu[doc], de = a.cu[doc + 1];
   const int q0 = ds + tix * BT;
@@ -105,23 +166,49 @@ __global__ __launch_bounds__(256, 2) void bwd_stats_kernel(BwdArgs a, BwdPlan pl
 #pragma unroll
   for (int ks = 0; ks < DQK / 16; ++ks)
     qreg[ks] = my_q < q1 ? *(const bf16x8*)(a.q + my_q * qrow + h * DQK + ks * 16 + hsel * 8) : zero8b();
+  TileCopy<DN> cn;
+  TileCopy<DR> cr;
+  cn.init(wave, lane);
+  cr.init(wave, lane);
+  const bf16* kvh = uniform_ptr(a.kv + h * (DN + DV));
+  const int nt = (q1 - ds + ST - 1) / ST;
+  auto issue = [&](int it, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    const int kb = ds + it * ST;
+    cn.issue(kvh + (int64_t)kb * kvrow, kvrow * 2, de - kb, sKn[buf], wave);
+    cr.issue(uniform_ptr(a.kpe + (int64_t)kb * a.kpe_stride), a.kpe_stride * 2, de - kb, sKr[buf], wave);
+  };
   const float c2 = a.scale * kLog2e;
   float m = -INFINITY, l = 0.f;
-  for (int kb = ds; kb < q1; kb += ST) {
-    __syncthreads();
-    load_tile<QP>(sK, a.kv + h * (DN + DV), kvrow, kb, ST, de, DN);
-    load_tile<QP>(sK, a.kpe, a.kpe_stride, kb, ST, de, DR, DN);
-    __syncthreads();
-    if (qw0 >= q1 || kb > qw0 + 31) continue;
+  auto step = [&](int it, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    const int kb = ds + it * ST;
+    vm_wait_all();
+    wg_barrier();
+    if (it + 1 < nt) issue(it + 1, BufC<buf ^ 1>{});
+    if (qw0 >= q1 || kb > qw0 + 31) return;
+    // S^T for two key blocks of 32 (alternating chains), operands read SD ahead
     f32x16 s[2];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[mt][e] = 0.f;
+    auto kread = [&](int i) {
+      const int kr = (i & 1) * 32 + (lane & 31), ks = i >> 1;
+      return ks < 8 ? *(const bf16x8*)&sKn[buf][offn(kr, ks * 16 + hsel * 8)]
+                    : *(const bf16x8*)&sKr[buf][offr(kr, (ks - 8) * 16 + hsel * 8)];
+    };
+    bf16x8 kf[SD];
 #pragma unroll
-      for (int ks = 0; ks < DQK / 16; ++ks)
-        s[mt] = mfma32(*(const bf16x8*)&sK[(mt * 32 + (lane & 31)) * QP + ks * 16 + hsel * 8], qreg[ks], s[mt]);
+    for (int i = 0; i < SD; ++i) kf[i] = kread(i);
+#pragma unroll
+    for (int i = 0; i < 24; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8 cur = kf[i % SD];
+      if (i + SD < 24) kf[i % SD] = kread(i + SD);
+      s[i & 1] = mfma32(cur, qreg[i >> 1], s[i & 1]);
     }
+    __builtin_amdgcn_sched_barrier(0);
     float mx = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -141,6 +228,11 @@ __global__ __launch_bounds__(256, 2) void bwd_stats_kernel(BwdArgs a, BwdPlan pl
       l = l * __builtin_amdgcn_exp2f(m - mn) + acc;
       m = mn;
     }
+  };
+  issue(0, BufC<0>{});
+  for (int it = 0; it < nt; it += 2) {
+    step(it, BufC<0>{});
+    if (it + 1 < nt) step(it + 1, BufC<1>{});
   }
   // combine the two lanes of a query (each saw half of every key block)
   const float mo = __shfl_xor(m, 32, 64), lo = __shfl_xor(l, 32, 64);
@@ -161,18 +253,21 @@ __global__ __launch_bounds__(256, 2) void bwd_stats_kernel(BwdArgs a, BwdPlan pl
   }
   d += __shfl_xor(d, 32, 64);
   if (my_q < q1 && hsel == 0) {
-    a.lse[(int64_t)my_q * H + h] = mm + __builtin_log2f(lt);
-    a.dsum[(int64_t)my_q * H + h] = d;
+    a.lse[(int64_t)h * a.n_tokens + my_q] = mm + __builtin_log2f(lt);
+    a.dsum[(int64_t)h * a.n_tokens + my_q] = d;
   }
 }
 
 // ----------------------------------------------------------------------------- pass 2: dq
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, BwdPlan plan) {
-  __shared__ __attribute__((aligned(16))) bf16 sK[ST * QP];
-  __shared__ __attribute__((aligned(16))) bf16 sV[ST * VP];
+  __shared__ __attribute__((aligned(16))) bf16 sKn[2][ST * DN];
+  __shared__ __attribute__((aligned(16))) bf16 sKr[2][ST * DR];
+  __shared__ __attribute__((aligned(16))) bf16 sV[2][ST * DV];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h = blockIdx.y, H = a.heads;
-  const uint32_t td = plan.t[blockIdx.x];
+  const int H = a.heads;
+  int h;
+  uint32_t td;
+  if (!work_item(plan, H, h, td)) return;
   const int doc = (int)(td >> 16), tix = (int)(td & 0xffff);
   const int ds = a.cu[doc], de = a.cu[doc + 1];
   const int q0 = ds + tix * BT;
@@ -190,53 +285,93 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, BwdPlan plan)
   for (int ks = 0; ks < DV / 16; ++ks)
     greg[ks] = live ? *(const bf16x8*)(a.dout + ((int64_t)my_q * H + h) * DV + ks * 16 + hsel * 8) : zero8b();
   const float c2 = a.scale * kLog2e;
-  const float lse = live ? a.lse[(int64_t)my_q * H + h] : 0.f;
-  const float dsum = live ? a.dsum[(int64_t)my_q * H + h] : 0.f;
+  const float lse = live ? a.lse[(int64_t)h * a.n_tokens + my_q] : 0.f;
+  const float dsum = live ? a.dsum[(int64_t)h * a.n_tokens + my_q] : 0.f;
   f32x16 acc[DQK / 32];
 #pragma unroll
   for (int b = 0; b < DQK / 32; ++b)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[b][e] = 0.f;
+  TileCopy<DN> cn;
+  TileCopy<DR> cr;
+  cn.init(wave, lane);
+  cr.init(wave, lane);
+  const bf16* kvh = uniform_ptr(a.kv + h * (DN + DV));
+  const int nt = (q1 - ds + ST - 1) / ST;
+  auto issue = [&](int it, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    const int kb = ds + it * ST;
+    cn.issue(kvh + (int64_t)kb * kvrow, kvrow * 2, de - kb, sKn[buf], wave);
+    cr.issue(uniform_ptr(a.kpe + (int64_t)kb * a.kpe_stride), a.kpe_stride * 2, de - kb, sKr[buf], wave);
+    cn.issue(kvh + (int64_t)kb * kvrow + DN, kvrow * 2, de - kb, sV[buf], wave);
+  };
 
-  for (int kb = ds; kb < q1; kb += ST) {
-    __syncthreads();
-    load_tile<QP>(sK, a.kv + h * (DN + DV), kvrow, kb, ST, de, DN);
-    load_tile<QP>(sK, a.kpe, a.kpe_stride, kb, ST, de, DR, DN);
-    load_tile<VP>(sV, a.kv + h * (DN + DV) + DN, kvrow, kb, ST, de, DV);
-    __syncthreads();
-    if (qw0 >= q1 || kb > qw0 + 31) continue;
-    // S^T [key, query] and dP^T = V dO^T, two key blocks of 32
-    f32x16 s[2], dp[2];
+  auto step = [&](int it, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    const int kb = ds + it * ST;
+    vm_wait_all();
+    wg_barrier();
+    if (it + 1 < nt) issue(it + 1, BufC<buf ^ 1>{});
+    if (qw0 >= q1 || kb > qw0 + 31) return;
+    // one key block of 32 at a time: S^T [key, query] and dP^T = V dO^T on
+    // alternating chains (operands read SD ahead), dS^T = P^T (dP^T - D) with
+    // P^T = 2^(s c2 - lse) masked past the query, then dQ^T [d, query] +=
+    // K^T [d, key] dS^T [key, query], the block's two k-steps covering keys
+    // mt*32 + jj*16 + {4h + [0,4), 8 + 4h + [0,4)} (operands read PD ahead)
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) { s[mt][e] = 0.f; dp[mt][e] = 0.f; }
       const int kr = mt * 32 + (lane & 31);
+      auto aread = [&](int i) {
+        if (i < 16) {
+          const int ks = i >> 1;
+          return (i & 1) ? *(const bf16x8*)&sV[buf][offn(kr, ks * 16 + hsel * 8)]
+                         : *(const bf16x8*)&sKn[buf][offn(kr, ks * 16 + hsel * 8)];
+        }
+        return *(const bf16x8*)&sKr[buf][offr(kr, (i - 16) * 16 + hsel * 8)];
+      };
+      auto bread = [&](int i) {
+        const int jj = i / 6, b = i % 6, r0 = mt * 32 + jj * 16;
+        return b < 4 ? tr_operand<true>(sKn[buf], r0, b * 32, lane) : tr_operand<false>(sKr[buf], r0, (b - 4) * 32, lane);
+      };
+      f32x16 s, dp;
 #pragma unroll
-      for (int ks = 0; ks < DQK / 16; ++ks)
-        s[mt] = mfma32(*(const bf16x8*)&sK[kr * QP + ks * 16 + hsel * 8], qreg[ks], s[mt]);
+      for (int e = 0; e < 16; ++e) { s[e] = 0.f; dp[e] = 0.f; }
+      bf16x8 af[SD];
 #pragma unroll
-      for (int ks = 0; ks < DV / 16; ++ks)
-        dp[mt] = mfma32(*(const bf16x8*)&sV[kr * VP + ks * 16 + hsel * 8], greg[ks], dp[mt]);
-    }
-    // dS^T = P^T (dP^T - D), P^T = 2^(s c2 - lse), masked past the query
-    bf16x8 dsb[4];
+      for (int i = 0; i < SD; ++i) af[i] = aread(i);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+      for (int i = 0; i < 20; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8 cur = af[i % SD];
+        if (i + SD < 20) af[i % SD] = aread(i + SD);
+        if (i < 16 && (i & 1)) dp = mfma32(cur, greg[i >> 1], dp);
+        else s = mfma32(cur, qreg[i < 16 ? i >> 1 : 8 + (i - 16)], s);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 bf[PD];
+#pragma unroll
+      for (int i = 0; i < PD; ++i) bf[i] = bread(i);
+      bf16x8 dsb[2];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int key = kb + mt * 32 + (e >> 2) * 8 + hsel * 4 + (e & 3);
-        const float p = (key <= my_q && key < de) ? __builtin_amdgcn_exp2f(s[mt][e] * c2 - lse) : 0.f;
-        dsb[mt * 2 + (e >> 3)][e & 7] = (bf16)(p * (dp[mt][e] - dsum));
+        const float p = key <= my_q ? __builtin_amdgcn_exp2f(s[e] * c2 - lse) : 0.f;
+        dsb[e >> 3][e & 7] = (bf16)(p * (dp[e] - dsum));
       }
-    // dQ^T [d, query] += K^T [d, key] dS^T [key, query]; k-step j covers keys
-    // (j/2)*32 + (j%2)*16 + {4h + [0,4), 8 + 4h + [0,4)}
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r0 = (j >> 1) * 32 + (j & 1) * 16;
-#pragma unroll
-      for (int b = 0; b < DQK / 32; ++b) acc[b] = mfma32(tr_operand<QP>(sK, r0, b * 32, lane), dsb[j], acc[b]);
+      for (int i = 0; i < 12; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8 cur = bf[i % PD];
+        if (i + PD < 12) bf[i % PD] = bread(i + PD);
+        acc[i % 6] = mfma32(cur, dsb[i / 6], acc[i % 6]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  issue(0, BufC<0>{});
+  for (int it = 0; it < nt; it += 2) {
+    step(it, BufC<0>{});
+    if (it + 1 < nt) step(it + 1, BufC<1>{});
   }
   if (!live) return;
   // lane holds query my_q, dims b*32 + (e/4)*8 + hsel*4 + e%4
@@ -254,12 +389,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, BwdPlan plan)
 
 // ----------------------------------------------------------------------------- pass 3: dk, dv
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, BwdPlan plan) {
-  __shared__ __attribute__((aligned(16))) bf16 sQ[ST * QP];
-  __shared__ __attribute__((aligned(16))) bf16 sG[ST * VP];
-  __shared__ float sL[ST], sD[ST];
+  __shared__ __attribute__((aligned(16))) bf16 sQn[2][ST * DN];
+  __shared__ __attribute__((aligned(16))) bf16 sQr[2][ST * DR];
+  __shared__ __attribute__((aligned(16))) bf16 sG[2][ST * DV];
+  __shared__ __attribute__((aligned(16))) float sL[2][ST];
+  __shared__ __attribute__((aligned(16))) float sD[2][ST];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h = blockIdx.y, H = a.heads;
-  const uint32_t td = plan.t[blockIdx.x];
+  const int H = a.heads;
+  int h;
+  uint32_t td;
+  if (!work_item(plan, H, h, td)) return;
   const int doc = (int)(td >> 16), tix = (int)(td & 0xffff);
   const int ds = a.cu[doc], de = a.cu[doc + 1];
   const int k0 = ds + tix * BT;
@@ -290,54 +429,111 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, BwdPlan pla
   for (int b = 0; b < DV / 32; ++b)
 #pragma unroll
     for (int e = 0; e < 16; ++e) dv[b][e] = 0.f;
-
+  TileCopy<DN> cn;
+  TileCopy<DR> cr;
+  cn.init(wave, lane);
+  cr.init(wave, lane);
+  const bf16* qh = uniform_ptr(a.q + h * DQK);
+  const bf16* gh = uniform_ptr(a.dout + h * DV);
+  const float* lh = a.lse + (int64_t)h * a.n_tokens;
+  const float* dh = a.dsum + (int64_t)h * a.n_tokens;
+  const int64_t grow = (int64_t)H * DV;
   // queries that see these keys: from the tile holding key k0 to the document end
-  for (int qb = ds + ((k0 - ds) / ST) * ST; qb < de; qb += ST) {
-    __syncthreads();
-    load_tile<QP>(sQ, a.q + h * DQK, qrow, qb, ST, de, DQK);
-    load_tile<VP>(sG, a.dout + h * DV, (int64_t)H * DV, qb, ST, de, DV);
-    if (threadIdx.x < ST) {
-      const int t = qb + threadIdx.x;
-      sL[threadIdx.x] = t < de ? a.lse[(int64_t)t * H + h] : 0.f;
-      sD[threadIdx.x] = t < de ? a.dsum[(int64_t)t * H + h] : 0.f;
+  const int qb0 = ds + ((k0 - ds) / ST) * ST;
+  const int nt = (de - qb0 + ST - 1) / ST;
+  auto issue = [&](int it, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    const int qb = qb0 + it * ST;
+    cn.issue(qh + (int64_t)qb * qrow, qrow * 2, de - qb, sQn[buf], wave);
+    cr.issue(qh + (int64_t)qb * qrow + DN, qrow * 2, de - qb, sQr[buf], wave);
+    cn.issue(gh + (int64_t)qb * grow, grow * 2, de - qb, sG[buf], wave);
+    if (wave == 0) {
+      const int t = min(qb + lane, de - 1);
+      lds_dma4_raw(lh + t, sL[buf]);
+      lds_dma4_raw(dh + t, sD[buf]);
     }
-    __syncthreads();
-    if (kw0 >= k1 || qb + ST - 1 < kw0) continue;
-    // S [query, key] = Q K^T and dP = dO V^T, two query blocks of 32
-    f32x16 s[2], dp[2];
+  };
+
+  auto step = [&](int it, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    const int qb = qb0 + it * ST;
+    vm_wait_all();
+    wg_barrier();
+    if (it + 1 < nt) issue(it + 1, BufC<buf ^ 1>{});
+    if (kw0 >= k1 || qb + ST - 1 < kw0) return;
+    // one query block of 32 at a time: S [query, key] = Q K^T and
+    // dP = dO V^T on alternating chains (operands read SD ahead),
+    // P = 2^(s c2 - lse[q]) for q >= key (same document), dS = P (dP - D[q]),
+    // then dV^T [dv, key] += dO^T [dv, query] P and dK^T [d, key] += Q^T dS
+    // (operands read PD ahead)
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) { s[mt][e] = 0.f; dp[mt][e] = 0.f; }
       const int qr = mt * 32 + (lane & 31);
+      auto aread = [&](int i) {
+        if (i < 16) {
+          const int ks = i >> 1;
+          return (i & 1) ? *(const bf16x8*)&sG[buf][offn(qr, ks * 16 + hsel * 8)]
+                         : *(const bf16x8*)&sQn[buf][offn(qr, ks * 16 + hsel * 8)];
+        }
+        return *(const bf16x8*)&sQr[buf][offr(qr, (i - 16) * 16 + hsel * 8)];
+      };
+      auto bread = [&](int i) {
+        const int jj = i / 10, b = i % 10, r0 = mt * 32 + jj * 16;
+        return b < 4 ? tr_operand<true>(sG[buf], r0, b * 32, lane)
+                     : b < 8 ? tr_operand<true>(sQn[buf], r0, (b - 4) * 32, lane)
+                             : tr_operand<false>(sQr[buf], r0, (b - 8) * 32, lane);
+      };
+      f32x16 s, dp;
 #pragma unroll
-      for (int ks = 0; ks < DQK / 16; ++ks)
-        s[mt] = mfma32(*(const bf16x8*)&sQ[qr * QP + ks * 16 + hsel * 8], kreg[ks], s[mt]);
+      for (int e = 0; e < 16; ++e) { s[e] = 0.f; dp[e] = 0.f; }
+      bf16x8 af[SD];
 #pragma unroll
-      for (int ks = 0; ks < DV / 16; ++ks)
-        dp[mt] = mfma32(*(const bf16x8*)&sG[qr * VP + ks * 16 + hsel * 8], vreg[ks], dp[mt]);
-    }
-    // P = 2^(s c2 - lse[q]) for q >= key (same document), dS = P (dP - D[q])
-    bf16x8 pb[4], dsb[4];
+      for (int i = 0; i < SD; ++i) af[i] = aread(i);
+      // lse and D of this lane's 16 query rows mt*32 + g*8 + hsel*4 + [0, 4)
+      float4 lq[4], dq4[4];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+      for (int g = 0; g < 4; ++g) {
+        lq[g] = *(const float4*)&sL[buf][mt * 32 + g * 8 + hsel * 4];
+        dq4[g] = *(const float4*)&sD[buf][mt * 32 + g * 8 + hsel * 4];
+      }
+#pragma unroll
+      for (int i = 0; i < 20; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8 cur = af[i % SD];
+        if (i + SD < 20) af[i % SD] = aread(i + SD);
+        if (i < 16 && (i & 1)) dp = mfma32(cur, vreg[i >> 1], dp);
+        else s = mfma32(cur, kreg[i < 16 ? i >> 1 : 8 + (i - 16)], s);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 bf[PD];
+#pragma unroll
+      for (int i = 0; i < PD; ++i) bf[i] = bread(i);
+      bf16x8 pb[2], dsb[2];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int ql = mt * 32 + (e >> 2) * 8 + hsel * 4 + (e & 3);
         const int t = qb + ql;
-        const float p = (t >= my_k && t < de && live) ? __builtin_amdgcn_exp2f(s[mt][e] * c2 - sL[ql]) : 0.f;
-        pb[mt * 2 + (e >> 3)][e & 7] = (bf16)p;
-        dsb[mt * 2 + (e >> 3)][e & 7] = (bf16)(p * (dp[mt][e] - sD[ql]));
+        const float lv = lq[e >> 2][e & 3], dvv = dq4[e >> 2][e & 3];
+        const float p = (t >= my_k && t < de && live) ? __builtin_amdgcn_exp2f(s[e] * c2 - lv) : 0.f;
+        pb[e >> 3][e & 7] = (bf16)p;
+        dsb[e >> 3][e & 7] = (bf16)(p * (dp[e] - dvv));
       }
-    // dV^T [dv, key] += dO^T [dv, query] P [query, key]; dK^T [d, key] += Q^T dS
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r0 = (j >> 1) * 32 + (j & 1) * 16;
-#pragma unroll
-      for (int b = 0; b < DV / 32; ++b) dv[b] = mfma32(tr_operand<VP>(sG, r0, b * 32, lane), pb[j], dv[b]);
-#pragma unroll
-      for (int b = 0; b < DQK / 32; ++b) dk[b] = mfma32(tr_operand<QP>(sQ, r0, b * 32, lane), dsb[j], dk[b]);
+      for (int i = 0; i < 20; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8 cur = bf[i % PD];
+        if (i + PD < 20) bf[i % PD] = bread(i + PD);
+        const int jj = i / 10, b = i % 10;
+        if (b < 4) dv[b] = mfma32(cur, pb[jj], dv[b]);
+        else dk[b - 4] = mfma32(cur, dsb[jj], dk[b - 4]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  issue(0, BufC<0>{});
+  for (int it = 0; it < nt; it += 2) {
+    step(it, BufC<0>{});
+    if (it + 1 < nt) step(it + 1, BufC<1>{});
   }
   if (!live) return;
   // lane holds key my_k, dims b*32 + (e/4)*8 + hsel*4 + e%4
@@ -394,6 +590,8 @@ hipError_t launch_attention_bwd(const AttnBwdArgs& g, const int32_t* cu_host, in
       tiles.push_back({std::min((i + 1) * BT, len), len - i * BT, ((uint32_t)d << 16) | (uint32_t)i});
   }
   BwdPlan plan;
+  plan.by_xcd = g.heads >= 8;
+  const unsigned heads_per_xcd = (unsigned)((g.heads + 7) / 8);
   for (int pass = 0; pass < 3; ++pass) {
     if (pass != 2)
       std::stable_sort(tiles.begin(), tiles.end(), [](const T& x, const T& y) { return x.q_work > y.q_work; });
@@ -402,7 +600,7 @@ hipError_t launch_attention_bwd(const AttnBwdArgs& g, const int32_t* cu_host, in
     for (size_t base = 0; base < tiles.size(); base += MAX_ITEMS) {
       plan.n = (int)std::min<size_t>(MAX_ITEMS, tiles.size() - base);
       for (int i = 0; i < plan.n; ++i) plan.t[i] = tiles[base + i].id;
-      dim3 grid((unsigned)plan.n, (unsigned)g.heads);
+      const unsigned grid = (plan.by_xcd ? 8u * heads_per_xcd : (unsigned)g.heads) * (unsigned)plan.n;
       if (pass == 0) bwd_stats_kernel<<<grid, 256, 0, s>>>(a, plan);
       else if (pass == 1) bwd_dq_kernel<<<grid, 256, 0, s>>>(a, plan);
       else bwd_dkdv_kernel<<<grid, 256, 0, s>>>(a, plan);
