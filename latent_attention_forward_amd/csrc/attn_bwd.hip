@@ -79,11 +79,10 @@ __device__ __forceinline__ int offr(int r, int col) { return r * 64 + (((col >> 
 
 __device__ __forceinline__ bf16x8 zero8b() { return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0)); }
 
-// 4-byte asynchronous global -> LDS copy (lane l lands at lds_base + 4 l);
-// awaited like the 16-byte copies.
-__device__ __forceinline__ void lds_dma4_raw(const void* gsrc, const void* lds_base) {
-  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(MLA_LDS const void*)(lds_base));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" : : "v"(gsrc), "s"(m) : "memory", "m0");
+// 4-byte asynchronous global -> LDS copy (lane l lands at lds_addr + 4 l, a
+// wave-uniform LDS address); awaited like the 16-byte copies.
+__device__ __forceinline__ void lds_dma4_m0(const void* gsrc, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" : : "v"(gsrc), "s"(lds_addr) : "memory", "m0");
 }
 
 // Transposing read of a swizzled tile: the A operand of 32 columns
@@ -134,12 +133,14 @@ struct TileCopy {
     const int pc = P % (W / 8);
     col_bytes = (pc ^ (W == 128 ? swn(row0) : swr(row0))) << 4;
   }
-  // rows at or past `valid` repeat row valid - 1
-  __device__ __forceinline__ void issue(const bf16* base, int64_t row_bytes, int valid, bf16* tile, int wave) const {
+  // rows at or past `valid` repeat row valid - 1; lds_tile: LDS byte address
+  // of the tile, wave: the wave index held in a scalar register
+  __device__ __forceinline__ void issue(const bf16* base, int row_bytes, int valid, uint32_t lds_tile,
+                                        int wave) const {
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
       const int r = min(row0 + i * STEP, valid - 1);
-      lds_dma16_sv(base, (uint32_t)(r * row_bytes + col_bytes), tile + (wave + 4 * i) * 512);
+      lds_dma16_sv_m0(base, (uint32_t)(r * row_bytes + col_bytes), lds_tile + (uint32_t)(wave + 4 * i) * 1024u);
     }
   }
 };
@@ -150,7 +151,7 @@ template <int B> struct BufC { static constexpr int value = B; };
 __global__ __launch_bounds__(256, 2) void bwd_stats_kernel(BwdArgs a, BwdPlan plan) {
   __shared__ __attribute__((aligned(16))) bf16 sKn[2][ST * DN];
   __shared__ __attribute__((aligned(16))) bf16 sKr[2][ST * DR];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int H = a.heads;
   int h;
   uint32_t td;
@@ -175,8 +176,9 @@ __global__ __launch_bounds__(256, 2) void bwd_stats_kernel(BwdArgs a, BwdPlan pl
   auto issue = [&](int it, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
     const int kb = ds + it * ST;
-    cn.issue(kvh + (int64_t)kb * kvrow, kvrow * 2, de - kb, sKn[buf], wave);
-    cr.issue(uniform_ptr(a.kpe + (int64_t)kb * a.kpe_stride), a.kpe_stride * 2, de - kb, sKr[buf], wave);
+    cn.issue(kvh + (int64_t)kb * kvrow, (int)(kvrow * 2), de - kb, lds_addr_of(sKn[buf]), wave);
+    cr.issue(uniform_ptr(a.kpe + (int64_t)kb * a.kpe_stride), (int)(a.kpe_stride * 2), de - kb, lds_addr_of(sKr[buf]),
+             wave);
   };
   const float c2 = a.scale * kLog2e;
   float m = -INFINITY, l = 0.f;
@@ -263,7 +265,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, BwdPlan plan)
   __shared__ __attribute__((aligned(16))) bf16 sKn[2][ST * DN];
   __shared__ __attribute__((aligned(16))) bf16 sKr[2][ST * DR];
   __shared__ __attribute__((aligned(16))) bf16 sV[2][ST * DV];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int H = a.heads;
   int h;
   uint32_t td;
@@ -301,9 +303,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, BwdPlan plan)
   auto issue = [&](int it, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
     const int kb = ds + it * ST;
-    cn.issue(kvh + (int64_t)kb * kvrow, kvrow * 2, de - kb, sKn[buf], wave);
-    cr.issue(uniform_ptr(a.kpe + (int64_t)kb * a.kpe_stride), a.kpe_stride * 2, de - kb, sKr[buf], wave);
-    cn.issue(kvh + (int64_t)kb * kvrow + DN, kvrow * 2, de - kb, sV[buf], wave);
+    cn.issue(kvh + (int64_t)kb * kvrow, (int)(kvrow * 2), de - kb, lds_addr_of(sKn[buf]), wave);
+    cr.issue(uniform_ptr(a.kpe + (int64_t)kb * a.kpe_stride), (int)(a.kpe_stride * 2), de - kb, lds_addr_of(sKr[buf]),
+             wave);
+    cn.issue(kvh + (int64_t)kb * kvrow + DN, (int)(kvrow * 2), de - kb, lds_addr_of(sV[buf]), wave);
   };
 
   auto step = [&](int it, auto bufc) {
@@ -394,7 +397,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, BwdPlan pla
   __shared__ __attribute__((aligned(16))) bf16 sG[2][ST * DV];
   __shared__ __attribute__((aligned(16))) float sL[2][ST];
   __shared__ __attribute__((aligned(16))) float sD[2][ST];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int H = a.heads;
   int h;
   uint32_t td;
@@ -444,13 +447,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, BwdPlan pla
   auto issue = [&](int it, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
     const int qb = qb0 + it * ST;
-    cn.issue(qh + (int64_t)qb * qrow, qrow * 2, de - qb, sQn[buf], wave);
-    cr.issue(qh + (int64_t)qb * qrow + DN, qrow * 2, de - qb, sQr[buf], wave);
-    cn.issue(gh + (int64_t)qb * grow, grow * 2, de - qb, sG[buf], wave);
+    cn.issue(qh + (int64_t)qb * qrow, (int)(qrow * 2), de - qb, lds_addr_of(sQn[buf]), wave);
+    cr.issue(qh + (int64_t)qb * qrow + DN, (int)(qrow * 2), de - qb, lds_addr_of(sQr[buf]), wave);
+    cn.issue(gh + (int64_t)qb * grow, (int)(grow * 2), de - qb, lds_addr_of(sG[buf]), wave);
     if (wave == 0) {
       const int t = min(qb + lane, de - 1);
-      lds_dma4_raw(lh + t, sL[buf]);
-      lds_dma4_raw(dh + t, sD[buf]);
+      lds_dma4_m0(lh + t, lds_addr_of(sL[buf]));
+      lds_dma4_m0(dh + t, lds_addr_of(sD[buf]));
     }
   };
 
@@ -489,13 +492,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, BwdPlan pla
       bf16x8 af[SD];
 #pragma unroll
       for (int i = 0; i < SD; ++i) af[i] = aread(i);
-      // lse and D of this lane's 16 query rows mt*32 + g*8 + hsel*4 + [0, 4)
-      float4 lq[4], dq4[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        lq[g] = *(const float4*)&sL[buf][mt * 32 + g * 8 + hsel * 4];
-        dq4[g] = *(const float4*)&sD[buf][mt * 32 + g * 8 + hsel * 4];
-      }
 #pragma unroll
       for (int i = 0; i < 20; ++i) {
         __builtin_amdgcn_sched_barrier(0);
@@ -508,15 +504,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, BwdPlan pla
       bf16x8 bf[PD];
 #pragma unroll
       for (int i = 0; i < PD; ++i) bf[i] = bread(i);
+      // lse and D of this lane's query rows mt*32 + g*8 + hsel*4 + [0, 4),
+      // read one group of 4 at a time
       bf16x8 pb[2], dsb[2];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int ql = mt * 32 + (e >> 2) * 8 + hsel * 4 + (e & 3);
-        const int t = qb + ql;
-        const float lv = lq[e >> 2][e & 3], dvv = dq4[e >> 2][e & 3];
-        const float p = (t >= my_k && t < de && live) ? __builtin_amdgcn_exp2f(s[e] * c2 - lv) : 0.f;
-        pb[e >> 3][e & 7] = (bf16)p;
-        dsb[e >> 3][e & 7] = (bf16)(p * (dp[e] - dvv));
+      for (int g = 0; g < 4; ++g) {
+        const float4 lq = *(const float4*)&sL[buf][mt * 32 + g * 8 + hsel * 4];
+        const float4 dq4 = *(const float4*)&sD[buf][mt * 32 + g * 8 + hsel * 4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = g * 4 + j;
+          const int t = qb + mt * 32 + g * 8 + hsel * 4 + j;
+          const float p = (t >= my_k && t < de && live) ? __builtin_amdgcn_exp2f(s[e] * c2 - lq[j]) : 0.f;
+          pb[e >> 3][e & 7] = (bf16)p;
+          dsb[e >> 3][e & 7] = (bf16)(p * (dp[e] - dq4[j]));
+        }
       }
 #pragma unroll
       for (int i = 0; i < 20; ++i) {
