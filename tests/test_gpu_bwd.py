@@ -109,7 +109,7 @@ def run_case(mla, sh, lens, seed=0, kpe_in_latent=False):
 
 
 @pytest.mark.parametrize("heads,lens", [(16, [1, 33, 200, 300]), (128, [257]), (32, [64, 128, 129]),
-                                        (128, [1000, 24])])
+                                        (128, [1000, 24]), (8, [5, 0, 130])])
 def test_attention_backward(mla, heads, lens):
     sh = mi.WORKLOADS["dsv3_prefill_4096"].replace(num_heads=heads)
     _say(f"case: attention backward heads={heads} lens={lens}")

@@ -122,6 +122,12 @@ def test_layer_backward_one_token_documents(mla):
     run_case(mla, VARIANTS["v3_yarn_q_lora"], [1, 1, 150, 1], seed=2)
 
 
+def test_layer_backward_empty_document(mla):
+    """An empty document between two others (repeated offset in cu_seqlens)."""
+    _say("case: layer backward, lens=[20, 0, 60]")
+    run_case(mla, VARIANTS["direct_q_plain_rope"], [20, 0, 60], seed=4)
+
+
 def test_layer_backward_megatron_full_size(mla):
     """The Megatron-default layer at its full size: hidden 2048, 16 heads,
     direct q projection, two documents of 2048 tokens."""
