@@ -457,6 +457,16 @@ hipError_t launch_flash_mfma(const FlashArgs& a, bool f16_operands, const int32_
   TilePlan plan;
   plan.heads_per_xcd = (a.heads + 7) / 8;
   plan.group = prefix_total > 0 ? kPrefixTileGroup : 1;
+  // When every workgroup of an XCD is resident at once (at most two per CU,
+  // 32 CUs per XCD), a CU keeps the two it is first given for the whole
+  // launch, slot s beside slot s + 32: then the tiles go longest first across
+  // documents with the second half reversed, so the k-th longest shares a CU
+  // with the k-th shortest (two documents of 2048 tokens, 16 heads: the
+  // busiest CU had 64 key tiles against an average of 34).
+  if (prefix_total == 0 && tiles.size() >= 2 && (int64_t)plan.heads_per_xcd * (int64_t)tiles.size() <= 64) {
+    std::stable_sort(tiles.begin(), tiles.end(), [](const T& x, const T& y) { return x.keys > y.keys; });
+    std::reverse(tiles.begin() + tiles.size() / 2, tiles.end());
+  }
   for (size_t base = 0; base < tiles.size(); base += MAX_TILES) {
     const int n = (int)std::min<size_t>(MAX_TILES, tiles.size() - base);
     plan.n = n;
