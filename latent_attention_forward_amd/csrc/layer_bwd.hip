@@ -38,6 +38,35 @@ __global__ __launch_bounds__(256) void transpose_kernel(const void* src, int64_t
   }
 }
 
+// bf16 source, 16-byte accesses: a 64 x 64 tile is read as rows of 8
+// chunks of 16 bytes, kept in LDS with rows padded to 72 elements, and
+// written as 8 chunks per output row (8 elements gathered down a column);
+// cols, ld_src and ld_dst multiples of 8, rows_pad a multiple of 64,
+// 16-byte aligned base addresses.
+__global__ __launch_bounds__(256) void transpose_vec_kernel(const bf16* src, int64_t ld_src, int rows, int cols,
+                                                            bf16* dst, int64_t ld_dst, int rows_pad) {
+  __shared__ __attribute__((aligned(16))) bf16 t[64][72];
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+  const int seg = (threadIdx.x & 7) * 8, sub = threadIdx.x >> 3;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int r = sub + 32 * it;
+    bf16x8 v = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+    if (r0 + r < rows && c0 + seg < cols) v = *(const bf16x8*)(src + (int64_t)(r0 + r) * ld_src + c0 + seg);
+    *(bf16x8*)&t[r][seg] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int c = sub + 32 * it;
+    if (c0 + c >= cols) continue;
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = t[seg + e][c];
+    *(bf16x8*)(dst + (int64_t)(c0 + c) * ld_dst + r0 + seg) = o;
+  }
+}
+
 // ----------------------------------------------------------------------------- gate
 __device__ __forceinline__ float sigmoid(float x) { return 1.f / (1.f + __expf(-x)); }
 
@@ -91,6 +120,62 @@ __global__ __launch_bounds__(256) void rope_back_kernel(RopeBackArgs a) {
   a.dst[row * a.ld_dst + col] = (bf16)v;
 }
 
+// The same on 8-element chunks (one thread per chunk: two 16-byte loads, one
+// 16-byte store; a rope chunk also loads its partner chunk), for widths, row
+// strides, rope offsets, strides and halves that are multiples of 8 and
+// 16-byte aligned rows.
+__global__ __launch_bounds__(256) void rope_back_vec_kernel(RopeBackArgs a) {
+  const int nch = a.width >> 3;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)a.n_rows * nch) return;
+  const int64_t row = i / nch;
+  const int ch = (int)(i - row * nch), col = ch * 8;
+  const float* src = a.src + row * a.ld_src;
+  const float4 v0 = *(const float4*)(src + col), v1 = *(const float4*)(src + col + 4);
+  float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  const int rel = col - a.rope_off;
+  if (a.rope_slices > 0 && rel >= 0) {
+    const int slice = rel / a.rope_stride, j0 = rel - slice * a.rope_stride;
+    if (slice < a.rope_slices && j0 < a.rope_dim) {
+      const int half = a.rope_dim / 2;
+      const int pos = a.positions[row];
+      const bool ok = pos >= 0 && pos < a.table_len;
+      const float* ct = a.cos_t + (int64_t)(ok ? pos : 0) * half;
+      const float* st = a.sin_t + (int64_t)(ok ? pos : 0) * half;
+      const float nan = __builtin_nanf("");
+      float y[8];
+      if (a.interleave) {
+        // pairs (2i, 2i + 1) inside the chunk, i = j0/2 .. j0/2 + 3
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const int pi = (j0 + e) >> 1;
+          const float c = ok ? ct[pi] : nan, sn = ok ? st[pi] : nan;
+          y[e] = v[e] * c + v[e + 1] * sn;
+          y[e + 1] = v[e + 1] * c - v[e] * sn;
+        }
+      } else {
+        // pairs (i, i + half): the partner chunk is half away
+        const bool first = j0 < half;
+        const int pi0 = first ? j0 : j0 - half;
+        const float* pp = src + col + (first ? half : -half);
+        const float4 p0 = *(const float4*)pp, p1 = *(const float4*)(pp + 4);
+        const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float c = ok ? ct[pi0 + e] : nan, sn = ok ? st[pi0 + e] : nan;
+          y[e] = first ? v[e] * c + pv[e] * sn : v[e] * c - pv[e] * sn;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = y[e];
+    }
+  }
+  bf16x8 o;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = (bf16)v[e];
+  *(bf16x8*)(a.dst + row * a.ld_dst + col) = o;
+}
+
 // ----------------------------------------------------------------------------- RMSNorm backward
 // One wave per row of width <= 64 * 32: x, dy fp32, gamma bf16 -> dx bf16 and
 // 1 / r for the gain's gradient.
@@ -142,6 +227,11 @@ hipError_t launch_transpose_bf16(const void* src, bool src_f32, int64_t ld_src, 
                                  int64_t ld_dst, int rows_pad, hipStream_t s) {
   if (cols <= 0 || rows_pad <= 0) return hipSuccess;
   dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows_pad + 63) / 64));
+  if (!src_f32 && cols % 8 == 0 && ld_src % 8 == 0 && ld_dst % 8 == 0 && rows_pad % 64 == 0 &&
+      (reinterpret_cast<uintptr_t>(src) % 16) == 0 && (reinterpret_cast<uintptr_t>(dst) % 16) == 0) {
+    transpose_vec_kernel<<<grid, 256, 0, s>>>((const bf16*)src, ld_src, rows, cols, dst, ld_dst, rows_pad);
+    return hipGetLastError();
+  }
   if (src_f32) transpose_kernel<true><<<grid, 256, 0, s>>>(src, ld_src, rows, cols, dst, ld_dst, rows_pad);
   else transpose_kernel<false><<<grid, 256, 0, s>>>(src, ld_src, rows, cols, dst, ld_dst, rows_pad);
   return hipGetLastError();
@@ -163,7 +253,16 @@ hipError_t launch_gate_bwd(const float* da2, const bf16* a, const float* g, bf16
 hipError_t launch_rope_back(const RopeBackArgs& a, hipStream_t s) {
   const int64_t n = (int64_t)a.n_rows * a.width;
   if (n <= 0) return hipSuccess;
-  rope_back_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a);
+  const bool rope = a.rope_slices > 0;
+  const bool vec = a.width % 8 == 0 && a.ld_src % 8 == 0 && a.ld_dst % 8 == 0 &&
+                   (reinterpret_cast<uintptr_t>(a.src) % 16) == 0 && (reinterpret_cast<uintptr_t>(a.dst) % 16) == 0 &&
+                   (!rope || (a.rope_off % 8 == 0 && a.rope_stride % 8 == 0 && a.rope_dim % 16 == 0));
+  if (vec) {
+    const int64_t nc = n / 8;
+    rope_back_vec_kernel<<<(unsigned)((nc + 255) / 256), 256, 0, s>>>(a);
+  } else {
+    rope_back_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 
