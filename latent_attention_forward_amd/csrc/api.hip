@@ -424,7 +424,7 @@ static mla_status attention_impl(const mla_config* cfg, const void* q, const voi
                                  int64_t kpe_stride, bool f16_operands, const int32_t* cu_dev,
                                  const int32_t* cu_host, int num_seqs, int n, void* attn, hipStream_t st,
                                  const int32_t* cuk_dev = nullptr, const int32_t* cuk_host = nullptr,
-                                 int n_keys = -1) {
+                                 int n_keys = -1, float* lse_out = nullptr) {
   // the MFMA kernel addresses the 64 key rows of a tile with 32-bit byte offsets
   if (cfg->dtype == MLA_BF16 &&
       (64 * kpe_stride * 2 >= ((int64_t)1 << 31) ||
@@ -434,7 +434,7 @@ static mla_status attention_impl(const mla_config* cfg, const void* q, const voi
   f.q = q; f.kv = kv; f.kpe = kpe; f.kpe_stride = kpe_stride; f.cu_dev = cu_dev; f.out = attn;
   f.n_tokens = n; f.heads = cfg->num_heads; f.nope = cfg->qk_nope_dim; f.rope = cfg->qk_rope_dim;
   f.dv = cfg->v_head_dim; f.kv_lora = cfg->kv_lora_rank; f.scale = scale_of(cfg); f.num_seqs = num_seqs;
-  f.cuk_dev = cuk_dev; f.n_keys = cuk_dev ? n_keys : n;
+  f.cuk_dev = cuk_dev; f.n_keys = cuk_dev ? n_keys : n; f.lse_out = lse_out;
   const hipError_t e = cfg->dtype == MLA_BF16 ? launch_flash_mfma(f, f16_operands, cu_host, cuk_host, num_seqs, st)
                                               : launch_flash_f32(f, st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
@@ -1103,8 +1103,10 @@ mla_status mla_prefill_bwd(const mla_config* cfg, const mla_weights* w, const vo
   if ((s = norm(ckv32, lw, lw, rkv, w->kv_a_gamma, rkv, rope ? 1 : 0, lat, lw)) != MLA_OK) return s;
   if ((s = gemm(lat, lw, w->w_kv_b, rkv, kv, (int64_t)H * dkvw, n, H * dkvw, rkv, false, false, false)) != MLA_OK)
     return s;
-  if ((s = attention_impl(cfg, q, kv, lat + rkv, lw, false, cu_seqlens_dev, cu_seqlens_host, num_seqs, n, attn, st)) !=
-      MLA_OK)
+  // the forward leaves its softmax statistics for the attention backward
+  float* lse_fwd = (float*)at(L.abw);
+  if ((s = attention_impl(cfg, q, kv, lat + rkv, lw, false, cu_seqlens_dev, cu_seqlens_host, num_seqs, n, attn, st,
+                          nullptr, nullptr, -1, lse_fwd)) != MLA_OK)
     return s;
   const bf16* a2 = attn;                         // the output projection's input
   float* gpre = (float*)at(L.gpre);
@@ -1162,6 +1164,7 @@ mla_status mla_prefill_bwd(const mla_config* cfg, const mla_weights* w, const vo
     a.dsum = (float*)(aw + align256((size_t)n * H * 4));
     a.dkr = (float*)(aw + 2 * align256((size_t)n * H * 4));
     a.dq = dq32; a.dkv = dkv32; a.dkpe = dkpe32;
+    a.lse_ready = true;
     if ((e = launch_attention_bwd(a, cu_seqlens_host, num_seqs, st)) != hipSuccess) return hip_fail(e, "attention backward");
   }
   // ---- RoPE backward, bf16 gradients

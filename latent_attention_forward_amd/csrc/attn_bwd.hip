@@ -10,7 +10,8 @@
 // Three passes, each on 32x32x16 bf16 MFMAs:
 //   1. stats: per (head, query) the log-sum-exp of the scaled scores in
 //      base-2 units (the forward's softmax statistics, recomputed: one QK^T
-//      pass) and D;
+//      pass) and D; skipped when the forward left its log-sum-exp (the dq
+//      pass then forms D);
 //   2. dq, query-major (workgroup = 128 queries of one head, keys in tiles of
 //      64): S^T = K Q^T and dP^T = V dO^T from the recomputed P^T, then
 //      dQ^T += K^T dS^T, K^T by transposing LDS reads;
@@ -68,6 +69,7 @@ struct BwdArgs {
   float* dkv;                        // [N, H, 256] = [dk_nope | dv]
   float* dkr;                        // [N, H, 64] per-head gradient of the shared key part
   float* dkpe;                       // [N, 64]
+  int d_in_dq;                       // the dq pass forms D (lse given by the forward)
 };
 
 // chunk swizzles (bits of the row permuted; see the header)
@@ -288,7 +290,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, BwdPlan plan)
     greg[ks] = live ? *(const bf16x8*)(a.dout + ((int64_t)my_q * H + h) * DV + ks * 16 + hsel * 8) : zero8b();
   const float c2 = a.scale * kLog2e;
   const float lse = live ? a.lse[(int64_t)h * a.n_tokens + my_q] : 0.f;
-  const float dsum = live ? a.dsum[(int64_t)h * a.n_tokens + my_q] : 0.f;
+  float dsum;
+  if (a.d_in_dq) {
+    // D = rowsum(dO * O) over the dims this lane holds of dO, then the other half
+    float d = 0.f;
+    if (live) {
+      const bf16* orow = a.o + ((int64_t)my_q * H + h) * DV + hsel * 8;
+#pragma unroll
+      for (int ks = 0; ks < DV / 16; ++ks) {
+        const bf16x8 ov = *(const bf16x8*)(orow + ks * 16);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d = fmaf((float)ov[e], (float)greg[ks][e], d);
+      }
+    }
+    d += __shfl_xor(d, 32, 64);
+    dsum = d;
+    if (live && hsel == 0) a.dsum[(int64_t)h * a.n_tokens + my_q] = d;
+  } else {
+    dsum = live ? a.dsum[(int64_t)h * a.n_tokens + my_q] : 0.f;
+  }
   f32x16 acc[DQK / 32];
 #pragma unroll
   for (int b = 0; b < DQK / 32; ++b)
@@ -580,6 +600,7 @@ hipError_t launch_attention_bwd(const AttnBwdArgs& g, const int32_t* cu_host, in
   a.q = (const bf16*)g.q; a.kv = (const bf16*)g.kv; a.kpe = (const bf16*)g.kpe; a.kpe_stride = g.kpe_stride;
   a.o = (const bf16*)g.o; a.dout = (const bf16*)g.dout; a.cu = g.cu_dev; a.n_tokens = g.n_tokens; a.heads = g.heads;
   a.scale = g.scale; a.lse = g.lse; a.dsum = g.dsum; a.dq = g.dq; a.dkv = g.dkv; a.dkr = g.dkr; a.dkpe = g.dkpe;
+  a.d_in_dq = g.lse_ready ? 1 : 0;
   if (g.n_tokens <= 0) return hipSuccess;
   // every (document, 128-row tile); the query-major passes take the tiles
   // with the longest key range first, the key-major pass those with the
@@ -594,7 +615,7 @@ hipError_t launch_attention_bwd(const AttnBwdArgs& g, const int32_t* cu_host, in
   BwdPlan plan;
   plan.by_xcd = g.heads >= 8;
   const unsigned heads_per_xcd = (unsigned)((g.heads + 7) / 8);
-  for (int pass = 0; pass < 3; ++pass) {
+  for (int pass = g.lse_ready ? 1 : 0; pass < 3; ++pass) {
     if (pass != 2)
       std::stable_sort(tiles.begin(), tiles.end(), [](const T& x, const T& y) { return x.q_work > y.q_work; });
     else

@@ -362,6 +362,7 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashArgs a, TilePla
   if (my_q >= q1) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = 1.f / l_tot;
+  if (a.lse_out && hsel == 0) a.lse_out[(int64_t)head * a.n_tokens + my_q] = m_ref + __builtin_log2f(l_tot);
   bf16* orow = O + (int64_t)my_q * H * DV + head * DV;
 #pragma unroll
   for (int d = 0; d < DV / 32; ++d)

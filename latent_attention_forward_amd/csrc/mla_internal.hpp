@@ -266,6 +266,10 @@ struct FlashArgs {
   const int32_t* cuk_dev; int n_keys;
   int n_tokens; int heads; int nope; int rope; int dv; int kv_lora;
   float scale; int num_seqs;
+  // optional [heads, n_tokens]: per (head, query) the base-2 log-sum-exp of
+  // scale * q.k (m + log2 l of the softmax as formed), for a backward;
+  // MFMA kernel, queries without a cached prefix
+  float* lse_out;
 };
 // MFMA kernel (nope 128, rope 64, dv 128) with bf16 or fp16 operands (q, kv,
 // kpe of that type); the output is bf16.  The tile plan is built from the host
@@ -281,8 +285,9 @@ struct AttnBwdArgs {
   const void* q; const void* kv; const void* kpe; int64_t kpe_stride;
   const void* o; const void* dout;
   const int32_t* cu_dev; int n_tokens; int heads; float scale;
-  float* lse; float* dsum; float* dkr;                 // [N, H], [N, H], [N, H, 64]
+  float* lse; float* dsum; float* dkr;                 // [H, N], [H, N], [N, H, 64]
   float* dq; float* dkv; float* dkpe;                  // [N, H, 192], [N, H, 256], [N, 64]
+  bool lse_ready;   // lse holds the forward's values: no statistics pass, D formed in the dq pass
 };
 hipError_t launch_attention_bwd(const AttnBwdArgs& a, const int32_t* cu_host, int num_seqs, hipStream_t s);
 
