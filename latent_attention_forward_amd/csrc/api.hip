@@ -920,7 +920,7 @@ mla_status mla_attention_prefill_bwd(const mla_config* cfg, const void* q, const
 namespace {
 struct LayerBwdWs {
   size_t pos, q_lat32, q_lat, q, ckv32, lat, kv, attn, gpre, a2, ot, dt, da2, da, dg, dq32, dkv32, dkpe32, abw,
-      dq16, dkv16, dckv, dcn32, dqln32, dql16, rinv, part, tr, total;
+      dq16, dkv16, dckv, dcn32, dqln32, dql16, rinv, part, tr, trb, xt, wot, total;
   int64_t npad;
 };
 
@@ -960,7 +960,10 @@ LayerBwdWs layer_bwd_layout(const mla_config* c, int64_t n) {
   w.rinv = take(n * 4);
   w.part = take((n + 255) / 256 * std::max(rkv, rq) * 4);
   const int64_t tcols = std::max({(int64_t)c->hidden, F, H * dkv, H * dqk, lw, rq, gro});
-  w.tr = take(tcols * w.npad * 2);
+  w.tr = take(tcols * w.npad * 2);                       // dY^T of a weight gradient
+  w.trb = take(std::max({F, rq, rkv, gro}) * w.npad * 2);  // X^T of a weight gradient
+  w.xt = take((int64_t)c->hidden * w.npad * 2);           // x^T (three weight gradients read it)
+  w.wot = take(c->o_groups > 0 ? 0 : F * c->hidden * 2);  // W_o^T (NT form of dA2 = dout W_o)
   w.total = off;
   return w;
 }
@@ -1041,15 +1044,27 @@ mla_status mla_prefill_bwd(const mla_config* cfg, const mla_weights* w, const vo
     const hipError_t err = launch_gemm_bf16(g, st);
     return err == hipSuccess ? MLA_OK : hip_fail(err, "layer backward GEMM");
   };
-  // dW [cols(dy), cols(xin)] = dy^T xin over the n tokens: dy transposed (and
-  // rounded to bf16) into the K-major buffer, then an NN product
+  // dW [cols(dy), cols(xin)] = dy^T xin over the n tokens: dy and xin
+  // transposed (rounded to bf16, zero past the last token) into K-major
+  // buffers, then an NT product over the padded token count (x^T, which three
+  // gradients read, is transposed once)
+  bf16* trb = (bf16*)at(L.trb);
+  bf16* xt = (bf16*)at(L.xt);
+  bool xt_ready = false;
   auto weight_grad = [&](const void* dy, bool dy_f32, int64_t ld_dy, int dy_cols, const void* xin, int64_t ld_x,
-                         int x_cols, float* out, int batch = 1, int64_t abs = 0, int64_t bbs = 0,
-                         int64_t cbs = 0, int m_rows = -1, int n_cols = -1) -> mla_status {
-    const hipError_t err = launch_transpose_bf16(dy, dy_f32, ld_dy, n, dy_cols, tr, npad, (int)npad, st);
+                         int x_cols, float* out) -> mla_status {
+    hipError_t err = launch_transpose_bf16(dy, dy_f32, ld_dy, n, dy_cols, tr, npad, (int)npad, st);
     if (err != hipSuccess) return hip_fail(err, "transpose");
-    return gemm(tr, npad, xin, ld_x, out, n_cols > 0 ? n_cols : x_cols, m_rows > 0 ? m_rows : dy_cols,
-                n_cols > 0 ? n_cols : x_cols, n, true, true, false, EPI_STORE, batch, abs, bbs, cbs);
+    const bf16* bt = trb;
+    if (xin == x) {
+      if (!xt_ready && (err = launch_transpose_bf16(x, false, hid, n, hid, xt, npad, (int)npad, st)) != hipSuccess)
+        return hip_fail(err, "transpose");
+      xt_ready = true;
+      bt = xt;
+    } else if ((err = launch_transpose_bf16(xin, false, ld_x, n, x_cols, trb, npad, (int)npad, st)) != hipSuccess) {
+      return hip_fail(err, "transpose");
+    }
+    return gemm(tr, npad, bt, npad, out, x_cols, dy_cols, x_cols, (int)npad, false, true, false);
   };
   auto norm = [&](const void* src, int64_t stride, int width, int norm_dim, const void* gamma, int rope_off,
                   int rope_slices, void* dst, int64_t dst_stride) -> mla_status {
@@ -1139,7 +1154,11 @@ mla_status mla_prefill_bwd(const mla_config* cfg, const mla_weights* w, const vo
       return s;
   } else {
     if ((s = weight_grad(dout, false, hid, hid, a2, F, F, dw->w_o)) != MLA_OK) return s;
-    if ((s = gemm(dout, hid, w->w_o, F, da2, F, n, F, hid, true, true, false)) != MLA_OK) return s;
+    // dA2 = dout W_o as an NT product against W_o^T
+    bf16* wot = (bf16*)at(L.wot);
+    if ((e = launch_transpose_bf16(w->w_o, false, F, hid, F, wot, hid, hid, st)) != hipSuccess)
+      return hip_fail(e, "transpose");
+    if ((s = gemm(dout, hid, wot, hid, da2, F, n, F, hid, false, true, false)) != MLA_OK) return s;
   }
   // ---- gate
   bf16* da = (bf16*)at(L.da);

@@ -240,7 +240,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmArgs g) {
 constexpr int GBM = 256, GBN = 256, GBK = 32, GSTAGES = 4;
 __device__ __forceinline__ int gsw(int r, int c) { return r * GBK + ((c ^ ((r >> 2) & 3)) << 3); }
 
-template <int EPI, int CT>   // CT: 0 bf16, 2 fp16, 3 MXFP8 (E4M3 codes + E8M0 block scales) output
+template <int EPI, int CT>   // CT: 0 bf16, 1 fp32, 2 fp16, 3 MXFP8 (E4M3 codes + E8M0 block scales) output
 __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g) {
   // operand stages, then (after the K loop) the 256x256 output tile in 16-bit
   // values: row r of 512 B with 16-byte chunk c at c ^ (r & 31)
@@ -387,6 +387,33 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g) {
         }
       }
     }
+  }
+
+  if constexpr (CT == 1) {
+    // fp32 output (plain store): the lane's 4 consecutive columns of a row
+    // leave as one 16-byte store, added to what C holds with c_acc
+    float* C = (float*)g.c + (int64_t)blockIdx.z * g.c_bstride;
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) {
+        const int m = m0 + wm * 128 + mi * 32 + r32;
+        if (m >= g.m) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + wn * 128 + ni * 32 + q * 8 + hs * 4;
+          if (n >= g.n) continue;
+          float4 v = make_float4(acc[ni][mi][q * 4 + 0], acc[ni][mi][q * 4 + 1], acc[ni][mi][q * 4 + 2],
+                                 acc[ni][mi][q * 4 + 3]);
+          float4* cp = (float4*)(C + (int64_t)m * g.ldc + n);
+          if (g.c_acc) {
+            const float4 o = *cp;
+            v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+          }
+          *cp = v;
+        }
+      }
+    return;
   }
 
   if constexpr (CT == 3) {
@@ -559,7 +586,8 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
   // strides, 256 rows of an operand within 32-bit byte offsets)
   {
     const int64_t bm = (g.m + GBM - 1) / GBM, bn = (g.n + GBN - 1) / GBN;
-    const bool fits = !g.b_kn && ct != 1 && g.k >= GBK && g.k % GBK == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 &&
+    const bool fits = !g.b_kn && (ct != 1 || (g.epilogue == EPI_STORE && g.ldc % 4 == 0 && g.n % 4 == 0)) &&
+                      g.k >= GBK && g.k % GBK == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 &&
                       g.a_bstride % 8 == 0 && g.b_bstride % 8 == 0 && (int64_t)GBM * g.lda * 2 < ((int64_t)1 << 31) &&
                       (int64_t)GBN * g.ldb * 2 < ((int64_t)1 << 31) &&
                       (g.epilogue != EPI_ROPE || (g.rope_head_stride % 64 == 0 && g.rope_off % 64 == 0));
@@ -573,6 +601,8 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
         else gemm_bf16_big_kernel<EPI_ROPE, 0><<<gb, 256, 0, s>>>(g);
       } else if (ct == 2) {
         gemm_bf16_big_kernel<EPI_STORE, 2><<<gb, 256, 0, s>>>(g);
+      } else if (ct == 1) {
+        gemm_bf16_big_kernel<EPI_STORE, 1><<<gb, 256, 0, s>>>(g);
       } else {
         gemm_bf16_big_kernel<EPI_STORE, 0><<<gb, 256, 0, s>>>(g);
       }
