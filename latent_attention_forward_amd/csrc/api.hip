@@ -920,9 +920,13 @@ mla_status mla_attention_prefill_bwd(const mla_config* cfg, const void* q, const
 namespace {
 struct LayerBwdWs {
   size_t pos, q_lat32, q_lat, q, ckv32, lat, kv, attn, gpre, a2, ot, dt, da2, da, dg, dq32, dkv32, dkpe32, abw,
-      dq16, dkv16, dckv, dcn32, dqln32, dql16, rinv, part, tr, trb, xt, wot, total;
+      dq16, dkv16, dckv, dcn32, dqln32, dql16, rinv, part, tr, trb, xt, wot, split, total;
   int64_t npad;
 };
+
+// the latent-side NN products of the layer backward (K = H * 256 or H * 192,
+// few output tiles) run as kSplitK products over K slices, summed after
+constexpr int kSplitK = 4;
 
 LayerBwdWs layer_bwd_layout(const mla_config* c, int64_t n) {
   const int64_t H = c->num_heads, rq = c->q_lora_rank, rkv = c->kv_lora_rank, dr = c->qk_rope_dim;
@@ -964,6 +968,7 @@ LayerBwdWs layer_bwd_layout(const mla_config* c, int64_t n) {
   w.trb = take(std::max({F, rq, rkv, gro}) * w.npad * 2);  // X^T of a weight gradient
   w.xt = take((int64_t)c->hidden * w.npad * 2);           // x^T (three weight gradients read it)
   w.wot = take(c->o_groups > 0 ? 0 : F * c->hidden * 2);  // W_o^T (NT form of dA2 = dout W_o)
+  w.split = take(kSplitK * n * std::max(rkv, rq) * 4);     // split-K partials of dc_n and dq_lat_n
   w.total = off;
   return w;
 }
@@ -1065,6 +1070,20 @@ mla_status mla_prefill_bwd(const mla_config* cfg, const mla_weights* w, const vo
       return hip_fail(err, "transpose");
     }
     return gemm(tr, npad, bt, npad, out, x_cols, dy_cols, x_cols, (int)npad, false, true, false);
+  };
+  // c [m, nn] fp32 = a [m, k] b [k, nn] (NN) as kSplitK products over slices
+  // of k (batched, into partial buffers) and their sum
+  auto gemm_nn_splitk = [&](const void* a, int64_t lda, const void* b, int64_t ldb, float* c, int m, int nn,
+                            int k) -> mla_status {
+    float* part = (float*)at(L.split);
+    if (k % (kSplitK * 8) != 0 || (int64_t)m * nn % 4 != 0)
+      return gemm(a, lda, b, ldb, c, nn, m, nn, k, true, true, false);
+    const int ks = k / kSplitK;
+    mla_status r = gemm(a, lda, b, ldb, part, nn, m, nn, ks, true, true, false, EPI_STORE, kSplitK, ks,
+                        (int64_t)ks * ldb, (int64_t)m * nn);
+    if (r != MLA_OK) return r;
+    const hipError_t err = launch_sum_partials(part, kSplitK, (int64_t)m * nn, c, st);
+    return err == hipSuccess ? MLA_OK : hip_fail(err, "split-K sum");
   };
   auto norm = [&](const void* src, int64_t stride, int width, int norm_dim, const void* gamma, int rope_off,
                   int rope_slices, void* dst, int64_t dst_stride) -> mla_status {
@@ -1196,8 +1215,7 @@ mla_status mla_prefill_bwd(const mla_config* cfg, const mla_weights* w, const vo
   // ---- kv up-projection, latent norm, joint down-projection
   float* dcn32 = (float*)at(L.dcn32);
   if ((s = weight_grad(dkv16, false, (int64_t)H * dkvw, H * dkvw, lat, lw, rkv, dw->w_kv_b)) != MLA_OK) return s;
-  if ((s = gemm(dkv16, (int64_t)H * dkvw, w->w_kv_b, rkv, dcn32, rkv, n, rkv, H * dkvw, true, true, false)) != MLA_OK)
-    return s;
+  if ((s = gemm_nn_splitk(dkv16, (int64_t)H * dkvw, w->w_kv_b, rkv, dcn32, n, rkv, H * dkvw)) != MLA_OK) return s;
   if ((s = norm_back(ckv32, lw, dcn32, rkv, w->kv_a_gamma, rkv, dckv, lw, dw->kv_a_gamma)) != MLA_OK) return s;
   if ((s = weight_grad(dckv, false, lw, lw, x, hid, hid, dw->w_kv_a)) != MLA_OK) return s;
   if ((s = gemm(dckv, lw, w->w_kv_a, hid, dx, hid, n, hid, lw, true, true, false)) != MLA_OK) return s;
@@ -1206,8 +1224,7 @@ mla_status mla_prefill_bwd(const mla_config* cfg, const mla_weights* w, const vo
     float* dqln32 = (float*)at(L.dqln32);
     bf16* dql16 = (bf16*)at(L.dql16);
     if ((s = weight_grad(dq16, false, (int64_t)H * dqk, H * dqk, q_lat, rq, rq, dw->w_q_b)) != MLA_OK) return s;
-    if ((s = gemm(dq16, (int64_t)H * dqk, w->w_q_b, rq, dqln32, rq, n, rq, H * dqk, true, true, false)) != MLA_OK)
-      return s;
+    if ((s = gemm_nn_splitk(dq16, (int64_t)H * dqk, w->w_q_b, rq, dqln32, n, rq, H * dqk)) != MLA_OK) return s;
     if ((s = norm_back(q_lat32, rq, dqln32, rq, w->q_a_gamma, rq, dql16, rq, dw->q_a_gamma)) != MLA_OK) return s;
     if ((s = weight_grad(dql16, false, rq, rq, x, hid, hid, dw->w_q_a)) != MLA_OK) return s;
     if ((s = gemm(dql16, rq, w->w_q_a, hid, dx, hid, n, hid, rq, true, true, true)) != MLA_OK) return s;

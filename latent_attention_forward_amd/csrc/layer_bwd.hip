@@ -221,7 +221,26 @@ __global__ __launch_bounds__(256) void dgamma_sum_kernel(const float* part, int 
   dgamma[c] = s;
 }
 
+// out[i] = sum over s of part[s * count + i], four floats per thread
+__global__ __launch_bounds__(256) void sum_partials_kernel(const float* part, int splits, int64_t count, float* out) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= count) return;
+  float4 acc = *(const float4*)(part + i);
+  for (int sp = 1; sp < splits; ++sp) {
+    const float4 v = *(const float4*)(part + (int64_t)sp * count + i);
+    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  }
+  *(float4*)(out + i) = acc;
+}
+
 }  // namespace
+
+hipError_t launch_sum_partials(const float* part, int splits, int64_t count, float* out, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  if (count % 4) return hipErrorInvalidValue;
+  sum_partials_kernel<<<(unsigned)((count / 4 + 255) / 256), 256, 0, s>>>(part, splits, count, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_transpose_bf16(const void* src, bool src_f32, int64_t ld_src, int rows, int cols, bf16* dst,
                                  int64_t ld_dst, int rows_pad, hipStream_t s) {

@@ -315,6 +315,9 @@ struct RmsNormBwdArgs {
   bf16* dx; int64_t ld_dx;                         // gradient of its input
   float* rinv;                                     // [n_rows] 1 / r (scratch)
 };
+// out[i] = sum over s < splits of part[s * count + i] (count a multiple of 4,
+// 16-byte aligned): the split-K partial products of a GEMM.
+hipError_t launch_sum_partials(const float* part, int splits, int64_t count, float* out, hipStream_t s);
 // dx and dgamma [width]; partials: (n_rows + 255) / 256 * width floats of scratch.
 hipError_t launch_rms_norm_bwd(const RmsNormBwdArgs& a, float* partials, float* dgamma, hipStream_t s);
 
