@@ -34,11 +34,15 @@
 // another (longest first).  When the queries follow a cached prefix (keys
 // offset per document, see FlashArgs), every tile of a document streams the
 // whole prefix, and the tiles of one head are issued in groups that run
-// together instead.
+// together instead.  A launch small enough that all its workgroups would be
+// resident at once, two to a CU, runs paired instead (8-wave workgroups, one
+// per CU, a long and a short tile shared out evenly between two halves; see
+// the kernel).
 #include "mla_internal.hpp"
 
 #include <vector>
 #include <algorithm>
+#include <type_traits>
 
 namespace mla {
 namespace {
@@ -82,46 +86,116 @@ __device__ __forceinline__ int kr_off(int r, int c) { return r * DR + ((c ^ ksw_
 __device__ __forceinline__ int vsw(int r, int c) { return c ^ ((r & 3) << 2); }
 __device__ __forceinline__ int voff(int r, int n) { return r * DV + (vsw(r, n >> 3) << 3) + (n & 7); }
 
-template <typename T>
-__global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashArgs a, TilePlan plan) {
-  typedef typename Vec<T>::v8 V8;
-  typedef typename Vec<T>::v4 V4;
-  __shared__ __attribute__((aligned(16))) T sKn[2][FK * DN];
-  __shared__ __attribute__((aligned(16))) T sKr[2][FK * DR];
-  __shared__ __attribute__((aligned(16))) T sV[2][FK * DV];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int H = a.heads;
-  // workgroup -> (head, tile): XCD x = blockIdx % 8 takes heads x, x+8, ...;
-  // within an XCD the plan's tiles go out in groups of plan.group, each group
-  // head by head and the group's tiles of one head back to back (a group of 1:
-  // tile index major across all the XCD's heads)
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int hpx = plan.heads_per_xcd, tg = plan.group;
-  const int gbase = slot / (tg * hpx) * tg, gs = min(tg, plan.n - gbase);
-  const int rem = slot - gbase * hpx;
-  const int hj = rem / gs, ti = gbase + rem - hj * gs;
-  const int head = xcd + 8 * hj;
-  if (head >= H) return;
-  const uint32_t td = plan.t[ti];
+// Geometry of one 128-query tile of a document (keys as described in FlashArgs).
+struct TileGeom {
+  int q0, q1;     // query rows [q0, q1); empty when q0 >= q1
+  int kst, kend;  // keys [kst, kend) are seen by some query of the tile
+  int koff;       // query row t sees keys up to t + koff
+  int ntiles;     // key tiles of FK from kst
+};
+__device__ __forceinline__ TileGeom tile_geom(const FlashArgs& a, uint32_t td) {
   const int doc = (int)(td >> 16), tix = (int)(td & 0xffff);
   const int ds = max(0, min(a.cu_dev[doc], a.n_tokens));
   const int de = max(ds, min(a.cu_dev[doc + 1], a.n_tokens));
-  // keys of the document: rows [kst, ...); query row t sees keys up to t + koff
-  int kst = ds, koff = 0;
+  TileGeom g;
+  g.kst = ds;
+  g.koff = 0;
+  g.q0 = ds + tix * FQ;
   if (a.cuk_dev) {
     const int k_s = max(0, min(a.cuk_dev[doc], a.n_keys));
     const int k_e = max(k_s, min(a.cuk_dev[doc + 1], a.n_keys));
-    if (k_e - k_s < de - ds) return;       // fewer keys than queries: rejected by the host
-    kst = k_s;
-    koff = k_e - de;
+    if (k_e - k_s < de - ds) {
+      g.q0 = de;                           // fewer keys than queries: rejected by the host
+    } else {
+      g.kst = k_s;
+      g.koff = k_e - de;
+    }
   }
-  const int q0 = ds + tix * FQ;
-  if (q0 >= de) return;
-  const int q1 = min(q0 + FQ, de);
-  const int kend = q1 + koff;              // keys [kst, kend) are seen by some query of the tile
-  const int ntiles = (kend - kst + FK - 1) / FK;
+  g.q1 = min(g.q0 + FQ, de);
+  g.kend = g.q1 + g.koff;
+  g.ntiles = g.q0 < g.q1 ? (g.kend - g.kst + FK - 1) / FK : 0;
+  return g;
+}
+constexpr uint32_t kNoTile = 0xffffffffu;
+
+// PAIRED: an 8-wave workgroup of two halves of 4 waves, for launches whose
+// workgroups all run at once (one per CU).  The plan gives each workgroup a
+// long tile and a short one of the same head (the k-th longest with the k-th
+// shortest); half 0 walks the long tile's first key tiles, half 1 the short
+// tile and then the rest of the long one, the split chosen so that both walk
+// about the same number of key tiles; at the end half 1 merges half 0's
+// partial result for the long tile (log-sum-exp weights) and stores it.
+// Both halves pass the same barriers (one per step; the shorter walk idles).
+template <typename T, bool PAIRED>
+__global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void flash_mfma_kernel(FlashArgs a, TilePlan plan) {
+  typedef typename Vec<T>::v8 V8;
+  typedef typename Vec<T>::v4 V4;
+  constexpr int NHALF = PAIRED ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) T sKn_[NHALF][2][FK * DN];
+  __shared__ __attribute__((aligned(16))) T sKr_[NHALF][2][FK * DR];
+  __shared__ __attribute__((aligned(16))) T sV_[NHALF][2][FK * DV];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = PAIRED ? (wid & 3) : wid;     // wave within its half
+  const int half = PAIRED ? (wid >> 2) : 0;
+  T (*sKn)[FK * DN] = sKn_[half];
+  T (*sKr)[FK * DR] = sKr_[half];
+  T (*sV)[FK * DV] = sV_[half];
+  const int H = a.heads;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int hpx = plan.heads_per_xcd;
+  // this half's walk: item 0 = key tiles [t00, t00 + n0) of tile g0, then
+  // item 1 = key tiles [t10, t10 + n1) of tile g1; nsteps = loop steps of the
+  // workgroup (the longer walk of its halves)
+  int head;
+  TileGeom g0, g1;
+  int t00 = 0, n0 = 0, t10 = 0, n1 = 0, nsteps = 0;
+  bool merge = false;
+  if constexpr (!PAIRED) {
+    // workgroup -> (head, tile): XCD x = blockIdx % 8 takes heads x, x+8, ...;
+    // within an XCD the plan's tiles go out in groups of plan.group, each
+    // group head by head and the group's tiles of one head back to back (a
+    // group of 1: tile index major across all the XCD's heads)
+    const int tg = plan.group;
+    const int gbase = slot / (tg * hpx) * tg, gs = min(tg, plan.n - gbase);
+    const int rem = slot - gbase * hpx;
+    const int hj = rem / gs, ti = gbase + rem - hj * gs;
+    head = xcd + 8 * hj;
+    if (head >= H) return;
+    g0 = tile_geom(a, plan.t[ti]);
+    if (g0.q0 >= g0.q1) return;
+    n0 = g0.ntiles;
+    nsteps = n0;
+    g1 = g0;
+  } else {
+    // workgroup -> (head, pair): XCD x takes heads x, x+8, ..., each head's
+    // plan.n pairs back to back
+    const int hj = slot / plan.n, p = slot - hj * plan.n;
+    head = xcd + 8 * hj;
+    if (head >= H) return;
+    const TileGeom gb = tile_geom(a, plan.t[2 * p]);
+    const uint32_t tsm = plan.t[2 * p + 1];
+    const TileGeom gsm = tile_geom(a, tsm == kNoTile ? plan.t[2 * p] : tsm);
+    const int nb = gb.ntiles, ns = tsm == kNoTile ? 0 : gsm.ntiles;
+    const int split = min(nb, (nb + ns + 1) >> 1);   // long-tile key tiles walked by half 0
+    merge = split < nb;
+    nsteps = max(split, ns + nb - split);
+    g0 = gb;
+    g1 = gb;
+    if (half == 0) {
+      n0 = split;
+    } else if (ns > 0) {
+      g0 = gsm;
+      n0 = ns;
+      t10 = split;
+      n1 = nb - split;
+    } else {
+      t00 = split;
+      n0 = nb - split;
+    }
+  }
+  const int nmine = n0 + n1;
 
   const T* Q = (const T*)a.q;
   const T* KV = (const T*)a.kv;
@@ -129,14 +203,19 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashArgs a, TilePla
   bf16* O = (bf16*)a.out;
   const int64_t q_row = (int64_t)H * DQK, kv_row = (int64_t)H * (DN + DV);
 
-  // ---- this wave's queries, held as the B operand (Q^T) for 12 k-steps of 16
-  const int qw0 = q0 + wave * 32;
-  const int my_q = qw0 + (lane & 31);
+  // the item being walked: its keys, and this wave's queries
+  int c_kst = g0.kst, c_kend = g0.kend, c_koff = g0.koff, c_q1 = g0.q1, c_t0 = t00;
+  int qw0 = g0.q0 + wave * 32;
+  int my_q = qw0 + (lane & 31);
   const int hsel = lane >> 5;
+  // ---- this wave's queries, held as the B operand (Q^T) for 12 k-steps of 16
   V8 qreg[DQK / 16];
+  auto load_q = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int ks = 0; ks < DQK / 16; ++ks)
-    qreg[ks] = (my_q < q1) ? *(const V8*)(Q + my_q * q_row + head * DQK + ks * 16 + hsel * 8) : zero8<V8>();
+    for (int ks = 0; ks < DQK / 16; ++ks)
+      qreg[ks] = (my_q < c_q1) ? *(const V8*)(Q + my_q * q_row + head * DQK + ks * 16 + hsel * 8) : zero8<V8>();
+  };
+  load_q();
 
   // ---- global->LDS copies.  Lane l of a wave fills the l-th 16 bytes of a
   // 1 KB block; each LDS position is mapped back to the (key row, logical
@@ -165,9 +244,9 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashArgs a, TilePla
     else if (k < 6) lds_dma16_sv(kpb, o_kr[k - 4], &sKr[buf][(wave + 4 * (k - 4)) * 512]);
     else lds_dma16_sv(kvb, o_v[k - 6], &sV[buf][(wave + 4 * (k - 6)) * 512]);
   };
-  auto issue_tile = [&](int t, auto bufc) {
+  // the key tile starting at kb of a query tile whose keys end at kend
+  auto issue_tile = [&](int kb, int kend, auto bufc) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
-    const int kb = kst + t * FK;
     if (kb + FK <= kend) {
       const T* kvb = kv_head + (int64_t)kb * kv_row;
       const T* kpb = KPE + (int64_t)kb * a.kpe_stride;
@@ -197,7 +276,6 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashArgs a, TilePla
       }
     }
   };
-
   const float c2 = a.scale * kLog2e;     // scores to base-2 exponent units
   float m_ref = -INFINITY, l_run = 0.f;  // exponent origin (base-2 units), running sum
   f32x16 o[DV / 32];
@@ -241,16 +319,70 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashArgs a, TilePla
   constexpr int SD = 4;   // S operand reads in flight
   constexpr int PD = 3;   // PV operands in flight
 
-  // The copies of tile t + 1 go out between the score MFMAs of tile t (one
-  // per other MFMA) rather than all at once after the barrier, where the
-  // copies of all eight waves of the CU queue at the address unit together.
-  auto step = [&](int t, auto bufc) {
+  // ---- normalise and store the walked item: lane holds query my_q, dv rows
+  // d*32 + qd*8 + h*4 + [0,4)
+  auto finish = [&]() __attribute__((always_inline)) {
+    if (my_q < c_q1) {
+      const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+      const float inv = 1.f / l_tot;
+      if (a.lse_out && hsel == 0) a.lse_out[(int64_t)head * a.n_tokens + my_q] = m_ref + __builtin_log2f(l_tot);
+      bf16* orow = O + (int64_t)my_q * H * DV + head * DV;
+#pragma unroll
+      for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          bf16x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (bf16)(o[d][qd * 4 + e] * inv);
+          *(bf16x4*)(orow + d * 32 + qd * 8 + hsel * 4) = v;
+        }
+    }
+  };
+  // (paired) item 0 done: store it, start item 1 from a fresh state
+  auto next_item = [&]() __attribute__((always_inline)) {
+    finish();
+    c_kst = g1.kst;
+    c_kend = g1.kend;
+    c_koff = g1.koff;
+    c_q1 = g1.q1;
+    c_t0 = t10 - n0;
+    qw0 = g1.q0 + wave * 32;
+    my_q = qw0 + (lane & 31);
+    m_ref = -INFINITY;
+    l_run = 0.f;
+#pragma unroll
+    for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[d][e] = 0.f;
+    load_q();
+  };
+
+  // Step v of this half's walk.  The copies of the next key tile go out
+  // between the score MFMAs of this one (one per other MFMA) rather than all
+  // at once after the barrier, where the copies of all eight waves of the CU
+  // queue at the address unit together.
+  auto step = [&](int v, auto bufc) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
-    const int kb = kst + t * FK;
-    const int kn = kb + FK;
-    const bool active = (qw0 < q1) && (kb <= qw0 + 31 + koff);
-    const bool spread = active && t + 1 < ntiles && kn + FK <= kend;
-    if (t + 1 < ntiles && !spread) issue_tile(t + 1, BufC<buf ^ 1>{});
+    if constexpr (PAIRED) {
+      if (v >= nmine) {                      // the shorter walk idles at the barrier
+        wg_barrier();
+        return;
+      }
+      if (n1 > 0 && v == n0) next_item();
+    }
+    const int kb = c_kst + (c_t0 + v) * FK;
+    const bool has_next = v + 1 < nmine;
+    // the next key tile: this item's next one, or item 1's first
+    int kn = kb + FK, kend_n = c_kend;
+    if constexpr (PAIRED) {
+      if (n1 > 0 && v + 1 == n0) {
+        kn = g1.kst + t10 * FK;
+        kend_n = g1.kend;
+      }
+    }
+    const bool active = (qw0 < c_q1) && (kb <= qw0 + 31 + c_koff);
+    const bool spread = active && has_next && kn + FK <= kend_n;
+    if (has_next && !spread) issue_tile(kn, kend_n, BufC<buf ^ 1>{});
     const T* kvn = kv_head + (int64_t)kn * kv_row;
     const T* kpn = KPE + (int64_t)kn * a.kpe_stride;
     if (active) {
@@ -280,13 +412,13 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashArgs a, TilePla
 #pragma unroll
       for (int i = 0; i < PD; ++i) vf[i] = vread(i, bufc);
       // ---- causal mask (only tiles that reach past this wave's first query)
-      if (kb + FK - 1 > qw0 + koff) {
+      if (kb + FK - 1 > qw0 + c_koff) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int key = kb + mt * 32 + (e >> 2) * 8 + hsel * 4 + (e & 3);
-            if (key > my_q + koff) s[mt][e] = -INFINITY;
+            if (key > my_q + c_koff) s[mt][e] = -INFINITY;
           }
       }
       __builtin_amdgcn_s_setprio(0);
@@ -346,33 +478,52 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashArgs a, TilePla
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
-    if (t + 1 < ntiles) vm_wait_all();
+    if (has_next) vm_wait_all();
     wg_barrier();
   };
 
-  issue_tile(0, BufC<0>{});
+  if (!PAIRED || nmine > 0) issue_tile(c_kst + c_t0 * FK, c_kend, BufC<0>{});
   vm_wait_all();
   __syncthreads();
-  for (int t = 0; t < ntiles; t += 2) {
-    step(t, BufC<0>{});
-    if (t + 1 < ntiles) step(t + 1, BufC<1>{});
+  for (int v = 0; v < nsteps; v += 2) {
+    step(v, BufC<0>{});
+    if (v + 1 < nsteps) step(v + 1, BufC<1>{});
   }
 
-  // ---- normalise and store: lane holds query my_q, dv rows d*32 + qd*8 + h*4 + [0,4)
-  if (my_q >= q1) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = 1.f / l_tot;
-  if (a.lse_out && hsel == 0) a.lse_out[(int64_t)head * a.n_tokens + my_q] = m_ref + __builtin_log2f(l_tot);
-  bf16* orow = O + (int64_t)my_q * H * DV + head * DV;
+  if constexpr (PAIRED) {
+    if (merge) {
+      // half 0's partial result for the long tile through LDS (the tiles are
+      // no longer read): wave w of either half holds the same queries
+      float* xo = reinterpret_cast<float*>(&sKn_[0][0][0]);   // 4 waves x 64 accumulators x 64 lanes
+      float* xm = reinterpret_cast<float*>(&sKr_[0][0][0]);   // 4 waves x (m, l) x 64 lanes
+      if (half == 0) {
 #pragma unroll
-  for (int d = 0; d < DV / 32; ++d)
+        for (int d = 0; d < DV / 32; ++d)
 #pragma unroll
-    for (int qd = 0; qd < 4; ++qd) {
-      bf16x4 v;
+          for (int e = 0; e < 16; ++e) xo[(wave * 64 + d * 16 + e) * 64 + lane] = o[d][e];
+        xm[(wave * 2) * 64 + lane] = m_ref;
+        xm[(wave * 2 + 1) * 64 + lane] = l_run;
+      }
+      __syncthreads();
+      if (half == 1) {
+        const float ma = xm[(wave * 2) * 64 + lane], la = xm[(wave * 2 + 1) * 64 + lane];
+        const float m = fmaxf(ma, m_ref);
+        const float wa = (ma == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ma - m);
+        const float wb = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = (bf16)(o[d][qd * 4 + e] * inv);
-      *(bf16x4*)(orow + d * 32 + qd * 8 + hsel * 4) = v;
+        for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[d][e] = xo[(wave * 64 + d * 16 + e) * 64 + lane] * wa + o[d][e] * wb;
+        l_run = la * wa + l_run * wb;
+        m_ref = m;
+        finish();
+      }
+      return;
     }
+    if (nmine > 0) finish();
+  } else {
+    finish();
+  }
 }
 
 // fp32 attention for the fp32 dtype (small shapes): one wavefront per (query,
@@ -458,13 +609,40 @@ hipError_t launch_flash_mfma(const FlashArgs& a, bool f16_operands, const int32_
   TilePlan plan;
   plan.heads_per_xcd = (a.heads + 7) / 8;
   plan.group = prefix_total > 0 ? kPrefixTileGroup : 1;
-  // When every workgroup of an XCD is resident at once (at most two per CU,
-  // 32 CUs per XCD), a CU keeps the two it is first given for the whole
-  // launch, slot s beside slot s + 32: then the tiles go longest first across
-  // documents with the second half reversed, so the k-th longest shares a CU
-  // with the k-th shortest (two documents of 2048 tokens, 16 heads: the
-  // busiest CU had 64 key tiles against an average of 34).
-  if (prefix_total == 0 && tiles.size() >= 2 && (int64_t)plan.heads_per_xcd * (int64_t)tiles.size() <= 64) {
+  const int64_t nt = (int64_t)tiles.size();
+  auto launch = [&](auto paired, int64_t blocks) -> hipError_t {
+    constexpr bool P = decltype(paired)::value;
+    if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+    dim3 grid((unsigned)blocks);
+    if (f16_operands)
+      flash_mfma_kernel<f16, P><<<grid, P ? 512 : 256, 0, s>>>(a, plan);
+    else
+      flash_mfma_kernel<bf16, P><<<grid, P ? 512 : 256, 0, s>>>(a, plan);
+    return hipGetLastError();
+  };
+  // A launch whose 4-wave workgroups would all be resident at once, two to a
+  // CU (32 CUs per XCD), keeps each CU's two for the whole launch, and the
+  // CU with the longest pair sets the time (two documents of 2048 tokens, 16
+  // heads: 64 key tiles against an average of 34, the longest tile of a pair
+  // running alone at one wave per SIMD once its partner is done).  Such a
+  // launch runs paired instead: one 8-wave workgroup per CU, the k-th longest
+  // tile of a head with its k-th shortest, the pair's key tiles split evenly
+  // between the two halves.
+  const int64_t pairs = (nt + 1) / 2;
+  if (prefix_total == 0 && nt >= 2 && plan.heads_per_xcd * nt > 32 && plan.heads_per_xcd * pairs <= 32) {
+    std::stable_sort(tiles.begin(), tiles.end(), [](const T& x, const T& y) { return x.keys > y.keys; });
+    plan.n = (int)pairs;
+    for (int64_t k = 0; k < pairs; ++k) {
+      plan.t[2 * k] = tiles[k].id;
+      plan.t[2 * k + 1] = (nt - 1 - k > k) ? tiles[nt - 1 - k].id : kNoTile;
+    }
+    return launch(std::true_type{}, (int64_t)8 * plan.heads_per_xcd * pairs);
+  }
+  // Otherwise, when the 4-wave workgroups are all resident at once, the
+  // tiles go longest first across documents with the second half reversed,
+  // so that slot s and slot s + 32 of an XCD (one CU) hold the k-th longest
+  // and the k-th shortest tile.
+  if (prefix_total == 0 && nt >= 2 && plan.heads_per_xcd * nt <= 64) {
     std::stable_sort(tiles.begin(), tiles.end(), [](const T& x, const T& y) { return x.keys > y.keys; });
     std::reverse(tiles.begin() + tiles.size() / 2, tiles.end());
   }
@@ -472,14 +650,7 @@ hipError_t launch_flash_mfma(const FlashArgs& a, bool f16_operands, const int32_
     const int n = (int)std::min<size_t>(MAX_TILES, tiles.size() - base);
     plan.n = n;
     for (int i = 0; i < n; ++i) plan.t[i] = tiles[base + i].id;
-    const int64_t blocks = (int64_t)8 * plan.heads_per_xcd * n;
-    if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
-    dim3 grid((unsigned)blocks);
-    if (f16_operands)
-      flash_mfma_kernel<f16><<<grid, 256, 0, s>>>(a, plan);
-    else
-      flash_mfma_kernel<bf16><<<grid, 256, 0, s>>>(a, plan);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = launch(std::false_type{}, (int64_t)8 * plan.heads_per_xcd * n);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

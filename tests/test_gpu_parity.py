@@ -255,6 +255,35 @@ def test_attention_core_one_long_document(mla):
     bf16_check(ref.reshape(len(rows), -1), got[rows].reshape(len(rows), -1), "sampled rows")
 
 
+@pytest.mark.parametrize("heads,lens,operand", [(16, [1500, 700, 37, 300, 0, 129], "bf16"), (8, [4100], "f16"),
+                                                  (5, [2000, 2100, 33], "bf16")])
+def test_attention_core_one_round_paired(mla, heads, lens, operand):
+    """Launches whose workgroups would all be resident at once, more than one
+    to a CU, run as paired 8-wave workgroups (a long tile split between two
+    halves and merged, a short tile beside it): an even and an odd number of
+    tiles (the middle tile alone, split), ragged documents and tails, a head
+    count that leaves XCDs without heads; every row against the oracle."""
+    _say(f"case: attention core paired heads={heads} lens={lens} operand={operand}")
+    sh = mi.WORKLOADS["megatron_2x2048"].replace(num_heads=heads)
+    rng = np.random.default_rng(heads + len(lens))
+    n = sum(lens)
+    if operand == "f16":
+        rnd, tdt = (lambda x: np.asarray(x, np.float16).astype(np.float32)), torch.float16
+    else:
+        rnd, tdt = mi.bf16_round, torch.bfloat16
+    q = rnd(rng.standard_normal((n, heads, 192)).astype(np.float32))
+    kv = rnd(rng.standard_normal((n, heads, 256)).astype(np.float32))
+    kpe = rnd(rng.standard_normal((n, 64)).astype(np.float32))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    attn = torch.full((n, heads, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
+    mla.attention_prefill(mla.make_config(sh), dev(q, tdt), dev(kv, tdt), dev(kpe, tdt),
+                          torch.from_numpy(cu).to(DEV), cu, attn)
+    torch.cuda.synchronize()
+    k = np.concatenate([kv[..., :128], np.broadcast_to(kpe[:, None, :], (n, heads, 64))], -1)
+    ref = om.causal_varlen_attention(q, k, kv[..., 128:], om.softmax_scale(sh), cu)
+    bf16_check(ref.reshape(n * heads, 128), attn.float().cpu().numpy().reshape(n * heads, 128), "attn paired")
+
+
 def test_attention_core_fp16_operands(mla):
     """fp16 operands (as inside the prefill layer), with a dense k_pe buffer."""
     _say("case: attention core fp16 operands")
