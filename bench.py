@@ -320,9 +320,10 @@ def main():
 
         def backward():
             """The attention backward on the bf16 operands, with the forward's
-            bf16 output and a seeded N(0, 1) output gradient."""
+            bf16 output and log-sum-exp and a seeded N(0, 1) output gradient."""
             qq, kk, pp = ops["bf16"]
-            runner("bf16")()
+            lse = torch.empty(H, n, dtype=torch.float32, device=dev)
+            mla.attention_prefill(cfg, qq, kk, pp, cu, cuh, attn, lse=lse)
             o = attn.clone()
             g = torch.Generator(device=dev).manual_seed(7)
             do = torch.randn(o.shape, device=dev, generator=g).to(torch.bfloat16)
@@ -330,7 +331,8 @@ def main():
             dkv = torch.empty(kk.shape, dtype=torch.float32, device=dev)
             dkpe = torch.empty(pp.shape, dtype=torch.float32, device=dev)
             ws = torch.empty(mla.attention_bwd_workspace_size(cfg, n), dtype=torch.uint8, device=dev)
-            return lambda: mla.attention_prefill_bwd(cfg, qq, kk, pp, cu, cuh, o, do, dq, dkv, dkpe, workspace=ws)
+            return lambda: mla.attention_prefill_bwd(cfg, qq, kk, pp, cu, cuh, o, do, dq, dkv, dkpe, workspace=ws,
+                                                     lse=lse)
         return {"shape": sh, "cu": cuh, "flops": attention_flops(sh, cuh), "run": runner, "ops": ops,
                 "bwd": backward, "bwd_flops": attention_bwd_flops(sh, cuh)}
 
@@ -527,7 +529,8 @@ def main():
             bwd_rec = {"workload": f"{name}, bf16 operands, fp32 dq / dkv / dkpe", "ms": round(b_ms, 4),
                        "tflops": round(b_tf, 2), "frac": round(b_tf / PEAK_MFMA_TFLOPS, 4),
                        "flops_per_launch": ao["bwd_flops"],
-                       "kernel": "mla_attention_prefill_bwd (stats, dq and dk/dv passes + k_pe head sum)"}
+                       "kernel": "mla_attention_prefill_bwd with the forward's log-sum-exp (dq pass forming D, "
+                                 "dk/dv pass, k_pe head sum)"}
         del ao
         torch.cuda.empty_cache()
         print(f"attention {name} done", file=sys.stderr, flush=True)

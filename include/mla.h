@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 5
+#define MLA_ABI_VERSION 6
 
 typedef enum mla_status {
   MLA_OK = 0,
@@ -243,11 +243,17 @@ mla_status mla_linear(const mla_config* cfg, const void* x, int64_t ldx, const v
  *   attn   [N, H, d_v] output, cfg.dtype (bf16 for both bf16 operand types).
  *          d_v != d_nope + d_rope is handled natively (no padding of v, unlike
  *          the FlashAttention adapters on the pages).
+ *   lse    NULL, or DEVICE fp32 [H, N] receiving per (head, query) the
+ *          base-2 log-sum-exp of the query's scores in base-2 units,
+ *          log2 sum_j 2^(scale * log2(e) * q.k_j) over the keys it sees (the
+ *          softmax denominator as the kernel formed it), for
+ *          mla_attention_prefill_bwd; bf16 configs only (MLA_ERR_UNSUPPORTED
+ *          for fp32)
  *   workspace may be NULL (no scratch is needed). */
 mla_status mla_attention_prefill(const mla_config* cfg, int32_t operand_dtype, const void* q, const void* kv,
                                  const void* kpe, int64_t kpe_stride,
                                  const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
-                                 int32_t num_seqs, void* attn,
+                                 int32_t num_seqs, void* attn, float* lse,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* The attention core for new queries over longer key sequences (a chunk of
@@ -379,13 +385,17 @@ mla_status mla_decode_absorbed_fwd_noalloc(const mla_config* cfg, const void* w_
  *          mla_attention_prefill (MLA_BF16 operands)
  *   out    [N, H, d_v] bf16, the forward's output for these operands; D =
  *          rowsum(dO * out) is formed from it as given
+ *   lse    NULL, or DEVICE fp32 [H, N]: the log-sum-exp that
+ *          mla_attention_prefill wrote for these operands (MLA_BF16); then
+ *          the softmax statistics are taken from it instead of recomputed
  *   dout   [N, H, d_v] bf16, the gradient of the output
  *   dq     [N, H, d_nope + d_rope] fp32, dkv [N, H, d_nope + d_v] fp32
  *          (per head [dk_nope | dv]), dkpe [N, d_rope] fp32 — all DEVICE,
  *          16-byte aligned, written completely
  *   workspace: DEVICE, >= mla_attention_bwd_workspace_size(cfg, N) bytes.
- * The forward's softmax statistics are recomputed (one extra QK^T pass); P
- * and dS are rounded to bf16 as MFMA operands, accumulation is fp32.
+ * Without lse the forward's softmax statistics are recomputed (one extra
+ * QK^T pass); P and dS are rounded to bf16 as MFMA operands, accumulation is
+ * fp32.
  * Errors: MLA_ERR_UNSUPPORTED for another dtype or head shape, more than
  * 65535 documents or a document longer than 65535 * 128 tokens;
  * MLA_ERR_INVALID_ARG for a missing pointer or bad offsets; MLA_ERR_MISALIGNED;
@@ -394,8 +404,8 @@ size_t mla_attention_bwd_workspace_size(const mla_config* cfg, int32_t num_token
 mla_status mla_attention_prefill_bwd(const mla_config* cfg, const void* q, const void* kv, const void* kpe,
                                      int64_t kpe_stride, const int32_t* cu_seqlens_dev,
                                      const int32_t* cu_seqlens_host, int32_t num_seqs, const void* out,
-                                     const void* dout, void* dq, void* dkv, void* dkpe, void* workspace,
-                                     size_t workspace_bytes, void* stream);
+                                     const float* lse, const void* dout, void* dq, void* dkv, void* dkpe,
+                                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Gradients of the layer's weights (mla_prefill_bwd): fp32 DEVICE arrays of
  * the shapes of the mla_weights fields of the same name, 16-byte aligned;

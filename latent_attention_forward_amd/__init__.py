@@ -67,7 +67,7 @@ _SIGNATURES = {
     "mla_latent_norm_rope": (_I32, [_CFG, _P, _I64, _I32, _I32, _I32, _P, _I32, _I32, _I32, _P, _P, _I32, _P,
                                     _P, _I64, _P, _I64, _P]),
     "mla_linear": (_I32, [_CFG, _P, _I64, _P, _P, _I64, _I32, _I32, _I32, _P]),
-    "mla_attention_prefill": (_I32, [_CFG, _I32, _P, _P, _P, _I64, _P, _P, _I32, _P, _P, _SZ, _P]),
+    "mla_attention_prefill": (_I32, [_CFG, _I32, _P, _P, _P, _I64, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
     "mla_prefill_fwd": (_I32, [_CFG, ctypes.POINTER(MlaWeights), _P, _P, _P, _I32, _P, _P, _P, _I32, _P, _P,
                                _P, _SZ, _P]),
     "mla_decode_absorbed_fwd": (_I32, [_CFG, _P, _P, _P, _P, _I32, _I32, _P, _I32, _P, _P, _I32, _P, _P, _SZ, _P]),
@@ -78,7 +78,7 @@ _SIGNATURES = {
     "mla_prefill_bwd_workspace_size": (_SZ, [_CFG, _I32]),
     "mla_prefill_bwd": (_I32, [_CFG, ctypes.POINTER(MlaWeights), _P, _P, _P, _I32, _P, _P, _P, _I32, _P, _P,
                                ctypes.POINTER(MlaWeightGrads), _P, _SZ, _P]),
-    "mla_attention_prefill_bwd": (_I32, [_CFG, _P, _P, _P, _I64, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "mla_attention_prefill_bwd": (_I32, [_CFG, _P, _P, _P, _I64, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mla_q_uproj_rope_mxfp8": (_I32, [_CFG, _P, _I64, _I32, _P, _P, _P, _P, _I32, _P, _P, _P]),
     "mla_cache_quantize_fp8": (_I32, [_P, _I64, _I64, _I32, ctypes.c_float, _P, _I64, _P]),
     "mla_decode_absorbed_fp8_fwd": (_I32, [_CFG, _P, _P, _P, _P, ctypes.c_float, _I32, _I32, _P, _I32, _P, _P, _I32,
@@ -290,10 +290,11 @@ def _operand_type(cfg: MlaConfig, q, kv, kpe):
 
 
 def attention_prefill(cfg: MlaConfig, q, kv, kpe, cu_seqlens_dev, cu_seqlens_host: Sequence[int], attn,
-                      kpe_stride: Optional[int] = None, stream=None):
+                      kpe_stride: Optional[int] = None, stream=None, lse=None):
     """Attention core.  ``kpe`` is a view whose row r is the shared rope key of
     token r (e.g. ``latent[:, r_kv:]``); its dtype (bf16 / fp16 / fp32, the
-    same as q and kv) sets the operand type."""
+    same as q and kv) sets the operand type.  ``lse``: optional fp32 [H, N]
+    receiving the base-2 log-sum-exp for ``attention_prefill_bwd``."""
     import numpy as np
     lib = load_library()
     cuh = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int32))
@@ -301,7 +302,8 @@ def attention_prefill(cfg: MlaConfig, q, kv, kpe, cu_seqlens_dev, cu_seqlens_hos
     _check(lib.mla_attention_prefill(ctypes.byref(cfg), op, _ptr(q), _ptr(kv), _ptr(kpe, rows=True),
                                      kpe.stride(0) if kpe_stride is None else kpe_stride,
                                      _ptr(cu_seqlens_dev, dtype=_i32(), name="cu_seqlens_dev"), cuh.ctypes.data,
-                                     len(cuh) - 1, _ptr(attn, dtype=_act(cfg), name="attn"), None, 0,
+                                     len(cuh) - 1, _ptr(attn, dtype=_act(cfg), name="attn"),
+                                     None if lse is None else _ptr(lse, dtype=_f32(), name="lse"), None, 0,
                                      _stream(stream)), "mla_attention_prefill")
 
 
@@ -455,10 +457,12 @@ def attention_bwd_workspace_size(cfg: MlaConfig, num_tokens: int) -> int:
 
 
 def attention_prefill_bwd(cfg: MlaConfig, q, kv, kpe, cu_seqlens_dev, cu_seqlens_host: Sequence[int], out, dout,
-                          dq, dkv, dkpe, workspace=None, stream=None):
+                          dq, dkv, dkpe, workspace=None, stream=None, lse=None):
     """Backward of the attention core (``mla_attention_prefill_bwd``): bf16
     q [N, H, 192], kv [N, H, 256], kpe [N, 64] (row-strided), out and dout
-    [N, H, 128]; fp32 dq [N, H, 192], dkv [N, H, 256], dkpe [N, 64]."""
+    [N, H, 128]; fp32 dq [N, H, 192], dkv [N, H, 256], dkpe [N, 64]; ``lse``:
+    optional fp32 [H, N] from ``attention_prefill`` (statistics not
+    recomputed)."""
     import numpy as np
     import torch
     lib = load_library()
@@ -470,7 +474,8 @@ def attention_prefill_bwd(cfg: MlaConfig, q, kv, kpe, cu_seqlens_dev, cu_seqlens
     _check(lib.mla_attention_prefill_bwd(
         ctypes.byref(cfg), _ptr(q, dtype=bf, name="q"), _ptr(kv, dtype=bf, name="kv"),
         _ptr(kpe, rows=True, dtype=bf, name="kpe"), kpe.stride(0), _ptr(cu_seqlens_dev, dtype=_i32(), name="cu"),
-        cuh.ctypes.data, len(cuh) - 1, _ptr(out, dtype=bf, name="out"), _ptr(dout, dtype=bf, name="dout"),
+        cuh.ctypes.data, len(cuh) - 1, _ptr(out, dtype=bf, name="out"),
+        None if lse is None else _ptr(lse, dtype=f32, name="lse"), _ptr(dout, dtype=bf, name="dout"),
         _ptr(dq, dtype=f32, name="dq"), _ptr(dkv, dtype=f32, name="dkv"), _ptr(dkpe, dtype=f32, name="dkpe"),
         _ptr(ws), ws.numel(), st.cuda_stream), "mla_attention_prefill_bwd")
     return ws

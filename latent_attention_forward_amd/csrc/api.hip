@@ -443,8 +443,8 @@ static mla_status attention_impl(const mla_config* cfg, const void* q, const voi
 
 mla_status mla_attention_prefill(const mla_config* cfg, int32_t operand_dtype, const void* q, const void* kv,
                                  const void* kpe, int64_t kpe_stride, const int32_t* cu_seqlens_dev,
-                                 const int32_t* cu_seqlens_host, int32_t num_seqs, void* attn, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
+                                 const int32_t* cu_seqlens_host, int32_t num_seqs, void* attn, float* lse,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
   (void)workspace; (void)workspace_bytes;
   mla_status s = check_config(cfg);
   if (s != MLA_OK) return s;
@@ -459,8 +459,10 @@ mla_status mla_attention_prefill(const mla_config* cfg, int32_t operand_dtype, c
   if (kpe_stride < cfg->qk_rope_dim) return fail(MLA_ERR_INVALID_ARG, "kpe_stride < d_rope");
   if (cfg->dtype == MLA_BF16 && (!aligned16(q) || !aligned16(kv) || !aligned16(kpe) || !aligned16(attn) || kpe_stride % 8))
     return fail(MLA_ERR_MISALIGNED, "bf16 attention needs 16-byte aligned tensors and kpe_stride % 8 == 0");
+  if (lse && cfg->dtype != MLA_BF16) return fail(MLA_ERR_UNSUPPORTED, "the log-sum-exp output needs a bf16 config");
+  if (lse && ((uintptr_t)lse & 3)) return fail(MLA_ERR_MISALIGNED, "lse must be 4-byte aligned");
   s = attention_impl(cfg, q, kv, kpe, kpe_stride, operand_dtype == MLA_F16, cu_seqlens_dev, cu_seqlens_host,
-                     num_seqs, n, attn, (hipStream_t)stream);
+                     num_seqs, n, attn, (hipStream_t)stream, nullptr, nullptr, -1, lse);
   return s == MLA_OK ? ok() : s;
 }
 
@@ -879,8 +881,8 @@ size_t mla_attention_bwd_workspace_size(const mla_config* cfg, int32_t num_token
 mla_status mla_attention_prefill_bwd(const mla_config* cfg, const void* q, const void* kv, const void* kpe,
                                      int64_t kpe_stride, const int32_t* cu_seqlens_dev,
                                      const int32_t* cu_seqlens_host, int32_t num_seqs, const void* out,
-                                     const void* dout, void* dq, void* dkv, void* dkpe, void* workspace,
-                                     size_t workspace_bytes, void* stream) {
+                                     const float* lse, const void* dout, void* dq, void* dkv, void* dkpe,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
   mla_status s = check_config(cfg);
   if (s != MLA_OK) return s;
   if (cfg->dtype != MLA_BF16) return fail(MLA_ERR_UNSUPPORTED, "the attention backward is compiled for bf16 only");
@@ -899,6 +901,7 @@ mla_status mla_attention_prefill_bwd(const mla_config* cfg, const void* q, const
   for (const void* p : ptrs)
     if (!aligned16(p)) return fail(MLA_ERR_MISALIGNED, "the attention backward needs 16-byte aligned tensors");
   if (kpe_stride % 8) return fail(MLA_ERR_MISALIGNED, "kpe_stride must be a multiple of 8");
+  if (lse && ((uintptr_t)lse & 3)) return fail(MLA_ERR_MISALIGNED, "lse must be 4-byte aligned");
   const size_t need = mla_attention_bwd_workspace_size(cfg, n);
   if (!workspace || workspace_bytes < need || !aligned16(workspace))
     return fail(MLA_ERR_WORKSPACE, "an aligned workspace of %zu bytes is needed", need);
@@ -907,7 +910,8 @@ mla_status mla_attention_prefill_bwd(const mla_config* cfg, const void* q, const
   AttnBwdArgs a{};
   a.q = q; a.kv = kv; a.kpe = kpe; a.kpe_stride = kpe_stride; a.o = out; a.dout = dout;
   a.cu_dev = cu_seqlens_dev; a.n_tokens = n; a.heads = cfg->num_heads; a.scale = scale_of(cfg);
-  a.lse = (float*)ws;
+  a.lse = lse ? const_cast<float*>(lse) : (float*)ws;   // given: read only
+  a.lse_ready = lse != nullptr;
   a.dsum = (float*)(ws + align256((size_t)n * H * 4));
   a.dkr = (float*)(ws + 2 * align256((size_t)n * H * 4));
   a.dq = (float*)dq; a.dkv = (float*)dkv; a.dkpe = (float*)dkpe;

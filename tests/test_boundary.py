@@ -37,7 +37,7 @@ def test_header_symbols_exported(lib):
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(mla.exported_symbols())
-    assert lib.mla_abi_version() == 5
+    assert lib.mla_abi_version() == 6
 
 
 def test_config_validation(lib):
@@ -179,18 +179,26 @@ def test_device_calls_reject_bad_arguments_before_launch(lib):
     b = lib.mla_attention_prefill_bwd
     cu2 = np.array([0, 100, 300], np.int32)
     args = lambda **kw: [kw.get(k, 4096) for k in ("q", "kv", "kpe")] + [kw.get("kpe_stride", 576), 4096,
-                                                                          cu2.ctypes.data, 2] + \
-        [kw.get(k, 4096) for k in ("out", "dout", "dq", "dkv", "dkpe", "ws")] + [kw.get("wsb", 1 << 30), None]
+                                                                          cu2.ctypes.data, 2, kw.get("out", 4096),
+                                                                          kw.get("lse", None)] + \
+        [kw.get(k, 4096) for k in ("dout", "dq", "dkv", "dkpe", "ws")] + [kw.get("wsb", 1 << 30), None]
     assert b(ctypes.byref(f32), *args()) == mla.MLA_ERR_UNSUPPORTED
     assert b(ctypes.byref(cfg), *args(dout=None)) == mla.MLA_ERR_INVALID_ARG
     assert b(ctypes.byref(cfg), *args(kpe_stride=32)) == mla.MLA_ERR_INVALID_ARG
     assert b(ctypes.byref(cfg), *args(dq=4100)) == mla.MLA_ERR_MISALIGNED
     assert b(ctypes.byref(cfg), *args(kpe_stride=580)) == mla.MLA_ERR_MISALIGNED
     assert b(ctypes.byref(cfg), *args(wsb=16)) == mla.MLA_ERR_WORKSPACE
+    assert b(ctypes.byref(cfg), *args(lse=4098)) == mla.MLA_ERR_MISALIGNED
+    # attention forward: the log-sum-exp output needs a bf16 config and 4-byte alignment
+    fa = lib.mla_attention_prefill
+    fargs = lambda c, op, lse: [ctypes.byref(c), op, 4096, 4096, 4096, 576, 4096, cu2.ctypes.data, 2, 4096, lse,
+                                None, 0, None]
+    assert fa(*fargs(f32, mla.MLA_F32, 4096)) == mla.MLA_ERR_UNSUPPORTED
+    assert fa(*fargs(cfg, mla.MLA_BF16, 4098)) == mla.MLA_ERR_MISALIGNED
     assert mla.attention_bwd_workspace_size(cfg, 300) == 2 * 153600 + 300 * 128 * 64 * 4
     empty = np.array([0, 0], np.int32)
     assert b(ctypes.byref(cfg), None, None, None, 576, None, empty.ctypes.data, 1, None, None, None, None, None,
-             None, 0, None) == mla.MLA_OK
+             None, None, 0, None) == mla.MLA_OK
     # layer backward: fp32 config, a missing weight gradient, workspace
     lb = lib.mla_prefill_bwd
     for name, _ in mla.MlaWeights._fields_:

@@ -69,7 +69,7 @@ def conditioning(q, k, v, dout, out, scale, cu, lse):
     return cq, ck, cv
 
 
-def run_case(mla, sh, lens, seed=0, kpe_in_latent=False):
+def run_case(mla, sh, lens, seed=0, kpe_in_latent=False, with_lse=False):
     H = sh.num_heads
     rng = np.random.default_rng(seed)
     n = int(sum(lens))
@@ -93,9 +93,24 @@ def run_case(mla, sh, lens, seed=0, kpe_in_latent=False):
         lat = torch.randn(n, 576, device=DEV).to(torch.bfloat16)
         lat[:, 512:] = kpe_d
         kpe_d = lat[:, 512:]
-    mla.attention_prefill_bwd(cfg, dev(q, torch.bfloat16), dev(kv, torch.bfloat16), kpe_d,
-                              torch.from_numpy(cu).to(DEV), cu, dev(o, torch.bfloat16),
-                              dev(dout, torch.bfloat16), dq, dkv, dkpe)
+    q_d, kv_d, cu_d = dev(q, torch.bfloat16), dev(kv, torch.bfloat16), torch.from_numpy(cu).to(DEV)
+    lse_d = None
+    if with_lse:
+        # the forward's log-sum-exp (base 2, [H, N]) against the oracle's
+        # natural one, then handed to the backward in place of its statistics.
+        # The forward sums P after rounding it to the operand type (the same
+        # P it multiplies by v), so its denominator is within a factor 1 +- u
+        # of the exact one: |lse error| <= u (+ fp32 arithmetic).
+        lse_d = torch.full((H, n), float("nan"), dtype=torch.float32, device=DEV)
+        attn = torch.empty(n, H, 128, dtype=torch.bfloat16, device=DEV)
+        mla.attention_prefill(cfg, q_d, kv_d, kpe_d, cu_d, cu, attn, lse=lse_d)
+        torch.cuda.synchronize()
+        got_lse = lse_d.cpu().numpy().T.astype(np.float64) * np.log(2.0)
+        err = float(np.max(np.abs(got_lse - lse)))
+        _say(f"  forward lse: max-abs error {err:.3e}")
+        assert err <= U + 1e-5, err
+    mla.attention_prefill_bwd(cfg, q_d, kv_d, kpe_d, cu_d, cu, dev(o, torch.bfloat16),
+                              dev(dout, torch.bfloat16), dq, dkv, dkpe, lse=lse_d)
     torch.cuda.synchronize()
     got = {"dq": dq.cpu().numpy(), "dkv": dkv.cpu().numpy(), "dkpe": dkpe.cpu().numpy()}
     ref = {"dq": rdq, "dkv": rdkv, "dkpe": rdkpe}
@@ -114,6 +129,17 @@ def test_attention_backward(mla, heads, lens):
     sh = mi.WORKLOADS["dsv3_prefill_4096"].replace(num_heads=heads)
     _say(f"case: attention backward heads={heads} lens={lens}")
     run_case(mla, sh, lens)
+
+
+@pytest.mark.parametrize("heads,lens", [(16, [1, 33, 200, 300]), (128, [257]), (8, [5, 0, 130]),
+                                        (16, [1500, 700])])
+def test_attention_backward_with_forward_lse(mla, heads, lens):
+    """The forward's log-sum-exp output (checked against the oracle's) passed
+    to the backward, which then skips its statistics pass and forms D in the dq
+    pass; 128 heads x [257] and 16 heads x [1500, 700] run the forward paired."""
+    sh = mi.WORKLOADS["dsv3_prefill_4096"].replace(num_heads=heads)
+    _say(f"case: attention backward with the forward lse, heads={heads} lens={lens}")
+    run_case(mla, sh, lens, seed=5, with_lse=True)
 
 
 def test_attention_backward_megatron_shape(mla):
