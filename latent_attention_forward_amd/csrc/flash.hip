@@ -210,12 +210,15 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void flash_mfma
   const int hsel = lane >> 5;
   // ---- this wave's queries, held as the B operand (Q^T) for 12 k-steps of 16
   V8 qreg[DQK / 16];
-  auto load_q = [&]() __attribute__((always_inline)) {
+  auto load_q = [&](int row, int q_end) __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < DQK / 16; ++ks)
-      qreg[ks] = (my_q < c_q1) ? *(const V8*)(Q + my_q * q_row + head * DQK + ks * 16 + hsel * 8) : zero8<V8>();
+      qreg[ks] = (row < q_end) ? *(const V8*)(Q + row * q_row + head * DQK + ks * 16 + hsel * 8) : zero8<V8>();
   };
-  load_q();
+  load_q(my_q, c_q1);
+  // (paired) item 1's queries, requested during item 0's last step once its
+  // score MFMAs no longer read them
+  auto load_next_q = [&]() __attribute__((always_inline)) { load_q(g1.q0 + wave * 32 + (lane & 31), g1.q1); };
 
   // ---- global->LDS copies.  Lane l of a wave fills the l-th 16 bytes of a
   // 1 KB block; each LDS position is mapped back to the (key row, logical
@@ -354,7 +357,6 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void flash_mfma
     for (int d = 0; d < DV / 32; ++d)
 #pragma unroll
       for (int e = 0; e < 16; ++e) o[d][e] = 0.f;
-    load_q();
   };
 
   // Step v of this half's walk.  The copies of the next key tile go out
@@ -383,6 +385,8 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void flash_mfma
     const bool active = (qw0 < c_q1) && (kb <= qw0 + 31 + c_koff);
     const bool spread = active && has_next && kn + FK <= kend_n;
     if (has_next && !spread) issue_tile(kn, kend_n, BufC<buf ^ 1>{});
+    const bool pre_q = PAIRED && n1 > 0 && v + 1 == n0;
+    if (pre_q && !active) load_next_q();
     const T* kvn = kv_head + (int64_t)kn * kv_row;
     const T* kpn = KPE + (int64_t)kn * a.kpe_stride;
     if (active) {
@@ -407,6 +411,7 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void flash_mfma
         if ((i & 1) && i < 20 && spread) issue_part(uniform_ptr(kvn), uniform_ptr(kpn), i >> 1, BufC<buf ^ 1>{});
       }
       __builtin_amdgcn_sched_barrier(0);
+      if (pre_q) load_next_q();
       // first PV operands, independent of the softmax
       V8 vf[PD];
 #pragma unroll
