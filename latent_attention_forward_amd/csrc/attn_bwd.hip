@@ -375,11 +375,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, BwdPlan plan)
 #pragma unroll
       for (int i = 0; i < PD; ++i) bf[i] = bread(i);
       bf16x8 dsb[2];
+      if (kb + mt * 32 + 31 <= qw0) {
+        // every key of the block is at or before the wave's first query
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = kb + mt * 32 + (e >> 2) * 8 + hsel * 4 + (e & 3);
-        const float p = key <= my_q ? __builtin_amdgcn_exp2f(s[e] * c2 - lse) : 0.f;
-        dsb[e >> 3][e & 7] = (bf16)(p * (dp[e] - dsum));
+        for (int e = 0; e < 16; ++e) {
+          const float p = __builtin_amdgcn_exp2f(s[e] * c2 - lse);
+          dsb[e >> 3][e & 7] = (bf16)(p * (dp[e] - dsum));
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = kb + mt * 32 + (e >> 2) * 8 + hsel * 4 + (e & 3);
+          const float p = key <= my_q ? __builtin_amdgcn_exp2f(s[e] * c2 - lse) : 0.f;
+          dsb[e >> 3][e & 7] = (bf16)(p * (dp[e] - dsum));
+        }
       }
 #pragma unroll
       for (int i = 0; i < 12; ++i) {
@@ -527,17 +536,35 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, BwdPlan pla
       // lse and D of this lane's query rows mt*32 + g*8 + hsel*4 + [0, 4),
       // read one group of 4 at a time
       bf16x8 pb[2], dsb[2];
+      // every query row of the block after every key of the wave, inside the
+      // document, every key live: no mask
+      const bool nomask = qb + mt * 32 >= kw0 + 31 && qb + mt * 32 + 31 < de && kw0 + 31 < k1;
+      if (nomask) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 lq = *(const float4*)&sL[buf][mt * 32 + g * 8 + hsel * 4];
-        const float4 dq4 = *(const float4*)&sD[buf][mt * 32 + g * 8 + hsel * 4];
+        for (int g = 0; g < 4; ++g) {
+          const float4 lq = *(const float4*)&sL[buf][mt * 32 + g * 8 + hsel * 4];
+          const float4 dq4 = *(const float4*)&sD[buf][mt * 32 + g * 8 + hsel * 4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int e = g * 4 + j;
-          const int t = qb + mt * 32 + g * 8 + hsel * 4 + j;
-          const float p = (t >= my_k && t < de && live) ? __builtin_amdgcn_exp2f(s[e] * c2 - lq[j]) : 0.f;
-          pb[e >> 3][e & 7] = (bf16)p;
-          dsb[e >> 3][e & 7] = (bf16)(p * (dp[e] - dq4[j]));
+          for (int j = 0; j < 4; ++j) {
+            const int e = g * 4 + j;
+            const float p = __builtin_amdgcn_exp2f(s[e] * c2 - lq[j]);
+            pb[e >> 3][e & 7] = (bf16)p;
+            dsb[e >> 3][e & 7] = (bf16)(p * (dp[e] - dq4[j]));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 lq = *(const float4*)&sL[buf][mt * 32 + g * 8 + hsel * 4];
+          const float4 dq4 = *(const float4*)&sD[buf][mt * 32 + g * 8 + hsel * 4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int e = g * 4 + j;
+            const int t = qb + mt * 32 + g * 8 + hsel * 4 + j;
+            const float p = (t >= my_k && t < de && live) ? __builtin_amdgcn_exp2f(s[e] * c2 - lq[j]) : 0.f;
+            pb[e >> 3][e & 7] = (bf16)p;
+            dsb[e >> 3][e & 7] = (bf16)(p * (dp[e] - dq4[j]));
+          }
         }
       }
 #pragma unroll
