@@ -117,6 +117,46 @@ def layer_flops(shape, n, attn):
     return f + attn
 
 
+def layer_gemms(shape, n):
+    """The prefill layer's projections in the order the library launches
+    them: (name, flops)."""
+    H, dqk, dv, r, dr = shape.num_heads, shape.qk_head_dim, shape.v_head_dim, shape.kv_lora_rank, shape.qk_rope_dim
+    g = []
+    if shape.q_lora_rank:
+        g += [("q_a", 2 * n * shape.hidden * shape.q_lora_rank), ("q_b", 2 * n * shape.q_lora_rank * H * dqk)]
+    else:
+        g += [("q_proj", 2 * n * shape.hidden * H * dqk)]
+    g += [("kv_a", 2 * n * shape.hidden * (r + dr)), ("kv_b", 2 * n * r * H * (shape.qk_nope_dim + dv))]
+    if shape.output_gate:
+        g += [("gate", 2 * n * shape.hidden * H * dv)]
+    if shape.o_groups:
+        g += [("o_a", 2 * n * H * dv * shape.o_lora_rank),
+              ("o_b", 2 * n * shape.o_groups * shape.o_lora_rank * shape.hidden)]
+    else:
+        g += [("o_proj", 2 * n * H * dv * shape.hidden)]
+    return g
+
+
+def device_kernels(torch, fn, reps, between=None):
+    """Device-side kernel durations (us) of `reps` calls of fn, from the torch
+    profiler (it records every kernel dispatched in the process, the
+    library's included); calls of `between` (not profiled work) are dropped
+    by name.  Returns one list of (name, us) per call, in launch order."""
+    from torch.profiler import profile, ProfilerActivity
+    calls = []
+    for _ in range(reps):
+        if between is not None:
+            between()
+        torch.cuda.synchronize()
+        with profile(activities=[ProfilerActivity.CUDA]) as prof:
+            fn()
+            torch.cuda.synchronize()
+        evs = sorted((e for e in prof.events() if e.device_type.name in ("CUDA", "HIP")),
+                     key=lambda e: e.time_range.start)
+        calls.append([(e.name, float(e.device_time)) for e in evs])
+    return calls
+
+
 def decode_bytes(shape, lens, max_blocks):
     H, r, dr, dn, dv = shape.num_heads, shape.kv_lora_rank, shape.qk_rope_dim, shape.qk_nope_dim, shape.v_head_dim
     B = len(lens)
@@ -623,6 +663,47 @@ def main():
                                   "flops_per_launch": c_aflops}}
         del chunk
 
+    # ------------------------------------------------------------------ per-kernel breakdown (profiler device times)
+    breakdown = None
+    try:
+        reps = 3
+        lcalls = device_kernels(torch, prefill, reps)
+        gl = layer_gemms(sh, n)
+        gem = [[us for nm, us in c if "gemm" in nm] for c in lcalls]
+        per_gemm = None
+        if all(len(c) == len(gl) for c in gem):
+            per_gemm = {}
+            for i, (nm, fl) in enumerate(gl):
+                us = sum(c[i] for c in gem) / reps
+                per_gemm[nm] = {"us": round(us, 1), "tflops": round(fl / (us * 1e-6) / 1e12, 1),
+                                "frac": round(fl / (us * 1e-6) / 1e12 / PEAK_MFMA_TFLOPS, 4)}
+        layer_kernel_us = sum(us for c in lcalls for _, us in c) / reps
+        flush_b = torch.zeros(512 << 20, dtype=torch.uint8, device=dev)
+        sink_b = torch.zeros(1, dtype=torch.int64, device=dev)
+        dcalls = device_kernels(torch, decode, reps, between=lambda: sink_b.copy_(flush_b.view(torch.int64).sum()))
+        del flush_b
+        dk = {}
+        for key in ("absorb_q", "decode_split", "decode_combine"):
+            t = [sum(us for nm, us in c if key in nm) for c in dcalls]
+            dk[key] = sum(t) / reps
+        keys_tot = int(lens_h.sum())
+        cache_b = keys_tot * (dsh.kv_lora_rank + dsh.qk_rope_dim) * 2
+        sp_flops = keys_tot * dsh.num_heads * 2 * ((dsh.kv_lora_rank + dsh.qk_rope_dim) + dsh.kv_lora_rank)
+        sp_us = dk["decode_split"]
+        breakdown = {
+            "source": "torch.profiler device durations, mean of 3 calls (the decode after a 512 MiB flush)",
+            "prefill_layer_kernels_us": round(layer_kernel_us, 1),
+            "prefill_gemms": per_gemm,
+            "decode_kernels_us": {k: round(v, 1) for k, v in dk.items()},
+            "decode_split_kernel": {"us": round(sp_us, 1), "cache_bytes": cache_b,
+                                    "cache_gbs": round(cache_b / (sp_us * 1e-6) / 1e9, 1),
+                                    "frac_hbm": round(cache_b / (sp_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                                    "tflops": round(sp_flops / (sp_us * 1e-6) / 1e12, 1),
+                                    "frac_mfma": round(sp_flops / (sp_us * 1e-6) / 1e12 / PEAK_MFMA_TFLOPS, 4)},
+        }
+    except Exception as ex:                      # the profiler is optional: report why it is missing
+        breakdown = {"error": f"{type(ex).__name__}: {ex}"[:200]}
+
     # ------------------------------------------------------------------ figures
     layer_tflops = layer_flops(sh, n, a_flops) / (prefill_ms * 1e-3) / 1e12
     d_bytes = decode_bytes(dsh, lens_h, max_blocks)
@@ -668,6 +749,7 @@ def main():
                      "bytes_per_call": d8_bytes}}
     if chunk_rec is not None:
         rec["chunked_prefill"] = chunk_rec
+    rec["kernel_breakdown"] = breakdown
     if bwd_rec is not None:
         rec["attention_backward"] = bwd_rec
     rec["layer_backward"] = layer_bwd_rec
