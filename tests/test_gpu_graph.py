@@ -141,3 +141,35 @@ def test_chunk_graph_replays_match_eager(mla):
 
     g = _capture(call)
     _replays(g, call, [out, lat], lambda: cache.mul_(0.5))
+
+
+def test_attention_forward_backward_graph_replays_match_eager(mla):
+    """The attention core with its log-sum-exp output (16 heads, documents
+    [1500, 700]: the paired one-round launch) and the backward given that
+    log-sum-exp, recorded as one graph."""
+    _say("case: graph of mla_attention_prefill (lse) + mla_attention_prefill_bwd, 16 heads, lens [1500, 700]")
+    sh = mi.WORKLOADS["dsv3_prefill_4096"].replace(num_heads=16)
+    cfg = mla.make_config(sh)
+    lens = [1500, 700]
+    n, H = sum(lens), 16
+    cuh = np.array([0, 1500, 2200], np.int32)
+    cu = torch.from_numpy(cuh).to(DEV)
+    g = torch.Generator(device=DEV).manual_seed(21)
+    q = torch.randn(n, H, 192, device=DEV, generator=g).to(torch.bfloat16)
+    kv = torch.randn(n, H, 256, device=DEV, generator=g).to(torch.bfloat16)
+    kpe = torch.randn(n, 64, device=DEV, generator=g).to(torch.bfloat16)
+    dout = torch.randn(n, H, 128, device=DEV, generator=g).to(torch.bfloat16)
+    attn = torch.empty(n, H, 128, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(H, n, dtype=torch.float32, device=DEV)
+    dq = torch.empty(n, H, 192, dtype=torch.float32, device=DEV)
+    dkv = torch.empty(n, H, 256, dtype=torch.float32, device=DEV)
+    dkpe = torch.empty(n, 64, dtype=torch.float32, device=DEV)
+    ws = torch.empty(mla.attention_bwd_workspace_size(cfg, n), dtype=torch.uint8, device=DEV)
+
+    def call():
+        mla.attention_prefill(cfg, q, kv, kpe, cu, cuh, attn, lse=lse)
+        mla.attention_prefill_bwd(cfg, q, kv, kpe, cu, cuh, attn, dout, dq, dkv, dkpe, workspace=ws, lse=lse)
+
+    graph = _capture(call)
+    refs = _replays(graph, call, [attn, lse, dq, dkv, dkpe], lambda: dout.mul_(-0.5))
+    assert all(bool(torch.isfinite(r).all()) for r in refs)
