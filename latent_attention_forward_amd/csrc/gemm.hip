@@ -257,6 +257,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g) {
   const bf16* B = (const bf16*)g.b + (int64_t)blockIdx.z * g.b_bstride + (int64_t)n0 * g.ldb;
   const int wm = wave >> 1, wn = wave & 1;
   const int nk = g.k / GBK;
+  // RoPE: the position of tile row tid, requested now for the table staging
+  const int spos = EPI == EPI_ROPE ? g.positions[min(m0 + tid, g.m - 1)] : 0;
 
   // Copies: instruction i of wave w fills the 1 KB block w + 4 i (16 rows) of a
   // tile; lane l takes row P / 4 and logical chunk (P % 4) ^ swizzle, P = 64
@@ -346,31 +348,70 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g) {
   // RoPE epilogue: rope slices are 64 columns starting at multiples of 64, so
   // a slice is N-tiles (2p, 2p+1) of a wave: rotate_half pair (i, i + 32) is
   // register e of tile 2p and of tile 2p+1 in the same lane; interleaved pairs
-  // (2i, 2i+1) are neighbours in a lane's run of 4.
+  // (2i, 2i+1) are neighbours in a lane's run of 4.  The cos / sin rows of the
+  // tile's 256 output rows are staged in the freed operand LDS first (thread t
+  // reads row t's, all in one memory round trip; NaN rows for positions
+  // outside the table).  Every pair of the wave's two 64-column slices is
+  // then rotated, the slices that are not rope slices by the angle 0
+  // (cos 1, sin 0: the same finite values), so the epilogue has no branch.
   if (EPI == EPI_ROPE) {
+    float rc[2], rs[2];                    // cos / sin override: (1, 0) outside rope slices
+    bool on[2];
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const int c0 = n0 + wn * 128 + p * 64;
-      if (c0 + 64 > g.n || (c0 % g.rope_head_stride) != g.rope_off) continue;
+      on[p] = c0 + 64 <= g.n && (c0 % g.rope_head_stride) == g.rope_off;
+      rc[p] = 1.f;
+      rs[p] = 0.f;
+    }
+    lds_wait_all();
+    wg_barrier();                          // every wave is done with the operand stages
+    float* tcs = (float*)smem;             // [256 rows][32], 16-byte chunk c of row r at c ^ (r & 7)
+    float* tsn = tcs + GBM * 32;
+    {
+      const int pos = spos;
+      const bool ok = pos >= 0 && pos < g.table_len;
+      const float* cs = g.cos_t + (int64_t)(ok ? pos : 0) * 32;
+      const float* sn = g.sin_t + (int64_t)(ok ? pos : 0) * 32;
+      const float nan = __builtin_nanf("");
+      const bool vec = ((reinterpret_cast<uintptr_t>(g.cos_t) | reinterpret_cast<uintptr_t>(g.sin_t)) & 15) == 0;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        float4 cv = make_float4(nan, nan, nan, nan), sv = cv;
+        if (ok && vec) {
+          cv = *(const float4*)(cs + 4 * c);
+          sv = *(const float4*)(sn + 4 * c);
+        } else if (ok) {
+          cv = make_float4(cs[4 * c], cs[4 * c + 1], cs[4 * c + 2], cs[4 * c + 3]);
+          sv = make_float4(sn[4 * c], sn[4 * c + 1], sn[4 * c + 2], sn[4 * c + 3]);
+        }
+        *(float4*)&tcs[tid * 32 + ((c ^ (tid & 7)) << 2)] = cv;
+        *(float4*)&tsn[tid * 32 + ((c ^ (tid & 7)) << 2)] = sv;
+      }
+    }
+    lds_wait_all();
+    wg_barrier();
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi) {
-        const int m = m0 + wm * 128 + mi * 32 + r32;
-        if (m >= g.m) continue;
-        const int pos = g.positions[m];
-        const bool ok = pos >= 0 && pos < g.table_len;
-        const float* cs = g.cos_t + (int64_t)(ok ? pos : 0) * 32;
-        const float* sn = g.sin_t + (int64_t)(ok ? pos : 0) * 32;
+        const int ml = wm * 128 + mi * 32 + r32;
+        const float* crow = tcs + ml * 32;
+        const float* srow = tsn + ml * 32;
         if (!g.rope_interleave) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
+          for (int q = 0; q < 4; ++q) {
+            const float4 c4 = *(const float4*)&crow[((2 * q + hs) ^ (ml & 7)) << 2];
+            const float4 s4 = *(const float4*)&srow[((2 * q + hs) ^ (ml & 7)) << 2];
+            const float cv[4] = {c4.x, c4.y, c4.z, c4.w}, sv[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const int i = q * 8 + hs * 4 + e;
+              const float c = on[p] ? cv[e] : rc[p], ss = on[p] ? sv[e] : rs[p];
               const float x0 = acc[2 * p][mi][q * 4 + e], x1 = acc[2 * p + 1][mi][q * 4 + e];
-              const float c = ok ? cs[i] : __builtin_nanf(""), sv = ok ? sn[i] : __builtin_nanf("");
-              acc[2 * p][mi][q * 4 + e] = x0 * c - x1 * sv;
-              acc[2 * p + 1][mi][q * 4 + e] = x1 * c + x0 * sv;
+              acc[2 * p][mi][q * 4 + e] = x0 * c - x1 * ss;
+              acc[2 * p + 1][mi][q * 4 + e] = x1 * c + x0 * ss;
             }
+          }
         } else {
 #pragma unroll
           for (int t = 0; t < 2; ++t)
@@ -379,14 +420,14 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g) {
 #pragma unroll
               for (int e = 0; e < 4; e += 2) {
                 const int i = (t * 32 + q * 8 + hs * 4 + e) >> 1;
+                const int at = (((i >> 2) ^ (ml & 7)) << 2) + (i & 3);
+                const float c = on[p] ? crow[at] : rc[p], ss = on[p] ? srow[at] : rs[p];
                 const float x0 = acc[2 * p + t][mi][q * 4 + e], x1 = acc[2 * p + t][mi][q * 4 + e + 1];
-                const float c = ok ? cs[i] : __builtin_nanf(""), sv = ok ? sn[i] : __builtin_nanf("");
-                acc[2 * p + t][mi][q * 4 + e] = x0 * c - x1 * sv;
-                acc[2 * p + t][mi][q * 4 + e + 1] = x1 * c + x0 * sv;
+                acc[2 * p + t][mi][q * 4 + e] = x0 * c - x1 * ss;
+                acc[2 * p + t][mi][q * 4 + e + 1] = x1 * c + x0 * ss;
               }
         }
       }
-    }
   }
 
   if constexpr (CT == 1) {
