@@ -146,7 +146,7 @@ PrefillWs prefill_layout(const mla_config* c, int64_t n, int64_t n_ctx = -1, int
   w.q_lat32 = off; off += align256(n * c->q_lora_rank * 4);   // fp32 down-projection before the norm
   w.q_lat = off; off += align256(n * c->q_lora_rank * es);
   w.q = off; off += align256(n * H * dqk * es);
-  w.ckv32 = off; off += align256(n * lw * 4);                  // fp32 [c | k_pe] before norm / RoPE
+  w.ckv32 = off; off += align256(2 * n * lw * 4);              // fp32 [c | k_pe] before norm / RoPE, two split-K partials
   w.latent = off; off += align256(n * lw * es);
   w.kpe16 = off; off += align256(n * c->qk_rope_dim * 2);      // fp16 shared rope key for attention
   const int64_t kv_rows = n_ctx >= 0 ? n_ctx : n;
@@ -640,10 +640,16 @@ static mla_status prefill_core(const mla_config* cfg, const mla_weights* w, cons
   // Output storage of each GEMM: OUT_ACT (the layer dtype), OUT_F32 (kept for a
   // following norm), OUT_F16 (attention operands of the bf16 layer).
   enum { OUT_ACT, OUT_F32, OUT_F16 };
+  // split > 1: the K range in `split` equal slices, one batch entry each,
+  // partial products at c + s * m * ldc (summed by the following norm)
   auto gemm = [&](const void* a, int64_t lda, const void* b, void* c, int64_t ldc, int m, int nn, int k,
-                  int out_kind, int epi, const void* gate) -> mla_status {
+                  int out_kind, int epi, const void* gate, int split = 1) -> mla_status {
     GemmArgs g{};
-    g.a = a; g.lda = lda; g.b = b; g.ldb = k; g.c = c; g.ldc = ldc; g.m = m; g.n = nn; g.k = k; g.batch = 1;
+    g.a = a; g.lda = lda; g.b = b; g.ldb = k; g.c = c; g.ldc = ldc; g.m = m; g.n = nn; g.k = k / split;
+    g.batch = split;
+    if (split > 1) {
+      g.a_bstride = k / split; g.b_bstride = k / split; g.c_bstride = (int64_t)m * ldc;
+    }
     g.c_f32 = out_kind == OUT_F32 && bf; g.c_f16 = out_kind == OUT_F16 && bf;
     g.epilogue = epi; g.gate_src = gate; g.ldg = ldc;
     g.cos_t = rope_cos; g.sin_t = rope_sin; g.table_len = rope_table_len; g.positions = positions;
@@ -654,8 +660,9 @@ static mla_status prefill_core(const mla_config* cfg, const mla_weights* w, cons
   };
   auto norm = [&](const void* src, int64_t stride, int width, int norm_dim, const void* gamma, int rope_off,
                   int rope_slices, int rope_stride, void* dst, int64_t dst_stride, bool src_f32,
-                  f16* aux = nullptr) -> mla_status {
+                  f16* aux = nullptr, int64_t src2_off = 0) -> mla_status {
     NormRopeArgs a{};
+    a.src2_off = src2_off;
     a.rope_aux = aux; a.rope_aux_stride = dr; a.interleave = cfg->rope_interleave;
     a.src = src; a.src_stride = stride; a.n_rows = n; a.row_width = width; a.norm_dim = norm_dim; a.gamma = gamma;
     a.eps = cfg->norm_eps; a.rope_offset = rope_off; a.rope_slices = rope_slices; a.rope_stride = rope_stride;
@@ -674,6 +681,11 @@ static mla_status prefill_core(const mla_config* cfg, const mla_weights* w, cons
   const int q_epi = (rope && bf) ? EPI_ROPE : EPI_STORE;
   const int att_kind = f16op ? OUT_F16 : OUT_ACT;
   f16* kpe16 = (f16*)(ws + L.kpe16);
+  // The joint down-projection (N = r_kv + d_rope = 576: 160 output tiles of
+  // 128 x 128 over K = hidden, a third of the CUs idle) runs as two K halves
+  // whose fp32 partials the latent norm adds (kv_a of the DeepSeek-V3 layer
+  // 127 -> 77 us; the q down-projection, 384 tiles, gained nothing so)
+  const int dsplit = (bf && hid % 64 == 0) ? 2 : 1;
   if (rq > 0) {
     void* ql_raw = bf ? (void*)q_lat32 : q_lat;
     if ((s = gemm(x, hid, w->w_q_a, ql_raw, rq, n, rq, hid, OUT_F32, EPI_STORE, nullptr)) != MLA_OK) return s;
@@ -688,8 +700,10 @@ static mla_status prefill_core(const mla_config* cfg, const mla_weights* w, cons
   // joint latent: down-projection, latent norm + k_pe RoPE -> [c_n | k_pe']
   {
     void* ckv_raw = bf ? (void*)ckv32 : (void*)(ws + L.ckv32);
-    if ((s = gemm(x, hid, w->w_kv_a, ckv_raw, lw, n, lw, hid, OUT_F32, EPI_STORE, nullptr)) != MLA_OK) return s;
-    if ((s = norm(ckv_raw, lw, lw, rkv, w->kv_a_gamma, rkv, rope ? 1 : 0, dr, lat, lw, true, f16op ? kpe16 : nullptr)) != MLA_OK) return s;
+    if ((s = gemm(x, hid, w->w_kv_a, ckv_raw, lw, n, lw, hid, OUT_F32, EPI_STORE, nullptr, dsplit)) != MLA_OK) return s;
+    if ((s = norm(ckv_raw, lw, lw, rkv, w->kv_a_gamma, rkv, rope ? 1 : 0, dr, lat, lw, true, f16op ? kpe16 : nullptr,
+                  dsplit > 1 ? (int64_t)n * lw : 0)) != MLA_OK)
+      return s;
   }
   // The rows keys and values are formed from: the new tokens' latent rows, or
   // for a chunk each sequence's cached prefix rows followed by its new rows.

@@ -232,6 +232,8 @@ struct NormRopeArgs {
   void* dst; int64_t dst_stride; const int32_t* slots; int64_t num_slots;
   f16* rope_aux; int64_t rope_aux_stride;          // optional fp16 copy of the rotated slice (one slice)
   int interleave;                                  // pairs (2i, 2i+1) instead of (i, i + d/2)
+  int64_t src2_off;                                // non-zero: each source value is the sum of the
+                                                   // elements at p and p + src2_off (two split-K partials)
 };
 // src/dst element types: bf16 -> bf16, fp32 -> fp32, or fp32 -> bf16 (src_f32 with bf16_io).
 hipError_t launch_norm_rope(const NormRopeArgs& a, bool bf16_io, hipStream_t s, bool src_f32 = false);

@@ -27,18 +27,20 @@ __global__ __launch_bounds__(64 * ROWS_PER_BLOCK) void norm_rope_kernel(NormRope
   }
   const TS* src = (const TS*)a.src + (int64_t)row * a.src_stride;
   T* dst = (T*)a.dst + drow * a.dst_stride;
+  // source value c (the sum of two split-K partials when src2_off is set)
+  auto ld = [&](int c) { return a.src2_off ? to_f32(src[c]) + to_f32(src[c + a.src2_off]) : to_f32(src[c]); };
 
   float rinv = 1.f;
   if (a.norm_dim > 0) {
     float ss = 0.f;
-    if (sizeof(TS) == 2 && (a.norm_dim & 7) == 0 && ((reinterpret_cast<uintptr_t>(src) & 15) == 0)) {
+    if (sizeof(TS) == 2 && !a.src2_off && (a.norm_dim & 7) == 0 && ((reinterpret_cast<uintptr_t>(src) & 15) == 0)) {
       for (int c = lane * 8; c < a.norm_dim; c += 64 * 8) {
         const bf16x8 v = *(const bf16x8*)(src + c);
 #pragma unroll
         for (int e = 0; e < 8; ++e) { const float f = (float)v[e]; ss = fmaf(f, f, ss); }
       }
     } else {
-      for (int c = lane; c < a.norm_dim; c += 64) { const float f = to_f32(src[c]); ss = fmaf(f, f, ss); }
+      for (int c = lane; c < a.norm_dim; c += 64) { const float f = ld(c); ss = fmaf(f, f, ss); }
     }
     ss = wave_sum(ss);
     rinv = rsqrtf(ss / (float)a.norm_dim + a.eps);
@@ -54,7 +56,7 @@ __global__ __launch_bounds__(64 * ROWS_PER_BLOCK) void norm_rope_kernel(NormRope
   // normalised / copied columns
   for (int c = lane; c < a.row_width; c += 64) {
     if (in_rope(c)) continue;
-    float v = to_f32(src[c]);
+    float v = ld(c);
     if (c < a.norm_dim) v = v * rinv * to_f32(((const T*)a.gamma)[c]);   // gain has the output dtype
     dst[c] = from_f32<T>(v);
     if (a.rope_aux && c >= a.rope_offset && c < a.rope_offset + a.rope_dim)   // unrotated shared part
@@ -69,7 +71,7 @@ __global__ __launch_bounds__(64 * ROWS_PER_BLOCK) void norm_rope_kernel(NormRope
     // pair (i, i + half), or (2i, 2i + 1) for interleaved pairs
     const int l0 = a.interleave ? 2 * i : i, l1 = a.interleave ? 2 * i + 1 : i + half;
     const int c0 = a.rope_offset + s * a.rope_stride + l0, c1 = a.rope_offset + s * a.rope_stride + l1;
-    const float x0 = to_f32(src[c0]), x1 = to_f32(src[c1]);
+    const float x0 = ld(c0), x1 = ld(c1);
     float y0, y1;
     if (pos_ok) {
       const float cs = a.cos_t[(int64_t)pos * half + i], sn = a.sin_t[(int64_t)pos * half + i];
@@ -106,6 +108,18 @@ __device__ __forceinline__ void load8f(const TS* p, float (&v)[8]) {
     const bf16x8 a = *(const bf16x8*)p;
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = (float)a[e];
+  }
+}
+// A source chunk: 8 values at p, plus the 8 at p + src2_off when the source
+// is two split-K partials.
+template <typename TS>
+__device__ __forceinline__ void load8src(const NormRopeArgs& a, const TS* p, float (&v)[8]) {
+  load8f(p, v);
+  if (a.src2_off) {
+    float t[8];
+    load8f(p + a.src2_off, t);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] += t[e];
   }
 }
 template <typename T>
@@ -154,7 +168,7 @@ __global__ __launch_bounds__(64 * ROWS_PER_BLOCK) void norm_rope_vec_kernel(Norm
     float ss = 0.f;
     for (int ch = lane; ch < nnorm; ch += 64) {
       float v[8];
-      load8f(src + ch * 8, v);
+      load8src(a, src + ch * 8, v);
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
     }
@@ -165,7 +179,7 @@ __global__ __launch_bounds__(64 * ROWS_PER_BLOCK) void norm_rope_vec_kernel(Norm
   for (int ch = lane; ch < nch; ch += 64) {
     if (in_rope(ch)) continue;
     float v[8];
-    load8f(src + ch * 8, v);
+    load8src(a, src + ch * 8, v);
     if (ch < nnorm) {
       float g[8];
       load8f((const T*)a.gamma + ch * 8, g);    // the gain has the output dtype
@@ -189,8 +203,8 @@ __global__ __launch_bounds__(64 * ROWS_PER_BLOCK) void norm_rope_vec_kernel(Norm
       const int s = p / per, j = p - s * per;
       const int c0 = a.rope_offset + s * a.rope_stride + 8 * j, c1 = c0 + half;
       float x0[8], x1[8], cs[8], sn[8];
-      load8f(src + c0, x0);
-      load8f(src + c1, x1);
+      load8src(a, src + c0, x0);
+      load8src(a, src + c1, x1);
       load8f(cs_row + 8 * j, cs);
       load8f(sn_row + 8 * j, sn);
       float y0[8], y1[8];
@@ -213,7 +227,7 @@ __global__ __launch_bounds__(64 * ROWS_PER_BLOCK) void norm_rope_vec_kernel(Norm
       const int s = p / per, j = p - s * per;
       const int c0 = a.rope_offset + s * a.rope_stride + 8 * j;
       float x[8], y[8];
-      load8f(src + c0, x);
+      load8src(a, src + c0, x);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float c = pos_ok ? cs_row[4 * j + e] : nan, sv = pos_ok ? sn_row[4 * j + e] : nan;
@@ -261,7 +275,7 @@ __global__ __launch_bounds__(64 * ROWS_PER_BLOCK) void norm_rope_reg_kernel(Norm
     const int ch = lane + 64 * i;
     own[i] = ch < nch && !in_rope(ch);
     if (own[i]) {
-      load8f(src + ch * 8, v[i]);
+      load8src(a, src + ch * 8, v[i]);
       if (ch < nnorm) load8f((const T*)a.gamma + ch * 8, g[i]);   // the gain has the output dtype
     }
   }
@@ -278,8 +292,8 @@ __global__ __launch_bounds__(64 * ROWS_PER_BLOCK) void norm_rope_reg_kernel(Norm
     if (rp[j]) {
       const int s = p / per, jj = p - s * per;
       const int c0 = a.rope_offset + s * a.rope_stride + 8 * jj;
-      load8f(src + c0, x0[j]);
-      load8f(src + c0 + half, x1[j]);
+      load8src(a, src + c0, x0[j]);
+      load8src(a, src + c0 + half, x1[j]);
       const int64_t trow = (int64_t)(pos_ok ? pos : 0) * half + 8 * jj;
       load8f(a.cos_t + trow, cs[j]);
       load8f(a.sin_t + trow, sn[j]);
