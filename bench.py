@@ -682,6 +682,8 @@ def main():
         sink_b = torch.zeros(1, dtype=torch.int64, device=dev)
         dcalls = device_kernels(torch, decode, reps, between=lambda: sink_b.copy_(flush_b.view(torch.int64).sum()))
         del flush_b
+        ncalls = device_kernels(torch, norm_rope, reps)
+        norm_dev_us = sum(us for c in ncalls for _, us in c) / reps
         dk = {}
         for key in ("absorb_q", "decode_split", "decode_combine"):
             t = [sum(us for nm, us in c if key in nm) for c in dcalls]
@@ -694,6 +696,9 @@ def main():
             "source": "torch.profiler device durations, mean of 3 calls (the decode after a 512 MiB flush)",
             "prefill_layer_kernels_us": round(layer_kernel_us, 1),
             "prefill_gemms": per_gemm,
+            "latent_norm_rope_kernel": {"us": round(norm_dev_us, 2),
+                                        "gbs": round(norm_bytes / (norm_dev_us * 1e-6) / 1e9, 1),
+                                        "frac": round(norm_bytes / (norm_dev_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
             "decode_kernels_us": {k: round(v, 1) for k, v in dk.items()},
             "decode_split_kernel": {"us": round(sp_us, 1), "cache_bytes": cache_b,
                                     "cache_gbs": round(cache_b / (sp_us * 1e-6) / 1e9, 1),
