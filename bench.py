@@ -113,7 +113,10 @@ def layer_flops(shape, n, attn):
     f += 2 * n * shape.hidden * (r + dr) + 2 * n * r * H * (shape.qk_nope_dim + dv)
     if shape.output_gate:
         f += 2 * n * shape.hidden * H * dv
-    f += 2 * n * H * dv * shape.hidden
+    if shape.o_groups:
+        f += 2 * n * H * dv * shape.o_lora_rank + 2 * n * shape.o_groups * shape.o_lora_rank * shape.hidden
+    else:
+        f += 2 * n * H * dv * shape.hidden
     return f + attn
 
 
@@ -550,6 +553,41 @@ def main():
     prefill_ms = sum(a.elapsed_time(b) for a, b in pe) / args.steps
     print(f"steps done: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
 
+    # ------------------------------------------------------------------ the same layer with the grouped low-rank
+    # output projection (8 groups x 1024, the guide's grouping), seeded N(0, 0.02) W_o_a / W_o_b
+    grouped_rec = None
+    if sh.o_groups == 0 and (sh.num_heads * sh.v_head_dim) % 8 == 0:
+        gsh = sh.replace(o_groups=8, o_lora_rank=1024)
+        gcfg = mla.make_config(gsh)
+        gcfg.attn_operand = cfg.attn_operand
+        gg = torch.Generator(device=dev).manual_seed(13)
+        fg = sh.num_heads * sh.v_head_dim // 8
+        Wg = dict(W)
+        Wg["w_o"] = None
+        Wg["w_o_a"] = (0.02 * torch.randn(8 * 1024, fg, device=dev, generator=gg)).to(torch.bfloat16)
+        Wg["w_o_b"] = (0.02 * torch.randn(sh.hidden, 8 * 1024, device=dev, generator=gg)).to(torch.bfloat16)
+        ws_g = torch.empty(mla.prefill_workspace_size(gcfg, n, len(cuh) - 1), dtype=torch.uint8, device=dev)
+        grouped = lambda: mla.prefill_fwd(gcfg, Wg, x, cu, cuh, out, latent_out=lat, rope_cos=cos, rope_sin=sin,
+                                          workspace=ws_g)
+        g_ms = timed(grouped, args.steps, warm=5)
+        g_fl = layer_flops(gsh, n, attention_flops(sh, cuh))
+        grouped_rec = {"workload": f"{args.prefill} with the output projection as 8 groups x 1024 (W_o_a, W_o_b)",
+                       "layer_ms": round(g_ms, 4), "layer_tflops": round(g_fl / (g_ms * 1e-3) / 1e12, 2)}
+        try:
+            gc = device_kernels(torch, grouped, 3)
+            gl = layer_gemms(gsh, n)
+            gem = [[us for nm, us in c if "gemm" in nm] for c in gc]
+            if all(len(c) == len(gl) for c in gem):
+                for i, (nm, fl) in enumerate(gl):
+                    if nm in ("o_a", "o_b"):
+                        us = sum(c[i] for c in gem) / len(gem)
+                        grouped_rec[nm] = {"us": round(us, 1), "tflops": round(fl / (us * 1e-6) / 1e12, 1),
+                                           "frac": round(fl / (us * 1e-6) / 1e12 / PEAK_MFMA_TFLOPS, 4)}
+        except Exception as ex:
+            grouped_rec["breakdown_error"] = f"{type(ex).__name__}: {ex}"[:200]
+        del Wg, ws_g
+        torch.cuda.empty_cache()
+
     # ------------------------------------------------------------------ attention kernel alone, graded workloads
     # warm-up launches bring the GPU to the kernel's steady state after the
     # layer steps (power and clock state, caches)
@@ -755,6 +793,8 @@ def main():
     if chunk_rec is not None:
         rec["chunked_prefill"] = chunk_rec
     rec["kernel_breakdown"] = breakdown
+    if grouped_rec is not None:
+        rec["grouped_o_proj_layer"] = grouped_rec
     if bwd_rec is not None:
         rec["attention_backward"] = bwd_rec
     rec["layer_backward"] = layer_bwd_rec
