@@ -937,7 +937,7 @@ mla_status mla_attention_prefill_bwd(const mla_config* cfg, const void* q, const
 // ---------------------------------------------------------------- layer backward
 namespace {
 struct LayerBwdWs {
-  size_t pos, q_lat32, q_lat, q, ckv32, lat, kv, attn, gpre, a2, ot, dt, da2, da, dg, dq32, dkv32, dkpe32, abw,
+  size_t pos, q_lat32, q_lat, q, ckv32, lat, kv, attn, gpre, a2, ot, dt, da2, da, dg, dkpe32, abw,
       dq16, dkv16, dckv, dcn32, dqln32, dql16, rinv, part, tr, trb, xt, wot, split, total;
   int64_t npad;
 };
@@ -966,11 +966,9 @@ LayerBwdWs layer_bwd_layout(const mla_config* c, int64_t n) {
   w.a2 = take(c->output_gate ? n * F * 2 : 0);
   w.ot = take(n * gro * 2);
   w.dt = take(n * gro * 2);
-  w.da2 = take(n * F * 4);
+  w.da2 = take(c->output_gate ? n * F * 4 : 0);        // fp32 dA2 for the gate's backward
   w.da = take(n * F * 2);
   w.dg = take(c->output_gate ? n * F * 2 : 0);
-  w.dq32 = take(n * H * dqk * 4);
-  w.dkv32 = take(n * H * dkv * 4);
   w.dkpe32 = take(n * dr * 4);
   w.abw = take(mla_attention_bwd_workspace_size(c, (int32_t)n));
   w.dq16 = take(n * H * dqk * 2);
@@ -1186,8 +1184,9 @@ mla_status mla_prefill_bwd(const mla_config* cfg, const mla_weights* w, const vo
     if ((s = gemm(tr, npad, a2, F, dw->w_o_a, fg, ro, fg, n, true, true, false, EPI_STORE, G, (int64_t)ro * npad, fg,
                   (int64_t)ro * fg)) != MLA_OK)
       return s;
-    if ((s = gemm(dt, gro, w->w_o_a, fg, da2, F, n, fg, ro, true, true, false, EPI_STORE, G, ro, (int64_t)ro * fg,
-                  fg)) != MLA_OK)
+    // dA2 in fp32 for the gate's backward, else straight to bf16 dA
+    if ((s = gemm(dt, gro, w->w_o_a, fg, cfg->output_gate ? (void*)da2 : at(L.da), F, n, fg, ro, true,
+                  cfg->output_gate, false, EPI_STORE, G, ro, (int64_t)ro * fg, fg)) != MLA_OK)
       return s;
   } else {
     if ((s = weight_grad(dout, false, hid, hid, a2, F, F, dw->w_o)) != MLA_OK) return s;
@@ -1195,22 +1194,21 @@ mla_status mla_prefill_bwd(const mla_config* cfg, const mla_weights* w, const vo
     bf16* wot = (bf16*)at(L.wot);
     if ((e = launch_transpose_bf16(w->w_o, false, F, hid, F, wot, hid, hid, st)) != hipSuccess)
       return hip_fail(e, "transpose");
-    if ((s = gemm(dout, hid, wot, hid, da2, F, n, F, hid, false, true, false)) != MLA_OK) return s;
+    if ((s = gemm(dout, hid, wot, hid, cfg->output_gate ? (void*)da2 : at(L.da), F, n, F, hid, false,
+                  cfg->output_gate, false)) != MLA_OK)
+      return s;
   }
   // ---- gate
   bf16* da = (bf16*)at(L.da);
   bf16* dgp = (bf16*)at(L.dg);
   if (cfg->output_gate) {
     if ((e = launch_gate_bwd(da2, attn, gpre, da, dgp, (int64_t)n * F, st)) != hipSuccess) return hip_fail(e, "gate backward");
-  } else {
-    RopeBackArgs a{};
-    a.src = da2; a.ld_src = F; a.n_rows = n; a.width = F; a.dst = da; a.ld_dst = F;
-    if ((e = launch_rope_back(a, st)) != hipSuccess) return hip_fail(e, "convert");
   }
-  // ---- attention core
-  float* dq32 = (float*)at(L.dq32);
-  float* dkv32 = (float*)at(L.dkv32);
+  // ---- attention core: bf16 dq (rotary map undone) and [dk_nope | dv],
+  // fp32 shared-key gradient
   float* dkpe32 = (float*)at(L.dkpe32);
+  bf16* dq16 = (bf16*)at(L.dq16);
+  bf16* dkv16 = (bf16*)at(L.dkv16);
   {
     AttnBwdArgs a{};
     char* aw = (char*)at(L.abw);
@@ -1219,16 +1217,15 @@ mla_status mla_prefill_bwd(const mla_config* cfg, const mla_weights* w, const vo
     a.lse = (float*)aw;
     a.dsum = (float*)(aw + align256((size_t)n * H * 4));
     a.dkr = (float*)(aw + 2 * align256((size_t)n * H * 4));
-    a.dq = dq32; a.dkv = dkv32; a.dkpe = dkpe32;
+    a.dkpe = dkpe32;
     a.lse_ready = true;
+    a.dq16 = dq16; a.dkv16 = dkv16;
+    a.rope = rope; a.rope_interleave = cfg->rope_interleave != 0; a.cos_t = rope_cos; a.sin_t = rope_sin;
+    a.table_len = rope_table_len; a.positions = positions;
     if ((e = launch_attention_bwd(a, cu_seqlens_host, num_seqs, st)) != hipSuccess) return hip_fail(e, "attention backward");
   }
-  // ---- RoPE backward, bf16 gradients
-  bf16* dq16 = (bf16*)at(L.dq16);
-  bf16* dkv16 = (bf16*)at(L.dkv16);
+  // ---- RoPE backward of the shared key part, bf16
   bf16* dckv = (bf16*)at(L.dckv);
-  if ((s = rope_back(dq32, (int64_t)H * dqk, H * dqk, dq16, (int64_t)H * dqk, dn, H, dqk)) != MLA_OK) return s;
-  if ((s = rope_back(dkv32, (int64_t)H * dkvw, H * dkvw, dkv16, (int64_t)H * dkvw, 0, 0, dr)) != MLA_OK) return s;
   if ((s = rope_back(dkpe32, dr, dr, dckv + rkv, lw, 0, 1, dr)) != MLA_OK) return s;
   // ---- kv up-projection, latent norm, joint down-projection
   float* dcn32 = (float*)at(L.dcn32);

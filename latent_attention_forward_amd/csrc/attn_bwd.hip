@@ -70,6 +70,12 @@ struct BwdArgs {
   float* dkr;                        // [N, H, 64] per-head gradient of the shared key part
   float* dkpe;                       // [N, 64]
   int d_in_dq;                       // the dq pass forms D (lse given by the forward)
+  // bf16 outputs in place of dq and of the [dk_nope | dv] part of dkv: dq16
+  // with the rotary map undone on dims 128..191 (rope set), the gradient with
+  // respect to the query before its rotation
+  bf16* dq16; bf16* dkv16;
+  const float* cos_t; const float* sin_t; const int32_t* positions;
+  int table_len; int rope; int rope_interleave;
 };
 
 // chunk swizzles (bits of the row permuted; see the header)
@@ -407,6 +413,52 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, BwdPlan plan)
   }
   if (!live) return;
   // lane holds query my_q, dims b*32 + (e/4)*8 + hsel*4 + e%4
+  if (a.dq16) {
+    f32x16 y[DQK / 32];
+#pragma unroll
+    for (int b = 0; b < DQK / 32; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) y[b][e] = acc[b][e] * a.scale;
+    if (a.rope) {
+      // the transpose of the rotation on the pairs of the 64 rotary dims
+      // (blocks 4 and 5): (i, i + 32) or, interleaved, (2i, 2i + 1)
+      const int pos = a.positions[my_q];
+      const bool ok = pos >= 0 && pos < a.table_len;
+      const float* ct = a.cos_t + (int64_t)(ok ? pos : 0) * (DR / 2);
+      const float* sn = a.sin_t + (int64_t)(ok ? pos : 0) * (DR / 2);
+      const float nan = __builtin_nanf("");
+      if (a.rope_interleave) {
+#pragma unroll
+        for (int b = 4; b < 6; ++b)
+#pragma unroll
+          for (int e = 0; e < 16; e += 2) {
+            const int pi = ((b - 4) * 32 + (e >> 2) * 8 + hsel * 4 + (e & 3)) >> 1;
+            const float c = ok ? ct[pi] : nan, s = ok ? sn[pi] : nan;
+            const float v0 = y[b][e], v1 = y[b][e + 1];
+            y[b][e] = v0 * c + v1 * s;
+            y[b][e + 1] = v1 * c - v0 * s;
+          }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int pi = (e >> 2) * 8 + hsel * 4 + (e & 3);
+          const float c = ok ? ct[pi] : nan, s = ok ? sn[pi] : nan;
+          const float v0 = y[4][e], v1 = y[5][e];
+          y[4][e] = v0 * c + v1 * s;
+          y[5][e] = v1 * c - v0 * s;
+        }
+      }
+    }
+    bf16* out16 = a.dq16 + ((int64_t)my_q * H + h) * DQK;
+#pragma unroll
+    for (int b = 0; b < DQK / 32; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const bf16x4 v = {(bf16)y[b][g * 4 + 0], (bf16)y[b][g * 4 + 1], (bf16)y[b][g * 4 + 2], (bf16)y[b][g * 4 + 3]};
+        *(bf16x4*)(out16 + b * 32 + g * 8 + hsel * 4) = v;
+      }
+    return;
+  }
   float* out = a.dq + ((int64_t)my_q * H + h) * DQK;
 #pragma unroll
   for (int b = 0; b < DQK / 32; ++b)
@@ -586,8 +638,34 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, BwdPlan pla
   }
   if (!live) return;
   // lane holds key my_k, dims b*32 + (e/4)*8 + hsel*4 + e%4
-  float* okv = a.dkv + ((int64_t)my_k * H + h) * (DN + DV);
   float* okr = a.dkr + ((int64_t)my_k * H + h) * DR;
+  if (a.dkv16) {
+    bf16* o16 = a.dkv16 + ((int64_t)my_k * H + h) * (DN + DV);
+#pragma unroll
+    for (int b = 0; b < DQK / 32; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float x0 = dk[b][g * 4 + 0] * a.scale, x1 = dk[b][g * 4 + 1] * a.scale;
+        const float x2 = dk[b][g * 4 + 2] * a.scale, x3 = dk[b][g * 4 + 3] * a.scale;
+        const int d = b * 32 + g * 8 + hsel * 4;
+        if (d < DN) {
+          const bf16x4 v = {(bf16)x0, (bf16)x1, (bf16)x2, (bf16)x3};
+          *(bf16x4*)(o16 + d) = v;
+        } else {
+          *(float4*)(okr + d - DN) = make_float4(x0, x1, x2, x3);
+        }
+      }
+#pragma unroll
+    for (int b = 0; b < DV / 32; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const bf16x4 v = {(bf16)dv[b][g * 4 + 0], (bf16)dv[b][g * 4 + 1], (bf16)dv[b][g * 4 + 2],
+                          (bf16)dv[b][g * 4 + 3]};
+        *(bf16x4*)(o16 + DN + b * 32 + g * 8 + hsel * 4) = v;
+      }
+    return;
+  }
+  float* okv = a.dkv + ((int64_t)my_k * H + h) * (DN + DV);
 #pragma unroll
   for (int b = 0; b < DQK / 32; ++b)
 #pragma unroll
@@ -628,6 +706,8 @@ hipError_t launch_attention_bwd(const AttnBwdArgs& g, const int32_t* cu_host, in
   a.o = (const bf16*)g.o; a.dout = (const bf16*)g.dout; a.cu = g.cu_dev; a.n_tokens = g.n_tokens; a.heads = g.heads;
   a.scale = g.scale; a.lse = g.lse; a.dsum = g.dsum; a.dq = g.dq; a.dkv = g.dkv; a.dkr = g.dkr; a.dkpe = g.dkpe;
   a.d_in_dq = g.lse_ready ? 1 : 0;
+  a.dq16 = g.dq16; a.dkv16 = g.dkv16; a.cos_t = g.cos_t; a.sin_t = g.sin_t; a.positions = g.positions;
+  a.table_len = g.table_len; a.rope = g.rope ? 1 : 0; a.rope_interleave = g.rope_interleave ? 1 : 0;
   if (g.n_tokens <= 0) return hipSuccess;
   // every (document, 128-row tile); the query-major passes take the tiles
   // with the longest key range first, the key-major pass those with the

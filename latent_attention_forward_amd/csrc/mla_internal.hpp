@@ -290,6 +290,11 @@ struct AttnBwdArgs {
   float* lse; float* dsum; float* dkr;                 // [H, N], [H, N], [N, H, 64]
   float* dq; float* dkv; float* dkpe;                  // [N, H, 192], [N, H, 256], [N, 64]
   bool lse_ready;   // lse holds the forward's values: no statistics pass, D formed in the dq pass
+  // optional bf16 outputs replacing dq and dkv's [dk_nope | dv] (dkr and dkpe
+  // stay fp32); dq16 has the rotary map undone on its rope dims when rope is set
+  bf16* dq16 = nullptr; bf16* dkv16 = nullptr;
+  const float* cos_t = nullptr; const float* sin_t = nullptr; const int32_t* positions = nullptr;
+  int table_len = 0; bool rope = false; bool rope_interleave = false;
 };
 hipError_t launch_attention_bwd(const AttnBwdArgs& a, const int32_t* cu_host, int num_seqs, hipStream_t s);
 
