@@ -1065,15 +1065,38 @@ mla_status mla_prefill_bwd(const mla_config* cfg, const mla_weights* w, const vo
     const hipError_t err = launch_gemm_bf16(g, st);
     return err == hipSuccess ? MLA_OK : hip_fail(err, "layer backward GEMM");
   };
-  // dW [cols(dy), cols(xin)] = dy^T xin over the n tokens: dy and xin
-  // transposed (rounded to bf16, zero past the last token) into K-major
-  // buffers, then an NT product over the padded token count (x^T, which three
-  // gradients read, is transposed once)
+  // dW [cols(dy), cols(xin)] = dy^T xin over the n tokens.  With at least
+  // 256 output tiles of 256 x 256 the first n - n % 32 tokens run on the
+  // 256x256 kernel reading dy and xin as stored (K-major operands) and the
+  // last n % 32 are added from their transposes (zero-padded to 64 tokens);
+  // otherwise dy and xin are transposed (rounded to bf16, zero past the last
+  // token) into K-major buffers for an NT product over the padded token count
+  // (x^T, which three gradients read, is transposed once).
   bf16* trb = (bf16*)at(L.trb);
   bf16* xt = (bf16*)at(L.xt);
   bool xt_ready = false;
   auto weight_grad = [&](const void* dy, bool dy_f32, int64_t ld_dy, int dy_cols, const void* xin, int64_t ld_x,
                          int x_cols, float* out) -> mla_status {
+    const int n32 = n / 32 * 32;
+    const int64_t out_tiles = (int64_t)((dy_cols + 255) / 256) * ((x_cols + 255) / 256);
+    if (!dy_f32 && n32 > 0 && out_tiles >= 256 && dy_cols % 8 == 0 && x_cols % 8 == 0 && ld_dy % 8 == 0 &&
+        ld_x % 8 == 0 && aligned16(dy) && aligned16(xin)) {
+      GemmArgs g{};
+      g.a = dy; g.lda = ld_dy; g.b = xin; g.ldb = ld_x; g.c = out; g.ldc = x_cols;
+      g.m = dy_cols; g.n = x_cols; g.k = n32; g.batch = 1; g.c_f32 = true; g.epilogue = EPI_STORE; g.kmajor = true;
+      hipError_t err = launch_gemm_bf16(g, st);
+      if (err != hipSuccess) return hip_fail(err, "weight-gradient GEMM");
+      if (n32 == n) return MLA_OK;
+      const int rows = n - n32;
+      bf16* xb = xin == x ? xt : trb;
+      if (xin == x) xt_ready = false;     // xt now holds the tail only
+      if ((err = launch_transpose_bf16((const bf16*)dy + (int64_t)n32 * ld_dy, false, ld_dy, rows, dy_cols, tr, 64,
+                                       64, st)) != hipSuccess ||
+          (err = launch_transpose_bf16((const bf16*)xin + (int64_t)n32 * ld_x, false, ld_x, rows, x_cols, xb, 64, 64,
+                                       st)) != hipSuccess)
+        return hip_fail(err, "transpose");
+      return gemm(tr, 64, xb, 64, out, x_cols, dy_cols, x_cols, 64, false, true, true);
+    }
     hipError_t err = launch_transpose_bf16(dy, dy_f32, ld_dy, n, dy_cols, tr, npad, (int)npad, st);
     if (err != hipSuccess) return hip_fail(err, "transpose");
     const bf16* bt = trb;

@@ -218,6 +218,10 @@ struct GemmArgs {
   // ld_scale bytes); n a multiple of 32
   bool c_mx; void* c_scale; int64_t ld_scale;
   bool c_acc;                                      // fp32 C (128x128 kernel): C += result instead of C = result
+  // both operands stored K-major, A [k, m] and B [k, n] (C = A^T B, the form
+  // of a weight gradient dY^T X over tokens): the 256x256 kernel only, fp32
+  // output, K a multiple of 32, m and n multiples of 8
+  bool kmajor;
 };
 enum { EPI_STORE = 0, EPI_GATE = 1, EPI_ROPE = 2 };
 

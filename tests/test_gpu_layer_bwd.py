@@ -115,6 +115,22 @@ def test_layer_backward_variants(mla, variant):
     run_case(mla, VARIANTS[variant], [37, 100, 3])
 
 
+# 128 heads: dW_kv_b ([128 * 256, 512]) and, with the direct q projection
+# and hidden 768, dW_q ([128 * 192, 768]) have at least 256 output tiles of
+# 256 x 256, so they run on K-major operands over the first 288 of the 300
+# tokens, the last 12 added from their transposes.
+MANY_HEADS = {
+    "q_lora": mi.WORKLOADS["dsv3_prefill_4096"].replace(q_lora_rank=128, hidden=256, num_heads=128),
+    "direct_q": mi.WORKLOADS["megatron_2x2048"].replace(hidden=768, num_heads=128),
+}
+
+
+@pytest.mark.parametrize("variant", list(MANY_HEADS))
+def test_layer_backward_many_heads(mla, variant):
+    _say(f"case: layer backward 128 heads {variant}, lens=[37, 100, 163]")
+    run_case(mla, MANY_HEADS[variant], [37, 100, 163], seed=6)
+
+
 def test_layer_backward_one_token_documents(mla):
     """Documents of one token (their attention gradient reaches only v) beside
     a document longer than one 128-row tile."""
