@@ -237,14 +237,15 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmArgs g) {
 // LDS tile [256 rows][32 k]: 4 chunks of 16 B per row, chunk c of row r at
 // c ^ ((r >> 2) & 3), so the 16 rows one 16-lane phase of an operand read
 // touches (4 rows per 256 B of banks) land on distinct banks.
-// K-major operands (KM): a stage is [32 k][256 columns], 32 chunks of 16 B
+// K-major operands (KM bit 0: A [k, m], bit 1: B [k, n]): a stage is
+// [32 k][256 columns], 32 chunks of 16 B
 // per k row, chunk c of row k at c ^ 2 (k & 3); an MFMA operand is read with
 // two transposing reads (ds_read_b64_tr_b16) per 8 k, each 16-lane phase
 // touching 4 k rows x 32 B, which the swizzle puts on distinct banks.
 constexpr int GBM = 256, GBN = 256, GBK = 32, GSTAGES = 4;
 __device__ __forceinline__ int gsw(int r, int c) { return r * GBK + ((c ^ ((r >> 2) & 3)) << 3); }
 
-template <int EPI, int CT, bool KM = false>   // CT: 0 bf16, 1 fp32, 2 fp16, 3 MXFP8 (E4M3 codes + E8M0 block scales) output
+template <int EPI, int CT, int KM = 0>   // CT: 0 bf16, 1 fp32, 2 fp16, 3 MXFP8 (E4M3 codes + E8M0 block scales) output
 __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g) {
   // operand stages, then (after the K loop) the 256x256 output tile in 16-bit
   // values: row r of 512 B with 16-byte chunk c at c ^ (r & 31)
@@ -257,8 +258,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g) {
   const int num_m = (g.m + GBM - 1) / GBM, num_n = (g.n + GBN - 1) / GBN;
   const int2 tc = tile_coords(blockIdx.x, num_m, num_n);
   const int m0 = tc.x * GBM, n0 = tc.y * GBN;
-  const bf16* A = (const bf16*)g.a + (int64_t)blockIdx.z * g.a_bstride + (KM ? (int64_t)m0 : (int64_t)m0 * g.lda);
-  const bf16* B = (const bf16*)g.b + (int64_t)blockIdx.z * g.b_bstride + (KM ? (int64_t)n0 : (int64_t)n0 * g.ldb);
+  constexpr bool KA = (KM & 1) != 0, KB = (KM & 2) != 0;
+  const bf16* A = (const bf16*)g.a + (int64_t)blockIdx.z * g.a_bstride + (KA ? (int64_t)m0 : (int64_t)m0 * g.lda);
+  const bf16* B = (const bf16*)g.b + (int64_t)blockIdx.z * g.b_bstride + (KB ? (int64_t)n0 : (int64_t)n0 * g.ldb);
   const int wm = wave >> 1, wn = wave & 1;
   const int nk = g.k / GBK;
   // RoPE: the position of tile row tid, requested now for the table staging
@@ -271,19 +273,14 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int P = (wave + 4 * i) * 64 + lane;
-    if constexpr (KM) {
-      // K-major: row k = P / 32, physical chunk P % 32 holds logical chunk
-      // (P % 32) ^ 2 (k & 3); columns past the matrix read its last chunk
-      const int k = P >> 5, c = (P & 31) ^ ((k & 3) << 1);
-      const int cx = min(m0 + c * 8, g.m - 8) - m0, cw = min(n0 + c * 8, g.n - 8) - n0;
-      offx[i] = (uint32_t)(((int64_t)k * g.lda + cx) * 2);
-      offw[i] = (uint32_t)(((int64_t)k * g.ldb + cw) * 2);
-    } else {
-      const int r = P >> 2, c = (P & 3) ^ ((r >> 2) & 3);
-      const int rx = min(m0 + r, g.m - 1) - m0, rw = min(n0 + r, g.n - 1) - n0;
-      offx[i] = (uint32_t)(((int64_t)rx * g.lda + c * 8) * 2);
-      offw[i] = (uint32_t)(((int64_t)rw * g.ldb + c * 8) * 2);
-    }
+    // K-major: row k = P / 32, physical chunk P % 32 holds logical chunk
+    // (P % 32) ^ 2 (k & 3); columns past the matrix read its last chunk
+    const int k = P >> 5, kc = (P & 31) ^ ((k & 3) << 1);
+    const int r = P >> 2, c = (P & 3) ^ ((r >> 2) & 3);
+    if constexpr (KA) offx[i] = (uint32_t)(((int64_t)k * g.lda + min(m0 + kc * 8, g.m - 8) - m0) * 2);
+    else offx[i] = (uint32_t)(((int64_t)(min(m0 + r, g.m - 1) - m0) * g.lda + c * 8) * 2);
+    if constexpr (KB) offw[i] = (uint32_t)(((int64_t)k * g.ldb + min(n0 + kc * 8, g.n - 8) - n0) * 2);
+    else offw[i] = (uint32_t)(((int64_t)(min(n0 + r, g.n - 1) - n0) * g.ldb + c * 8) * 2);
   }
   // LDS byte address of this wave's first block in stage 0 of each operand
   const uint32_t lx = lds_addr_of(&sX[0][0]) + (uint32_t)wave * 1024u;
@@ -291,8 +288,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g) {
   // copy j (0..7) of step kt: x blocks for j < 4, w blocks for j >= 4
   auto issue_part = [&](int kt, int j) __attribute__((always_inline)) {
     const uint32_t st = (uint32_t)(kt % GSTAGES) * (GBM * GBK * 2);
-    const int64_t ka = KM ? (int64_t)kt * GBK * g.lda : (int64_t)kt * GBK;
-    const int64_t kb = KM ? (int64_t)kt * GBK * g.ldb : (int64_t)kt * GBK;
+    const int64_t ka = KA ? (int64_t)kt * GBK * g.lda : (int64_t)kt * GBK;
+    const int64_t kb = KB ? (int64_t)kt * GBK * g.ldb : (int64_t)kt * GBK;
     if (j < 4) lds_dma16_sv_m0(uniform_ptr(A + ka), offx[j], lx + st + j * 4096u);
     else lds_dma16_sv_m0(uniform_ptr(B + kb), offw[j - 4], lw + st + (j - 4) * 4096u);
   };
@@ -313,27 +310,21 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g) {
   // chunk 2 ks + lane/32; the swizzle depends on the row only through bits 2-3,
   // the same for every mi / ni
   const int r32 = lane & 31, hs = lane >> 5;
+  // K-major operand, transposing reads: lane L of 16-lane group q addresses
+  // k row ks*16 + (q/2)*8 + u*4 + L/4 at column 32 i + (q%2)*16 + 4 (L%4) of
+  // the wave's 128; the swizzle term 2 (k & 3) = 2 (L/4 & 3) flips bit 2 of
+  // the chunk index (bit 0 of i), so element offsets are base[i % 2] +
+  // 64 (i/2) + 256 (16 ks + 4 u).  Row-major operand: base[ks].
   int xoff[2], woff[2];
-  if constexpr (KM) {
-    // transposing reads: lane L of 16-lane group q addresses k row
-    // ks*16 + (q/2)*8 + u*4 + L/4 at column 32 i + (q%2)*16 + 4 (L%4) of the
-    // wave's 128; the swizzle term 2 (k & 3) = 2 (L/4 & 3) flips bit 2 of the
-    // chunk index (bit 0 of i), so element offsets are base[i % 2] + 64 (i/2)
-    // + 256 (16 ks + 4 u)
+  {
     const int q = lane >> 4, L = lane & 15, sw = ((L >> 2) & 3) << 1;
+    const int rowk = ((q >> 1) * 8 + (L >> 2)) * GBM;
 #pragma unroll
-    for (int ip = 0; ip < 2; ++ip) {
-      const int rowk = ((q >> 1) * 8 + (L >> 2)) * GBM;
-      const int cx = wm * 16 + 4 * ip + 2 * (q & 1) + ((L & 3) >> 1);
-      const int cw = wn * 16 + 4 * ip + 2 * (q & 1) + ((L & 3) >> 1);
-      xoff[ip] = rowk + ((cx ^ sw) << 3) + 4 * (L & 1);
-      woff[ip] = rowk + ((cw ^ sw) << 3) + 4 * (L & 1);
-    }
-  } else {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      xoff[ks] = gsw(wm * 128 + r32, 2 * ks + hs);
-      woff[ks] = gsw(wn * 128 + r32, 2 * ks + hs);
+    for (int j = 0; j < 2; ++j) {
+      const int cx = wm * 16 + 4 * j + 2 * (q & 1) + ((L & 3) >> 1);
+      const int cw = wn * 16 + 4 * j + 2 * (q & 1) + ((L & 3) >> 1);
+      xoff[j] = KA ? rowk + ((cx ^ sw) << 3) + 4 * (L & 1) : gsw(wm * 128 + r32, 2 * j + hs);
+      woff[j] = KB ? rowk + ((cw ^ sw) << 3) + 4 * (L & 1) : gsw(wn * 128 + r32, 2 * j + hs);
     }
   }
   // The copies of step kiss (when >= 0) go out one per 4 MFMAs: issued all at
@@ -347,14 +338,15 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g) {
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if constexpr (KM) {
-          const int o = (i >> 1) * 64 + ks * 16 * GBM;
+        const int o = (i >> 1) * 64 + ks * 16 * GBM;
+        if constexpr (KA)
           x[ks][i] = cat8(lds_read_tr(&sX[st][xoff[i & 1] + o]), lds_read_tr(&sX[st][xoff[i & 1] + o + 4 * GBM]));
-          w[ks][i] = cat8(lds_read_tr(&sW[st][woff[i & 1] + o]), lds_read_tr(&sW[st][woff[i & 1] + o + 4 * GBM]));
-        } else {
+        else
           x[ks][i] = *(const bf16x8*)&sX[st][xoff[ks] + i * 32 * GBK];
+        if constexpr (KB)
+          w[ks][i] = cat8(lds_read_tr(&sW[st][woff[i & 1] + o]), lds_read_tr(&sW[st][woff[i & 1] + o + 4 * GBM]));
+        else
           w[ks][i] = *(const bf16x8*)&sW[st][woff[ks] + i * 32 * GBK];
-        }
       }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -669,8 +661,22 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
                     (int64_t)GBK * g.lda * 2 < ((int64_t)1 << 31) && (int64_t)GBK * g.ldb * 2 < ((int64_t)1 << 31);
     if (!ok) return hipErrorInvalidValue;
     dim3 gb((unsigned)(((g.m + GBM - 1) / GBM) * ((g.n + GBN - 1) / GBN)), 1, g.batch);
-    gemm_bf16_big_kernel<EPI_STORE, 1, true><<<gb, 256, 0, s>>>(g);
+    gemm_bf16_big_kernel<EPI_STORE, 1, 3><<<gb, 256, 0, s>>>(g);
     return hipGetLastError();
+  }
+  // NN with fp32 output (B [k, n] K-major): the 256x256 kernel when its grid
+  // covers every CU at least once, else the 128x128 kernel below
+  if (g.b_kn) {
+    const int64_t bm = (g.m + GBM - 1) / GBM, bn = (g.n + GBN - 1) / GBN;
+    const bool ok = ct == 1 && g.epilogue == EPI_STORE && g.k >= GBK && g.k % GBK == 0 && g.n % 8 == 0 &&
+                    g.lda % 8 == 0 && g.ldb % 8 == 0 && g.ldb >= g.n && g.ldc % 4 == 0 && g.a_bstride % 8 == 0 &&
+                    g.b_bstride % 8 == 0 && (int64_t)GBM * g.lda * 2 < ((int64_t)1 << 31) &&
+                    (int64_t)GBK * g.ldb * 2 < ((int64_t)1 << 31);
+    if (ok && bm * bn * g.batch >= 256) {
+      dim3 gb((unsigned)(bm * bn), 1, g.batch);
+      gemm_bf16_big_kernel<EPI_STORE, 1, 2><<<gb, 256, 0, s>>>(g);
+      return hipGetLastError();
+    }
   }
   // the 256x256 kernel when its grid covers every CU at least once and the
   // operands suit its copies (K a multiple of 32, 16-byte rows and batch

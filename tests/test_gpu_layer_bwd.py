@@ -131,6 +131,16 @@ def test_layer_backward_many_heads(mla, variant):
     run_case(mla, MANY_HEADS[variant], [37, 100, 163], seed=6)
 
 
+def test_layer_backward_wide_hidden(mla):
+    """4096 tokens, hidden 4096, 8 heads, q latent 1536: the NN products dx =
+    dc W_kv_a + dq_lat W_q_a (16 x 16 output tiles) and the split-K product
+    dq W_q_b (16 x 6 tiles x 4 slices) have at least 256 tiles of 256 x 256
+    and read their [k, n] weight K-major on the 256x256 kernel."""
+    _say("case: layer backward, hidden 4096, 8 heads, lens=[2048, 2048]")
+    sh = mi.WORKLOADS["dsv3_prefill_4096"].replace(q_lora_rank=1536, hidden=4096, num_heads=8)
+    run_case(mla, sh, [2048, 2048], seed=7)
+
+
 def test_layer_backward_one_token_documents(mla):
     """Documents of one token (their attention gradient reaches only v) beside
     a document longer than one 128-row tile."""
