@@ -984,7 +984,7 @@ LayerBwdWs layer_bwd_layout(const mla_config* c, int64_t n) {
   w.trb = take(std::max({F, rq, rkv, gro}) * w.npad * 2);  // X^T of a weight gradient
   w.xt = take((int64_t)c->hidden * w.npad * 2);           // x^T (three weight gradients read it)
   w.wot = take(c->o_groups > 0 ? 0 : F * c->hidden * 2);  // W_o^T (NT form of dA2 = dout W_o)
-  w.split = take(kSplitK * n * std::max(rkv, rq) * 4);     // split-K partials of dc_n and dq_lat_n
+  w.split = take(n * std::max(kSplitK * std::max(rkv, rq), 2 * kSplitK * rkv) * 4);   // split-K partials of dc_n, dq_lat_n
   w.total = off;
   return w;
 }
@@ -1111,17 +1111,21 @@ mla_status mla_prefill_bwd(const mla_config* cfg, const mla_weights* w, const vo
     return gemm(tr, npad, bt, npad, out, x_cols, dy_cols, x_cols, (int)npad, false, true, false);
   };
   // c [m, nn] fp32 = a [m, k] b [k, nn] (NN) as kSplitK products over slices
-  // of k (batched, into partial buffers) and their sum
+  // of k (batched, into partial buffers) and their sum; 2 kSplitK slices when
+  // that (and only that) gives the 256x256 kernel its 256 tiles (nn <= r_kv)
   auto gemm_nn_splitk = [&](const void* a, int64_t lda, const void* b, int64_t ldb, float* c, int m, int nn,
                             int k) -> mla_status {
     float* part = (float*)at(L.split);
     if (k % (kSplitK * 8) != 0 || (int64_t)m * nn % 4 != 0)
       return gemm(a, lda, b, ldb, c, nn, m, nn, k, true, true, false);
-    const int ks = k / kSplitK;
-    mla_status r = gemm(a, lda, b, ldb, part, nn, m, nn, ks, true, true, false, EPI_STORE, kSplitK, ks,
+    const int64_t tiles = (int64_t)((m + 255) / 256) * ((nn + 255) / 256);
+    const int split = tiles * kSplitK < 256 && tiles * 2 * kSplitK >= 256 && k % (2 * kSplitK * 32) == 0 &&
+                              nn <= rkv ? 2 * kSplitK : kSplitK;
+    const int ks = k / split;
+    mla_status r = gemm(a, lda, b, ldb, part, nn, m, nn, ks, true, true, false, EPI_STORE, split, ks,
                         (int64_t)ks * ldb, (int64_t)m * nn);
     if (r != MLA_OK) return r;
-    const hipError_t err = launch_sum_partials(part, kSplitK, (int64_t)m * nn, c, st);
+    const hipError_t err = launch_sum_partials(part, split, (int64_t)m * nn, c, st);
     return err == hipSuccess ? MLA_OK : hip_fail(err, "split-K sum");
   };
   auto norm = [&](const void* src, int64_t stride, int width, int norm_dim, const void* gamma, int rope_off,
